@@ -1,0 +1,198 @@
+"""fp64 CPU oracle for the 3x3 convolution -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It loads ``liboracle_conv3x3.so``
+(plain C, built from ``conv3x3_oracle.c`` by ``build.sh``) and shares nothing
+with the HIP library.  The C file's header states the definition it follows
+(PyTorch Conv2d semantics, read from the sourcepulse summary of the C++/CUDA
+UNet project, sections "How It Works", "Quick Start & Requirements" and
+"Highlighted Details") and the pins that check it.
+
+All functions take numpy arrays or CPU torch tensors (any real dtype; they are
+widened to float64, which is exact for float32 and bfloat16 values) and return
+float64 numpy arrays.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# CONV3X3_ORACLE_LIB lets the pin suite run against a deliberately broken
+# build (tests/test_oracle_mutants.py); normal use never sets it.
+LIB_PATH = os.environ.get("CONV3X3_ORACLE_LIB") or os.path.join(_HERE, "liboracle_conv3x3.so")
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+_i = ctypes.c_int
+_n = ctypes.c_int64
+
+
+def build():
+    """Compile the oracle with gcc."""
+    subprocess.check_call(["sh", os.path.join(_HERE, "build.sh")])
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: widen through float32 (exact for bf16)
+        a = a.detach().cpu().float().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _idx(idx):
+    return np.ascontiguousarray(np.asarray(idx, dtype=np.int64).ravel())
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+class Oracle:
+    """One loaded build of the oracle library (the default one, or a test build)."""
+
+    def __init__(self, path=LIB_PATH):
+        lib = ctypes.CDLL(path)
+        lib.oracle_conv3x3_fwd.argtypes = [_D, _D, _D, _D, _i, _i, _i, _i, _i]
+        lib.oracle_conv3x3_bwd_data.argtypes = [_D, _D, _D, _i, _i, _i, _i, _i]
+        lib.oracle_conv3x3_bwd_weight.argtypes = [_D, _D, _D, _D, _i, _i, _i, _i, _i]
+        lib.oracle_conv3x3_fwd_at.argtypes = [_D, _D, _D, _i, _i, _i, _i, _i, _I64, _n, _D]
+        lib.oracle_conv3x3_bwd_data_at.argtypes = [_D, _D, _i, _i, _i, _i, _i, _I64, _n, _D]
+        lib.oracle_conv3x3_bwd_weight_at.argtypes = [_D, _D, _i, _i, _i, _i, _i, _I64, _n, _D]
+        lib.oracle_conv3x3_bias_grad_at.argtypes = [_D, _i, _i, _i, _i, _I64, _n, _D]
+        for f in ("oracle_conv3x3_fwd", "oracle_conv3x3_bwd_data",
+                  "oracle_conv3x3_bwd_weight", "oracle_conv3x3_fwd_at",
+                  "oracle_conv3x3_bwd_data_at", "oracle_conv3x3_bwd_weight_at",
+                  "oracle_conv3x3_bias_grad_at", "oracle_num_threads"):
+            getattr(lib, f).restype = _i
+        self.lib = lib
+
+    def num_threads(self):
+        return self.lib.oracle_num_threads()
+
+    def conv3x3_fwd(self, x, w, b=None):
+        """y [N,K,H,W] for x [N,C,H,W], w [K,C,3,3], optional b [K]."""
+        x, w, b = _f64(x), _f64(w), _f64(b)
+        N, C, H, W = x.shape
+        K = w.shape[0]
+        assert w.shape == (K, C, 3, 3) and (b is None or b.shape == (K,))
+        y = np.empty((N, K, H, W), np.float64)
+        _check(self.lib.oracle_conv3x3_fwd(_p(x), _p(w), _p(b), _p(y), N, C, K, H, W), "fwd")
+        return y
+
+    def conv3x3_bwd_data(self, g, w):
+        """dx [N,C,H,W] for g [N,K,H,W], w [K,C,3,3]."""
+        g, w = _f64(g), _f64(w)
+        N, K, H, W = g.shape
+        C = w.shape[1]
+        assert w.shape == (K, C, 3, 3)
+        dx = np.empty((N, C, H, W), np.float64)
+        _check(self.lib.oracle_conv3x3_bwd_data(_p(g), _p(w), _p(dx), N, C, K, H, W),
+               "bwd_data")
+        return dx
+
+    def conv3x3_bwd_weight(self, x, g, want_db=True):
+        """(dw [K,C,3,3], db [K] or None) for x [N,C,H,W], g [N,K,H,W]."""
+        x, g = _f64(x), _f64(g)
+        N, C, H, W = x.shape
+        K = g.shape[1]
+        assert g.shape == (N, K, H, W)
+        dw = np.empty((K, C, 3, 3), np.float64)
+        db = np.empty((K,), np.float64) if want_db else None
+        _check(self.lib.oracle_conv3x3_bwd_weight(_p(x), _p(g), _p(dw), _p(db),
+                                                  N, C, K, H, W), "bwd_weight")
+        return dw, db
+
+    def conv3x3_fwd_at(self, x, w, b, idx):
+        """y.ravel()[idx], each element computed on its own."""
+        x, w, b, idx = _f64(x), _f64(w), _f64(b), _idx(idx)
+        N, C, H, W = x.shape
+        K = w.shape[0]
+        out = np.empty(idx.shape, np.float64)
+        _check(self.lib.oracle_conv3x3_fwd_at(_p(x), _p(w), _p(b), N, C, K, H, W,
+                                              idx.ctypes.data_as(_I64), idx.size, _p(out)),
+               "fwd_at")
+        return out
+
+    def conv3x3_bwd_data_at(self, g, w, idx):
+        """dx.ravel()[idx], each element computed on its own."""
+        g, w, idx = _f64(g), _f64(w), _idx(idx)
+        N, K, H, W = g.shape
+        C = w.shape[1]
+        out = np.empty(idx.shape, np.float64)
+        _check(self.lib.oracle_conv3x3_bwd_data_at(_p(g), _p(w), N, C, K, H, W,
+                                                   idx.ctypes.data_as(_I64), idx.size,
+                                                   _p(out)), "bwd_data_at")
+        return out
+
+    def conv3x3_bwd_weight_at(self, x, g, idx):
+        """dw.ravel()[idx], each element computed on its own."""
+        x, g, idx = _f64(x), _f64(g), _idx(idx)
+        N, C, H, W = x.shape
+        K = g.shape[1]
+        out = np.empty(idx.shape, np.float64)
+        _check(self.lib.oracle_conv3x3_bwd_weight_at(_p(x), _p(g), N, C, K, H, W,
+                                                     idx.ctypes.data_as(_I64), idx.size,
+                                                     _p(out)), "bwd_weight_at")
+        return out
+
+    def conv3x3_bias_grad_at(self, g, idx):
+        """db[idx], each element computed on its own."""
+        g, idx = _f64(g), _idx(idx)
+        N, K, H, W = g.shape
+        out = np.empty(idx.shape, np.float64)
+        _check(self.lib.oracle_conv3x3_bias_grad_at(_p(g), N, K, H, W,
+                                                    idx.ctypes.data_as(_I64), idx.size,
+                                                    _p(out)), "bias_grad_at")
+        return out
+
+
+_default = None
+
+
+def _o():
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def num_threads():
+    return _o().num_threads()
+
+
+def conv3x3_fwd(x, w, b=None):
+    return _o().conv3x3_fwd(x, w, b)
+
+
+def conv3x3_bwd_data(g, w):
+    return _o().conv3x3_bwd_data(g, w)
+
+
+def conv3x3_bwd_weight(x, g, want_db=True):
+    return _o().conv3x3_bwd_weight(x, g, want_db)
+
+
+def conv3x3_fwd_at(x, w, b, idx):
+    return _o().conv3x3_fwd_at(x, w, b, idx)
+
+
+def conv3x3_bwd_data_at(g, w, idx):
+    return _o().conv3x3_bwd_data_at(g, w, idx)
+
+
+def conv3x3_bwd_weight_at(x, g, idx):
+    return _o().conv3x3_bwd_weight_at(x, g, idx)
+
+
+def conv3x3_bias_grad_at(g, idx):
+    return _o().conv3x3_bias_grad_at(g, idx)
