@@ -1,0 +1,214 @@
+"""Benchmark of the gfx950 conv3x3 path: forward + bias, backward-data and
+backward-weight (+ bias gradient) of one UNet stem layer on one GPU.
+
+One step = the whole path over one batch of seeded synthetic input already
+resident in device memory: conv3x3_fwd, conv3x3_bwd_data, conv3x3_bwd_weight.
+The workload is the UNet stem convolution at 64x64 image resolution
+(N=32, C=64 -> K=64, H=W=64, float32); the diffusion UNet these layers come
+from is trained on ImageNet 64x64 in the sources, and seeded N(0,1)
+activations / gradients with Kaiming-uniform weights stand in for that data.
+
+Prints ONE JSON line: throughput in TFLOP/s (2*N*H*W*C*K*9 per pass, three
+passes per step), the roofline figure of the slowest kernel (timed with HIP
+events on the stream the kernels run on) and the fp64 CPU oracle's
+throughput on a bounded sample of the same layer (test infrastructure, timed
+only as a reported baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--sweep OUT.json]
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "conv3x3 fwd+bwd TFLOP/s and % of MFMA/HBM roofline on 1 MI355X"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # dense MFMA peaks, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def flops_per_pass(N, C, K, H, W):
+    return 2.0 * N * H * W * C * K * 9
+
+
+def alg_bytes(pass_, N, C, K, H, W, dtype):
+    """Each tensor crosses HBM once: inputs at their dtype, outputs float32."""
+    s = 4 if dtype == "f32" else 2
+    M = N * H * W
+    if pass_ == "fwd":
+        return s * (M * C + 9 * K * C) + 4 * K + 4 * M * K
+    if pass_ == "bwd_data":
+        return s * (M * K + 9 * K * C) + 4 * M * C
+    return s * (M * C + M * K) + 4 * (9 * K * C + K)
+
+
+class LayerRun:
+    """Device buffers and the three pass launches of one layer."""
+
+    def __init__(self, layer):
+        import torch
+        import diffusion_unet_x3_amd as lib3
+        import workloads as wl
+        self.lib3, self.layer = lib3, layer
+        dev = torch.device("cuda", 0)
+        inp = wl.make_inputs(layer)
+        self.x, self.w, self.g = (inp[k].to(dev) for k in ("x", "w", "g"))
+        self.b = inp["b"].to(dev)
+        N, C, K, H, W = layer.shape
+        self.y = torch.empty((N, K, H, W), device=dev)
+        self.dx = torch.empty((N, C, H, W), device=dev)
+        self.dw = torch.empty((K, C, 3, 3), device=dev)
+        self.db = torch.empty((K,), device=dev)
+        code = lib3.CONV3X3_F32 if layer.dtype == "f32" else lib3.CONV3X3_BF16
+        ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y)
+
+    def bwd_data(self):
+        self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx)
+
+    def bwd_weight(self):
+        self.lib3.conv3x3_bwd_weight(self.x, self.g, dw=self.dw, db=self.db, workspace=self.ws)
+
+    def passes(self):
+        return (("fwd", self.fwd), ("bwd_data", self.bwd_data), ("bwd_weight", self.bwd_weight))
+
+
+def time_layer(run, steps, warmup):
+    """Per-pass average ms (events between the passes) and per-step ms."""
+    import torch
+    for _ in range(warmup):
+        for _, f in run.passes():
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        ev[i][0].record()
+        for j, (_, f) in enumerate(run.passes()):
+            f()
+            ev[i][j + 1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = {}
+    for j, (name, _) in enumerate(run.passes()):
+        per[name] = sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
+    return total_ms / steps, per
+
+
+def cpu_baseline(layer, budget_s=15.0):
+    """fp64 oracle on the layer's shape with the batch cut to fit the budget."""
+    import oracle
+    import workloads as wl
+    from dataclasses import replace
+    N, C, K, H, W = layer.shape
+    probe = replace(layer, N=1)
+    inp = wl.make_inputs(probe)
+    t = time.perf_counter()
+    oracle.conv3x3_fwd(inp["x"], inp["w"], inp["b"])
+    t1 = time.perf_counter() - t
+    n = int(max(1, min(N, budget_s / max(3 * t1, 1e-6))))
+    sample = replace(layer, N=n)
+    inp = wl.make_inputs(sample)
+    x, w, b, g = (oracle._f64(inp[k]) for k in ("x", "w", "b", "g"))
+    t = time.perf_counter()
+    oracle.conv3x3_fwd(x, w, b)
+    oracle.conv3x3_bwd_data(g, w)
+    oracle.conv3x3_bwd_weight(x, g)
+    dt = time.perf_counter() - t
+    fl = 3 * flops_per_pass(n, C, K, H, W)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"all three passes of the same layer at N={n} of {N} images "
+                      f"({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); cpu: {platform.processor() or platform.machine()}"}
+
+
+def sweep(out_path, steps, warmup):
+    import torch
+    import workloads as wl
+    rows = []
+    for cfg, layers in sorted(wl.CONFIGS.items()):
+        for layer in layers:
+            run = LayerRun(layer)
+            ms, per = time_layer(run, steps, warmup)
+            N, C, K, H, W = layer.shape
+            f = flops_per_pass(N, C, K, H, W)
+            row = {"config": cfg, "layer": layer.name, "dtype": layer.dtype,
+                   "shape": [N, C, K, H, W], "ms_step": ms}
+            for p, t in per.items():
+                tf = f / (t * 1e-3) / 1e12
+                row[p] = {"ms": t, "tflops": tf, "mfma_frac": tf / PEAK_TFLOPS[layer.dtype],
+                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype) / (t * 1e-3) / 1e9}
+            rows.append(row)
+            print(f"{layer.name:44s} " + " ".join(
+                f"{p}={row[p]['ms'] * 1e3:8.1f}us {row[p]['tflops']:7.1f}TF" for p in per),
+                file=sys.stderr, flush=True)
+            del run
+            torch.cuda.empty_cache()
+    with open(out_path, "w") as fh:
+        json.dump(rows, fh, indent=1)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", metavar="OUT_JSON", help="also time every configured layer")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    layer = wl.CONFIGS[2][0]
+    N, C, K, H, W = layer.shape
+    run = LayerRun(layer)
+    ms, per = time_layer(run, args.steps, args.warmup)
+    f = flops_per_pass(N, C, K, H, W)
+    value = 3 * f / (ms * 1e-3) / 1e12
+    dom = max(per, key=per.get)
+    achieved = f / (per[dom] * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": layer.dtype, "data": "synthetic",
+        "config": {"workload": "unet_stem_conv3x3_fwd_bias+bwd_data+bwd_weight",
+                   "N": N, "C_in": C, "C_out": K, "H": H, "W": W, "stride": 1, "pad": 1,
+                   "layout": "NCHW", "seed": layer.seed, "global_batch": N,
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 3),
+                     "peak": PEAK_TFLOPS[layer.dtype], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS[layer.dtype], 4), "traffic": None},
+        "passes": {p: {"us": round(t * 1e3, 2),
+                       "tflops": round(f / (t * 1e-3) / 1e12, 2),
+                       "alg_gbs": round(alg_bytes(p, N, C, K, H, W, layer.dtype) /
+                                        (t * 1e-3) / 1e9, 1)} for p, t in per.items()},
+    }
+    del run
+    torch.cuda.empty_cache()
+    if args.sweep:
+        sweep(args.sweep, max(5, args.steps // 5), 3)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(layer)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+"""Python binding of the gfx950 conv3x3 library (libconv3x3.so).
+
+Argument marshalling only: every step of the convolution runs in the HIP
+kernels behind the C ABI declared in ``include/conv3x3.h``; PyTorch supplies
+device memory and the current stream.  The functions carry the C names:
+
+    conv3x3_fwd(x, w, bias=None, out=None)                    -> y
+    conv3x3_bwd_data(g, w, out=None)                          -> dx
+    conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None,
+                       workspace=None)                        -> (dw, db)
+    conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)   -> bytes
+    conv3x3_status_string(code)                               -> str
+    conv3x3_plan(pass_, N, C, K, H, W, dtype)                 -> dict
+
+Tensors are NCHW / OIHW, contiguous, on a GPU; x, w, g are float32 or
+bfloat16 (all three alike), bias is float32, outputs are float32.  There is
+no fallback: if the library is missing, importing this package raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconv3x3.so")
+
+CONV3X3_F32 = 0
+CONV3X3_BF16 = 1
+PASS_FWD, PASS_BWD_DATA, PASS_BWD_WEIGHT = 0, 1, 2
+STATUS = {
+    "OK": 0, "ERR_NULL_POINTER": 1, "ERR_BAD_SHAPE": 2, "ERR_BAD_DTYPE": 3,
+    "ERR_WORKSPACE": 4, "ERR_ALIAS": 5, "ERR_HIP": 6, "ERR_BAD_PASS": 7,
+}
+EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_size",
+            "conv3x3_bwd_weight", "conv3x3_status_string", "conv3x3_plan"]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "pass_", "dtype", "kernel", "tile_m", "tile_n", "tile_imgs", "tile_h", "tile_w",
+        "chunk", "threads", "grid_x", "grid_y", "grid_z", "lds_bytes", "split")] + \
+        [("workspace_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -m diffusion_unet_x3_amd.build "
+            "or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    lib.conv3x3_fwd.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_fwd.restype = i
+    lib.conv3x3_bwd_data.argtypes = [vp, vp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data.restype = i
+    lib.conv3x3_bwd_weight_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.conv3x3_bwd_weight_workspace_size.restype = ctypes.c_size_t
+    lib.conv3x3_bwd_weight.argtypes = [vp, vp, fp, fp, vp, ctypes.c_size_t,
+                                       i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight.restype = i
+    lib.conv3x3_status_string.argtypes = [i]
+    lib.conv3x3_status_string.restype = ctypes.c_char_p
+    lib.conv3x3_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.conv3x3_plan.restype = i
+    return lib
+
+
+lib = _load()
+
+
+def conv3x3_status_string(code):
+    return lib.conv3x3_status_string(int(code)).decode()
+
+
+def _raise(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {conv3x3_status_string(rc)} (status {rc})")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return CONV3X3_F32
+    if t.dtype == torch.bfloat16:
+        return CONV3X3_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check(t, name, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _f32_out(out, shape, like, name):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    _check(out, name, len(shape))
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must be float32 of shape {tuple(shape)}")
+    return out
+
+
+def conv3x3_fwd(x, w, bias=None, out=None):
+    """y = conv3x3(x; w) + bias (stride 1, zero padding 1), float32 output."""
+    _check(x, "x", 4)
+    _check(w, "w", 4)
+    N, C, H, W = x.shape
+    K = w.shape[0]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != x.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with x's dtype")
+    if bias is not None:
+        _check(bias, "bias", 1)
+        if bias.dtype != torch.float32 or bias.shape[0] != K:
+            raise ValueError("bias must be float32 [K]")
+    y = _f32_out(out, (N, K, H, W), x, "out")
+    rc = lib.conv3x3_fwd(x.data_ptr(), w.data_ptr(),
+                         None if bias is None else bias.data_ptr(), y.data_ptr(),
+                         N, C, K, H, W, _dtype_code(x), _stream(x))
+    _raise(rc, "conv3x3_fwd")
+    return y
+
+
+def conv3x3_bwd_data(g, w, out=None):
+    """dx = d<conv3x3(x; w), g>/dx, float32 output."""
+    _check(g, "g", 4)
+    _check(w, "w", 4)
+    N, K, H, W = g.shape
+    C = w.shape[1]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with g's dtype")
+    dx = _f32_out(out, (N, C, H, W), g, "out")
+    rc = lib.conv3x3_bwd_data(g.data_ptr(), w.data_ptr(), dx.data_ptr(),
+                              N, C, K, H, W, _dtype_code(g), _stream(g))
+    _raise(rc, "conv3x3_bwd_data")
+    return dx
+
+
+def conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype=CONV3X3_F32):
+    n = lib.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid problem for conv3x3_bwd_weight_workspace_size")
+    return n
+
+
+def conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None, workspace=None):
+    """(dw, db) = gradients of <conv3x3(x; w) + b, g> w.r.t. w and b, float32."""
+    _check(x, "x", 4)
+    _check(g, "g", 4)
+    N, C, H, W = x.shape
+    K = g.shape[1]
+    if tuple(g.shape) != (N, K, H, W) or g.dtype != x.dtype:
+        raise ValueError("g must be [N, K, H, W] with x's dtype")
+    code = _dtype_code(x)
+    dw = _f32_out(dw, (K, C, 3, 3), x, "dw")
+    if want_db:
+        db = _f32_out(db, (K,), x, "db")
+    else:
+        db = None
+    need = conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.conv3x3_bwd_weight(x.data_ptr(), g.data_ptr(), dw.data_ptr(),
+                                None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
+                                N, C, K, H, W, code, _stream(x))
+    _raise(rc, "conv3x3_bwd_weight")
+    return dw, db
+
+
+def conv3x3_plan(pass_, N, C, K, H, W, dtype=CONV3X3_F32):
+    """The launch plan the library uses for one pass (host-side query)."""
+    p = Plan()
+    rc = lib.conv3x3_plan(pass_, N, C, K, H, W, dtype, ctypes.byref(p))
+    _raise(rc, "conv3x3_plan")
+    return {name: getattr(p, name) for name, _ in Plan._fields_}

@@ -1,0 +1,51 @@
+// Device-side building blocks shared by the conv3x3 kernels: vector types,
+// the MFMA steps, and the pixel-block coordinate helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace conv3x3 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// D(32x32) += A(32x2) * B(2x32), fp32 in, fp32 accumulate.  Lane l supplies
+// A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator register v of lane l
+// holds D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.  Lane l
+// supplies A[l % 32][8 * (l / 32) + 0..7] and B[8 * (l / 32) + 0..7][l % 32];
+// the accumulator layout is the one of the fp32 step above.
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held by register v of this lane.
+__device__ __forceinline__ int acc_row(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }
+
+// Decode a workgroup's pixel block origin from its linear block index.
+struct BlockOrigin {
+  int n0, h0, w0;
+};
+
+template <int TW, int TH, int IMGS>
+__device__ __forceinline__ BlockOrigin block_origin(int b, int tiles_w, int tiles_h) {
+  BlockOrigin o;
+  const int tw_i = b % tiles_w;
+  b /= tiles_w;
+  const int th_i = b % tiles_h;
+  const int tn_i = b / tiles_h;
+  o.n0 = tn_i * IMGS;
+  o.h0 = th_i * TH;
+  o.w0 = tw_i * TW;
+  return o;
+}
+
+}  // namespace conv3x3

@@ -1,0 +1,333 @@
+// Forward (+bias) and backward-data 3x3 convolution, float32, gfx950.
+//
+// One implicit-GEMM kernel serves both passes (see the C header for the
+// formulas):
+//   forward       : out[n,co,p] = bias[co] + sum_{ci,tap} src[n,ci,p+tap] w[co,ci,tap]
+//                   with src = x (Cin = C), co over K;
+//   backward-data : the same with src = g (Cin = K), co over C and the weight
+//                   read as w[ci, co, 8 - tap] -- the transpose and 180-degree
+//                   rotation happen in the LDS staging index, never in memory.
+//
+// Workgroup: 256 threads (4 wave64s) own BCO output channels x a pixel block
+// of IMGS x TH x TW pixels (128).  Waves split it 2 (channels) x 2 (pixels);
+// each wave accumulates (BCO/2) x 64 outputs in 32x32 MFMA tiles.  Per LDS
+// fill the block stages CB input channels of the source with their one-pixel
+// halo (zero where the halo leaves the image) and the matching CB x 9 x BCO
+// weights; the next fill's global loads are issued before the current fill's
+// MFMAs so that their latency hides behind the math.  MFMA 32x32x2 f32: the
+// two reduction elements of a step are two consecutive input channels at the
+// same tap; lanes 0-31 and 32-63 read them from adjacent LDS planes.
+#include "common.hpp"
+#include "launch.hpp"
+#include "lds_layout.hpp"
+
+namespace conv3x3 {
+
+template <int MODE, int TW, int TH, int IMGS, int BCO, int CB, bool VEC>
+__global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
+    const float* __restrict__ src, const float* __restrict__ wt, const float* __restrict__ bias,
+    float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h) {
+  constexpr int BM = IMGS * TH * TW;
+  static_assert(BM == 128, "pixel block must hold 128 pixels");
+  constexpr int RS = fwd_f32_rs(TW);
+  constexpr int PL = fwd_f32_plane(IMGS, TH, TW);
+  constexpr int WS = fwd_f32_wstride(BCO);
+  constexpr int MI = BCO / 64;  // 32x32 tiles per wave along channels
+  constexpr int NJ = BM / 64;   // 32x32 tiles per wave along pixels
+  constexpr int HR = TH + 2;    // staged rows per image (with halo)
+
+  __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
+  __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wco = wave & 1, wpx = wave >> 1;
+  const BlockOrigin o = block_origin<TW, TH, IMGS>(blockIdx.x, tiles_w, tiles_h);
+  const int co0 = blockIdx.y * BCO;
+  const long HW = (long)H * W;
+
+  // ---------------- staging: source tile ----------------
+  // Vector path: interior columns as float4 (W % 4 == 0 so a float4 never
+  // straddles the image edge), the two halo columns as scalars.
+  constexpr int XQ = TW / 4;
+  constexpr int XV_ITEMS = CB * IMGS * HR * XQ;
+  constexpr int XV_N = (XV_ITEMS + 255) / 256;
+  constexpr int XH_ITEMS = CB * IMGS * HR * 2;
+  constexpr int XH_N = (XH_ITEMS + 255) / 256;
+  // Scalar path: every column of the staged rows.
+  constexpr int XS_ITEMS = CB * IMGS * HR * (TW + 2);
+  constexpr int XS_N = (XS_ITEMS + 255) / 256;
+  f32x4 xv[VEC ? XV_N : 1];
+  float xf[VEC ? XH_N : 1];
+
+  // ---------------- staging: weight tile ----------------
+  // Forward: for each co, the CB x 9 weights w[co, c0.., :] are contiguous.
+  // Backward-data: for each ci (= k), the BCO x 9 weights w[ci, co0.., :] are.
+  constexpr int RUN = MODE == kFwd ? CB * 9 : BCO * 9;
+  constexpr int NRUN = MODE == kFwd ? BCO : CB;
+  constexpr int WV_ITEMS = NRUN * RUN / 4;
+  constexpr int WV_N = (WV_ITEMS + 255) / 256;
+  constexpr int WS_ITEMS = CB * 9 * BCO;
+  constexpr int WS_N = (WS_ITEMS + 255) / 256;
+  f32x4 wv[VEC ? WV_N : 1];
+
+  // Vector path: global -> registers here (one fill ahead), registers -> LDS
+  // in store_tiles.  Scalar path: everything happens in store_tiles.
+  auto load_tiles = [&](int c0) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < XV_N; ++k) {
+        const int it = tid + k * 256;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (XV_ITEMS % 256 == 0 || it < XV_ITEMS) {
+          const int q = it % XQ;
+          int t = it / XQ;
+          const int rr = t % HR;
+          t /= HR;
+          const int img = t % IMGS;
+          const int ch = t / IMGS;
+          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
+          if (n < N && c < Cin && h >= 0 && h < H && w < W)
+            v = *reinterpret_cast<const f32x4*>(src + ((long)n * Cin + c) * HW + (long)h * W + w);
+        }
+        xv[k] = v;
+      }
+#pragma unroll
+      for (int k = 0; k < XH_N; ++k) {
+        const int it = tid + k * 256;
+        float v = 0.f;
+        if (XH_ITEMS % 256 == 0 || it < XH_ITEMS) {
+          const int side = it & 1;
+          int t = it >> 1;
+          const int rr = t % HR;
+          t /= HR;
+          const int img = t % IMGS;
+          const int ch = t / IMGS;
+          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1;
+          const int w = o.w0 + (side ? TW : -1);
+          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
+            v = src[((long)n * Cin + c) * HW + (long)h * W + w];
+        }
+        xf[k] = v;
+      }
+    }
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < WV_N; ++k) {
+        const int it = tid + k * 256;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (WV_ITEMS % 256 == 0 || it < WV_ITEMS) {
+          const int run = it / (RUN / 4);
+          const int e = 4 * (it % (RUN / 4));
+          if constexpr (MODE == kFwd) {
+            const int co = co0 + run;
+            if (co < Cout && e < (Cin - c0) * 9)
+              v = *reinterpret_cast<const f32x4*>(wt + ((long)co * Cin + c0) * 9 + e);
+          } else {
+            const int ci = c0 + run;
+            if (ci < Cin && e < (Cout - co0) * 9)
+              v = *reinterpret_cast<const f32x4*>(wt + ((long)ci * Cout + co0) * 9 + e);
+          }
+        }
+        wv[k] = v;
+      }
+    }
+  };
+
+  // LDS slot of weight element e (0 <= e < RUN) of run `run`.
+  auto w_slot = [&](int run, int e) -> int {
+    if constexpr (MODE == kFwd) {
+      return e * WS + run;  // e = ci_l * 9 + tap, co_l = run
+    } else {
+      return (run * 9 + (8 - e % 9)) * WS + e / 9;  // ci_l = run, co_l = e/9, tap = 8 - e%9
+    }
+  };
+
+  auto store_tiles = [&](int c0) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < XV_N; ++k) {
+        const int it = tid + k * 256;
+        if (XV_ITEMS % 256 == 0 || it < XV_ITEMS) {
+          const int q = it % XQ;
+          const int t = it / XQ;  // (ch * IMGS + img) * HR + rr
+          *reinterpret_cast<f32x4*>(&xs[t * RS + 4 + 4 * q]) = xv[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < XH_N; ++k) {
+        const int it = tid + k * 256;
+        if (XH_ITEMS % 256 == 0 || it < XH_ITEMS) {
+          const int side = it & 1;
+          const int t = it >> 1;
+          xs[t * RS + 4 + (side ? TW : -1)] = xf[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < WV_N; ++k) {
+        const int it = tid + k * 256;
+        if (WV_ITEMS % 256 == 0 || it < WV_ITEMS) {
+          const int run = it / (RUN / 4);
+          const int e = 4 * (it % (RUN / 4));
+          ws[w_slot(run, e + 0)] = wv[k].x;
+          ws[w_slot(run, e + 1)] = wv[k].y;
+          ws[w_slot(run, e + 2)] = wv[k].z;
+          ws[w_slot(run, e + 3)] = wv[k].w;
+        }
+      }
+    } else {
+      // Scalar path (ragged shapes): global loads go straight to LDS.
+#pragma unroll 4
+      for (int k = 0; k < XS_N; ++k) {
+        const int it = tid + k * 256;
+        if (XS_ITEMS % 256 == 0 || it < XS_ITEMS) {
+          const int cc = it % (TW + 2) - 1;
+          const int t = it / (TW + 2);  // (ch * IMGS + img) * HR + rr
+          const int rr = t % HR;
+          const int img = (t / HR) % IMGS;
+          const int ch = t / (HR * IMGS);
+          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + cc;
+          float v = 0.f;
+          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
+            v = src[((long)n * Cin + c) * HW + (long)h * W + w];
+          xs[t * RS + 4 + cc] = v;
+        }
+      }
+#pragma unroll 4
+      for (int k = 0; k < WS_N; ++k) {
+        const int it = tid + k * 256;
+        if (WS_ITEMS % 256 == 0 || it < WS_ITEMS) {
+          const int run = it / RUN;
+          const int e = it % RUN;
+          float v = 0.f;
+          if constexpr (MODE == kFwd) {
+            const int co = co0 + run, ci = c0 + e / 9;
+            if (co < Cout && ci < Cin) v = wt[((long)co * Cin + ci) * 9 + e % 9];
+          } else {
+            const int ci = c0 + run, co = co0 + e / 9;
+            if (ci < Cin && co < Cout) v = wt[((long)ci * Cout + co) * 9 + e % 9];
+          }
+          ws[w_slot(run, e)] = v;
+        }
+      }
+    }
+  };
+
+  // ---------------- per-lane operand offsets ----------------
+  int boff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int p = wpx * (BM / 2) + j * 32 + l32;
+    const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+    boff[j] = hi * PL + (img * HR + row) * RS + 4 + col - 1;
+  }
+  const int aoff = hi * 9 * WS + wco * (BCO / 2) + l32;
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nchunks = (Cin + CB - 1) / CB;
+  load_tiles(0);
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    if (chunk) __syncthreads();
+    store_tiles(chunk * CB);
+    __syncthreads();
+    if (chunk + 1 < nchunks) load_tiles((chunk + 1) * CB);
+#pragma unroll 2
+    for (int cp = 0; cp < CB / 2; ++cp) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          float a[MI], b[NJ];
+#pragma unroll
+          for (int i = 0; i < MI; ++i) a[i] = ws[aoff + (2 * cp * 9 + r * 3 + s) * WS + i * 32];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) b[j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x2_f32(a[i], b[j], acc[i][j]);
+        }
+      }
+    }
+  }
+
+  // ---------------- epilogue: bias + NCHW stores ----------------
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int p = wpx * (BM / 2) + j * 32 + l32;
+    const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+    const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+    if (n >= N || h >= H || w >= W) continue;
+    float* out = dst + (long)n * Cout * HW + (long)h * W + w;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int co = co0 + wco * (BCO / 2) + i * 32 + acc_row(v, hi);
+        if (co < Cout) {
+          float val = acc[i][j][v];
+          if (MODE == kFwd && bias) val += bias[co];
+          out[(long)co * HW] = val;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launcher: dispatch the plan's geometry / tile to an instantiation.
+
+template <int MODE, int TW, int TH, int IMGS, int BCO, int CB>
+static void launch_geom(const Plan& pl, bool vec, const float* src, const float* wt,
+                        const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+                        hipStream_t stream) {
+  dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
+  if (vec)
+    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, CB, true>), grid, block, 0,
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, CB, false>), grid, block, 0,
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+}
+
+template <int MODE, int BCO, int CB>
+static bool launch_bco(const Plan& pl, bool vec, const float* src, const float* wt,
+                       const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+                       hipStream_t s) {
+  switch (pl.geom) {
+    case kG64x2: launch_geom<MODE, 64, 2, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
+    case kG32x4: launch_geom<MODE, 32, 4, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
+    case kG16x8: launch_geom<MODE, 16, 8, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
+    case kG8x16: launch_geom<MODE, 8, 16, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
+    case kG8x8x2: launch_geom<MODE, 8, 8, 2, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
+    default: return false;
+  }
+}
+
+template <int MODE>
+static bool launch_mode(const Plan& pl, bool vec, const float* src, const float* wt,
+                        const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+                        hipStream_t s) {
+  if (pl.tile_co == 64 && pl.chunk == 16)
+    return launch_bco<MODE, 64, 16>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s);
+  if (pl.tile_co == 128 && pl.chunk == 8)
+    return launch_bco<MODE, 128, 8>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s);
+  return false;
+}
+
+bool launch_fwd_f32(const Plan& pl, bool vec, const float* src, const float* wt, const float* bias,
+                    float* dst, int N, int Cin, int Cout, int H, int W, hipStream_t stream) {
+  if (pl.pass == kFwd)
+    return launch_mode<kFwd>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, stream);
+  return launch_mode<kBwdData>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, stream);
+}
+
+}  // namespace conv3x3

@@ -1,0 +1,31 @@
+// Host launchers of the conv3x3 kernel families (one per source file).
+// Each returns false when the plan names a variant the file does not hold.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "planner.hpp"
+
+namespace conv3x3 {
+
+// Forward (pl.pass == kFwd; src = x, Cin = C, Cout = K) or backward-data
+// (pl.pass == kBwdData; src = g, Cin = K, Cout = C; bias ignored), float32.
+bool launch_fwd_f32(const Plan& pl, bool vec, const float* src, const float* wt, const float* bias,
+                    float* dst, int N, int Cin, int Cout, int H, int W, hipStream_t stream);
+
+// Same, bfloat16 inputs (raw 16-bit patterns), float32 outputs.
+bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
+                     const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+                     hipStream_t stream);
+
+// Backward-weight (+ optional db), float32; ws holds the per-slice partials
+// when pl.split > 1.
+bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
+                      float* db, float* ws, int N, int C, int K, int H, int W, hipStream_t stream);
+
+// Same, bfloat16 inputs.
+bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
+                       float* db, float* ws, int N, int C, int K, int H, int W,
+                       hipStream_t stream);
+
+}  // namespace conv3x3

@@ -1,0 +1,74 @@
+// LDS layouts of the conv3x3 kernels, shared by the kernels and the planner.
+//
+// Forward / backward-data, float32 (MFMA 32x32x2, reduction pairs of input
+// channels at one tap):
+//   x tile : [chunk][imgs][th + 2][RS]  floats, RS = tw + 8.  Image column
+//            cc in [-1, tw] of the block sits at row offset 4 + cc, so the
+//            interior starts 16-byte aligned and each row is written with
+//            128-bit stores; rows/columns outside the image hold zero.
+//   w tile : [chunk][9][co_tile + 1]  floats (the +1 keeps the transposing
+//            stores free of bank conflicts).
+//
+// Forward / backward-data, bfloat16 (MFMA 32x32x16, each lane supplies 8
+// consecutive input channels at one tap):
+//   x tile : [chunk / 8][imgs][th + 2][RS][8]  bf16 -- 8 channels of one
+//            pixel form one 16-byte LDS word, so the MFMA operand is a single
+//            128-bit LDS read; RS = tw + 8, image column cc at 4 + cc.
+//   w tile : [9][chunk / 8][co_tile][8]  bf16.
+//
+// Backward-weight, float32 (MFMA 32x32x2, reduction pairs of pixels):
+//   g tile : [64 k][P + 1]  floats, P = imgs * th * tw pixels per chunk.
+//   x tile : [64 c][PLW]  floats, PLW = imgs * (th + 2) * (tw + 2) rounded up
+//            to odd so that 32 channels read at one pixel hit 32 banks;
+//            image column cc in [-1, tw] sits at row offset 1 + cc.
+#pragma once
+
+#if defined(__HIPCC__)
+#define CONV3X3_HD __host__ __device__
+#else
+#define CONV3X3_HD
+#endif
+
+namespace conv3x3 {
+
+// ---- forward / backward-data, float32 ----
+CONV3X3_HD constexpr int fwd_f32_rs(int tw) { return tw + 8; }
+CONV3X3_HD constexpr int fwd_f32_plane(int imgs, int th, int tw) {
+  return imgs * (th + 2) * fwd_f32_rs(tw);
+}
+CONV3X3_HD constexpr int fwd_f32_wstride(int co_tile) { return co_tile + 1; }
+CONV3X3_HD constexpr int fwd_f32_x_floats(int cb, int imgs, int th, int tw) {
+  return cb * fwd_f32_plane(imgs, th, tw);
+}
+CONV3X3_HD constexpr int fwd_f32_w_floats(int cb, int co_tile) {
+  return cb * 9 * fwd_f32_wstride(co_tile);
+}
+CONV3X3_HD constexpr int fwd_f32_lds_bytes(int cb, int imgs, int th, int tw, int co_tile) {
+  return 4 * (fwd_f32_x_floats(cb, imgs, th, tw) + fwd_f32_w_floats(cb, co_tile));
+}
+
+// ---- forward / backward-data, bfloat16 ----
+CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw + 8; }
+CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {  // in 16-byte words
+  return imgs * (th + 2) * fwd_bf16_rs(tw);
+}
+CONV3X3_HD constexpr int fwd_bf16_lds_bytes(int cb, int imgs, int th, int tw, int co_tile) {
+  return 16 * (cb / 8) * fwd_bf16_plane(imgs, th, tw) + 2 * 9 * cb * co_tile;
+}
+
+// ---- backward-weight, float32 ----
+CONV3X3_HD constexpr int wgrad_f32_gstride(int imgs, int th, int tw) { return imgs * th * tw + 1; }
+CONV3X3_HD constexpr int wgrad_f32_rs(int tw) { return tw + 2; }
+CONV3X3_HD constexpr int wgrad_f32_plane(int imgs, int th, int tw) {
+  return (imgs * (th + 2) * wgrad_f32_rs(tw)) | 1;
+}
+CONV3X3_HD constexpr int wgrad_f32_lds_bytes(int imgs, int th, int tw) {
+  return 4 * 64 * (wgrad_f32_gstride(imgs, th, tw) + wgrad_f32_plane(imgs, th, tw));
+}
+
+// ---- backward-weight, bfloat16 ----
+CONV3X3_HD constexpr int wgrad_bf16_lds_bytes(int imgs, int th, int tw) {
+  return 2 * 64 * (imgs * th * tw + 8) + 2 * 64 * (imgs * (th + 2) * (tw + 16));
+}
+
+}  // namespace conv3x3

@@ -1,0 +1,89 @@
+// Launch planning for the 3x3 convolution kernels (host only, no HIP calls).
+//
+// The forward and backward-data passes are one implicit GEMM: rows are
+// output channels (K for the forward pass, C for backward-data), columns are
+// output pixels (M = N*H*W), and the reduction runs over 9 taps x input
+// channels.  A workgroup owns a tile of `tile_co` output channels by a pixel
+// block of tile_imgs x tile_h x tile_w pixels; the reduction is staged in
+// LDS `chunk` input channels at a time.
+//
+// The backward-weight pass is the GEMM dw[k, (c, tap)] = sum_pixels
+// g[k, p] * x[c, p + tap offset]: a workgroup owns 64 k x 64 c x 9 taps and
+// walks a slice of the pixel reduction, `chunk` pixels per LDS fill; the
+// reduction is split into `split` slices whose partial sums are added by a
+// second kernel in a fixed order.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace conv3x3 {
+
+enum Pass { kFwd = 0, kBwdData = 1, kBwdWeight = 2 };
+enum DType { kF32 = 0, kBF16 = 1 };
+
+// Pixel-block geometries, shared by every kernel family.  The block is
+// imgs x th x tw pixels; tw is the width of the block (power of two).
+enum Geom {
+  kG64x2 = 0,   // tw 64, th 2
+  kG32x4 = 1,   // tw 32, th 4
+  kG16x8 = 2,   // tw 16, th 8
+  kG8x16 = 3,   // tw 8,  th 16
+  kG8x8x2 = 4,  // tw 8,  th 8, two images
+  kG64x1 = 5,   // tw 64, th 1
+  kG32x2 = 6,   // tw 32, th 2
+  kG16x4 = 7,   // tw 16, th 4
+  kG8x8 = 8,    // tw 8,  th 8
+  kNumGeom = 9
+};
+
+struct GeomDims {
+  int tw, th, imgs;
+};
+
+inline GeomDims geom_dims(int g) {
+  switch (g) {
+    case kG64x2: return {64, 2, 1};
+    case kG32x4: return {32, 4, 1};
+    case kG16x8: return {16, 8, 1};
+    case kG8x16: return {8, 16, 1};
+    case kG8x8x2: return {8, 8, 2};
+    case kG64x1: return {64, 1, 1};
+    case kG32x2: return {32, 2, 1};
+    case kG16x4: return {16, 4, 1};
+    default: return {8, 8, 1};
+  }
+}
+
+struct Plan {
+  int pass = 0;
+  int dtype = 0;
+  int geom = 0;       // Geom
+  int tile_co = 0;    // fwd/bwd_data: output channels per WG; bwd_weight: k per WG
+  int tile_ci = 0;    // bwd_weight: input channels per WG
+  int tw = 0, th = 0, imgs = 0;
+  int chunk = 0;      // channels (fwd/bwd_data) or pixels (bwd_weight) per LDS fill
+  int threads = 256;
+  int tiles_w = 0, tiles_h = 0, tiles_n = 0;
+  int grid_x = 0, grid_y = 0, grid_z = 0;
+  int lds_bytes = 0;
+  int split = 1;          // bwd_weight: reduction slices
+  int chunks_per_split = 0;
+  int nchunks = 0;
+  int vec = 0;            // 1: 128-bit global paths allowed (decided at launch; 0 here)
+  size_t workspace_bytes = 0;
+};
+
+// Problem dims as the implicit GEMM sees them.  For backward-data the
+// "input" channels are K (g is the input) and the output channels are C.
+struct Problem {
+  int pass, dtype;
+  int N, C, K, H, W;
+};
+
+bool plan(const Problem& p, Plan* out);
+
+// Minimum workspace bytes for a bwd_weight plan.
+size_t wgrad_workspace_bytes(const Plan& pl, int C, int K);
+
+}  // namespace conv3x3

@@ -1,0 +1,160 @@
+/*
+ * conv3x3.h -- C ABI of the gfx950 (MI355X) 3x3 convolution library.
+ *
+ * The operation is the stride-1, zero-padding-1 3x3 convolution that the
+ * sourcepulse summary of the C++/CUDA diffusion-UNet project singles out as
+ * the layer worth hand-written kernels ("How It Works"; forward timings and
+ * the forward/backward comparison with PyTorch in "Highlighted Details";
+ * the lagging backward pass in "Limitations & Caveats").  The model is built
+ * by a PyTorch script ("Quick Start & Requirements"), so the operation is read
+ * as PyTorch's Conv2d(kernel 3, stride 1, padding 1) -- a cross-correlation:
+ *
+ *   y [n,k,h,w] = bias[k] + sum_{c,r,s} x[n,c,h+r-1,w+s-1] * w[k,c,r,s]
+ *   dx[n,c,h,w] = sum_{k,r,s} g[n,k,h-r+1,w-s+1] * w[k,c,r,s]
+ *   dw[k,c,r,s] = sum_{n,h,w} g[n,k,h,w] * x[n,c,h+r-1,w+s-1]
+ *   db[k]       = sum_{n,h,w} g[n,k,h,w]
+ *
+ * with x, g read as zero outside the H x W image.  dx, dw, db are the
+ * gradients of <y, g> with respect to x, w and bias.
+ *
+ * Layouts (all dense, row-major, no strides):
+ *   x, dx : [N][C][H][W]      g, y : [N][K][H][W]
+ *   w, dw : [K][C][3][3]      bias, db : [K]
+ *
+ * dtype (the `dtype` argument):
+ *   CONV3X3_F32  : x, w, g are float32.
+ *   CONV3X3_BF16 : x, w, g are bfloat16 (raw 16-bit patterns); products are
+ *                  exact and accumulate in float32.
+ *   In both modes bias is float32 and every output (y, dx, dw, db) is float32.
+ *
+ * Memory and ownership: every pointer is a device pointer (hipMalloc'd or
+ * torch-allocated) owned by the caller.  The library allocates nothing,
+ * keeps no mutable global state and is safe to call from several host
+ * threads.  Outputs are overwritten, never accumulated into.  Outputs must
+ * not alias inputs (identical base pointers are rejected; partial overlap is
+ * undefined).  No alignment is required: 128-bit paths are used when the
+ * base address and row length allow it.
+ *
+ * Streams and errors: work is enqueued on `stream` (NULL = the null stream)
+ * and the call returns without synchronising.  Argument errors return a
+ * nonzero status BEFORE anything is enqueued.  A failed launch returns
+ * CONV3X3_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation, as usual for HIP.
+ *
+ * Size limits: N, C, K, H, W >= 1; every tensor holds fewer than 2^31
+ * elements (else CONV3X3_ERR_BAD_SHAPE).
+ */
+#ifndef CONV3X3_H
+#define CONV3X3_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t, declared here so that C callers need no HIP
+ * headers.  NULL selects the null stream. */
+typedef struct ihipStream_t* conv3x3_stream_t;
+
+typedef enum {
+  CONV3X3_F32 = 0,
+  CONV3X3_BF16 = 1
+} conv3x3_dtype_t;
+
+typedef enum {
+  CONV3X3_OK = 0,
+  CONV3X3_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  CONV3X3_ERR_BAD_SHAPE = 2,    /* a dimension < 1, or a tensor >= 2^31 elements */
+  CONV3X3_ERR_BAD_DTYPE = 3,    /* dtype is not a conv3x3_dtype_t value */
+  CONV3X3_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
+  CONV3X3_ERR_ALIAS = 5,        /* an output shares its base pointer with an input */
+  CONV3X3_ERR_HIP = 6,          /* the HIP runtime rejected a launch */
+  CONV3X3_ERR_BAD_PASS = 7      /* conv3x3_plan: unknown pass */
+} conv3x3_status_t;
+
+typedef enum {
+  CONV3X3_PASS_FWD = 0,
+  CONV3X3_PASS_BWD_DATA = 1,
+  CONV3X3_PASS_BWD_WEIGHT = 2
+} conv3x3_pass_t;
+
+/*
+ * Forward with fused bias:  y = conv(x; w) + bias.
+ *   x    : [N][C][H][W], dtype          w : [K][C][3][3], dtype
+ *   bias : [K] float32, or NULL for no bias
+ *   y    : [N][K][H][W] float32 (overwritten)
+ * Implicit GEMM with M = N*H*W pixels, N = K output channels and a
+ * reduction of length 9*C; input tiles and their one-pixel halo are staged
+ * in LDS, the products run on MFMA.
+ */
+int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y,
+                int N, int C, int K, int H, int W, int dtype,
+                conv3x3_stream_t stream);
+
+/*
+ * Backward-data:  dx = gradient of <conv(x; w), g> with respect to x.
+ *   g  : [N][K][H][W], dtype      w : [K][C][3][3], dtype
+ *   dx : [N][C][H][W] float32 (overwritten)
+ * The same implicit GEMM as the forward pass over g, with the weight tile
+ * transposed (k <-> c) and rotated by 180 degrees while it is staged in LDS.
+ */
+int conv3x3_bwd_data(const void* g, const void* w, float* dx,
+                     int N, int C, int K, int H, int W, int dtype,
+                     conv3x3_stream_t stream);
+
+/*
+ * Bytes of device workspace conv3x3_bwd_weight needs for this problem
+ * (0 if it needs none).  Returns (size_t)-1 for invalid arguments.
+ */
+size_t conv3x3_bwd_weight_workspace_size(int N, int C, int K, int H, int W, int dtype);
+
+/*
+ * Backward-weight and bias gradient:
+ *   x  : [N][C][H][W], dtype      g : [N][K][H][W], dtype
+ *   dw : [K][C][3][3] float32 (overwritten)
+ *   db : [K] float32 (overwritten), or NULL to skip the bias gradient
+ *   workspace : device buffer of at least
+ *               conv3x3_bwd_weight_workspace_size(...) bytes (may be NULL
+ *               when that size is 0); its contents are scratch.
+ * The pixel reduction (length N*H*W) is split into slices whose partial sums
+ * are written to the workspace and then added in a fixed order by a second
+ * kernel on the same stream: no atomics, bitwise-reproducible results.
+ */
+int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db,
+                       void* workspace, size_t workspace_bytes,
+                       int N, int C, int K, int H, int W, int dtype,
+                       conv3x3_stream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* conv3x3_status_string(int status);
+
+/*
+ * Launch plan the library would use for a pass (host only; no GPU needed).
+ * Lets callers and tests see tile shapes, grid, LDS use and split factor.
+ */
+typedef struct {
+  int pass;            /* conv3x3_pass_t */
+  int dtype;           /* conv3x3_dtype_t */
+  int kernel;          /* internal kernel variant id */
+  int tile_m;          /* rows of the WG tile: output channels (fwd, bwd_data) or k (bwd_weight) */
+  int tile_n;          /* columns of the WG tile: pixels (fwd, bwd_data) or input channels (bwd_weight) */
+  int tile_imgs;       /* pixel tile = tile_imgs x tile_h x tile_w */
+  int tile_h;
+  int tile_w;
+  int chunk;           /* reduction chunk staged per LDS fill: channels, or pixels (bwd_weight) */
+  int threads;         /* threads per workgroup */
+  int grid_x, grid_y, grid_z;
+  int lds_bytes;       /* static LDS per workgroup */
+  int split;           /* bwd_weight: number of reduction slices (1 = none) */
+  size_t workspace_bytes;
+} conv3x3_plan_t;
+
+int conv3x3_plan(int pass, int N, int C, int K, int H, int W, int dtype,
+                 conv3x3_plan_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV3X3_H */

@@ -1,0 +1,97 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before touching the GPU (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_unet_x3_amd as lib3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv3x3.h")
+L = lib3.lib
+S = lib3.STATUS
+
+# Distinct non-null fake device addresses: never dereferenced, because every
+# call below fails validation first.
+X, Wt, B, Y, G, WS = (ctypes.c_void_p(0x10000 * (i + 1)) for i in range(6))
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv3x3_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = _declared_functions()
+    assert set(names) == set(lib3.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(8):
+        assert lib3.conv3x3_status_string(code)
+    assert lib3.conv3x3_status_string(0) == "success"
+    assert "unknown" in lib3.conv3x3_status_string(99)
+
+
+@pytest.mark.parametrize("dims", [(0, 1, 1, 1, 1), (1, 0, 1, 1, 1), (1, 1, 0, 1, 1),
+                                  (1, 1, 1, 0, 1), (1, 1, 1, 1, 0), (-1, 4, 4, 4, 4),
+                                  (2, 1 << 16, 4, 128, 128),      # x has 2^31 elements
+                                  (1, 4, 1 << 16, 1 << 8, 1 << 7),  # y has 2^31 elements
+                                  (1, 1 << 14, 1 << 14, 1, 1)])   # w has > 2^31 elements
+def test_bad_shapes_rejected(dims):
+    N, C, K, H, W = dims
+    assert L.conv3x3_fwd(X, Wt, B, Y, N, C, K, H, W, 0, None) == S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_bwd_data(G, Wt, Y, N, C, K, H, W, 0, None) == S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_bwd_weight(X, G, Y, B, WS, 1 << 40, N, C, K, H, W, 0, None) == S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, 0) == ctypes.c_size_t(-1).value
+
+
+def test_null_pointers_rejected():
+    d = (2, 3, 4, 5, 6)
+    assert L.conv3x3_fwd(None, Wt, B, Y, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_fwd(X, None, B, Y, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_fwd(X, Wt, B, None, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_data(None, Wt, Y, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_data(G, Wt, None, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_weight(None, G, Y, B, WS, 1 << 40, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_weight(X, G, None, B, WS, 1 << 40, *d, 0, None) == S["ERR_NULL_POINTER"]
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_bad_dtype_rejected(dtype):
+    d = (2, 3, 4, 5, 6)
+    assert L.conv3x3_fwd(X, Wt, B, Y, *d, dtype, None) == S["ERR_BAD_DTYPE"]
+    assert L.conv3x3_bwd_data(G, Wt, Y, *d, dtype, None) == S["ERR_BAD_DTYPE"]
+    assert L.conv3x3_bwd_weight(X, G, Y, B, WS, 1 << 40, *d, dtype, None) == S["ERR_BAD_DTYPE"]
+
+
+def test_aliasing_rejected():
+    d = (2, 3, 4, 5, 6)
+    assert L.conv3x3_fwd(X, Wt, B, X, *d, 0, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_fwd(X, Wt, B, B, *d, 0, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_bwd_data(G, Wt, G, *d, 0, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_bwd_weight(X, G, X, B, WS, 1 << 40, *d, 0, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_bwd_weight(X, G, Y, Y, WS, 1 << 40, *d, 0, None) == S["ERR_ALIAS"]
+
+
+def test_workspace_checked():
+    N, C, K, H, W = 32, 64, 64, 64, 64
+    need = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W)
+    assert need > 0
+    assert L.conv3x3_bwd_weight(X, G, Y, B, None, need, N, C, K, H, W, 0, None) == S["ERR_WORKSPACE"]
+    assert L.conv3x3_bwd_weight(X, G, Y, B, WS, need - 1, N, C, K, H, W, 0, None) == S["ERR_WORKSPACE"]
+    assert L.conv3x3_bwd_weight(X, G, Y, B, X, need, N, C, K, H, W, 0, None) == S["ERR_ALIAS"]
+
+
+def test_plan_query_errors():
+    p = lib3.Plan()
+    assert L.conv3x3_plan(3, 1, 1, 1, 1, 1, 0, ctypes.byref(p)) == S["ERR_BAD_PASS"]
+    assert L.conv3x3_plan(0, 1, 1, 1, 1, 1, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_plan(0, 1, 1, 1, 1, 1, 5, ctypes.byref(p)) == S["ERR_BAD_DTYPE"]

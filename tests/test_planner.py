@@ -1,0 +1,47 @@
+"""CPU checks of the launch planner (through the C ABI's plan query): every
+problem is tiled completely, LDS fits a gfx950 compute unit, the
+backward-weight split never leaves a slice empty and its workspace formula
+holds."""
+import math
+
+import pytest
+
+import diffusion_unet_x3_amd as lib3
+import workloads as wl
+
+LDS_PER_CU = 160 * 1024
+SHAPES = sorted({l.shape for c in wl.CONFIGS.values() for l in c} | set(wl.RAGGED_SHAPES))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_forward_type_plans_cover_problem(shape, dtype):
+    N, C, K, H, W = shape
+    for pass_, cout in ((lib3.PASS_FWD, K), (lib3.PASS_BWD_DATA, C)):
+        p = lib3.conv3x3_plan(pass_, N, C, K, H, W, dtype)
+        assert p["tile_n"] == p["tile_imgs"] * p["tile_h"] * p["tile_w"]
+        tiles = (math.ceil(N / p["tile_imgs"]) * math.ceil(H / p["tile_h"]) *
+                 math.ceil(W / p["tile_w"]))
+        assert p["grid_x"] == tiles
+        assert p["grid_y"] * p["tile_m"] >= cout > (p["grid_y"] - 1) * p["tile_m"]
+        assert 0 < p["lds_bytes"] <= LDS_PER_CU
+        assert p["threads"] == 256 and p["split"] == 1 and p["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_weight_gradient_plans(shape, dtype):
+    N, C, K, H, W = shape
+    p = lib3.conv3x3_plan(lib3.PASS_BWD_WEIGHT, N, C, K, H, W, dtype)
+    chunks = (math.ceil(N / p["tile_imgs"]) * math.ceil(H / p["tile_h"]) *
+              math.ceil(W / p["tile_w"]))
+    S = p["split"]
+    assert 1 <= S <= chunks
+    per = math.ceil(chunks / S)
+    assert (S - 1) * per < chunks <= S * per  # no empty slice
+    assert p["grid_x"] == S
+    assert p["grid_y"] * p["tile_n"] >= C and p["grid_z"] * p["tile_m"] >= K
+    assert 0 < p["lds_bytes"] <= LDS_PER_CU
+    ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)
+    assert ws == p["workspace_bytes"]
+    assert ws == (0 if S == 1 else S * (K * C * 9 + K) * 4)
