@@ -4,17 +4,19 @@
 //   db[k]       = sum_{n,h,w} g[n,k,h,w]
 //
 // A GEMM with rows k, columns (c, tap) and a reduction over pixels -- the
-// contiguous axis of both NCHW operands.  A workgroup (4 wave64s) owns
-// 64 k x 64 c x 9 taps (each wave 32 k x 32 c x 9 taps, nine 32x32
-// accumulators that share the g operand) and walks one slice of the pixel
-// reduction, 64 pixels (an IMGS x TH x TW block) per LDS fill: g for those
-// pixels and x for the same block plus its one-pixel halo.  MFMA 32x32x2
-// f32: the two reduction elements of a step are two horizontally adjacent
-// pixels.  Each slice writes its partial sums (and, in the workgroups of the
-// first channel tile, the partial db, reduced across lanes with fixed-order
-// cross-lane adds) to its own workspace slot; wgrad_reduce_kernel then adds
-// the slots in slice order.  No atomics anywhere: results are bitwise
-// reproducible.
+// contiguous axis of both NCHW operands.  A workgroup of 12 wave64s owns
+// 64 k x 64 c x 9 taps: wave w takes the 32 x 32 block (kb, cb) and kernel
+// row r = w % 3, i.e. three 32x32 accumulators (s = 0, 1, 2) that share the
+// g operand.  Three waves per SIMD keep the MFMA pipe fed while others wait
+// on LDS.  The workgroup walks one slice of the pixel reduction, 64 pixels
+// (an IMGS x TH x TW block) per LDS fill: g for those pixels and x for the
+// same block plus its one-pixel halo.  MFMA 32x32x2 f32: the two reduction
+// elements of a step are two horizontally adjacent pixels.  Each slice writes
+// its partial sums, tap-major ([tap][k][c], so the stores are coalesced),
+// and -- in the workgroups of the first channel tile -- the partial db,
+// reduced across lanes with fixed-order cross-lane adds, to its own
+// workspace slot; wgrad_reduce_kernel adds the slots in a fixed order.  No
+// atomics anywhere: results are bitwise reproducible.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -22,7 +24,7 @@
 namespace conv3x3 {
 
 template <int TW, int TH, int IMGS, bool VEC>
-__global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
+__global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ g, float* __restrict__ out,
     float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
     int nchunks, int per_split, long slice_stride) {
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int wk = wave & 1, wc = wave >> 1;
+  const int r = wave % 3, kb = (wave / 3) & 1, cb = wave / 6;
   const int slice = blockIdx.x;
   const int c0 = blockIdx.y * 64;
   const int k0 = blockIdx.z * 64;
@@ -49,16 +51,16 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
   // g tile: 64 k x P pixels.  x tile: 64 c x IMGS x HR rows x (TW + 2) columns.
   constexpr int XQ = TW / 4;
   constexpr int GV_ITEMS = 64 * IMGS * TH * XQ;
-  constexpr int GV_N = GV_ITEMS / 256;
+  constexpr int NT = 768;
+  constexpr int GV_N = (GV_ITEMS + NT - 1) / NT;
   constexpr int XV_ITEMS = 64 * IMGS * HR * XQ;
-  constexpr int XV_N = (XV_ITEMS + 255) / 256;
+  constexpr int XV_N = (XV_ITEMS + NT - 1) / NT;
   constexpr int XH_ITEMS = 64 * IMGS * HR * 2;
-  constexpr int XH_N = (XH_ITEMS + 255) / 256;
+  constexpr int XH_N = (XH_ITEMS + NT - 1) / NT;
   constexpr int GS_ITEMS = 64 * P;
-  constexpr int GS_N = GS_ITEMS / 256;
+  constexpr int GS_N = (GS_ITEMS + NT - 1) / NT;
   constexpr int XS_ITEMS = 64 * IMGS * HR * (TW + 2);
-  constexpr int XS_N = (XS_ITEMS + 255) / 256;
-  static_assert(GV_ITEMS % 256 == 0 && GS_ITEMS % 256 == 0, "g tile must split evenly");
+  constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
 
   f32x4 gv[VEC ? GV_N : 1];
   f32x4 xv[VEC ? XV_N : 1];
@@ -69,7 +71,12 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < GV_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (GV_ITEMS % NT != 0 && it >= GV_ITEMS) {
+          gv[k] = v;
+          continue;
+        }
         const int q = it % XQ;
         int t = it / XQ;
         const int row = t % TH;
@@ -77,16 +84,15 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
         const int img = t % IMGS;
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 4 * q;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (n < N && kk < K && h < H && w < W)
           v = *reinterpret_cast<const f32x4*>(g + ((long)n * K + kk) * HW + (long)h * W + w);
         gv[k] = v;
       }
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (XV_ITEMS % 256 == 0 || it < XV_ITEMS) {
+        if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
           const int q = it % XQ;
           int t = it / XQ;
           const int rr = t % HR;
@@ -101,9 +107,9 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
         float v = 0.f;
-        if (XH_ITEMS % 256 == 0 || it < XH_ITEMS) {
+        if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
           const int side = it & 1;
           int t = it >> 1;
           const int rr = t % HR;
@@ -126,7 +132,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < GV_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
+        if (GV_ITEMS % NT != 0 && it >= GV_ITEMS) continue;
         const int q = it % XQ;
         const int t = it / XQ;  // (kl * IMGS + img) * TH + row
         const int kl = t / (IMGS * TH);
@@ -139,8 +146,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
-        const int it = tid + k * 256;
-        if (XV_ITEMS % 256 == 0 || it < XV_ITEMS) {
+        const int it = tid + k * NT;
+        if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
           const int q = it % XQ;
           const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
           const int cl = t / (IMGS * HR);
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
-        const int it = tid + k * 256;
-        if (XH_ITEMS % 256 == 0 || it < XH_ITEMS) {
+        const int it = tid + k * NT;
+        if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
           const int side = it & 1;
           const int t = it >> 1;
           const int cl = t / (IMGS * HR);
@@ -166,7 +173,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
       const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
 #pragma unroll 4
       for (int k = 0; k < GS_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
+        if (GS_ITEMS % NT != 0 && it >= GS_ITEMS) continue;
         const int col = it % TW;
         int t = it / TW;
         const int row = t % TH;
@@ -180,8 +188,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
       }
 #pragma unroll 4
       for (int k = 0; k < XS_N; ++k) {
-        const int it = tid + k * 256;
-        if (XS_ITEMS % 256 == 0 || it < XS_ITEMS) {
+        const int it = tid + k * NT;
+        if (XS_ITEMS % NT == 0 || it < XS_ITEMS) {
           const int cc = it % (TW + 2) - 1;
           int t = it / (TW + 2);
           const int rr = t % HR;
@@ -198,17 +206,17 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
     }
   };
 
-  f32x16 acc[9];
+  f32x16 acc[3];
 #pragma unroll
-  for (int t = 0; t < 9; ++t)
+  for (int t = 0; t < 3; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
   float dbsum = 0.f;
 
   const int chunk_begin = slice * per_split;
   const int chunk_end = min(nchunks, chunk_begin + per_split);
-  const int goff = (wk * 32 + l32) * GS;
-  const int xoff = (wc * 32 + l32) * PLW;
+  const int goff = (kb * 32 + l32) * GS;
+  const int xoff = (cb * 32 + l32) * PLW + r * RSW;
 
   if (chunk_begin < chunk_end) load_tiles(chunk_begin);
   for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
@@ -216,37 +224,41 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
     store_tiles(chunk);
     __syncthreads();
     if (chunk + 1 < chunk_end) load_tiles(chunk + 1);
-#pragma unroll 4
+#pragma unroll 8
     for (int q2 = 0; q2 < P / 2; ++q2) {
       const int p = 2 * q2 + hi;
       const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
       const float a = gs[goff + p];
       const int xb = xoff + (img * HR + row) * RSW + col;
 #pragma unroll
-      for (int r = 0; r < 3; ++r)
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-          acc[r * 3 + s] = mfma_32x32x2_f32(a, xs[xb + r * RSW + s], acc[r * 3 + s]);
+      for (int s = 0; s < 3; ++s) acc[s] = mfma_32x32x2_f32(a, xs[xb + s], acc[s]);
     }
-    if (do_db) {
+    if (do_db && tid < 256) {
       const int kl = tid >> 2, part = tid & 3;
 #pragma unroll
       for (int i = 0; i < P / 4; ++i) dbsum += gs[kl * GS + part + 4 * i];
     }
   }
 
-  // Partial dw of this slice: [k][c][tap] at out + slice * slice_stride.
-  float* o_dw = out + (long)slice * slice_stride;
+  // Partial dw of this slice.  Split: tap-major [tap][k][c] slot at
+  // out + slice * slice_stride (32 consecutive c per store).  No split: dw
+  // itself, [k][c][tap].
+  const int c = c0 + cb * 32 + l32;
 #pragma unroll
-  for (int t = 0; t < 9; ++t) {
+  for (int s = 0; s < 3; ++s) {
+    const int t = r * 3 + s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int k = k0 + wk * 32 + acc_row(v, hi);
-      const int c = c0 + wc * 32 + l32;
-      if (k < K && c < C) o_dw[((long)k * C + c) * 9 + t] = acc[t][v];
+      const int k = k0 + kb * 32 + acc_row(v, hi);
+      if (k < K && c < C) {
+        if (slice_stride)
+          out[(long)slice * slice_stride + ((long)t * K + k) * C + c] = acc[s][v];
+        else
+          out[((long)k * C + c) * 9 + t] = acc[s][v];
+      }
     }
   }
-  if (do_db) {
+  if (do_db && tid < 256) {
     // Lanes 4j..4j+3 hold four interleaved partial sums of one k: add them
     // pairwise, (p0 + p1) + (p2 + p3), the same way every time.
     dbsum += __shfl_xor(dbsum, 1);
@@ -256,23 +268,47 @@ __global__ __launch_bounds__(256, 1) void wgrad_f32_kernel(
   }
 }
 
-// dw[e] = sum_{s < S} ws[s][e] and db[k] = sum_{s < S} ws_db[s][k], added in
-// slice order s = 0, 1, ..., S-1 (one thread per output element).
+// Split-K epilogue.  Workspace: S tap-major partial slots [S][9][K][C],
+// then S partial db rows [S][K].  Each workgroup owns 64 consecutive
+// elements; wave q of 4 adds the slots of a fixed contiguous quarter of the
+// slices in slice order, and wave 0 adds the four quarter sums as
+// ((q0 + q1) + q2) + q3.  The order never changes, so the result is bitwise
+// reproducible.  dw is written back in [k][c][tap] order.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ ws,
                                                            float* __restrict__ dw,
                                                            float* __restrict__ db, int S,
-                                                           long n_dw, int K) {
-  const long e = (long)blockIdx.x * 256 + threadIdx.x;
-  if (e < n_dw) {
-    float s = 0.f;
-    for (int i = 0; i < S; ++i) s += ws[(long)i * n_dw + e];
-    dw[e] = s;
-  } else if (db != nullptr && e < n_dw + K) {
-    const long k = e - n_dw;
-    const float* wdb = ws + (long)S * n_dw;
-    float s = 0.f;
-    for (int i = 0; i < S; ++i) s += wdb[(long)i * K + k];
-    db[k] = s;
+                                                           int C, int K) {
+  __shared__ float part[4][64];
+  const long n_dw = (long)K * C * 9;
+  const long total = n_dw + (db != nullptr ? K : 0);
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const long e = (long)blockIdx.x * 64 + lane;
+  const int per = (S + 3) / 4;
+  const int s0 = min(S, q * per), s1 = min(S, s0 + per);
+  float sum = 0.f;
+  if (e < total) {
+    const float* base;
+    long stride;
+    if (e < n_dw) {
+      base = ws + e;
+      stride = n_dw;
+    } else {
+      base = ws + (long)S * n_dw + (e - n_dw);
+      stride = K;
+    }
+    for (int i = s0; i < s1; ++i) sum += base[(long)i * stride];
+  }
+  part[q][lane] = sum;
+  __syncthreads();
+  if (q == 0 && e < total) {
+    const float v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    if (e < n_dw) {
+      const long t = e / ((long)K * C);
+      const long kc = e % ((long)K * C);  // k * C + c
+      dw[kc * 9 + t] = v;
+    } else {
+      db[e - n_dw] = v;
+    }
   }
 }
 
@@ -280,7 +316,7 @@ template <int TW, int TH, int IMGS>
 static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const float* g,
                               float* out, float* out_db, long slice_stride, int N, int C, int K,
                               int H, int W, hipStream_t stream) {
-  dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z), block(256, 1, 1);
+  dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z), block(pl.threads, 1, 1);
   if (vec)
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
                        out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
@@ -307,8 +343,8 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, 
   }
   if (pl.split > 1) {
     const long total = n_dw + (db ? K : 0);
-    dim3 grid((unsigned)((total + 255) / 256)), block(256);
-    hipLaunchKernelGGL(wgrad_reduce_kernel, grid, block, 0, stream, ws, dw, db, pl.split, n_dw, K);
+    dim3 grid((unsigned)((total + 63) / 64)), block(256);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, grid, block, 0, stream, ws, dw, db, pl.split, C, K);
   }
   return true;
 }

@@ -28,9 +28,9 @@ int wgrad_geom(int W) {
   return kG8x8;
 }
 
-// Number of workgroups the weight-gradient pass aims for: two per compute
-// unit on a 256-CU device.
-constexpr int kWgradTargetWGs = 512;
+// Number of workgroups the weight-gradient pass aims for: one 12-wave
+// workgroup per compute unit on a 256-CU device.
+constexpr int kWgradTargetWGs = 256;
 
 }  // namespace
 
@@ -89,7 +89,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.grid_x = pl.split;
     pl.grid_y = ceil_div(p.C, pl.tile_ci);
     pl.grid_z = ceil_div(p.K, pl.tile_co);
-    pl.threads = 256;
+    pl.threads = p.dtype == kF32 ? 768 : 256;
     pl.lds_bytes = p.dtype == kF32
         ? wgrad_f32_lds_bytes(pl.imgs, pl.th, pl.tw)
         : wgrad_bf16_lds_bytes(pl.imgs, pl.th, pl.tw);
