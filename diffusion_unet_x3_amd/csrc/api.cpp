@@ -120,7 +120,7 @@ int conv3x3_bwd_data(const void* g, const void* w, float* dx, int N, int C, int 
     const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w);
     ok = launch_fwd_f32(pl, vec, (const float*)g, (const float*)w, nullptr, dx, N, K, C, H, W, s);
   } else {
-    const bool vec = W % 8 == 0 && K % 8 == 0 && aligned16(g) && aligned16(w);
+    const bool vec = W % 8 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w);
     ok = launch_fwd_bf16(pl, vec, (const uint16_t*)g, (const uint16_t*)w, nullptr, dx, N, K, C, H,
                          W, s);
   }

@@ -1,6 +1,301 @@
+// Backward-weight and bias gradient of the 3x3 convolution, bfloat16 inputs
+// with float32 accumulation and output, gfx950.
+//
+// Same decomposition as the float32 kernel -- a workgroup of 12 wave64s owns
+// 64 k x 64 c x 9 taps, wave w the 32 x 32 block (kb, cb) and kernel row
+// r = w % 3 -- on v_mfma_f32_32x32x16_bf16, whose lanes each supply 8
+// consecutive reduction elements.  The reduction runs over pixels, the
+// contiguous axis of NCHW, so both operands come straight from
+// pixel-contiguous LDS tiles: g as [k][pixel] and x as [c][img][row][col]
+// with its one-pixel halo.  Eight pixels of one row start at an 8-aligned
+// column, so the g operand and the centre tap (s = 1) of x are aligned
+// 128-bit LDS reads; the left and right taps (s = 0, 2) are the same words
+// shifted by one bf16 element, assembled with funnel shifts from the aligned
+// word and one dword of its neighbour -- no unaligned LDS access.  A pixel
+// chunk is 128 pixels (8 MFMA steps).  Partial sums and the split-K reduce
+// are those of the float32 kernel.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_layout.hpp"
+
 namespace conv3x3 {
-bool launch_wgrad_bf16(const Plan&, bool, const uint16_t*, const uint16_t*, float*, float*, float*,
-                       int, int, int, int, int, hipStream_t) { return false; }
+
+namespace {
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+}  // namespace
+
+template <int TW, int TH, int IMGS, bool VEC>
+__global__ __launch_bounds__(768) void wgrad_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, float* __restrict__ out,
+    float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
+    int nchunks, int per_split, long slice_stride) {
+  constexpr int P = IMGS * TH * TW;
+  static_assert(P == 128, "pixel chunk must hold 128 pixels");
+  static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
+  constexpr int GSB = wgrad_bf16_gstride(IMGS, TH, TW);
+  constexpr int RSX = wgrad_bf16_rs(TW);
+  constexpr int PLX = wgrad_bf16_plane(IMGS, TH, TW);
+  constexpr int HR = TH + 2;
+  constexpr int NT = 768;
+
+  __shared__ __attribute__((aligned(16))) uint16_t gs[64 * GSB];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * PLX];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int r = wave % 3, kb = (wave / 3) & 1, cb = wave / 6;
+  const int slice = blockIdx.x;
+  const int c0 = blockIdx.y * 64;
+  const int k0 = blockIdx.z * 64;
+  const long HW = (long)H * W;
+  const bool do_db = out_db != nullptr && blockIdx.y == 0;
+
+  constexpr int XQ = TW / 8;                      // 8-pixel words per row
+  constexpr int GI = 64 * IMGS * TH * XQ;         // g words per chunk
+  constexpr int GN = (GI + NT - 1) / NT;
+  constexpr int XI = 64 * IMGS * HR * XQ;         // x words per chunk
+  constexpr int XN = (XI + NT - 1) / NT;
+  constexpr int HI_ = 64 * IMGS * HR * 2;         // x halo elements
+  constexpr int HN = (HI_ + NT - 1) / NT;
+  u32x4 gv[VEC ? GN : 1];
+  u32x4 xv[VEC ? XN : 1];
+  uint16_t xh[VEC ? HN : 1];
+
+  auto load_tiles = [&](int chunk) {
+    if constexpr (VEC) {
+      const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
+#pragma unroll
+      for (int k = 0; k < GN; ++k) {
+        const int it = tid + k * NT;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (GI % NT == 0 || it < GI) {
+          const int q = it % XQ;
+          int t = it / XQ;
+          const int row = t % TH;
+          t /= TH;
+          const int img = t % IMGS;
+          const int kl = t / IMGS;
+          const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 8 * q;
+          if (n < N && kk < K && h < H && w < W)
+            v = *reinterpret_cast<const u32x4*>(g + ((long)n * K + kk) * HW + (long)h * W + w);
+        }
+        gv[k] = v;
+      }
+#pragma unroll
+      for (int k = 0; k < XN; ++k) {
+        const int it = tid + k * NT;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (XI % NT == 0 || it < XI) {
+          const int q = it % XQ;
+          int t = it / XQ;
+          const int rr = t % HR;
+          t /= HR;
+          const int img = t % IMGS;
+          const int cl = t / IMGS;
+          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
+          if (n < N && c < C && h >= 0 && h < H && w < W)
+            v = *reinterpret_cast<const u32x4*>(x + ((long)n * C + c) * HW + (long)h * W + w);
+        }
+        xv[k] = v;
+      }
+#pragma unroll
+      for (int k = 0; k < HN; ++k) {
+        const int it = tid + k * NT;
+        uint16_t v = 0;
+        if (HI_ % NT == 0 || it < HI_) {
+          const int side = it & 1;
+          int t = it >> 1;
+          const int rr = t % HR;
+          t /= HR;
+          const int img = t % IMGS;
+          const int cl = t / IMGS;
+          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
+          const int w = o.w0 + (side ? TW : -1);
+          if (n < N && c < C && h >= 0 && h < H && w >= 0 && w < W)
+            v = x[((long)n * C + c) * HW + (long)h * W + w];
+        }
+        xh[k] = v;
+      }
+    }
+  };
+
+  auto store_tiles = [&](int chunk) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < GN; ++k) {
+        const int it = tid + k * NT;
+        if (GI % NT == 0 || it < GI) {
+          const int q = it % XQ;
+          const int t = it / XQ;  // (kl * IMGS + img) * TH + row
+          const int kl = t / (IMGS * TH);
+          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = gv[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < XN; ++k) {
+        const int it = tid + k * NT;
+        if (XI % NT == 0 || it < XI) {
+          const int q = it % XQ;
+          const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
+          const int cl = t / (IMGS * HR);
+          *reinterpret_cast<u32x4*>(&xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + 8 * q]) = xv[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < HN; ++k) {
+        const int it = tid + k * NT;
+        if (HI_ % NT == 0 || it < HI_) {
+          const int side = it & 1;
+          const int t = it >> 1;
+          const int cl = t / (IMGS * HR);
+          xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + (side ? TW : -1)] = xh[k];
+        }
+      }
+    } else {
+      // Scalar path (ragged shapes): 16-bit loads straight into LDS.
+      const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
+      constexpr int GS_ = 64 * P;
+#pragma unroll 4
+      for (int k = 0; k < (GS_ + NT - 1) / NT; ++k) {
+        const int it = tid + k * NT;
+        if (GS_ % NT == 0 || it < GS_) {
+          const int col = it % TW;
+          int t = it / TW;
+          const int row = t % TH;
+          t /= TH;
+          const int img = t % IMGS;
+          const int kl = t / IMGS;
+          const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + col;
+          uint16_t v = 0;
+          if (n < N && kk < K && h < H && w < W) v = g[((long)n * K + kk) * HW + (long)h * W + w];
+          gs[kl * GSB + it % P] = v;
+        }
+      }
+      constexpr int XS_ = 64 * IMGS * HR * (TW + 2);
+#pragma unroll 4
+      for (int k = 0; k < (XS_ + NT - 1) / NT; ++k) {
+        const int it = tid + k * NT;
+        if (XS_ % NT == 0 || it < XS_) {
+          const int cc = it % (TW + 2) - 1;
+          int t = it / (TW + 2);
+          const int rr = t % HR;
+          t /= HR;
+          const int img = t % IMGS;
+          const int cl = t / IMGS;
+          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + cc;
+          uint16_t v = 0;
+          if (n < N && c < C && h >= 0 && h < H && w >= 0 && w < W)
+            v = x[((long)n * C + c) * HW + (long)h * W + w];
+          xs[cl * PLX + (img * HR + rr) * RSX + 8 + cc] = v;
+        }
+      }
+    }
+  };
+
+  f32x16 acc[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+  float dbsum = 0.f;
+
+  const int chunk_begin = slice * per_split;
+  const int chunk_end = min(nchunks, chunk_begin + per_split);
+  const int goff = (kb * 32 + l32) * GSB;
+  const int xoff = (cb * 32 + l32) * PLX + r * RSX + 8;
+
+  if (chunk_begin < chunk_end) load_tiles(chunk_begin);
+  for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
+    if (chunk != chunk_begin) __syncthreads();
+    store_tiles(chunk);
+    __syncthreads();
+    if (chunk + 1 < chunk_end) load_tiles(chunk + 1);
+#pragma unroll 4
+    for (int ks = 0; ks < P / 16; ++ks) {
+      const int p = ks * 16 + hi * 8;  // first of this lane's 8 pixels (one row)
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&gs[goff + p]);
+      const int xb = xoff + (img * HR + row) * RSX + col;
+      const u32x4 cur = *reinterpret_cast<const u32x4*>(&xs[xb]);
+      const uint32_t prev = *reinterpret_cast<const uint32_t*>(&xs[xb - 2]);
+      const uint32_t next = *reinterpret_cast<const uint32_t*>(&xs[xb + 8]);
+      u32x4 left, right;  // columns col-1 .. col+6 and col+1 .. col+8
+      left.x = __builtin_amdgcn_alignbit(cur.x, prev, 16);
+      left.y = __builtin_amdgcn_alignbit(cur.y, cur.x, 16);
+      left.z = __builtin_amdgcn_alignbit(cur.z, cur.y, 16);
+      left.w = __builtin_amdgcn_alignbit(cur.w, cur.z, 16);
+      right.x = left.y;
+      right.y = left.z;
+      right.z = left.w;
+      right.w = __builtin_amdgcn_alignbit(next, cur.w, 16);
+      acc[0] = mfma_32x32x16_bf16(a, left, acc[0]);
+      acc[1] = mfma_32x32x16_bf16(a, cur, acc[1]);
+      acc[2] = mfma_32x32x16_bf16(a, right, acc[2]);
+    }
+    if (do_db && tid < 256) {
+      const int kl = tid >> 2, part = tid & 3;
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i) dbsum += bf16_to_f32(gs[kl * GSB + part + 4 * i]);
+    }
+  }
+
+  const int c = c0 + cb * 32 + l32;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int t = r * 3 + s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = k0 + kb * 32 + acc_row(v, hi);
+      if (k < K && c < C) {
+        if (slice_stride)
+          out[(long)slice * slice_stride + ((long)t * K + k) * C + c] = acc[s][v];
+        else
+          out[((long)k * C + c) * 9 + t] = acc[s][v];
+      }
+    }
+  }
+  if (do_db && tid < 256) {
+    dbsum += __shfl_xor(dbsum, 1);
+    dbsum += __shfl_xor(dbsum, 2);
+    const int kl = tid >> 2;
+    if ((tid & 3) == 0 && k0 + kl < K) out_db[(long)slice * K + k0 + kl] = dbsum;
+  }
 }
+
+template <int TW, int TH, int IMGS>
+static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g,
+                                   float* out, float* out_db, long slice_stride, int N, int C,
+                                   int K, int H, int W, hipStream_t stream) {
+  dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z), block(pl.threads, 1, 1);
+  if (vec)
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
+                       out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
+                       pl.chunks_per_split, slice_stride);
+  else
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
+                       out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
+                       pl.chunks_per_split, slice_stride);
+}
+
+bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
+                       float* db, float* ws, int N, int C, int K, int H, int W,
+                       hipStream_t stream) {
+  if (pl.threads != 768) return false;
+  const long n_dw = (long)K * C * 9;
+  float* out = pl.split > 1 ? ws : dw;
+  float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
+  const long stride = pl.split > 1 ? n_dw : 0;
+  switch (pl.geom) {
+    case kG64x2: launch_wgrad_bf16_geom<64, 2, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
+    case kG32x4: launch_wgrad_bf16_geom<32, 4, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
+    case kG16x8: launch_wgrad_bf16_geom<16, 8, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
+    case kG8x16: launch_wgrad_bf16_geom<8, 16, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
+    case kG8x8x2: launch_wgrad_bf16_geom<8, 8, 2>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
+    default: return false;
+  }
+  if (pl.split > 1) launch_wgrad_reduce(ws, dw, db, pl.split, C, K, stream);
+  return true;
+}
+
+}  // namespace conv3x3

@@ -330,6 +330,7 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const fl
 bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
                       float* db, float* ws, int N, int C, int K, int H, int W,
                       hipStream_t stream) {
+  if (pl.threads != 768) return false;
   const long n_dw = (long)K * C * 9;
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
@@ -341,12 +342,15 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, 
     case kG8x8: launch_wgrad_geom<8, 8, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
     default: return false;
   }
-  if (pl.split > 1) {
-    const long total = n_dw + (db ? K : 0);
-    dim3 grid((unsigned)((total + 63) / 64)), block(256);
-    hipLaunchKernelGGL(wgrad_reduce_kernel, grid, block, 0, stream, ws, dw, db, pl.split, C, K);
-  }
+  if (pl.split > 1) launch_wgrad_reduce(ws, dw, db, pl.split, C, K, stream);
   return true;
+}
+
+void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C, int K,
+                         hipStream_t stream) {
+  const long total = (long)K * C * 9 + (db ? K : 0);
+  dim3 grid((unsigned)((total + 63) / 64)), block(256);
+  hipLaunchKernelGGL(wgrad_reduce_kernel, grid, block, 0, stream, ws, dw, db, split, C, K);
 }
 
 }  // namespace conv3x3

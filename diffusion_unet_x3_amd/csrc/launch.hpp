@@ -23,6 +23,10 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16
 bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
                       float* db, float* ws, int N, int C, int K, int H, int W, hipStream_t stream);
 
+// Fixed-order sum of the split-K partial slots (both dtypes).
+void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C, int K,
+                         hipStream_t stream);
+
 // Same, bfloat16 inputs.
 bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
                        float* db, float* ws, int N, int C, int K, int H, int W,

@@ -52,8 +52,12 @@ CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw + 8; }
 CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {  // in 16-byte words
   return imgs * (th + 2) * fwd_bf16_rs(tw);
 }
-CONV3X3_HD constexpr int fwd_bf16_lds_bytes(int cb, int imgs, int th, int tw, int co_tile) {
-  return 16 * (cb / 8) * fwd_bf16_plane(imgs, th, tw) + 2 * 9 * cb * co_tile;
+// Backward-data adds a raw copy of the weight rows (cb x co_tile x 9 bf16)
+// that is transposed LDS-to-LDS into the w tile.
+CONV3X3_HD constexpr int fwd_bf16_lds_bytes(int cb, int imgs, int th, int tw, int co_tile,
+                                            bool bwd_data) {
+  return 16 * (cb / 8) * fwd_bf16_plane(imgs, th, tw) + 2 * 9 * cb * co_tile +
+         (bwd_data ? 2 * 9 * cb * co_tile : 0);
 }
 
 // ---- backward-weight, float32 ----
@@ -67,8 +71,20 @@ CONV3X3_HD constexpr int wgrad_f32_lds_bytes(int imgs, int th, int tw) {
 }
 
 // ---- backward-weight, bfloat16 ----
+// g tile : [64 k][P + 8] bf16 (row stride 2P + 16 bytes: eight lanes reading
+//          eight k rows at one pixel hit eight different 16-byte bank groups).
+// x tile : [64 c][PLX] bf16, PLX = imgs * (th + 2) * (tw + 16) rounded up to
+//          8 mod 64 (a plane is 16 mod 128 bytes, for the same reason); image
+//          column cc in [-1, tw] sits at row offset 8 + cc, so 8-pixel runs
+//          starting at a multiple-of-8 column are 16-byte aligned.
+CONV3X3_HD constexpr int wgrad_bf16_gstride(int imgs, int th, int tw) { return imgs * th * tw + 8; }
+CONV3X3_HD constexpr int wgrad_bf16_rs(int tw) { return tw + 16; }
+CONV3X3_HD constexpr int wgrad_bf16_plane(int imgs, int th, int tw) {
+  return imgs * (th + 2) * wgrad_bf16_rs(tw) +
+         ((8 - (imgs * (th + 2) * wgrad_bf16_rs(tw)) % 64) + 64) % 64;
+}
 CONV3X3_HD constexpr int wgrad_bf16_lds_bytes(int imgs, int th, int tw) {
-  return 2 * 64 * (imgs * th * tw + 8) + 2 * 64 * (imgs * (th + 2) * (tw + 16));
+  return 2 * 64 * (wgrad_bf16_gstride(imgs, th, tw) + wgrad_bf16_plane(imgs, th, tw));
 }
 
 }  // namespace conv3x3

@@ -55,7 +55,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.tile_co = cout > 64 ? 128 : 64;
     // Channels per LDS fill: 16 with 64-channel tiles, 8 with 128-channel
     // tiles, so every fill holds the same 144 MFMA steps per wave.
-    pl.chunk = p.dtype == kF32 ? (pl.tile_co == 64 ? 16 : 8) : 32;
+    pl.chunk = p.dtype == kF32 ? (pl.tile_co == 64 ? 16 : 8) : 16;
     pl.tiles_w = ceil_div(p.W, pl.tw);
     pl.tiles_h = ceil_div(p.H, pl.th);
     pl.tiles_n = ceil_div(p.N, pl.imgs);
@@ -65,10 +65,12 @@ bool plan(const Problem& p, Plan* out) {
     pl.threads = 256;
     pl.lds_bytes = p.dtype == kF32
         ? fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
-        : fwd_bf16_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co);
+        : fwd_bf16_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co, p.pass == kBwdData);
     pl.split = 1;
   } else if (p.pass == kBwdWeight) {
-    pl.geom = wgrad_geom(p.W);
+    // float32: 64-pixel chunks (32 MFMA steps); bfloat16: 128-pixel chunks
+    // (8 MFMA steps of 16 pixels).
+    pl.geom = p.dtype == kF32 ? wgrad_geom(p.W) : fwd_geom(p.H, p.W);
     GeomDims d = geom_dims(pl.geom);
     pl.tw = d.tw;
     pl.th = d.th;
@@ -89,7 +91,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.grid_x = pl.split;
     pl.grid_y = ceil_div(p.C, pl.tile_ci);
     pl.grid_z = ceil_div(p.K, pl.tile_co);
-    pl.threads = p.dtype == kF32 ? 768 : 256;
+    pl.threads = 768;
     pl.lds_bytes = p.dtype == kF32
         ? wgrad_f32_lds_bytes(pl.imgs, pl.th, pl.tw)
         : wgrad_bf16_lds_bytes(pl.imgs, pl.th, pl.tw);
