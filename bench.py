@@ -135,12 +135,15 @@ def cpu_baseline(layer, budget_s=15.0):
                       f"({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); cpu: {platform.processor() or platform.machine()}"}
 
 
-def sweep(out_path, steps, warmup):
+def sweep(out_path, steps, warmup, match=None):
+    import re
     import torch
     import workloads as wl
     rows = []
     for cfg, layers in sorted(wl.CONFIGS.items()):
         for layer in layers:
+            if match and not re.search(match, layer.name):
+                continue
             run = LayerRun(layer)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
@@ -168,6 +171,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", metavar="OUT_JSON", help="also time every configured layer")
+    ap.add_argument("--sweep-match", metavar="REGEX", help="only sweep layers whose name matches")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0, metavar="MB",
+                    help="also run a plain device-to-device copy of MB megabytes (a known "
+                         "amount of HBM traffic for scaling profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -203,8 +210,17 @@ def main():
     }
     del run
     torch.cuda.empty_cache()
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
     if args.sweep:
-        sweep(args.sweep, max(5, args.steps // 5), 3)
+        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -64,7 +64,7 @@ int conv3x3_plan(int pass, int N, int C, int K, int H, int W, int dtype, conv3x3
   if (!plan(Problem{pass, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_PASS;
   out->pass = pl.pass;
   out->dtype = pl.dtype;
-  out->kernel = pl.geom;
+  out->kernel = pl.wave_co;
   out->tile_m = pl.tile_co;
   out->tile_n = pass == CONV3X3_PASS_BWD_WEIGHT ? pl.tile_ci : pl.imgs * pl.th * pl.tw;
   out->tile_imgs = pl.imgs;

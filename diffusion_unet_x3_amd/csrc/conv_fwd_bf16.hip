@@ -8,20 +8,29 @@
 // lanes 0-31 supply channels 0-7 and lanes 32-63 channels 8-15 of a
 // 16-channel LDS fill.  To make the pixel operand a single 128-bit LDS read,
 // the x tile is stored channel-interleaved: one 16-byte LDS word holds 8
-// channels of one pixel ([group][img][row][col] words).  It is built from
-// 128-bit NCHW loads (8 pixels of one channel) by a 4-channel x 8-pixel
-// transpose in registers; no global memory is ever transposed.
+// channels of one pixel ([group][img][row][col] words).  Eight lanes load
+// 8 pixels of 8 different channels with 128-bit NCHW loads and transpose the
+// 8 x 8 block among themselves with three butterfly exchanges; each lane then
+// stores one whole word and neighbouring lanes store neighbouring words, so
+// the stores are free of bank conflicts.  No global memory is transposed.
 //
 // Weights, as one 16-byte word per (tap, 8-channel group, output channel):
-//   forward       : w[co, c0 + 8g .. + 7, 0..8] is 144 contiguous bytes, loaded
-//                   with nine 128-bit loads and rearranged in registers;
-//   backward-data : the reduction channel is k, the slowest axis of w, so the
-//                   raw rows w[k, co0.., 0..8] are first copied to LDS and then
-//                   transposed LDS-to-LDS in 8 x 8 blocks, with the 180-degree
-//                   tap rotation applied in the store index.
+// the raw weight rows are first copied to LDS with coalesced 128-bit loads
+// (into the space of the x tile, which is refilled afterwards), then
+// rearranged LDS-to-LDS:
+//   forward       : w[co, c0 .. c0+15, 0..8] is one contiguous 288-byte run;
+//                   each 8-channel half is rearranged in registers into nine
+//                   tap words;
+//   backward-data : the reduction channel is k, the slowest axis of w; the
+//                   rows w[k, co0.., 0..8] are transposed in 8 x 8 blocks, with
+//                   the 180-degree tap rotation applied in the store index.
+//
+// Workgroup: 4 wave64s; WCO waves split the BCO output channels and 4 / WCO
+// the pixel block; each wave holds MI x NJ 32x32 accumulators.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
+#include "tile_configs.hpp"
 
 namespace conv3x3 {
 
@@ -40,184 +49,234 @@ __device__ __forceinline__ uint32_t elem(const uint32_t* d) {
   return (E & 1) ? (d[E >> 1] >> 16) : (d[E >> 1] & 0xffffu);
 }
 
+// 8 x 8 transpose of 16-bit elements held by 8 consecutive lanes: on entry
+// lane i (i = lane % 8) holds row i (elements 0..7 in d), on exit column i.
+// Three stages swap the off-diagonal blocks of size 4, 2 and 1.
+__device__ __forceinline__ u32x4 transpose8x8(u32x4 d, int i) {
+  {
+    const bool b = i & 4;
+    const uint32_t s0 = b ? d.x : d.z, s1 = b ? d.y : d.w;
+    const uint32_t r0 = __shfl_xor(s0, 4), r1 = __shfl_xor(s1, 4);
+    if (b) {
+      d.x = r0;
+      d.y = r1;
+    } else {
+      d.z = r0;
+      d.w = r1;
+    }
+  }
+  {
+    const bool b = i & 2;
+    const uint32_t s0 = b ? d.x : d.y, s1 = b ? d.z : d.w;
+    const uint32_t r0 = __shfl_xor(s0, 2), r1 = __shfl_xor(s1, 2);
+    if (b) {
+      d.x = r0;
+      d.z = r1;
+    } else {
+      d.y = r0;
+      d.w = r1;
+    }
+  }
+  {
+    const bool b = i & 1;
+    const uint32_t s0 = b ? pack_lo(d.x, d.y) : pack_hi(d.x, d.y);
+    const uint32_t s1 = b ? pack_lo(d.z, d.w) : pack_hi(d.z, d.w);
+    const uint32_t r0 = __shfl_xor(s0, 1), r1 = __shfl_xor(s1, 1);
+    if (b) {
+      d.x = (d.x & 0xffff0000u) | (r0 & 0xffffu);
+      d.y = (d.y & 0xffff0000u) | (r0 >> 16);
+      d.z = (d.z & 0xffff0000u) | (r1 & 0xffffu);
+      d.w = (d.w & 0xffff0000u) | (r1 >> 16);
+    } else {
+      d.x = (d.x & 0xffffu) | (r0 << 16);
+      d.y = (d.y & 0xffffu) | (r0 & 0xffff0000u);
+      d.z = (d.z & 0xffffu) | (r1 << 16);
+      d.w = (d.w & 0xffffu) | (r1 & 0xffff0000u);
+    }
+  }
+  return d;
+}
+
 }  // namespace
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, bool VEC>
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, bool VEC>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ wt,
     const float* __restrict__ bias, float* __restrict__ dst, int N, int Cin, int Cout, int H,
     int W, int tiles_w, int tiles_h) {
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
-  static_assert(BM == 128, "pixel block must hold 128 pixels");
+  constexpr int WPX = 4 / WCO;
+  constexpr int MI = BCO / (32 * WCO);
+  constexpr int NJ = BM / (32 * WPX);
+  static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
+                "tile does not split into 32x32 wave tiles");
   constexpr int RS = fwd_bf16_rs(TW);
   constexpr int HR = TH + 2;
   constexpr int PLW = fwd_bf16_plane(IMGS, TH, TW);  // words per 8-channel plane
-  constexpr int MI = BCO / 64;
-  constexpr int NJ = BM / 64;
-  constexpr int EW = BCO * 9 / 8;  // raw weight words per reduction channel (backward-data)
+  constexpr int EW = BCO * 9 / 8;                    // raw weight words per reduction channel
+  constexpr int XWORDS = fwd_bf16_xregion_words(IMGS, TH, TW, BCO, VEC);
 
-  __shared__ u32x4 xs[2 * PLW];
+  __shared__ u32x4 xs[XWORDS];  // x tile; also the raw weight rows while they are staged
   __shared__ u32x4 wa[9 * 2 * BCO];
-  __shared__ u32x4 wraw[MODE == kBwdData && VEC ? CB * EW : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int wco = wave & 1, wpx = wave >> 1;
+  const int wco = wave % WCO, wpx = wave / WCO;
   const BlockOrigin o = block_origin<TW, TH, IMGS>(blockIdx.x, tiles_w, tiles_h);
   const int co0 = blockIdx.y * BCO;
   const long HW = (long)H * W;
 
-  // ---- vector staging (W % 8 == 0, channel counts % 8 == 0, 16-byte bases) ----
-  // x: item (c4, img, rr, q8) = 4 channels x 8 pixels.
-  constexpr int XI = 4 * IMGS * HR * (TW / 8);
-  constexpr int XH = 4 * IMGS * HR * 2;  // halo items: 4 channels x 1 pixel
-  static_assert(XI <= 256 && XH <= 256, "one x item per thread");
-  // weights: forward item (co_l, g) = 9 words; backward-data raw item = 1 word.
-  constexpr int WI = MODE == kFwd ? 2 * BCO : CB * EW;
-  constexpr int WN = MODE == kFwd ? 1 : (WI + 255) / 256;
-  constexpr int WR = MODE == kFwd ? 9 : WN;
-  u32x4 xr[4];
-  uint32_t hr[2];
-  u32x4 wr[WR];
+  // ---- vector staging (W % 8 == 0, weight channel counts % 8 == 0, 16-byte bases) ----
+  // x: item (ch, q, rr, img), ch fastest: 8 pixels of one channel.  Items
+  // come in groups of 16 = two 8-lane transpose groups, so a transpose group
+  // is always wholly inside or wholly outside the item range.
+  constexpr int XI = CB * IMGS * HR * (TW / 8);
+  constexpr int XN = (XI + 255) / 256;
+  constexpr int XH = 2 * IMGS * HR * 2;  // halo items: 8 channels x 1 pixel
+  static_assert(XH <= 256, "one halo item per thread");
+  // weights: one raw 16-byte word per item (forward: BCO runs of 18 words,
+  // backward-data: CB rows of EW words).
+  constexpr int WI = CB * EW;
+  constexpr int WN = (WI + 255) / 256;
+  constexpr int WR = WN;
+  u32x4 xr[VEC ? XN : 1];
+  u32x4 hr;
+  u32x4 wr[VEC ? WR : 1];
 
   auto load_tiles = [&](int c0) {
     if constexpr (VEC) {
-      {
-        const int it = tid;
-        if (it < XI) {
-          const int q = it % (TW / 8);
-          int t = it / (TW / 8);
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int c4 = t / IMGS;
-          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
-          const bool ok = n < N && h >= 0 && h < H && w < W;
+      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = c0 + 4 * c4 + i;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (ok && c < Cin)
-              v = *reinterpret_cast<const u32x4*>(src + ((long)n * Cin + c) * HW + (long)h * W + w);
-            xr[i] = v;
-          }
-        }
+      for (int k = 0; k < XN; ++k) {
+        const int it = tid + 256 * k;
+        const int ch = it & 15;
+        int t = it >> 4;
+        const int q = t % (TW / 8);
+        t /= TW / 8;
+        const int rr = t % HR;
+        const int img = t / HR;
+        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q, c = c0 + ch;
+        const bool ok = (XI % 256 == 0 || it < XI) && n < N && c < Cin && h >= 0 && h < H && w < W;
+        const long idx = ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + idx);
+        xr[k] = ok ? v : z;
       }
-      {
-        const int it = tid;
-        hr[0] = hr[1] = 0u;
-        if (it < XH) {
-          const int side = it & 1;
-          int t = it >> 1;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int c4 = t / IMGS;
-          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + (side ? TW : -1);
-          if (n < N && h >= 0 && h < H && w >= 0 && w < W) {
-            uint32_t v[4];
+      hr = z;
+      if (tid < XH) {
+        const int side = tid & 1;
+        int t = tid >> 1;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int g = t / IMGS;
+        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + (side ? TW : -1);
+        if (n < N && h >= 0 && h < H && w >= 0 && w < W) {
+          uint32_t v[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int c = c0 + 4 * c4 + i;
-              v[i] = c < Cin ? src[((long)n * Cin + c) * HW + (long)h * W + w] : 0u;
-            }
-            hr[0] = v[0] | (v[1] << 16);
-            hr[1] = v[2] | (v[3] << 16);
+          for (int i = 0; i < 8; ++i) {
+            const int c = c0 + 8 * g + i;
+            v[i] = c < Cin ? src[((long)n * Cin + c) * HW + (long)h * W + w] : 0u;
           }
+          hr.x = v[0] | (v[1] << 16);
+          hr.y = v[2] | (v[3] << 16);
+          hr.z = v[4] | (v[5] << 16);
+          hr.w = v[6] | (v[7] << 16);
         }
       }
       if constexpr (MODE == kFwd) {
-        const int co_l = tid >> 1, gq = tid & 1;
-        const int co = co0 + co_l;
-        const bool ok = tid < WI && co < Cout && c0 + 8 * gq < Cin;
-        const uint16_t* p = wt + ((long)co * Cin + c0 + 8 * gq) * 9;
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (ok) v = reinterpret_cast<const u32x4*>(p)[i];
-          wr[i] = v;
+        for (int k = 0; k < WN; ++k) {
+          const int it = tid + 256 * k;
+          const int run = it / 18, piece = it % 18;  // 18 words per output channel
+          const int co = co0 + run;
+          const bool ok = (WI % 256 == 0 || it < WI) && co < Cout && 8 * piece < (Cin - c0) * 9;
+          const long idx = ok ? ((long)co * Cin + c0) * 9 + 8 * piece : 0;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(wt + idx);
+          wr[k] = ok ? v : z;
         }
       } else {
 #pragma unroll
         for (int k = 0; k < WN; ++k) {
           const int it = tid + 256 * k;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (WI % 256 == 0 || it < WI) {
-            const int kl = it / EW, e8 = it % EW;
-            if (c0 + kl < Cin && 8 * e8 < (Cout - co0) * 9)
-              v = *reinterpret_cast<const u32x4*>(wt + ((long)(c0 + kl) * Cout + co0) * 9 + 8 * e8);
-          }
-          wr[k] = v;
+          const int kl = it / EW, e8 = it % EW;
+          const bool ok = (WI % 256 == 0 || it < WI) && c0 + kl < Cin && 8 * e8 < (Cout - co0) * 9;
+          const long idx = ok ? ((long)(c0 + kl) * Cout + co0) * 9 + 8 * e8 : 0;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(wt + idx);
+          wr[k] = ok ? v : z;
         }
       }
     }
   };
 
+  auto store_x = [&]() {
+#pragma unroll
+    for (int k = 0; k < XN; ++k) {
+      const int it = tid + 256 * k;
+      const u32x4 v = transpose8x8(xr[k], lane & 7);  // all lanes take part
+      if (XI % 256 == 0 || it < XI) {
+        const int ch = it & 15;
+        int t = it >> 4;
+        const int q = t % (TW / 8);
+        t /= TW / 8;  // img * HR + rr
+        xs[(ch >> 3) * PLW + t * RS + 4 + 8 * q + (ch & 7)] = v;
+      }
+    }
+    if (tid < XH) {
+      const int side = tid & 1;
+      const int t = tid >> 1;  // (g * IMGS + img) * HR + rr
+      const int g = t / (IMGS * HR);
+      xs[g * PLW + (t % (IMGS * HR)) * RS + 4 + (side ? TW : -1)] = hr;
+    }
+  };
+
   auto store_tiles = [&](int c0) {
     if constexpr (VEC) {
-      if (tid < XI) {
-        const int q = tid % (TW / 8);
-        const int t = tid / (TW / 8);  // (c4 * IMGS + img) * HR + rr
-        const int c4 = t / (IMGS * HR);
-        const int row = t % (IMGS * HR);
-        uint2* d = reinterpret_cast<uint2*>(&xs[(c4 >> 1) * PLW + row * RS + 4 + 8 * q]) + (c4 & 1);
+      // Raw weight words into the x region, rearranged into wa, then the x tile.
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int dw = p >> 1;
-          uint2 v;
-          if (p & 1) {
-            v.x = pack_hi(xr[0][dw], xr[1][dw]);
-            v.y = pack_hi(xr[2][dw], xr[3][dw]);
-          } else {
-            v.x = pack_lo(xr[0][dw], xr[1][dw]);
-            v.y = pack_lo(xr[2][dw], xr[3][dw]);
-          }
-          d[2 * p] = v;  // word stride is two uint2
-        }
+      for (int k = 0; k < WN; ++k) {
+        const int it = tid + 256 * k;
+        if (WI % 256 == 0 || it < WI) xs[it] = wr[k];
       }
-      if (tid < XH) {
-        const int side = tid & 1;
-        const int t = tid >> 1;
-        const int c4 = t / (IMGS * HR);
-        const int row = t % (IMGS * HR);
-        uint2* d = reinterpret_cast<uint2*>(&xs[(c4 >> 1) * PLW + row * RS + 4 + (side ? TW : -1)]) +
-                   (c4 & 1);
-        *d = make_uint2(hr[0], hr[1]);
-      }
+      __syncthreads();
       if constexpr (MODE == kFwd) {
-        if (tid < WI) {
-          const int co_l = tid >> 1, gq = tid & 1;
-          const uint32_t* d = reinterpret_cast<const uint32_t*>(wr);  // 36 dwords, e = ci * 9 + t
-          // word for tap t: channels (2q, 2q+1) -> elements 2q*9+t and (2q+1)*9+t
-#define CONV3X3_WWORD(T)                                                                   \
-  {                                                                                       \
-    u32x4 v;                                                                              \
-    v.x = elem<0 * 9 + T>(d) | (elem<1 * 9 + T>(d) << 16);                                \
-    v.y = elem<2 * 9 + T>(d) | (elem<3 * 9 + T>(d) << 16);                                \
-    v.z = elem<4 * 9 + T>(d) | (elem<5 * 9 + T>(d) << 16);                                \
-    v.w = elem<6 * 9 + T>(d) | (elem<7 * 9 + T>(d) << 16);                                \
-    wa[((T) * 2 + gq) * BCO + co_l] = v;                                                  \
-  }
-          CONV3X3_WWORD(0)
-          CONV3X3_WWORD(1)
-          CONV3X3_WWORD(2)
-          CONV3X3_WWORD(3)
-          CONV3X3_WWORD(4)
-          CONV3X3_WWORD(5)
-          CONV3X3_WWORD(6)
-          CONV3X3_WWORD(7)
-          CONV3X3_WWORD(8)
-#undef CONV3X3_WWORD
-        }
-      } else {
+        // Item (co_l, gq), gq fastest: words 9 * it .. 9 * it + 8 hold
+        // w[co0 + co_l, c0 + 8 gq .. + 7, 0..8] as e = ci * 9 + t.
 #pragma unroll
-        for (int k = 0; k < WN; ++k) {
+        for (int k = 0; k < (2 * BCO + 255) / 256; ++k) {
           const int it = tid + 256 * k;
-          if (WI % 256 == 0 || it < WI) wraw[it] = wr[k];
+          if ((2 * BCO) % 256 == 0 || it < 2 * BCO) {
+            const int co_l = it >> 1, gq = it & 1;
+            u32x4 raw[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) raw[i] = xs[9 * it + i];
+            const uint32_t* d = reinterpret_cast<const uint32_t*>(raw);
+            // word for tap t: channels (2q, 2q+1) -> elements 2q*9+t and (2q+1)*9+t
+#define CONV3X3_WWORD(T)                                                   \
+  {                                                                       \
+    u32x4 v;                                                              \
+    v.x = elem<0 * 9 + T>(d) | (elem<1 * 9 + T>(d) << 16);                \
+    v.y = elem<2 * 9 + T>(d) | (elem<3 * 9 + T>(d) << 16);                \
+    v.z = elem<4 * 9 + T>(d) | (elem<5 * 9 + T>(d) << 16);                \
+    v.w = elem<6 * 9 + T>(d) | (elem<7 * 9 + T>(d) << 16);                \
+    wa[((T) * 2 + gq) * BCO + co_l] = v;                                  \
+  }
+            CONV3X3_WWORD(0)
+            CONV3X3_WWORD(1)
+            CONV3X3_WWORD(2)
+            CONV3X3_WWORD(3)
+            CONV3X3_WWORD(4)
+            CONV3X3_WWORD(5)
+            CONV3X3_WWORD(6)
+            CONV3X3_WWORD(7)
+            CONV3X3_WWORD(8)
+#undef CONV3X3_WWORD
+          }
         }
         __syncthreads();
+        store_x();
+      } else {
         // 8 x 8 transpose: 8 reduction channels (k) x 8 consecutive (co, tap)
         // elements of the raw rows -> 8 words of 8 k each.
         constexpr int TI = 2 * EW;
@@ -228,7 +287,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
             const int g = it / EW, eb = it % EW;
             u32x4 in[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) in[j] = wraw[(8 * g + j) * EW + eb];
+            for (int j = 0; j < 8; ++j) in[j] = xs[(8 * g + j) * EW + eb];
 #pragma unroll
             for (int ei = 0; ei < 8; ++ei) {
               const int dw = ei >> 1;
@@ -249,6 +308,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
             }
           }
         }
+        __syncthreads();
+        store_x();
       }
     } else {
       // Scalar path (ragged shapes): 16-bit loads straight into LDS.
@@ -301,11 +362,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   int boff[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int p = wpx * (BM / 2) + j * 32 + l32;
+    const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     boff[j] = hi * PLW + (img * HR + row) * RS + 4 + col - 1;
   }
-  const int aoff = hi * BCO + wco * (BCO / 2) + l32;
+  const int aoff = hi * BCO + wco * (BCO / WCO) + l32;
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -315,6 +376,15 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  u32x4 a[2][MI], b[2][NJ];
+  auto read_tap = [&](int buf, int t) {
+    const int r = t / 3, s = t % 3;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[buf][i] = wa[aoff + t * 2 * BCO + i * 32];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + r * RS + s];
+  };
+
   const int nchunks = (Cin + CB - 1) / CB;
   load_tiles(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
@@ -322,26 +392,24 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     store_tiles(chunk * CB);
     __syncthreads();
     if (chunk + 1 < nchunks) load_tiles((chunk + 1) * CB);
+    // Tap t's operands are read while tap t-1's MFMAs run.
+    read_tap(0, 0);
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
+    for (int t = 0; t < 9; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < 9) read_tap(cur ^ 1, t + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        u32x4 a[MI], b[NJ];
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int i = 0; i < MI; ++i) a[i] = wa[aoff + (r * 3 + s) * 2 * BCO + i * 32];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) b[j] = xs[boff[j] + r * RS + s];
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16_bf16(a[i], b[j], acc[i][j]);
-      }
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = mfma_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j]);
     }
   }
 
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int p = wpx * (BM / 2) + j * 32 + l32;
+    const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
     if (n >= N || h >= H || w >= W) continue;
@@ -350,7 +418,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int co = co0 + wco * (BCO / 2) + i * 32 + acc_row(v, hi);
+        const int co = co0 + wco * (BCO / WCO) + i * 32 + acc_row(v, hi);
         if (co < Cout) {
           float val = acc[i][j][v];
           if (MODE == kFwd && bias) val += bias[co];
@@ -361,48 +429,36 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   }
 }
 
-template <int MODE, int TW, int TH, int IMGS, int BCO>
-static void launch_bf16_geom(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
-                             const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                             hipStream_t stream) {
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
+static void launch_bf16_cfg(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
+                            const float* bias, float* dst, int N, int Cin, int Cout, int H,
+                            int W, hipStream_t stream) {
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
   if (vec)
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, true>), grid, block, 0, stream,
-                       src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, true>), grid, block, 0,
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, false>), grid, block, 0, stream,
-                       src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
-}
-
-template <int MODE, int BCO>
-static bool launch_bf16_bco(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
-                            const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                            hipStream_t s) {
-  switch (pl.geom) {
-    case kG64x2: launch_bf16_geom<MODE, 64, 2, 1, BCO>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG32x4: launch_bf16_geom<MODE, 32, 4, 1, BCO>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG16x8: launch_bf16_geom<MODE, 16, 8, 1, BCO>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG8x16: launch_bf16_geom<MODE, 8, 16, 1, BCO>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG8x8x2: launch_bf16_geom<MODE, 8, 8, 2, BCO>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    default: return false;
-  }
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, false>), grid, block, 0,
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
 }
 
 bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
                      const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
                      hipStream_t stream) {
   if (pl.chunk != 16) return false;
-  if (pl.pass == kFwd) {
-    if (pl.tile_co == 128)
-      return launch_bf16_bco<kFwd, 128>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, stream);
-    if (pl.tile_co == 64)
-      return launch_bf16_bco<kFwd, 64>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, stream);
-  } else {
-    if (pl.tile_co == 128)
-      return launch_bf16_bco<kBwdData, 128>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, stream);
-    if (pl.tile_co == 64)
-      return launch_bf16_bco<kBwdData, 64>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, stream);
+#define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                                 \
+  if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                \
+      pl.wave_co == WCO_) {                                                                   \
+    if (pl.pass == kFwd)                                                                      \
+      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin,  \
+                                                        Cout, H, W, stream);                  \
+    else                                                                                      \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, nullptr, dst, N, \
+                                                            Cin, Cout, H, W, stream);         \
+    return true;                                                                              \
   }
+  CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)
+#undef CONV3X3_X
   return false;
 }
 

@@ -9,32 +9,38 @@
 //                   rotation happen in the LDS staging index, never in memory.
 //
 // Workgroup: 256 threads (4 wave64s) own BCO output channels x a pixel block
-// of IMGS x TH x TW pixels (128).  Waves split it 2 (channels) x 2 (pixels);
-// each wave accumulates (BCO/2) x 64 outputs in 32x32 MFMA tiles.  Per LDS
-// fill the block stages CB input channels of the source with their one-pixel
-// halo (zero where the halo leaves the image) and the matching CB x 9 x BCO
+// of IMGS x TH x TW pixels.  WCO waves split the channels and 4 / WCO the
+// pixels; each wave accumulates MI x NJ 32x32 MFMA tiles.  Per LDS fill the
+// block stages CB input channels of the source with their one-pixel halo
+// (zero where the halo leaves the image) and the matching CB x 9 x BCO
 // weights; the next fill's global loads are issued before the current fill's
 // MFMAs so that their latency hides behind the math.  MFMA 32x32x2 f32: the
 // two reduction elements of a step are two consecutive input channels at the
-// same tap; lanes 0-31 and 32-63 read them from adjacent LDS planes.
+// same tap; lanes 0-31 and 32-63 read them from adjacent LDS planes.  The
+// operands of step t+1 are read from LDS into a second register set while
+// the MFMAs of step t run.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
+#include "tile_configs.hpp"
 
 namespace conv3x3 {
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int CB, bool VEC>
-__global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h) {
   constexpr int BM = IMGS * TH * TW;
-  static_assert(BM == 128, "pixel block must hold 128 pixels");
+  constexpr int WPX = 4 / WCO;
+  constexpr int MI = BCO / (32 * WCO);  // 32x32 tiles per wave along channels
+  constexpr int NJ = BM / (32 * WPX);   // 32x32 tiles per wave along pixels
+  static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
+                "tile does not split into 32x32 wave tiles");
   constexpr int RS = fwd_f32_rs(TW);
   constexpr int PL = fwd_f32_plane(IMGS, TH, TW);
   constexpr int WS = fwd_f32_wstride(BCO);
-  constexpr int MI = BCO / 64;  // 32x32 tiles per wave along channels
-  constexpr int NJ = BM / 64;   // 32x32 tiles per wave along pixels
-  constexpr int HR = TH + 2;    // staged rows per image (with halo)
+  constexpr int HR = TH + 2;  // staged rows per image (with halo)
+  constexpr int NSTEP = CB / 2 * 9;
 
   __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
@@ -42,7 +48,7 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int wco = wave & 1, wpx = wave >> 1;
+  const int wco = wave % WCO, wpx = wave / WCO;
   const BlockOrigin o = block_origin<TW, TH, IMGS>(blockIdx.x, tiles_w, tiles_h);
   const int co0 = blockIdx.y * BCO;
   const long HW = (long)H * W;
@@ -76,61 +82,59 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
   // in store_tiles.  Scalar path: everything happens in store_tiles.
   auto load_tiles = [&](int c0) {
     if constexpr (VEC) {
+      // Loads are unconditional: an item outside the tensor reads element 0
+      // and is replaced by zero, so the staging code has no branches.
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
         const int it = tid + k * 256;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (XV_ITEMS % 256 == 0 || it < XV_ITEMS) {
-          const int q = it % XQ;
-          int t = it / XQ;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int ch = t / IMGS;
-          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
-          if (n < N && c < Cin && h >= 0 && h < H && w < W)
-            v = *reinterpret_cast<const f32x4*>(src + ((long)n * Cin + c) * HW + (long)h * W + w);
-        }
-        xv[k] = v;
+        const int q = it % XQ;
+        int t = it / XQ;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int ch = t / IMGS;
+        const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
+        const bool ok = (XV_ITEMS % 256 == 0 || it < XV_ITEMS) && n < N && c < Cin && h >= 0 &&
+                        h < H && w < W;
+        const long idx = ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + idx);
+        xv[k] = ok ? v : z;
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
         const int it = tid + k * 256;
-        float v = 0.f;
-        if (XH_ITEMS % 256 == 0 || it < XH_ITEMS) {
-          const int side = it & 1;
-          int t = it >> 1;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int ch = t / IMGS;
-          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1;
-          const int w = o.w0 + (side ? TW : -1);
-          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
-            v = src[((long)n * Cin + c) * HW + (long)h * W + w];
-        }
-        xf[k] = v;
+        const int side = it & 1;
+        int t = it >> 1;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int ch = t / IMGS;
+        const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1;
+        const int w = o.w0 + (side ? TW : -1);
+        const bool ok = (XH_ITEMS % 256 == 0 || it < XH_ITEMS) && n < N && c < Cin && h >= 0 &&
+                        h < H && w >= 0 && w < W;
+        const float v = src[ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0];
+        xf[k] = ok ? v : 0.f;
       }
-    }
-    if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
         const int it = tid + k * 256;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (WV_ITEMS % 256 == 0 || it < WV_ITEMS) {
-          const int run = it / (RUN / 4);
-          const int e = 4 * (it % (RUN / 4));
-          if constexpr (MODE == kFwd) {
-            const int co = co0 + run;
-            if (co < Cout && e < (Cin - c0) * 9)
-              v = *reinterpret_cast<const f32x4*>(wt + ((long)co * Cin + c0) * 9 + e);
-          } else {
-            const int ci = c0 + run;
-            if (ci < Cin && e < (Cout - co0) * 9)
-              v = *reinterpret_cast<const f32x4*>(wt + ((long)ci * Cout + co0) * 9 + e);
-          }
+        const int run = it / (RUN / 4);
+        const int e = 4 * (it % (RUN / 4));
+        bool ok;
+        long idx;
+        if constexpr (MODE == kFwd) {
+          const int co = co0 + run;
+          ok = (WV_ITEMS % 256 == 0 || it < WV_ITEMS) && co < Cout && e < (Cin - c0) * 9;
+          idx = ((long)co * Cin + c0) * 9 + e;
+        } else {
+          const int ci = c0 + run;
+          ok = (WV_ITEMS % 256 == 0 || it < WV_ITEMS) && ci < Cin && e < (Cout - co0) * 9;
+          idx = ((long)ci * Cout + co0) * 9 + e;
         }
-        wv[k] = v;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(wt + (ok ? idx : 0));
+        wv[k] = ok ? v : z;
       }
     }
   };
@@ -218,11 +222,11 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
   int boff[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int p = wpx * (BM / 2) + j * 32 + l32;
+    const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     boff[j] = hi * PL + (img * HR + row) * RS + 4 + col - 1;
   }
-  const int aoff = hi * 9 * WS + wco * (BCO / 2) + l32;
+  const int aoff = hi * 9 * WS + wco * (BCO / WCO) + l32;
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -232,6 +236,16 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // Operands of one MFMA step st = (cp, r, s), cp the channel pair.
+  float a[2][MI], b[2][NJ];
+  auto read_step = [&](int buf, int st) {
+    const int cp = st / 9, r = (st % 9) / 3, s = st % 3;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + (2 * cp * 9 + r * 3 + s) * WS + i * 32];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
+  };
+
   const int nchunks = (Cin + CB - 1) / CB;
   load_tiles(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
@@ -239,30 +253,26 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
     store_tiles(chunk * CB);
     __syncthreads();
     if (chunk + 1 < nchunks) load_tiles((chunk + 1) * CB);
-#pragma unroll 2
-    for (int cp = 0; cp < CB / 2; ++cp) {
+    read_step(0, 0);
 #pragma unroll
-      for (int r = 0; r < 3; ++r) {
+    for (int st = 0; st < NSTEP; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < NSTEP) read_step(cur ^ 1, st + 1);
+      // Keep the next step's LDS reads ahead of this step's MFMAs (the
+      // scheduler would otherwise sink them next to their use).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          float a[MI], b[NJ];
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int i = 0; i < MI; ++i) a[i] = ws[aoff + (2 * cp * 9 + r * 3 + s) * WS + i * 32];
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) b[j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x2_f32(a[i], b[j], acc[i][j]);
-        }
-      }
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = mfma_32x32x2_f32(a[cur][i], b[cur][j], acc[i][j]);
     }
   }
 
   // ---------------- epilogue: bias + NCHW stores ----------------
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int p = wpx * (BM / 2) + j * 32 + l32;
+    const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
     if (n >= N || h >= H || w >= W) continue;
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int co = co0 + wco * (BCO / 2) + i * 32 + acc_row(v, hi);
+        const int co = co0 + wco * (BCO / WCO) + i * 32 + acc_row(v, hi);
         if (co < Cout) {
           float val = acc[i][j][v];
           if (MODE == kFwd && bias) val += bias[co];
@@ -283,43 +293,36 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Host launcher: dispatch the plan's geometry / tile to an instantiation.
+// Host launcher: dispatch the plan's tile to its instantiation.
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int CB>
-static void launch_geom(const Plan& pl, bool vec, const float* src, const float* wt,
-                        const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                        hipStream_t stream) {
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
+static void launch_cfg(const Plan& pl, bool vec, const float* src, const float* wt,
+                       const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+                       hipStream_t stream) {
+  constexpr int CB = 8;
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
   if (vec)
-    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, CB, true>), grid, block, 0,
+    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, true>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
   else
-    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, CB, false>), grid, block, 0,
+    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, false>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
-}
-
-template <int MODE, int BCO, int CB>
-static bool launch_bco(const Plan& pl, bool vec, const float* src, const float* wt,
-                       const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                       hipStream_t s) {
-  switch (pl.geom) {
-    case kG64x2: launch_geom<MODE, 64, 2, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG32x4: launch_geom<MODE, 32, 4, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG16x8: launch_geom<MODE, 16, 8, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG8x16: launch_geom<MODE, 8, 16, 1, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    case kG8x8x2: launch_geom<MODE, 8, 8, 2, BCO, CB>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s); return true;
-    default: return false;
-  }
 }
 
 template <int MODE>
 static bool launch_mode(const Plan& pl, bool vec, const float* src, const float* wt,
                         const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
                         hipStream_t s) {
-  if (pl.tile_co == 64 && pl.chunk == 16)
-    return launch_bco<MODE, 64, 16>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s);
-  if (pl.tile_co == 128 && pl.chunk == 8)
-    return launch_bco<MODE, 128, 8>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, s);
+  if (pl.chunk != 8) return false;
+#define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                               \
+  if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&              \
+      pl.wave_co == WCO_) {                                                                 \
+    launch_cfg<MODE, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin, Cout, \
+                                                 H, W, s);                                  \
+    return true;                                                                            \
+  }
+  CONV3X3_FWD_F32_CONFIGS(CONV3X3_X)
+#undef CONV3X3_X
   return false;
 }
 

@@ -17,6 +17,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
+#include "tile_configs.hpp"
 
 namespace conv3x3 {
 
@@ -205,33 +206,45 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   const int goff = (kb * 32 + l32) * GSB;
   const int xoff = (cb * 32 + l32) * PLX + r * RSX + 8;
 
+  // Operands of one step: g word, x word, and the x dwords on either side.
+  u32x4 ga[2], xc[2];
+  uint32_t xp[2], xn[2];
+  auto read_step = [&](int buf, int ks) {
+    const int p = ks * 16 + hi * 8;  // first of this lane's 8 pixels (one row)
+    const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+    ga[buf] = *reinterpret_cast<const u32x4*>(&gs[goff + p]);
+    const int xb = xoff + (img * HR + row) * RSX + col;
+    xc[buf] = *reinterpret_cast<const u32x4*>(&xs[xb]);
+    xp[buf] = *reinterpret_cast<const uint32_t*>(&xs[xb - 2]);
+    xn[buf] = *reinterpret_cast<const uint32_t*>(&xs[xb + 8]);
+  };
+
   if (chunk_begin < chunk_end) load_tiles(chunk_begin);
   for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
     if (chunk != chunk_begin) __syncthreads();
     store_tiles(chunk);
     __syncthreads();
     if (chunk + 1 < chunk_end) load_tiles(chunk + 1);
-#pragma unroll 4
+    // Step ks (16 pixels) reads its operands while step ks-1's MFMAs run.
+    read_step(0, 0);
+#pragma unroll
     for (int ks = 0; ks < P / 16; ++ks) {
-      const int p = ks * 16 + hi * 8;  // first of this lane's 8 pixels (one row)
-      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&gs[goff + p]);
-      const int xb = xoff + (img * HR + row) * RSX + col;
-      const u32x4 cur = *reinterpret_cast<const u32x4*>(&xs[xb]);
-      const uint32_t prev = *reinterpret_cast<const uint32_t*>(&xs[xb - 2]);
-      const uint32_t next = *reinterpret_cast<const uint32_t*>(&xs[xb + 8]);
+      const int cb_ = ks & 1;
+      if (ks + 1 < P / 16) read_step(cb_ ^ 1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 c = xc[cb_];
       u32x4 left, right;  // columns col-1 .. col+6 and col+1 .. col+8
-      left.x = __builtin_amdgcn_alignbit(cur.x, prev, 16);
-      left.y = __builtin_amdgcn_alignbit(cur.y, cur.x, 16);
-      left.z = __builtin_amdgcn_alignbit(cur.z, cur.y, 16);
-      left.w = __builtin_amdgcn_alignbit(cur.w, cur.z, 16);
+      left.x = __builtin_amdgcn_alignbit(c.x, xp[cb_], 16);
+      left.y = __builtin_amdgcn_alignbit(c.y, c.x, 16);
+      left.z = __builtin_amdgcn_alignbit(c.z, c.y, 16);
+      left.w = __builtin_amdgcn_alignbit(c.w, c.z, 16);
       right.x = left.y;
       right.y = left.z;
       right.z = left.w;
-      right.w = __builtin_amdgcn_alignbit(next, cur.w, 16);
-      acc[0] = mfma_32x32x16_bf16(a, left, acc[0]);
-      acc[1] = mfma_32x32x16_bf16(a, cur, acc[1]);
-      acc[2] = mfma_32x32x16_bf16(a, right, acc[2]);
+      right.w = __builtin_amdgcn_alignbit(xn[cb_], c.w, 16);
+      acc[0] = mfma_32x32x16_bf16(ga[cb_], left, acc[0]);
+      acc[1] = mfma_32x32x16_bf16(ga[cb_], c, acc[1]);
+      acc[2] = mfma_32x32x16_bf16(ga[cb_], right, acc[2]);
     }
     if (do_db && tid < 256) {
       const int kl = tid >> 2, part = tid & 3;
@@ -286,14 +299,15 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
   const long stride = pl.split > 1 ? n_dw : 0;
-  switch (pl.geom) {
-    case kG64x2: launch_wgrad_bf16_geom<64, 2, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG32x4: launch_wgrad_bf16_geom<32, 4, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG16x8: launch_wgrad_bf16_geom<16, 8, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG8x16: launch_wgrad_bf16_geom<8, 16, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG8x8x2: launch_wgrad_bf16_geom<8, 8, 2>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    default: return false;
+  bool found = false;
+#define CONV3X3_X(TW_, TH_, IMGS_)                                                           \
+  if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                          \
+    launch_wgrad_bf16_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream);  \
+    found = true;                                                                            \
   }
+  CONV3X3_WGRAD_BF16_CONFIGS(CONV3X3_X)
+#undef CONV3X3_X
+  if (!found) return false;
   if (pl.split > 1) launch_wgrad_reduce(ws, dw, db, pl.split, C, K, stream);
   return true;
 }

@@ -20,6 +20,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
+#include "tile_configs.hpp"
 
 namespace conv3x3 {
 
@@ -218,20 +219,31 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const int goff = (kb * 32 + l32) * GS;
   const int xoff = (cb * 32 + l32) * PLW + r * RSW;
 
+  float a[2], b[2][3];
+  auto read_step = [&](int buf, int q2) {
+    const int p = 2 * q2 + hi;
+    const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+    a[buf] = gs[goff + p];
+    const int xb = xoff + (img * HR + row) * RSW + col;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) b[buf][s] = xs[xb + s];
+  };
+
   if (chunk_begin < chunk_end) load_tiles(chunk_begin);
   for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
     if (chunk != chunk_begin) __syncthreads();
     store_tiles(chunk);
     __syncthreads();
     if (chunk + 1 < chunk_end) load_tiles(chunk + 1);
-#pragma unroll 8
-    for (int q2 = 0; q2 < P / 2; ++q2) {
-      const int p = 2 * q2 + hi;
-      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
-      const float a = gs[goff + p];
-      const int xb = xoff + (img * HR + row) * RSW + col;
+    // Step q2 (two pixels) reads its operands while step q2-1's MFMAs run.
+    read_step(0, 0);
 #pragma unroll
-      for (int s = 0; s < 3; ++s) acc[s] = mfma_32x32x2_f32(a, xs[xb + s], acc[s]);
+    for (int q2 = 0; q2 < P / 2; ++q2) {
+      const int cur = q2 & 1;
+      if (q2 + 1 < P / 2) read_step(cur ^ 1, q2 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 3; ++s) acc[s] = mfma_32x32x2_f32(a[cur], b[cur][s], acc[s]);
     }
     if (do_db && tid < 256) {
       const int kl = tid >> 2, part = tid & 3;
@@ -296,7 +308,16 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
       base = ws + (long)S * n_dw + (e - n_dw);
       stride = K;
     }
-    for (int i = s0; i < s1; ++i) sum += base[(long)i * stride];
+    // Loads are issued eight slots at a time; the adds stay in slot order.
+    int i = s0;
+    for (; i + 8 <= s1; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = base[(long)(i + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; i < s1; ++i) sum += base[(long)i * stride];
   }
   part[q][lane] = sum;
   __syncthreads();
@@ -335,13 +356,15 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, 
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
   const long stride = pl.split > 1 ? n_dw : 0;
-  switch (pl.geom) {
-    case kG64x1: launch_wgrad_geom<64, 1, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG32x2: launch_wgrad_geom<32, 2, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG16x4: launch_wgrad_geom<16, 4, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    case kG8x8: launch_wgrad_geom<8, 8, 1>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream); break;
-    default: return false;
+  bool found = false;
+#define CONV3X3_X(TW_, TH_, IMGS_)                                                           \
+  if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                          \
+    launch_wgrad_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream);  \
+    found = true;                                                                            \
   }
+  CONV3X3_WGRAD_F32_CONFIGS(CONV3X3_X)
+#undef CONV3X3_X
+  if (!found) return false;
   if (pl.split > 1) launch_wgrad_reduce(ws, dw, db, pl.split, C, K, stream);
   return true;
 }

@@ -10,11 +10,12 @@
 //            stores free of bank conflicts).
 //
 // Forward / backward-data, bfloat16 (MFMA 32x32x16, each lane supplies 8
-// consecutive input channels at one tap):
-//   x tile : [chunk / 8][imgs][th + 2][RS][8]  bf16 -- 8 channels of one
-//            pixel form one 16-byte LDS word, so the MFMA operand is a single
-//            128-bit LDS read; RS = tw + 8, image column cc at 4 + cc.
-//   w tile : [9][chunk / 8][co_tile][8]  bf16.
+// consecutive input channels at one tap; 16-channel fills):
+//   x tile : [2][plane] words, a plane = [imgs][th + 2][RS] 16-byte words,
+//            one word = 8 channels of one pixel, so the MFMA operand is a
+//            single 128-bit LDS read; RS = tw + 8, image column cc at 4 + cc.
+//   w tile : [9][2][co_tile] words (8 input channels of one tap and output
+//            channel).
 //
 // Backward-weight, float32 (MFMA 32x32x2, reduction pairs of pixels):
 //   g tile : [64 k][P + 1]  floats, P = imgs * th * tw pixels per chunk.
@@ -48,16 +49,24 @@ CONV3X3_HD constexpr int fwd_f32_lds_bytes(int cb, int imgs, int th, int tw, int
 }
 
 // ---- forward / backward-data, bfloat16 ----
+// Plane of one 8-channel group, in 16-byte words, padded to 8 mod 16 words
+// so that the two groups' words written by one transpose step fall in
+// different banks.
 CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw + 8; }
-CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {  // in 16-byte words
-  return imgs * (th + 2) * fwd_bf16_rs(tw);
+CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {
+  return imgs * (th + 2) * fwd_bf16_rs(tw) + ((8 - (imgs * (th + 2) * fwd_bf16_rs(tw)) % 16) + 16) % 16;
 }
-// Backward-data adds a raw copy of the weight rows (cb x co_tile x 9 bf16)
-// that is transposed LDS-to-LDS into the w tile.
-CONV3X3_HD constexpr int fwd_bf16_lds_bytes(int cb, int imgs, int th, int tw, int co_tile,
-                                            bool bwd_data) {
-  return 16 * (cb / 8) * fwd_bf16_plane(imgs, th, tw) + 2 * 9 * cb * co_tile +
-         (bwd_data ? 2 * 9 * cb * co_tile : 0);
+// Words of the x region: the x tile (two 8-channel planes), or the raw
+// weight rows (16 channels x co_tile x 9 bf16) staged there before being
+// rearranged (vector path), whichever is larger.
+CONV3X3_HD constexpr int fwd_bf16_xregion_words(int imgs, int th, int tw, int co_tile,
+                                                bool raw_weights) {
+  return (raw_weights && 16 * co_tile * 9 / 8 > 2 * fwd_bf16_plane(imgs, th, tw))
+             ? 16 * co_tile * 9 / 8
+             : 2 * fwd_bf16_plane(imgs, th, tw);
+}
+CONV3X3_HD constexpr int fwd_bf16_lds_bytes(int imgs, int th, int tw, int co_tile) {
+  return 16 * (fwd_bf16_xregion_words(imgs, th, tw, co_tile, true) + 9 * 2 * co_tile);
 }
 
 // ---- backward-weight, float32 ----

@@ -2,6 +2,7 @@
 #include "planner.hpp"
 
 #include "lds_layout.hpp"
+#include "tile_configs.hpp"
 
 namespace conv3x3 {
 
@@ -9,24 +10,60 @@ namespace {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Pixel block for the forward-type kernels: 128 pixels, as wide as the
-// image allows (power of two, 8..64), two images per block for images of
-// at most 8x8.
-int fwd_geom(int H, int W) {
-  if (W > 32) return kG64x2;
-  if (W > 16) return kG32x4;
-  if (W > 8) return kG16x8;
-  if (H > 8) return kG8x16;
-  return kG8x8x2;
+struct Block {
+  int tw, th, imgs;
+};
+
+bool fwd_cfg_exists(int dtype, const Block& b, int co, int wco) {
+#define CONV3X3_X(TW, TH, IMGS, CO, WCO) \
+  if (b.tw == TW && b.th == TH && b.imgs == IMGS && co == CO && wco == WCO) return true;
+  if (dtype == kF32) {
+    CONV3X3_FWD_F32_CONFIGS(CONV3X3_X)
+  } else {
+    CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)
+  }
+#undef CONV3X3_X
+  return false;
 }
 
-// Pixel chunk for the weight-gradient kernel: 64 pixels.
-int wgrad_geom(int W) {
-  if (W > 32) return kG64x1;
-  if (W > 16) return kG32x2;
-  if (W > 8) return kG16x4;
-  return kG8x8;
+bool wgrad_cfg_exists(int dtype, const Block& b) {
+#define CONV3X3_X(TW, TH, IMGS) \
+  if (b.tw == TW && b.th == TH && b.imgs == IMGS) return true;
+  if (dtype == kF32) {
+    CONV3X3_WGRAD_F32_CONFIGS(CONV3X3_X)
+  } else {
+    CONV3X3_WGRAD_BF16_CONFIGS(CONV3X3_X)
+  }
+#undef CONV3X3_X
+  return false;
 }
+
+// A pixel block of `bm` pixels for an H x W image: as wide as the image
+// allows (power of two, 8..64) and as tall as the block; when the image is
+// shorter than the block, several images share it.
+Block pick_block(int bm, int H, int W) {
+  Block b;
+  b.tw = W > 32 ? 64 : W > 16 ? 32 : W > 8 ? 16 : 8;
+  const int rows = bm / b.tw;
+  int hp = 1;
+  while (hp < H) hp *= 2;
+  if (rows <= hp) {
+    b.th = rows;
+    b.imgs = 1;
+  } else {
+    b.th = hp;
+    b.imgs = rows / hp;
+  }
+  return b;
+}
+
+int blocks_of(const Block& b, int N, int H, int W) {
+  return ceil_div(N, b.imgs) * ceil_div(H, b.th) * ceil_div(W, b.tw);
+}
+
+// Grids smaller than this leave compute units idle; the planner then falls
+// back to smaller workgroup tiles.
+constexpr int kMinWGs = 256;
 
 // Number of workgroups the weight-gradient pass aims for: one 12-wave
 // workgroup per compute unit on a 256-CU device.
@@ -44,18 +81,47 @@ bool plan(const Problem& p, Plan* out) {
   pl.pass = p.pass;
   pl.dtype = p.dtype;
   if (p.pass == kFwd || p.pass == kBwdData) {
-    const int cin = p.pass == kFwd ? p.C : p.K;
     const int cout = p.pass == kFwd ? p.K : p.C;
-    (void)cin;
-    pl.geom = fwd_geom(p.H, p.W);
-    GeomDims d = geom_dims(pl.geom);
-    pl.tw = d.tw;
-    pl.th = d.th;
-    pl.imgs = d.imgs;
-    pl.tile_co = cout > 64 ? 128 : 64;
-    // Channels per LDS fill: 16 with 64-channel tiles, 8 with 128-channel
-    // tiles, so every fill holds the same 144 MFMA steps per wave.
-    pl.chunk = p.dtype == kF32 ? (pl.tile_co == 64 ? 16 : 8) : 16;
+    // Candidate workgroup tiles, preferred first: (pixels, channels, waves
+    // along channels).
+    struct Cand {
+      int bm, co, wco;
+    };
+    Cand cands[3];
+    int ncand;
+    if (p.dtype == kF32) {
+      cands[0] = cout <= 64 ? Cand{256, 64, 1} : Cand{128, 128, 2};
+      cands[1] = Cand{64, 64, 2};
+      ncand = 2;
+    } else if (cout > 64) {
+      cands[0] = Cand{256, 128, 2};
+      cands[1] = Cand{128, 64, 2};
+      cands[2] = Cand{64, 64, 2};
+      ncand = 3;
+    } else {
+      cands[0] = Cand{128, 64, 2};
+      cands[1] = Cand{64, 64, 2};
+      ncand = 2;
+    }
+    int pick = -1;
+    Block blk{};
+    for (int i = 0; i < ncand; ++i) {
+      Block b = pick_block(cands[i].bm, p.H, p.W);
+      if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco))
+        b = Block{b.tw, cands[i].bm / b.tw, 1};
+      if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco)) continue;
+      const int wgs = blocks_of(b, p.N, p.H, p.W) * ceil_div(cout, cands[i].co);
+      pick = i;
+      blk = b;
+      if (wgs >= kMinWGs) break;
+    }
+    if (pick < 0) return false;
+    pl.tw = blk.tw;
+    pl.th = blk.th;
+    pl.imgs = blk.imgs;
+    pl.tile_co = cands[pick].co;
+    pl.wave_co = cands[pick].wco;
+    pl.chunk = p.dtype == kF32 ? 8 : 16;
     pl.tiles_w = ceil_div(p.W, pl.tw);
     pl.tiles_h = ceil_div(p.H, pl.th);
     pl.tiles_n = ceil_div(p.N, pl.imgs);
@@ -65,19 +131,20 @@ bool plan(const Problem& p, Plan* out) {
     pl.threads = 256;
     pl.lds_bytes = p.dtype == kF32
         ? fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
-        : fwd_bf16_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co, p.pass == kBwdData);
+        : fwd_bf16_lds_bytes(pl.imgs, pl.th, pl.tw, pl.tile_co);
     pl.split = 1;
   } else if (p.pass == kBwdWeight) {
     // float32: 64-pixel chunks (32 MFMA steps); bfloat16: 128-pixel chunks
     // (8 MFMA steps of 16 pixels).
-    pl.geom = p.dtype == kF32 ? wgrad_geom(p.W) : fwd_geom(p.H, p.W);
-    GeomDims d = geom_dims(pl.geom);
-    pl.tw = d.tw;
-    pl.th = d.th;
-    pl.imgs = d.imgs;
+    Block b = pick_block(p.dtype == kF32 ? 64 : 128, p.H, p.W);
+    if (!wgrad_cfg_exists(p.dtype, b)) b = Block{b.tw, (p.dtype == kF32 ? 64 : 128) / b.tw, 1};
+    if (!wgrad_cfg_exists(p.dtype, b)) return false;
+    pl.tw = b.tw;
+    pl.th = b.th;
+    pl.imgs = b.imgs;
     pl.tile_co = 64;
     pl.tile_ci = 64;
-    pl.chunk = d.tw * d.th * d.imgs;
+    pl.chunk = b.tw * b.th * b.imgs;
     pl.tiles_w = ceil_div(p.W, pl.tw);
     pl.tiles_h = ceil_div(p.H, pl.th);
     pl.tiles_n = ceil_div(p.N, pl.imgs);

@@ -22,46 +22,13 @@ namespace conv3x3 {
 enum Pass { kFwd = 0, kBwdData = 1, kBwdWeight = 2 };
 enum DType { kF32 = 0, kBF16 = 1 };
 
-// Pixel-block geometries, shared by every kernel family.  The block is
-// imgs x th x tw pixels; tw is the width of the block (power of two).
-enum Geom {
-  kG64x2 = 0,   // tw 64, th 2
-  kG32x4 = 1,   // tw 32, th 4
-  kG16x8 = 2,   // tw 16, th 8
-  kG8x16 = 3,   // tw 8,  th 16
-  kG8x8x2 = 4,  // tw 8,  th 8, two images
-  kG64x1 = 5,   // tw 64, th 1
-  kG32x2 = 6,   // tw 32, th 2
-  kG16x4 = 7,   // tw 16, th 4
-  kG8x8 = 8,    // tw 8,  th 8
-  kNumGeom = 9
-};
-
-struct GeomDims {
-  int tw, th, imgs;
-};
-
-inline GeomDims geom_dims(int g) {
-  switch (g) {
-    case kG64x2: return {64, 2, 1};
-    case kG32x4: return {32, 4, 1};
-    case kG16x8: return {16, 8, 1};
-    case kG8x16: return {8, 16, 1};
-    case kG8x8x2: return {8, 8, 2};
-    case kG64x1: return {64, 1, 1};
-    case kG32x2: return {32, 2, 1};
-    case kG16x4: return {16, 4, 1};
-    default: return {8, 8, 1};
-  }
-}
-
 struct Plan {
   int pass = 0;
   int dtype = 0;
-  int geom = 0;       // Geom
   int tile_co = 0;    // fwd/bwd_data: output channels per WG; bwd_weight: k per WG
+  int wave_co = 0;    // fwd/bwd_data: waves along the channel dimension
   int tile_ci = 0;    // bwd_weight: input channels per WG
-  int tw = 0, th = 0, imgs = 0;
+  int tw = 0, th = 0, imgs = 0;  // pixel block (fwd/bwd_data) or chunk (bwd_weight)
   int chunk = 0;      // channels (fwd/bwd_data) or pixels (bwd_weight) per LDS fill
   int threads = 256;
   int tiles_w = 0, tiles_h = 0, tiles_n = 0;

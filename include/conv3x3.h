@@ -136,7 +136,7 @@ const char* conv3x3_status_string(int status);
 typedef struct {
   int pass;            /* conv3x3_pass_t */
   int dtype;           /* conv3x3_dtype_t */
-  int kernel;          /* internal kernel variant id */
+  int kernel;          /* fwd/bwd_data: waves along the channel tile (1 or 2); else 0 */
   int tile_m;          /* rows of the WG tile: output channels (fwd, bwd_data) or k (bwd_weight) */
   int tile_n;          /* columns of the WG tile: pixels (fwd, bwd_data) or input channels (bwd_weight) */
   int tile_imgs;       /* pixel tile = tile_imgs x tile_h x tile_w */
