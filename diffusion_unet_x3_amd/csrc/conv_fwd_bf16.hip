@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
 
   __shared__ u32x4 xs[XWORDS];  // x tile; also the raw weight rows while they are staged
   __shared__ u32x4 wa[9 * 2 * BCO];
+  __shared__ float bias_s[MODE == kFwd ? BCO : 1];  // this tile's biases (0 without bias)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -385,6 +386,12 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + r * RS + s];
   };
 
+  if constexpr (MODE == kFwd) {
+    // Visible to the epilogue through the chunk loop's barriers.
+    for (int i = tid; i < BCO; i += 256)
+      bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
+  }
+
   const int nchunks = (Cin + CB - 1) / CB;
   load_tiles(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         const int co = co0 + wco * (BCO / WCO) + i * 32 + acc_row(v, hi);
         if (co < Cout) {
           float val = acc[i][j][v];
-          if (MODE == kFwd && bias) val += bias[co];
+          if constexpr (MODE == kFwd) val += bias_s[co - co0];
           out[(long)co * HW] = val;
         }
       }

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 
   __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
+  __shared__ float bias_s[MODE == kFwd ? BCO : 1];  // this tile's biases (0 without bias)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -246,6 +247,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
   };
 
+  if constexpr (MODE == kFwd) {
+    // Visible to the epilogue through the chunk loop's barriers.
+    for (int i = tid; i < BCO; i += 256)
+      bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
+  }
+
   const int nchunks = (Cin + CB - 1) / CB;
   load_tiles(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
         const int co = co0 + wco * (BCO / WCO) + i * 32 + acc_row(v, hi);
         if (co < Cout) {
           float val = acc[i][j][v];
-          if (MODE == kFwd && bias) val += bias[co];
+          if constexpr (MODE == kFwd) val += bias_s[co - co0];
           out[(long)co * HW] = val;
         }
       }

@@ -132,6 +132,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.lds_bytes = p.dtype == kF32
         ? fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
         : fwd_bf16_lds_bytes(pl.imgs, pl.th, pl.tw, pl.tile_co);
+    if (p.pass == kFwd) pl.lds_bytes += 4 * pl.tile_co;  // the tile's biases
     pl.split = 1;
   } else if (p.pass == kBwdWeight) {
     // float32: 64-pixel chunks (32 MFMA steps); bfloat16: 128-pixel chunks
