@@ -28,7 +28,7 @@ template <int TW, int TH, int IMGS, bool VEC>
 __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ g, float* __restrict__ out,
     float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
-    int nchunks, int per_split, long slice_stride) {
+    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P == 64, "pixel chunk must hold 64 pixels");
   constexpr int GS = wgrad_f32_gstride(IMGS, TH, TW);
@@ -43,11 +43,19 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int r = wave % 3, kb = (wave / 3) & 1, cb = wave / 6;
-  const int slice = blockIdx.x;
-  const int c0 = blockIdx.y * 64;
-  const int k0 = blockIdx.z * 64;
+  // XCD-aware placement: the hardware deals consecutive workgroups to the 8
+  // XCDs in turn, so workgroup b takes logical index (b % 8) * (grid / 8) +
+  // b / 8.  Each XCD then runs a contiguous range of logical indices -- all
+  // channel tiles of the same slices -- and a slice's x / g data is fetched
+  // into one L2.  The grid is padded to a multiple of 8; spare workgroups exit.
+  const int ntile = tiles_c * tiles_k;
+  const int L = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  if (L >= split * ntile) return;
+  const int slice = L / ntile, tile = L % ntile;
+  const int c0 = (tile % tiles_c) * 64;
+  const int k0 = (tile / tiles_c) * 64;
   const long HW = (long)H * W;
-  const bool do_db = out_db != nullptr && blockIdx.y == 0;
+  const bool do_db = out_db != nullptr && tile % tiles_c == 0;
 
   // g tile: 64 k x P pixels.  x tile: 64 c x IMGS x HR rows x (TW + 2) columns.
   constexpr int XQ = TW / 4;
@@ -337,15 +345,17 @@ template <int TW, int TH, int IMGS>
 static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const float* g,
                               float* out, float* out_db, long slice_stride, int N, int C, int K,
                               int H, int W, hipStream_t stream) {
-  dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z), block(pl.threads, 1, 1);
+  dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
   if (vec)
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
                        out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride);
+                       pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
+                       (K + 63) / 64);
   else
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
                        out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride);
+                       pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
+                       (K + 63) / 64);
 }
 
 bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,

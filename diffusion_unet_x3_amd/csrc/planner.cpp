@@ -150,15 +150,17 @@ bool plan(const Problem& p, Plan* out) {
     pl.tiles_h = ceil_div(p.H, pl.th);
     pl.tiles_n = ceil_div(p.N, pl.imgs);
     pl.nchunks = pl.tiles_n * pl.tiles_h * pl.tiles_w;
+    // One round of 12-wave workgroups (one per compute unit): as many
+    // reduction slices as fit next to the channel tiles.
     const int tiles = ceil_div(p.K, pl.tile_co) * ceil_div(p.C, pl.tile_ci);
-    int split = ceil_div(kWgradTargetWGs, tiles);
+    int split = kWgradTargetWGs / tiles;
     if (split > pl.nchunks) split = pl.nchunks;
     if (split < 1) split = 1;
     pl.chunks_per_split = ceil_div(pl.nchunks, split);
     pl.split = ceil_div(pl.nchunks, pl.chunks_per_split);  // no empty slices
-    pl.grid_x = pl.split;
-    pl.grid_y = ceil_div(p.C, pl.tile_ci);
-    pl.grid_z = ceil_div(p.K, pl.tile_co);
+    pl.grid_x = ceil_div(pl.split * tiles, 8) * 8;  // whole XCD rounds; spare WGs exit
+    pl.grid_y = 1;
+    pl.grid_z = 1;
     pl.threads = 768;
     pl.lds_bytes = p.dtype == kF32
         ? wgrad_f32_lds_bytes(pl.imgs, pl.th, pl.tw)

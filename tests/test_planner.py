@@ -39,8 +39,11 @@ def test_weight_gradient_plans(shape, dtype):
     assert 1 <= S <= chunks
     per = math.ceil(chunks / S)
     assert (S - 1) * per < chunks <= S * per  # no empty slice
-    assert p["grid_x"] == S
-    assert p["grid_y"] * p["tile_n"] >= C and p["grid_z"] * p["tile_m"] >= K
+    tiles = math.ceil(C / p["tile_n"]) * math.ceil(K / p["tile_m"])
+    # 1-D grid: S x tiles workgroups padded to whole rounds of the 8 XCDs
+    assert p["grid_x"] % 8 == 0 and S * tiles <= p["grid_x"] < S * tiles + 8
+    assert p["grid_y"] == 1 and p["grid_z"] == 1
+    assert S * tiles <= 256 or S == 1
     assert 0 < p["lds_bytes"] <= LDS_PER_CU
     ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)
     assert ws == p["workspace_bytes"]
