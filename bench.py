@@ -29,8 +29,79 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "conv3x3 fwd+bwd TFLOP/s and % of MFMA/HBM roofline on 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_f32_unet_stem_32x64to64_64x64_traffic.json")
+# Kernels launched by each pass of the stem layer (name prefixes in profiler output).
+PASS_KERNELS = {"fwd": ["conv3x3::fwd_f32_kernel<0,"],
+                "bwd_data": ["conv3x3::fwd_f32_kernel<1,"],
+                "bwd_weight": ["conv3x3::wgrad_f32_kernel<", "conv3x3::wgrad_reduce_kernel"]}
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # dense MFMA peaks, MI355X
 PEAK_HBM_GBS = 8000.0
+
+
+def library_source_digest():
+    """sha256 over the HIP library's sources: profiler byte counts recorded
+    for one digest are reported only while the sources still match it."""
+    import hashlib
+    csrc = os.path.join(ROOT, "diffusion_unet_x3_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def record_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    of `bench.py --copy-calibration-mb 512` into per-pass HBM bytes.  Each
+    counter is scaled so that the 512 MiB device copy reads what it moved."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                name = r["Kernel_Name"].replace("void ", "")
+                vals.setdefault((name, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    big = max((k for k in write if k[0].startswith("__amd_rocclr_copyBuffer")), key=lambda k: k[1])
+    copy_kib = 512 * 1024
+    f_factor = copy_kib / statistics.median(fetch[big])
+    w_factor = copy_kib / statistics.median(write[big])
+    kernels = {}
+    for (name, grid), v in fetch.items():
+        if name.startswith("conv3x3::"):
+            kernels[name] = {"grid": grid, "fetch_kib": statistics.median(v),
+                             "write_kib": statistics.median(write[(name, grid)])}
+    passes = {}
+    for p, prefixes in PASS_KERNELS.items():
+        ks = [k for k in kernels if any(k.startswith(q) for q in prefixes)]
+        passes[p] = {"kernels": ks, "hbm_bytes": sum(
+            (kernels[k]["fetch_kib"] * f_factor + kernels[k]["write_kib"] * w_factor) * 1024
+            for k in ks)}
+    rec = {"source_digest": library_source_digest(),
+           "calibration": {"copy_mib": 512, "fetch_kib_read": statistics.median(fetch[big]),
+                           "write_kib_read": statistics.median(write[big]),
+                           "fetch_factor": f_factor, "write_factor": w_factor},
+           "kernels": kernels, "passes": passes}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
+def recorded_traffic(pass_name):
+    """HBM bytes per launch of a pass, or None if not recorded for these sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != library_source_digest():
+        return None
+    b = rec.get("passes", {}).get(pass_name, {}).get("hbm_bytes")
+    return int(b) if b else None
 
 
 def flops_per_pass(N, C, K, H, W):
@@ -172,10 +243,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", metavar="OUT_JSON", help="also time every configured layer")
     ap.add_argument("--sweep-match", metavar="REGEX", help="only sweep layers whose name matches")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
+                         "(FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--copy-calibration-mb", type=int, default=0, metavar="MB",
                     help="also run a plain device-to-device copy of MB megabytes (a known "
                          "amount of HBM traffic for scaling profiler byte counters)")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic)["passes"]))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -200,9 +277,12 @@ def main():
                    "N": N, "C_in": C, "C_out": K, "H": H, "W": W, "stride": 1, "pad": 1,
                    "layout": "NCHW", "seed": layer.seed, "global_batch": N,
                    "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 3),
+        "roofline": {"bound": "mfma", "kernel": dom, "kernels": PASS_KERNELS[dom],
+                     "achieved": round(achieved, 3),
                      "peak": PEAK_TFLOPS[layer.dtype], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS[layer.dtype], 4), "traffic": None},
+                     "frac": round(achieved / PEAK_TFLOPS[layer.dtype], 4),
+                     "traffic": recorded_traffic(dom),
+                     "alg_bytes": alg_bytes(dom, N, C, K, H, W, layer.dtype)},
         "passes": {p: {"us": round(t * 1e3, 2),
                        "tflops": round(f / (t * 1e-3) / 1e12, 2),
                        "alg_gbs": round(alg_bytes(p, N, C, K, H, W, layer.dtype) /
