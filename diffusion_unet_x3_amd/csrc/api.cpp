@@ -31,6 +31,9 @@ int check_dtype(int dtype) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The bf16 vector paths read through 32-bit buffer offsets.
+bool buffer_sized(long elems) { return elems * 2 < 2147483648L; }
+
 int launch_status() {
   return hipGetLastError() == hipSuccess ? CONV3X3_OK : CONV3X3_ERR_HIP;
 }
@@ -97,7 +100,8 @@ int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y, int N
     const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(x) && aligned16(w);
     ok = launch_fwd_f32(pl, vec, (const float*)x, (const float*)w, bias, y, N, C, K, H, W, s);
   } else {
-    const bool vec = W % 8 == 0 && C % 8 == 0 && aligned16(x) && aligned16(w);
+    const bool vec = W % 8 == 0 && C % 16 == 0 && aligned16(x) && aligned16(w) &&
+                     buffer_sized((long)N * C * H * W) && buffer_sized((long)K * C * 9);
     ok = launch_fwd_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)w, bias, y, N, C, K, H, W, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
@@ -120,7 +124,8 @@ int conv3x3_bwd_data(const void* g, const void* w, float* dx, int N, int C, int 
     const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w);
     ok = launch_fwd_f32(pl, vec, (const float*)g, (const float*)w, nullptr, dx, N, K, C, H, W, s);
   } else {
-    const bool vec = W % 8 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w);
+    const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w) &&
+                     buffer_sized((long)N * K * H * W) && buffer_sized((long)K * C * 9);
     ok = launch_fwd_bf16(pl, vec, (const uint16_t*)g, (const uint16_t*)w, nullptr, dx, N, K, C, H,
                          W, s);
   }

@@ -49,3 +49,27 @@ __device__ __forceinline__ BlockOrigin block_origin(int b, int tiles_w, int tile
 }
 
 }  // namespace conv3x3
+
+namespace conv3x3 {
+
+// Raw buffer view of a tensor for the vector staging paths.  Loads take a
+// per-lane byte offset; an offset at or past the view's size reads zeros
+// (the hardware range check), which is how out-of-image halo rows and
+// columns, and items past a tile's edge, become zero without branches.  Only
+// the per-lane offset is range-checked, so callers keep every term of the
+// address in it.  Views are limited to tensors of fewer than 2^31 bytes;
+// kOutside + any in-range offset stays below 2^32 and past the view.
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(v, (int)off, 0, 0);
+}
+
+}  // namespace conv3x3

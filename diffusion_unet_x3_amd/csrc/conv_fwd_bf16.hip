@@ -103,7 +103,7 @@ template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, bool VEC>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ wt,
     const float* __restrict__ bias, float* __restrict__ dst, int N, int Cin, int Cout, int H,
-    int W, int tiles_w, int tiles_h) {
+    int W, int tiles_w, int tiles_h, uint32_t src_bytes, uint32_t wt_bytes) {
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
   constexpr int WPX = 4 / WCO;
@@ -146,68 +146,75 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   u32x4 hr;
   u32x4 wr[VEC ? WR : 1];
 
+  // Vector path (host guarantees Cin % 16 == 0, so every fill is whole):
+  // each staged item's byte offset is computed once; a fill only adds the
+  // channel step, and items outside the tensors hold kOutside and read zero.
+  const __amdgpu_buffer_rsrc_t sv = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t wv = buffer_view(wt, wt_bytes);
+  uint32_t xoff[VEC ? XN : 1], hoff = kOutside, woff[VEC ? WN : 1];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < XN; ++k) {
+      const int it = tid + 256 * k;
+      const int ch = it & 15;
+      int t = it >> 4;
+      const int q = t % (TW / 8);
+      t /= TW / 8;
+      const int rr = t % HR;
+      const int img = t / HR;
+      const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
+      const bool ok = (XI % 256 == 0 || it < XI) && n < N && h >= 0 && h < H && w < W;
+      xoff[k] = ok ? 2u * (uint32_t)(((n * Cin + ch) * H + h) * W + w) : kOutside;
+    }
+    if (tid < XH) {
+      const int side = tid & 1;
+      int t = tid >> 1;
+      const int rr = t % HR;
+      t /= HR;
+      const int img = t % IMGS;
+      const int g = t / IMGS;
+      const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + (side ? TW : -1);
+      if (n < N && h >= 0 && h < H && w >= 0 && w < W)
+        hoff = 2u * (uint32_t)(((n * Cin + 8 * g) * H + h) * W + w);
+    }
+#pragma unroll
+    for (int k = 0; k < WN; ++k) {
+      const int it = tid + 256 * k;
+      bool ok;
+      uint32_t e;
+      if constexpr (MODE == kFwd) {
+        const int run = it / 18, piece = it % 18;  // 18 words per output channel
+        ok = (WI % 256 == 0 || it < WI) && co0 + run < Cout;
+        e = (uint32_t)(((co0 + run) * Cin) * 9 + 8 * piece);
+      } else {
+        const int kl = it / EW, e8 = it % EW;
+        ok = (WI % 256 == 0 || it < WI) && 8 * e8 < (Cout - co0) * 9;
+        e = (uint32_t)((kl * Cout + co0) * 9 + 8 * e8);
+      }
+      woff[k] = ok ? 2u * e : kOutside;
+    }
+  }
+  const uint32_t hw2 = 2u * (uint32_t)(H * W);
+  // bytes between consecutive fills: 16 channels of the source, and of w
+  const uint32_t xstep = 16u * hw2;
+  const uint32_t wstep = MODE == kFwd ? 2u * 16u * 9u : 2u * 16u * 9u * (uint32_t)Cout;
+
   auto load_tiles = [&](int c0) {
     if constexpr (VEC) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
+      const uint32_t f = (uint32_t)(c0 / 16);
 #pragma unroll
-      for (int k = 0; k < XN; ++k) {
-        const int it = tid + 256 * k;
-        const int ch = it & 15;
-        int t = it >> 4;
-        const int q = t % (TW / 8);
-        t /= TW / 8;
-        const int rr = t % HR;
-        const int img = t / HR;
-        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q, c = c0 + ch;
-        const bool ok = (XI % 256 == 0 || it < XI) && n < N && c < Cin && h >= 0 && h < H && w < W;
-        const long idx = ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + idx);
-        xr[k] = ok ? v : z;
+      for (int k = 0; k < XN; ++k) xr[k] = buffer_load16(sv, xoff[k] + f * xstep);
+      {
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = buffer_load2(sv, hoff + f * xstep + (uint32_t)i * hw2);
+        hr.x = v[0] | (v[1] << 16);
+        hr.y = v[2] | (v[3] << 16);
+        hr.z = v[4] | (v[5] << 16);
+        hr.w = v[6] | (v[7] << 16);
       }
-      hr = z;
-      if (tid < XH) {
-        const int side = tid & 1;
-        int t = tid >> 1;
-        const int rr = t % HR;
-        t /= HR;
-        const int img = t % IMGS;
-        const int g = t / IMGS;
-        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + (side ? TW : -1);
-        if (n < N && h >= 0 && h < H && w >= 0 && w < W) {
-          uint32_t v[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int c = c0 + 8 * g + i;
-            v[i] = c < Cin ? src[((long)n * Cin + c) * HW + (long)h * W + w] : 0u;
-          }
-          hr.x = v[0] | (v[1] << 16);
-          hr.y = v[2] | (v[3] << 16);
-          hr.z = v[4] | (v[5] << 16);
-          hr.w = v[6] | (v[7] << 16);
-        }
-      }
-      if constexpr (MODE == kFwd) {
-#pragma unroll
-        for (int k = 0; k < WN; ++k) {
-          const int it = tid + 256 * k;
-          const int run = it / 18, piece = it % 18;  // 18 words per output channel
-          const int co = co0 + run;
-          const bool ok = (WI % 256 == 0 || it < WI) && co < Cout && 8 * piece < (Cin - c0) * 9;
-          const long idx = ok ? ((long)co * Cin + c0) * 9 + 8 * piece : 0;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(wt + idx);
-          wr[k] = ok ? v : z;
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < WN; ++k) {
-          const int it = tid + 256 * k;
-          const int kl = it / EW, e8 = it % EW;
-          const bool ok = (WI % 256 == 0 || it < WI) && c0 + kl < Cin && 8 * e8 < (Cout - co0) * 9;
-          const long idx = ok ? ((long)(c0 + kl) * Cout + co0) * 9 + 8 * e8 : 0;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(wt + idx);
-          wr[k] = ok ? v : z;
-        }
-      }
+      for (int k = 0; k < WN; ++k) wr[k] = buffer_load16(wv, woff[k] + f * wstep);
     }
   };
 
@@ -443,10 +450,12 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, const uint16_t* src, const
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
   if (vec)
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, true>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                       (uint32_t)((long)N * Cin * H * W * 2), (uint32_t)((long)Cin * Cout * 9 * 2));
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, false>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u,
+                       0u);
 }
 
 bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
