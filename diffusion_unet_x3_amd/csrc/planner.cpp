@@ -103,18 +103,32 @@ bool plan(const Problem& p, Plan* out) {
       cands[1] = Cand{64, 64, 2};
       ncand = 2;
     }
-    int pick = -1;
-    Block blk{};
+    // Take the first candidate that fills the device without wasting much of
+    // its tile on pixels past the image (a block taller than the image or a
+    // ragged edge); otherwise the last (smallest) one that fits.
+    Block blks[3];
+    double eff[3];
+    int wgs[3];
+    double best_eff = 0.0;
     for (int i = 0; i < ncand; ++i) {
       Block b = pick_block(cands[i].bm, p.H, p.W);
       if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco))
         b = Block{b.tw, cands[i].bm / b.tw, 1};
+      blks[i] = b;
+      eff[i] = 0.0;
+      wgs[i] = 0;
       if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco)) continue;
-      const int wgs = blocks_of(b, p.N, p.H, p.W) * ceil_div(cout, cands[i].co);
-      pick = i;
-      blk = b;
-      if (wgs >= kMinWGs) break;
+      wgs[i] = blocks_of(b, p.N, p.H, p.W) * ceil_div(cout, cands[i].co);
+      eff[i] = (double)p.N * p.H * p.W * cout / ((double)wgs[i] * cands[i].bm * cands[i].co);
+      if (eff[i] > best_eff) best_eff = eff[i];
     }
+    int pick = -1;
+    for (int i = 0; i < ncand; ++i) {
+      if (wgs[i] == 0) continue;
+      pick = i;
+      if (wgs[i] >= kMinWGs && eff[i] >= 0.8 * best_eff) break;
+    }
+    const Block blk = pick >= 0 ? blks[pick] : Block{};
     if (pick < 0) return false;
     pl.tw = blk.tw;
     pl.th = blk.th;

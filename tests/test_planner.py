@@ -30,6 +30,25 @@ def test_forward_type_plans_cover_problem(shape, dtype):
 
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("dtype", [0, 1])
+def test_forward_type_tiles_fit_the_image(shape, dtype):
+    """On images of at least 8 x 8 pixels (the smallest block), a pixel block
+    is never taller than the image rounded up to a power of two (a taller
+    block only multiplies zero padding), and on layers whose images are a
+    power of two on a side, at least half of the pixels the grid covers are
+    pixels of the problem."""
+    N, C, K, H, W = shape
+    if H < 8 or W < 8:
+        pytest.skip("image smaller than the smallest pixel block")
+    hp = 1 << max(0, (H - 1).bit_length())
+    for pass_, cout in ((lib3.PASS_FWD, K), (lib3.PASS_BWD_DATA, C)):
+        p = lib3.conv3x3_plan(pass_, N, C, K, H, W, dtype)
+        assert p["tile_h"] <= hp
+        if H == hp and W == 1 << max(0, (W - 1).bit_length()):
+            assert N * H * W >= 0.5 * p["grid_x"] * p["tile_n"]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype", [0, 1])
 def test_weight_gradient_plans(shape, dtype):
     N, C, K, H, W = shape
     p = lib3.conv3x3_plan(lib3.PASS_BWD_WEIGHT, N, C, K, H, W, dtype)
