@@ -72,4 +72,13 @@ __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t v, uint3
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(v, (int)off, 0, 0);
 }
 
+// Store one float at byte offset voff + soff of a view; soff is uniform
+// across the wave (a scalar register).  The range check applies to voff, so
+// a lane with voff = kOutside stores nothing.
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t v, uint32_t voff,
+                                              uint32_t soff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), v, (int)voff,
+                                        (int)soff, 0);
+}
+
 }  // namespace conv3x3

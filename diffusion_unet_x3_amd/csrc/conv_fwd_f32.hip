@@ -26,12 +26,14 @@
 
 namespace conv3x3 {
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC>
-__global__ __launch_bounds__(256) void fwd_f32_kernel(
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ wt, const float* __restrict__ bias,
-    float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h) {
+    float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h,
+    uint32_t dst_bytes) {
   constexpr int BM = IMGS * TH * TW;
-  constexpr int WPX = 4 / WCO;
+  constexpr int NT = 64 * NW;  // threads
+  constexpr int WPX = NW / WCO;
   constexpr int MI = BCO / (32 * WCO);  // 32x32 tiles per wave along channels
   constexpr int NJ = BM / (32 * WPX);   // 32x32 tiles per wave along pixels
   static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
@@ -59,12 +61,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   // straddles the image edge), the two halo columns as scalars.
   constexpr int XQ = TW / 4;
   constexpr int XV_ITEMS = CB * IMGS * HR * XQ;
-  constexpr int XV_N = (XV_ITEMS + 255) / 256;
+  constexpr int XV_N = (XV_ITEMS + NT - 1) / NT;
   constexpr int XH_ITEMS = CB * IMGS * HR * 2;
-  constexpr int XH_N = (XH_ITEMS + 255) / 256;
+  constexpr int XH_N = (XH_ITEMS + NT - 1) / NT;
   // Scalar path: every column of the staged rows.
   constexpr int XS_ITEMS = CB * IMGS * HR * (TW + 2);
-  constexpr int XS_N = (XS_ITEMS + 255) / 256;
+  constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
 
@@ -74,9 +76,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   constexpr int RUN = MODE == kFwd ? CB * 9 : BCO * 9;
   constexpr int NRUN = MODE == kFwd ? BCO : CB;
   constexpr int WV_ITEMS = NRUN * RUN / 4;
-  constexpr int WV_N = (WV_ITEMS + 255) / 256;
+  constexpr int WV_N = (WV_ITEMS + NT - 1) / NT;
   constexpr int WS_ITEMS = CB * 9 * BCO;
-  constexpr int WS_N = (WS_ITEMS + 255) / 256;
+  constexpr int WS_N = (WS_ITEMS + NT - 1) / NT;
   f32x4 wv[VEC ? WV_N : 1];
 
   // Vector path: global -> registers here (one fill ahead), registers -> LDS
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
         const int q = it % XQ;
         int t = it / XQ;
         const int rr = t % HR;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
         const int img = t % IMGS;
         const int ch = t / IMGS;
         const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
-        const bool ok = (XV_ITEMS % 256 == 0 || it < XV_ITEMS) && n < N && c < Cin && h >= 0 &&
+        const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && c < Cin && h >= 0 &&
                         h < H && w < W;
         const long idx = ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0;
         const f32x4 v = *reinterpret_cast<const f32x4*>(src + idx);
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
         const int side = it & 1;
         int t = it >> 1;
         const int rr = t % HR;
@@ -113,25 +115,25 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
         const int ch = t / IMGS;
         const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1;
         const int w = o.w0 + (side ? TW : -1);
-        const bool ok = (XH_ITEMS % 256 == 0 || it < XH_ITEMS) && n < N && c < Cin && h >= 0 &&
+        const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && c < Cin && h >= 0 &&
                         h < H && w >= 0 && w < W;
         const float v = src[ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0];
         xf[k] = ok ? v : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
-        const int it = tid + k * 256;
+        const int it = tid + k * NT;
         const int run = it / (RUN / 4);
         const int e = 4 * (it % (RUN / 4));
         bool ok;
         long idx;
         if constexpr (MODE == kFwd) {
           const int co = co0 + run;
-          ok = (WV_ITEMS % 256 == 0 || it < WV_ITEMS) && co < Cout && e < (Cin - c0) * 9;
+          ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && co < Cout && e < (Cin - c0) * 9;
           idx = ((long)co * Cin + c0) * 9 + e;
         } else {
           const int ci = c0 + run;
-          ok = (WV_ITEMS % 256 == 0 || it < WV_ITEMS) && ci < Cin && e < (Cout - co0) * 9;
+          ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && ci < Cin && e < (Cout - co0) * 9;
           idx = ((long)ci * Cout + co0) * 9 + e;
         }
         const f32x4 v = *reinterpret_cast<const f32x4*>(wt + (ok ? idx : 0));
@@ -153,8 +155,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
-        const int it = tid + k * 256;
-        if (XV_ITEMS % 256 == 0 || it < XV_ITEMS) {
+        const int it = tid + k * NT;
+        if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
           const int q = it % XQ;
           const int t = it / XQ;  // (ch * IMGS + img) * HR + rr
           *reinterpret_cast<f32x4*>(&xs[t * RS + 4 + 4 * q]) = xv[k];
@@ -162,8 +164,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
-        const int it = tid + k * 256;
-        if (XH_ITEMS % 256 == 0 || it < XH_ITEMS) {
+        const int it = tid + k * NT;
+        if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
           const int side = it & 1;
           const int t = it >> 1;
           xs[t * RS + 4 + (side ? TW : -1)] = xf[k];
@@ -171,8 +173,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
-        const int it = tid + k * 256;
-        if (WV_ITEMS % 256 == 0 || it < WV_ITEMS) {
+        const int it = tid + k * NT;
+        if (WV_ITEMS % NT == 0 || it < WV_ITEMS) {
           const int run = it / (RUN / 4);
           const int e = 4 * (it % (RUN / 4));
           ws[w_slot(run, e + 0)] = wv[k].x;
@@ -185,8 +187,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       // Scalar path (ragged shapes): global loads go straight to LDS.
 #pragma unroll 4
       for (int k = 0; k < XS_N; ++k) {
-        const int it = tid + k * 256;
-        if (XS_ITEMS % 256 == 0 || it < XS_ITEMS) {
+        const int it = tid + k * NT;
+        if (XS_ITEMS % NT == 0 || it < XS_ITEMS) {
           const int cc = it % (TW + 2) - 1;
           const int t = it / (TW + 2);  // (ch * IMGS + img) * HR + rr
           const int rr = t % HR;
@@ -201,8 +203,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
       }
 #pragma unroll 4
       for (int k = 0; k < WS_N; ++k) {
-        const int it = tid + k * 256;
-        if (WS_ITEMS % 256 == 0 || it < WS_ITEMS) {
+        const int it = tid + k * NT;
+        if (WS_ITEMS % NT == 0 || it < WS_ITEMS) {
           const int run = it / RUN;
           const int e = it % RUN;
           float v = 0.f;
@@ -229,14 +231,6 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   }
   const int aoff = hi * 9 * WS + wco * (BCO / WCO) + l32;
 
-  f32x16 acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
   // Operands of one MFMA step st = (cp, r, s), cp the channel pair.
   float a[2][MI], b[2][NJ];
   auto read_step = [&](int buf, int st) {
@@ -247,10 +241,22 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
   };
 
+  // Forward: the accumulators start at the tile's biases (zero without
+  // bias), so the epilogue is stores only.
   if constexpr (MODE == kFwd) {
-    // Visible to the epilogue through the chunk loop's barriers.
-    for (int i = tid; i < BCO; i += 256)
+    for (int i = tid; i < BCO; i += NT)
       bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
+    __syncthreads();
+  }
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    f32x16 init;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      init[v] = MODE == kFwd ? bias_s[wco * (BCO / WCO) + i * 32 + acc_row(v, hi)] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
   const int nchunks = (Cin + CB - 1) / CB;
@@ -276,7 +282,33 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     }
   }
 
-  // ---------------- epilogue: bias + NCHW stores ----------------
+  // ---------------- epilogue: NCHW stores ----------------
+  const int cw = co0 + wco * (BCO / WCO);  // first output channel of this wave
+  if (dst_bytes != 0 && co0 + BCO <= Cout) {
+    // Whole channel tile in range: one buffer store per accumulator element,
+    // the lane's byte offset computed once per pixel column j and the
+    // channel step a uniform (scalar) offset.  Pixels outside the image get
+    // an offset past the view and the hardware drops their stores.
+    const __amdgpu_buffer_rsrc_t dv = buffer_view(dst, dst_bytes);
+    const uint32_t plane = (uint32_t)HW * 4u;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wpx * (BM / WPX) + j * 32 + l32;
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      const uint32_t off =
+          (n < N && h < H && w < W)
+              ? (((uint32_t)n * Cout + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
+              : kOutside;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
+                        acc[i][j][v]);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int p = wpx * (BM / WPX) + j * 32 + l32;
@@ -288,12 +320,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int co = co0 + wco * (BCO / WCO) + i * 32 + acc_row(v, hi);
-        if (co < Cout) {
-          float val = acc[i][j][v];
-          if constexpr (MODE == kFwd) val += bias_s[co - co0];
-          out[(long)co * HW] = val;
-        }
+        const int co = cw + i * 32 + acc_row(v, hi);
+        if (co < Cout) out[(long)co * HW] = acc[i][j][v];
       }
     }
   }
@@ -308,12 +336,17 @@ static void launch_cfg(const Plan& pl, bool vec, const float* src, const float* 
                        hipStream_t stream) {
   constexpr int CB = 8;
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
+  // Buffer-view stores need the output below 2 GiB (32-bit byte offsets).
+  const long out_bytes = (long)N * Cout * H * W * 4;
+  const uint32_t dst_bytes = out_bytes < 2147483648L ? (uint32_t)out_bytes : 0u;
   if (vec)
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, true>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                       dst_bytes);
   else
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, false>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h);
+                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                       dst_bytes);
 }
 
 template <int MODE>

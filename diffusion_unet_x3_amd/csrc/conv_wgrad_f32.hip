@@ -36,8 +36,10 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   constexpr int PLW = wgrad_f32_plane(IMGS, TH, TW);
   constexpr int HR = TH + 2;
 
-  __shared__ float gs[64 * GS];
-  __shared__ float xs[64 * PLW];
+  // Two LDS buffers: chunk i is read from one while chunk i + 1 is written
+  // into the other.
+  __shared__ float gs_buf[2][64 * GS];
+  __shared__ float xs_buf[2][64 * PLW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -137,7 +139,9 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
 
   // Vector path: global -> registers in load_tiles (one chunk ahead),
   // registers -> LDS here.  Scalar path: everything happens here.
-  auto store_tiles = [&](int chunk) {
+  auto store_tiles = [&](int chunk, int buf) {
+    float* gs = gs_buf[buf];
+    float* xs = xs_buf[buf];
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < GV_N; ++k) {
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const int xoff = (cb * 32 + l32) * PLW + r * RSW;
 
   float a[2], b[2][3];
-  auto read_step = [&](int buf, int q2) {
+  auto read_step = [&](const float* gs, const float* xs, int buf, int q2) {
     const int p = 2 * q2 + hi;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     a[buf] = gs[goff + p];
@@ -237,27 +241,44 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     for (int s = 0; s < 3; ++s) b[buf][s] = xs[xb + s];
   };
 
-  if (chunk_begin < chunk_end) load_tiles(chunk_begin);
-  for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
-    if (chunk != chunk_begin) __syncthreads();
-    store_tiles(chunk);
+  // Chunk i is computed from LDS buffer i & 1.  Partway through its MFMA
+  // steps the registers holding chunk i + 1 are written to the other buffer
+  // (last read in iteration i - 1, before the barrier that ended it) and the
+  // global loads of chunk i + 2 are issued into them, so staging runs beside
+  // the MFMAs of waves that are still computing.  One barrier per chunk.
+  constexpr int kStoreStep = 2;
+  if (chunk_begin < chunk_end) {
+    load_tiles(chunk_begin);
+    store_tiles(chunk_begin, 0);
+    if (chunk_begin + 1 < chunk_end) load_tiles(chunk_begin + 1);
     __syncthreads();
-    if (chunk + 1 < chunk_end) load_tiles(chunk + 1);
+  }
+  for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
+    const int cur_buf = (chunk - chunk_begin) & 1;
+    const float* gs = gs_buf[cur_buf];
+    const float* xs = xs_buf[cur_buf];
     // Step q2 (two pixels) reads its operands while step q2-1's MFMAs run.
-    read_step(0, 0);
+    read_step(gs, xs, 0, 0);
 #pragma unroll
     for (int q2 = 0; q2 < P / 2; ++q2) {
       const int cur = q2 & 1;
-      if (q2 + 1 < P / 2) read_step(cur ^ 1, q2 + 1);
+      if (q2 + 1 < P / 2) read_step(gs, xs, cur ^ 1, q2 + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 3; ++s) acc[s] = mfma_32x32x2_f32(a[cur], b[cur][s], acc[s]);
+      if (q2 == kStoreStep && chunk + 1 < chunk_end) {
+        __builtin_amdgcn_sched_barrier(0);
+        store_tiles(chunk + 1, cur_buf ^ 1);
+        if (chunk + 2 < chunk_end) load_tiles(chunk + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (do_db && tid < 256) {
       const int kl = tid >> 2, part = tid & 3;
 #pragma unroll
       for (int i = 0; i < P / 4; ++i) dbsum += gs[kl * GS + part + 4 * i];
     }
+    __syncthreads();
   }
 
   // Partial dw of this slice.  Split: tap-major [tap][k][c] slot at
@@ -272,7 +293,8 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       const int k = k0 + kb * 32 + acc_row(v, hi);
       if (k < K && c < C) {
         if (slice_stride)
-          out[(long)slice * slice_stride + ((long)t * K + k) * C + c] = acc[s][v];
+          __builtin_nontemporal_store(
+              acc[s][v], &out[(long)slice * slice_stride + ((long)t * K + k) * C + c]);
         else
           out[((long)k * C + c) * 9 + t] = acc[s][v];
       }
@@ -341,6 +363,63 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   }
 }
 
+// The same epilogue with 128-bit loads, for workspaces whose slots and db
+// rows are 16-byte aligned ((K * C) % 4 == 0, K % 4 == 0 when db is
+// wanted).  Each lane owns 4 consecutive elements; eight waves each add a
+// fixed contiguous eighth of the slices in slice order, and wave 0 adds the
+// eight partial sums in wave order.
+__global__ __launch_bounds__(512) void wgrad_reduce4_kernel(const float* __restrict__ ws,
+                                                            float* __restrict__ dw,
+                                                            float* __restrict__ db, int S,
+                                                            int C, int K) {
+  __shared__ f32x4 part[8][64];
+  const long n_dw = (long)K * C * 9;
+  const long total = n_dw + (db != nullptr ? K : 0);
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const long e = ((long)blockIdx.x * 64 + lane) * 4;
+  const int per = (S + 7) / 8;
+  const int s0 = min(S, q * per), s1 = min(S, s0 + per);
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  if (e < total) {
+    const float* base;
+    long stride;
+    if (e < n_dw) {
+      base = ws + e;
+      stride = n_dw;
+    } else {
+      base = ws + (long)S * n_dw + (e - n_dw);
+      stride = K;
+    }
+    int i = s0;
+    for (; i + 8 <= s1; i += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (long)(i + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; i < s1; ++i) sum += *reinterpret_cast<const f32x4*>(base + (long)i * stride);
+  }
+  part[q][lane] = sum;
+  __syncthreads();
+  if (q == 0 && e < total) {
+    f32x4 v = part[0][lane];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) v += part[j][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long ej = e + j;
+      if (ej < n_dw) {
+        const long t = ej / ((long)K * C);
+        const long kc = ej % ((long)K * C);
+        dw[kc * 9 + t] = v[j];
+      } else {
+        db[ej - n_dw] = v[j];
+      }
+    }
+  }
+}
+
 template <int TW, int TH, int IMGS>
 static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const float* g,
                               float* out, float* out_db, long slice_stride, int N, int C, int K,
@@ -382,8 +461,15 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, 
 void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C, int K,
                          hipStream_t stream) {
   const long total = (long)K * C * 9 + (db ? K : 0);
-  dim3 grid((unsigned)((total + 63) / 64)), block(256);
-  hipLaunchKernelGGL(wgrad_reduce_kernel, grid, block, 0, stream, ws, dw, db, split, C, K);
+  const bool vec4 = ((long)K * C) % 4 == 0 && (db == nullptr || K % 4 == 0) &&
+                    (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
+  if (vec4) {
+    dim3 grid((unsigned)((total + 255) / 256)), block(512);
+    hipLaunchKernelGGL(wgrad_reduce4_kernel, grid, block, 0, stream, ws, dw, db, split, C, K);
+  } else {
+    dim3 grid((unsigned)((total + 63) / 64)), block(256);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, grid, block, 0, stream, ws, dw, db, split, C, K);
+  }
 }
 
 }  // namespace conv3x3

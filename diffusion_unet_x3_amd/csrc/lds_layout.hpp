@@ -75,8 +75,9 @@ CONV3X3_HD constexpr int wgrad_f32_rs(int tw) { return tw + 2; }
 CONV3X3_HD constexpr int wgrad_f32_plane(int imgs, int th, int tw) {
   return (imgs * (th + 2) * wgrad_f32_rs(tw)) | 1;
 }
+// Two buffers of each tile (chunk i + 1 is staged while chunk i is read).
 CONV3X3_HD constexpr int wgrad_f32_lds_bytes(int imgs, int th, int tw) {
-  return 4 * 64 * (wgrad_f32_gstride(imgs, th, tw) + wgrad_f32_plane(imgs, th, tw));
+  return 2 * 4 * 64 * (wgrad_f32_gstride(imgs, th, tw) + wgrad_f32_plane(imgs, th, tw));
 }
 
 // ---- backward-weight, bfloat16 ----
