@@ -8,25 +8,27 @@
 // lanes 0-31 supply channels 0-7 and lanes 32-63 channels 8-15 of a
 // 16-channel LDS fill.  To make the pixel operand a single 128-bit LDS read,
 // the x tile is stored channel-interleaved: one 16-byte LDS word holds 8
-// channels of one pixel ([group][img][row][col] words).  Eight lanes load
-// 8 pixels of 8 different channels with 128-bit NCHW loads and transpose the
-// 8 x 8 block among themselves with three butterfly exchanges; each lane then
-// stores one whole word and neighbouring lanes store neighbouring words, so
-// the stores are free of bank conflicts.  No global memory is transposed.
+// channels of one pixel ([group][img][row][col] words).  A lane loads an
+// 8 x 8 block (8 pixels of 8 channels, eight 128-bit NCHW row loads) and
+// transposes it in registers with byte permutes into eight words.  No global
+// memory is transposed.
 //
 // Weights, as one 16-byte word per (tap, 8-channel group, output channel):
-// the raw weight rows are first copied to LDS with coalesced 128-bit loads
-// (into the space of the x tile, which is refilled afterwards), then
-// rearranged LDS-to-LDS:
-//   forward       : w[co, c0 .. c0+15, 0..8] is one contiguous 288-byte run;
-//                   each 8-channel half is rearranged in registers into nine
-//                   tap words;
-//   backward-data : the reduction channel is k, the slowest axis of w; the
-//                   rows w[k, co0.., 0..8] are transposed in 8 x 8 blocks, with
-//                   the 180-degree tap rotation applied in the store index.
+//   forward       : w[co, c0 + 8g .. + 7, 0..8] is one contiguous, 16-byte
+//                   aligned 144-byte run; a lane loads it as nine words and
+//                   forms the nine tap words with byte permutes;
+//   backward-data : the reduction channel is k, the slowest axis of w; a lane
+//                   loads the same eight (c, tap) elements of eight rows
+//                   w[k, co0.., ..] and transposes them like the x tile, the
+//                   180-degree tap rotation applied in the store index.
 //
-// Workgroup: 4 wave64s; WCO waves split the BCO output channels and 4 / WCO
-// the pixel block; each wave holds MI x NJ 32x32 accumulators.
+// Workgroup: NW wave64s; WCO waves split the BCO output channels and
+// NW / WCO the pixel block; each wave holds MI x NJ 32x32 accumulators.  The
+// LDS tiles are double-buffered: while the MFMAs of fill i read one buffer,
+// the same waves write fill i + 1 (loaded into registers one fill ahead)
+// into the other between their MFMA groups, and issue the global loads of
+// fill i + 2.  One barrier per fill.  Forward accumulators start at the bias,
+// so the epilogue is stores only.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -36,77 +38,57 @@ namespace conv3x3 {
 
 namespace {
 
-// Low / high 16 bits of two dwords packed into one.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-// Element e (bf16) of an array of packed dwords.
-template <int E>
-__device__ __forceinline__ uint32_t elem(const uint32_t* d) {
-  return (E & 1) ? (d[E >> 1] >> 16) : (d[E >> 1] & 0xffffu);
+// Word i of the 8 x 8 transpose of eight 8-element rows r[0..7] (16-bit
+// elements): element j of the result is element i of row j.  Dword m packs
+// rows 2m and 2m + 1, picked with one byte permute.
+template <int I>
+__device__ __forceinline__ u32x4 column_word(const u32x4* r) {
+  // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0-3 pick bytes of lo,
+  // 4-7 bytes of hi; result byte b is the byte named by selector byte b.
+  constexpr uint32_t sel = (I & 1) ? 0x07060302u : 0x05040100u;
+  u32x4 v;
+  v.x = __builtin_amdgcn_perm(r[1][I >> 1], r[0][I >> 1], sel);
+  v.y = __builtin_amdgcn_perm(r[3][I >> 1], r[2][I >> 1], sel);
+  v.z = __builtin_amdgcn_perm(r[5][I >> 1], r[4][I >> 1], sel);
+  v.w = __builtin_amdgcn_perm(r[7][I >> 1], r[6][I >> 1], sel);
+  return v;
 }
 
-// 8 x 8 transpose of 16-bit elements held by 8 consecutive lanes: on entry
-// lane i (i = lane % 8) holds row i (elements 0..7 in d), on exit column i.
-// Three stages swap the off-diagonal blocks of size 4, 2 and 1.
-__device__ __forceinline__ u32x4 transpose8x8(u32x4 d, int i) {
-  {
-    const bool b = i & 4;
-    const uint32_t s0 = b ? d.x : d.z, s1 = b ? d.y : d.w;
-    const uint32_t r0 = __shfl_xor(s0, 4), r1 = __shfl_xor(s1, 4);
-    if (b) {
-      d.x = r0;
-      d.y = r1;
-    } else {
-      d.z = r0;
-      d.w = r1;
-    }
-  }
-  {
-    const bool b = i & 2;
-    const uint32_t s0 = b ? d.x : d.y, s1 = b ? d.z : d.w;
-    const uint32_t r0 = __shfl_xor(s0, 2), r1 = __shfl_xor(s1, 2);
-    if (b) {
-      d.x = r0;
-      d.z = r1;
-    } else {
-      d.y = r0;
-      d.w = r1;
-    }
-  }
-  {
-    const bool b = i & 1;
-    const uint32_t s0 = b ? pack_lo(d.x, d.y) : pack_hi(d.x, d.y);
-    const uint32_t s1 = b ? pack_lo(d.z, d.w) : pack_hi(d.z, d.w);
-    const uint32_t r0 = __shfl_xor(s0, 1), r1 = __shfl_xor(s1, 1);
-    if (b) {
-      d.x = (d.x & 0xffff0000u) | (r0 & 0xffffu);
-      d.y = (d.y & 0xffff0000u) | (r0 >> 16);
-      d.z = (d.z & 0xffff0000u) | (r1 & 0xffffu);
-      d.w = (d.w & 0xffff0000u) | (r1 >> 16);
-    } else {
-      d.x = (d.x & 0xffffu) | (r0 << 16);
-      d.y = (d.y & 0xffffu) | (r0 & 0xffff0000u);
-      d.z = (d.z & 0xffffu) | (r1 << 16);
-      d.w = (d.w & 0xffffu) | (r1 & 0xffff0000u);
-    }
-  }
-  return d;
+// Dword m (m = 0..3) of the tap-T word of a 72-element raw weight run
+// (element ci * 9 + tap, ci = 0..7): elements (2m) * 9 + T and
+// (2m + 1) * 9 + T, picked from their dwords with one byte permute.
+template <int T, int M>
+__device__ __forceinline__ uint32_t tap_dword(const uint32_t* d) {
+  constexpr int E0 = (2 * M) * 9 + T, E1 = (2 * M + 1) * 9 + T;
+  // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0-3 pick bytes of lo,
+  // 4-7 bytes of hi; result byte b is the byte named by selector byte b.
+  constexpr uint32_t sel = (uint32_t)(2 * (E0 & 1)) | (uint32_t)(2 * (E0 & 1) + 1) << 8 |
+                           (uint32_t)(4 + 2 * (E1 & 1)) << 16 |
+                           (uint32_t)(5 + 2 * (E1 & 1)) << 24;
+  return __builtin_amdgcn_perm(d[E1 >> 1], d[E0 >> 1], sel);
+}
+
+template <int T>
+__device__ __forceinline__ u32x4 tap_word(const uint32_t* d) {
+  u32x4 v;
+  v.x = tap_dword<T, 0>(d);
+  v.y = tap_dword<T, 1>(d);
+  v.z = tap_dword<T, 2>(d);
+  v.w = tap_dword<T, 3>(d);
+  return v;
 }
 
 }  // namespace
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, bool VEC>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC>
+__global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ wt,
     const float* __restrict__ bias, float* __restrict__ dst, int N, int Cin, int Cout, int H,
-    int W, int tiles_w, int tiles_h, uint32_t src_bytes, uint32_t wt_bytes) {
+    int W, int tiles_w, int tiles_h, uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes) {
+  constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
-  constexpr int WPX = 4 / WCO;
+  constexpr int WPX = NW / WCO;
   constexpr int MI = BCO / (32 * WCO);
   constexpr int NJ = BM / (32 * WPX);
   static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
@@ -114,11 +96,12 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   constexpr int RS = fwd_bf16_rs(TW);
   constexpr int HR = TH + 2;
   constexpr int PLW = fwd_bf16_plane(IMGS, TH, TW);  // words per 8-channel plane
-  constexpr int EW = BCO * 9 / 8;                    // raw weight words per reduction channel
-  constexpr int XWORDS = fwd_bf16_xregion_words(IMGS, TH, TW, BCO, VEC);
+  constexpr int XW = 2 * PLW;                        // words of one x buffer
+  constexpr int WW = 9 * 2 * BCO;                    // words of one weight buffer
+  constexpr int EW = BCO * 9 / 8;                    // raw weight words per k row (bwd-data)
 
-  __shared__ u32x4 xs[XWORDS];  // x tile; also the raw weight rows while they are staged
-  __shared__ u32x4 wa[9 * 2 * BCO];
+  __shared__ u32x4 xs[2 * XW];
+  __shared__ u32x4 wa[2 * WW];
   __shared__ float bias_s[MODE == kFwd ? BCO : 1];  // this tile's biases (0 without bias)
 
   const int tid = threadIdx.x;
@@ -129,44 +112,50 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   const int co0 = blockIdx.y * BCO;
   const long HW = (long)H * W;
 
-  // ---- vector staging (W % 8 == 0, weight channel counts % 8 == 0, 16-byte bases) ----
-  // x: item (ch, q, rr, img), ch fastest: 8 pixels of one channel.  Items
-  // come in groups of 16 = two 8-lane transpose groups, so a transpose group
-  // is always wholly inside or wholly outside the item range.
-  constexpr int XI = CB * IMGS * HR * (TW / 8);
-  constexpr int XN = (XI + 255) / 256;
-  constexpr int XH = 2 * IMGS * HR * 2;  // halo items: 8 channels x 1 pixel
-  static_assert(XH <= 256, "one halo item per thread");
-  // weights: one raw 16-byte word per item (forward: BCO runs of 18 words,
-  // backward-data: CB rows of EW words).
-  constexpr int WI = CB * EW;
-  constexpr int WN = (WI + 255) / 256;
-  constexpr int WR = WN;
-  u32x4 xr[VEC ? XN : 1];
-  u32x4 hr;
-  u32x4 wr[VEC ? WR : 1];
+  // ---- vector staging (W % 8 == 0, Cin % 16 == 0, 16-byte bases) ----
+  // Each staging thread owns one item and holds it in stg[] from its global
+  // loads (one fill ahead) until it writes it to LDS:
+  //   x item (q, rr, img, g), threads [0, XI): the 8 x 8 block of channels
+  //     c0 + 8g .. + 7 x pixels 8q .. 8q + 7 of one staged row, as eight
+  //     128-bit row loads, written as eight channel-interleaved words;
+  //   halo item, threads [0, XH): 8 channels of one halo-column pixel;
+  //   weight item, threads [NT - WI, NT): forward (co_l, g): the 144-byte run
+  //     w[co0 + co_l, c0 + 8g .. + 7, 0..8] (nine loads, nine tap words);
+  //     backward-data (g, eb): word eb of the rows w[c0 + 8g + i, co0.., ..],
+  //     i = 0..7 (eight loads, transposed into eight words of 8 k each).
+  constexpr int XI = 2 * IMGS * HR * (TW / 8);
+  constexpr int XH = 2 * IMGS * HR * 2;
+  constexpr int WI = MODE == kFwd ? 2 * BCO : 2 * EW;
+  constexpr int W0 = NT - WI;
+  static_assert(XI <= W0 && XH <= NT, "one staging item per thread");
+  constexpr int NSTG = MODE == kFwd ? 9 : 8;
+  const bool xrole = tid < XI, hrole = tid < XH, wrole = tid >= W0;
 
-  // Vector path (host guarantees Cin % 16 == 0, so every fill is whole):
-  // each staged item's byte offset is computed once; a fill only adds the
-  // channel step, and items outside the tensors hold kOutside and read zero.
+  u32x4 stg[VEC ? NSTG : 1];
+  u32x4 hr = {0u, 0u, 0u, 0u};
+
+  // Byte offsets, computed once; a fill adds the channel step.  Items
+  // outside the tensors hold kOutside and read zero.
   const __amdgpu_buffer_rsrc_t sv = buffer_view(src, src_bytes);
   const __amdgpu_buffer_rsrc_t wv = buffer_view(wt, wt_bytes);
-  uint32_t xoff[VEC ? XN : 1], hoff = kOutside, woff[VEC ? WN : 1];
+  const uint32_t hw2 = 2u * (uint32_t)(H * W);
+  uint32_t xoff = kOutside, hoff = kOutside, woff = kOutside;
+  int xdst = 0;  // LDS word of the x item's first pixel
   if constexpr (VEC) {
-#pragma unroll
-    for (int k = 0; k < XN; ++k) {
-      const int it = tid + 256 * k;
-      const int ch = it & 15;
-      int t = it >> 4;
+    if (xrole) {
+      int t = tid;
       const int q = t % (TW / 8);
       t /= TW / 8;
       const int rr = t % HR;
-      const int img = t / HR;
+      t /= HR;
+      const int img = t % IMGS;
+      const int g = t / IMGS;
       const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
-      const bool ok = (XI % 256 == 0 || it < XI) && n < N && h >= 0 && h < H && w < W;
-      xoff[k] = ok ? 2u * (uint32_t)(((n * Cin + ch) * H + h) * W + w) : kOutside;
+      if (n < N && h >= 0 && h < H && w < W)
+        xoff = 2u * (uint32_t)(((n * Cin + 8 * g) * H + h) * W + w);
+      xdst = g * PLW + (img * HR + rr) * RS + 4 + 8 * q;
     }
-    if (tid < XH) {
+    if (hrole) {
       const int side = tid & 1;
       int t = tid >> 1;
       const int rr = t % HR;
@@ -177,193 +166,148 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       if (n < N && h >= 0 && h < H && w >= 0 && w < W)
         hoff = 2u * (uint32_t)(((n * Cin + 8 * g) * H + h) * W + w);
     }
-#pragma unroll
-    for (int k = 0; k < WN; ++k) {
-      const int it = tid + 256 * k;
-      bool ok;
-      uint32_t e;
+    if (wrole) {
+      const int it = tid - W0;
       if constexpr (MODE == kFwd) {
-        const int run = it / 18, piece = it % 18;  // 18 words per output channel
-        ok = (WI % 256 == 0 || it < WI) && co0 + run < Cout;
-        e = (uint32_t)(((co0 + run) * Cin) * 9 + 8 * piece);
+        const int co_l = it >> 1, g = it & 1;
+        if (co0 + co_l < Cout) woff = 2u * (uint32_t)(((co0 + co_l) * Cin + 8 * g) * 9);
       } else {
-        const int kl = it / EW, e8 = it % EW;
-        ok = (WI % 256 == 0 || it < WI) && 8 * e8 < (Cout - co0) * 9;
-        e = (uint32_t)((kl * Cout + co0) * 9 + 8 * e8);
+        const int g = it / EW, eb = it % EW;
+        if (8 * eb < (Cout - co0) * 9)
+          woff = 2u * (uint32_t)(((8 * g) * Cout + co0) * 9 + 8 * eb);
       }
-      woff[k] = ok ? 2u * e : kOutside;
     }
   }
-  const uint32_t hw2 = 2u * (uint32_t)(H * W);
-  // bytes between consecutive fills: 16 channels of the source, and of w
+  // bytes between consecutive fills: 16 channels of the source, and of w;
+  // bytes between the rows of a backward-data weight item
   const uint32_t xstep = 16u * hw2;
   const uint32_t wstep = MODE == kFwd ? 2u * 16u * 9u : 2u * 16u * 9u * (uint32_t)Cout;
+  const uint32_t wrow = 2u * 9u * (uint32_t)Cout;
 
   auto load_tiles = [&](int c0) {
-    if constexpr (VEC) {
-      const uint32_t f = (uint32_t)(c0 / 16);
+    const uint32_t f = (uint32_t)(c0 / 16);
+    if (xrole) {
 #pragma unroll
-      for (int k = 0; k < XN; ++k) xr[k] = buffer_load16(sv, xoff[k] + f * xstep);
-      {
-        uint32_t v[8];
+      for (int i = 0; i < 8; ++i) stg[i] = buffer_load16(sv, xoff + f * xstep + (uint32_t)i * hw2);
+    }
+    if (hrole) {
+      uint32_t v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = buffer_load2(sv, hoff + f * xstep + (uint32_t)i * hw2);
-        hr.x = v[0] | (v[1] << 16);
-        hr.y = v[2] | (v[3] << 16);
-        hr.z = v[4] | (v[5] << 16);
-        hr.w = v[6] | (v[7] << 16);
+      for (int i = 0; i < 8; ++i) v[i] = buffer_load2(sv, hoff + f * xstep + (uint32_t)i * hw2);
+      hr.x = v[0] | (v[1] << 16);
+      hr.y = v[2] | (v[3] << 16);
+      hr.z = v[4] | (v[5] << 16);
+      hr.w = v[6] | (v[7] << 16);
+    }
+    if (wrole) {
+      if constexpr (MODE == kFwd) {
+#pragma unroll
+        for (int j = 0; j < 9; ++j) stg[j] = buffer_load16(wv, woff + f * wstep + 16u * (uint32_t)j);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) stg[i] = buffer_load16(wv, woff + f * wstep + (uint32_t)i * wrow);
       }
-#pragma unroll
-      for (int k = 0; k < WN; ++k) wr[k] = buffer_load16(wv, woff[k] + f * wstep);
     }
   };
 
-  auto store_x = [&]() {
-#pragma unroll
-    for (int k = 0; k < XN; ++k) {
-      const int it = tid + 256 * k;
-      const u32x4 v = transpose8x8(xr[k], lane & 7);  // all lanes take part
-      if (XI % 256 == 0 || it < XI) {
-        const int ch = it & 15;
-        int t = it >> 4;
-        const int q = t % (TW / 8);
-        t /= TW / 8;  // img * HR + rr
-        xs[(ch >> 3) * PLW + t * RS + 4 + 8 * q + (ch & 7)] = v;
-      }
+  auto store_tiles = [&](int buf) {
+    if (xrole) {
+      u32x4* d = xs + buf * XW + xdst;
+      d[0] = column_word<0>(stg);
+      d[1] = column_word<1>(stg);
+      d[2] = column_word<2>(stg);
+      d[3] = column_word<3>(stg);
+      d[4] = column_word<4>(stg);
+      d[5] = column_word<5>(stg);
+      d[6] = column_word<6>(stg);
+      d[7] = column_word<7>(stg);
     }
-    if (tid < XH) {
+    if (hrole) {
       const int side = tid & 1;
       const int t = tid >> 1;  // (g * IMGS + img) * HR + rr
       const int g = t / (IMGS * HR);
-      xs[g * PLW + (t % (IMGS * HR)) * RS + 4 + (side ? TW : -1)] = hr;
+      xs[buf * XW + g * PLW + (t % (IMGS * HR)) * RS + 4 + (side ? TW : -1)] = hr;
+    }
+    if (wrole) {
+      u32x4* wb = wa + buf * WW;
+      const int it = tid - W0;
+      if constexpr (MODE == kFwd) {
+        const int co_l = it >> 1, g = it & 1;
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(stg);
+        wb[(0 * 2 + g) * BCO + co_l] = tap_word<0>(d);
+        wb[(1 * 2 + g) * BCO + co_l] = tap_word<1>(d);
+        wb[(2 * 2 + g) * BCO + co_l] = tap_word<2>(d);
+        wb[(3 * 2 + g) * BCO + co_l] = tap_word<3>(d);
+        wb[(4 * 2 + g) * BCO + co_l] = tap_word<4>(d);
+        wb[(5 * 2 + g) * BCO + co_l] = tap_word<5>(d);
+        wb[(6 * 2 + g) * BCO + co_l] = tap_word<6>(d);
+        wb[(7 * 2 + g) * BCO + co_l] = tap_word<7>(d);
+        wb[(8 * 2 + g) * BCO + co_l] = tap_word<8>(d);
+      } else {
+        // column i: element e = 8 eb + i (= co_l * 9 + tap of the stored,
+        // unrotated weight) of rows 8g .. 8g + 7
+        const int g = it / EW, eb = it % EW;
+        auto put = [&](int i, u32x4 v) {
+          const int e = 8 * eb + i;
+          wb[((8 - e % 9) * 2 + g) * BCO + e / 9] = v;
+        };
+        put(0, column_word<0>(stg));
+        put(1, column_word<1>(stg));
+        put(2, column_word<2>(stg));
+        put(3, column_word<3>(stg));
+        put(4, column_word<4>(stg));
+        put(5, column_word<5>(stg));
+        put(6, column_word<6>(stg));
+        put(7, column_word<7>(stg));
+      }
     }
   };
 
-  auto store_tiles = [&](int c0) {
-    if constexpr (VEC) {
-      // Raw weight words into the x region, rearranged into wa, then the x tile.
-#pragma unroll
-      for (int k = 0; k < WN; ++k) {
-        const int it = tid + 256 * k;
-        if (WI % 256 == 0 || it < WI) xs[it] = wr[k];
-      }
-      __syncthreads();
-      if constexpr (MODE == kFwd) {
-        // Item (co_l, gq), gq fastest: words 9 * it .. 9 * it + 8 hold
-        // w[co0 + co_l, c0 + 8 gq .. + 7, 0..8] as e = ci * 9 + t.
-#pragma unroll
-        for (int k = 0; k < (2 * BCO + 255) / 256; ++k) {
-          const int it = tid + 256 * k;
-          if ((2 * BCO) % 256 == 0 || it < 2 * BCO) {
-            const int co_l = it >> 1, gq = it & 1;
-            u32x4 raw[9];
-#pragma unroll
-            for (int i = 0; i < 9; ++i) raw[i] = xs[9 * it + i];
-            const uint32_t* d = reinterpret_cast<const uint32_t*>(raw);
-            // word for tap t: channels (2q, 2q+1) -> elements 2q*9+t and (2q+1)*9+t
-#define CONV3X3_WWORD(T)                                                   \
-  {                                                                       \
-    u32x4 v;                                                              \
-    v.x = elem<0 * 9 + T>(d) | (elem<1 * 9 + T>(d) << 16);                \
-    v.y = elem<2 * 9 + T>(d) | (elem<3 * 9 + T>(d) << 16);                \
-    v.z = elem<4 * 9 + T>(d) | (elem<5 * 9 + T>(d) << 16);                \
-    v.w = elem<6 * 9 + T>(d) | (elem<7 * 9 + T>(d) << 16);                \
-    wa[((T) * 2 + gq) * BCO + co_l] = v;                                  \
-  }
-            CONV3X3_WWORD(0)
-            CONV3X3_WWORD(1)
-            CONV3X3_WWORD(2)
-            CONV3X3_WWORD(3)
-            CONV3X3_WWORD(4)
-            CONV3X3_WWORD(5)
-            CONV3X3_WWORD(6)
-            CONV3X3_WWORD(7)
-            CONV3X3_WWORD(8)
-#undef CONV3X3_WWORD
-          }
-        }
-        __syncthreads();
-        store_x();
-      } else {
-        // 8 x 8 transpose: 8 reduction channels (k) x 8 consecutive (co, tap)
-        // elements of the raw rows -> 8 words of 8 k each.
-        constexpr int TI = 2 * EW;
-#pragma unroll
-        for (int k = 0; k < (TI + 255) / 256; ++k) {
-          const int it = tid + 256 * k;
-          if (TI % 256 == 0 || it < TI) {
-            const int g = it / EW, eb = it % EW;
-            u32x4 in[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) in[j] = xs[(8 * g + j) * EW + eb];
-#pragma unroll
-            for (int ei = 0; ei < 8; ++ei) {
-              const int dw = ei >> 1;
-              u32x4 v;
-              if (ei & 1) {
-                v.x = pack_hi(in[0][dw], in[1][dw]);
-                v.y = pack_hi(in[2][dw], in[3][dw]);
-                v.z = pack_hi(in[4][dw], in[5][dw]);
-                v.w = pack_hi(in[6][dw], in[7][dw]);
-              } else {
-                v.x = pack_lo(in[0][dw], in[1][dw]);
-                v.y = pack_lo(in[2][dw], in[3][dw]);
-                v.z = pack_lo(in[4][dw], in[5][dw]);
-                v.w = pack_lo(in[6][dw], in[7][dw]);
-              }
-              const int e = 8 * eb + ei;  // co_l * 9 + tap of the stored (unrotated) weight
-              wa[((8 - e % 9) * 2 + g) * BCO + e / 9] = v;
-            }
-          }
-        }
-        __syncthreads();
-        store_x();
-      }
-    } else {
-      // Scalar path (ragged shapes): 16-bit loads straight into LDS.
-      uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
-      uint16_t* wh = reinterpret_cast<uint16_t*>(wa);
-      constexpr int XS = CB * IMGS * HR * (TW + 2);
+  // Scalar path (ragged shapes): 16-bit loads straight into LDS buffer buf.
+  auto fill_scalar = [&](int c0, int buf) {
+    uint16_t* xh = reinterpret_cast<uint16_t*>(xs + buf * XW);
+    uint16_t* wh = reinterpret_cast<uint16_t*>(wa + buf * WW);
+    constexpr int XS = CB * IMGS * HR * (TW + 2);
 #pragma unroll 4
-      for (int k = 0; k < (XS + 255) / 256; ++k) {
-        const int it = tid + 256 * k;
-        if (XS % 256 == 0 || it < XS) {
-          const int cc = it % (TW + 2) - 1;
-          const int t = it / (TW + 2);  // (ch * IMGS + img) * HR + rr
-          const int rr = t % HR;
-          const int img = (t / HR) % IMGS;
-          const int ch = t / (HR * IMGS);
-          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + cc;
-          uint16_t v = 0;
-          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
-            v = src[((long)n * Cin + c) * HW + (long)h * W + w];
-          xh[((ch >> 3) * PLW + (img * HR + rr) * RS + 4 + cc) * 8 + (ch & 7)] = v;
-        }
-      }
-      constexpr int WS = CB * 9 * BCO;
-#pragma unroll 4
-      for (int k = 0; k < WS / 256; ++k) {
-        const int it = tid + 256 * k;
-        int ci_l, co_l, tap;
+    for (int k = 0; k < (XS + NT - 1) / NT; ++k) {
+      const int it = tid + NT * k;
+      if (XS % NT == 0 || it < XS) {
+        const int cc = it % (TW + 2) - 1;
+        const int t = it / (TW + 2);  // (ch * IMGS + img) * HR + rr
+        const int rr = t % HR;
+        const int img = (t / HR) % IMGS;
+        const int ch = t / (HR * IMGS);
+        const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + cc;
         uint16_t v = 0;
-        if constexpr (MODE == kFwd) {
-          co_l = it / (CB * 9);
-          const int e = it % (CB * 9);
-          ci_l = e / 9;
-          tap = e % 9;
-          const int co = co0 + co_l, ci = c0 + ci_l;
-          if (co < Cout && ci < Cin) v = wt[((long)co * Cin + ci) * 9 + tap];
-        } else {
-          ci_l = it / (BCO * 9);
-          const int e = it % (BCO * 9);
-          co_l = e / 9;
-          const int tg = e % 9;
-          tap = 8 - tg;
-          const int co = co0 + co_l, ci = c0 + ci_l;
-          if (co < Cout && ci < Cin) v = wt[((long)ci * Cout + co) * 9 + tg];
-        }
-        wh[((tap * 2 + (ci_l >> 3)) * BCO + co_l) * 8 + (ci_l & 7)] = v;
+        if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
+          v = src[((long)n * Cin + c) * HW + (long)h * W + w];
+        xh[((ch >> 3) * PLW + (img * HR + rr) * RS + 4 + cc) * 8 + (ch & 7)] = v;
       }
+    }
+    constexpr int WSI = CB * 9 * BCO;
+#pragma unroll 4
+    for (int k = 0; k < (WSI + NT - 1) / NT; ++k) {
+      const int it = tid + NT * k;
+      if (WSI % NT != 0 && it >= WSI) continue;
+      int ci_l, co_l, tap;
+      uint16_t v = 0;
+      if constexpr (MODE == kFwd) {
+        co_l = it / (CB * 9);
+        const int e = it % (CB * 9);
+        ci_l = e / 9;
+        tap = e % 9;
+        const int co = co0 + co_l, ci = c0 + ci_l;
+        if (co < Cout && ci < Cin) v = wt[((long)co * Cin + ci) * 9 + tap];
+      } else {
+        ci_l = it / (BCO * 9);
+        const int e = it % (BCO * 9);
+        co_l = e / 9;
+        const int tg = e % 9;
+        tap = 8 - tg;
+        const int co = co0 + co_l, ci = c0 + ci_l;
+        if (co < Cout && ci < Cin) v = wt[((long)ci * Cout + co) * 9 + tg];
+      }
+      wh[((tap * 2 + (ci_l >> 3)) * BCO + co_l) * 8 + (ci_l & 7)] = v;
     }
   };
 
@@ -376,51 +320,100 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   }
   const int aoff = hi * BCO + wco * (BCO / WCO) + l32;
 
-  f32x16 acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  u32x4 a[2][MI], b[2][NJ];
-  auto read_tap = [&](int buf, int t) {
-    const int r = t / 3, s = t % 3;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) a[buf][i] = wa[aoff + t * 2 * BCO + i * 32];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + r * RS + s];
-  };
-
+  // Forward: the accumulators start at the tile's biases (zero without
+  // bias), so the epilogue is stores only.
   if constexpr (MODE == kFwd) {
-    // Visible to the epilogue through the chunk loop's barriers.
-    for (int i = tid; i < BCO; i += 256)
+    for (int i = tid; i < BCO; i += NT)
       bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
   }
-
   const int nchunks = (Cin + CB - 1) / CB;
-  load_tiles(0);
+  if constexpr (VEC) {
+    load_tiles(0);
+    store_tiles(0);
+    if (nchunks > 1) load_tiles(CB);
+  } else {
+    fill_scalar(0, 0);
+  }
+  __syncthreads();
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    f32x16 init;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      init[v] = MODE == kFwd ? bias_s[wco * (BCO / WCO) + i * 32 + acc_row(v, hi)] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = init;
+  }
+
+  u32x4 a[2][MI], b[2][NJ];
   for (int chunk = 0; chunk < nchunks; ++chunk) {
-    if (chunk) __syncthreads();
-    store_tiles(chunk * CB);
-    __syncthreads();
-    if (chunk + 1 < nchunks) load_tiles((chunk + 1) * CB);
-    // Tap t's operands are read while tap t-1's MFMAs run.
+    const int cur = chunk & 1;
+    const u32x4* xb = xs + cur * XW;
+    const u32x4* wb = wa + cur * WW;
+    const bool next = chunk + 1 < nchunks;
+    auto read_tap = [&](int rb, int t) {
+      const int r = t / 3, s = t % 3;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[rb][i] = wb[aoff + t * 2 * BCO + i * 32];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[rb][j] = xb[boff[j] + r * RS + s];
+    };
+    // Tap t's operands are read while tap t-1's MFMAs run.  The next fill
+    // is written to the other buffer after tap 0 (that buffer was last read
+    // before the barrier ending the previous fill), and the loads of the
+    // fill after it are issued after tap 1.
     read_tap(0, 0);
 #pragma unroll
     for (int t = 0; t < 9; ++t) {
-      const int cur = t & 1;
-      if (t + 1 < 9) read_tap(cur ^ 1, t + 1);
+      const int rb = t & 1;
+      if (t + 1 < 9) read_tap(rb ^ 1, t + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = mfma_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j]);
+          acc[i][j] = mfma_32x32x16_bf16(a[rb][i], b[rb][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (VEC) {
+        if (t == 0 && next) store_tiles(cur ^ 1);
+        if (t == 1 && chunk + 2 < nchunks) load_tiles((chunk + 2) * CB);
+      } else {
+        if (t == 0 && next) fill_scalar((chunk + 1) * CB, cur ^ 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __syncthreads();
   }
 
+  // ---------------- epilogue: NCHW stores ----------------
+  const int cw = co0 + wco * (BCO / WCO);  // first output channel of this wave
+  if (dst_bytes != 0 && co0 + BCO <= Cout) {
+    // Whole channel tile in range: one buffer store per accumulator element,
+    // the lane's byte offset computed once per pixel column j and the channel
+    // step a uniform (scalar) offset.  Pixels outside the image get an offset
+    // past the view and the hardware drops their stores.
+    const __amdgpu_buffer_rsrc_t dv = buffer_view(dst, dst_bytes);
+    const uint32_t plane = (uint32_t)HW * 4u;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wpx * (BM / WPX) + j * 32 + l32;
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      const uint32_t off =
+          (n < N && h < H && w < W)
+              ? (((uint32_t)n * Cout + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
+              : kOutside;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
+                        acc[i][j][v]);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int p = wpx * (BM / WPX) + j * 32 + l32;
@@ -432,46 +425,46 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int co = co0 + wco * (BCO / WCO) + i * 32 + acc_row(v, hi);
-        if (co < Cout) {
-          float val = acc[i][j][v];
-          if constexpr (MODE == kFwd) val += bias_s[co - co0];
-          out[(long)co * HW] = val;
-        }
+        const int co = cw + i * 32 + acc_row(v, hi);
+        if (co < Cout) out[(long)co * HW] = acc[i][j][v];
       }
     }
   }
 }
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
 static void launch_bf16_cfg(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
                             const float* bias, float* dst, int N, int Cin, int Cout, int H,
                             int W, hipStream_t stream) {
-  dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
+  dim3 grid(pl.grid_x, pl.grid_y, 1), block(64 * NW, 1, 1);
+  // Buffer-view stores need the output below 2 GiB (32-bit byte offsets).
+  const long out_bytes = (long)N * Cout * H * W * 4;
+  const uint32_t dst_bytes = out_bytes < 2147483648L ? (uint32_t)out_bytes : 0u;
   if (vec)
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, true>), grid, block, 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       (uint32_t)((long)N * Cin * H * W * 2), (uint32_t)((long)Cin * Cout * 9 * 2));
+                       (uint32_t)((long)N * Cin * H * W * 2), (uint32_t)((long)Cin * Cout * 9 * 2),
+                       dst_bytes);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, false>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u,
-                       0u);
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false>), grid, block,
+                       0, stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                       0u, 0u, dst_bytes);
 }
 
 bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
                      const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
                      hipStream_t stream) {
   if (pl.chunk != 16) return false;
-#define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                                 \
-  if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                \
-      pl.wave_co == WCO_) {                                                                   \
-    if (pl.pass == kFwd)                                                                      \
-      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin,  \
-                                                        Cout, H, W, stream);                  \
-    else                                                                                      \
-      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, nullptr, dst, N, \
-                                                            Cin, Cout, H, W, stream);         \
-    return true;                                                                              \
+#define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_, NW_)                                              \
+  if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                  \
+      pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \
+    if (pl.pass == kFwd)                                                                        \
+      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, bias, dst, N,    \
+                                                             Cin, Cout, H, W, stream);          \
+    else                                                                                        \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, nullptr, dst, \
+                                                                 N, Cin, Cout, H, W, stream);   \
+    return true;                                                                                \
   }
   CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)
 #undef CONV3X3_X

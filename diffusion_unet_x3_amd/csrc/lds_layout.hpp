@@ -10,7 +10,8 @@
 //            stores free of bank conflicts).
 //
 // Forward / backward-data, bfloat16 (MFMA 32x32x16, each lane supplies 8
-// consecutive input channels at one tap; 16-channel fills):
+// consecutive input channels at one tap; 16-channel fills; both tiles are
+// double-buffered):
 //   x tile : [2][plane] words, a plane = [imgs][th + 2][RS] 16-byte words,
 //            one word = 8 channels of one pixel, so the MFMA operand is a
 //            single 128-bit LDS read; RS = tw + 8, image column cc at 4 + cc.
@@ -56,17 +57,9 @@ CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw + 8; }
 CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {
   return imgs * (th + 2) * fwd_bf16_rs(tw) + ((8 - (imgs * (th + 2) * fwd_bf16_rs(tw)) % 16) + 16) % 16;
 }
-// Words of the x region: the x tile (two 8-channel planes), or the raw
-// weight rows (16 channels x co_tile x 9 bf16) staged there before being
-// rearranged (vector path), whichever is larger.
-CONV3X3_HD constexpr int fwd_bf16_xregion_words(int imgs, int th, int tw, int co_tile,
-                                                bool raw_weights) {
-  return (raw_weights && 16 * co_tile * 9 / 8 > 2 * fwd_bf16_plane(imgs, th, tw))
-             ? 16 * co_tile * 9 / 8
-             : 2 * fwd_bf16_plane(imgs, th, tw);
-}
+// Two buffers of the x tile (two 8-channel planes) and of the weight tile.
 CONV3X3_HD constexpr int fwd_bf16_lds_bytes(int imgs, int th, int tw, int co_tile) {
-  return 16 * (fwd_bf16_xregion_words(imgs, th, tw, co_tile, true) + 9 * 2 * co_tile);
+  return 2 * 16 * (2 * fwd_bf16_plane(imgs, th, tw) + 9 * 2 * co_tile);
 }
 
 // ---- backward-weight, float32 ----

@@ -14,15 +14,18 @@ struct Block {
   int tw, th, imgs;
 };
 
-bool fwd_cfg_exists(int dtype, const Block& b, int co, int wco) {
-#define CONV3X3_X(TW, TH, IMGS, CO, WCO) \
-  if (b.tw == TW && b.th == TH && b.imgs == IMGS && co == CO && wco == WCO) return true;
+bool fwd_cfg_exists(int dtype, const Block& b, int co, int wco, int nw) {
+#define CONV3X3_X5(TW, TH, IMGS, CO, WCO) \
+  if (b.tw == TW && b.th == TH && b.imgs == IMGS && co == CO && wco == WCO && nw == 4) return true;
+#define CONV3X3_X6(TW, TH, IMGS, CO, WCO, NW) \
+  if (b.tw == TW && b.th == TH && b.imgs == IMGS && co == CO && wco == WCO && nw == NW) return true;
   if (dtype == kF32) {
-    CONV3X3_FWD_F32_CONFIGS(CONV3X3_X)
+    CONV3X3_FWD_F32_CONFIGS(CONV3X3_X5)
   } else {
-    CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)
+    CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X6)
   }
-#undef CONV3X3_X
+#undef CONV3X3_X5
+#undef CONV3X3_X6
   return false;
 }
 
@@ -85,22 +88,22 @@ bool plan(const Problem& p, Plan* out) {
     // Candidate workgroup tiles, preferred first: (pixels, channels, waves
     // along channels).
     struct Cand {
-      int bm, co, wco;
+      int bm, co, wco, nw;
     };
     Cand cands[3];
     int ncand;
     if (p.dtype == kF32) {
-      cands[0] = cout <= 64 ? Cand{256, 64, 1} : Cand{128, 128, 2};
-      cands[1] = Cand{64, 64, 2};
+      cands[0] = cout <= 64 ? Cand{256, 64, 1, 4} : Cand{128, 128, 2, 4};
+      cands[1] = Cand{64, 64, 2, 4};
       ncand = 2;
     } else if (cout > 64) {
-      cands[0] = Cand{256, 128, 2};
-      cands[1] = Cand{128, 64, 2};
-      cands[2] = Cand{64, 64, 2};
+      cands[0] = Cand{256, 128, 2, 8};
+      cands[1] = Cand{128, 64, 2, 4};
+      cands[2] = Cand{64, 64, 2, 4};
       ncand = 3;
     } else {
-      cands[0] = Cand{128, 64, 2};
-      cands[1] = Cand{64, 64, 2};
+      cands[0] = Cand{128, 64, 2, 4};
+      cands[1] = Cand{64, 64, 2, 4};
       ncand = 2;
     }
     // Take the first candidate that fills the device without wasting much of
@@ -112,12 +115,12 @@ bool plan(const Problem& p, Plan* out) {
     double best_eff = 0.0;
     for (int i = 0; i < ncand; ++i) {
       Block b = pick_block(cands[i].bm, p.H, p.W);
-      if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco))
+      if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco, cands[i].nw))
         b = Block{b.tw, cands[i].bm / b.tw, 1};
       blks[i] = b;
       eff[i] = 0.0;
       wgs[i] = 0;
-      if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco)) continue;
+      if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco, cands[i].nw)) continue;
       wgs[i] = blocks_of(b, p.N, p.H, p.W) * ceil_div(cout, cands[i].co);
       eff[i] = (double)p.N * p.H * p.W * cout / ((double)wgs[i] * cands[i].bm * cands[i].co);
       if (eff[i] > best_eff) best_eff = eff[i];
@@ -142,7 +145,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.grid_x = pl.tiles_n * pl.tiles_h * pl.tiles_w;
     pl.grid_y = ceil_div(cout, pl.tile_co);
     pl.grid_z = 1;
-    pl.threads = 256;
+    pl.threads = 64 * cands[pick].nw;
     pl.lds_bytes = p.dtype == kF32
         ? fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
         : fwd_bf16_lds_bytes(pl.imgs, pl.th, pl.tw, pl.tile_co);

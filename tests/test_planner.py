@@ -25,7 +25,7 @@ def test_forward_type_plans_cover_problem(shape, dtype):
         assert p["grid_x"] == tiles
         assert p["grid_y"] * p["tile_m"] >= cout > (p["grid_y"] - 1) * p["tile_m"]
         assert 0 < p["lds_bytes"] <= LDS_PER_CU
-        assert p["threads"] == 256 and p["split"] == 1 and p["workspace_bytes"] == 0
+        assert p["threads"] in (256, 512) and p["split"] == 1 and p["workspace_bytes"] == 0
 
 
 @pytest.mark.parametrize("shape", SHAPES)
