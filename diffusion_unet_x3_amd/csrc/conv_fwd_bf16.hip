@@ -115,11 +115,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // ---- vector staging (W % 8 == 0, Cin % 16 == 0, 16-byte bases) ----
   // Each staging thread owns one item and holds it in stg[] from its global
   // loads (one fill ahead) until it writes it to LDS:
-  //   x item (q, rr, img, g), threads [0, XI): the 8 x 8 block of channels
+  //   x item (rr, q, img, g), threads [0, XI): the 8 x 8 block of channels
   //     c0 + 8g .. + 7 x pixels 8q .. 8q + 7 of one staged row, as eight
   //     128-bit row loads, written as eight channel-interleaved words;
   //   halo item, threads [0, XH): 8 channels of one halo-column pixel;
-  //   weight item, threads [NT - WI, NT): forward (co_l, g): the 144-byte run
+  //   weight item, threads [NT - WI, NT): forward (co_l, g), co_l fastest:
+  //     the 144-byte run
   //     w[co0 + co_l, c0 + 8g .. + 7, 0..8] (nine loads, nine tap words);
   //     backward-data (g, eb): word eb of the rows w[c0 + 8g + i, co0.., ..],
   //     i = 0..7 (eight loads, transposed into eight words of 8 k each).
@@ -143,11 +144,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   int xdst = 0;  // LDS word of the x item's first pixel
   if constexpr (VEC) {
     if (xrole) {
+      // rows fastest: with the odd row stride, 16 consecutive lanes write
+      // 16 different bank groups
       int t = tid;
-      const int q = t % (TW / 8);
-      t /= TW / 8;
       const int rr = t % HR;
       t /= HR;
+      const int q = t % (TW / 8);
+      t /= TW / 8;
       const int img = t % IMGS;
       const int g = t / IMGS;
       const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     if (wrole) {
       const int it = tid - W0;
       if constexpr (MODE == kFwd) {
-        const int co_l = it >> 1, g = it & 1;
+        const int co_l = it % BCO, g = it / BCO;  // consecutive lanes: consecutive co
         if (co0 + co_l < Cout) woff = 2u * (uint32_t)(((co0 + co_l) * Cin + 8 * g) * 9);
       } else {
         const int g = it / EW, eb = it % EW;
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       u32x4* wb = wa + buf * WW;
       const int it = tid - W0;
       if constexpr (MODE == kFwd) {
-        const int co_l = it >> 1, g = it & 1;
+        const int co_l = it % BCO, g = it / BCO;
         const uint32_t* d = reinterpret_cast<const uint32_t*>(stg);
         wb[(0 * 2 + g) * BCO + co_l] = tap_word<0>(d);
         wb[(1 * 2 + g) * BCO + co_l] = tap_word<1>(d);
@@ -347,28 +350,36 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
+  // Operands of one tap: a = weights (MI words), b = pixels (NJ words).
   u32x4 a[2][MI], b[2][NJ];
+  auto read_tap = [&](int cbuf, int rb, int t) {
+    const u32x4* xb = xs + cbuf * XW;
+    const u32x4* wb = wa + cbuf * WW;
+    const int r = t / 3, s = t % 3;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[rb][i] = wb[aoff + t * 2 * BCO + i * 32];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[rb][j] = xb[boff[j] + r * RS + s];
+  };
+  // Tap t's operands are read while tap t-1's MFMAs run.  The next fill is
+  // written to the other buffer after tap 0 (that buffer was last read
+  // before the previous fill's barrier), and the loads of the fill after it
+  // are issued after tap 1.  The barrier sits before tap 8's MFMAs: by then
+  // every lane has written the next fill and read its last operands of
+  // this one, so tap 0 of the next fill is read while tap 8 runs.
+  read_tap(0, 0, 0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     const int cur = chunk & 1;
-    const u32x4* xb = xs + cur * XW;
-    const u32x4* wb = wa + cur * WW;
     const bool next = chunk + 1 < nchunks;
-    auto read_tap = [&](int rb, int t) {
-      const int r = t / 3, s = t % 3;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) a[rb][i] = wb[aoff + t * 2 * BCO + i * 32];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) b[rb][j] = xb[boff[j] + r * RS + s];
-    };
-    // Tap t's operands are read while tap t-1's MFMAs run.  The next fill
-    // is written to the other buffer after tap 0 (that buffer was last read
-    // before the barrier ending the previous fill), and the loads of the
-    // fill after it are issued after tap 1.
-    read_tap(0, 0);
 #pragma unroll
     for (int t = 0; t < 9; ++t) {
       const int rb = t & 1;
-      if (t + 1 < 9) read_tap(rb ^ 1, t + 1);
+      if (t + 1 < 9) {
+        read_tap(cur, rb ^ 1, t + 1);
+      } else if (next) {
+        __syncthreads();
+        read_tap(cur ^ 1, rb ^ 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -384,7 +395,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+    // tap 0 of the next fill was read into the second operand set
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[0][i] = a[1][i];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[0][j] = b[1][j];
   }
 
   // ---------------- epilogue: NCHW stores ----------------

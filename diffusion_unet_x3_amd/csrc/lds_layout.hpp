@@ -14,7 +14,8 @@
 // double-buffered):
 //   x tile : [2][plane] words, a plane = [imgs][th + 2][RS] 16-byte words,
 //            one word = 8 channels of one pixel, so the MFMA operand is a
-//            single 128-bit LDS read; RS = tw + 8, image column cc at 4 + cc.
+//            single 128-bit LDS read; RS = tw + 9 (24 for tw = 8), image column cc
+//            at 4 + cc.
 //   w tile : [9][2][co_tile] words (8 input channels of one tap and output
 //            channel).
 //
@@ -53,7 +54,12 @@ CONV3X3_HD constexpr int fwd_f32_lds_bytes(int cb, int imgs, int th, int tw, int
 // Plane of one 8-channel group, in 16-byte words, padded to 8 mod 16 words
 // so that the two groups' words written by one transpose step fall in
 // different banks.
-CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw + 8; }
+// Row stride in words.  tw >= 16: odd, so that the staging lanes, which
+// write rows-fastest, put 16 consecutive rows in 16 different bank groups
+// (the MFMA operand reads cover whole 16-word runs of one row either way).
+// tw = 8: 24 (8 mod 16), so that the operand reads of two consecutive rows by
+// one 16-lane group fall in disjoint bank halves.
+CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw == 8 ? 24 : tw + 9; }
 CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {
   return imgs * (th + 2) * fwd_bf16_rs(tw) + ((8 - (imgs * (th + 2) * fwd_bf16_rs(tw)) % 16) + 16) % 16;
 }
