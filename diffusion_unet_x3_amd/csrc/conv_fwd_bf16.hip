@@ -22,12 +22,16 @@
 //                   w[k, co0.., ..] and transposes them like the x tile, the
 //                   180-degree tap rotation applied in the store index.
 //
-// Workgroup: NW wave64s; WCO waves split the BCO output channels and
-// NW / WCO the pixel block; each wave holds MI x NJ 32x32 accumulators.  The
-// LDS tiles are double-buffered: while the MFMAs of fill i read one buffer,
-// the same waves write fill i + 1 (loaded into registers one fill ahead)
-// into the other between their MFMA groups, and issue the global loads of
-// fill i + 2.  One barrier per fill.  Forward accumulators start at the bias,
+// Workgroup: NW wave64s.  The compute waves (all four of a four-wave
+// workgroup; waves 0-3, one per SIMD, of an eight-wave one) split the tile:
+// WCO of them the BCO output channels and the rest the pixel block, each
+// holding MI x NJ 32x32 accumulators.  The LDS tiles are double-buffered:
+// while the MFMAs of fill i read one buffer, fill i + 1 (loaded into
+// registers one fill ahead) is written into the other and the global loads
+// of fill i + 2 are issued -- by the same waves between their MFMA groups
+// (four waves), or by waves 4-7, which do nothing else (eight waves; the
+// compute waves then hold 64 x 128 wave tiles, 6 operand reads per 8
+// MFMAs).  One barrier per fill.  Forward accumulators start at the bias,
 // so the epilogue is stores only.
 #include "common.hpp"
 #include "launch.hpp"
@@ -88,7 +92,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
-  constexpr int WPX = NW / WCO;
+  // Eight-wave workgroups are wave-specialised: waves 0-3 (one per SIMD)
+  // only read operands from LDS and run MFMAs, waves 4-7 only stage tiles.
+  // Four-wave workgroups do both in every wave.
+  constexpr bool WSPEC = NW == 8;
+  constexpr int NC = WSPEC ? 4 : NW;        // compute waves
+  constexpr int NP = WSPEC ? 256 : NT;      // staging threads
+  constexpr int WPX = NC / WCO;
   constexpr int MI = BCO / (32 * WCO);
   constexpr int NJ = BM / (32 * WPX);
   static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
@@ -107,32 +117,46 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int wco = wave % WCO, wpx = wave / WCO;
   const BlockOrigin o = block_origin<TW, TH, IMGS>(blockIdx.x, tiles_w, tiles_h);
   const int co0 = blockIdx.y * BCO;
   const long HW = (long)H * W;
+  const int nchunks = (Cin + CB - 1) / CB;
+  // staging thread index (-1: this thread stages nothing)
+  const int sp = WSPEC ? (wave >= NC ? tid - 64 * NC : -1) : tid;
 
   // ---- vector staging (W % 8 == 0, Cin % 16 == 0, 16-byte bases) ----
-  // Each staging thread owns one item and holds it in stg[] from its global
-  // loads (one fill ahead) until it writes it to LDS:
-  //   x item (rr, q, img, g), threads [0, XI): the 8 x 8 block of channels
+  // A staging thread owns items and holds them in registers from their
+  // global loads (one fill ahead) until it writes them to LDS:
+  //   x item (rr, q, img, g), sp in [0, XI): the 8 x 8 block of channels
   //     c0 + 8g .. + 7 x pixels 8q .. 8q + 7 of one staged row, as eight
   //     128-bit row loads, written as eight channel-interleaved words;
-  //   halo item, threads [0, XH): 8 channels of one halo-column pixel;
-  //   weight item, threads [NT - WI, NT): forward (co_l, g), co_l fastest:
-  //     the 144-byte run
+  //   halo item, sp in [0, XH): 8 channels of one halo-column pixel;
+  //   weight items: forward (co_l, g), co_l fastest: the 144-byte run
   //     w[co0 + co_l, c0 + 8g .. + 7, 0..8] (nine loads, nine tap words);
   //     backward-data (g, eb): word eb of the rows w[c0 + 8g + i, co0.., ..],
   //     i = 0..7 (eight loads, transposed into eight words of 8 k each).
+  //     Wave-specialised: items sp and sp + 256; otherwise the last WI
+  //     threads, so that x and weight staging sit in different waves.
   constexpr int XI = 2 * IMGS * HR * (TW / 8);
   constexpr int XH = 2 * IMGS * HR * 2;
   constexpr int WI = MODE == kFwd ? 2 * BCO : 2 * EW;
-  constexpr int W0 = NT - WI;
-  static_assert(XI <= W0 && XH <= NT, "one staging item per thread");
+  constexpr int WK = WSPEC ? (WI + NP - 1) / NP : 1;  // weight items per staging thread
+  static_assert(XI <= NP && XH <= NP && (WSPEC || XI + WI <= NP), "staging items fit");
   constexpr int NSTG = MODE == kFwd ? 9 : 8;
-  const bool xrole = tid < XI, hrole = tid < XH, wrole = tid >= W0;
 
-  u32x4 stg[VEC ? NSTG : 1];
+  auto w_item = [&](int k) -> int {
+    if (sp < 0) return -1;
+    if constexpr (WSPEC) {
+      const int it = sp + NP * k;
+      return it < WI ? it : -1;
+    } else {
+      return sp >= NP - WI ? sp - (NP - WI) : -1;
+    }
+  };
+  const bool xrole = sp >= 0 && sp < XI, hrole = sp >= 0 && sp < XH;
+
+  u32x4 sx[VEC ? 8 : 1];
+  u32x4 sw[VEC ? WK : 1][VEC ? NSTG : 1];
   u32x4 hr = {0u, 0u, 0u, 0u};
 
   // Byte offsets, computed once; a fill adds the channel step.  Items
@@ -140,13 +164,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t sv = buffer_view(src, src_bytes);
   const __amdgpu_buffer_rsrc_t wv = buffer_view(wt, wt_bytes);
   const uint32_t hw2 = 2u * (uint32_t)(H * W);
-  uint32_t xoff = kOutside, hoff = kOutside, woff = kOutside;
+  uint32_t xoff = kOutside, hoff = kOutside, woff[WK];
   int xdst = 0;  // LDS word of the x item's first pixel
+#pragma unroll
+  for (int k = 0; k < WK; ++k) woff[k] = kOutside;
   if constexpr (VEC) {
     if (xrole) {
       // rows fastest: with the odd row stride, 16 consecutive lanes write
       // 16 different bank groups
-      int t = tid;
+      int t = sp;
       const int rr = t % HR;
       t /= HR;
       const int q = t % (TW / 8);
@@ -159,8 +185,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       xdst = g * PLW + (img * HR + rr) * RS + 4 + 8 * q;
     }
     if (hrole) {
-      const int side = tid & 1;
-      int t = tid >> 1;
+      const int side = sp & 1;
+      int t = sp >> 1;
       const int rr = t % HR;
       t /= HR;
       const int img = t % IMGS;
@@ -169,15 +195,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if (n < N && h >= 0 && h < H && w >= 0 && w < W)
         hoff = 2u * (uint32_t)(((n * Cin + 8 * g) * H + h) * W + w);
     }
-    if (wrole) {
-      const int it = tid - W0;
+#pragma unroll
+    for (int k = 0; k < WK; ++k) {
+      const int it = w_item(k);
+      if (it < 0) continue;
       if constexpr (MODE == kFwd) {
         const int co_l = it % BCO, g = it / BCO;  // consecutive lanes: consecutive co
-        if (co0 + co_l < Cout) woff = 2u * (uint32_t)(((co0 + co_l) * Cin + 8 * g) * 9);
+        if (co0 + co_l < Cout) woff[k] = 2u * (uint32_t)(((co0 + co_l) * Cin + 8 * g) * 9);
       } else {
         const int g = it / EW, eb = it % EW;
         if (8 * eb < (Cout - co0) * 9)
-          woff = 2u * (uint32_t)(((8 * g) * Cout + co0) * 9 + 8 * eb);
+          woff[k] = 2u * (uint32_t)(((8 * g) * Cout + co0) * 9 + 8 * eb);
       }
     }
   }
@@ -191,7 +219,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint32_t f = (uint32_t)(c0 / 16);
     if (xrole) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) stg[i] = buffer_load16(sv, xoff + f * xstep + (uint32_t)i * hw2);
+      for (int i = 0; i < 8; ++i) sx[i] = buffer_load16(sv, xoff + f * xstep + (uint32_t)i * hw2);
     }
     if (hrole) {
       uint32_t v[8];
@@ -202,13 +230,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       hr.z = v[4] | (v[5] << 16);
       hr.w = v[6] | (v[7] << 16);
     }
-    if (wrole) {
+#pragma unroll
+    for (int k = 0; k < WK; ++k) {
+      if (w_item(k) < 0) continue;
       if constexpr (MODE == kFwd) {
 #pragma unroll
-        for (int j = 0; j < 9; ++j) stg[j] = buffer_load16(wv, woff + f * wstep + 16u * (uint32_t)j);
+        for (int j = 0; j < 9; ++j)
+          sw[k][j] = buffer_load16(wv, woff[k] + f * wstep + 16u * (uint32_t)j);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) stg[i] = buffer_load16(wv, woff + f * wstep + (uint32_t)i * wrow);
+        for (int i = 0; i < 8; ++i)
+          sw[k][i] = buffer_load16(wv, woff[k] + f * wstep + (uint32_t)i * wrow);
       }
     }
   };
@@ -216,27 +248,29 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   auto store_tiles = [&](int buf) {
     if (xrole) {
       u32x4* d = xs + buf * XW + xdst;
-      d[0] = column_word<0>(stg);
-      d[1] = column_word<1>(stg);
-      d[2] = column_word<2>(stg);
-      d[3] = column_word<3>(stg);
-      d[4] = column_word<4>(stg);
-      d[5] = column_word<5>(stg);
-      d[6] = column_word<6>(stg);
-      d[7] = column_word<7>(stg);
+      d[0] = column_word<0>(sx);
+      d[1] = column_word<1>(sx);
+      d[2] = column_word<2>(sx);
+      d[3] = column_word<3>(sx);
+      d[4] = column_word<4>(sx);
+      d[5] = column_word<5>(sx);
+      d[6] = column_word<6>(sx);
+      d[7] = column_word<7>(sx);
     }
     if (hrole) {
-      const int side = tid & 1;
-      const int t = tid >> 1;  // (g * IMGS + img) * HR + rr
+      const int side = sp & 1;
+      const int t = sp >> 1;  // (g * IMGS + img) * HR + rr
       const int g = t / (IMGS * HR);
       xs[buf * XW + g * PLW + (t % (IMGS * HR)) * RS + 4 + (side ? TW : -1)] = hr;
     }
-    if (wrole) {
-      u32x4* wb = wa + buf * WW;
-      const int it = tid - W0;
+    u32x4* wb = wa + buf * WW;
+#pragma unroll
+    for (int k = 0; k < WK; ++k) {
+      const int it = w_item(k);
+      if (it < 0) continue;
       if constexpr (MODE == kFwd) {
         const int co_l = it % BCO, g = it / BCO;
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(stg);
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(sw[k]);
         wb[(0 * 2 + g) * BCO + co_l] = tap_word<0>(d);
         wb[(1 * 2 + g) * BCO + co_l] = tap_word<1>(d);
         wb[(2 * 2 + g) * BCO + co_l] = tap_word<2>(d);
@@ -254,27 +288,29 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
           const int e = 8 * eb + i;
           wb[((8 - e % 9) * 2 + g) * BCO + e / 9] = v;
         };
-        put(0, column_word<0>(stg));
-        put(1, column_word<1>(stg));
-        put(2, column_word<2>(stg));
-        put(3, column_word<3>(stg));
-        put(4, column_word<4>(stg));
-        put(5, column_word<5>(stg));
-        put(6, column_word<6>(stg));
-        put(7, column_word<7>(stg));
+        put(0, column_word<0>(sw[k]));
+        put(1, column_word<1>(sw[k]));
+        put(2, column_word<2>(sw[k]));
+        put(3, column_word<3>(sw[k]));
+        put(4, column_word<4>(sw[k]));
+        put(5, column_word<5>(sw[k]));
+        put(6, column_word<6>(sw[k]));
+        put(7, column_word<7>(sw[k]));
       }
     }
   };
 
-  // Scalar path (ragged shapes): 16-bit loads straight into LDS buffer buf.
+  // Scalar path (ragged shapes): 16-bit loads straight into LDS buffer buf,
+  // by the staging threads.
   auto fill_scalar = [&](int c0, int buf) {
+    if (sp < 0) return;
     uint16_t* xh = reinterpret_cast<uint16_t*>(xs + buf * XW);
     uint16_t* wh = reinterpret_cast<uint16_t*>(wa + buf * WW);
     constexpr int XS = CB * IMGS * HR * (TW + 2);
 #pragma unroll 4
-    for (int k = 0; k < (XS + NT - 1) / NT; ++k) {
-      const int it = tid + NT * k;
-      if (XS % NT == 0 || it < XS) {
+    for (int k = 0; k < (XS + NP - 1) / NP; ++k) {
+      const int it = sp + NP * k;
+      if (XS % NP == 0 || it < XS) {
         const int cc = it % (TW + 2) - 1;
         const int t = it / (TW + 2);  // (ch * IMGS + img) * HR + rr
         const int rr = t % HR;
@@ -289,9 +325,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
     constexpr int WSI = CB * 9 * BCO;
 #pragma unroll 4
-    for (int k = 0; k < (WSI + NT - 1) / NT; ++k) {
-      const int it = tid + NT * k;
-      if (WSI % NT != 0 && it >= WSI) continue;
+    for (int k = 0; k < (WSI + NP - 1) / NP; ++k) {
+      const int it = sp + NP * k;
+      if (WSI % NP != 0 && it >= WSI) continue;
       int ci_l, co_l, tap;
       uint16_t v = 0;
       if constexpr (MODE == kFwd) {
@@ -313,7 +349,45 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       wh[((tap * 2 + (ci_l >> 3)) * BCO + co_l) * 8 + (ci_l & 7)] = v;
     }
   };
+  auto stage_next = [&](int chunk) {  // write fill chunk + 1, load fill chunk + 2
+    if constexpr (VEC) {
+      if (chunk + 1 < nchunks) store_tiles((chunk + 1) & 1);
+      if (chunk + 2 < nchunks) load_tiles((chunk + 2) * CB);
+    } else {
+      if (chunk + 1 < nchunks) fill_scalar((chunk + 1) * CB, (chunk + 1) & 1);
+    }
+  };
 
+  // ---- prologue: fill 0 in buffer 0, fill 1 in registers ----
+  if constexpr (MODE == kFwd) {
+    for (int i = tid; i < BCO; i += NT)
+      bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
+  }
+  if constexpr (VEC) {
+    load_tiles(0);
+    store_tiles(0);
+    if (nchunks > 1) load_tiles(CB);
+  } else {
+    fill_scalar(0, 0);
+  }
+  __syncthreads();
+
+  if constexpr (WSPEC) {
+    if (wave >= NC) {
+      // Staging waves: between the barrier of fill i - 1 and that of fill i,
+      // write fill i + 1 into buffer (i + 1) & 1 (last read by the compute
+      // waves before the barrier of fill i - 1) and load fill i + 2.  One
+      // barrier per fill, matching the compute waves.
+      for (int chunk = 0; chunk + 1 < nchunks; ++chunk) {
+        stage_next(chunk);
+        __syncthreads();
+      }
+      return;
+    }
+  }
+
+  // ---- compute ----
+  const int wco = wave % WCO, wpx = wave / WCO;
   int boff[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -325,20 +399,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // Forward: the accumulators start at the tile's biases (zero without
   // bias), so the epilogue is stores only.
-  if constexpr (MODE == kFwd) {
-    for (int i = tid; i < BCO; i += NT)
-      bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
-  }
-  const int nchunks = (Cin + CB - 1) / CB;
-  if constexpr (VEC) {
-    load_tiles(0);
-    store_tiles(0);
-    if (nchunks > 1) load_tiles(CB);
-  } else {
-    fill_scalar(0, 0);
-  }
-  __syncthreads();
-
   f32x16 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -350,7 +410,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
-  // Operands of one tap: a = weights (MI words), b = pixels (NJ words).
+  // Operands of one tap: a = weights (MI words), b = pixels (NJ words); tap
+  // t in register set t & 1.
   u32x4 a[2][MI], b[2][NJ];
   auto read_tap = [&](int cbuf, int rb, int t) {
     const u32x4* xb = xs + cbuf * XW;
@@ -361,11 +422,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b[rb][j] = xb[boff[j] + r * RS + s];
   };
-  // Tap t's operands are read while tap t-1's MFMAs run.  The next fill is
-  // written to the other buffer after tap 0 (that buffer was last read
-  // before the previous fill's barrier), and the loads of the fill after it
-  // are issued after tap 1.  The barrier sits before tap 8's MFMAs: by then
-  // every lane has written the next fill and read its last operands of
+  // Tap t's operands are read while tap t-1's MFMAs run.  The barrier sits
+  // before tap 8's MFMAs: by then the next fill is written (by the staging
+  // waves, or here after tap 0) and every lane has read its last operands of
   // this one, so tap 0 of the next fill is read while tap 8 runs.
   read_tap(0, 0, 0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
@@ -387,13 +446,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = mfma_32x32x16_bf16(a[rb][i], b[rb][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (VEC) {
-        if (t == 0 && next) store_tiles(cur ^ 1);
-        if (t == 1 && chunk + 2 < nchunks) load_tiles((chunk + 2) * CB);
-      } else {
-        if (t == 0 && next) fill_scalar((chunk + 1) * CB, cur ^ 1);
+      if constexpr (!WSPEC) {
+        // written after tap 0: the other buffer was last read before the
+        // previous fill's barrier
+        if (t == 0) stage_next(chunk);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     // tap 0 of the next fill was read into the second operand set
 #pragma unroll

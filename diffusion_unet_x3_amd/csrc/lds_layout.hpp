@@ -54,11 +54,15 @@ CONV3X3_HD constexpr int fwd_f32_lds_bytes(int cb, int imgs, int th, int tw, int
 // Plane of one 8-channel group, in 16-byte words, padded to 8 mod 16 words
 // so that the two groups' words written by one transpose step fall in
 // different banks.
-// Row stride in words.  tw >= 16: odd, so that the staging lanes, which
+// Row stride in words.  A 128-bit LDS read serves the lane groups
+// {0-7, 24-31} and {8-15, 16-23} (and the same in the upper half) together,
+// and the 16 words of a group need 16 different bank groups (word mod 16).
+// tw = 8: the MFMA pixel operand is four rows of 8, conflict-free with a
+// stride of 8 mod 16.  Wider tiles: odd, so that the staging lanes, which
 // write rows-fastest, put 16 consecutive rows in 16 different bank groups
-// (the MFMA operand reads cover whole 16-word runs of one row either way).
-// tw = 8: 24 (8 mod 16), so that the operand reads of two consecutive rows by
-// one 16-lane group fall in disjoint bank halves.
+// (the operand reads of tw >= 32 are conflict-free for any stride; tw = 16
+// would need 0 mod 16, which makes the staging stores 8-way conflicts and
+// measured slower overall).
 CONV3X3_HD constexpr int fwd_bf16_rs(int tw) { return tw == 8 ? 24 : tw + 9; }
 CONV3X3_HD constexpr int fwd_bf16_plane(int imgs, int th, int tw) {
   return imgs * (th + 2) * fwd_bf16_rs(tw) + ((8 - (imgs * (th + 2) * fwd_bf16_rs(tw)) % 16) + 16) % 16;

@@ -97,7 +97,7 @@ bool plan(const Problem& p, Plan* out) {
       cands[1] = Cand{64, 64, 2, 4};
       ncand = 2;
     } else if (cout > 64) {
-      cands[0] = Cand{256, 128, 2, 8};
+      cands[0] = Cand{256, 128, 1, 8};
       cands[1] = Cand{128, 64, 2, 4};
       cands[2] = Cand{64, 64, 2, 4};
       ncand = 3;

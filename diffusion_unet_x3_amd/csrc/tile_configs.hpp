@@ -21,12 +21,13 @@
   X(64, 1, 1, 64, 2) X(32, 2, 1, 64, 2) X(16, 4, 1, 64, 2) X(8, 8, 1, 64, 2)
 
 // bfloat16: X(tw, th, imgs, co_tile, wave_co, waves).  Eight waves over
-// 256-pixel x 128-channel tiles (64 x 64 wave tiles, two waves per SIMD);
-// four waves over 128 x 64 (64 x 32 wave tiles) and 64 x 64 (32 x 32) for
-// layers with few output pixels.
+// 256-pixel x 128-channel tiles: the two waves of a SIMD split each fill's
+// taps, each holding a 64-pixel x 128-channel wave tile; four waves over
+// 128 x 64 (64 x 32 wave tiles) and 64 x 64 (32 x 32) for layers with few
+// output pixels.
 #define CONV3X3_FWD_BF16_CONFIGS(X)                                                   \
-  X(64, 4, 1, 128, 2, 8) X(32, 8, 1, 128, 2, 8) X(16, 16, 1, 128, 2, 8)               \
-  X(8, 32, 1, 128, 2, 8) X(8, 8, 4, 128, 2, 8)                                        \
+  X(64, 4, 1, 128, 1, 8) X(32, 8, 1, 128, 1, 8) X(16, 16, 1, 128, 1, 8)               \
+  X(8, 32, 1, 128, 1, 8) X(8, 8, 4, 128, 1, 8)                                        \
   X(64, 2, 1, 64, 2, 4) X(32, 4, 1, 64, 2, 4) X(16, 8, 1, 64, 2, 4) X(8, 16, 1, 64, 2, 4) \
   X(8, 8, 2, 64, 2, 4)                                                                \
   X(64, 1, 1, 64, 2, 4) X(32, 2, 1, 64, 2, 4) X(16, 4, 1, 64, 2, 4) X(8, 8, 1, 64, 2, 4)
