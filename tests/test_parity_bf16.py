@@ -34,6 +34,32 @@ def test_small_shapes_full_compare(shape, exact):
     print(errs)
 
 
+# Shapes whose forward or backward-data plan is the eight-wave,
+# wave-specialised 256-pixel x 128-channel tile (every tile geometry, and a
+# ragged channel tile), small enough for a full oracle compare.
+EIGHT_WAVE = [((32, 16, 256, 32, 32), "fwd"), ((32, 256, 16, 32, 32), "bwd_data"),
+              ((32, 16, 200, 32, 32), "fwd"), ((32, 200, 16, 32, 32), "bwd_data"),
+              ((64, 16, 512, 16, 16), "fwd"), ((16, 16, 128, 64, 64), "fwd"),
+              ((256, 16, 512, 8, 8), "fwd"), ((16, 128, 16, 64, 64), "bwd_data")]
+
+
+@pytest.mark.parametrize("case", EIGHT_WAVE, ids=lambda c: "x".join(map(str, c[0])) + "-" + c[1])
+@pytest.mark.parametrize("exact", [False, True], ids=["random", "integer"])
+def test_eight_wave_tiles_full_compare(case, exact):
+    import diffusion_unet_x3_amd as lib3
+    shape, pass_name = case
+    pass_id = lib3.PASS_FWD if pass_name == "fwd" else lib3.PASS_BWD_DATA
+    assert lib3.conv3x3_plan(pass_id, *shape, lib3.CONV3X3_BF16)["threads"] == 512, \
+        "shape no longer selects the eight-wave tile"
+    layer = wl.small_layer(*shape, dtype="bf16", seed=29)
+    print(f"[parity] bf16 eight-wave {shape} {pass_name} exact={exact}", flush=True)
+    inp = wl.make_inputs(layer, integer_exact=exact)
+    gpu = run_gpu(inp)
+    ref = oracle_full(inp)
+    errs = check(pairs(gpu, ref), "bf16", exact=exact, label=str(shape))
+    print(errs)
+
+
 def test_quantisation_error_is_reported_not_graded():
     """Against the oracle on the float32 values before rounding to bf16 the
     error is the inputs' quantisation error (informational), still far

@@ -39,6 +39,30 @@ def test_small_shapes_full_compare(shape, exact):
     check(pairs(gpu, ref), "f32", exact=exact, label=str(shape))
 
 
+# Shapes whose forward or backward-data plan is one of the large tiles
+# (256 pixels x 64 channels, 128 x 128, and a ragged channel tile), small
+# enough for a full oracle compare.
+LARGE_TILES = [((16, 8, 64, 64, 64), "fwd"), ((16, 8, 64, 64, 64), "bwd_data"),
+               ((32, 8, 128, 32, 32), "fwd"), ((32, 128, 8, 32, 32), "bwd_data"),
+               ((16, 8, 200, 32, 32), "fwd"), ((16, 200, 8, 32, 32), "bwd_data")]
+
+
+@pytest.mark.parametrize("case", LARGE_TILES, ids=lambda c: "x".join(map(str, c[0])) + "-" + c[1])
+@pytest.mark.parametrize("exact", [False, True], ids=["random", "integer"])
+def test_large_tiles_full_compare(case, exact):
+    import diffusion_unet_x3_amd as lib3
+    shape, pass_name = case
+    pass_id = lib3.PASS_FWD if pass_name == "fwd" else lib3.PASS_BWD_DATA
+    p = lib3.conv3x3_plan(pass_id, *shape, lib3.CONV3X3_F32)
+    assert p["tile_m"] * p["tile_n"] == 16384, "shape no longer selects a large tile"
+    layer = wl.small_layer(*shape, dtype="f32", seed=31)
+    _flush(f"f32 large tile {shape} {pass_name} exact={exact}")
+    inp = wl.make_inputs(layer, integer_exact=exact)
+    gpu = run_gpu(inp)
+    ref = oracle_full(inp)
+    check(pairs(gpu, ref), "f32", exact=exact, label=str(shape))
+
+
 def test_no_bias_and_no_db():
     layer = wl.small_layer(2, 24, 40, 9, 20, dtype="f32", seed=3)
     inp = wl.make_inputs(layer)
