@@ -33,7 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_f32_unet_stem_32x64to64_6
 # Kernels launched by each pass of the stem layer (name prefixes in profiler output).
 PASS_KERNELS = {"fwd": ["conv3x3::fwd_f32_kernel<0,"],
                 "bwd_data": ["conv3x3::fwd_f32_kernel<1,"],
-                "bwd_weight": ["conv3x3::wgrad_f32_kernel<", "conv3x3::wgrad_reduce_kernel"]}
+                "bwd_weight": ["conv3x3::wgrad_f32_kernel<", "conv3x3::wgrad_reduce"]}
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # dense MFMA peaks, MI355X
 PEAK_HBM_GBS = 8000.0
 
