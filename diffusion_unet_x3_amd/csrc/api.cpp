@@ -165,7 +165,8 @@ int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db, void*
     ok = launch_wgrad_f32(pl, vec, (const float*)x, (const float*)g, dw, db, (float*)workspace, N,
                           C, K, H, W, s);
   } else {
-    const bool vec = W % 8 == 0 && aligned16(x) && aligned16(g);
+    const bool vec = W % 8 == 0 && aligned16(x) && aligned16(g) &&
+                     buffer_sized((long)N * C * H * W) && buffer_sized((long)N * K * H * W);
     ok = launch_wgrad_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)g, dw, db,
                            (float*)workspace, N, C, K, H, W, s);
   }

@@ -12,8 +12,9 @@
 // 128-bit LDS reads; the left and right taps (s = 0, 2) are the same words
 // shifted by one bf16 element, assembled with funnel shifts from the aligned
 // word and one dword of its neighbour -- no unaligned LDS access.  A pixel
-// chunk is 128 pixels (8 MFMA steps).  Partial sums and the split-K reduce
-// are those of the float32 kernel.
+// chunk is 128 pixels (8 MFMA steps; 64 for 8-wide images), staged through
+// buffer views into double-buffered LDS, one barrier per chunk.  Partial
+// sums and the split-K reduce are those of the float32 kernel.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -29,9 +30,10 @@ template <int TW, int TH, int IMGS, bool VEC>
 __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, float* __restrict__ out,
     float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
-    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k) {
+    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k,
+    uint32_t x_bytes, uint32_t g_bytes) {
   constexpr int P = IMGS * TH * TW;
-  static_assert(P == 128, "pixel chunk must hold 128 pixels");
+  static_assert(P % 16 == 0, "whole 16-pixel MFMA steps");
   static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
   constexpr int GSB = wgrad_bf16_gstride(IMGS, TH, TW);
   constexpr int RSX = wgrad_bf16_rs(TW);
@@ -39,8 +41,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   constexpr int HR = TH + 2;
   constexpr int NT = 768;
 
-  __shared__ __attribute__((aligned(16))) uint16_t gs[64 * GSB];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * PLX];
+  // Two LDS buffers: chunk i is read from one while chunk i + 1 is written
+  // into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t gs_buf[2][64 * GSB];
+  __shared__ __attribute__((aligned(16))) uint16_t xs_buf[2][64 * PLX];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -71,65 +75,61 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   u32x4 xv[VEC ? XN : 1];
   uint16_t xh[VEC ? HN : 1];
 
+  // Vector path: buffer views; an item outside the tensors or the image
+  // reads zero through an offset past the view (32-bit offset arithmetic).
+  const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
+  const __amdgpu_buffer_rsrc_t xview = buffer_view(x, x_bytes);
   auto load_tiles = [&](int chunk) {
     if constexpr (VEC) {
       const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
 #pragma unroll
       for (int k = 0; k < GN; ++k) {
         const int it = tid + k * NT;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (GI % NT == 0 || it < GI) {
-          const int q = it % XQ;
-          int t = it / XQ;
-          const int row = t % TH;
-          t /= TH;
-          const int img = t % IMGS;
-          const int kl = t / IMGS;
-          const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 8 * q;
-          if (n < N && kk < K && h < H && w < W)
-            v = *reinterpret_cast<const u32x4*>(g + ((long)n * K + kk) * HW + (long)h * W + w);
-        }
-        gv[k] = v;
+        const int q = it % XQ;
+        int t = it / XQ;
+        const int row = t % TH;
+        t /= TH;
+        const int img = t % IMGS;
+        const int kl = t / IMGS;
+        const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 8 * q;
+        const bool ok = (GI % NT == 0 || it < GI) && n < N && kk < K && h < H && w < W;
+        gv[k] = buffer_load16(gview, ok ? 2u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside);
       }
 #pragma unroll
       for (int k = 0; k < XN; ++k) {
         const int it = tid + k * NT;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (XI % NT == 0 || it < XI) {
-          const int q = it % XQ;
-          int t = it / XQ;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int cl = t / IMGS;
-          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
-          if (n < N && c < C && h >= 0 && h < H && w < W)
-            v = *reinterpret_cast<const u32x4*>(x + ((long)n * C + c) * HW + (long)h * W + w);
-        }
-        xv[k] = v;
+        const int q = it % XQ;
+        int t = it / XQ;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int cl = t / IMGS;
+        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
+        const bool ok = (XI % NT == 0 || it < XI) && n < N && c < C && h >= 0 && h < H && w < W;
+        xv[k] = buffer_load16(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w) : kOutside);
       }
 #pragma unroll
       for (int k = 0; k < HN; ++k) {
         const int it = tid + k * NT;
-        uint16_t v = 0;
-        if (HI_ % NT == 0 || it < HI_) {
-          const int side = it & 1;
-          int t = it >> 1;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int cl = t / IMGS;
-          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
-          const int w = o.w0 + (side ? TW : -1);
-          if (n < N && c < C && h >= 0 && h < H && w >= 0 && w < W)
-            v = x[((long)n * C + c) * HW + (long)h * W + w];
-        }
-        xh[k] = v;
+        const int side = it & 1;
+        int t = it >> 1;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int cl = t / IMGS;
+        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
+        const int w = o.w0 + (side ? TW : -1);
+        const bool ok = (HI_ % NT == 0 || it < HI_) && n < N && c < C && h >= 0 && h < H &&
+                        w >= 0 && w < W;
+        xh[k] = (uint16_t)buffer_load2(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w)
+                                                 : kOutside);
       }
     }
   };
 
-  auto store_tiles = [&](int chunk) {
+  auto store_tiles = [&](int chunk, int buf) {
+    uint16_t* gs = gs_buf[buf];
+    uint16_t* xs = xs_buf[buf];
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < GN; ++k) {
@@ -217,28 +217,38 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   // Operands of one step: g word, x word, and the x dwords on either side.
   u32x4 ga[2], xc[2];
   uint32_t xp[2], xn[2];
-  auto read_step = [&](int buf, int ks) {
+  auto read_step = [&](const uint16_t* gs, const uint16_t* xs, int rb, int ks) {
     const int p = ks * 16 + hi * 8;  // first of this lane's 8 pixels (one row)
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
-    ga[buf] = *reinterpret_cast<const u32x4*>(&gs[goff + p]);
+    ga[rb] = *reinterpret_cast<const u32x4*>(&gs[goff + p]);
     const int xb = xoff + (img * HR + row) * RSX + col;
-    xc[buf] = *reinterpret_cast<const u32x4*>(&xs[xb]);
-    xp[buf] = *reinterpret_cast<const uint32_t*>(&xs[xb - 2]);
-    xn[buf] = *reinterpret_cast<const uint32_t*>(&xs[xb + 8]);
+    xc[rb] = *reinterpret_cast<const u32x4*>(&xs[xb]);
+    xp[rb] = *reinterpret_cast<const uint32_t*>(&xs[xb - 2]);
+    xn[rb] = *reinterpret_cast<const uint32_t*>(&xs[xb + 8]);
   };
 
-  if (chunk_begin < chunk_end) load_tiles(chunk_begin);
-  for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
-    if (chunk != chunk_begin) __syncthreads();
-    store_tiles(chunk);
+  // Chunk i is computed from LDS buffer i & 1.  After its second MFMA step
+  // the registers holding chunk i + 1 are written to the other buffer (last
+  // read in chunk i - 1, before the barrier that ended it) and the global
+  // loads of chunk i + 2 are issued into them, so staging runs beside the
+  // MFMAs of waves that are still computing.  One barrier per chunk.
+  constexpr int kStoreStep = 1;
+  if (chunk_begin < chunk_end) {
+    load_tiles(chunk_begin);
+    store_tiles(chunk_begin, 0);
+    if (chunk_begin + 1 < chunk_end) load_tiles(chunk_begin + 1);
     __syncthreads();
-    if (chunk + 1 < chunk_end) load_tiles(chunk + 1);
+  }
+  for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
+    const int cur = (chunk - chunk_begin) & 1;
+    const uint16_t* gs = gs_buf[cur];
+    const uint16_t* xs = xs_buf[cur];
     // Step ks (16 pixels) reads its operands while step ks-1's MFMAs run.
-    read_step(0, 0);
+    read_step(gs, xs, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < P / 16; ++ks) {
       const int cb_ = ks & 1;
-      if (ks + 1 < P / 16) read_step(cb_ ^ 1, ks + 1);
+      if (ks + 1 < P / 16) read_step(gs, xs, cb_ ^ 1, ks + 1);
       __builtin_amdgcn_sched_barrier(0);
       const u32x4 c = xc[cb_];
       u32x4 left, right;  // columns col-1 .. col+6 and col+1 .. col+8
@@ -253,12 +263,19 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
       acc[0] = mfma_32x32x16_bf16(ga[cb_], left, acc[0]);
       acc[1] = mfma_32x32x16_bf16(ga[cb_], c, acc[1]);
       acc[2] = mfma_32x32x16_bf16(ga[cb_], right, acc[2]);
+      if (ks == kStoreStep && chunk + 1 < chunk_end) {
+        __builtin_amdgcn_sched_barrier(0);
+        store_tiles(chunk + 1, cur ^ 1);
+        if (chunk + 2 < chunk_end) load_tiles(chunk + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (do_db && tid < 256) {
       const int kl = tid >> 2, part = tid & 3;
 #pragma unroll
       for (int i = 0; i < P / 4; ++i) dbsum += bf16_to_f32(gs[kl * GSB + part + 4 * i]);
     }
+    __syncthreads();
   }
 
   const int c = c0 + cb * 32 + l32;
@@ -293,12 +310,13 @@ static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, const uint16_t* x, 
     hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
                        out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64);
+                       (K + 63) / 64, (uint32_t)((long)N * C * H * W * 2),
+                       (uint32_t)((long)N * K * H * W * 2));
   else
     hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
                        out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64);
+                       (K + 63) / 64, 0u, 0u);
 }
 
 bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,

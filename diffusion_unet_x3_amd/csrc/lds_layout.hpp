@@ -96,8 +96,9 @@ CONV3X3_HD constexpr int wgrad_bf16_plane(int imgs, int th, int tw) {
   return imgs * (th + 2) * wgrad_bf16_rs(tw) +
          ((8 - (imgs * (th + 2) * wgrad_bf16_rs(tw)) % 64) + 64) % 64;
 }
+// Two buffers of each tile (chunk i + 1 is staged while chunk i is read).
 CONV3X3_HD constexpr int wgrad_bf16_lds_bytes(int imgs, int th, int tw) {
-  return 2 * 64 * (wgrad_bf16_gstride(imgs, th, tw) + wgrad_bf16_plane(imgs, th, tw));
+  return 2 * 2 * 64 * (wgrad_bf16_gstride(imgs, th, tw) + wgrad_bf16_plane(imgs, th, tw));
 }
 
 }  // namespace conv3x3

@@ -153,9 +153,10 @@ bool plan(const Problem& p, Plan* out) {
     pl.split = 1;
   } else if (p.pass == kBwdWeight) {
     // float32: 64-pixel chunks (32 MFMA steps); bfloat16: 128-pixel chunks
-    // (8 MFMA steps of 16 pixels).
-    Block b = pick_block(p.dtype == kF32 ? 64 : 128, p.H, p.W);
-    if (!wgrad_cfg_exists(p.dtype, b)) b = Block{b.tw, (p.dtype == kF32 ? 64 : 128) / b.tw, 1};
+    // (8 MFMA steps of 16 pixels), 64 for images at most 8 wide.
+    const int cp = p.dtype == kF32 ? 64 : (p.W <= 8 ? 64 : 128);
+    Block b = pick_block(cp, p.H, p.W);
+    if (!wgrad_cfg_exists(p.dtype, b)) b = Block{b.tw, cp / b.tw, 1};
     if (!wgrad_cfg_exists(p.dtype, b)) return false;
     pl.tw = b.tw;
     pl.th = b.th;

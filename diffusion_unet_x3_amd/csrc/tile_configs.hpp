@@ -34,4 +34,6 @@
 
 // Backward-weight pixel chunks: X(tw, th, imgs).
 #define CONV3X3_WGRAD_F32_CONFIGS(X) X(64, 1, 1) X(32, 2, 1) X(16, 4, 1) X(8, 8, 1)
-#define CONV3X3_WGRAD_BF16_CONFIGS(X) X(64, 2, 1) X(32, 4, 1) X(16, 8, 1) X(8, 16, 1) X(8, 8, 2)
+// bfloat16: 128-pixel chunks; 64 for images at most 8 wide (two buffers of
+// the 8-wide layout at 128 pixels would not fit the LDS).
+#define CONV3X3_WGRAD_BF16_CONFIGS(X) X(64, 2, 1) X(32, 4, 1) X(16, 8, 1) X(8, 16, 1) X(8, 8, 1)
