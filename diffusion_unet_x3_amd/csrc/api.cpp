@@ -97,7 +97,8 @@ int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y, int N
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(x) && aligned16(w);
+    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(x) && aligned16(w) &&
+                     buffer_sized(2L * N * C * H * W) && buffer_sized(2L * K * C * 9);
     ok = launch_fwd_f32(pl, vec, (const float*)x, (const float*)w, bias, y, N, C, K, H, W, s);
   } else {
     const bool vec = W % 8 == 0 && C % 16 == 0 && aligned16(x) && aligned16(w) &&
@@ -121,7 +122,8 @@ int conv3x3_bwd_data(const void* g, const void* w, float* dx, int N, int C, int 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w);
+    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w) &&
+                     buffer_sized(2L * N * K * H * W) && buffer_sized(2L * K * C * 9);
     ok = launch_fwd_f32(pl, vec, (const float*)g, (const float*)w, nullptr, dx, N, K, C, H, W, s);
   } else {
     const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w) &&
@@ -161,7 +163,8 @@ int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db, void*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && aligned16(x) && aligned16(g);
+    const bool vec = W % 4 == 0 && aligned16(x) && aligned16(g) &&
+                     buffer_sized(2L * N * C * H * W) && buffer_sized(2L * N * K * H * W);
     ok = launch_wgrad_f32(pl, vec, (const float*)x, (const float*)g, dw, db, (float*)workspace, N,
                           C, K, H, W, s);
   } else {

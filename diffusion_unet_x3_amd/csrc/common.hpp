@@ -68,6 +68,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t v, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, 0));
 }
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(v, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t v, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(v, (int)off, 0, 0);
 }

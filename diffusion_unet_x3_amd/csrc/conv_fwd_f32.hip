@@ -30,7 +30,7 @@ template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h,
-    uint32_t dst_bytes) {
+    uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -83,11 +83,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 
   // Vector path: global -> registers here (one fill ahead), registers -> LDS
   // in store_tiles.  Scalar path: everything happens in store_tiles.
+  // Vector path: buffer views (32-bit offsets); an item outside the tensors
+  // or the image reads zero through an offset past the view.
+  const __amdgpu_buffer_rsrc_t sview = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t wview = buffer_view(wt, wt_bytes);
   auto load_tiles = [&](int c0) {
     if constexpr (VEC) {
-      // Loads are unconditional: an item outside the tensor reads element 0
-      // and is replaced by zero, so the staging code has no branches.
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
         const int it = tid + k * NT;
@@ -100,9 +101,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && c < Cin && h >= 0 &&
                         h < H && w < W;
-        const long idx = ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + idx);
-        xv[k] = ok ? v : z;
+        xv[k] = __builtin_bit_cast(
+            f32x4, buffer_load16(sview, ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w)
+                                            : kOutside));
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
@@ -117,8 +118,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int w = o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && c < Cin && h >= 0 &&
                         h < H && w >= 0 && w < W;
-        const float v = src[ok ? ((long)n * Cin + c) * HW + (long)h * W + w : 0];
-        xf[k] = ok ? v : 0.f;
+        xf[k] = __builtin_bit_cast(
+            float, buffer_load4(sview, ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w)
+                                          : kOutside));
       }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
@@ -126,18 +128,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int run = it / (RUN / 4);
         const int e = 4 * (it % (RUN / 4));
         bool ok;
-        long idx;
+        int idx;
         if constexpr (MODE == kFwd) {
           const int co = co0 + run;
           ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && co < Cout && e < (Cin - c0) * 9;
-          idx = ((long)co * Cin + c0) * 9 + e;
+          idx = (co * Cin + c0) * 9 + e;
         } else {
           const int ci = c0 + run;
           ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && ci < Cin && e < (Cout - co0) * 9;
-          idx = ((long)ci * Cout + co0) * 9 + e;
+          idx = (ci * Cout + co0) * 9 + e;
         }
-        const f32x4 v = *reinterpret_cast<const f32x4*>(wt + (ok ? idx : 0));
-        wv[k] = ok ? v : z;
+        wv[k] = __builtin_bit_cast(f32x4, buffer_load16(wview, ok ? 4u * (uint32_t)idx : kOutside));
       }
     }
   };
@@ -342,11 +343,12 @@ static void launch_cfg(const Plan& pl, bool vec, const float* src, const float* 
   if (vec)
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, true>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                       (uint32_t)((long)N * Cin * H * W * 4), (uint32_t)((long)Cin * Cout * 9 * 4),
                        dst_bytes);
   else
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, false>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       dst_bytes);
+                       0u, 0u, dst_bytes);
 }
 
 template <int MODE>

@@ -28,7 +28,8 @@ template <int TW, int TH, int IMGS, bool VEC>
 __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ g, float* __restrict__ out,
     float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
-    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k) {
+    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k,
+    uint32_t x_bytes, uint32_t g_bytes) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P == 64, "pixel chunk must hold 64 pixels");
   constexpr int GS = wgrad_f32_gstride(IMGS, TH, TW);
@@ -77,17 +78,17 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
 
+  // Vector path: buffer views; an item outside the tensors or the image
+  // reads zero through an offset past the view (32-bit offset arithmetic,
+  // no branches).
+  const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
+  const __amdgpu_buffer_rsrc_t xview = buffer_view(x, x_bytes);
   auto load_tiles = [&](int chunk) {
-    const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
     if constexpr (VEC) {
+      const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
 #pragma unroll
       for (int k = 0; k < GV_N; ++k) {
         const int it = tid + k * NT;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (GV_ITEMS % NT != 0 && it >= GV_ITEMS) {
-          gv[k] = v;
-          continue;
-        }
         const int q = it % XQ;
         int t = it / XQ;
         const int row = t % TH;
@@ -95,44 +96,43 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int img = t % IMGS;
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 4 * q;
-        if (n < N && kk < K && h < H && w < W)
-          v = *reinterpret_cast<const f32x4*>(g + ((long)n * K + kk) * HW + (long)h * W + w);
-        gv[k] = v;
+        const bool ok = (GV_ITEMS % NT == 0 || it < GV_ITEMS) && n < N && kk < K && h < H && w < W;
+        gv[k] = __builtin_bit_cast(
+            f32x4, buffer_load16(gview, ok ? 4u * (uint32_t)(((n * K + kk) * H + h) * W + w)
+                                            : kOutside));
       }
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
         const int it = tid + k * NT;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
-          const int q = it % XQ;
-          int t = it / XQ;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int cl = t / IMGS;
-          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
-          if (n < N && c < C && h >= 0 && h < H && w < W)
-            v = *reinterpret_cast<const f32x4*>(x + ((long)n * C + c) * HW + (long)h * W + w);
-        }
-        xv[k] = v;
+        const int q = it % XQ;
+        int t = it / XQ;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int cl = t / IMGS;
+        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
+        const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && c < C && h >= 0 &&
+                        h < H && w < W;
+        xv[k] = __builtin_bit_cast(
+            f32x4, buffer_load16(xview, ok ? 4u * (uint32_t)(((n * C + c) * H + h) * W + w)
+                                            : kOutside));
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
         const int it = tid + k * NT;
-        float v = 0.f;
-        if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
-          const int side = it & 1;
-          int t = it >> 1;
-          const int rr = t % HR;
-          t /= HR;
-          const int img = t % IMGS;
-          const int cl = t / IMGS;
-          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
-          const int w = o.w0 + (side ? TW : -1);
-          if (n < N && c < C && h >= 0 && h < H && w >= 0 && w < W)
-            v = x[((long)n * C + c) * HW + (long)h * W + w];
-        }
-        xf[k] = v;
+        const int side = it & 1;
+        int t = it >> 1;
+        const int rr = t % HR;
+        t /= HR;
+        const int img = t % IMGS;
+        const int cl = t / IMGS;
+        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
+        const int w = o.w0 + (side ? TW : -1);
+        const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && c < C && h >= 0 &&
+                        h < H && w >= 0 && w < W;
+        xf[k] = __builtin_bit_cast(
+            float, buffer_load4(xview, ok ? 4u * (uint32_t)(((n * C + c) * H + h) * W + w)
+                                          : kOutside));
       }
     }
   };
@@ -429,12 +429,13 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const fl
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
                        out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64);
+                       (K + 63) / 64, (uint32_t)((long)N * C * H * W * 4),
+                       (uint32_t)((long)N * K * H * W * 4));
   else
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
                        out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64);
+                       (K + 63) / 64, 0u, 0u);
 }
 
 bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
