@@ -293,8 +293,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       const int k = k0 + kb * 32 + acc_row(v, hi);
       if (k < K && c < C) {
         if (slice_stride)
-          __builtin_nontemporal_store(
-              acc[s][v], &out[(long)slice * slice_stride + ((long)t * K + k) * C + c]);
+          out[(long)slice * slice_stride + ((long)t * K + k) * C + c] = acc[s][v];
         else
           out[((long)k * C + c) * 9 + t] = acc[s][v];
       }
