@@ -33,6 +33,8 @@
 // compute waves then hold 64 x 128 wave tiles, 6 operand reads per 8
 // MFMAs).  One barrier per fill.  Forward accumulators start at the bias,
 // so the epilogue is stores only.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -126,7 +128,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // ---- vector staging (W % 8 == 0, Cin % 16 == 0, 16-byte bases) ----
   // A staging thread owns items and holds them in registers from their
-  // global loads (one fill ahead) until it writes them to LDS:
+  // global loads until it writes them to LDS.  Four-wave workgroups keep two
+  // register sets: the loads of fill i + 3 go into the set just written to
+  // LDS as fill i + 1, so each load has two fills of MFMA work to arrive.
+  // (Their threads stage either x or weights, so the two roles share the
+  // registers of a set.)  Eight-wave workgroups keep one set, loaded one
+  // fill ahead by their staging waves.  Items:
   //   x item (rr, q, img, g), sp in [0, XI): the 8 x 8 block of channels
   //     c0 + 8g .. + 7 x pixels 8q .. 8q + 7 of one staged row, as eight
   //     128-bit row loads, written as eight channel-interleaved words;
@@ -154,10 +161,25 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
   };
   const bool xrole = sp >= 0 && sp < XI, hrole = sp >= 0 && sp < XH;
+  // With a single tile across the width both halo columns are padding (the
+  // tile starts at column 0 and is at least as wide as the image): their LDS
+  // words stay zero and nothing is loaded for them.
+  const bool halo_loads = tiles_w > 1;
 
-  u32x4 sx[VEC ? 8 : 1];
-  u32x4 sw[VEC ? WK : 1][VEC ? NSTG : 1];
-  u32x4 hr = {0u, 0u, 0u, 0u};
+  constexpr int NSET = WSPEC ? 1 : 2;
+  constexpr int WBASE = WSPEC ? 8 : 0;  // first register word of the weight items
+  constexpr int SLOTS = WSPEC ? 8 + WK * NSTG : (NSTG > 8 ? NSTG : 8);
+  u32x4 st[NSET][VEC ? SLOTS : 1];
+  // halo values as loaded (one channel each); packed into a word when the
+  // fill is written, so that issuing the loads never waits for them
+  uint32_t hv[NSET][8];
+#pragma unroll
+  for (int k = 0; k < NSET; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hv[k][i] = 0u;
+  // register set of fill f >= 1 (fill 0 is staged through set 0)
+  using Set0 = std::integral_constant<int, 0>;
+  using SetOdd = std::integral_constant<int, NSET - 1>;
 
   // Byte offsets, computed once; a fill adds the channel step.  Items
   // outside the tensors hold kOutside and read zero.
@@ -215,20 +237,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const uint32_t wstep = MODE == kFwd ? 2u * 16u * 9u : 2u * 16u * 9u * (uint32_t)Cout;
   const uint32_t wrow = 2u * 9u * (uint32_t)Cout;
 
-  auto load_tiles = [&](int c0) {
+  auto load_tiles = [&](auto set_c, int c0) {
+    constexpr int S = decltype(set_c)::value;
     const uint32_t f = (uint32_t)(c0 / 16);
     if (xrole) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sx[i] = buffer_load16(sv, xoff + f * xstep + (uint32_t)i * hw2);
+      for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, xoff + f * xstep + (uint32_t)i * hw2);
     }
-    if (hrole) {
-      uint32_t v[8];
+    if (hrole && halo_loads) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = buffer_load2(sv, hoff + f * xstep + (uint32_t)i * hw2);
-      hr.x = v[0] | (v[1] << 16);
-      hr.y = v[2] | (v[3] << 16);
-      hr.z = v[4] | (v[5] << 16);
-      hr.w = v[6] | (v[7] << 16);
+      for (int i = 0; i < 8; ++i) hv[S][i] = buffer_load2(sv, hoff + f * xstep + (uint32_t)i * hw2);
     }
 #pragma unroll
     for (int k = 0; k < WK; ++k) {
@@ -236,32 +254,35 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if constexpr (MODE == kFwd) {
 #pragma unroll
         for (int j = 0; j < 9; ++j)
-          sw[k][j] = buffer_load16(wv, woff[k] + f * wstep + 16u * (uint32_t)j);
+          st[S][WBASE + k * NSTG + j] = buffer_load16(wv, woff[k] + f * wstep + 16u * (uint32_t)j);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          sw[k][i] = buffer_load16(wv, woff[k] + f * wstep + (uint32_t)i * wrow);
+          st[S][WBASE + k * NSTG + i] = buffer_load16(wv, woff[k] + f * wstep + (uint32_t)i * wrow);
       }
     }
   };
 
-  auto store_tiles = [&](int buf) {
+  auto store_tiles = [&](auto set_c, int buf) {
+    constexpr int S = decltype(set_c)::value;
     if (xrole) {
       u32x4* d = xs + buf * XW + xdst;
-      d[0] = column_word<0>(sx);
-      d[1] = column_word<1>(sx);
-      d[2] = column_word<2>(sx);
-      d[3] = column_word<3>(sx);
-      d[4] = column_word<4>(sx);
-      d[5] = column_word<5>(sx);
-      d[6] = column_word<6>(sx);
-      d[7] = column_word<7>(sx);
+      d[0] = column_word<0>(st[S]);
+      d[1] = column_word<1>(st[S]);
+      d[2] = column_word<2>(st[S]);
+      d[3] = column_word<3>(st[S]);
+      d[4] = column_word<4>(st[S]);
+      d[5] = column_word<5>(st[S]);
+      d[6] = column_word<6>(st[S]);
+      d[7] = column_word<7>(st[S]);
     }
     if (hrole) {
       const int side = sp & 1;
       const int t = sp >> 1;  // (g * IMGS + img) * HR + rr
       const int g = t / (IMGS * HR);
-      xs[buf * XW + g * PLW + (t % (IMGS * HR)) * RS + 4 + (side ? TW : -1)] = hr;
+      const u32x4 h = {hv[S][0] | (hv[S][1] << 16), hv[S][2] | (hv[S][3] << 16),
+                       hv[S][4] | (hv[S][5] << 16), hv[S][6] | (hv[S][7] << 16)};
+      xs[buf * XW + g * PLW + (t % (IMGS * HR)) * RS + 4 + (side ? TW : -1)] = h;
     }
     u32x4* wb = wa + buf * WW;
 #pragma unroll
@@ -270,7 +291,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if (it < 0) continue;
       if constexpr (MODE == kFwd) {
         const int co_l = it % BCO, g = it / BCO;
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(sw[k]);
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(&st[S][WBASE + k * NSTG]);
         wb[(0 * 2 + g) * BCO + co_l] = tap_word<0>(d);
         wb[(1 * 2 + g) * BCO + co_l] = tap_word<1>(d);
         wb[(2 * 2 + g) * BCO + co_l] = tap_word<2>(d);
@@ -288,14 +309,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
           const int e = 8 * eb + i;
           wb[((8 - e % 9) * 2 + g) * BCO + e / 9] = v;
         };
-        put(0, column_word<0>(sw[k]));
-        put(1, column_word<1>(sw[k]));
-        put(2, column_word<2>(sw[k]));
-        put(3, column_word<3>(sw[k]));
-        put(4, column_word<4>(sw[k]));
-        put(5, column_word<5>(sw[k]));
-        put(6, column_word<6>(sw[k]));
-        put(7, column_word<7>(sw[k]));
+        put(0, column_word<0>(&st[S][WBASE + k * NSTG]));
+        put(1, column_word<1>(&st[S][WBASE + k * NSTG]));
+        put(2, column_word<2>(&st[S][WBASE + k * NSTG]));
+        put(3, column_word<3>(&st[S][WBASE + k * NSTG]));
+        put(4, column_word<4>(&st[S][WBASE + k * NSTG]));
+        put(5, column_word<5>(&st[S][WBASE + k * NSTG]));
+        put(6, column_word<6>(&st[S][WBASE + k * NSTG]));
+        put(7, column_word<7>(&st[S][WBASE + k * NSTG]));
       }
     }
   };
@@ -349,24 +370,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       wh[((tap * 2 + (ci_l >> 3)) * BCO + co_l) * 8 + (ci_l & 7)] = v;
     }
   };
-  auto stage_next = [&](int chunk) {  // write fill chunk + 1, load fill chunk + 2
+  // Write fill chunk + 1 (held in set_c) to LDS and load fill
+  // chunk + 1 + NSET into the same set.
+  auto stage_next = [&](auto set_c, int chunk) {
     if constexpr (VEC) {
-      if (chunk + 1 < nchunks) store_tiles((chunk + 1) & 1);
-      if (chunk + 2 < nchunks) load_tiles((chunk + 2) * CB);
+      if (chunk + 1 < nchunks) store_tiles(set_c, (chunk + 1) & 1);
+      if (chunk + 1 + NSET < nchunks) load_tiles(set_c, (chunk + 1 + NSET) * CB);
     } else {
       if (chunk + 1 < nchunks) fill_scalar((chunk + 1) * CB, (chunk + 1) & 1);
     }
   };
 
-  // ---- prologue: fill 0 in buffer 0, fill 1 in registers ----
+  // ---- prologue: fill 0 in buffer 0, the next NSET fills in registers ----
   if constexpr (MODE == kFwd) {
     for (int i = tid; i < BCO; i += NT)
       bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
   }
   if constexpr (VEC) {
-    load_tiles(0);
-    store_tiles(0);
-    if (nchunks > 1) load_tiles(CB);
+    load_tiles(Set0{}, 0);
+    store_tiles(Set0{}, 0);
+    if (nchunks > 1) load_tiles(SetOdd{}, CB);
+    if (NSET == 2 && nchunks > 2) load_tiles(Set0{}, 2 * CB);
   } else {
     fill_scalar(0, 0);
   }
@@ -378,9 +402,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       // write fill i + 1 into buffer (i + 1) & 1 (last read by the compute
       // waves before the barrier of fill i - 1) and load fill i + 2.  One
       // barrier per fill, matching the compute waves.
-      for (int chunk = 0; chunk + 1 < nchunks; ++chunk) {
-        stage_next(chunk);
+      for (int chunk = 0; chunk + 1 < nchunks; chunk += 2) {
+        stage_next(SetOdd{}, chunk);
         __syncthreads();
+        if (chunk + 2 < nchunks) {
+          stage_next(Set0{}, chunk + 1);
+          __syncthreads();
+        }
       }
       return;
     }
@@ -410,54 +438,115 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
-  // Operands of one tap: a = weights (MI words), b = pixels (NJ words); tap
-  // t in register set t & 1.
-  u32x4 a[2][MI], b[2][NJ];
-  auto read_tap = [&](int cbuf, int rb, int t) {
-    const u32x4* xb = xs + cbuf * XW;
-    const u32x4* wb = wa + cbuf * WW;
-    const int r = t / 3, s = t % 3;
+  // Single-block wave tiles (one MFMA per tap) would wait out an LDS read
+  // round trip at every tap, so they hold all nine taps of a fill in
+  // registers: slot t is refilled with tap t of the next fill as soon as this
+  // fill's MFMAs of tap t are issued (from the barrier step on), about a fill
+  // ahead of its use.  Larger wave tiles read one tap ahead.
+  constexpr bool DEEP = MI * NJ == 1;
+  if constexpr (DEEP) {
+    // The barrier sits at step kBar: the next fill has been written by then
+    // (by the staging waves, or here after tap 0), and every read of the
+    // buffer it replaces was issued during the previous fill.
+    constexpr int kBar = 2;
+    u32x4 ad[9][MI], bd[9][NJ];
+    auto read_slot = [&](int cbuf, int t) {
+      const u32x4* xb = xs + cbuf * XW;
+      const u32x4* wb = wa + cbuf * WW;
+      const int r = t / 3, s = t % 3;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) a[rb][i] = wb[aoff + t * 2 * BCO + i * 32];
+      for (int i = 0; i < MI; ++i) ad[t][i] = wb[aoff + t * 2 * BCO + i * 32];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) b[rb][j] = xb[boff[j] + r * RS + s];
-  };
-  // Tap t's operands are read while tap t-1's MFMAs run.  The barrier sits
-  // before tap 8's MFMAs: by then the next fill is written (by the staging
-  // waves, or here after tap 0) and every lane has read its last operands of
-  // this one, so tap 0 of the next fill is read while tap 8 runs.
-  read_tap(0, 0, 0);
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    const int cur = chunk & 1;
-    const bool next = chunk + 1 < nchunks;
+      for (int j = 0; j < NJ; ++j) bd[t][j] = xb[boff[j] + r * RS + s];
+    };
 #pragma unroll
-    for (int t = 0; t < 9; ++t) {
-      const int rb = t & 1;
-      if (t + 1 < 9) {
-        read_tap(cur, rb ^ 1, t + 1);
-      } else if (next) {
-        __syncthreads();
-        read_tap(cur ^ 1, rb ^ 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < 9; ++t) read_slot(0, t);
+    auto run_fill = [&](auto set_c, int chunk) {
+      const int cur = chunk & 1;
+      const bool next = chunk + 1 < nchunks;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = mfma_32x32x16_bf16(a[rb][i], b[rb][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!WSPEC) {
-        // written after tap 0: the other buffer was last read before the
-        // previous fill's barrier
-        if (t == 0) stage_next(chunk);
+      for (int t = 0; t < 9; ++t) {
+        if (t == kBar && next) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = mfma_32x32x16_bf16(ad[t][i], bd[t][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!WSPEC) {
+          if (t == 0) stage_next(set_c, chunk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (next && t >= kBar) {
+          if (t == kBar) {
+#pragma unroll
+            for (int u = 0; u <= kBar; ++u) read_slot(cur ^ 1, u);
+          } else {
+            read_slot(cur ^ 1, t);
+          }
+        }
       }
+    };
+    for (int chunk = 0; chunk < nchunks; chunk += 2) {
+      run_fill(SetOdd{}, chunk);
+      if (chunk + 1 < nchunks) run_fill(Set0{}, chunk + 1);
     }
-    // tap 0 of the next fill was read into the second operand set
+  } else {
+    // Operands of one tap: a = weights (MI words), b = pixels (NJ words); tap
+    // t in register set t & 1.
+    u32x4 a[2][MI], b[2][NJ];
+    auto read_tap = [&](int cbuf, int rb, int t) {
+      const u32x4* xb = xs + cbuf * XW;
+      const u32x4* wb = wa + cbuf * WW;
+      const int r = t / 3, s = t % 3;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) a[0][i] = a[1][i];
+      for (int i = 0; i < MI; ++i) a[rb][i] = wb[aoff + t * 2 * BCO + i * 32];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) b[0][j] = b[1][j];
+      for (int j = 0; j < NJ; ++j) b[rb][j] = xb[boff[j] + r * RS + s];
+    };
+    // Tap t's operands are read while tap t-1's MFMAs run.  The barrier sits
+    // before tap 8's MFMAs: by then the next fill is written (by the staging
+    // waves, or here after tap 0) and every lane has read its last operands of
+    // this one, so tap 0 of the next fill is read while tap 8 runs.
+    // One fill; set_c is the staging register set that holds fill chunk + 1.
+    auto run_fill = [&](auto set_c, int chunk) {
+      const int cur = chunk & 1;
+      const bool next = chunk + 1 < nchunks;
+#pragma unroll
+      for (int t = 0; t < 9; ++t) {
+        const int rb = t & 1;
+        if (t + 1 < 9) {
+          read_tap(cur, rb ^ 1, t + 1);
+        } else if (next) {
+          __syncthreads();
+          read_tap(cur ^ 1, rb ^ 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = mfma_32x32x16_bf16(a[rb][i], b[rb][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!WSPEC) {
+          // written after tap 0: the other buffer was last read before the
+          // previous fill's barrier
+          if (t == 0) stage_next(set_c, chunk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // tap 0 of the next fill was read into the second operand set
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[0][i] = a[1][i];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[0][j] = b[1][j];
+    };
+    read_tap(0, 0, 0);
+    for (int chunk = 0; chunk < nchunks; chunk += 2) {
+      run_fill(SetOdd{}, chunk);
+      if (chunk + 1 < nchunks) run_fill(Set0{}, chunk + 1);
+    }
   }
 
   // ---------------- epilogue: NCHW stores ----------------

@@ -69,6 +69,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
+  // With a single tile across the width both halo columns are padding: they
+  // stay zero and are not loaded.
+  const bool halo_loads = tiles_w > 1;
+#pragma unroll
+  for (int k = 0; k < (VEC ? XH_N : 1); ++k) xf[k] = 0.f;
 
   // ---------------- staging: weight tile ----------------
   // Forward: for each co, the CB x 9 weights w[co, c0.., :] are contiguous.
@@ -107,6 +112,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
+        if (!halo_loads) break;
         const int it = tid + k * NT;
         const int side = it & 1;
         int t = it >> 1;

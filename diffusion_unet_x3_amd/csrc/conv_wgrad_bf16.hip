@@ -15,6 +15,8 @@
 // chunk is 128 pixels (8 MFMA steps; 64 for 8-wide images), staged through
 // buffer views into double-buffered LDS, one barrier per chunk.  Partial
 // sums and the split-K reduce are those of the float32 kernel.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -71,15 +73,24 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   constexpr int XN = (XI + NT - 1) / NT;
   constexpr int HI_ = 64 * IMGS * HR * 2;         // x halo elements
   constexpr int HN = (HI_ + NT - 1) / NT;
-  u32x4 gv[VEC ? GN : 1];
-  u32x4 xv[VEC ? XN : 1];
-  uint16_t xh[VEC ? HN : 1];
+  // Two register sets: the global loads of chunk i + 3 are issued into the
+  // set just emptied into LDS for chunk i + 1, so each load has two chunks of
+  // MFMA work to arrive.
+  u32x4 gv[2][VEC ? GN : 1];
+  u32x4 xv[2][VEC ? XN : 1];
+  uint16_t xh[2][VEC ? HN : 1];
+  // With a single tile across the width both halo columns are padding: they
+  // stay zero and are not loaded.
+  const bool halo_loads = tiles_w > 1;
+#pragma unroll
+  for (int k = 0; k < (VEC ? HN : 1); ++k) xh[0][k] = xh[1][k] = 0;
 
   // Vector path: buffer views; an item outside the tensors or the image
   // reads zero through an offset past the view (32-bit offset arithmetic).
   const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
   const __amdgpu_buffer_rsrc_t xview = buffer_view(x, x_bytes);
-  auto load_tiles = [&](int chunk) {
+  auto load_tiles = [&](auto set_c, int chunk) {
+    constexpr int SET = decltype(set_c)::value;
     if constexpr (VEC) {
       const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
 #pragma unroll
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 8 * q;
         const bool ok = (GI % NT == 0 || it < GI) && n < N && kk < K && h < H && w < W;
-        gv[k] = buffer_load16(gview, ok ? 2u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside);
+        gv[SET][k] = buffer_load16(gview, ok ? 2u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside);
       }
 #pragma unroll
       for (int k = 0; k < XN; ++k) {
@@ -106,10 +117,11 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int cl = t / IMGS;
         const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
         const bool ok = (XI % NT == 0 || it < XI) && n < N && c < C && h >= 0 && h < H && w < W;
-        xv[k] = buffer_load16(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w) : kOutside);
+        xv[SET][k] = buffer_load16(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w) : kOutside);
       }
 #pragma unroll
       for (int k = 0; k < HN; ++k) {
+        if (!halo_loads) break;
         const int it = tid + k * NT;
         const int side = it & 1;
         int t = it >> 1;
@@ -121,13 +133,14 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int w = o.w0 + (side ? TW : -1);
         const bool ok = (HI_ % NT == 0 || it < HI_) && n < N && c < C && h >= 0 && h < H &&
                         w >= 0 && w < W;
-        xh[k] = (uint16_t)buffer_load2(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w)
+        xh[SET][k] = (uint16_t)buffer_load2(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w)
                                                  : kOutside);
       }
     }
   };
 
-  auto store_tiles = [&](int chunk, int buf) {
+  auto store_tiles = [&](auto set_c, int chunk, int buf) {
+    constexpr int SET = decltype(set_c)::value;
     uint16_t* gs = gs_buf[buf];
     uint16_t* xs = xs_buf[buf];
     if constexpr (VEC) {
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int q = it % XQ;
           const int t = it / XQ;  // (kl * IMGS + img) * TH + row
           const int kl = t / (IMGS * TH);
-          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = gv[k];
+          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = gv[SET][k];
         }
       }
 #pragma unroll
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int q = it % XQ;
           const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
           const int cl = t / (IMGS * HR);
-          *reinterpret_cast<u32x4*>(&xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + 8 * q]) = xv[k];
+          *reinterpret_cast<u32x4*>(&xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + 8 * q]) = xv[SET][k];
         }
       }
 #pragma unroll
@@ -158,7 +171,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int side = it & 1;
           const int t = it >> 1;
           const int cl = t / (IMGS * HR);
-          xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + (side ? TW : -1)] = xh[k];
+          xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + (side ? TW : -1)] = xh[SET][k];
         }
       }
     } else {
@@ -228,18 +241,22 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   };
 
   // Chunk i is computed from LDS buffer i & 1.  After its second MFMA step
-  // the registers holding chunk i + 1 are written to the other buffer (last
+  // the register set holding chunk i + 1 is written to the other buffer (last
   // read in chunk i - 1, before the barrier that ended it) and the global
-  // loads of chunk i + 2 are issued into them, so staging runs beside the
-  // MFMAs of waves that are still computing.  One barrier per chunk.
+  // loads of chunk i + 3 are issued into it, so staging runs beside the MFMAs
+  // of waves that are still computing.  One barrier per chunk.
   constexpr int kStoreStep = 1;
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
   if (chunk_begin < chunk_end) {
-    load_tiles(chunk_begin);
-    store_tiles(chunk_begin, 0);
-    if (chunk_begin + 1 < chunk_end) load_tiles(chunk_begin + 1);
+    load_tiles(Set0{}, chunk_begin);
+    store_tiles(Set0{}, chunk_begin, 0);
+    if (chunk_begin + 1 < chunk_end) load_tiles(Set1{}, chunk_begin + 1);
+    if (chunk_begin + 2 < chunk_end) load_tiles(Set0{}, chunk_begin + 2);
     __syncthreads();
   }
-  for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
+  // One chunk; SET is the register set that holds chunk + 1.
+  auto run_chunk = [&](auto set_c, int chunk) {
     const int cur = (chunk - chunk_begin) & 1;
     const uint16_t* gs = gs_buf[cur];
     const uint16_t* xs = xs_buf[cur];
@@ -265,8 +282,8 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
       acc[2] = mfma_32x32x16_bf16(ga[cb_], right, acc[2]);
       if (ks == kStoreStep && chunk + 1 < chunk_end) {
         __builtin_amdgcn_sched_barrier(0);
-        store_tiles(chunk + 1, cur ^ 1);
-        if (chunk + 2 < chunk_end) load_tiles(chunk + 2);
+        store_tiles(set_c, chunk + 1, cur ^ 1);
+        if (chunk + 3 < chunk_end) load_tiles(set_c, chunk + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -276,6 +293,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
       for (int i = 0; i < P / 4; ++i) dbsum += bf16_to_f32(gs[kl * GSB + part + 4 * i]);
     }
     __syncthreads();
+  };
+  for (int chunk = chunk_begin; chunk < chunk_end; chunk += 2) {
+    run_chunk(Set1{}, chunk);
+    if (chunk + 1 < chunk_end) run_chunk(Set0{}, chunk + 1);
   }
 
   const int c = c0 + cb * 32 + l32;

@@ -77,6 +77,11 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   f32x4 gv[VEC ? GV_N : 1];
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
+  // With a single tile across the width both halo columns are padding: they
+  // stay zero and are not loaded.
+  const bool halo_loads = tiles_w > 1;
+#pragma unroll
+  for (int k = 0; k < (VEC ? XH_N : 1); ++k) xf[k] = 0.f;
 
   // Vector path: buffer views; an item outside the tensors or the image
   // reads zero through an offset past the view (32-bit offset arithmetic,
@@ -119,6 +124,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
+        if (!halo_loads) break;
         const int it = tid + k * NT;
         const int side = it & 1;
         int t = it >> 1;

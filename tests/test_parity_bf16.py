@@ -19,7 +19,9 @@ pytestmark = pytest.mark.gpu
 SMALL = [(2, 64, 64, 32, 32), (1, 1, 1, 1, 1), (1, 3, 5, 7, 9), (2, 17, 33, 5, 13),
          (3, 64, 64, 31, 33), (1, 513, 7, 8, 8), (2, 16, 24, 8, 16), (2, 40, 130, 10, 72),
          (1, 136, 24, 6, 16), (3, 8, 8, 17, 8), (5, 16, 16, 8, 8), (2, 32, 72, 16, 16),
-         (1, 24, 40, 12, 64)]
+         (1, 24, 40, 12, 64),
+         # vector paths with two and three tiles across the width (halo columns loaded)
+         (2, 32, 48, 9, 80), (1, 16, 32, 4, 136)]
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))

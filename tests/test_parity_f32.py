@@ -21,6 +21,8 @@ SMALL = [(2, 64, 64, 32, 32)] + wl.RAGGED_SHAPES + [
     (3, 8, 8, 17, 8),       # W = 8 tiles, H over 16
     (5, 16, 16, 8, 8),      # 8x8 images in pairs, odd image count
     (2, 32, 72, 16, 16),
+    (2, 24, 40, 9, 80),     # vector path, two tiles across the width (halo columns loaded)
+    (1, 16, 16, 4, 136),    # vector path, three tiles across the width
 ]
 
 

@@ -67,3 +67,15 @@ def test_weight_gradient_plans(shape, dtype):
     ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)
     assert ws == p["workspace_bytes"]
     assert ws == (0 if S == 1 else S * (K * C * 9 + K) * 4)
+
+
+@pytest.mark.parametrize("shape,dtype", [((2, 24, 40, 9, 80), 0), ((1, 16, 16, 4, 136), 0),
+                                         ((2, 32, 48, 9, 80), 1), ((1, 16, 32, 4, 136), 1)])
+def test_wide_parity_shapes_span_several_tiles(shape, dtype):
+    """The parity shapes that exercise halo-column loads really put more than
+    one tile across the width in every pass (with a single tile the halo
+    columns are padding and the kernels load nothing for them)."""
+    N, C, K, H, W = shape
+    for pass_ in (lib3.PASS_FWD, lib3.PASS_BWD_DATA, lib3.PASS_BWD_WEIGHT):
+        p = lib3.conv3x3_plan(pass_, N, C, K, H, W, dtype)
+        assert math.ceil(W / p["tile_w"]) > 1
