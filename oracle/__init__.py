@@ -11,6 +11,12 @@ UNet project, sections "How It Works", "Quick Start & Requirements" and
 All functions take numpy arrays or CPU torch tensors (any real dtype; they are
 widened to float64, which is exact for float32 and bfloat16 values) and return
 float64 numpy arrays.
+
+The fused-activation functions (``act_*``, ``conv3x3_fwd_act``,
+``conv3x3_bwd_act``) follow the reading in the C file's "fused activation"
+section: activation 0 = identity, 1 = SiLU, 2 = leaky ReLU (slope 0.2) on the
+biased convolution output z; the backward takes the gradient at the
+activation's output and multiplies it by act'(z).
 """
 import ctypes
 import os
@@ -22,6 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # CONV3X3_ORACLE_LIB lets the pin suite run against a deliberately broken
 # build (tests/test_oracle_mutants.py); normal use never sets it.
 LIB_PATH = os.environ.get("CONV3X3_ORACLE_LIB") or os.path.join(_HERE, "liboracle_conv3x3.so")
+
+ACT_NONE, ACT_SILU, ACT_LRELU = 0, 1, 2
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I64 = ctypes.POINTER(ctypes.c_int64)
@@ -67,10 +75,14 @@ class Oracle:
         lib.oracle_conv3x3_bwd_data_at.argtypes = [_D, _D, _i, _i, _i, _i, _i, _I64, _n, _D]
         lib.oracle_conv3x3_bwd_weight_at.argtypes = [_D, _D, _i, _i, _i, _i, _i, _I64, _n, _D]
         lib.oracle_conv3x3_bias_grad_at.argtypes = [_D, _i, _i, _i, _i, _I64, _n, _D]
+        lib.oracle_act_forward.argtypes = [_D, _D, _n, _i]
+        lib.oracle_act_grad.argtypes = [_D, _D, _D, _n, _i]
+        lib.oracle_act_grad_bf16.argtypes = [_D, _D, _D, _n, _i]
         for f in ("oracle_conv3x3_fwd", "oracle_conv3x3_bwd_data",
                   "oracle_conv3x3_bwd_weight", "oracle_conv3x3_fwd_at",
                   "oracle_conv3x3_bwd_data_at", "oracle_conv3x3_bwd_weight_at",
-                  "oracle_conv3x3_bias_grad_at", "oracle_num_threads"):
+                  "oracle_conv3x3_bias_grad_at", "oracle_act_forward", "oracle_act_grad",
+                  "oracle_act_grad_bf16", "oracle_num_threads"):
             getattr(lib, f).restype = _i
         self.lib = lib
 
@@ -143,6 +155,23 @@ class Oracle:
                                                      _p(out)), "bwd_weight_at")
         return out
 
+    def act_forward(self, z, act):
+        """act(z), elementwise, same shape."""
+        z = _f64(z)
+        y = np.empty_like(z)
+        _check(self.lib.oracle_act_forward(_p(z), _p(y), z.size, act), "act_forward")
+        return y
+
+    def act_grad(self, gy, z, act, bf16=False):
+        """g = gy * act'(z), elementwise.  bf16=True: the product is formed in
+        float32 and rounded to bfloat16 (the bfloat16 path's operand)."""
+        gy, z = _f64(gy), _f64(z)
+        assert gy.shape == z.shape
+        g = np.empty_like(gy)
+        f = self.lib.oracle_act_grad_bf16 if bf16 else self.lib.oracle_act_grad
+        _check(f(_p(gy), _p(z), _p(g), gy.size, act), "act_grad")
+        return g
+
     def conv3x3_bias_grad_at(self, g, idx):
         """db[idx], each element computed on its own."""
         g, idx = _f64(g), _idx(idx)
@@ -196,3 +225,26 @@ def conv3x3_bwd_weight_at(x, g, idx):
 
 def conv3x3_bias_grad_at(g, idx):
     return _o().conv3x3_bias_grad_at(g, idx)
+
+
+def act_forward(z, act):
+    return _o().act_forward(z, act)
+
+
+def act_grad(gy, z, act, bf16=False):
+    return _o().act_grad(gy, z, act, bf16)
+
+
+def conv3x3_fwd_act(x, w, b, act):
+    """(y, z): z = conv3x3_fwd(x, w, b), y = act(z)."""
+    z = conv3x3_fwd(x, w, b)
+    return act_forward(z, act), z
+
+
+def conv3x3_bwd_act(x, w, gy, z, act, bf16=False, want_db=True):
+    """(dx, dw, db) of L = <act(z), gy> with z = conv3x3_fwd(x, w, b): the
+    convolution's backward on g = gy * act'(z)."""
+    g = act_grad(gy, z, act, bf16)
+    dx = conv3x3_bwd_data(g, w)
+    dw, db = conv3x3_bwd_weight(x, g, want_db)
+    return dx, dw, db

@@ -34,8 +34,10 @@
  * delta / shift / identity invariants, bilinearity, the adjoint identities,
  * central finite differences of L, and torch.nn.functional.conv2d in float64.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -229,6 +231,81 @@ int oracle_conv3x3_bias_grad_at(const double* g, int N, int K, int H, int W,
     if (idx[j] < 0 || idx[j] >= K) return 2;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t j = 0; j < count; ++j) out[j] = bias_grad_one(g, N, K, H, W, (int)idx[j]);
+  return 0;
+}
+
+/* ---- fused activation ------------------------------------------------------
+ * The project-guide page on StyleGAN2's custom CUDA kernels describes fusing a
+ * bias and an activation (a leaky ReLU that comes with a bias term) into one
+ * operation, to save memory traffic; the diffusion UNet's activation is SiLU.
+ * Read as: the forward convolution's output with its bias, z, goes through
+ *   act 0: identity     act(z) = z
+ *   act 1: SiLU         act(z) = z * sigmoid(z)
+ *   act 2: leaky ReLU   act(z) = z (z >= 0), 0.2 z (z < 0)   (no gain)
+ * and the backward pass multiplies the gradient arriving at act's output, gy,
+ * by act'(z) to get the convolution's output gradient g = gy * act'(z).  The
+ * derivatives, written out from the definitions:
+ *   SiLU:        act'(z) = s (1 + z (1 - s)),  s = sigmoid(z) = 1 / (1 + e^-z)
+ *   leaky ReLU:  act'(z) = 1 for z > 0, 0.2 otherwise (z = 0 takes the slope)
+ */
+static double act_value(int act, double z) {
+  if (act == 1) return z / (1.0 + exp(-z));
+  if (act == 2) return z >= 0.0 ? z : 0.2 * z;
+  return z;
+}
+
+static double act_slope(int act, double z) {
+  if (act == 1) {
+    double sg = 1.0 / (1.0 + exp(-z));
+    return sg * (1.0 + z * (1.0 - sg));
+  }
+  if (act == 2) return z > 0.0 ? 1.0 : 0.2;
+  return 1.0;
+}
+
+/* The same slope evaluated in float arithmetic: the bfloat16 path forms
+ * g = gy * act'(z) in float32 before rounding it to a bfloat16 operand. */
+static float act_slope_f32(int act, float z) {
+  if (act == 1) {
+    float sg = 1.0f / (1.0f + expf(-z));
+    return sg * (1.0f + z * (1.0f - sg));
+  }
+  if (act == 2) return z > 0.0f ? 1.0f : 0.2f;
+  return 1.0f;
+}
+
+/* float -> bfloat16 -> float, round to nearest, ties to even (finite inputs). */
+static float round_bf16(float v) {
+  uint32_t u;
+  memcpy(&u, &v, sizeof u);
+  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+  memcpy(&v, &u, sizeof v);
+  return v;
+}
+
+static int bad_act(int act) { return act < 0 || act > 2; }
+
+int oracle_act_forward(const double* z, double* y, int64_t n, int act) {
+  if (!z || !y || n < 0 || bad_act(act)) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) y[i] = act_value(act, z[i]);
+  return 0;
+}
+
+int oracle_act_grad(const double* gy, const double* z, double* g, int64_t n, int act) {
+  if (!gy || !z || !g || n < 0 || bad_act(act)) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) g[i] = gy[i] * act_slope(act, z[i]);
+  return 0;
+}
+
+/* bfloat16 path: gy is a bfloat16 value and z a float32 value (both exact in
+ * double); g = bf16(float(gy) * act'_f32(float(z))). */
+int oracle_act_grad_bf16(const double* gy, const double* z, double* g, int64_t n, int act) {
+  if (!gy || !z || !g || n < 0 || bad_act(act)) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    g[i] = (double)round_bf16((float)gy[i] * act_slope_f32(act, (float)z[i]));
   return 0;
 }
 

@@ -1,7 +1,8 @@
 """The pins must be sharp: plant one plausible mistake at a time in a copy of
 the oracle's C source (a flipped tap offset, a dropped bias, an unflipped or
 transposed weight, a dropped channel, a wrong padding bound, a short bias
-gradient), build it with gcc into a temporary directory, and check that the
+gradient, a wrong activation value, slope or bfloat16 rounding), build it with
+gcc into a temporary directory, and check that the
 oracle pin suite fails against every mutant while it passes on the real
 build.  Everything here runs on the CPU."""
 import os
@@ -14,12 +15,12 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "conv3x3_oracle.c")
 PIN_FILES = ["test_oracle_hand.py", "test_oracle_invariants.py", "test_oracle_adjoint.py",
-             "test_oracle_fd.py", "test_oracle_torch.py"]
+             "test_oracle_fd.py", "test_oracle_torch.py", "test_oracle_act.py"]
 
 
 def _func(src, name):
     """(start, end) of a static function's text in the source."""
-    m = re.search(r"static double " + name + r"\(", src)
+    m = re.search(r"static (?:double|float) " + name + r"\(", src)
     assert m, name
     end = src.index("\n}\n", m.start()) + 3
     return m.start(), end
@@ -45,6 +46,12 @@ MUTANTS = {
                                  "g[IDX4(n, k, h, w, K, H, W)] * x[IDX4(n, c, ih, iw, C, H, W)]",
                                  "g[IDX4(n, k, ih, iw, K, H, W)] * x[IDX4(n, c, h, w, C, H, W)]"),
     "bias_grad_short_row": ("bias_grad_one", "w < W;", "w + 1 < W;"),
+    "silu_sigmoid_sign": ("act_value", "exp(-z)", "exp(z)"),
+    "lrelu_value_slope": ("act_value", "0.2 * z", "0.02 * z"),
+    "silu_slope_dropped_term": ("act_slope", "sg * (1.0 + z * (1.0 - sg))", "sg"),
+    "lrelu_slope_sides_swapped": ("act_slope", "z > 0.0 ? 1.0 : 0.2", "z > 0.0 ? 0.2 : 1.0"),
+    "silu_f32_slope_wrong": ("act_slope_f32", "z * (1.0f - sg)", "z * sg"),
+    "bf16_truncates": ("round_bf16", "(u + 0x7fffu + ((u >> 16) & 1u))", "(u)"),
 }
 
 
@@ -67,6 +74,6 @@ def test_pins_reject_mutant(name, tmp_path):
     c.write_text(mutated)
     so = tmp_path / "libmutant.so"
     subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                           "-o", str(so), str(c)])
+                           "-o", str(so), str(c), "-lm"])
     r = _run_pins(str(so))
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
