@@ -108,21 +108,36 @@ def flops_per_pass(N, C, K, H, W):
     return 2.0 * N * H * W * C * K * 9
 
 
-def alg_bytes(pass_, N, C, K, H, W, dtype):
-    """Each tensor crosses HBM once: inputs at their dtype, outputs float32."""
+ACT_CODES = {"none": 0, "silu": 1, "lrelu": 2}
+
+
+def fused_backward(act, dtype):
+    """The backward passes fuse the activation on float32 only."""
+    return act != "none" and dtype == "f32"
+
+
+def alg_bytes(pass_, N, C, K, H, W, dtype, act="none"):
+    """Each tensor crosses HBM once: inputs at their dtype, outputs float32.
+    With a fused activation the forward also writes z and the fused backward
+    passes also read it (float32, the output's shape)."""
     s = 4 if dtype == "f32" else 2
     M = N * H * W
+    z = 4 * M * K
     if pass_ == "fwd":
-        return s * (M * C + 9 * K * C) + 4 * K + 4 * M * K
+        return s * (M * C + 9 * K * C) + 4 * K + 4 * M * K + (z if act != "none" else 0)
+    extra = z if fused_backward(act, dtype) else 0
     if pass_ == "bwd_data":
-        return s * (M * K + 9 * K * C) + 4 * M * C
-    return s * (M * C + M * K) + 4 * (9 * K * C + K)
+        return s * (M * K + 9 * K * C) + 4 * M * C + extra
+    return s * (M * C + M * K) + 4 * (9 * K * C + K) + extra
 
 
 class LayerRun:
-    """Device buffers and the three pass launches of one layer."""
+    """Device buffers and the three pass launches of one layer.  act: the
+    forward fuses the activation (and writes z), the float32 backward passes
+    read z and fuse its derivative; the bfloat16 backward passes run on gy
+    as is."""
 
-    def __init__(self, layer):
+    def __init__(self, layer, act="none"):
         import torch
         import diffusion_unet_x3_amd as lib3
         import workloads as wl
@@ -136,18 +151,32 @@ class LayerRun:
         self.dx = torch.empty((N, C, H, W), device=dev)
         self.dw = torch.empty((K, C, 3, 3), device=dev)
         self.db = torch.empty((K,), device=dev)
+        self.act = ACT_CODES[act]
+        self.fused_bwd = fused_backward(act, layer.dtype)
+        self.z = torch.empty((N, K, H, W), device=dev) if self.act else None
         code = lib3.CONV3X3_F32 if layer.dtype == "f32" else lib3.CONV3X3_BF16
         ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def fwd(self):
-        self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y)
+        if self.act:
+            self.lib3.conv3x3_fwd_act(self.x, self.w, self.b, act=self.act, out=self.y, z=self.z)
+        else:
+            self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y)
 
     def bwd_data(self):
-        self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx)
+        if self.fused_bwd:
+            self.lib3.conv3x3_bwd_data_act(self.g, self.z, self.w, act=self.act, out=self.dx)
+        else:
+            self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx)
 
     def bwd_weight(self):
-        self.lib3.conv3x3_bwd_weight(self.x, self.g, dw=self.dw, db=self.db, workspace=self.ws)
+        if self.fused_bwd:
+            self.lib3.conv3x3_bwd_weight_act(self.x, self.g, self.z, act=self.act, dw=self.dw,
+                                             db=self.db, workspace=self.ws)
+        else:
+            self.lib3.conv3x3_bwd_weight(self.x, self.g, dw=self.dw, db=self.db,
+                                         workspace=self.ws)
 
     def passes(self):
         return (("fwd", self.fwd), ("bwd_data", self.bwd_data), ("bwd_weight", self.bwd_weight))
@@ -206,7 +235,7 @@ def cpu_baseline(layer, budget_s=15.0):
                       f"({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); cpu: {platform.processor() or platform.machine()}"}
 
 
-def sweep(out_path, steps, warmup, match=None):
+def sweep(out_path, steps, warmup, match=None, act="none"):
     import re
     import torch
     import workloads as wl
@@ -215,16 +244,16 @@ def sweep(out_path, steps, warmup, match=None):
         for layer in layers:
             if match and not re.search(match, layer.name):
                 continue
-            run = LayerRun(layer)
+            run = LayerRun(layer, act)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
             f = flops_per_pass(N, C, K, H, W)
-            row = {"config": cfg, "layer": layer.name, "dtype": layer.dtype,
+            row = {"config": cfg, "layer": layer.name, "dtype": layer.dtype, "act": act,
                    "shape": [N, C, K, H, W], "ms_step": ms}
             for p, t in per.items():
                 tf = f / (t * 1e-3) / 1e12
                 row[p] = {"ms": t, "tflops": tf, "mfma_frac": tf / PEAK_TFLOPS[layer.dtype],
-                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype) / (t * 1e-3) / 1e9}
+                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype, act) / (t * 1e-3) / 1e9}
             rows.append(row)
             print(f"{layer.name:44s} " + " ".join(
                 f"{p}={row[p]['ms'] * 1e3:8.1f}us {row[p]['tflops']:7.1f}TF" for p in per),
@@ -243,6 +272,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", metavar="OUT_JSON", help="also time every configured layer")
     ap.add_argument("--sweep-match", metavar="REGEX", help="only sweep layers whose name matches")
+    ap.add_argument("--act", choices=sorted(ACT_CODES), default="none",
+                    help="time the fused-activation entry points (forward epilogue; "
+                         "float32 backward prologue) instead of the plain ones")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -262,7 +294,7 @@ def main():
     import workloads as wl
     layer = wl.CONFIGS[2][0]
     N, C, K, H, W = layer.shape
-    run = LayerRun(layer)
+    run = LayerRun(layer, args.act)
     ms, per = time_layer(run, args.steps, args.warmup)
     f = flops_per_pass(N, C, K, H, W)
     value = 3 * f / (ms * 1e-3) / 1e12
@@ -273,7 +305,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": layer.dtype, "data": "synthetic",
-        "config": {"workload": "unet_stem_conv3x3_fwd_bias+bwd_data+bwd_weight",
+        "config": {"workload": "unet_stem_conv3x3_fwd_bias+bwd_data+bwd_weight" if args.act == "none"
+                   else f"unet_stem_conv3x3_fwd_bias_{args.act}+bwd_data+bwd_weight (fused {args.act})",
                    "N": N, "C_in": C, "C_out": K, "H": H, "W": W, "stride": 1, "pad": 1,
                    "layout": "NCHW", "seed": layer.seed, "global_batch": N,
                    "parallelism": "single_gpu"},
@@ -281,11 +314,11 @@ def main():
                      "achieved": round(achieved, 3),
                      "peak": PEAK_TFLOPS[layer.dtype], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS[layer.dtype], 4),
-                     "traffic": recorded_traffic(dom),
-                     "alg_bytes": alg_bytes(dom, N, C, K, H, W, layer.dtype)},
+                     "traffic": recorded_traffic(dom) if args.act == "none" else None,
+                     "alg_bytes": alg_bytes(dom, N, C, K, H, W, layer.dtype, args.act)},
         "passes": {p: {"us": round(t * 1e3, 2),
                        "tflops": round(f / (t * 1e-3) / 1e12, 2),
-                       "alg_gbs": round(alg_bytes(p, N, C, K, H, W, layer.dtype) /
+                       "alg_gbs": round(alg_bytes(p, N, C, K, H, W, layer.dtype, args.act) /
                                         (t * 1e-3) / 1e9, 1)} for p, t in per.items()},
     }
     del run
@@ -300,7 +333,7 @@ def main():
         del a, b
         torch.cuda.empty_cache()
     if args.sweep:
-        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match)
+        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -9,8 +9,17 @@ device memory and the current stream.  The functions carry the C names:
     conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None,
                        workspace=None)                        -> (dw, db)
     conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)   -> bytes
+    conv3x3_fwd_act(x, w, bias=None, act=ACT_SILU, want_z=True,
+                    out=None, z=None)                         -> (y, z)
+    conv3x3_bwd_data_act(gy, z, w, act=ACT_SILU, out=None)    -> dx
+    conv3x3_bwd_weight_act(x, gy, z, act=ACT_SILU, want_db=True,
+                           dw=None, db=None, workspace=None)  -> (dw, db)
     conv3x3_status_string(code)                               -> str
     conv3x3_plan(pass_, N, C, K, H, W, dtype)                 -> dict
+
+The *_act functions fuse an activation (ACT_NONE, ACT_SILU, ACT_LRELU) into
+the forward epilogue and, through z = the forward's pre-activation, into the
+gradient loader of the backward passes (float32 backward only).
 
 Tensors are NCHW / OIHW, contiguous, on a GPU; x, w, g are float32 or
 bfloat16 (all three alike), bias is float32, outputs are float32.  There is
@@ -27,12 +36,15 @@ LIB_PATH = os.path.join(_HERE, "libconv3x3.so")
 CONV3X3_F32 = 0
 CONV3X3_BF16 = 1
 PASS_FWD, PASS_BWD_DATA, PASS_BWD_WEIGHT = 0, 1, 2
+ACT_NONE, ACT_SILU, ACT_LRELU = 0, 1, 2
 STATUS = {
     "OK": 0, "ERR_NULL_POINTER": 1, "ERR_BAD_SHAPE": 2, "ERR_BAD_DTYPE": 3,
     "ERR_WORKSPACE": 4, "ERR_ALIAS": 5, "ERR_HIP": 6, "ERR_BAD_PASS": 7,
+    "ERR_BAD_ACT": 8, "ERR_UNSUPPORTED": 9,
 }
 EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_size",
-            "conv3x3_bwd_weight", "conv3x3_status_string", "conv3x3_plan"]
+            "conv3x3_bwd_weight", "conv3x3_status_string", "conv3x3_plan",
+            "conv3x3_fwd_act", "conv3x3_bwd_data_act", "conv3x3_bwd_weight_act"]
 
 
 class Plan(ctypes.Structure):
@@ -58,6 +70,13 @@ def _load():
     lib.conv3x3_bwd_weight.argtypes = [vp, vp, fp, fp, vp, ctypes.c_size_t,
                                        i, i, i, i, i, i, vp]
     lib.conv3x3_bwd_weight.restype = i
+    lib.conv3x3_fwd_act.argtypes = [vp, vp, fp, fp, fp, i, i, i, i, i, i, i, vp]
+    lib.conv3x3_fwd_act.restype = i
+    lib.conv3x3_bwd_data_act.argtypes = [vp, fp, vp, fp, i, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data_act.restype = i
+    lib.conv3x3_bwd_weight_act.argtypes = [vp, vp, fp, fp, fp, vp, ctypes.c_size_t,
+                                           i, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight_act.restype = i
     lib.conv3x3_status_string.argtypes = [i]
     lib.conv3x3_status_string.restype = ctypes.c_char_p
     lib.conv3x3_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
@@ -172,6 +191,80 @@ def conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None, workspace=None):
                                 None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
                                 N, C, K, H, W, code, _stream(x))
     _raise(rc, "conv3x3_bwd_weight")
+    return dw, db
+
+
+def conv3x3_fwd_act(x, w, bias=None, act=ACT_SILU, want_z=True, out=None, z=None):
+    """(y, z): z = conv3x3(x; w) + bias, y = act(z), both float32 (z None
+    unless want_z)."""
+    _check(x, "x", 4)
+    _check(w, "w", 4)
+    N, C, H, W = x.shape
+    K = w.shape[0]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != x.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with x's dtype")
+    if bias is not None:
+        _check(bias, "bias", 1)
+        if bias.dtype != torch.float32 or bias.shape[0] != K:
+            raise ValueError("bias must be float32 [K]")
+    y = _f32_out(out, (N, K, H, W), x, "out")
+    z = _f32_out(z, (N, K, H, W), x, "z") if want_z else None
+    rc = lib.conv3x3_fwd_act(x.data_ptr(), w.data_ptr(),
+                             None if bias is None else bias.data_ptr(), y.data_ptr(),
+                             None if z is None else z.data_ptr(),
+                             N, C, K, H, W, _dtype_code(x), int(act), _stream(x))
+    _raise(rc, "conv3x3_fwd_act")
+    return y, z
+
+
+def _check_z(z, shape):
+    _check(z, "z", 4)
+    if z.dtype != torch.float32 or tuple(z.shape) != tuple(shape):
+        raise ValueError(f"z must be float32 of shape {tuple(shape)}")
+
+
+def conv3x3_bwd_data_act(gy, z, w, act=ACT_SILU, out=None):
+    """dx of <act(conv3x3(x; w) + b), gy>, given z = conv3x3(x; w) + b."""
+    _check(gy, "gy", 4)
+    _check(w, "w", 4)
+    N, K, H, W = gy.shape
+    C = w.shape[1]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != gy.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with gy's dtype")
+    if z is not None:
+        _check_z(z, (N, K, H, W))
+    dx = _f32_out(out, (N, C, H, W), gy, "out")
+    rc = lib.conv3x3_bwd_data_act(gy.data_ptr(), None if z is None else z.data_ptr(),
+                                  w.data_ptr(), dx.data_ptr(), N, C, K, H, W, _dtype_code(gy),
+                                  int(act), _stream(gy))
+    _raise(rc, "conv3x3_bwd_data_act")
+    return dx
+
+
+def conv3x3_bwd_weight_act(x, gy, z, act=ACT_SILU, want_db=True, dw=None, db=None,
+                           workspace=None):
+    """(dw, db) of <act(conv3x3(x; w) + b), gy>, given z = conv3x3(x; w) + b."""
+    _check(x, "x", 4)
+    _check(gy, "gy", 4)
+    N, C, H, W = x.shape
+    K = gy.shape[1]
+    if tuple(gy.shape) != (N, K, H, W) or gy.dtype != x.dtype:
+        raise ValueError("gy must be [N, K, H, W] with x's dtype")
+    if z is not None:
+        _check_z(z, (N, K, H, W))
+    code = _dtype_code(x)
+    dw = _f32_out(dw, (K, C, 3, 3), x, "dw")
+    db = _f32_out(db, (K,), x, "db") if want_db else None
+    need = conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.conv3x3_bwd_weight_act(x.data_ptr(), gy.data_ptr(),
+                                    None if z is None else z.data_ptr(), dw.data_ptr(),
+                                    None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
+                                    N, C, K, H, W, code, int(act), _stream(x))
+    _raise(rc, "conv3x3_bwd_weight_act")
     return dw, db
 
 

@@ -38,6 +38,127 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? CONV3X3_OK : CONV3X3_ERR_HIP;
 }
 
+int check_act(int act) {
+  return (act >= CONV3X3_ACT_NONE && act <= CONV3X3_ACT_LRELU) ? CONV3X3_OK : CONV3X3_ERR_BAD_ACT;
+}
+
+int fwd_impl(const void* x, const void* w, const float* bias, float* y, float* z, int N, int C,
+             int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+  if (!x || !w || !y) return CONV3X3_ERR_NULL_POINTER;
+  int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  rc = check_act(act);
+  if (rc) return rc;
+  if ((const void*)y == x || (const void*)y == w || (bias && y == bias)) return CONV3X3_ERR_ALIAS;
+  if (z && ((const void*)z == x || (const void*)z == w || z == bias || z == y))
+    return CONV3X3_ERR_ALIAS;
+  Plan pl;
+  if (!plan(Problem{kFwd, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  ActArgs a;
+  a.act = act;
+  a.zout = z;
+  bool ok;
+  if (dtype == CONV3X3_F32) {
+    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(x) && aligned16(w) &&
+                     buffer_sized(2L * N * C * H * W) && buffer_sized(2L * K * C * 9);
+    ok = launch_fwd_f32(pl, vec, (const float*)x, (const float*)w, bias, y, N, C, K, H, W, a, s);
+  } else {
+    const bool vec = W % 8 == 0 && C % 16 == 0 && aligned16(x) && aligned16(w) &&
+                     buffer_sized((long)N * C * H * W) && buffer_sized((long)K * C * 9);
+    ok = launch_fwd_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)w, bias, y, N, C, K, H, W,
+                         a, s);
+  }
+  if (!ok) return CONV3X3_ERR_BAD_SHAPE;
+  return launch_status();
+}
+
+int bwd_data_impl(const void* g, const float* z, const void* w, float* dx, int N, int C, int K,
+                  int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+  if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
+  int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  rc = check_act(act);
+  if (rc) return rc;
+  if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
+  if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
+  if ((const void*)dx == g || (const void*)dx == w || (act != CONV3X3_ACT_NONE && dx == z))
+    return CONV3X3_ERR_ALIAS;
+  Plan pl;
+  if (!plan(Problem{kBwdData, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  ActArgs a;
+  if (act != CONV3X3_ACT_NONE) {
+    a.act = act;
+    a.zsrc = z;
+  }
+  bool ok;
+  if (dtype == CONV3X3_F32) {
+    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w) &&
+                     (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * K * H * W) &&
+                     buffer_sized(2L * K * C * 9);
+    ok = launch_fwd_f32(pl, vec, (const float*)g, (const float*)w, nullptr, dx, N, K, C, H, W, a,
+                        s);
+  } else {
+    const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w) &&
+                     buffer_sized((long)N * K * H * W) && buffer_sized((long)K * C * 9);
+    ok = launch_fwd_bf16(pl, vec, (const uint16_t*)g, (const uint16_t*)w, nullptr, dx, N, K, C, H,
+                         W, a, s);
+  }
+  if (!ok) return CONV3X3_ERR_BAD_SHAPE;
+  return launch_status();
+}
+
+int bwd_weight_impl(const void* x, const void* g, const float* z, float* dw, float* db,
+                    void* workspace, size_t workspace_bytes, int N, int C, int K, int H, int W,
+                    int dtype, int act, conv3x3_stream_t stream) {
+  if (!x || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
+  int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  rc = check_act(act);
+  if (rc) return rc;
+  if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
+  if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
+  if ((const void*)dw == x || (const void*)dw == g || (db && ((const void*)db == x ||
+                                                              (const void*)db == g || db == dw)))
+    return CONV3X3_ERR_ALIAS;
+  if (act != CONV3X3_ACT_NONE && (dw == z || (db && db == z))) return CONV3X3_ERR_ALIAS;
+  Plan pl;
+  if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
+    return CONV3X3_ERR_WORKSPACE;
+  if (workspace && (workspace == x || workspace == g || workspace == dw ||
+                    (db && workspace == db) || (act != CONV3X3_ACT_NONE && workspace == z)))
+    return CONV3X3_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  ActArgs a;
+  if (act != CONV3X3_ACT_NONE) {
+    a.act = act;
+    a.zsrc = z;
+  }
+  bool ok;
+  if (dtype == CONV3X3_F32) {
+    const bool vec = W % 4 == 0 && aligned16(x) && aligned16(g) &&
+                     (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * C * H * W) &&
+                     buffer_sized(2L * N * K * H * W);
+    ok = launch_wgrad_f32(pl, vec, (const float*)x, (const float*)g, dw, db, (float*)workspace, N,
+                          C, K, H, W, a, s);
+  } else {
+    const bool vec = W % 8 == 0 && aligned16(x) && aligned16(g) &&
+                     buffer_sized((long)N * C * H * W) && buffer_sized((long)N * K * H * W);
+    ok = launch_wgrad_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)g, dw, db,
+                           (float*)workspace, N, C, K, H, W, a, s);
+  }
+  if (!ok) return CONV3X3_ERR_BAD_SHAPE;
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -52,6 +173,8 @@ const char* conv3x3_status_string(int status) {
     case CONV3X3_ERR_ALIAS: return "an output aliases an input";
     case CONV3X3_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case CONV3X3_ERR_BAD_PASS: return "unknown pass";
+    case CONV3X3_ERR_BAD_ACT: return "unknown activation (expected a conv3x3_act_t value)";
+    case CONV3X3_ERR_UNSUPPORTED: return "this dtype's backward pass has no fused activation";
     default: return "unknown status code";
   }
 }
@@ -86,53 +209,22 @@ int conv3x3_plan(int pass, int N, int C, int K, int H, int W, int dtype, conv3x3
 
 int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y, int N, int C, int K,
                 int H, int W, int dtype, conv3x3_stream_t stream) {
-  if (!x || !w || !y) return CONV3X3_ERR_NULL_POINTER;
-  int rc = check_dims(N, C, K, H, W);
-  if (rc) return rc;
-  rc = check_dtype(dtype);
-  if (rc) return rc;
-  if ((const void*)y == x || (const void*)y == w || (bias && y == bias)) return CONV3X3_ERR_ALIAS;
-  Plan pl;
-  if (!plan(Problem{kFwd, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  bool ok;
-  if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(x) && aligned16(w) &&
-                     buffer_sized(2L * N * C * H * W) && buffer_sized(2L * K * C * 9);
-    ok = launch_fwd_f32(pl, vec, (const float*)x, (const float*)w, bias, y, N, C, K, H, W, s);
-  } else {
-    const bool vec = W % 8 == 0 && C % 16 == 0 && aligned16(x) && aligned16(w) &&
-                     buffer_sized((long)N * C * H * W) && buffer_sized((long)K * C * 9);
-    ok = launch_fwd_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)w, bias, y, N, C, K, H, W, s);
-  }
-  if (!ok) return CONV3X3_ERR_BAD_SHAPE;
-  return launch_status();
+  return fwd_impl(x, w, bias, y, nullptr, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream);
 }
 
 int conv3x3_bwd_data(const void* g, const void* w, float* dx, int N, int C, int K, int H, int W,
                      int dtype, conv3x3_stream_t stream) {
-  if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
-  int rc = check_dims(N, C, K, H, W);
-  if (rc) return rc;
-  rc = check_dtype(dtype);
-  if (rc) return rc;
-  if ((const void*)dx == g || (const void*)dx == w) return CONV3X3_ERR_ALIAS;
-  Plan pl;
-  if (!plan(Problem{kBwdData, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  bool ok;
-  if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w) &&
-                     buffer_sized(2L * N * K * H * W) && buffer_sized(2L * K * C * 9);
-    ok = launch_fwd_f32(pl, vec, (const float*)g, (const float*)w, nullptr, dx, N, K, C, H, W, s);
-  } else {
-    const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w) &&
-                     buffer_sized((long)N * K * H * W) && buffer_sized((long)K * C * 9);
-    ok = launch_fwd_bf16(pl, vec, (const uint16_t*)g, (const uint16_t*)w, nullptr, dx, N, K, C, H,
-                         W, s);
-  }
-  if (!ok) return CONV3X3_ERR_BAD_SHAPE;
-  return launch_status();
+  return bwd_data_impl(g, nullptr, w, dx, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream);
+}
+
+int conv3x3_fwd_act(const void* x, const void* w, const float* bias, float* y, float* z, int N,
+                    int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+  return fwd_impl(x, w, bias, y, z, N, C, K, H, W, dtype, act, stream);
+}
+
+int conv3x3_bwd_data_act(const void* gy, const float* z, const void* w, float* dx, int N, int C,
+                         int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+  return bwd_data_impl(gy, z, w, dx, N, C, K, H, W, dtype, act, stream);
 }
 
 size_t conv3x3_bwd_weight_workspace_size(int N, int C, int K, int H, int W, int dtype) {
@@ -145,36 +237,15 @@ size_t conv3x3_bwd_weight_workspace_size(int N, int C, int K, int H, int W, int 
 int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db, void* workspace,
                        size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
                        conv3x3_stream_t stream) {
-  if (!x || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
-  int rc = check_dims(N, C, K, H, W);
-  if (rc) return rc;
-  rc = check_dtype(dtype);
-  if (rc) return rc;
-  if ((const void*)dw == x || (const void*)dw == g || (db && ((const void*)db == x ||
-                                                              (const void*)db == g || db == dw)))
-    return CONV3X3_ERR_ALIAS;
-  Plan pl;
-  if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
-  if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
-    return CONV3X3_ERR_WORKSPACE;
-  if (workspace && (workspace == x || workspace == g || workspace == dw ||
-                    (db && workspace == db)))
-    return CONV3X3_ERR_ALIAS;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  bool ok;
-  if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && aligned16(x) && aligned16(g) &&
-                     buffer_sized(2L * N * C * H * W) && buffer_sized(2L * N * K * H * W);
-    ok = launch_wgrad_f32(pl, vec, (const float*)x, (const float*)g, dw, db, (float*)workspace, N,
-                          C, K, H, W, s);
-  } else {
-    const bool vec = W % 8 == 0 && aligned16(x) && aligned16(g) &&
-                     buffer_sized((long)N * C * H * W) && buffer_sized((long)N * K * H * W);
-    ok = launch_wgrad_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)g, dw, db,
-                           (float*)workspace, N, C, K, H, W, s);
-  }
-  if (!ok) return CONV3X3_ERR_BAD_SHAPE;
-  return launch_status();
+  return bwd_weight_impl(x, g, nullptr, dw, db, workspace, workspace_bytes, N, C, K, H, W, dtype,
+                         CONV3X3_ACT_NONE, stream);
+}
+
+int conv3x3_bwd_weight_act(const void* x, const void* gy, const float* z, float* dw, float* db,
+                           void* workspace, size_t workspace_bytes, int N, int C, int K, int H,
+                           int W, int dtype, int act, conv3x3_stream_t stream) {
+  return bwd_weight_impl(x, gy, z, dw, db, workspace, workspace_bytes, N, C, K, H, W, dtype, act,
+                         stream);
 }
 
 }  // extern "C"

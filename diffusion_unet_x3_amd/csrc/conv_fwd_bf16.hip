@@ -35,6 +35,7 @@
 // so the epilogue is stores only.
 #include <type_traits>
 
+#include "activation.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -90,7 +91,8 @@ template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ wt,
     const float* __restrict__ bias, float* __restrict__ dst, int N, int Cin, int Cout, int H,
-    int W, int tiles_w, int tiles_h, uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes) {
+    int W, int tiles_w, int tiles_h, uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
+    int act, float* __restrict__ zout) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -550,13 +552,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   }
 
   // ---------------- epilogue: NCHW stores ----------------
+  // Forward with a fused activation: y = act(z), z = the accumulator (bias
+  // included), also written to zout when it is given.
   const int cw = co0 + wco * (BCO / WCO);  // first output channel of this wave
+  const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
   if (dst_bytes != 0 && co0 + BCO <= Cout) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the channel
     // step a uniform (scalar) offset.  Pixels outside the image get an offset
     // past the view and the hardware drops their stores.
     const __amdgpu_buffer_rsrc_t dv = buffer_view(dst, dst_bytes);
+    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : dst_bytes);
     const uint32_t plane = (uint32_t)HW * 4u;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -567,12 +573,23 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
           (n < N && h < H && w < W)
               ? (((uint32_t)n * Cout + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
               : kOutside;
+      if (plain) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
-                        acc[i][j][v]);
+          for (int v = 0; v < 16; ++v)
+            buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
+                          acc[i][j][v]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t so = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane;
+            if (zout) buffer_store4(zov, off, so, acc[i][j][v]);
+            buffer_store4(dv, off, so, act_value(act, acc[i][j][v]));
+          }
+      }
     }
     return;
   }
@@ -588,7 +605,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int co = cw + i * 32 + acc_row(v, hi);
-        if (co < Cout) out[(long)co * HW] = acc[i][j][v];
+        if (co < Cout) {
+          if (plain) {
+            out[(long)co * HW] = acc[i][j][v];
+          } else {
+            if (zout) zout[(out - dst) + (long)co * HW] = acc[i][j][v];
+            out[(long)co * HW] = act_value(act, acc[i][j][v]);
+          }
+        }
       }
     }
   }
@@ -597,7 +621,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
 static void launch_bf16_cfg(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
                             const float* bias, float* dst, int N, int Cin, int Cout, int H,
-                            int W, hipStream_t stream) {
+                            int W, const ActArgs& a, hipStream_t stream) {
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(64 * NW, 1, 1);
   // Buffer-view stores need the output below 2 GiB (32-bit byte offsets).
   const long out_bytes = (long)N * Cout * H * W * 4;
@@ -606,26 +630,29 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, const uint16_t* src, const
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
                        (uint32_t)((long)N * Cin * H * W * 2), (uint32_t)((long)Cin * Cout * 9 * 2),
-                       dst_bytes);
+                       dst_bytes, a.act, a.zout);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false>), grid, block,
                        0, stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       0u, 0u, dst_bytes);
+                       0u, 0u, dst_bytes, a.act, a.zout);
 }
 
 bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
                      const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                     hipStream_t stream) {
+                     const ActArgs& a, hipStream_t stream) {
   if (pl.chunk != 16) return false;
+  // The bfloat16 backward-data pass has no fused activation (the caller
+  // rejects one).
+  if (pl.pass != kFwd && a.zsrc != nullptr) return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_, NW_)                                              \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                  \
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \
     if (pl.pass == kFwd)                                                                        \
       launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, bias, dst, N,    \
-                                                             Cin, Cout, H, W, stream);          \
+                                                             Cin, Cout, H, W, a, stream);       \
     else                                                                                        \
       launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, nullptr, dst, \
-                                                                 N, Cin, Cout, H, W, stream);   \
+                                                                 N, Cin, Cout, H, W, a, stream); \
     return true;                                                                                \
   }
   CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)

@@ -19,6 +19,7 @@
 // same tap; lanes 0-31 and 32-63 read them from adjacent LDS planes.  The
 // operands of step t+1 are read from LDS into a second register set while
 // the MFMAs of step t run.
+#include "activation.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -30,7 +31,8 @@ template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h,
-    uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes) {
+    uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes, int act, float* __restrict__ zout,
+    const float* __restrict__ zsrc) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -69,6 +71,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
+  // Backward-data with a fused activation: z at the same positions as the
+  // gradient source; the source is multiplied by act'(z) when it is written
+  // to LDS (the loads of both are in flight together until then).
+  const bool zs = MODE == kBwdData && zsrc != nullptr;
+  f32x4 zv[VEC ? XV_N : 1];
+  float zf[VEC ? XH_N : 1];
+  // halo values that are not loaded stay zero, and so does their z (a zero
+  // gradient times act'(0) is zero; times act'(garbage) might not be)
+#pragma unroll
+  for (int k = 0; k < (VEC ? XH_N : 1); ++k) zf[k] = 0.f;
   // With a single tile across the width both halo columns are padding: they
   // stay zero and are not loaded.
   const bool halo_loads = tiles_w > 1;
@@ -91,6 +103,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // Vector path: buffer views (32-bit offsets); an item outside the tensors
   // or the image reads zero through an offset past the view.
   const __amdgpu_buffer_rsrc_t sview = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t zview = buffer_view(zsrc, zs ? src_bytes : 0u);
   const __amdgpu_buffer_rsrc_t wview = buffer_view(wt, wt_bytes);
   auto load_tiles = [&](int c0) {
     if constexpr (VEC) {
@@ -106,9 +119,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && c < Cin && h >= 0 &&
                         h < H && w < W;
-        xv[k] = __builtin_bit_cast(
-            f32x4, buffer_load16(sview, ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w)
-                                            : kOutside));
+        const uint32_t off = ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w) : kOutside;
+        xv[k] = __builtin_bit_cast(f32x4, buffer_load16(sview, off));
+        if (zs) zv[k] = __builtin_bit_cast(f32x4, buffer_load16(zview, off));
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
@@ -124,9 +137,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int w = o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && c < Cin && h >= 0 &&
                         h < H && w >= 0 && w < W;
-        xf[k] = __builtin_bit_cast(
-            float, buffer_load4(sview, ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w)
-                                          : kOutside));
+        const uint32_t off = ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w) : kOutside;
+        xf[k] = __builtin_bit_cast(float, buffer_load4(sview, off));
+        if (zs) zf[k] = __builtin_bit_cast(float, buffer_load4(zview, off));
       }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
@@ -166,7 +179,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
           const int q = it % XQ;
           const int t = it / XQ;  // (ch * IMGS + img) * HR + rr
-          *reinterpret_cast<f32x4*>(&xs[t * RS + 4 + 4 * q]) = xv[k];
+          f32x4 v = xv[k];
+          if (zs) {
+            v.x *= act_slope(act, zv[k].x);
+            v.y *= act_slope(act, zv[k].y);
+            v.z *= act_slope(act, zv[k].z);
+            v.w *= act_slope(act, zv[k].w);
+          }
+          *reinterpret_cast<f32x4*>(&xs[t * RS + 4 + 4 * q]) = v;
         }
       }
 #pragma unroll
@@ -175,7 +195,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
           const int side = it & 1;
           const int t = it >> 1;
-          xs[t * RS + 4 + (side ? TW : -1)] = xf[k];
+          xs[t * RS + 4 + (side ? TW : -1)] = zs ? xf[k] * act_slope(act, zf[k]) : xf[k];
         }
       }
 #pragma unroll
@@ -203,8 +223,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int ch = t / (HR * IMGS);
           const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
-          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
-            v = src[((long)n * Cin + c) * HW + (long)h * W + w];
+          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W) {
+            const long e = ((long)n * Cin + c) * HW + (long)h * W + w;
+            v = src[e];
+            if (zs) v *= act_slope(act, zsrc[e]);
+          }
           xs[t * RS + 4 + cc] = v;
         }
       }
@@ -290,13 +313,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   }
 
   // ---------------- epilogue: NCHW stores ----------------
+  // Forward with a fused activation: y = act(z), z = the accumulator (bias
+  // included), also written to zout when it is given.
   const int cw = co0 + wco * (BCO / WCO);  // first output channel of this wave
+  const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
   if (dst_bytes != 0 && co0 + BCO <= Cout) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the
     // channel step a uniform (scalar) offset.  Pixels outside the image get
     // an offset past the view and the hardware drops their stores.
     const __amdgpu_buffer_rsrc_t dv = buffer_view(dst, dst_bytes);
+    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : dst_bytes);
     const uint32_t plane = (uint32_t)HW * 4u;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -307,12 +334,23 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           (n < N && h < H && w < W)
               ? (((uint32_t)n * Cout + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
               : kOutside;
+      if (plain) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
-                        acc[i][j][v]);
+          for (int v = 0; v < 16; ++v)
+            buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
+                          acc[i][j][v]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t so = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane;
+            if (zout) buffer_store4(zov, off, so, acc[i][j][v]);
+            buffer_store4(dv, off, so, act_value(act, acc[i][j][v]));
+          }
+      }
     }
     return;
   }
@@ -328,7 +366,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int co = cw + i * 32 + acc_row(v, hi);
-        if (co < Cout) out[(long)co * HW] = acc[i][j][v];
+        if (co < Cout) {
+          if (plain) {
+            out[(long)co * HW] = acc[i][j][v];
+          } else {
+            if (zout) zout[(out - dst) + (long)co * HW] = acc[i][j][v];
+            out[(long)co * HW] = act_value(act, acc[i][j][v]);
+          }
+        }
       }
     }
   }
@@ -340,7 +385,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
 static void launch_cfg(const Plan& pl, bool vec, const float* src, const float* wt,
                        const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                       hipStream_t stream) {
+                       const ActArgs& a, hipStream_t stream) {
   constexpr int CB = 8;
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
   // Buffer-view stores need the output below 2 GiB (32-bit byte offsets).
@@ -350,23 +395,23 @@ static void launch_cfg(const Plan& pl, bool vec, const float* src, const float* 
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, true>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
                        (uint32_t)((long)N * Cin * H * W * 4), (uint32_t)((long)Cin * Cout * 9 * 4),
-                       dst_bytes);
+                       dst_bytes, a.act, a.zout, a.zsrc);
   else
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, false>), grid, block, 0,
                        stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       0u, 0u, dst_bytes);
+                       0u, 0u, dst_bytes, a.act, a.zout, a.zsrc);
 }
 
 template <int MODE>
 static bool launch_mode(const Plan& pl, bool vec, const float* src, const float* wt,
                         const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                        hipStream_t s) {
+                        const ActArgs& a, hipStream_t s) {
   if (pl.chunk != 8) return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                               \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&              \
       pl.wave_co == WCO_) {                                                                 \
     launch_cfg<MODE, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin, Cout, \
-                                                 H, W, s);                                  \
+                                                 H, W, a, s);                               \
     return true;                                                                            \
   }
   CONV3X3_FWD_F32_CONFIGS(CONV3X3_X)
@@ -375,10 +420,11 @@ static bool launch_mode(const Plan& pl, bool vec, const float* src, const float*
 }
 
 bool launch_fwd_f32(const Plan& pl, bool vec, const float* src, const float* wt, const float* bias,
-                    float* dst, int N, int Cin, int Cout, int H, int W, hipStream_t stream) {
+                    float* dst, int N, int Cin, int Cout, int H, int W, const ActArgs& a,
+                    hipStream_t stream) {
   if (pl.pass == kFwd)
-    return launch_mode<kFwd>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, stream);
-  return launch_mode<kBwdData>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, stream);
+    return launch_mode<kFwd>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, stream);
+  return launch_mode<kBwdData>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, stream);
 }
 
 }  // namespace conv3x3

@@ -341,9 +341,12 @@ static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, const uint16_t* x, 
 }
 
 bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
-                       float* db, float* ws, int N, int C, int K, int H, int W,
+                       float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                        hipStream_t stream) {
   if (pl.threads != 768) return false;
+  // No fused activation on the bfloat16 backward-weight pass (the caller
+  // rejects one).
+  if (a.zsrc != nullptr) return false;
   const long n_dw = (long)K * C * 9;
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);

@@ -17,6 +17,7 @@
 // reduced across lanes with fixed-order cross-lane adds, to its own
 // workspace slot; wgrad_reduce_kernel adds the slots in a fixed order.  No
 // atomics anywhere: results are bitwise reproducible.
+#include "activation.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_layout.hpp"
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ g, float* __restrict__ out,
     float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
     int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k,
-    uint32_t x_bytes, uint32_t g_bytes) {
+    uint32_t x_bytes, uint32_t g_bytes, int act, const float* __restrict__ zsrc) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P == 64, "pixel chunk must hold 64 pixels");
   constexpr int GS = wgrad_f32_gstride(IMGS, TH, TW);
@@ -75,6 +76,10 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
 
   f32x4 gv[VEC ? GV_N : 1];
+  // Fused activation: z at the positions of g; g is multiplied by act'(z)
+  // when it is written to LDS.
+  const bool zs = zsrc != nullptr;
+  f32x4 zv[VEC ? GV_N : 1];
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
   // With a single tile across the width both halo columns are padding: they
@@ -87,6 +92,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   // reads zero through an offset past the view (32-bit offset arithmetic,
   // no branches).
   const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
+  const __amdgpu_buffer_rsrc_t zview = buffer_view(zsrc, zs ? g_bytes : 0u);
   const __amdgpu_buffer_rsrc_t xview = buffer_view(x, x_bytes);
   auto load_tiles = [&](int chunk) {
     if constexpr (VEC) {
@@ -102,9 +108,9 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 4 * q;
         const bool ok = (GV_ITEMS % NT == 0 || it < GV_ITEMS) && n < N && kk < K && h < H && w < W;
-        gv[k] = __builtin_bit_cast(
-            f32x4, buffer_load16(gview, ok ? 4u * (uint32_t)(((n * K + kk) * H + h) * W + w)
-                                            : kOutside));
+        const uint32_t off = ok ? 4u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside;
+        gv[k] = __builtin_bit_cast(f32x4, buffer_load16(gview, off));
+        if (zs) zv[k] = __builtin_bit_cast(f32x4, buffer_load16(zview, off));
       }
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
@@ -158,10 +164,17 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int kl = t / (IMGS * TH);
         const int p = (t % (IMGS * TH)) * TW + 4 * q;
         float* d = &gs[kl * GS + p];
-        d[0] = gv[k].x;
-        d[1] = gv[k].y;
-        d[2] = gv[k].z;
-        d[3] = gv[k].w;
+        f32x4 v = gv[k];
+        if (zs) {
+          v.x *= act_slope(act, zv[k].x);
+          v.y *= act_slope(act, zv[k].y);
+          v.z *= act_slope(act, zv[k].z);
+          v.w *= act_slope(act, zv[k].w);
+        }
+        d[0] = v.x;
+        d[1] = v.y;
+        d[2] = v.z;
+        d[3] = v.w;
       }
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
@@ -202,7 +215,11 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + col;
         float v = 0.f;
-        if (n < N && kk < K && h < H && w < W) v = g[((long)n * K + kk) * HW + (long)h * W + w];
+        if (n < N && kk < K && h < H && w < W) {
+          const long e = ((long)n * K + kk) * HW + (long)h * W + w;
+          v = g[e];
+          if (zs) v *= act_slope(act, zsrc[e]);
+        }
         gs[kl * GS + it % P] = v;
       }
 #pragma unroll 4
@@ -428,23 +445,23 @@ __global__ __launch_bounds__(512) void wgrad_reduce4_kernel(const float* __restr
 template <int TW, int TH, int IMGS>
 static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const float* g,
                               float* out, float* out_db, long slice_stride, int N, int C, int K,
-                              int H, int W, hipStream_t stream) {
+                              int H, int W, const ActArgs& a, hipStream_t stream) {
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
   if (vec)
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
                        out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
                        (K + 63) / 64, (uint32_t)((long)N * C * H * W * 4),
-                       (uint32_t)((long)N * K * H * W * 4));
+                       (uint32_t)((long)N * K * H * W * 4), a.act, a.zsrc);
   else
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
                        out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64, 0u, 0u);
+                       (K + 63) / 64, 0u, 0u, a.act, a.zsrc);
 }
 
 bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
-                      float* db, float* ws, int N, int C, int K, int H, int W,
+                      float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                       hipStream_t stream) {
   if (pl.threads != 768) return false;
   const long n_dw = (long)K * C * 9;
@@ -454,7 +471,7 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, 
   bool found = false;
 #define CONV3X3_X(TW_, TH_, IMGS_)                                                           \
   if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                          \
-    launch_wgrad_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream);  \
+    launch_wgrad_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, a, stream);  \
     found = true;                                                                            \
   }
   CONV3X3_WGRAD_F32_CONFIGS(CONV3X3_X)

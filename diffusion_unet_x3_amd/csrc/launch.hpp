@@ -4,24 +4,30 @@
 
 #include <hip/hip_runtime.h>
 
+#include "activation.hpp"
 #include "planner.hpp"
 
 namespace conv3x3 {
 
 // Forward (pl.pass == kFwd; src = x, Cin = C, Cout = K) or backward-data
 // (pl.pass == kBwdData; src = g, Cin = K, Cout = C; bias ignored), float32.
+// a: forward -- a.act and a.zout fused into the epilogue; backward-data --
+// the source is multiplied by act'(a.zsrc) as it is staged (a.zsrc has the
+// source's shape).
 bool launch_fwd_f32(const Plan& pl, bool vec, const float* src, const float* wt, const float* bias,
-                    float* dst, int N, int Cin, int Cout, int H, int W, hipStream_t stream);
+                    float* dst, int N, int Cin, int Cout, int H, int W, const ActArgs& a,
+                    hipStream_t stream);
 
 // Same, bfloat16 inputs (raw 16-bit patterns), float32 outputs.
 bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
                      const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                     hipStream_t stream);
+                     const ActArgs& a, hipStream_t stream);
 
 // Backward-weight (+ optional db), float32; ws holds the per-slice partials
-// when pl.split > 1.
+// when pl.split > 1.  g is multiplied by act'(a.zsrc) as it is staged.
 bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
-                      float* db, float* ws, int N, int C, int K, int H, int W, hipStream_t stream);
+                      float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
+                      hipStream_t stream);
 
 // Fixed-order sum of the split-K partial slots (both dtypes).
 void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C, int K,
@@ -29,7 +35,7 @@ void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C
 
 // Same, bfloat16 inputs.
 bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
-                       float* db, float* ws, int N, int C, int K, int H, int W,
+                       float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                        hipStream_t stream);
 
 }  // namespace conv3x3

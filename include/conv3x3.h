@@ -70,8 +70,30 @@ typedef enum {
   CONV3X3_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
   CONV3X3_ERR_ALIAS = 5,        /* an output shares its base pointer with an input */
   CONV3X3_ERR_HIP = 6,          /* the HIP runtime rejected a launch */
-  CONV3X3_ERR_BAD_PASS = 7      /* conv3x3_plan: unknown pass */
+  CONV3X3_ERR_BAD_PASS = 7,     /* conv3x3_plan: unknown pass */
+  CONV3X3_ERR_BAD_ACT = 8,      /* act is not a conv3x3_act_t value */
+  CONV3X3_ERR_UNSUPPORTED = 9   /* a fused activation this dtype's pass does not provide */
 } conv3x3_status_t;
+
+/*
+ * Activation fused into the convolution (the *_act entry points).  The
+ * project-guide page on StyleGAN2's custom CUDA kernels fuses a bias and an
+ * activation -- a leaky ReLU with a bias term -- into one kernel to save a
+ * round trip through memory; here the activation is applied to the biased
+ * convolution output z = conv(x; w) + bias:
+ *   CONV3X3_ACT_NONE  : act(z) = z
+ *   CONV3X3_ACT_SILU  : act(z) = z * sigmoid(z)            (the UNet's)
+ *   CONV3X3_ACT_LRELU : act(z) = z (z >= 0), 0.2 z (z < 0)  (no gain)
+ * The backward entry points take gy, the gradient at the activation's
+ * output, and z, and run the convolution backward on g = gy * act'(z), with
+ * act'(z) = s (1 + z (1 - s)), s = sigmoid(z), for SiLU and 1 (z > 0) or
+ * 0.2 (z <= 0) for the leaky ReLU.
+ */
+typedef enum {
+  CONV3X3_ACT_NONE = 0,
+  CONV3X3_ACT_SILU = 1,
+  CONV3X3_ACT_LRELU = 2
+} conv3x3_act_t;
 
 typedef enum {
   CONV3X3_PASS_FWD = 0,
@@ -125,6 +147,44 @@ int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db,
                        void* workspace, size_t workspace_bytes,
                        int N, int C, int K, int H, int W, int dtype,
                        conv3x3_stream_t stream);
+
+/*
+ * Forward with fused bias and activation:  z = conv(x; w) + bias,  y = act(z).
+ *   x, w, bias, y : as conv3x3_fwd (y now holds act(z))
+ *   z   : [N][K][H][W] float32 (overwritten), or NULL when not needed; the
+ *         backward entry points below take it
+ *   act : conv3x3_act_t
+ * The activation is applied to the accumulators as they are stored (no
+ * extra pass over y).  Errors as conv3x3_fwd, plus CONV3X3_ERR_BAD_ACT.
+ */
+int conv3x3_fwd_act(const void* x, const void* w, const float* bias, float* y, float* z,
+                    int N, int C, int K, int H, int W, int dtype, int act,
+                    conv3x3_stream_t stream);
+
+/*
+ * Backward-data through the activation:  dx = conv3x3_bwd_data(g = gy * act'(z), w).
+ *   gy : [N][K][H][W], dtype (the gradient at the activation's output)
+ *   z  : [N][K][H][W] float32, the forward's pre-activation (may be NULL
+ *        only when act is CONV3X3_ACT_NONE)
+ *   w, dx : as conv3x3_bwd_data
+ * g is formed as gy and z are staged into LDS; it never exists in memory.
+ * float32 only for now: a bfloat16 call with an activation other than
+ * CONV3X3_ACT_NONE returns CONV3X3_ERR_UNSUPPORTED.
+ */
+int conv3x3_bwd_data_act(const void* gy, const float* z, const void* w, float* dx,
+                         int N, int C, int K, int H, int W, int dtype, int act,
+                         conv3x3_stream_t stream);
+
+/*
+ * Backward-weight and bias gradient through the activation:
+ *   dw, db = conv3x3_bwd_weight(x, g = gy * act'(z)); arguments as
+ *   conv3x3_bwd_weight, plus gy / z / act as conv3x3_bwd_data_act (same
+ *   workspace size).  float32 only for now, as conv3x3_bwd_data_act.
+ */
+int conv3x3_bwd_weight_act(const void* x, const void* gy, const float* z, float* dw, float* db,
+                           void* workspace, size_t workspace_bytes,
+                           int N, int C, int K, int H, int W, int dtype, int act,
+                           conv3x3_stream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* conv3x3_status_string(int status);

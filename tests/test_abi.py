@@ -16,7 +16,7 @@ S = lib3.STATUS
 
 # Distinct non-null fake device addresses: never dereferenced, because every
 # call below fails validation first.
-X, Wt, B, Y, G, WS = (ctypes.c_void_p(0x10000 * (i + 1)) for i in range(6))
+X, Wt, B, Y, G, WS, Z = (ctypes.c_void_p(0x10000 * (i + 1)) for i in range(7))
 
 
 def _declared_functions():
@@ -34,8 +34,9 @@ def test_header_functions_are_exported():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(10):
         assert lib3.conv3x3_status_string(code)
+        assert "unknown status" not in lib3.conv3x3_status_string(code)
     assert lib3.conv3x3_status_string(0) == "success"
     assert "unknown" in lib3.conv3x3_status_string(99)
 
@@ -95,3 +96,44 @@ def test_plan_query_errors():
     assert L.conv3x3_plan(3, 1, 1, 1, 1, 1, 0, ctypes.byref(p)) == S["ERR_BAD_PASS"]
     assert L.conv3x3_plan(0, 1, 1, 1, 1, 1, 0, None) == S["ERR_NULL_POINTER"]
     assert L.conv3x3_plan(0, 1, 1, 1, 1, 1, 5, ctypes.byref(p)) == S["ERR_BAD_DTYPE"]
+
+
+# ---- fused-activation entry points ------------------------------------------
+
+@pytest.mark.parametrize("act", [-1, 3, 17])
+def test_bad_activation_rejected(act):
+    d = (2, 3, 4, 5, 6)
+    assert L.conv3x3_fwd_act(X, Wt, B, Y, Z, *d, 0, act, None) == S["ERR_BAD_ACT"]
+    assert L.conv3x3_bwd_data_act(G, Z, Wt, Y, *d, 0, act, None) == S["ERR_BAD_ACT"]
+    assert L.conv3x3_bwd_weight_act(X, G, Z, Y, B, WS, 1 << 40, *d, 0, act, None) == \
+        S["ERR_BAD_ACT"]
+
+
+def test_activation_argument_checks():
+    d = (2, 3, 4, 5, 6)
+    silu = lib3.ACT_SILU
+    # shapes, dtypes and required pointers as the plain entry points
+    assert L.conv3x3_fwd_act(X, Wt, B, Y, Z, 0, 3, 4, 5, 6, 0, silu, None) == S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_fwd_act(None, Wt, B, Y, Z, *d, 0, silu, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_fwd_act(X, Wt, B, Y, Z, *d, 2, silu, None) == S["ERR_BAD_DTYPE"]
+    # z may not alias another argument
+    assert L.conv3x3_fwd_act(X, Wt, B, Y, Y, *d, 0, silu, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_fwd_act(X, Wt, B, Y, X, *d, 0, silu, None) == S["ERR_ALIAS"]
+    # the backward passes need z for any activation other than none ...
+    assert L.conv3x3_bwd_data_act(G, None, Wt, Y, *d, 0, silu, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_weight_act(X, G, None, Y, B, WS, 1 << 40, *d, 0, silu, None) == \
+        S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_data_act(G, Z, Wt, Z, *d, 0, silu, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_bwd_weight_act(X, G, Z, Z, B, WS, 1 << 40, *d, 0, silu, None) == \
+        S["ERR_ALIAS"]
+    # ... and fuse one on float32 only
+    assert L.conv3x3_bwd_data_act(G, Z, Wt, Y, *d, 1, silu, None) == S["ERR_UNSUPPORTED"]
+    assert L.conv3x3_bwd_weight_act(X, G, Z, Y, B, WS, 1 << 40, *d, 1, lib3.ACT_LRELU, None) == \
+        S["ERR_UNSUPPORTED"]
+    # workspace rules carry over
+    N, C, K, H, W = 32, 64, 64, 64, 64
+    need = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W)
+    assert L.conv3x3_bwd_weight_act(X, G, Z, Y, B, WS, need - 1, N, C, K, H, W, 0, silu, None) == \
+        S["ERR_WORKSPACE"]
+    assert L.conv3x3_bwd_weight_act(X, G, Z, Y, B, Z, need, N, C, K, H, W, 0, silu, None) == \
+        S["ERR_ALIAS"]

@@ -33,6 +33,20 @@ def test_stem_layer_flops_and_algorithmic_bytes():
     assert bench.alg_bytes("fwd", N, C, K, H, W, "bf16") == 2 * (M * C + 9 * K * C) + 4 * K + 4 * M * K
 
 
+def test_fused_activation_bytes():
+    N, C, K, H, W = 32, 64, 64, 64, 64
+    M = N * H * W
+    z = 4 * M * K
+    for p in ("fwd", "bwd_data", "bwd_weight"):
+        plain = bench.alg_bytes(p, N, C, K, H, W, "f32")
+        assert bench.alg_bytes(p, N, C, K, H, W, "f32", "silu") == plain + z
+    # bf16: the forward writes z; the backward passes run unfused
+    assert bench.alg_bytes("fwd", N, C, K, H, W, "bf16", "silu") == \
+        bench.alg_bytes("fwd", N, C, K, H, W, "bf16") + z
+    assert bench.alg_bytes("bwd_data", N, C, K, H, W, "bf16", "silu") == \
+        bench.alg_bytes("bwd_data", N, C, K, H, W, "bf16")
+
+
 def _write_counters(path, counter, rows):
     with open(path, "w", newline="") as fh:
         w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
