@@ -248,3 +248,41 @@ def conv3x3_bwd_act(x, w, gy, z, act, bf16=False, want_db=True):
     dx = conv3x3_bwd_data(g, w)
     dw, db = conv3x3_bwd_weight(x, g, want_db)
     return dx, dw, db
+
+
+# ---------------------------------------------------------------------------
+# Concatenated input (up-path skip connections).  The UNet of the sourcepulse
+# summary ("How It Works") is read as the standard one: each up-path block's
+# first convolution takes the channel concatenation [a ; b] of the upsampled
+# features a (C0 channels) and the skip tensor b (C1 channels).  The oracle is
+# that definition written out: the convolution of the concatenated tensor,
+# and for backward-data the split of its input gradient at channel C0.
+
+
+def _cat(x0, x1):
+    return np.concatenate([_f64(x0), _f64(x1)], axis=1)
+
+
+def conv3x3_fwd_cat(x0, x1, w, b=None):
+    """y = conv3x3_fwd([x0 ; x1], w, b); w has C0 + C1 input channels."""
+    return conv3x3_fwd(_cat(x0, x1), w, b)
+
+
+def conv3x3_bwd_data_cat(g, w, C0):
+    """(dx0, dx1): the gradient of <conv([x0 ; x1]; w), g> with respect to
+    x0 (channels 0..C0-1 of the concatenation) and x1 (the rest)."""
+    dx = conv3x3_bwd_data(g, w)
+    return dx[:, :C0], dx[:, C0:]
+
+
+def conv3x3_bwd_weight_cat(x0, x1, g, want_db=True):
+    """(dw, db) of <conv([x0 ; x1]; w) + b, g>."""
+    return conv3x3_bwd_weight(_cat(x0, x1), g, want_db)
+
+
+def conv3x3_fwd_cat_at(x0, x1, w, b, idx):
+    return conv3x3_fwd_at(_cat(x0, x1), w, b, idx)
+
+
+def conv3x3_bwd_weight_cat_at(x0, x1, g, idx):
+    return conv3x3_bwd_weight_at(_cat(x0, x1), g, idx)
