@@ -14,12 +14,21 @@ device memory and the current stream.  The functions carry the C names:
     conv3x3_bwd_data_act(gy, z, w, act=ACT_SILU, out=None)    -> dx
     conv3x3_bwd_weight_act(x, gy, z, act=ACT_SILU, want_db=True,
                            dw=None, db=None, workspace=None)  -> (dw, db)
+    conv3x3_fwd_cat(x0, x1, w, bias=None, out=None)           -> y
+    conv3x3_bwd_data_cat(g, w, C0, out0=None, out1=None)      -> (dx0, dx1)
+    conv3x3_bwd_weight_cat(x0, x1, g, want_db=True, dw=None, db=None,
+                           workspace=None)                    -> (dw, db)
+    conv3x3_bwd_weight_cat_workspace_size(N, C0, C1, K, H, W, dtype) -> bytes
     conv3x3_status_string(code)                               -> str
     conv3x3_plan(pass_, N, C, K, H, W, dtype)                 -> dict
+    conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype)        -> dict
 
 The *_act functions fuse an activation (ACT_NONE, ACT_SILU, ACT_LRELU) into
 the forward epilogue and, through z = the forward's pre-activation, into the
-gradient loader of the backward passes (float32 backward only).
+gradient loader of the backward passes (float32 backward only).  The *_cat
+functions take the input as two tensors x0, x1 whose channel concatenation
+[x0 ; x1] is the convolution's input (a UNet's up-path skip input) and never
+form the concatenation; backward-data returns the two gradient halves.
 
 Tensors are NCHW / OIHW, contiguous, on a GPU; x, w, g are float32 or
 bfloat16 (all three alike), bias is float32, outputs are float32.  There is
@@ -44,7 +53,9 @@ STATUS = {
 }
 EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_size",
             "conv3x3_bwd_weight", "conv3x3_status_string", "conv3x3_plan",
-            "conv3x3_fwd_act", "conv3x3_bwd_data_act", "conv3x3_bwd_weight_act"]
+            "conv3x3_fwd_act", "conv3x3_bwd_data_act", "conv3x3_bwd_weight_act",
+            "conv3x3_fwd_cat", "conv3x3_bwd_data_cat", "conv3x3_bwd_weight_cat_workspace_size",
+            "conv3x3_bwd_weight_cat", "conv3x3_plan_cat"]
 
 
 class Plan(ctypes.Structure):
@@ -81,6 +92,17 @@ def _load():
     lib.conv3x3_status_string.restype = ctypes.c_char_p
     lib.conv3x3_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.conv3x3_plan.restype = i
+    lib.conv3x3_fwd_cat.argtypes = [vp, vp, i, i, vp, fp, fp, i, i, i, i, i, vp]
+    lib.conv3x3_fwd_cat.restype = i
+    lib.conv3x3_bwd_data_cat.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data_cat.restype = i
+    lib.conv3x3_bwd_weight_cat_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.conv3x3_bwd_weight_cat_workspace_size.restype = ctypes.c_size_t
+    lib.conv3x3_bwd_weight_cat.argtypes = [vp, vp, i, i, vp, fp, fp, vp, ctypes.c_size_t,
+                                           i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight_cat.restype = i
+    lib.conv3x3_plan_cat.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.conv3x3_plan_cat.restype = i
     return lib
 
 
@@ -273,4 +295,94 @@ def conv3x3_plan(pass_, N, C, K, H, W, dtype=CONV3X3_F32):
     p = Plan()
     rc = lib.conv3x3_plan(pass_, N, C, K, H, W, dtype, ctypes.byref(p))
     _raise(rc, "conv3x3_plan")
+    return {name: getattr(p, name) for name, _ in Plan._fields_}
+
+
+def _halves(x0, x1):
+    _check(x0, "x0", 4)
+    _check(x1, "x1", 4)
+    N, C0, H, W = x0.shape
+    if (x1.shape[0], x1.shape[2], x1.shape[3]) != (N, H, W) or x1.dtype != x0.dtype:
+        raise ValueError("x1 must be [N, C1, H, W] with x0's N, H, W and dtype")
+    return N, C0, x1.shape[1], H, W
+
+
+def _ptr(t):
+    """Device address of t, or None for a tensor with no elements."""
+    return t.data_ptr() if t.numel() else None
+
+
+def conv3x3_fwd_cat(x0, x1, w, bias=None, out=None):
+    """y = conv3x3([x0 ; x1]; w) + bias, the input being the channel
+    concatenation of x0 and x1 (never formed)."""
+    N, C0, C1, H, W = _halves(x0, x1)
+    _check(w, "w", 4)
+    K = w.shape[0]
+    if tuple(w.shape) != (K, C0 + C1, 3, 3) or w.dtype != x0.dtype:
+        raise ValueError("w must be [K, C0 + C1, 3, 3] with x0's dtype")
+    if bias is not None:
+        _check(bias, "bias", 1)
+        if bias.dtype != torch.float32 or bias.shape[0] != K:
+            raise ValueError("bias must be float32 [K]")
+    y = _f32_out(out, (N, K, H, W), x0, "out")
+    rc = lib.conv3x3_fwd_cat(_ptr(x0), _ptr(x1), C0, C1, w.data_ptr(),
+                             None if bias is None else bias.data_ptr(), y.data_ptr(),
+                             N, K, H, W, _dtype_code(x0), _stream(w))
+    _raise(rc, "conv3x3_fwd_cat")
+    return y
+
+
+def conv3x3_bwd_data_cat(g, w, C0, out0=None, out1=None):
+    """(dx0, dx1): the input gradient of conv3x3([x0 ; x1]; w) split at
+    channel C0, float32."""
+    _check(g, "g", 4)
+    _check(w, "w", 4)
+    N, K, H, W = g.shape
+    C = w.shape[1]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with g's dtype")
+    if not 0 <= C0 <= C:
+        raise ValueError("C0 must lie in [0, C]")
+    dx0 = _f32_out(out0, (N, C0, H, W), g, "out0")
+    dx1 = _f32_out(out1, (N, C - C0, H, W), g, "out1")
+    rc = lib.conv3x3_bwd_data_cat(g.data_ptr(), w.data_ptr(), _ptr(dx0), _ptr(dx1), C0, C - C0,
+                                  N, K, H, W, _dtype_code(g), _stream(g))
+    _raise(rc, "conv3x3_bwd_data_cat")
+    return dx0, dx1
+
+
+def conv3x3_bwd_weight_cat_workspace_size(N, C0, C1, K, H, W, dtype=CONV3X3_F32):
+    n = lib.conv3x3_bwd_weight_cat_workspace_size(N, C0, C1, K, H, W, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid problem for conv3x3_bwd_weight_cat_workspace_size")
+    return n
+
+
+def conv3x3_bwd_weight_cat(x0, x1, g, want_db=True, dw=None, db=None, workspace=None):
+    """(dw, db) of <conv3x3([x0 ; x1]; w) + b, g>, float32."""
+    N, C0, C1, H, W = _halves(x0, x1)
+    _check(g, "g", 4)
+    K = g.shape[1]
+    if tuple(g.shape) != (N, K, H, W) or g.dtype != x0.dtype:
+        raise ValueError("g must be [N, K, H, W] with x0's dtype")
+    code = _dtype_code(x0)
+    dw = _f32_out(dw, (K, C0 + C1, 3, 3), g, "dw")
+    db = _f32_out(db, (K,), g, "db") if want_db else None
+    need = conv3x3_bwd_weight_cat_workspace_size(N, C0, C1, K, H, W, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=g.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.conv3x3_bwd_weight_cat(_ptr(x0), _ptr(x1), C0, C1, g.data_ptr(), dw.data_ptr(),
+                                    None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
+                                    N, K, H, W, code, _stream(g))
+    _raise(rc, "conv3x3_bwd_weight_cat")
+    return dw, db
+
+
+def conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype=CONV3X3_F32):
+    """The launch plan of a *_cat call (host-side query)."""
+    p = Plan()
+    rc = lib.conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype, ctypes.byref(p))
+    _raise(rc, "conv3x3_plan_cat")
     return {name: getattr(p, name) for name, _ in Plan._fields_}

@@ -42,42 +42,78 @@ int check_act(int act) {
   return (act >= CONV3X3_ACT_NONE && act <= CONV3X3_ACT_LRELU) ? CONV3X3_OK : CONV3X3_ERR_BAD_ACT;
 }
 
-int fwd_impl(const void* x, const void* w, const float* bias, float* y, float* z, int N, int C,
-             int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
-  if (!x || !w || !y) return CONV3X3_ERR_NULL_POINTER;
+// x (or dx) as one tensor or as the concatenation of two: channels
+// [0, c0) at p0 and [c0, C) at p1.  A part with no channels may be NULL.
+template <typename T>
+Split<T> one(T* p, int C) {
+  Split<T> s;
+  s.p0 = p;
+  s.c0 = C;
+  return s;
+}
+
+// Channel counts of a concatenation: both >= 0, at least one channel, and a
+// sum that fits an int (the other limits are check_dims' on the sum).
+int check_halves(int C0, int C1) {
+  if (C0 < 0 || C1 < 0 || (long)C0 + C1 < 1 || (long)C0 + C1 > kMaxElems)
+    return CONV3X3_ERR_BAD_SHAPE;
+  return CONV3X3_OK;
+}
+
+template <typename T>
+bool parts_present(const Split<T>& s, int C) {
+  return (s.c0 == 0 || s.p0) && (s.c0 == C || s.p1);
+}
+
+template <typename T>
+bool parts_aligned(const Split<T>& s) {
+  return aligned16(s.p0) && aligned16(s.p1);
+}
+
+// p (non-null) is the base pointer of one of the parts
+template <typename T>
+bool is_part(const Split<T>& s, const void* p) {
+  return p && (p == (const void*)s.p0 || p == (const void*)s.p1);
+}
+
+int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, float* z, int N,
+             int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+  if (!parts_present(x, C) || !w || !y) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
   rc = check_dtype(dtype);
   if (rc) return rc;
   rc = check_act(act);
   if (rc) return rc;
-  if ((const void*)y == x || (const void*)y == w || (bias && y == bias)) return CONV3X3_ERR_ALIAS;
-  if (z && ((const void*)z == x || (const void*)z == w || z == bias || z == y))
-    return CONV3X3_ERR_ALIAS;
+  if (is_part(x, y) || (const void*)y == w || (bias && y == bias)) return CONV3X3_ERR_ALIAS;
+  if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kFwd, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (!plan(Problem{kFwd, dtype, N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   a.act = act;
   a.zout = z;
+  const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(x) && aligned16(w) &&
-                     buffer_sized(2L * N * C * H * W) && buffer_sized(2L * K * C * 9);
-    ok = launch_fwd_f32(pl, vec, (const float*)x, (const float*)w, bias, y, N, C, K, H, W, a, s);
+    const bool vec = W % 4 == 0 && C % 4 == 0 && x.c0 % 4 == 0 && parts_aligned(x) &&
+                     aligned16(w) && buffer_sized(2L * N * C * hw) && buffer_sized(2L * K * C * 9);
+    Split<const float> xs{(const float*)x.p0, (const float*)x.p1, x.c0};
+    ok = launch_fwd_f32(pl, vec, xs, (const float*)w, bias, one(y, K), N, C, K, H, W, a, s);
   } else {
-    const bool vec = W % 8 == 0 && C % 16 == 0 && aligned16(x) && aligned16(w) &&
-                     buffer_sized((long)N * C * H * W) && buffer_sized((long)K * C * 9);
-    ok = launch_fwd_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)w, bias, y, N, C, K, H, W,
-                         a, s);
+    const bool vec = W % 8 == 0 && C % 16 == 0 && x.c0 % 16 == 0 && parts_aligned(x) &&
+                     aligned16(w) && buffer_sized((long)N * C * hw) &&
+                     buffer_sized((long)K * C * 9);
+    Split<const uint16_t> xs{(const uint16_t*)x.p0, (const uint16_t*)x.p1, x.c0};
+    ok = launch_fwd_bf16(pl, vec, xs, (const uint16_t*)w, bias, one(y, K), N, C, K, H, W, a, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
 }
 
-int bwd_data_impl(const void* g, const float* z, const void* w, float* dx, int N, int C, int K,
-                  int H, int W, int dtype, int act, conv3x3_stream_t stream) {
-  if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
+int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx, int N, int C,
+                  int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+  if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
   rc = check_dtype(dtype);
@@ -86,37 +122,40 @@ int bwd_data_impl(const void* g, const float* z, const void* w, float* dx, int N
   if (rc) return rc;
   if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
   if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
-  if ((const void*)dx == g || (const void*)dx == w || (act != CONV3X3_ACT_NONE && dx == z))
+  if (is_part(dx, g) || is_part(dx, w) || (act != CONV3X3_ACT_NONE && is_part(dx, z)) ||
+      (dx.c0 > 0 && dx.c0 < C && dx.p0 == dx.p1))
     return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kBwdData, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (!plan(Problem{kBwdData, dtype, N, C, K, H, W, dx.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   if (act != CONV3X3_ACT_NONE) {
     a.act = act;
     a.zsrc = z;
   }
+  const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && aligned16(g) && aligned16(w) &&
-                     (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * K * H * W) &&
-                     buffer_sized(2L * K * C * 9);
-    ok = launch_fwd_f32(pl, vec, (const float*)g, (const float*)w, nullptr, dx, N, K, C, H, W, a,
-                        s);
+    const bool vec = W % 4 == 0 && C % 4 == 0 && dx.c0 % 4 == 0 && aligned16(g) &&
+                     aligned16(w) && (!a.zsrc || aligned16(a.zsrc)) &&
+                     buffer_sized(2L * N * K * hw) && buffer_sized(2L * K * C * 9);
+    ok = launch_fwd_f32(pl, vec, one((const float*)g, K), (const float*)w, nullptr, dx, N, K, C,
+                        H, W, a, s);
   } else {
-    const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && aligned16(g) && aligned16(w) &&
-                     buffer_sized((long)N * K * H * W) && buffer_sized((long)K * C * 9);
-    ok = launch_fwd_bf16(pl, vec, (const uint16_t*)g, (const uint16_t*)w, nullptr, dx, N, K, C, H,
-                         W, a, s);
+    const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && dx.c0 % 8 == 0 &&
+                     aligned16(g) && aligned16(w) && buffer_sized((long)N * K * hw) &&
+                     buffer_sized((long)K * C * 9);
+    ok = launch_fwd_bf16(pl, vec, one((const uint16_t*)g, K), (const uint16_t*)w, nullptr, dx, N,
+                         K, C, H, W, a, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
 }
 
-int bwd_weight_impl(const void* x, const void* g, const float* z, float* dw, float* db,
+int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* dw, float* db,
                     void* workspace, size_t workspace_bytes, int N, int C, int K, int H, int W,
                     int dtype, int act, conv3x3_stream_t stream) {
-  if (!x || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
+  if (!parts_present(x, C) || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
   rc = check_dtype(dtype);
@@ -125,15 +164,15 @@ int bwd_weight_impl(const void* x, const void* g, const float* z, float* dw, flo
   if (rc) return rc;
   if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
   if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
-  if ((const void*)dw == x || (const void*)dw == g || (db && ((const void*)db == x ||
-                                                              (const void*)db == g || db == dw)))
+  if (is_part(x, dw) || (const void*)dw == g ||
+      (db && (is_part(x, db) || (const void*)db == g || db == dw)))
     return CONV3X3_ERR_ALIAS;
   if (act != CONV3X3_ACT_NONE && (dw == z || (db && db == z))) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
-  if (workspace && (workspace == x || workspace == g || workspace == dw ||
+  if (workspace && (is_part(x, workspace) || workspace == g || workspace == dw ||
                     (db && workspace == db) || (act != CONV3X3_ACT_NONE && workspace == z)))
     return CONV3X3_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -142,21 +181,57 @@ int bwd_weight_impl(const void* x, const void* g, const float* z, float* dw, flo
     a.act = act;
     a.zsrc = z;
   }
+  const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && aligned16(x) && aligned16(g) &&
-                     (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * C * H * W) &&
-                     buffer_sized(2L * N * K * H * W);
-    ok = launch_wgrad_f32(pl, vec, (const float*)x, (const float*)g, dw, db, (float*)workspace, N,
-                          C, K, H, W, a, s);
+    const bool vec = W % 4 == 0 && parts_aligned(x) && aligned16(g) &&
+                     (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * C * hw) &&
+                     buffer_sized(2L * N * K * hw);
+    Split<const float> xs{(const float*)x.p0, (const float*)x.p1, x.c0};
+    ok = launch_wgrad_f32(pl, vec, xs, (const float*)g, dw, db, (float*)workspace, N, C, K, H, W,
+                          a, s);
   } else {
-    const bool vec = W % 8 == 0 && aligned16(x) && aligned16(g) &&
-                     buffer_sized((long)N * C * H * W) && buffer_sized((long)N * K * H * W);
-    ok = launch_wgrad_bf16(pl, vec, (const uint16_t*)x, (const uint16_t*)g, dw, db,
-                           (float*)workspace, N, C, K, H, W, a, s);
+    const bool vec = W % 8 == 0 && parts_aligned(x) && aligned16(g) &&
+                     buffer_sized((long)N * C * hw) && buffer_sized((long)N * K * hw);
+    Split<const uint16_t> xs{(const uint16_t*)x.p0, (const uint16_t*)x.p1, x.c0};
+    ok = launch_wgrad_bf16(pl, vec, xs, (const uint16_t*)g, dw, db, (float*)workspace, N, C, K, H,
+                           W, a, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
+}
+
+int fill_plan(const Plan& pl, int pass, conv3x3_plan_t* out) {
+  out->pass = pl.pass;
+  out->dtype = pl.dtype;
+  out->kernel = pl.wave_co;
+  out->tile_m = pl.tile_co;
+  out->tile_n = pass == CONV3X3_PASS_BWD_WEIGHT ? pl.tile_ci : pl.imgs * pl.th * pl.tw;
+  out->tile_imgs = pl.imgs;
+  out->tile_h = pl.th;
+  out->tile_w = pl.tw;
+  out->chunk = pl.chunk;
+  out->threads = pl.threads;
+  out->grid_x = pl.grid_x;
+  out->grid_y = pl.grid_y;
+  out->grid_z = pl.grid_z;
+  out->lds_bytes = pl.lds_bytes;
+  out->split = pl.split;
+  out->workspace_bytes = pl.workspace_bytes;
+  return CONV3X3_OK;
+}
+
+int plan_impl(int pass, int N, int C, int K, int H, int W, int dtype, int C0,
+              conv3x3_plan_t* out) {
+  if (!out) return CONV3X3_ERR_NULL_POINTER;
+  if (pass < CONV3X3_PASS_FWD || pass > CONV3X3_PASS_BWD_WEIGHT) return CONV3X3_ERR_BAD_PASS;
+  int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  Plan pl;
+  if (!plan(Problem{pass, dtype, N, C, K, H, W, C0}, &pl)) return CONV3X3_ERR_BAD_PASS;
+  return fill_plan(pl, pass, out);
 }
 
 }  // namespace
@@ -180,51 +255,70 @@ const char* conv3x3_status_string(int status) {
 }
 
 int conv3x3_plan(int pass, int N, int C, int K, int H, int W, int dtype, conv3x3_plan_t* out) {
-  if (!out) return CONV3X3_ERR_NULL_POINTER;
-  if (pass < CONV3X3_PASS_FWD || pass > CONV3X3_PASS_BWD_WEIGHT) return CONV3X3_ERR_BAD_PASS;
-  int rc = check_dims(N, C, K, H, W);
+  return plan_impl(pass, N, C, K, H, W, dtype, -1, out);
+}
+
+int conv3x3_plan_cat(int pass, int N, int C0, int C1, int K, int H, int W, int dtype,
+                     conv3x3_plan_t* out) {
+  const int rc = check_halves(C0, C1);
   if (rc) return rc;
-  rc = check_dtype(dtype);
-  if (rc) return rc;
-  Plan pl;
-  if (!plan(Problem{pass, dtype, N, C, K, H, W}, &pl)) return CONV3X3_ERR_BAD_PASS;
-  out->pass = pl.pass;
-  out->dtype = pl.dtype;
-  out->kernel = pl.wave_co;
-  out->tile_m = pl.tile_co;
-  out->tile_n = pass == CONV3X3_PASS_BWD_WEIGHT ? pl.tile_ci : pl.imgs * pl.th * pl.tw;
-  out->tile_imgs = pl.imgs;
-  out->tile_h = pl.th;
-  out->tile_w = pl.tw;
-  out->chunk = pl.chunk;
-  out->threads = pl.threads;
-  out->grid_x = pl.grid_x;
-  out->grid_y = pl.grid_y;
-  out->grid_z = pl.grid_z;
-  out->lds_bytes = pl.lds_bytes;
-  out->split = pl.split;
-  out->workspace_bytes = pl.workspace_bytes;
-  return CONV3X3_OK;
+  return plan_impl(pass, N, C0 + C1, K, H, W, dtype, C0, out);
 }
 
 int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y, int N, int C, int K,
                 int H, int W, int dtype, conv3x3_stream_t stream) {
-  return fwd_impl(x, w, bias, y, nullptr, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream);
+  return fwd_impl(one(x, C), w, bias, y, nullptr, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream);
 }
 
 int conv3x3_bwd_data(const void* g, const void* w, float* dx, int N, int C, int K, int H, int W,
                      int dtype, conv3x3_stream_t stream) {
-  return bwd_data_impl(g, nullptr, w, dx, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream);
+  return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, H, W, dtype, CONV3X3_ACT_NONE,
+                       stream);
 }
 
 int conv3x3_fwd_act(const void* x, const void* w, const float* bias, float* y, float* z, int N,
                     int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
-  return fwd_impl(x, w, bias, y, z, N, C, K, H, W, dtype, act, stream);
+  return fwd_impl(one(x, C), w, bias, y, z, N, C, K, H, W, dtype, act, stream);
 }
 
 int conv3x3_bwd_data_act(const void* gy, const float* z, const void* w, float* dx, int N, int C,
                          int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
-  return bwd_data_impl(gy, z, w, dx, N, C, K, H, W, dtype, act, stream);
+  return bwd_data_impl(gy, z, w, one(dx, C), N, C, K, H, W, dtype, act, stream);
+}
+
+int conv3x3_fwd_cat(const void* x0, const void* x1, int C0, int C1, const void* w,
+                    const float* bias, float* y, int N, int K, int H, int W, int dtype,
+                    conv3x3_stream_t stream) {
+  const int rc = check_halves(C0, C1);
+  if (rc) return rc;
+  return fwd_impl(Split<const void>{x0, x1, C0}, w, bias, y, nullptr, N, C0 + C1, K, H, W, dtype,
+                  CONV3X3_ACT_NONE, stream);
+}
+
+int conv3x3_bwd_data_cat(const void* g, const void* w, float* dx0, float* dx1, int C0, int C1,
+                         int N, int K, int H, int W, int dtype, conv3x3_stream_t stream) {
+  const int rc = check_halves(C0, C1);
+  if (rc) return rc;
+  return bwd_data_impl(g, nullptr, w, Split<float>{dx0, dx1, C0}, N, C0 + C1, K, H, W, dtype,
+                       CONV3X3_ACT_NONE, stream);
+}
+
+size_t conv3x3_bwd_weight_cat_workspace_size(int N, int C0, int C1, int K, int H, int W,
+                                             int dtype) {
+  if (check_halves(C0, C1) || check_dims(N, C0 + C1, K, H, W) || check_dtype(dtype))
+    return (size_t)-1;
+  Plan pl;
+  if (!plan(Problem{kBwdWeight, dtype, N, C0 + C1, K, H, W, C0}, &pl)) return (size_t)-1;
+  return pl.workspace_bytes;
+}
+
+int conv3x3_bwd_weight_cat(const void* x0, const void* x1, int C0, int C1, const void* g,
+                           float* dw, float* db, void* workspace, size_t workspace_bytes, int N,
+                           int K, int H, int W, int dtype, conv3x3_stream_t stream) {
+  const int rc = check_halves(C0, C1);
+  if (rc) return rc;
+  return bwd_weight_impl(Split<const void>{x0, x1, C0}, g, nullptr, dw, db, workspace,
+                         workspace_bytes, N, C0 + C1, K, H, W, dtype, CONV3X3_ACT_NONE, stream);
 }
 
 size_t conv3x3_bwd_weight_workspace_size(int N, int C, int K, int H, int W, int dtype) {
@@ -237,15 +331,15 @@ size_t conv3x3_bwd_weight_workspace_size(int N, int C, int K, int H, int W, int 
 int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db, void* workspace,
                        size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
                        conv3x3_stream_t stream) {
-  return bwd_weight_impl(x, g, nullptr, dw, db, workspace, workspace_bytes, N, C, K, H, W, dtype,
-                         CONV3X3_ACT_NONE, stream);
+  return bwd_weight_impl(one(x, C), g, nullptr, dw, db, workspace, workspace_bytes, N, C, K, H,
+                         W, dtype, CONV3X3_ACT_NONE, stream);
 }
 
 int conv3x3_bwd_weight_act(const void* x, const void* gy, const float* z, float* dw, float* db,
                            void* workspace, size_t workspace_bytes, int N, int C, int K, int H,
                            int W, int dtype, int act, conv3x3_stream_t stream) {
-  return bwd_weight_impl(x, gy, z, dw, db, workspace, workspace_bytes, N, C, K, H, W, dtype, act,
-                         stream);
+  return bwd_weight_impl(one(x, C), gy, z, dw, db, workspace, workspace_bytes, N, C, K, H, W,
+                         dtype, act, stream);
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@
 // memory is transposed.
 //
 // Weights, as one 16-byte word per (tap, 8-channel group, output channel):
-//   forward       : w[co, c0 + 8g .. + 7, 0..8] is one contiguous, 16-byte
+//   forward       : w[co, 16f + 8g .. + 7, 0..8] is one contiguous, 16-byte
 //                   aligned 144-byte run; a lane loads it as nine words and
 //                   forms the nine tap words with byte permutes;
 //   backward-data : the reduction channel is k, the slowest axis of w; a lane
@@ -33,6 +33,12 @@
 // compute waves then hold 64 x 128 wave tiles, 6 operand reads per 8
 // MFMAs).  One barrier per fill.  Forward accumulators start at the bias,
 // so the epilogue is stores only.
+//
+// Either channel axis may be a concatenation of two tensors, as in the
+// float32 kernel: source channels [0, cin0) from src and [cin0, Cin) from
+// src1, output channels [0, cout0) to dst and [cout0, Cout) to dst1; every
+// fill and every channel tile lies inside one tensor.  (The vector path
+// needs cin0 % 16 == 0, so its fills are whole, and cout0 % 8 == 0.)
 #include <type_traits>
 
 #include "activation.hpp"
@@ -89,10 +95,11 @@ __device__ __forceinline__ u32x4 tap_word(const uint32_t* d) {
 
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ src, const uint16_t* __restrict__ wt,
-    const float* __restrict__ bias, float* __restrict__ dst, int N, int Cin, int Cout, int H,
-    int W, int tiles_w, int tiles_h, uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
-    int act, float* __restrict__ zout) {
+    const uint16_t* __restrict__ src, const uint16_t* __restrict__ src1, int cin0,
+    const uint16_t* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
+    float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
+    int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
+    uint32_t dst1_bytes, int act, float* __restrict__ zout) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -122,9 +129,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const BlockOrigin o = block_origin<TW, TH, IMGS>(blockIdx.x, tiles_w, tiles_h);
-  const int co0 = blockIdx.y * BCO;
   const long HW = (long)H * W;
-  const int nchunks = (Cin + CB - 1) / CB;
+  // This workgroup's output channel tile: channels col0 .. col0 + co_n - 1 of
+  // output tensor `oseg` (ocs channels), channel co0 of the weight and bias.
+  const int nt0 = (cout0 + BCO - 1) / BCO;
+  const bool oseg = (int)blockIdx.y >= nt0;
+  const int col0 = ((int)blockIdx.y - (oseg ? nt0 : 0)) * BCO;
+  const int ocs = oseg ? Cout - cout0 : cout0;
+  const int co0 = (oseg ? cout0 : 0) + col0;
+  const int co_n = min(BCO, ocs - col0);
+  // Reduction fills: nq0 over src's channels, then src1's.
+  const int nq0 = (cin0 + CB - 1) / CB;
+  const int nchunks = nq0 + (Cin - cin0 + CB - 1) / CB;
   // staging thread index (-1: this thread stages nothing)
   const int sp = WSPEC ? (wave >= NC ? tid - 64 * NC : -1) : tid;
 
@@ -137,13 +153,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // registers of a set.)  Eight-wave workgroups keep one set, loaded one
   // fill ahead by their staging waves.  Items:
   //   x item (rr, q, img, g), sp in [0, XI): the 8 x 8 block of channels
-  //     c0 + 8g .. + 7 x pixels 8q .. 8q + 7 of one staged row, as eight
-  //     128-bit row loads, written as eight channel-interleaved words;
+  //     8g .. 8g + 7 of the fill x pixels 8q .. 8q + 7 of one staged row,
+  //     as eight 128-bit row loads, written as eight channel-interleaved
+  //     words;
   //   halo item, sp in [0, XH): 8 channels of one halo-column pixel;
-  //   weight items: forward (co_l, g), co_l fastest: the 144-byte run
-  //     w[co0 + co_l, c0 + 8g .. + 7, 0..8] (nine loads, nine tap words);
-  //     backward-data (g, eb): word eb of the rows w[c0 + 8g + i, co0.., ..],
-  //     i = 0..7 (eight loads, transposed into eight words of 8 k each).
+  //   weight items, fill f: forward (co_l, g), co_l fastest: the 144-byte
+  //     run w[co0 + co_l, 16f + 8g .. + 7, 0..8] (nine loads, nine tap
+  //     words); backward-data (g, eb): word eb of the rows
+  //     w[16f + 8g + i, co0.., ..], i = 0..7 (eight loads, transposed into
+  //     eight words of 8 k each).
   //     Wave-specialised: items sp and sp + 256; otherwise the last WI
   //     threads, so that x and weight staging sit in different waves.
   constexpr int XI = 2 * IMGS * HR * (TW / 8);
@@ -185,10 +203,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // Byte offsets, computed once; a fill adds the channel step.  Items
   // outside the tensors hold kOutside and read zero.
-  const __amdgpu_buffer_rsrc_t sv = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t sv0 = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t sv1 = buffer_view(src1, src1_bytes);
   const __amdgpu_buffer_rsrc_t wv = buffer_view(wt, wt_bytes);
   const uint32_t hw2 = 2u * (uint32_t)(H * W);
-  uint32_t xoff = kOutside, hoff = kOutside, woff[WK];
+  // x and halo item offsets in src (channel 8g of image n) and in src1
+  uint32_t xoff = kOutside, hoff = kOutside, xoff1 = kOutside, hoff1 = kOutside, woff[WK];
   int xdst = 0;  // LDS word of the x item's first pixel
 #pragma unroll
   for (int k = 0; k < WK; ++k) woff[k] = kOutside;
@@ -204,8 +224,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const int img = t % IMGS;
       const int g = t / IMGS;
       const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
-      if (n < N && h >= 0 && h < H && w < W)
-        xoff = 2u * (uint32_t)(((n * Cin + 8 * g) * H + h) * W + w);
+      if (n < N && h >= 0 && h < H && w < W) {
+        xoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * H + h) * W + w);
+        xoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * H + h) * W + w);
+      }
       xdst = g * PLW + (img * HR + rr) * RS + 4 + 8 * q;
     }
     if (hrole) {
@@ -216,8 +238,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const int img = t % IMGS;
       const int g = t / IMGS;
       const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + (side ? TW : -1);
-      if (n < N && h >= 0 && h < H && w >= 0 && w < W)
-        hoff = 2u * (uint32_t)(((n * Cin + 8 * g) * H + h) * W + w);
+      if (n < N && h >= 0 && h < H && w >= 0 && w < W) {
+        hoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * H + h) * W + w);
+        hoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * H + h) * W + w);
+      }
     }
 #pragma unroll
     for (int k = 0; k < WK; ++k) {
@@ -225,10 +249,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if (it < 0) continue;
       if constexpr (MODE == kFwd) {
         const int co_l = it % BCO, g = it / BCO;  // consecutive lanes: consecutive co
-        if (co0 + co_l < Cout) woff[k] = 2u * (uint32_t)(((co0 + co_l) * Cin + 8 * g) * 9);
+        if (co_l < co_n) woff[k] = 2u * (uint32_t)(((co0 + co_l) * Cin + 8 * g) * 9);
       } else {
         const int g = it / EW, eb = it % EW;
-        if (8 * eb < (Cout - co0) * 9)
+        if (8 * eb < co_n * 9)
           woff[k] = 2u * (uint32_t)(((8 * g) * Cout + co0) * 9 + 8 * eb);
       }
     }
@@ -239,16 +263,23 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const uint32_t wstep = MODE == kFwd ? 2u * 16u * 9u : 2u * 16u * 9u * (uint32_t)Cout;
   const uint32_t wrow = 2u * 9u * (uint32_t)Cout;
 
-  auto load_tiles = [&](auto set_c, int c0) {
+  // (fills are whole here, so fill f of src1 starts at weight channel
+  // 16 (nq0 + f); items outside the image keep kOutside through the select)
+  auto load_tiles = [&](auto set_c, int chunk) {
     constexpr int S = decltype(set_c)::value;
-    const uint32_t f = (uint32_t)(c0 / 16);
+    const uint32_t f = (uint32_t)chunk;
+    const bool s1 = chunk >= nq0;
+    const __amdgpu_buffer_rsrc_t sv = s1 ? sv1 : sv0;
+    const uint32_t fx = (uint32_t)(chunk - (s1 ? nq0 : 0)) * xstep;
     if (xrole) {
+      const uint32_t b = (s1 ? xoff1 : xoff) + fx;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, xoff + f * xstep + (uint32_t)i * hw2);
+      for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, b + (uint32_t)i * hw2);
     }
     if (hrole && halo_loads) {
+      const uint32_t b = (s1 ? hoff1 : hoff) + fx;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hv[S][i] = buffer_load2(sv, hoff + f * xstep + (uint32_t)i * hw2);
+      for (int i = 0; i < 8; ++i) hv[S][i] = buffer_load2(sv, b + (uint32_t)i * hw2);
     }
 #pragma unroll
     for (int k = 0; k < WK; ++k) {
@@ -325,8 +356,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // Scalar path (ragged shapes): 16-bit loads straight into LDS buffer buf,
   // by the staging threads.
-  auto fill_scalar = [&](int c0, int buf) {
+  auto fill_scalar = [&](int chunk, int buf) {
     if (sp < 0) return;
+    const bool s1 = chunk >= nq0;
+    const int cl0 = (chunk - (s1 ? nq0 : 0)) * CB;  // first channel within its tensor
+    const int cs = s1 ? Cin - cin0 : cin0;            // channels of that tensor
+    const int cg0 = (s1 ? cin0 : 0) + cl0;            // first channel in the weight
+    const int cn = min(CB, cs - cl0);                 // valid channels of the fill
+    const uint16_t* sx = s1 ? src1 : src;
     uint16_t* xh = reinterpret_cast<uint16_t*>(xs + buf * XW);
     uint16_t* wh = reinterpret_cast<uint16_t*>(wa + buf * WW);
     constexpr int XS = CB * IMGS * HR * (TW + 2);
@@ -339,10 +376,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
         const int rr = t % HR;
         const int img = (t / HR) % IMGS;
         const int ch = t / (HR * IMGS);
-        const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + cc;
+        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
         uint16_t v = 0;
-        if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W)
-          v = src[((long)n * Cin + c) * HW + (long)h * W + w];
+        if (n < N && ch < cn && h >= 0 && h < H && w >= 0 && w < W)
+          v = sx[((long)n * cs + cl0 + ch) * HW + (long)h * W + w];
         xh[((ch >> 3) * PLW + (img * HR + rr) * RS + 4 + cc) * 8 + (ch & 7)] = v;
       }
     }
@@ -358,16 +395,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
         const int e = it % (CB * 9);
         ci_l = e / 9;
         tap = e % 9;
-        const int co = co0 + co_l, ci = c0 + ci_l;
-        if (co < Cout && ci < Cin) v = wt[((long)co * Cin + ci) * 9 + tap];
+        if (co_l < co_n && ci_l < cn) v = wt[((long)(co0 + co_l) * Cin + cg0 + ci_l) * 9 + tap];
       } else {
         ci_l = it / (BCO * 9);
         const int e = it % (BCO * 9);
         co_l = e / 9;
         const int tg = e % 9;
         tap = 8 - tg;
-        const int co = co0 + co_l, ci = c0 + ci_l;
-        if (co < Cout && ci < Cin) v = wt[((long)ci * Cout + co) * 9 + tg];
+        if (co_l < co_n && ci_l < cn) v = wt[((long)(cg0 + ci_l) * Cout + co0 + co_l) * 9 + tg];
       }
       wh[((tap * 2 + (ci_l >> 3)) * BCO + co_l) * 8 + (ci_l & 7)] = v;
     }
@@ -377,22 +412,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   auto stage_next = [&](auto set_c, int chunk) {
     if constexpr (VEC) {
       if (chunk + 1 < nchunks) store_tiles(set_c, (chunk + 1) & 1);
-      if (chunk + 1 + NSET < nchunks) load_tiles(set_c, (chunk + 1 + NSET) * CB);
+      if (chunk + 1 + NSET < nchunks) load_tiles(set_c, chunk + 1 + NSET);
     } else {
-      if (chunk + 1 < nchunks) fill_scalar((chunk + 1) * CB, (chunk + 1) & 1);
+      if (chunk + 1 < nchunks) fill_scalar(chunk + 1, (chunk + 1) & 1);
     }
   };
 
   // ---- prologue: fill 0 in buffer 0, the next NSET fills in registers ----
   if constexpr (MODE == kFwd) {
     for (int i = tid; i < BCO; i += NT)
-      bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
+      bias_s[i] = (bias != nullptr && i < co_n) ? bias[co0 + i] : 0.f;
   }
   if constexpr (VEC) {
     load_tiles(Set0{}, 0);
     store_tiles(Set0{}, 0);
-    if (nchunks > 1) load_tiles(SetOdd{}, CB);
-    if (NSET == 2 && nchunks > 2) load_tiles(Set0{}, 2 * CB);
+    if (nchunks > 1) load_tiles(SetOdd{}, 1);
+    if (NSET == 2 && nchunks > 2) load_tiles(Set0{}, 2);
   } else {
     fill_scalar(0, 0);
   }
@@ -554,15 +589,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // ---------------- epilogue: NCHW stores ----------------
   // Forward with a fused activation: y = act(z), z = the accumulator (bias
   // included), also written to zout when it is given.
-  const int cw = co0 + wco * (BCO / WCO);  // first output channel of this wave
+  // (zout, forward only, has the shape of dst; the output is then one tensor.)
+  const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
   const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
-  if (dst_bytes != 0 && co0 + BCO <= Cout) {
+  float* const od = oseg ? dst1 : dst;
+  const uint32_t od_bytes = oseg ? dst1_bytes : dst_bytes;
+  if (od_bytes != 0 && co_n == BCO) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the channel
     // step a uniform (scalar) offset.  Pixels outside the image get an offset
     // past the view and the hardware drops their stores.
-    const __amdgpu_buffer_rsrc_t dv = buffer_view(dst, dst_bytes);
-    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : dst_bytes);
+    const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
+    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : od_bytes);
     const uint32_t plane = (uint32_t)HW * 4u;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -571,7 +609,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
       const uint32_t off =
           (n < N && h < H && w < W)
-              ? (((uint32_t)n * Cout + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
+              ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
               : kOutside;
       if (plain) {
 #pragma unroll
@@ -599,17 +637,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
     if (n >= N || h >= H || w >= W) continue;
-    float* out = dst + (long)n * Cout * HW + (long)h * W + w;
+    float* out = od + (long)n * ocs * HW + (long)h * W + w;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int co = cw + i * 32 + acc_row(v, hi);
-        if (co < Cout) {
+        if (co < ocs) {
           if (plain) {
             out[(long)co * HW] = acc[i][j][v];
           } else {
-            if (zout) zout[(out - dst) + (long)co * HW] = acc[i][j][v];
+            if (zout) zout[(out - od) + (long)co * HW] = acc[i][j][v];
             out[(long)co * HW] = act_value(act, acc[i][j][v]);
           }
         }
@@ -619,26 +657,32 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 }
 
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
-static void launch_bf16_cfg(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
-                            const float* bias, float* dst, int N, int Cin, int Cout, int H,
-                            int W, const ActArgs& a, hipStream_t stream) {
+static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
+                            const uint16_t* wt, const float* bias, Split<float> dst, int N,
+                            int Cin, int Cout, int H, int W, const ActArgs& a,
+                            hipStream_t stream) {
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(64 * NW, 1, 1);
-  // Buffer-view stores need the output below 2 GiB (32-bit byte offsets).
-  const long out_bytes = (long)N * Cout * H * W * 4;
-  const uint32_t dst_bytes = out_bytes < 2147483648L ? (uint32_t)out_bytes : 0u;
+  // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
+  // offsets); otherwise both take the plain-store path.
+  const long hw = (long)H * W;
+  const long ob0 = (long)N * dst.c0 * hw * 4, ob1 = (long)N * (Cout - dst.c0) * hw * 4;
+  const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
+  const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
   if (vec)
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       (uint32_t)((long)N * Cin * H * W * 2), (uint32_t)((long)Cin * Cout * 9 * 2),
-                       dst_bytes, a.act, a.zout);
+                       stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
+                       Cout, H, W, pl.tiles_w, pl.tiles_h, (uint32_t)(N * src.c0 * hw * 2),
+                       (uint32_t)(N * (Cin - src.c0) * hw * 2),
+                       (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false>), grid, block,
-                       0, stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       0u, 0u, dst_bytes, a.act, a.zout);
+                       0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N,
+                       Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1, a.act,
+                       a.zout);
 }
 
-bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
-                     const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
+                     const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
                      const ActArgs& a, hipStream_t stream) {
   if (pl.chunk != 16) return false;
   // The bfloat16 backward-data pass has no fused activation (the caller

@@ -19,6 +19,14 @@
 // same tap; lanes 0-31 and 32-63 read them from adjacent LDS planes.  The
 // operands of step t+1 are read from LDS into a second register set while
 // the MFMAs of step t run.
+//
+// Either channel axis may be a concatenation of two tensors (a UNet's
+// up-path input [upsampled ; skip], or the two halves of its gradient):
+// source channels [0, cin0) come from src and [cin0, Cin) from src1, output
+// channels [0, cout0) go to dst and [cout0, Cout) to dst1.  Every LDS fill
+// and every channel tile lies inside one of the two tensors (a tensor's
+// ragged last fill or tile is zero-padded like any ragged channel count), so
+// the choice of tensor is uniform per fill and per workgroup.
 #include "activation.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -29,10 +37,11 @@ namespace conv3x3 {
 
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
-    const float* __restrict__ src, const float* __restrict__ wt, const float* __restrict__ bias,
-    float* __restrict__ dst, int N, int Cin, int Cout, int H, int W, int tiles_w, int tiles_h,
-    uint32_t src_bytes, uint32_t wt_bytes, uint32_t dst_bytes, int act, float* __restrict__ zout,
-    const float* __restrict__ zsrc) {
+    const float* __restrict__ src, const float* __restrict__ src1, int cin0,
+    const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
+    float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
+    int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
+    uint32_t dst1_bytes, int act, float* __restrict__ zout, const float* __restrict__ zsrc) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -55,8 +64,34 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   const int l32 = lane & 31, hi = lane >> 5;
   const int wco = wave % WCO, wpx = wave / WCO;
   const BlockOrigin o = block_origin<TW, TH, IMGS>(blockIdx.x, tiles_w, tiles_h);
-  const int co0 = blockIdx.y * BCO;
   const long HW = (long)H * W;
+  // This workgroup's output channel tile: channels col0 .. col0 + co_n - 1 of
+  // output tensor `oseg` (ocs channels), channel co0 of the weight and bias.
+  const int nt0 = (cout0 + BCO - 1) / BCO;
+  const bool oseg = (int)blockIdx.y >= nt0;
+  const int col0 = ((int)blockIdx.y - (oseg ? nt0 : 0)) * BCO;
+  const int ocs = oseg ? Cout - cout0 : cout0;
+  const int co0 = (oseg ? cout0 : 0) + col0;
+  const int co_n = min(BCO, ocs - col0);
+  // Reduction fills: nq0 over src's channels, then src1's.
+  const int nq0 = (cin0 + CB - 1) / CB;
+  const int nchunks = nq0 + (Cin - cin0 + CB - 1) / CB;
+  struct Fill {
+    bool s1;  // the fill reads src1
+    int cl0;  // first channel of the fill within its tensor
+    int cs;   // channels of that tensor
+    int cg0;  // first channel of the fill in the weight
+    int cn;   // valid channels of the fill
+  };
+  auto fill_of = [&](int chunk) {
+    Fill f;
+    f.s1 = chunk >= nq0;
+    f.cl0 = (chunk - (f.s1 ? nq0 : 0)) * CB;
+    f.cs = f.s1 ? Cin - cin0 : cin0;
+    f.cg0 = (f.s1 ? cin0 : 0) + f.cl0;
+    f.cn = min(CB, f.cs - f.cl0);
+    return f;
+  };
 
   // ---------------- staging: source tile ----------------
   // Vector path: interior columns as float4 (W % 4 == 0 so a float4 never
@@ -88,7 +123,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   for (int k = 0; k < (VEC ? XH_N : 1); ++k) xf[k] = 0.f;
 
   // ---------------- staging: weight tile ----------------
-  // Forward: for each co, the CB x 9 weights w[co, c0.., :] are contiguous.
+  // Forward: for each co, the CB x 9 weights w[co, cg0.., :] are contiguous.
   // Backward-data: for each ci (= k), the BCO x 9 weights w[ci, co0.., :] are.
   constexpr int RUN = MODE == kFwd ? CB * 9 : BCO * 9;
   constexpr int NRUN = MODE == kFwd ? BCO : CB;
@@ -102,11 +137,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // in store_tiles.  Scalar path: everything happens in store_tiles.
   // Vector path: buffer views (32-bit offsets); an item outside the tensors
   // or the image reads zero through an offset past the view.
-  const __amdgpu_buffer_rsrc_t sview = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t sview0 = buffer_view(src, src_bytes);
+  const __amdgpu_buffer_rsrc_t sview1 = buffer_view(src1, src1_bytes);
   const __amdgpu_buffer_rsrc_t zview = buffer_view(zsrc, zs ? src_bytes : 0u);
   const __amdgpu_buffer_rsrc_t wview = buffer_view(wt, wt_bytes);
-  auto load_tiles = [&](int c0) {
+  auto load_tiles = [&](int chunk) {
     if constexpr (VEC) {
+      const Fill f = fill_of(chunk);
+      const __amdgpu_buffer_rsrc_t sview = f.s1 ? sview1 : sview0;
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
         const int it = tid + k * NT;
@@ -116,10 +154,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int ch = t / IMGS;
-        const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
-        const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && c < Cin && h >= 0 &&
+        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
+        const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w < W;
-        const uint32_t off = ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w) : kOutside;
+        const uint32_t off =
+            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xv[k] = __builtin_bit_cast(f32x4, buffer_load16(sview, off));
         if (zs) zv[k] = __builtin_bit_cast(f32x4, buffer_load16(zview, off));
       }
@@ -133,11 +172,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int ch = t / IMGS;
-        const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1;
+        const int n = o.n0 + img, h = o.h0 + rr - 1;
         const int w = o.w0 + (side ? TW : -1);
-        const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && c < Cin && h >= 0 &&
+        const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
-        const uint32_t off = ok ? 4u * (uint32_t)(((n * Cin + c) * H + h) * W + w) : kOutside;
+        const uint32_t off =
+            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xf[k] = __builtin_bit_cast(float, buffer_load4(sview, off));
         if (zs) zf[k] = __builtin_bit_cast(float, buffer_load4(zview, off));
       }
@@ -149,13 +189,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         bool ok;
         int idx;
         if constexpr (MODE == kFwd) {
-          const int co = co0 + run;
-          ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && co < Cout && e < (Cin - c0) * 9;
-          idx = (co * Cin + c0) * 9 + e;
+          ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && run < co_n && e < f.cn * 9;
+          idx = ((co0 + run) * Cin + f.cg0) * 9 + e;
         } else {
-          const int ci = c0 + run;
-          ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && ci < Cin && e < (Cout - co0) * 9;
-          idx = (ci * Cout + co0) * 9 + e;
+          ok = (WV_ITEMS % NT == 0 || it < WV_ITEMS) && run < f.cn && e < co_n * 9;
+          idx = ((f.cg0 + run) * Cout + co0) * 9 + e;
         }
         wv[k] = __builtin_bit_cast(f32x4, buffer_load16(wview, ok ? 4u * (uint32_t)idx : kOutside));
       }
@@ -171,7 +209,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     }
   };
 
-  auto store_tiles = [&](int c0) {
+  auto store_tiles = [&](int chunk) {
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
@@ -212,6 +250,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       }
     } else {
       // Scalar path (ragged shapes): global loads go straight to LDS.
+      const Fill f = fill_of(chunk);
+      const float* sp = f.s1 ? src1 : src;
 #pragma unroll 4
       for (int k = 0; k < XS_N; ++k) {
         const int it = tid + k * NT;
@@ -221,11 +261,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int rr = t % HR;
           const int img = (t / HR) % IMGS;
           const int ch = t / (HR * IMGS);
-          const int n = o.n0 + img, c = c0 + ch, h = o.h0 + rr - 1, w = o.w0 + cc;
+          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
-          if (n < N && c < Cin && h >= 0 && h < H && w >= 0 && w < W) {
-            const long e = ((long)n * Cin + c) * HW + (long)h * W + w;
-            v = src[e];
+          if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W) {
+            const long e = ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
+            v = sp[e];
             if (zs) v *= act_slope(act, zsrc[e]);
           }
           xs[t * RS + 4 + cc] = v;
@@ -239,11 +279,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int e = it % RUN;
           float v = 0.f;
           if constexpr (MODE == kFwd) {
-            const int co = co0 + run, ci = c0 + e / 9;
-            if (co < Cout && ci < Cin) v = wt[((long)co * Cin + ci) * 9 + e % 9];
+            if (run < co_n && e / 9 < f.cn)
+              v = wt[((long)(co0 + run) * Cin + f.cg0 + e / 9) * 9 + e % 9];
           } else {
-            const int ci = c0 + run, co = co0 + e / 9;
-            if (ci < Cin && co < Cout) v = wt[((long)ci * Cout + co) * 9 + e % 9];
+            if (run < f.cn && e / 9 < co_n)
+              v = wt[((long)(f.cg0 + run) * Cout + co0 + e / 9) * 9 + e % 9];
           }
           ws[w_slot(run, e)] = v;
         }
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // bias), so the epilogue is stores only.
   if constexpr (MODE == kFwd) {
     for (int i = tid; i < BCO; i += NT)
-      bias_s[i] = (bias != nullptr && co0 + i < Cout) ? bias[co0 + i] : 0.f;
+      bias_s[i] = (bias != nullptr && i < co_n) ? bias[co0 + i] : 0.f;
     __syncthreads();
   }
   f32x16 acc[MI][NJ];
@@ -289,13 +329,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
-  const int nchunks = (Cin + CB - 1) / CB;
   load_tiles(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     if (chunk) __syncthreads();
-    store_tiles(chunk * CB);
+    store_tiles(chunk);
     __syncthreads();
-    if (chunk + 1 < nchunks) load_tiles((chunk + 1) * CB);
+    if (chunk + 1 < nchunks) load_tiles(chunk + 1);
     read_step(0, 0);
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
@@ -315,15 +354,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // ---------------- epilogue: NCHW stores ----------------
   // Forward with a fused activation: y = act(z), z = the accumulator (bias
   // included), also written to zout when it is given.
-  const int cw = co0 + wco * (BCO / WCO);  // first output channel of this wave
+  // (zout, forward only, has the shape of dst; the output is then one tensor.)
+  const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
   const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
-  if (dst_bytes != 0 && co0 + BCO <= Cout) {
+  float* const od = oseg ? dst1 : dst;
+  const uint32_t od_bytes = oseg ? dst1_bytes : dst_bytes;
+  if (od_bytes != 0 && co_n == BCO) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the
     // channel step a uniform (scalar) offset.  Pixels outside the image get
     // an offset past the view and the hardware drops their stores.
-    const __amdgpu_buffer_rsrc_t dv = buffer_view(dst, dst_bytes);
-    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : dst_bytes);
+    const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
+    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : od_bytes);
     const uint32_t plane = (uint32_t)HW * 4u;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
       const uint32_t off =
           (n < N && h < H && w < W)
-              ? (((uint32_t)n * Cout + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
+              ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
               : kOutside;
       if (plain) {
 #pragma unroll
@@ -360,17 +402,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
     if (n >= N || h >= H || w >= W) continue;
-    float* out = dst + (long)n * Cout * HW + (long)h * W + w;
+    float* out = od + (long)n * ocs * HW + (long)h * W + w;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int co = cw + i * 32 + acc_row(v, hi);
-        if (co < Cout) {
+        if (co < ocs) {
           if (plain) {
             out[(long)co * HW] = acc[i][j][v];
           } else {
-            if (zout) zout[(out - dst) + (long)co * HW] = acc[i][j][v];
+            if (zout) zout[(out - od) + (long)co * HW] = acc[i][j][v];
             out[(long)co * HW] = act_value(act, acc[i][j][v]);
           }
         }
@@ -383,29 +425,34 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 // Host launcher: dispatch the plan's tile to its instantiation.
 
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
-static void launch_cfg(const Plan& pl, bool vec, const float* src, const float* wt,
-                       const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                       const ActArgs& a, hipStream_t stream) {
+static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const float* wt,
+                       const float* bias, Split<float> dst, int N, int Cin, int Cout, int H,
+                       int W, const ActArgs& a, hipStream_t stream) {
   constexpr int CB = 8;
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
-  // Buffer-view stores need the output below 2 GiB (32-bit byte offsets).
-  const long out_bytes = (long)N * Cout * H * W * 4;
-  const uint32_t dst_bytes = out_bytes < 2147483648L ? (uint32_t)out_bytes : 0u;
+  // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
+  // offsets); otherwise both take the plain-store path.
+  const long hw4 = (long)H * W * 4;
+  const long ob0 = (long)N * dst.c0 * hw4, ob1 = (long)N * (Cout - dst.c0) * hw4;
+  const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
+  const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
   if (vec)
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, true>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       (uint32_t)((long)N * Cin * H * W * 4), (uint32_t)((long)Cin * Cout * 9 * 4),
-                       dst_bytes, a.act, a.zout, a.zsrc);
+                       stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
+                       Cout, H, W, pl.tiles_w, pl.tiles_h, (uint32_t)(N * src.c0 * hw4),
+                       (uint32_t)(N * (Cin - src.c0) * hw4), (uint32_t)((long)Cin * Cout * 9 * 4),
+                       db0, db1, a.act, a.zout, a.zsrc);
   else
     hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, false>), grid, block, 0,
-                       stream, src, wt, bias, dst, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
-                       0u, 0u, dst_bytes, a.act, a.zout, a.zsrc);
+                       stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
+                       Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1, a.act, a.zout,
+                       a.zsrc);
 }
 
 template <int MODE>
-static bool launch_mode(const Plan& pl, bool vec, const float* src, const float* wt,
-                        const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
-                        const ActArgs& a, hipStream_t s) {
+static bool launch_mode(const Plan& pl, bool vec, Split<const float> src, const float* wt,
+                        const float* bias, Split<float> dst, int N, int Cin, int Cout, int H,
+                        int W, const ActArgs& a, hipStream_t s) {
   if (pl.chunk != 8) return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                               \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&              \
@@ -419,9 +466,9 @@ static bool launch_mode(const Plan& pl, bool vec, const float* src, const float*
   return false;
 }
 
-bool launch_fwd_f32(const Plan& pl, bool vec, const float* src, const float* wt, const float* bias,
-                    float* dst, int N, int Cin, int Cout, int H, int W, const ActArgs& a,
-                    hipStream_t stream) {
+bool launch_fwd_f32(const Plan& pl, bool vec, Split<const float> src, const float* wt,
+                    const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
+                    const ActArgs& a, hipStream_t stream) {
   if (pl.pass == kFwd)
     return launch_mode<kFwd>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, stream);
   return launch_mode<kBwdData>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, stream);

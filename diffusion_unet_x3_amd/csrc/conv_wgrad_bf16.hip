@@ -14,7 +14,9 @@
 // word and one dword of its neighbour -- no unaligned LDS access.  A pixel
 // chunk is 128 pixels (8 MFMA steps; 64 for 8-wide images), staged through
 // buffer views into double-buffered LDS, one barrier per chunk.  Partial
-// sums and the split-K reduce are those of the float32 kernel.
+// sums and the split-K reduce are those of the float32 kernel, and so is
+// the handling of an x made of two tensors (channels [0, cx0) in x, the rest
+// in x1; one tensor per 64-channel tile).
 #include <type_traits>
 
 #include "common.hpp"
@@ -30,10 +32,11 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 
 template <int TW, int TH, int IMGS, bool VEC>
 __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, float* __restrict__ out,
-    float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
-    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k,
-    uint32_t x_bytes, uint32_t g_bytes) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ x1, int cx0,
+    const uint16_t* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
+    int C, int K, int H, int W, int tiles_w, int tiles_h, int nchunks, int per_split,
+    long slice_stride, int split, int tiles_c, int tiles_k, uint32_t x_bytes, uint32_t x1_bytes,
+    uint32_t g_bytes) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P % 16 == 0, "whole 16-pixel MFMA steps");
   static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
@@ -61,7 +64,15 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   const int L = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   if (L >= split * ntile) return;
   const int slice = L / ntile, tile = L % ntile;
-  const int c0 = (tile % tiles_c) * 64;
+  // channel tile: channels cl0 .. cl0 + cn - 1 of x tensor `xseg` (cs
+  // channels; x holds [0, cx0), x1 the rest), channel c0 of dw
+  const int ct = tile % tiles_c, nct0 = (cx0 + 63) / 64;
+  const bool xseg = ct >= nct0;
+  const int cl0 = (ct - (xseg ? nct0 : 0)) * 64;
+  const int cs = xseg ? C - cx0 : cx0;
+  const int c0 = (xseg ? cx0 : 0) + cl0;
+  const int cn = min(64, cs - cl0);
+  const uint16_t* const xsrc = xseg ? x1 : x;
   const int k0 = (tile / tiles_c) * 64;
   const long HW = (long)H * W;
   const bool do_db = out_db != nullptr && tile % tiles_c == 0;
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   // Vector path: buffer views; an item outside the tensors or the image
   // reads zero through an offset past the view (32-bit offset arithmetic).
   const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
-  const __amdgpu_buffer_rsrc_t xview = buffer_view(x, x_bytes);
+  const __amdgpu_buffer_rsrc_t xview = buffer_view(xsrc, xseg ? x1_bytes : x_bytes);
   auto load_tiles = [&](auto set_c, int chunk) {
     constexpr int SET = decltype(set_c)::value;
     if constexpr (VEC) {
@@ -115,9 +126,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int cl = t / IMGS;
-        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
-        const bool ok = (XI % NT == 0 || it < XI) && n < N && c < C && h >= 0 && h < H && w < W;
-        xv[SET][k] = buffer_load16(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w) : kOutside);
+        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
+        const bool ok = (XI % NT == 0 || it < XI) && n < N && cl < cn && h >= 0 && h < H && w < W;
+        xv[SET][k] = buffer_load16(
+            xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w) : kOutside);
       }
 #pragma unroll
       for (int k = 0; k < HN; ++k) {
@@ -129,12 +141,12 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int cl = t / IMGS;
-        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
+        const int n = o.n0 + img, h = o.h0 + rr - 1;
         const int w = o.w0 + (side ? TW : -1);
-        const bool ok = (HI_ % NT == 0 || it < HI_) && n < N && c < C && h >= 0 && h < H &&
+        const bool ok = (HI_ % NT == 0 || it < HI_) && n < N && cl < cn && h >= 0 && h < H &&
                         w >= 0 && w < W;
-        xh[SET][k] = (uint16_t)buffer_load2(xview, ok ? 2u * (uint32_t)(((n * C + c) * H + h) * W + w)
-                                                 : kOutside);
+        xh[SET][k] = (uint16_t)buffer_load2(
+            xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w) : kOutside);
       }
     }
   };
@@ -205,10 +217,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           t /= HR;
           const int img = t % IMGS;
           const int cl = t / IMGS;
-          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + cc;
+          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           uint16_t v = 0;
-          if (n < N && c < C && h >= 0 && h < H && w >= 0 && w < W)
-            v = x[((long)n * C + c) * HW + (long)h * W + w];
+          if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W)
+            v = xsrc[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
           xs[cl * PLX + (img * HR + rr) * RSX + 8 + cc] = v;
         }
       }
@@ -300,13 +312,14 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   }
 
   const int c = c0 + cb * 32 + l32;
+  const bool c_ok = cb * 32 + l32 < cn;
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     const int t = r * 3 + s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int k = k0 + kb * 32 + acc_row(v, hi);
-      if (k < K && c < C) {
+      if (k < K && c_ok) {
         if (slice_stride)
           out[(long)slice * slice_stride + ((long)t * K + k) * C + c] = acc[s][v];
         else
@@ -323,26 +336,29 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
 }
 
 template <int TW, int TH, int IMGS>
-static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g,
-                                   float* out, float* out_db, long slice_stride, int N, int C,
-                                   int K, int H, int W, hipStream_t stream) {
+static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, Split<const uint16_t> x,
+                                   const uint16_t* g, float* out, float* out_db,
+                                   long slice_stride, int N, int C, int K, int H, int W,
+                                   hipStream_t stream) {
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
+  const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
+  const long hw2 = (long)H * W * 2;
   if (vec)
-    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
-                       out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64, (uint32_t)((long)N * C * H * W * 2),
-                       (uint32_t)((long)N * K * H * W * 2));
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x.p0,
+                       x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
+                       pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
+                       (K + 63) / 64, (uint32_t)(N * x.c0 * hw2),
+                       (uint32_t)(N * (C - x.c0) * hw2), (uint32_t)(N * K * hw2));
   else
-    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
-                       out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64, 0u, 0u);
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x.p0,
+                       x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
+                       pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
+                       (K + 63) / 64, 0u, 0u, 0u);
 }
 
-bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
-                       float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
-                       hipStream_t stream) {
+bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
+                       float* dw, float* db, float* ws, int N, int C, int K, int H, int W,
+                       const ActArgs& a, hipStream_t stream) {
   if (pl.threads != 768) return false;
   // No fused activation on the bfloat16 backward-weight pass (the caller
   // rejects one).
@@ -352,10 +368,11 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
   const long stride = pl.split > 1 ? n_dw : 0;
   bool found = false;
-#define CONV3X3_X(TW_, TH_, IMGS_)                                                           \
-  if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                          \
-    launch_wgrad_bf16_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, stream);  \
-    found = true;                                                                            \
+#define CONV3X3_X(TW_, TH_, IMGS_)                                                          \
+  if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                         \
+    launch_wgrad_bf16_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, \
+                                            W, stream);                                     \
+    found = true;                                                                           \
   }
   CONV3X3_WGRAD_BF16_CONFIGS(CONV3X3_X)
 #undef CONV3X3_X

@@ -17,6 +17,11 @@
 // reduced across lanes with fixed-order cross-lane adds, to its own
 // workspace slot; wgrad_reduce_kernel adds the slots in a fixed order.  No
 // atomics anywhere: results are bitwise reproducible.
+//
+// x may be the channel concatenation of two tensors (a UNet's up-path input
+// [upsampled ; skip]): channels [0, cx0) from x and [cx0, C) from x1.  Each
+// 64-channel tile lies inside one of them (a tensor's ragged last tile is
+// zero-padded), so the choice is uniform per workgroup.
 #include "activation.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -27,10 +32,11 @@ namespace conv3x3 {
 
 template <int TW, int TH, int IMGS, bool VEC>
 __global__ __launch_bounds__(768) void wgrad_f32_kernel(
-    const float* __restrict__ x, const float* __restrict__ g, float* __restrict__ out,
-    float* __restrict__ out_db, int N, int C, int K, int H, int W, int tiles_w, int tiles_h,
-    int nchunks, int per_split, long slice_stride, int split, int tiles_c, int tiles_k,
-    uint32_t x_bytes, uint32_t g_bytes, int act, const float* __restrict__ zsrc) {
+    const float* __restrict__ x, const float* __restrict__ x1, int cx0,
+    const float* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
+    int C, int K, int H, int W, int tiles_w, int tiles_h, int nchunks, int per_split,
+    long slice_stride, int split, int tiles_c, int tiles_k, uint32_t x_bytes, uint32_t x1_bytes,
+    uint32_t g_bytes, int act, const float* __restrict__ zsrc) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P == 64, "pixel chunk must hold 64 pixels");
   constexpr int GS = wgrad_f32_gstride(IMGS, TH, TW);
@@ -56,7 +62,15 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const int L = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   if (L >= split * ntile) return;
   const int slice = L / ntile, tile = L % ntile;
-  const int c0 = (tile % tiles_c) * 64;
+  // channel tile: channels cl0 .. cl0 + cn - 1 of x tensor `xseg` (cs
+  // channels), channel c0 of dw
+  const int ct = tile % tiles_c, nct0 = (cx0 + 63) / 64;
+  const bool xseg = ct >= nct0;
+  const int cl0 = (ct - (xseg ? nct0 : 0)) * 64;
+  const int cs = xseg ? C - cx0 : cx0;
+  const int c0 = (xseg ? cx0 : 0) + cl0;
+  const int cn = min(64, cs - cl0);
+  const float* const xp = xseg ? x1 : x;
   const int k0 = (tile / tiles_c) * 64;
   const long HW = (long)H * W;
   const bool do_db = out_db != nullptr && tile % tiles_c == 0;
@@ -93,7 +107,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   // no branches).
   const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
   const __amdgpu_buffer_rsrc_t zview = buffer_view(zsrc, zs ? g_bytes : 0u);
-  const __amdgpu_buffer_rsrc_t xview = buffer_view(x, x_bytes);
+  const __amdgpu_buffer_rsrc_t xview = buffer_view(xp, xseg ? x1_bytes : x_bytes);
   auto load_tiles = [&](int chunk) {
     if constexpr (VEC) {
       const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
@@ -121,11 +135,11 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int cl = t / IMGS;
-        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
-        const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && c < C && h >= 0 &&
+        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
+        const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && cl < cn && h >= 0 &&
                         h < H && w < W;
         xv[k] = __builtin_bit_cast(
-            f32x4, buffer_load16(xview, ok ? 4u * (uint32_t)(((n * C + c) * H + h) * W + w)
+            f32x4, buffer_load16(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
                                             : kOutside));
       }
 #pragma unroll
@@ -138,12 +152,12 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int cl = t / IMGS;
-        const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1;
+        const int n = o.n0 + img, h = o.h0 + rr - 1;
         const int w = o.w0 + (side ? TW : -1);
-        const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && c < C && h >= 0 &&
+        const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && cl < cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
         xf[k] = __builtin_bit_cast(
-            float, buffer_load4(xview, ok ? 4u * (uint32_t)(((n * C + c) * H + h) * W + w)
+            float, buffer_load4(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
                                           : kOutside));
       }
     }
@@ -232,10 +246,10 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
           t /= HR;
           const int img = t % IMGS;
           const int cl = t / IMGS;
-          const int n = o.n0 + img, c = c0 + cl, h = o.h0 + rr - 1, w = o.w0 + cc;
+          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
-          if (n < N && c < C && h >= 0 && h < H && w >= 0 && w < W)
-            v = x[((long)n * C + c) * HW + (long)h * W + w];
+          if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W)
+            v = xp[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
           xs[cl * PLW + (img * HR + rr) * RSW + 1 + cc] = v;
         }
       }
@@ -308,13 +322,14 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   // out + slice * slice_stride (32 consecutive c per store).  No split: dw
   // itself, [k][c][tap].
   const int c = c0 + cb * 32 + l32;
+  const bool c_ok = cb * 32 + l32 < cn;
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     const int t = r * 3 + s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int k = k0 + kb * 32 + acc_row(v, hi);
-      if (k < K && c < C) {
+      if (k < K && c_ok) {
         if (slice_stride)
           out[(long)slice * slice_stride + ((long)t * K + k) * C + c] = acc[s][v];
         else
@@ -443,24 +458,26 @@ __global__ __launch_bounds__(512) void wgrad_reduce4_kernel(const float* __restr
 }
 
 template <int TW, int TH, int IMGS>
-static void launch_wgrad_geom(const Plan& pl, bool vec, const float* x, const float* g,
+static void launch_wgrad_geom(const Plan& pl, bool vec, Split<const float> x, const float* g,
                               float* out, float* out_db, long slice_stride, int N, int C, int K,
                               int H, int W, const ActArgs& a, hipStream_t stream) {
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
+  const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
+  const long hw4 = (long)H * W * 4;
   if (vec)
-    hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x, g, out,
-                       out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64, (uint32_t)((long)N * C * H * W * 4),
-                       (uint32_t)((long)N * K * H * W * 4), a.act, a.zsrc);
+    hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x.p0, x.p1,
+                       x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
+                       pl.chunks_per_split, slice_stride, pl.split, tiles_c, (K + 63) / 64,
+                       (uint32_t)(N * x.c0 * hw4), (uint32_t)(N * (C - x.c0) * hw4),
+                       (uint32_t)(N * K * hw4), a.act, a.zsrc);
   else
-    hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x, g,
-                       out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride, pl.split, (C + 63) / 64,
-                       (K + 63) / 64, 0u, 0u, a.act, a.zsrc);
+    hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x.p0,
+                       x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
+                       pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
+                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc);
 }
 
-bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
+bool launch_wgrad_f32(const Plan& pl, bool vec, Split<const float> x, const float* g, float* dw,
                       float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                       hipStream_t stream) {
   if (pl.threads != 768) return false;
@@ -471,7 +488,8 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, 
   bool found = false;
 #define CONV3X3_X(TW_, TH_, IMGS_)                                                           \
   if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                          \
-    launch_wgrad_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, a, stream);  \
+    launch_wgrad_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, W, a, \
+                                       stream);                                              \
     found = true;                                                                            \
   }
   CONV3X3_WGRAD_F32_CONFIGS(CONV3X3_X)

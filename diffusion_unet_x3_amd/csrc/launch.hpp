@@ -9,23 +9,32 @@
 
 namespace conv3x3 {
 
+// A channel axis held by two tensors: channels [0, c0) in p0 and [c0, C) in
+// p1 (the concatenation [p0 ; p1]).  One tensor is c0 = C (p1 unused).
+template <typename T>
+struct Split {
+  T* p0 = nullptr;
+  T* p1 = nullptr;
+  int c0 = 0;
+};
+
 // Forward (pl.pass == kFwd; src = x, Cin = C, Cout = K) or backward-data
 // (pl.pass == kBwdData; src = g, Cin = K, Cout = C; bias ignored), float32.
-// a: forward -- a.act and a.zout fused into the epilogue; backward-data --
-// the source is multiplied by act'(a.zsrc) as it is staged (a.zsrc has the
-// source's shape).
-bool launch_fwd_f32(const Plan& pl, bool vec, const float* src, const float* wt, const float* bias,
-                    float* dst, int N, int Cin, int Cout, int H, int W, const ActArgs& a,
-                    hipStream_t stream);
+// a: forward -- a.act and a.zout fused into the epilogue (dst one tensor);
+// backward-data -- the source is multiplied by act'(a.zsrc) as it is staged
+// (a.zsrc has the source's shape; src one tensor).
+bool launch_fwd_f32(const Plan& pl, bool vec, Split<const float> src, const float* wt,
+                    const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
+                    const ActArgs& a, hipStream_t stream);
 
 // Same, bfloat16 inputs (raw 16-bit patterns), float32 outputs.
-bool launch_fwd_bf16(const Plan& pl, bool vec, const uint16_t* src, const uint16_t* wt,
-                     const float* bias, float* dst, int N, int Cin, int Cout, int H, int W,
+bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
+                     const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
                      const ActArgs& a, hipStream_t stream);
 
 // Backward-weight (+ optional db), float32; ws holds the per-slice partials
 // when pl.split > 1.  g is multiplied by act'(a.zsrc) as it is staged.
-bool launch_wgrad_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
+bool launch_wgrad_f32(const Plan& pl, bool vec, Split<const float> x, const float* g, float* dw,
                       float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                       hipStream_t stream);
 
@@ -34,7 +43,8 @@ void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C
                          hipStream_t stream);
 
 // Same, bfloat16 inputs.
-bool launch_wgrad_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g, float* dw,
+bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
+                       float* dw,
                        float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                        hipStream_t stream);
 

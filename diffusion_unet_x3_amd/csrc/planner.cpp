@@ -10,6 +10,13 @@ namespace {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Tiles of `tile` channels over C channels held by one tensor (c0 < 0 or
+// c0 == C) or by two (c0 and C - c0 channels, tiled separately).
+int channel_tiles(int C, int c0, int tile) {
+  if (c0 < 0 || c0 >= C) return ceil_div(C, tile);
+  return ceil_div(c0, tile) + ceil_div(C - c0, tile);
+}
+
 struct Block {
   int tw, th, imgs;
 };
@@ -85,6 +92,7 @@ bool plan(const Problem& p, Plan* out) {
   pl.dtype = p.dtype;
   if (p.pass == kFwd || p.pass == kBwdData) {
     const int cout = p.pass == kFwd ? p.K : p.C;
+    const int cout0 = p.pass == kFwd ? -1 : p.C0;  // backward-data: dx may be two tensors
     // Candidate workgroup tiles, preferred first: (pixels, channels, waves
     // along channels).
     struct Cand {
@@ -121,7 +129,7 @@ bool plan(const Problem& p, Plan* out) {
       eff[i] = 0.0;
       wgs[i] = 0;
       if (!fwd_cfg_exists(p.dtype, b, cands[i].co, cands[i].wco, cands[i].nw)) continue;
-      wgs[i] = blocks_of(b, p.N, p.H, p.W) * ceil_div(cout, cands[i].co);
+      wgs[i] = blocks_of(b, p.N, p.H, p.W) * channel_tiles(cout, cout0, cands[i].co);
       eff[i] = (double)p.N * p.H * p.W * cout / ((double)wgs[i] * cands[i].bm * cands[i].co);
       if (eff[i] > best_eff) best_eff = eff[i];
     }
@@ -143,7 +151,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.tiles_h = ceil_div(p.H, pl.th);
     pl.tiles_n = ceil_div(p.N, pl.imgs);
     pl.grid_x = pl.tiles_n * pl.tiles_h * pl.tiles_w;
-    pl.grid_y = ceil_div(cout, pl.tile_co);
+    pl.grid_y = channel_tiles(cout, cout0, pl.tile_co);
     pl.grid_z = 1;
     pl.threads = 64 * cands[pick].nw;
     pl.lds_bytes = p.dtype == kF32
@@ -170,7 +178,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.nchunks = pl.tiles_n * pl.tiles_h * pl.tiles_w;
     // One round of 12-wave workgroups (one per compute unit): as many
     // reduction slices as fit next to the channel tiles.
-    const int tiles = ceil_div(p.K, pl.tile_co) * ceil_div(p.C, pl.tile_ci);
+    const int tiles = ceil_div(p.K, pl.tile_co) * channel_tiles(p.C, p.C0, pl.tile_ci);
     int split = kWgradTargetWGs / tiles;
     if (split > pl.nchunks) split = pl.nchunks;
     if (split < 1) split = 1;

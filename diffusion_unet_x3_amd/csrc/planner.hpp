@@ -43,9 +43,13 @@ struct Plan {
 
 // Problem dims as the implicit GEMM sees them.  For backward-data the
 // "input" channels are K (g is the input) and the output channels are C.
+// C0: when x (and dx) is the concatenation of two tensors, the channels of
+// the first; -1 (or C) for one tensor.  Channel tiles never straddle the two
+// tensors, so the number of C tiles is that of each tensor added.
 struct Problem {
   int pass, dtype;
   int N, C, K, H, W;
+  int C0 = -1;
 };
 
 bool plan(const Problem& p, Plan* out);

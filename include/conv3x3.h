@@ -186,6 +186,38 @@ int conv3x3_bwd_weight_act(const void* x, const void* gy, const float* z, float*
                            int N, int C, int K, int H, int W, int dtype, int act,
                            conv3x3_stream_t stream);
 
+/*
+ * Concatenated input (a UNet's up-path blocks take the channel
+ * concatenation [x0 ; x1] of the upsampled features and the skip tensor --
+ * the standard UNet that the sourcepulse summary's "How It Works" builds).
+ * These entry points run the convolution of that concatenation with C0 + C1
+ * input channels, reading x0 ([N][C0][H][W]) and x1 ([N][C1][H][W]) where
+ * they are: the concatenated tensor is never formed.  w is
+ * [K][C0 + C1][3][3] (channels 0..C0-1 act on x0).  Backward-data writes the
+ * input gradient's two halves, dx0 [N][C0][H][W] and dx1 [N][C1][H][W].
+ * C0 >= 0, C1 >= 0, C0 + C1 >= 1; a half with no channels is not read or
+ * written and its pointer may be NULL (the call is then the plain one).
+ * Otherwise arguments, dtypes, limits (on C = C0 + C1), ownership and errors
+ * are those of the plain entry points.  Every workgroup reads (or writes)
+ * one half, so there is no per-element selection; a half whose channel count
+ * is not a multiple of the channel tile costs one partly filled tile.
+ */
+int conv3x3_fwd_cat(const void* x0, const void* x1, int C0, int C1, const void* w,
+                    const float* bias, float* y, int N, int K, int H, int W, int dtype,
+                    conv3x3_stream_t stream);
+
+int conv3x3_bwd_data_cat(const void* g, const void* w, float* dx0, float* dx1, int C0, int C1,
+                         int N, int K, int H, int W, int dtype, conv3x3_stream_t stream);
+
+/* Workspace bytes of conv3x3_bwd_weight_cat ((size_t)-1 for invalid
+ * arguments); it can differ from the plain size for C0 + C1 channels. */
+size_t conv3x3_bwd_weight_cat_workspace_size(int N, int C0, int C1, int K, int H, int W,
+                                             int dtype);
+
+int conv3x3_bwd_weight_cat(const void* x0, const void* x1, int C0, int C1, const void* g,
+                           float* dw, float* db, void* workspace, size_t workspace_bytes, int N,
+                           int K, int H, int W, int dtype, conv3x3_stream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* conv3x3_status_string(int status);
 
@@ -212,6 +244,10 @@ typedef struct {
 
 int conv3x3_plan(int pass, int N, int C, int K, int H, int W, int dtype,
                  conv3x3_plan_t* out);
+
+/* The plan of a *_cat call (C0 + C1 channels in two tensors). */
+int conv3x3_plan_cat(int pass, int N, int C0, int C1, int K, int H, int W, int dtype,
+                     conv3x3_plan_t* out);
 
 #ifdef __cplusplus
 }

@@ -137,3 +137,68 @@ def test_activation_argument_checks():
         S["ERR_WORKSPACE"]
     assert L.conv3x3_bwd_weight_act(X, G, Z, Y, B, Z, need, N, C, K, H, W, 0, silu, None) == \
         S["ERR_ALIAS"]
+
+
+X1, DX0, DX1 = (ctypes.c_void_p(0x10000 * (i + 11)) for i in range(3))
+
+
+@pytest.mark.parametrize("halves", [(-1, 4), (4, -1), (0, 0), (2**30, 2**30)])
+def test_concat_bad_halves_rejected(halves):
+    C0, C1 = halves
+    bad = S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_fwd_cat(X, X1, C0, C1, Wt, B, Y, 2, 4, 5, 5, 0, None) == bad
+    assert L.conv3x3_bwd_data_cat(G, Wt, DX0, DX1, C0, C1, 2, 4, 5, 5, 0, None) == bad
+    assert L.conv3x3_bwd_weight_cat(X, X1, C0, C1, G, Y, B, WS, 1 << 30, 2, 4, 5, 5, 0,
+                                    None) == bad
+    assert L.conv3x3_bwd_weight_cat_workspace_size(2, C0, C1, 4, 5, 5, 0) == \
+        ctypes.c_size_t(-1).value
+    p = lib3.Plan()
+    assert L.conv3x3_plan_cat(0, 2, C0, C1, 4, 5, 5, 0, ctypes.byref(p)) == bad
+
+
+def test_concat_missing_half_rejected():
+    null = S["ERR_NULL_POINTER"]
+    # a half with channels needs its pointer
+    assert L.conv3x3_fwd_cat(None, X1, 3, 4, Wt, B, Y, 2, 4, 5, 5, 0, None) == null
+    assert L.conv3x3_fwd_cat(X, None, 3, 4, Wt, B, Y, 2, 4, 5, 5, 0, None) == null
+    assert L.conv3x3_bwd_data_cat(G, Wt, None, DX1, 3, 4, 2, 4, 5, 5, 0, None) == null
+    assert L.conv3x3_bwd_data_cat(G, Wt, DX0, None, 3, 4, 2, 4, 5, 5, 0, None) == null
+    assert L.conv3x3_bwd_weight_cat(X, None, 3, 4, G, Y, B, WS, 1 << 30, 2, 4, 5, 5, 0,
+                                    None) == null
+    # an empty half may be NULL: the call then fails on the next check only
+    # (a bad dtype here), not on the pointer
+    bad_dtype = S["ERR_BAD_DTYPE"]
+    assert L.conv3x3_fwd_cat(None, X1, 0, 4, Wt, B, Y, 2, 4, 5, 5, 7, None) == bad_dtype
+    assert L.conv3x3_bwd_data_cat(G, Wt, DX0, None, 3, 0, 2, 4, 5, 5, 7, None) == bad_dtype
+
+
+def test_concat_aliasing_rejected():
+    alias = S["ERR_ALIAS"]
+    assert L.conv3x3_fwd_cat(X, X1, 3, 4, Wt, B, X1, 2, 4, 5, 5, 0, None) == alias
+    assert L.conv3x3_bwd_data_cat(G, Wt, DX0, DX0, 3, 4, 2, 4, 5, 5, 0, None) == alias
+    assert L.conv3x3_bwd_data_cat(G, Wt, DX0, G, 3, 4, 2, 4, 5, 5, 0, None) == alias
+    assert L.conv3x3_bwd_weight_cat(X, X1, 3, 4, G, X1, B, WS, 1 << 30, 2, 4, 5, 5, 0,
+                                    None) == alias
+
+
+def test_concat_plans_tile_each_half():
+    """Channel tiles never straddle the two tensors: the bwd_data grid and the
+    bwd_weight tile count are the sums over the halves."""
+    p = lib3.conv3x3_plan_cat(lib3.PASS_BWD_DATA, 32, 100, 28, 256, 32, 32)
+    q = lib3.conv3x3_plan(lib3.PASS_BWD_DATA, 32, 128, 256, 32, 32)
+    m = p["tile_m"]
+    assert p["grid_y"] == -(-100 // m) + -(-28 // m)
+    assert q["grid_y"] == -(-128 // q["tile_m"])
+    # halves that are whole tiles give the plain plan
+    assert lib3.conv3x3_plan_cat(lib3.PASS_BWD_DATA, 32, 512, 128, 256, 32, 32) == \
+        lib3.conv3x3_plan(lib3.PASS_BWD_DATA, 32, 640, 256, 32, 32)
+    assert lib3.conv3x3_plan_cat(lib3.PASS_BWD_WEIGHT, 32, 512, 128, 256, 32, 32) == \
+        lib3.conv3x3_plan(lib3.PASS_BWD_WEIGHT, 32, 640, 256, 32, 32)
+    # an empty half is the plain plan too
+    for pas in (0, 1, 2):
+        assert lib3.conv3x3_plan_cat(pas, 4, 0, 24, 16, 9, 9) == \
+            lib3.conv3x3_plan(pas, 4, 24, 16, 9, 9)
+    # ragged halves: bwd_weight has one more 64-channel tile
+    r = lib3.conv3x3_plan_cat(lib3.PASS_BWD_WEIGHT, 2, 40, 40, 64, 8, 8)
+    assert r["workspace_bytes"] == \
+        lib3.conv3x3_bwd_weight_cat_workspace_size(2, 40, 40, 64, 8, 8, 0)
