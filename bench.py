@@ -135,9 +135,10 @@ class LayerRun:
     """Device buffers and the three pass launches of one layer.  act: the
     forward fuses the activation (and writes z), the float32 backward passes
     read z and fuse its derivative; the bfloat16 backward passes run on gy
-    as is."""
+    as is.  cat: a layer whose input is a skip concatenation (layer.cat > 0)
+    runs the *_cat entry points on its two halves."""
 
-    def __init__(self, layer, act="none"):
+    def __init__(self, layer, act="none", cat=False):
         import torch
         import diffusion_unet_x3_amd as lib3
         import workloads as wl
@@ -155,23 +156,57 @@ class LayerRun:
         self.fused_bwd = fused_backward(act, layer.dtype)
         self.z = torch.empty((N, K, H, W), device=dev) if self.act else None
         code = lib3.CONV3X3_F32 if layer.dtype == "f32" else lib3.CONV3X3_BF16
-        ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
+        self.C0 = layer.cat if cat else 0
+        if self.C0:
+            if self.act:
+                raise ValueError("the *_cat entry points take no activation")
+            C0 = self.C0
+            self.x0 = self.x[:, :C0].contiguous()
+            self.x1 = self.x[:, C0:].contiguous()
+            self.dx0 = torch.empty((N, C0, H, W), device=dev)
+            self.dx1 = torch.empty((N, C - C0, H, W), device=dev)
+            ws = lib3.conv3x3_bwd_weight_cat_workspace_size(N, C0, C - C0, K, H, W, code)
+        else:
+            ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
 
+    def concat_copy_ms(self, steps=10):
+        """Average time of the copy that forms [x0 ; x1] as one tensor (what
+        the *_cat entry points avoid), for comparison only."""
+        import torch
+        for _ in range(2):
+            torch.cat([self.x0, self.x1], 1, out=self.x)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            torch.cat([self.x0, self.x1], 1, out=self.x)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
     def fwd(self):
-        if self.act:
+        if self.C0:
+            self.lib3.conv3x3_fwd_cat(self.x0, self.x1, self.w, self.b, out=self.y)
+        elif self.act:
             self.lib3.conv3x3_fwd_act(self.x, self.w, self.b, act=self.act, out=self.y, z=self.z)
         else:
             self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y)
 
     def bwd_data(self):
-        if self.fused_bwd:
+        if self.C0:
+            self.lib3.conv3x3_bwd_data_cat(self.g, self.w, self.C0, out0=self.dx0,
+                                           out1=self.dx1)
+        elif self.fused_bwd:
             self.lib3.conv3x3_bwd_data_act(self.g, self.z, self.w, act=self.act, out=self.dx)
         else:
             self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx)
 
     def bwd_weight(self):
-        if self.fused_bwd:
+        if self.C0:
+            self.lib3.conv3x3_bwd_weight_cat(self.x0, self.x1, self.g, dw=self.dw, db=self.db,
+                                             workspace=self.ws)
+        elif self.fused_bwd:
             self.lib3.conv3x3_bwd_weight_act(self.x, self.g, self.z, act=self.act, dw=self.dw,
                                              db=self.db, workspace=self.ws)
         else:
@@ -235,7 +270,7 @@ def cpu_baseline(layer, budget_s=15.0):
                       f"({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); cpu: {platform.processor() or platform.machine()}"}
 
 
-def sweep(out_path, steps, warmup, match=None, act="none"):
+def sweep(out_path, steps, warmup, match=None, act="none", cat=False):
     import re
     import torch
     import workloads as wl
@@ -244,12 +279,17 @@ def sweep(out_path, steps, warmup, match=None, act="none"):
         for layer in layers:
             if match and not re.search(match, layer.name):
                 continue
-            run = LayerRun(layer, act)
+            if cat and not layer.cat:
+                continue
+            run = LayerRun(layer, act, cat)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
             f = flops_per_pass(N, C, K, H, W)
             row = {"config": cfg, "layer": layer.name, "dtype": layer.dtype, "act": act,
                    "shape": [N, C, K, H, W], "ms_step": ms}
+            if cat:
+                row["cat"] = layer.cat
+                row["concat_copy_ms"] = run.concat_copy_ms()
             for p, t in per.items():
                 tf = f / (t * 1e-3) / 1e12
                 row[p] = {"ms": t, "tflops": tf, "mfma_frac": tf / PEAK_TFLOPS[layer.dtype],
@@ -275,6 +315,9 @@ def main():
     ap.add_argument("--act", choices=sorted(ACT_CODES), default="none",
                     help="time the fused-activation entry points (forward epilogue; "
                          "float32 backward prologue) instead of the plain ones")
+    ap.add_argument("--cat", action="store_true",
+                    help="with --sweep: time only the layers whose input is a skip "
+                         "concatenation, through the *_cat entry points")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -333,7 +376,7 @@ def main():
         del a, b
         torch.cuda.empty_cache()
     if args.sweep:
-        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act)
+        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -37,6 +37,7 @@ class Layer:
     w_bound: float = 0.0        # U(-w_bound, w_bound); 0 -> Kaiming-uniform sqrt(6/(9C))
     b_bound: float = 0.05
     g_std: float = 1.0
+    cat: int = 0                # > 0: the input is [first `cat` channels ; the rest]
 
     @property
     def weight_bound(self):
@@ -51,7 +52,8 @@ def _unet_sweep(dtype):
     """32 stride-1 3x3 convs of one 64x64 UNet training step: channel
     multipliers [1,2,3,4] on base 128 at resolutions 64/32/16/8, two convs per
     residual block, two blocks per level, down and up paths; up-path blocks
-    take the skip concatenation as one contiguous C_in-channel input."""
+    take the skip concatenation as one contiguous C_in-channel input; ``cat``
+    records where it splits (upsampled features first, then the skip)."""
     ch = [128, 256, 384, 512]
     res = [64, 32, 16, 8]
     layers = []
@@ -62,15 +64,17 @@ def _unet_sweep(dtype):
             layers.append((f"down{lv}", cin, c, res[lv]))
         prev = c
     below = 512
+    cats = [0] * len(layers)
     for lv in reversed(range(4)):
         c = ch[lv]
-        for cin in (below + c, c, 2 * c, c):
+        for cin, first in ((below + c, below), (c, 0), (2 * c, c), (c, 0)):
             layers.append((f"up{lv}", cin, c, res[lv]))
+            cats.append(first)
         below = c
     out = []
     for i, (nm, cin, cout, r) in enumerate(layers):
         out.append(Layer(f"{nm}_{i:02d}_{cin}to{cout}_{r}x{r}_{dtype}", 32, cin, cout, r, r,
-                         dtype, 4, i))
+                         dtype, 4, i, cat=cats[i]))
     return out
 
 
