@@ -286,3 +286,44 @@ def conv3x3_fwd_cat_at(x0, x1, w, b, idx):
 
 def conv3x3_bwd_weight_cat_at(x0, x1, g, idx):
     return conv3x3_bwd_weight_at(_cat(x0, x1), g, idx)
+
+
+# ---------------------------------------------------------------------------
+# Input prologue (GroupNorm-apply + SiLU before the convolution).  The fused
+# bias-and-activation kernel of the project-guide page on StyleGAN2's custom
+# kernels saves a round trip through memory; the same saving on the input
+# side is read as follows: a UNet residual block feeds its convolution
+# a = SiLU(u), u = x * scale[n, c] + shift[n, c], where scale and shift fold a
+# GroupNorm's statistics and affine parameters into one multiplier and one
+# offset per sample and channel.  The convolution pads a (not x) with zeros.
+# The backward passes: the gradient with respect to u is
+# bwd_data(g, w) * SiLU'(u) (what the GroupNorm backward consumes), and dw is
+# the plain backward-weight with the input a.
+
+
+def _prologue_u(x, scale, shift):
+    x = _f64(x)
+    s, t = _f64(scale), _f64(shift)
+    N, C = x.shape[:2]
+    assert s.shape == (N, C) and t.shape == (N, C)
+    return x * s[:, :, None, None] + t[:, :, None, None]
+
+
+def prologue_apply(x, scale, shift):
+    """a = SiLU(x * scale[n, c] + shift[n, c])."""
+    return act_forward(_prologue_u(x, scale, shift), ACT_SILU)
+
+
+def conv3x3_fwd_gnsilu(x, scale, shift, w, b=None):
+    """y = conv3x3_fwd(SiLU(x * scale + shift), w, b)."""
+    return conv3x3_fwd(prologue_apply(x, scale, shift), w, b)
+
+
+def conv3x3_bwd_data_gnsilu(g, w, x, scale, shift):
+    """du = gradient of <y, g> with respect to u = x * scale + shift."""
+    return act_grad(conv3x3_bwd_data(g, w), _prologue_u(x, scale, shift), ACT_SILU)
+
+
+def conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True):
+    """(dw, db) of <conv3x3(SiLU(x * scale + shift); w) + b, g>."""
+    return conv3x3_bwd_weight(prologue_apply(x, scale, shift), g, want_db)
