@@ -116,19 +116,22 @@ def fused_backward(act, dtype):
     return act != "none" and dtype == "f32"
 
 
-def alg_bytes(pass_, N, C, K, H, W, dtype, act="none"):
+def alg_bytes(pass_, N, C, K, H, W, dtype, act="none", prologue=False):
     """Each tensor crosses HBM once: inputs at their dtype, outputs float32.
     With a fused activation the forward also writes z and the fused backward
-    passes also read it (float32, the output's shape)."""
+    passes also read it (float32, the output's shape).  With the input
+    prologue every pass reads scale and shift ([N, C] float32) and
+    backward-data also reads x."""
     s = 4 if dtype == "f32" else 2
     M = N * H * W
     z = 4 * M * K
+    pro = 8 * N * C if prologue else 0
     if pass_ == "fwd":
-        return s * (M * C + 9 * K * C) + 4 * K + 4 * M * K + (z if act != "none" else 0)
+        return s * (M * C + 9 * K * C) + 4 * K + 4 * M * K + (z if act != "none" else 0) + pro
     extra = z if fused_backward(act, dtype) else 0
     if pass_ == "bwd_data":
-        return s * (M * K + 9 * K * C) + 4 * M * C + extra
-    return s * (M * C + M * K) + 4 * (9 * K * C + K) + extra
+        return s * (M * K + 9 * K * C) + 4 * M * C + extra + pro + (s * M * C if prologue else 0)
+    return s * (M * C + M * K) + 4 * (9 * K * C + K) + extra + pro
 
 
 class LayerRun:
@@ -136,9 +139,10 @@ class LayerRun:
     forward fuses the activation (and writes z), the float32 backward passes
     read z and fuse its derivative; the bfloat16 backward passes run on gy
     as is.  cat: a layer whose input is a skip concatenation (layer.cat > 0)
-    runs the *_cat entry points on its two halves."""
+    runs the *_cat entry points on its two halves.  prologue: the *_gnsilu
+    entry points (GroupNorm-apply + SiLU in the loader; float32)."""
 
-    def __init__(self, layer, act="none", cat=False):
+    def __init__(self, layer, act="none", cat=False, prologue=False):
         import torch
         import diffusion_unet_x3_amd as lib3
         import workloads as wl
@@ -157,6 +161,11 @@ class LayerRun:
         self.z = torch.empty((N, K, H, W), device=dev) if self.act else None
         code = lib3.CONV3X3_F32 if layer.dtype == "f32" else lib3.CONV3X3_BF16
         self.C0 = layer.cat if cat else 0
+        self.pro = prologue
+        if prologue:
+            if self.act or cat or layer.dtype != "f32":
+                raise ValueError("the *_gnsilu entry points: float32, no other fusion")
+            self.scale, self.shift = (v.to(dev) for v in wl.make_prologue(layer))
         if self.C0:
             if self.act:
                 raise ValueError("the *_cat entry points take no activation")
@@ -186,7 +195,10 @@ class LayerRun:
         return t0.elapsed_time(t1) / steps
 
     def fwd(self):
-        if self.C0:
+        if self.pro:
+            self.lib3.conv3x3_fwd_gnsilu(self.x, self.scale, self.shift, self.w, self.b,
+                                         out=self.y)
+        elif self.C0:
             self.lib3.conv3x3_fwd_cat(self.x0, self.x1, self.w, self.b, out=self.y)
         elif self.act:
             self.lib3.conv3x3_fwd_act(self.x, self.w, self.b, act=self.act, out=self.y, z=self.z)
@@ -194,7 +206,10 @@ class LayerRun:
             self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y)
 
     def bwd_data(self):
-        if self.C0:
+        if self.pro:
+            self.lib3.conv3x3_bwd_data_gnsilu(self.g, self.w, self.x, self.scale, self.shift,
+                                              out=self.dx)
+        elif self.C0:
             self.lib3.conv3x3_bwd_data_cat(self.g, self.w, self.C0, out0=self.dx0,
                                            out1=self.dx1)
         elif self.fused_bwd:
@@ -203,7 +218,10 @@ class LayerRun:
             self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx)
 
     def bwd_weight(self):
-        if self.C0:
+        if self.pro:
+            self.lib3.conv3x3_bwd_weight_gnsilu(self.x, self.scale, self.shift, self.g,
+                                                dw=self.dw, db=self.db, workspace=self.ws)
+        elif self.C0:
             self.lib3.conv3x3_bwd_weight_cat(self.x0, self.x1, self.g, dw=self.dw, db=self.db,
                                              workspace=self.ws)
         elif self.fused_bwd:
@@ -270,7 +288,7 @@ def cpu_baseline(layer, budget_s=15.0):
                       f"({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); cpu: {platform.processor() or platform.machine()}"}
 
 
-def sweep(out_path, steps, warmup, match=None, act="none", cat=False):
+def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False):
     import re
     import torch
     import workloads as wl
@@ -279,21 +297,22 @@ def sweep(out_path, steps, warmup, match=None, act="none", cat=False):
         for layer in layers:
             if match and not re.search(match, layer.name):
                 continue
-            if cat and not layer.cat:
+            if (cat and not layer.cat) or (prologue and layer.dtype != "f32"):
                 continue
-            run = LayerRun(layer, act, cat)
+            run = LayerRun(layer, act, cat, prologue)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
             f = flops_per_pass(N, C, K, H, W)
             row = {"config": cfg, "layer": layer.name, "dtype": layer.dtype, "act": act,
-                   "shape": [N, C, K, H, W], "ms_step": ms}
+                   "prologue": prologue, "shape": [N, C, K, H, W], "ms_step": ms}
             if cat:
                 row["cat"] = layer.cat
                 row["concat_copy_ms"] = run.concat_copy_ms()
             for p, t in per.items():
                 tf = f / (t * 1e-3) / 1e12
                 row[p] = {"ms": t, "tflops": tf, "mfma_frac": tf / PEAK_TFLOPS[layer.dtype],
-                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype, act) / (t * 1e-3) / 1e9}
+                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype, act, prologue) /
+                          (t * 1e-3) / 1e9}
             rows.append(row)
             print(f"{layer.name:44s} " + " ".join(
                 f"{p}={row[p]['ms'] * 1e3:8.1f}us {row[p]['tflops']:7.1f}TF" for p in per),
@@ -318,6 +337,9 @@ def main():
     ap.add_argument("--cat", action="store_true",
                     help="with --sweep: time only the layers whose input is a skip "
                          "concatenation, through the *_cat entry points")
+    ap.add_argument("--gnsilu", action="store_true",
+                    help="with --sweep: time the float32 layers through the *_gnsilu entry "
+                         "points (GroupNorm-apply + SiLU input prologue)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -376,7 +398,8 @@ def main():
         del a, b
         torch.cuda.empty_cache()
     if args.sweep:
-        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat)
+        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat,
+              args.gnsilu)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

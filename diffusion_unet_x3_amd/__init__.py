@@ -19,6 +19,10 @@ device memory and the current stream.  The functions carry the C names:
     conv3x3_bwd_weight_cat(x0, x1, g, want_db=True, dw=None, db=None,
                            workspace=None)                    -> (dw, db)
     conv3x3_bwd_weight_cat_workspace_size(N, C0, C1, K, H, W, dtype) -> bytes
+    conv3x3_fwd_gnsilu(x, scale, shift, w, bias=None, out=None) -> y
+    conv3x3_bwd_data_gnsilu(g, w, x, scale, shift, out=None)  -> du
+    conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True, dw=None,
+                              db=None, workspace=None)        -> (dw, db)
     conv3x3_status_string(code)                               -> str
     conv3x3_plan(pass_, N, C, K, H, W, dtype)                 -> dict
     conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype)        -> dict
@@ -28,7 +32,11 @@ the forward epilogue and, through z = the forward's pre-activation, into the
 gradient loader of the backward passes (float32 backward only).  The *_cat
 functions take the input as two tensors x0, x1 whose channel concatenation
 [x0 ; x1] is the convolution's input (a UNet's up-path skip input) and never
-form the concatenation; backward-data returns the two gradient halves.
+form the concatenation; backward-data returns the two gradient halves.  The
+*_gnsilu functions fuse a GroupNorm-apply + SiLU input prologue: the
+convolution's input is SiLU(x * scale[n, c] + shift[n, c]) (scale, shift
+float32 [N, C]); backward-data returns du, the gradient at
+u = x * scale + shift (float32 only).
 
 Tensors are NCHW / OIHW, contiguous, on a GPU; x, w, g are float32 or
 bfloat16 (all three alike), bias is float32, outputs are float32.  There is
@@ -55,7 +63,8 @@ EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_siz
             "conv3x3_bwd_weight", "conv3x3_status_string", "conv3x3_plan",
             "conv3x3_fwd_act", "conv3x3_bwd_data_act", "conv3x3_bwd_weight_act",
             "conv3x3_fwd_cat", "conv3x3_bwd_data_cat", "conv3x3_bwd_weight_cat_workspace_size",
-            "conv3x3_bwd_weight_cat", "conv3x3_plan_cat"]
+            "conv3x3_bwd_weight_cat", "conv3x3_plan_cat", "conv3x3_fwd_gnsilu",
+            "conv3x3_bwd_data_gnsilu", "conv3x3_bwd_weight_gnsilu"]
 
 
 class Plan(ctypes.Structure):
@@ -103,6 +112,13 @@ def _load():
     lib.conv3x3_bwd_weight_cat.restype = i
     lib.conv3x3_plan_cat.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.conv3x3_plan_cat.restype = i
+    lib.conv3x3_fwd_gnsilu.argtypes = [vp, fp, fp, vp, fp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_fwd_gnsilu.restype = i
+    lib.conv3x3_bwd_data_gnsilu.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data_gnsilu.restype = i
+    lib.conv3x3_bwd_weight_gnsilu.argtypes = [vp, fp, fp, vp, fp, fp, vp, ctypes.c_size_t,
+                                              i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight_gnsilu.restype = i
     return lib
 
 
@@ -386,3 +402,77 @@ def conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype=CONV3X3_F32):
     rc = lib.conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype, ctypes.byref(p))
     _raise(rc, "conv3x3_plan_cat")
     return {name: getattr(p, name) for name, _ in Plan._fields_}
+
+
+def _check_affine(scale, shift, N, C):
+    for t, name in ((scale, "scale"), (shift, "shift")):
+        _check(t, name, 2)
+        if t.dtype != torch.float32 or tuple(t.shape) != (N, C):
+            raise ValueError(f"{name} must be float32 [N, C] = [{N}, {C}]")
+
+
+def conv3x3_fwd_gnsilu(x, scale, shift, w, bias=None, out=None):
+    """y = conv3x3(SiLU(x * scale + shift); w) + bias, float32."""
+    _check(x, "x", 4)
+    _check(w, "w", 4)
+    N, C, H, W = x.shape
+    K = w.shape[0]
+    _check_affine(scale, shift, N, C)
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != x.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with x's dtype")
+    if bias is not None:
+        _check(bias, "bias", 1)
+        if bias.dtype != torch.float32 or bias.shape[0] != K:
+            raise ValueError("bias must be float32 [K]")
+    y = _f32_out(out, (N, K, H, W), x, "out")
+    rc = lib.conv3x3_fwd_gnsilu(x.data_ptr(), scale.data_ptr(), shift.data_ptr(), w.data_ptr(),
+                                None if bias is None else bias.data_ptr(), y.data_ptr(),
+                                N, C, K, H, W, _dtype_code(x), _stream(x))
+    _raise(rc, "conv3x3_fwd_gnsilu")
+    return y
+
+
+def conv3x3_bwd_data_gnsilu(g, w, x, scale, shift, out=None):
+    """du = conv3x3_bwd_data(g, w) * SiLU'(x * scale + shift), float32."""
+    _check(g, "g", 4)
+    _check(w, "w", 4)
+    _check(x, "x", 4)
+    N, K, H, W = g.shape
+    C = w.shape[1]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with g's dtype")
+    if tuple(x.shape) != (N, C, H, W) or x.dtype != g.dtype:
+        raise ValueError("x must be [N, C, H, W] with g's dtype")
+    _check_affine(scale, shift, N, C)
+    du = _f32_out(out, (N, C, H, W), g, "out")
+    rc = lib.conv3x3_bwd_data_gnsilu(g.data_ptr(), w.data_ptr(), x.data_ptr(), scale.data_ptr(),
+                                     shift.data_ptr(), du.data_ptr(), N, C, K, H, W,
+                                     _dtype_code(g), _stream(g))
+    _raise(rc, "conv3x3_bwd_data_gnsilu")
+    return du
+
+
+def conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True, dw=None, db=None,
+                              workspace=None):
+    """(dw, db) of <conv3x3(SiLU(x * scale + shift); w) + b, g>, float32."""
+    _check(x, "x", 4)
+    _check(g, "g", 4)
+    N, C, H, W = x.shape
+    K = g.shape[1]
+    if tuple(g.shape) != (N, K, H, W) or g.dtype != x.dtype:
+        raise ValueError("g must be [N, K, H, W] with x's dtype")
+    _check_affine(scale, shift, N, C)
+    code = _dtype_code(x)
+    dw = _f32_out(dw, (K, C, 3, 3), x, "dw")
+    db = _f32_out(db, (K,), x, "db") if want_db else None
+    need = conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.conv3x3_bwd_weight_gnsilu(x.data_ptr(), scale.data_ptr(), shift.data_ptr(),
+                                       g.data_ptr(), dw.data_ptr(),
+                                       None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
+                                       N, C, K, H, W, code, _stream(x))
+    _raise(rc, "conv3x3_bwd_weight_gnsilu")
+    return dw, db

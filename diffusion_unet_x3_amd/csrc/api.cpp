@@ -76,8 +76,24 @@ bool is_part(const Split<T>& s, const void* p) {
   return p && (p == (const void*)s.p0 || p == (const void*)s.p1);
 }
 
+// The input prologue's per-sample, per-channel scale and shift (both or
+// neither); float32 only.
+struct Prologue {
+  const float* scale = nullptr;
+  const float* shift = nullptr;
+  bool on() const { return scale || shift; }
+};
+
+int check_prologue(const Prologue& pr, int dtype) {
+  if (!pr.on()) return CONV3X3_OK;
+  if (!pr.scale || !pr.shift) return CONV3X3_ERR_NULL_POINTER;
+  if (dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
+  return CONV3X3_OK;
+}
+
 int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, float* z, int N,
-             int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+             int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
+             Prologue pr = Prologue()) {
   if (!parts_present(x, C) || !w || !y) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -85,14 +101,19 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (rc) return rc;
   rc = check_act(act);
   if (rc) return rc;
+  rc = check_prologue(pr, dtype);
+  if (rc) return rc;
   if (is_part(x, y) || (const void*)y == w || (bias && y == bias)) return CONV3X3_ERR_ALIAS;
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
+  if (pr.on() && (y == pr.scale || y == pr.shift)) return CONV3X3_ERR_ALIAS;
   Plan pl;
   if (!plan(Problem{kFwd, dtype, N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   a.act = act;
   a.zout = z;
+  a.pscale = pr.scale;
+  a.pshift = pr.shift;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -112,8 +133,10 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
 }
 
 int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx, int N, int C,
-                  int K, int H, int W, int dtype, int act, conv3x3_stream_t stream) {
+                  int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
+                  Prologue pr = Prologue(), const void* px = nullptr) {
   if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
+  if (pr.on() && !px) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
   rc = check_dtype(dtype);
@@ -122,9 +145,15 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   if (rc) return rc;
   if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
   if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
+  rc = check_prologue(pr, dtype);
+  if (rc) return rc;
   if (is_part(dx, g) || is_part(dx, w) || (act != CONV3X3_ACT_NONE && is_part(dx, z)) ||
       (dx.c0 > 0 && dx.c0 < C && dx.p0 == dx.p1))
     return CONV3X3_ERR_ALIAS;
+  if (pr.on() && (is_part(dx, px) || is_part(dx, pr.scale) || is_part(dx, pr.shift)))
+    return CONV3X3_ERR_ALIAS;
+  // du's epilogue reads x through a 32-bit buffer view, like the stores
+  if (pr.on() && 4L * N * C * H * W >= 2147483648L) return CONV3X3_ERR_UNSUPPORTED;
   Plan pl;
   if (!plan(Problem{kBwdData, dtype, N, C, K, H, W, dx.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -133,6 +162,9 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
     a.act = act;
     a.zsrc = z;
   }
+  a.pscale = pr.scale;
+  a.pshift = pr.shift;
+  a.px = (const float*)px;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -154,7 +186,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
 
 int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* dw, float* db,
                     void* workspace, size_t workspace_bytes, int N, int C, int K, int H, int W,
-                    int dtype, int act, conv3x3_stream_t stream) {
+                    int dtype, int act, conv3x3_stream_t stream, Prologue pr = Prologue()) {
   if (!parts_present(x, C) || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -168,12 +200,18 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
       (db && (is_part(x, db) || (const void*)db == g || db == dw)))
     return CONV3X3_ERR_ALIAS;
   if (act != CONV3X3_ACT_NONE && (dw == z || (db && db == z))) return CONV3X3_ERR_ALIAS;
+  rc = check_prologue(pr, dtype);
+  if (rc) return rc;
+  if (pr.on() && (dw == pr.scale || dw == pr.shift ||
+                  (db && (db == pr.scale || db == pr.shift))))
+    return CONV3X3_ERR_ALIAS;
   Plan pl;
   if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
   if (workspace && (is_part(x, workspace) || workspace == g || workspace == dw ||
-                    (db && workspace == db) || (act != CONV3X3_ACT_NONE && workspace == z)))
+                    (db && workspace == db) || (act != CONV3X3_ACT_NONE && workspace == z) ||
+                    (pr.on() && (workspace == pr.scale || workspace == pr.shift))))
     return CONV3X3_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
@@ -181,6 +219,8 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
     a.act = act;
     a.zsrc = z;
   }
+  a.pscale = pr.scale;
+  a.pshift = pr.shift;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -249,7 +289,7 @@ const char* conv3x3_status_string(int status) {
     case CONV3X3_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case CONV3X3_ERR_BAD_PASS: return "unknown pass";
     case CONV3X3_ERR_BAD_ACT: return "unknown activation (expected a conv3x3_act_t value)";
-    case CONV3X3_ERR_UNSUPPORTED: return "this dtype's backward pass has no fused activation";
+    case CONV3X3_ERR_UNSUPPORTED: return "this fusion is not provided for this dtype or size";
     default: return "unknown status code";
   }
 }
@@ -340,6 +380,31 @@ int conv3x3_bwd_weight_act(const void* x, const void* gy, const float* z, float*
                            int W, int dtype, int act, conv3x3_stream_t stream) {
   return bwd_weight_impl(one(x, C), gy, z, dw, db, workspace, workspace_bytes, N, C, K, H, W,
                          dtype, act, stream);
+}
+
+int conv3x3_fwd_gnsilu(const void* x, const float* scale, const float* shift, const void* w,
+                       const float* bias, float* y, int N, int C, int K, int H, int W, int dtype,
+                       conv3x3_stream_t stream) {
+  if (!scale || !shift) return CONV3X3_ERR_NULL_POINTER;
+  return fwd_impl(one(x, C), w, bias, y, nullptr, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
+                  Prologue{scale, shift});
+}
+
+int conv3x3_bwd_data_gnsilu(const void* g, const void* w, const void* x, const float* scale,
+                            const float* shift, float* du, int N, int C, int K, int H, int W,
+                            int dtype, conv3x3_stream_t stream) {
+  if (!scale || !shift) return CONV3X3_ERR_NULL_POINTER;
+  return bwd_data_impl(g, nullptr, w, one(du, C), N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
+                       Prologue{scale, shift}, x);
+}
+
+int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* shift,
+                              const void* g, float* dw, float* db, void* workspace,
+                              size_t workspace_bytes, int N, int C, int K, int H, int W,
+                              int dtype, conv3x3_stream_t stream) {
+  if (!scale || !shift) return CONV3X3_ERR_NULL_POINTER;
+  return bwd_weight_impl(one(x, C), g, nullptr, dw, db, workspace, workspace_bytes, N, C, K, H,
+                         W, dtype, CONV3X3_ACT_NONE, stream, Prologue{scale, shift});
 }
 
 }  // extern "C"

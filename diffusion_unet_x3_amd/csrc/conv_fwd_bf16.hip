@@ -685,9 +685,9 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
                      const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
                      const ActArgs& a, hipStream_t stream) {
   if (pl.chunk != 16) return false;
-  // The bfloat16 backward-data pass has no fused activation (the caller
-  // rejects one).
-  if (pl.pass != kFwd && a.zsrc != nullptr) return false;
+  // The bfloat16 backward-data pass has no fused activation and neither
+  // pass has the input prologue (the caller rejects them).
+  if ((pl.pass != kFwd && a.zsrc != nullptr) || a.pscale != nullptr) return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_, NW_)                                              \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                  \
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \

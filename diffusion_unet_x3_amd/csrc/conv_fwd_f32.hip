@@ -35,13 +35,19 @@
 
 namespace conv3x3 {
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4>
+// PRO: the input prologue (forward: SiLU(x * scale + shift) in the loader;
+// backward-data: du = acc * SiLU'(u) in the epilogue); a separate
+// instantiation, so that the plain kernels keep their registers.
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
+          bool PRO = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
     float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
-    uint32_t dst1_bytes, int act, float* __restrict__ zout, const float* __restrict__ zsrc) {
+    uint32_t dst1_bytes, int act, float* __restrict__ zout, const float* __restrict__ zsrc,
+    const float* __restrict__ pscale, const float* __restrict__ pshift,
+    const float* __restrict__ px) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -121,6 +127,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   const bool halo_loads = tiles_w > 1;
 #pragma unroll
   for (int k = 0; k < (VEC ? XH_N : 1); ++k) xf[k] = 0.f;
+  // Forward with the input prologue: each staged x value becomes
+  // SiLU(x * scale[n, c] + shift[n, c]).  An item outside the image or the
+  // channels loads x = scale = shift = 0 (offsets past the views) and so
+  // stages SiLU(0) = 0: the padding stays zero after the activation.
+  constexpr bool pro = MODE == kFwd && PRO;
+  float psv[VEC && pro ? XV_N : 1], ptv[VEC && pro ? XV_N : 1];
+  float psh[VEC && pro ? XH_N : 1], pth[VEC && pro ? XH_N : 1];
+#pragma unroll
+  for (int k = 0; k < (VEC && pro ? XH_N : 1); ++k) psh[k] = pth[k] = 0.f;
+  const uint32_t pbytes = pro ? 4u * (uint32_t)(N * Cin) : 0u;
+  const __amdgpu_buffer_rsrc_t psview = buffer_view(pscale, pbytes);
+  const __amdgpu_buffer_rsrc_t ptview = buffer_view(pshift, pbytes);
 
   // ---------------- staging: weight tile ----------------
   // Forward: for each co, the CB x 9 weights w[co, cg0.., :] are contiguous.
@@ -161,6 +179,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
             ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xv[k] = __builtin_bit_cast(f32x4, buffer_load16(sview, off));
         if (zs) zv[k] = __builtin_bit_cast(f32x4, buffer_load16(zview, off));
+        if constexpr (pro) {
+          const uint32_t po = ok ? 4u * (uint32_t)(n * Cin + f.cg0 + ch) : kOutside;
+          psv[k] = __builtin_bit_cast(float, buffer_load4(psview, po));
+          ptv[k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
+        }
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
@@ -180,6 +203,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
             ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xf[k] = __builtin_bit_cast(float, buffer_load4(sview, off));
         if (zs) zf[k] = __builtin_bit_cast(float, buffer_load4(zview, off));
+        if constexpr (pro) {
+          const uint32_t po = ok ? 4u * (uint32_t)(n * Cin + f.cg0 + ch) : kOutside;
+          psh[k] = __builtin_bit_cast(float, buffer_load4(psview, po));
+          pth[k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
+        }
       }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
@@ -224,6 +252,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
             v.z *= act_slope(act, zv[k].z);
             v.w *= act_slope(act, zv[k].w);
           }
+          if constexpr (pro) {
+            v.x = act_value(kActSilu, v.x * psv[k] + ptv[k]);
+            v.y = act_value(kActSilu, v.y * psv[k] + ptv[k]);
+            v.z = act_value(kActSilu, v.z * psv[k] + ptv[k]);
+            v.w = act_value(kActSilu, v.w * psv[k] + ptv[k]);
+          }
           *reinterpret_cast<f32x4*>(&xs[t * RS + 4 + 4 * q]) = v;
         }
       }
@@ -233,7 +267,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
           const int side = it & 1;
           const int t = it >> 1;
-          xs[t * RS + 4 + (side ? TW : -1)] = zs ? xf[k] * act_slope(act, zf[k]) : xf[k];
+          float v = zs ? xf[k] * act_slope(act, zf[k]) : xf[k];
+          if constexpr (pro) v = act_value(kActSilu, v * psh[k] + pth[k]);
+          xs[t * RS + 4 + (side ? TW : -1)] = v;
         }
       }
 #pragma unroll
@@ -267,6 +303,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
             const long e = ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
             v = sp[e];
             if (zs) v *= act_slope(act, zsrc[e]);
+            if constexpr (pro) {
+              const long pc = (long)n * Cin + f.cg0 + ch;
+              v = act_value(kActSilu, v * pscale[pc] + pshift[pc]);
+            }
           }
           xs[t * RS + 4 + cc] = v;
         }
@@ -355,10 +395,62 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // Forward with a fused activation: y = act(z), z = the accumulator (bias
   // included), also written to zout when it is given.
   // (zout, forward only, has the shape of dst; the output is then one tensor.)
+  // Backward-data with the input prologue: du = acc * SiLU'(x * scale +
+  // shift) at the output position (px has dx's shape, one tensor).
   const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
-  const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
   float* const od = oseg ? dst1 : dst;
   const uint32_t od_bytes = oseg ? dst1_bytes : dst_bytes;
+  if constexpr (MODE == kBwdData && PRO) {
+    // scale and shift of the tile's channels and images, through LDS (the
+    // operand tiles are no longer read); then, four elements at a time, x at
+    // the output position, du = acc * SiLU'(u) and its store (one offset
+    // for both; elements outside the tensor read zero and store nothing).
+    static_assert(2 * IMGS * BCO <= fwd_f32_x_floats(CB, IMGS, TH, TW), "scale/shift fit");
+    float* ps_s = xs;
+    float* pt_s = xs + IMGS * BCO;
+    __syncthreads();
+    for (int e = tid; e < IMGS * BCO; e += NT) {
+      const int n = o.n0 + e / BCO, co = col0 + e % BCO;
+      const bool ok = n < N && co < ocs;
+      ps_s[e] = ok ? pscale[(long)n * Cout + co] : 0.f;
+      pt_s[e] = ok ? pshift[(long)n * Cout + co] : 0.f;
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t xview_b = buffer_view(px, od_bytes);
+    const __amdgpu_buffer_rsrc_t dview_b = buffer_view(od, od_bytes);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wpx * (BM / WPX) + j * 32 + l32;
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      const bool in = n < N && h < H && w < W;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int v0 = 0; v0 < 16; v0 += 4) {
+          float xe[4];
+          uint32_t xo[4];
+#pragma unroll
+          for (int v = v0; v < v0 + 4; ++v) {
+            const int co = cw + i * 32 + acc_row(v, hi);
+            xo[v - v0] =
+                in && co < ocs
+                    ? (((uint32_t)n * ocs + co) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
+                    : kOutside;
+            xe[v - v0] = __builtin_bit_cast(float, buffer_load4(xview_b, xo[v - v0]));
+          }
+#pragma unroll
+          for (int v = v0; v < v0 + 4; ++v) {
+            const int e = img * BCO + (cw - col0) + i * 32 + acc_row(v, hi);
+            buffer_store4(dview_b, xo[v - v0], 0u,
+                          acc[i][j][v] * act_slope(kActSilu, xe[v - v0] * ps_s[e] + pt_s[e]));
+          }
+        }
+      }
+    }
+    return;
+  }
+  const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
   if (od_bytes != 0 && co_n == BCO) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the
@@ -436,17 +528,26 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   const long ob0 = (long)N * dst.c0 * hw4, ob1 = (long)N * (Cout - dst.c0) * hw4;
   const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
-  if (vec)
-    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, true>), grid, block, 0,
-                       stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
-                       Cout, H, W, pl.tiles_w, pl.tiles_h, (uint32_t)(N * src.c0 * hw4),
-                       (uint32_t)(N * (Cin - src.c0) * hw4), (uint32_t)((long)Cin * Cout * 9 * 4),
-                       db0, db1, a.act, a.zout, a.zsrc);
-  else
-    hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, false>), grid, block, 0,
-                       stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
-                       Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1, a.act, a.zout,
-                       a.zsrc);
+  const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * hw4) : 0u;
+  const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * hw4) : 0u;
+  const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
+#define CONV3X3_L(VEC_, PRO_)                                                                     \
+  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_>), grid,     \
+                     block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
+                     Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,       \
+                     a.zout, a.zsrc, a.pscale, a.pshift, a.px)
+  if (a.pscale) {
+    if (vec)
+      CONV3X3_L(true, true);
+    else
+      CONV3X3_L(false, true);
+  } else {
+    if (vec)
+      CONV3X3_L(true, false);
+    else
+      CONV3X3_L(false, false);
+  }
+#undef CONV3X3_L
 }
 
 template <int MODE>

@@ -360,9 +360,9 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const 
                        float* dw, float* db, float* ws, int N, int C, int K, int H, int W,
                        const ActArgs& a, hipStream_t stream) {
   if (pl.threads != 768) return false;
-  // No fused activation on the bfloat16 backward-weight pass (the caller
-  // rejects one).
-  if (a.zsrc != nullptr) return false;
+  // No fused activation or input prologue on the bfloat16 backward-weight
+  // pass (the caller rejects them).
+  if (a.zsrc != nullptr || a.pscale != nullptr) return false;
   const long n_dw = (long)K * C * 9;
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);

@@ -36,7 +36,8 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
     int C, int K, int H, int W, int tiles_w, int tiles_h, int nchunks, int per_split,
     long slice_stride, int split, int tiles_c, int tiles_k, uint32_t x_bytes, uint32_t x1_bytes,
-    uint32_t g_bytes, int act, const float* __restrict__ zsrc) {
+    uint32_t g_bytes, int act, const float* __restrict__ zsrc, const float* __restrict__ pscale,
+    const float* __restrict__ pshift) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P == 64, "pixel chunk must hold 64 pixels");
   constexpr int GS = wgrad_f32_gstride(IMGS, TH, TW);
@@ -101,6 +102,16 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const bool halo_loads = tiles_w > 1;
 #pragma unroll
   for (int k = 0; k < (VEC ? XH_N : 1); ++k) xf[k] = 0.f;
+  // Input prologue: each staged x value becomes SiLU(x * scale[n, c] +
+  // shift[n, c]); items outside the image or the channels load x = scale =
+  // shift = 0 and stage SiLU(0) = 0, so the padding stays zero.
+  const bool pro = pscale != nullptr;
+  float psv[VEC ? XV_N : 1], ptv[VEC ? XV_N : 1], psh[VEC ? XH_N : 1], pth[VEC ? XH_N : 1];
+#pragma unroll
+  for (int k = 0; k < (VEC ? XH_N : 1); ++k) psh[k] = pth[k] = 0.f;
+  const uint32_t pbytes = pro ? 4u * (uint32_t)(N * C) : 0u;
+  const __amdgpu_buffer_rsrc_t psview = buffer_view(pscale, pbytes);
+  const __amdgpu_buffer_rsrc_t ptview = buffer_view(pshift, pbytes);
 
   // Vector path: buffer views; an item outside the tensors or the image
   // reads zero through an offset past the view (32-bit offset arithmetic,
@@ -141,6 +152,11 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         xv[k] = __builtin_bit_cast(
             f32x4, buffer_load16(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
                                             : kOutside));
+        if (pro) {
+          const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
+          psv[k] = __builtin_bit_cast(float, buffer_load4(psview, po));
+          ptv[k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
+        }
       }
 #pragma unroll
       for (int k = 0; k < XH_N; ++k) {
@@ -159,6 +175,11 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         xf[k] = __builtin_bit_cast(
             float, buffer_load4(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
                                           : kOutside));
+        if (pro) {
+          const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
+          psh[k] = __builtin_bit_cast(float, buffer_load4(psview, po));
+          pth[k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
+        }
       }
     }
   };
@@ -198,10 +219,17 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
           const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
           const int cl = t / (IMGS * HR);
           float* d = &xs[cl * PLW + (t % (IMGS * HR)) * RSW + 1 + 4 * q];
-          d[0] = xv[k].x;
-          d[1] = xv[k].y;
-          d[2] = xv[k].z;
-          d[3] = xv[k].w;
+          f32x4 v = xv[k];
+          if (pro) {
+            v.x = act_value(kActSilu, v.x * psv[k] + ptv[k]);
+            v.y = act_value(kActSilu, v.y * psv[k] + ptv[k]);
+            v.z = act_value(kActSilu, v.z * psv[k] + ptv[k]);
+            v.w = act_value(kActSilu, v.w * psv[k] + ptv[k]);
+          }
+          d[0] = v.x;
+          d[1] = v.y;
+          d[2] = v.z;
+          d[3] = v.w;
         }
       }
 #pragma unroll
@@ -211,7 +239,8 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
           const int side = it & 1;
           const int t = it >> 1;
           const int cl = t / (IMGS * HR);
-          xs[cl * PLW + (t % (IMGS * HR)) * RSW + 1 + (side ? TW : -1)] = xf[k];
+          xs[cl * PLW + (t % (IMGS * HR)) * RSW + 1 + (side ? TW : -1)] =
+              pro ? act_value(kActSilu, xf[k] * psh[k] + pth[k]) : xf[k];
         }
       }
     } else {
@@ -248,8 +277,13 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
           const int cl = t / IMGS;
           const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
-          if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W)
+          if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W) {
             v = xp[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
+            if (pro) {
+              const long pc = (long)n * C + c0 + cl;
+              v = act_value(kActSilu, v * pscale[pc] + pshift[pc]);
+            }
+          }
           xs[cl * PLW + (img * HR + rr) * RSW + 1 + cc] = v;
         }
       }
@@ -469,12 +503,12 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, Split<const float> x, co
                        x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
                        pl.chunks_per_split, slice_stride, pl.split, tiles_c, (K + 63) / 64,
                        (uint32_t)(N * x.c0 * hw4), (uint32_t)(N * (C - x.c0) * hw4),
-                       (uint32_t)(N * K * hw4), a.act, a.zsrc);
+                       (uint32_t)(N * K * hw4), a.act, a.zsrc, a.pscale, a.pshift);
   else
     hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x.p0,
                        x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
-                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc);
+                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc, a.pscale, a.pshift);
 }
 
 bool launch_wgrad_f32(const Plan& pl, bool vec, Split<const float> x, const float* g, float* dw,

@@ -72,7 +72,7 @@ typedef enum {
   CONV3X3_ERR_HIP = 6,          /* the HIP runtime rejected a launch */
   CONV3X3_ERR_BAD_PASS = 7,     /* conv3x3_plan: unknown pass */
   CONV3X3_ERR_BAD_ACT = 8,      /* act is not a conv3x3_act_t value */
-  CONV3X3_ERR_UNSUPPORTED = 9   /* a fused activation this dtype's pass does not provide */
+  CONV3X3_ERR_UNSUPPORTED = 9   /* a fusion this dtype (or size) does not provide */
 } conv3x3_status_t;
 
 /*
@@ -217,6 +217,42 @@ size_t conv3x3_bwd_weight_cat_workspace_size(int N, int C0, int C1, int K, int H
 int conv3x3_bwd_weight_cat(const void* x0, const void* x1, int C0, int C1, const void* g,
                            float* dw, float* db, void* workspace, size_t workspace_bytes, int N,
                            int K, int H, int W, int dtype, conv3x3_stream_t stream);
+
+/*
+ * Input prologue: GroupNorm-apply + SiLU fused into the convolution's input
+ * loader -- the input-side counterpart of the fused bias + activation of the
+ * project-guide page on StyleGAN2's custom kernels, as a UNet residual block
+ * uses it before its convolution.  The convolution's input is
+ *   a = SiLU(u),  u = x * scale[n, c] + shift[n, c],
+ * zero-padded after the activation; scale and shift ([N][C] float32) fold a
+ * GroupNorm's statistics and affine parameters into one multiplier and one
+ * offset per sample and channel (computing them is the caller's).  a is
+ * formed as x is staged and never exists in memory.
+ *
+ *   conv3x3_fwd_gnsilu        : y = conv(a; w) + bias (as conv3x3_fwd)
+ *   conv3x3_bwd_data_gnsilu   : du = conv3x3_bwd_data(g, w) * SiLU'(u), the
+ *                               gradient with respect to u (what a GroupNorm
+ *                               backward takes); x, scale, shift are the
+ *                               forward's and du is [N][C][H][W] float32
+ *   conv3x3_bwd_weight_gnsilu : dw, db of the convolution on a (as
+ *                               conv3x3_bwd_weight, same workspace size)
+ *
+ * float32 only (CONV3X3_ERR_UNSUPPORTED for bfloat16); backward-data also
+ * needs x below 2 GiB (else CONV3X3_ERR_UNSUPPORTED).  scale and shift must
+ * not be NULL.  Other arguments, limits and errors as the plain passes.
+ */
+int conv3x3_fwd_gnsilu(const void* x, const float* scale, const float* shift, const void* w,
+                       const float* bias, float* y, int N, int C, int K, int H, int W, int dtype,
+                       conv3x3_stream_t stream);
+
+int conv3x3_bwd_data_gnsilu(const void* g, const void* w, const void* x, const float* scale,
+                            const float* shift, float* du, int N, int C, int K, int H, int W,
+                            int dtype, conv3x3_stream_t stream);
+
+int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* shift,
+                              const void* g, float* dw, float* db, void* workspace,
+                              size_t workspace_bytes, int N, int C, int K, int H, int W,
+                              int dtype, conv3x3_stream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* conv3x3_status_string(int status);

@@ -202,3 +202,29 @@ def test_concat_plans_tile_each_half():
     r = lib3.conv3x3_plan_cat(lib3.PASS_BWD_WEIGHT, 2, 40, 40, 64, 8, 8)
     assert r["workspace_bytes"] == \
         lib3.conv3x3_bwd_weight_cat_workspace_size(2, 40, 40, 64, 8, 8, 0)
+
+
+SC, SH = (ctypes.c_void_p(0x10000 * (i + 21)) for i in range(2))
+
+
+def test_prologue_argument_checks():
+    d = (2, 4, 4, 5, 5)  # N, C, K, H, W
+    null, unsup, alias = S["ERR_NULL_POINTER"], S["ERR_UNSUPPORTED"], S["ERR_ALIAS"]
+    # scale and shift are required
+    assert L.conv3x3_fwd_gnsilu(X, None, SH, Wt, B, Y, *d, 0, None) == null
+    assert L.conv3x3_fwd_gnsilu(X, SC, None, Wt, B, Y, *d, 0, None) == null
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, None, Y, *d, 0, None) == null
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, None, SC, SH, Y, *d, 0, None) == null
+    assert L.conv3x3_bwd_weight_gnsilu(X, None, SH, G, Y, B, WS, 1 << 30, *d, 0, None) == null
+    # float32 only
+    assert L.conv3x3_fwd_gnsilu(X, SC, SH, Wt, B, Y, *d, 1, None) == unsup
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, Y, *d, 1, None) == unsup
+    assert L.conv3x3_bwd_weight_gnsilu(X, SC, SH, G, Y, B, WS, 1 << 30, *d, 1, None) == unsup
+    # outputs may not alias scale / shift / x
+    assert L.conv3x3_fwd_gnsilu(X, SC, SH, Wt, B, SC, *d, 0, None) == alias
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, X, *d, 0, None) == alias
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, SH, *d, 0, None) == alias
+    assert L.conv3x3_bwd_weight_gnsilu(X, SC, SH, G, SC, B, WS, 1 << 30, *d, 0, None) == alias
+    # backward-data's x must stay below 2 GiB (a 32-bit buffer view)
+    big = (64, 1024, 4, 128, 128)
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, Y, *big, 0, None) == unsup

@@ -130,3 +130,15 @@ def make_inputs(layer, integer_exact=False, with_bias=True):
         raise ValueError(f"unknown dtype {layer.dtype}")
     return {"x": x.contiguous(), "w": w.contiguous(),
             "b": b.contiguous() if with_bias else None, "g": g.contiguous()}
+
+
+def make_prologue(layer):
+    """Seeded per-sample, per-channel scale [N, C] ~ U(0.5, 1.5) and shift
+    [N, C] ~ N(0, 0.5^2), float32 CPU tensors: a GroupNorm folded into one
+    multiplier and one offset per sample and channel, at the magnitudes a
+    trained network's normalisation produces."""
+    gen = torch.Generator("cpu").manual_seed(layer.seed * 1000 + layer.index + 500)
+    N, C = layer.N, layer.C
+    scale = torch.rand((N, C), generator=gen) + 0.5
+    shift = torch.randn((N, C), generator=gen) * 0.5
+    return scale.contiguous(), shift.contiguous()
