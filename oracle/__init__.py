@@ -327,3 +327,33 @@ def conv3x3_bwd_data_gnsilu(g, w, x, scale, shift):
 def conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True):
     """(dw, db) of <conv3x3(SiLU(x * scale + shift); w) + b, g>."""
     return conv3x3_bwd_weight(prologue_apply(x, scale, shift), g, want_db)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 outputs.  bfloat16 is the float32 exponent with an 8-bit
+# significand (7 stored bits); the diffusion-fast README's "Bfloat16"
+# section runs its pipeline in it.  A float32 accumulator written as
+# bfloat16 is read as rounded to nearest, ties to even -- IEEE's default
+# rounding -- and the oracle rounds its exact (fp64) result the same way, in
+# one step (rounding through float32 first could round a value twice).
+
+
+def round_to_bf16(a):
+    """Round float64 values to the nearest bfloat16 value, ties to even."""
+    a = np.asarray(a, dtype=np.float64)
+    out = np.zeros_like(a)
+    nz = a != 0
+    x = a[nz]
+    # spacing of bfloat16 values around x: 2^(e - 7) for |x| in [2^e, 2^(e+1)),
+    # and the subnormal spacing 2^-133 below 2^-126
+    e = np.floor(np.log2(np.abs(x)))
+    e = np.maximum(e, -126.0)
+    ulp = np.ldexp(1.0, (e - 7).astype(np.int64))
+    q = x / ulp                      # exact: division by a power of two
+    # np.log2 can be off by one next to a power of two: then |q| leaves
+    # [128, 256) and the spacing is twice (or half) as large
+    ulp = np.where(np.abs(q) >= 256.0, ulp * 2.0, ulp)
+    ulp = np.where((np.abs(q) < 128.0) & (e > -126.0), ulp * 0.5, ulp)
+    q = x / ulp
+    out[nz] = np.round(q) * ulp      # np.round: half to even
+    return out
