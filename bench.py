@@ -116,21 +116,22 @@ def fused_backward(act, dtype):
     return act != "none" and dtype == "f32"
 
 
-def alg_bytes(pass_, N, C, K, H, W, dtype, act="none", prologue=False):
+def alg_bytes(pass_, N, C, K, H, W, dtype, act="none", prologue=False, out_bf16=False):
     """Each tensor crosses HBM once: inputs at their dtype, outputs float32.
     With a fused activation the forward also writes z and the fused backward
     passes also read it (float32, the output's shape).  With the input
     prologue every pass reads scale and shift ([N, C] float32) and
-    backward-data also reads x."""
+    backward-data also reads x.  out_bf16: y and dx are written as bf16."""
     s = 4 if dtype == "f32" else 2
+    o = 2 if out_bf16 else 4
     M = N * H * W
     z = 4 * M * K
     pro = 8 * N * C if prologue else 0
     if pass_ == "fwd":
-        return s * (M * C + 9 * K * C) + 4 * K + 4 * M * K + (z if act != "none" else 0) + pro
+        return s * (M * C + 9 * K * C) + 4 * K + o * M * K + (z if act != "none" else 0) + pro
     extra = z if fused_backward(act, dtype) else 0
     if pass_ == "bwd_data":
-        return s * (M * K + 9 * K * C) + 4 * M * C + extra + pro + (s * M * C if prologue else 0)
+        return s * (M * K + 9 * K * C) + o * M * C + extra + pro + (s * M * C if prologue else 0)
     return s * (M * C + M * K) + 4 * (9 * K * C + K) + extra + pro
 
 
@@ -142,7 +143,7 @@ class LayerRun:
     runs the *_cat entry points on its two halves.  prologue: the *_gnsilu
     entry points (GroupNorm-apply + SiLU in the loader; float32)."""
 
-    def __init__(self, layer, act="none", cat=False, prologue=False):
+    def __init__(self, layer, act="none", cat=False, prologue=False, out_bf16=False):
         import torch
         import diffusion_unet_x3_amd as lib3
         import workloads as wl
@@ -152,8 +153,11 @@ class LayerRun:
         self.x, self.w, self.g = (inp[k].to(dev) for k in ("x", "w", "g"))
         self.b = inp["b"].to(dev)
         N, C, K, H, W = layer.shape
-        self.y = torch.empty((N, K, H, W), device=dev)
-        self.dx = torch.empty((N, C, H, W), device=dev)
+        if out_bf16 and layer.dtype != "bf16":
+            raise ValueError("bfloat16 outputs need a bfloat16 layer")
+        od = torch.bfloat16 if out_bf16 else torch.float32
+        self.y = torch.empty((N, K, H, W), device=dev, dtype=od)
+        self.dx = torch.empty((N, C, H, W), device=dev, dtype=od)
         self.dw = torch.empty((K, C, 3, 3), device=dev)
         self.db = torch.empty((K,), device=dev)
         self.act = ACT_CODES[act]
@@ -172,8 +176,8 @@ class LayerRun:
             C0 = self.C0
             self.x0 = self.x[:, :C0].contiguous()
             self.x1 = self.x[:, C0:].contiguous()
-            self.dx0 = torch.empty((N, C0, H, W), device=dev)
-            self.dx1 = torch.empty((N, C - C0, H, W), device=dev)
+            self.dx0 = torch.empty((N, C0, H, W), device=dev, dtype=od)
+            self.dx1 = torch.empty((N, C - C0, H, W), device=dev, dtype=od)
             ws = lib3.conv3x3_bwd_weight_cat_workspace_size(N, C0, C - C0, K, H, W, code)
         else:
             ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
@@ -288,7 +292,8 @@ def cpu_baseline(layer, budget_s=15.0):
                       f"({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); cpu: {platform.processor() or platform.machine()}"}
 
 
-def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False):
+def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False,
+          out_bf16=False):
     import re
     import torch
     import workloads as wl
@@ -297,22 +302,24 @@ def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=F
         for layer in layers:
             if match and not re.search(match, layer.name):
                 continue
-            if (cat and not layer.cat) or (prologue and layer.dtype != "f32"):
+            if (cat and not layer.cat) or (prologue and layer.dtype != "f32") or \
+                    (out_bf16 and layer.dtype != "bf16"):
                 continue
-            run = LayerRun(layer, act, cat, prologue)
+            run = LayerRun(layer, act, cat, prologue, out_bf16)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
             f = flops_per_pass(N, C, K, H, W)
             row = {"config": cfg, "layer": layer.name, "dtype": layer.dtype, "act": act,
-                   "prologue": prologue, "shape": [N, C, K, H, W], "ms_step": ms}
+                   "prologue": prologue, "out_bf16": out_bf16, "shape": [N, C, K, H, W],
+                   "ms_step": ms}
             if cat:
                 row["cat"] = layer.cat
                 row["concat_copy_ms"] = run.concat_copy_ms()
             for p, t in per.items():
                 tf = f / (t * 1e-3) / 1e12
                 row[p] = {"ms": t, "tflops": tf, "mfma_frac": tf / PEAK_TFLOPS[layer.dtype],
-                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype, act, prologue) /
-                          (t * 1e-3) / 1e9}
+                          "alg_gbs": alg_bytes(p, N, C, K, H, W, layer.dtype, act, prologue,
+                                               out_bf16) / (t * 1e-3) / 1e9}
             rows.append(row)
             print(f"{layer.name:44s} " + " ".join(
                 f"{p}={row[p]['ms'] * 1e3:8.1f}us {row[p]['tflops']:7.1f}TF" for p in per),
@@ -340,6 +347,9 @@ def main():
     ap.add_argument("--gnsilu", action="store_true",
                     help="with --sweep: time the float32 layers through the *_gnsilu entry "
                          "points (GroupNorm-apply + SiLU input prologue)")
+    ap.add_argument("--out-bf16", action="store_true",
+                    help="with --sweep: time the bfloat16 layers with y and dx written as "
+                         "bfloat16 (CONV3X3_BF16_IO)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -399,7 +409,7 @@ def main():
         torch.cuda.empty_cache()
     if args.sweep:
         sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat,
-              args.gnsilu)
+              args.gnsilu, args.out_bf16)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -4,8 +4,8 @@ Argument marshalling only: every step of the convolution runs in the HIP
 kernels behind the C ABI declared in ``include/conv3x3.h``; PyTorch supplies
 device memory and the current stream.  The functions carry the C names:
 
-    conv3x3_fwd(x, w, bias=None, out=None)                    -> y
-    conv3x3_bwd_data(g, w, out=None)                          -> dx
+    conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None)    -> y
+    conv3x3_bwd_data(g, w, out=None, out_dtype=None)          -> dx
     conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None,
                        workspace=None)                        -> (dw, db)
     conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)   -> bytes
@@ -39,7 +39,9 @@ float32 [N, C]); backward-data returns du, the gradient at
 u = x * scale + shift (float32 only).
 
 Tensors are NCHW / OIHW, contiguous, on a GPU; x, w, g are float32 or
-bfloat16 (all three alike), bias is float32, outputs are float32.  There is
+bfloat16 (all three alike), bias is float32, outputs are float32 -- except
+that with bfloat16 inputs y and dx may be written as bfloat16 (pass a
+bfloat16 ``out`` or ``out_dtype=torch.bfloat16``; CONV3X3_BF16_IO).  There is
 no fallback: if the library is missing, importing this package raises.
 """
 import ctypes
@@ -52,6 +54,7 @@ LIB_PATH = os.path.join(_HERE, "libconv3x3.so")
 
 CONV3X3_F32 = 0
 CONV3X3_BF16 = 1
+CONV3X3_BF16_IO = 2  # bf16 inputs, bf16 y / dx
 PASS_FWD, PASS_BWD_DATA, PASS_BWD_WEIGHT = 0, 1, 2
 ACT_NONE, ACT_SILU, ACT_LRELU = 0, 1, 2
 STATUS = {
@@ -155,6 +158,23 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _act_out(out, shape, like, name, out_dtype):
+    """The activation-shaped output (y or dx) and the dtype code of the call:
+    bfloat16 inputs may write it as bfloat16 (out given as a bfloat16 tensor,
+    or out_dtype=torch.bfloat16), everything else writes float32."""
+    want = out.dtype if out is not None else (out_dtype or torch.float32)
+    if want == torch.bfloat16:
+        if like.dtype != torch.bfloat16:
+            raise ValueError("bfloat16 outputs need bfloat16 inputs")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=like.device)
+        _check(out, name, len(shape))
+        if tuple(out.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}")
+        return out, CONV3X3_BF16_IO
+    return _f32_out(out, shape, like, name), _dtype_code(like)
+
+
 def _f32_out(out, shape, like, name):
     if out is None:
         return torch.empty(shape, dtype=torch.float32, device=like.device)
@@ -164,8 +184,9 @@ def _f32_out(out, shape, like, name):
     return out
 
 
-def conv3x3_fwd(x, w, bias=None, out=None):
-    """y = conv3x3(x; w) + bias (stride 1, zero padding 1), float32 output."""
+def conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None):
+    """y = conv3x3(x; w) + bias (stride 1, zero padding 1); float32 output, or
+    bfloat16 for bfloat16 inputs with a bfloat16 out / out_dtype."""
     _check(x, "x", 4)
     _check(w, "w", 4)
     N, C, H, W = x.shape
@@ -176,25 +197,26 @@ def conv3x3_fwd(x, w, bias=None, out=None):
         _check(bias, "bias", 1)
         if bias.dtype != torch.float32 or bias.shape[0] != K:
             raise ValueError("bias must be float32 [K]")
-    y = _f32_out(out, (N, K, H, W), x, "out")
+    y, code = _act_out(out, (N, K, H, W), x, "out", out_dtype)
     rc = lib.conv3x3_fwd(x.data_ptr(), w.data_ptr(),
                          None if bias is None else bias.data_ptr(), y.data_ptr(),
-                         N, C, K, H, W, _dtype_code(x), _stream(x))
+                         N, C, K, H, W, code, _stream(x))
     _raise(rc, "conv3x3_fwd")
     return y
 
 
-def conv3x3_bwd_data(g, w, out=None):
-    """dx = d<conv3x3(x; w), g>/dx, float32 output."""
+def conv3x3_bwd_data(g, w, out=None, out_dtype=None):
+    """dx = d<conv3x3(x; w), g>/dx; float32 output, or bfloat16 as
+    conv3x3_fwd."""
     _check(g, "g", 4)
     _check(w, "w", 4)
     N, K, H, W = g.shape
     C = w.shape[1]
     if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
         raise ValueError("w must be [K, C, 3, 3] with g's dtype")
-    dx = _f32_out(out, (N, C, H, W), g, "out")
+    dx, code = _act_out(out, (N, C, H, W), g, "out", out_dtype)
     rc = lib.conv3x3_bwd_data(g.data_ptr(), w.data_ptr(), dx.data_ptr(),
-                              N, C, K, H, W, _dtype_code(g), _stream(g))
+                              N, C, K, H, W, code, _stream(g))
     _raise(rc, "conv3x3_bwd_data")
     return dx
 
@@ -232,7 +254,8 @@ def conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None, workspace=None):
     return dw, db
 
 
-def conv3x3_fwd_act(x, w, bias=None, act=ACT_SILU, want_z=True, out=None, z=None):
+def conv3x3_fwd_act(x, w, bias=None, act=ACT_SILU, want_z=True, out=None, z=None,
+                    out_dtype=None):
     """(y, z): z = conv3x3(x; w) + bias, y = act(z), both float32 (z None
     unless want_z)."""
     _check(x, "x", 4)
@@ -245,12 +268,12 @@ def conv3x3_fwd_act(x, w, bias=None, act=ACT_SILU, want_z=True, out=None, z=None
         _check(bias, "bias", 1)
         if bias.dtype != torch.float32 or bias.shape[0] != K:
             raise ValueError("bias must be float32 [K]")
-    y = _f32_out(out, (N, K, H, W), x, "out")
+    y, code = _act_out(out, (N, K, H, W), x, "out", out_dtype)
     z = _f32_out(z, (N, K, H, W), x, "z") if want_z else None
     rc = lib.conv3x3_fwd_act(x.data_ptr(), w.data_ptr(),
                              None if bias is None else bias.data_ptr(), y.data_ptr(),
                              None if z is None else z.data_ptr(),
-                             N, C, K, H, W, _dtype_code(x), int(act), _stream(x))
+                             N, C, K, H, W, code, int(act), _stream(x))
     _raise(rc, "conv3x3_fwd_act")
     return y, z
 
@@ -328,7 +351,7 @@ def _ptr(t):
     return t.data_ptr() if t.numel() else None
 
 
-def conv3x3_fwd_cat(x0, x1, w, bias=None, out=None):
+def conv3x3_fwd_cat(x0, x1, w, bias=None, out=None, out_dtype=None):
     """y = conv3x3([x0 ; x1]; w) + bias, the input being the channel
     concatenation of x0 and x1 (never formed)."""
     N, C0, C1, H, W = _halves(x0, x1)
@@ -340,15 +363,15 @@ def conv3x3_fwd_cat(x0, x1, w, bias=None, out=None):
         _check(bias, "bias", 1)
         if bias.dtype != torch.float32 or bias.shape[0] != K:
             raise ValueError("bias must be float32 [K]")
-    y = _f32_out(out, (N, K, H, W), x0, "out")
+    y, code = _act_out(out, (N, K, H, W), x0, "out", out_dtype)
     rc = lib.conv3x3_fwd_cat(_ptr(x0), _ptr(x1), C0, C1, w.data_ptr(),
                              None if bias is None else bias.data_ptr(), y.data_ptr(),
-                             N, K, H, W, _dtype_code(x0), _stream(w))
+                             N, K, H, W, code, _stream(w))
     _raise(rc, "conv3x3_fwd_cat")
     return y
 
 
-def conv3x3_bwd_data_cat(g, w, C0, out0=None, out1=None):
+def conv3x3_bwd_data_cat(g, w, C0, out0=None, out1=None, out_dtype=None):
     """(dx0, dx1): the input gradient of conv3x3([x0 ; x1]; w) split at
     channel C0, float32."""
     _check(g, "g", 4)
@@ -359,10 +382,12 @@ def conv3x3_bwd_data_cat(g, w, C0, out0=None, out1=None):
         raise ValueError("w must be [K, C, 3, 3] with g's dtype")
     if not 0 <= C0 <= C:
         raise ValueError("C0 must lie in [0, C]")
-    dx0 = _f32_out(out0, (N, C0, H, W), g, "out0")
-    dx1 = _f32_out(out1, (N, C - C0, H, W), g, "out1")
+    dx0, code = _act_out(out0, (N, C0, H, W), g, "out0", out_dtype)
+    dx1, code1 = _act_out(out1, (N, C - C0, H, W), g, "out1", out_dtype or dx0.dtype)
+    if code1 != code:
+        raise ValueError("out0 and out1 must have the same dtype")
     rc = lib.conv3x3_bwd_data_cat(g.data_ptr(), w.data_ptr(), _ptr(dx0), _ptr(dx1), C0, C - C0,
-                                  N, K, H, W, _dtype_code(g), _stream(g))
+                                  N, K, H, W, code, _stream(g))
     _raise(rc, "conv3x3_bwd_data_cat")
     return dx0, dx1
 

@@ -26,8 +26,13 @@ int check_dims(int N, int C, int K, int H, int W) {
 }
 
 int check_dtype(int dtype) {
-  return (dtype == CONV3X3_F32 || dtype == CONV3X3_BF16) ? CONV3X3_OK : CONV3X3_ERR_BAD_DTYPE;
+  return (dtype == CONV3X3_F32 || dtype == CONV3X3_BF16 || dtype == CONV3X3_BF16_IO)
+             ? CONV3X3_OK
+             : CONV3X3_ERR_BAD_DTYPE;
 }
+
+// The planner's dtype: the arithmetic (both bf16 modes run the bf16 kernels).
+int kdt(int dtype) { return dtype == CONV3X3_F32 ? kF32 : kBF16; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -107,7 +112,7 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
   if (pr.on() && (y == pr.scale || y == pr.shift)) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kFwd, dtype, N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (!plan(Problem{kFwd, kdt(dtype), N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   a.act = act;
@@ -126,7 +131,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
                      aligned16(w) && buffer_sized((long)N * C * hw) &&
                      buffer_sized((long)K * C * 9);
     Split<const uint16_t> xs{(const uint16_t*)x.p0, (const uint16_t*)x.p1, x.c0};
-    ok = launch_fwd_bf16(pl, vec, xs, (const uint16_t*)w, bias, one(y, K), N, C, K, H, W, a, s);
+    ok = launch_fwd_bf16(pl, vec, xs, (const uint16_t*)w, bias, one(y, K), N, C, K, H, W, a,
+                         dtype == CONV3X3_BF16_IO, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
@@ -155,7 +161,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   // du's epilogue reads x through a 32-bit buffer view, like the stores
   if (pr.on() && 4L * N * C * H * W >= 2147483648L) return CONV3X3_ERR_UNSUPPORTED;
   Plan pl;
-  if (!plan(Problem{kBwdData, dtype, N, C, K, H, W, dx.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (!plan(Problem{kBwdData, kdt(dtype), N, C, K, H, W, dx.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   if (act != CONV3X3_ACT_NONE) {
@@ -178,7 +184,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
                      aligned16(g) && aligned16(w) && buffer_sized((long)N * K * hw) &&
                      buffer_sized((long)K * C * 9);
     ok = launch_fwd_bf16(pl, vec, one((const uint16_t*)g, K), (const uint16_t*)w, nullptr, dx, N,
-                         K, C, H, W, a, s);
+                         K, C, H, W, a, dtype == CONV3X3_BF16_IO, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
@@ -206,7 +212,7 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
                   (db && (db == pr.scale || db == pr.shift))))
     return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (!plan(Problem{kBwdWeight, kdt(dtype), N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
   if (workspace && (is_part(x, workspace) || workspace == g || workspace == dw ||
@@ -270,8 +276,10 @@ int plan_impl(int pass, int N, int C, int K, int H, int W, int dtype, int C0,
   rc = check_dtype(dtype);
   if (rc) return rc;
   Plan pl;
-  if (!plan(Problem{pass, dtype, N, C, K, H, W, C0}, &pl)) return CONV3X3_ERR_BAD_PASS;
-  return fill_plan(pl, pass, out);
+  if (!plan(Problem{pass, kdt(dtype), N, C, K, H, W, C0}, &pl)) return CONV3X3_ERR_BAD_PASS;
+  rc = fill_plan(pl, pass, out);
+  out->dtype = dtype;
+  return rc;
 }
 
 }  // namespace
@@ -283,7 +291,7 @@ const char* conv3x3_status_string(int status) {
     case CONV3X3_OK: return "success";
     case CONV3X3_ERR_NULL_POINTER: return "a required pointer is NULL";
     case CONV3X3_ERR_BAD_SHAPE: return "invalid shape: every dimension must be >= 1 and every tensor < 2^31 elements";
-    case CONV3X3_ERR_BAD_DTYPE: return "unknown dtype (expected CONV3X3_F32 or CONV3X3_BF16)";
+    case CONV3X3_ERR_BAD_DTYPE: return "unknown dtype (expected a conv3x3_dtype_t value)";
     case CONV3X3_ERR_WORKSPACE: return "workspace missing or smaller than conv3x3_bwd_weight_workspace_size()";
     case CONV3X3_ERR_ALIAS: return "an output aliases an input";
     case CONV3X3_ERR_HIP: return "the HIP runtime rejected a kernel launch";
@@ -348,7 +356,7 @@ size_t conv3x3_bwd_weight_cat_workspace_size(int N, int C0, int C1, int K, int H
   if (check_halves(C0, C1) || check_dims(N, C0 + C1, K, H, W) || check_dtype(dtype))
     return (size_t)-1;
   Plan pl;
-  if (!plan(Problem{kBwdWeight, dtype, N, C0 + C1, K, H, W, C0}, &pl)) return (size_t)-1;
+  if (!plan(Problem{kBwdWeight, kdt(dtype), N, C0 + C1, K, H, W, C0}, &pl)) return (size_t)-1;
   return pl.workspace_bytes;
 }
 
@@ -364,7 +372,7 @@ int conv3x3_bwd_weight_cat(const void* x0, const void* x1, int C0, int C1, const
 size_t conv3x3_bwd_weight_workspace_size(int N, int C, int K, int H, int W, int dtype) {
   if (check_dims(N, C, K, H, W) || check_dtype(dtype)) return (size_t)-1;
   Plan pl;
-  if (!plan(Problem{kBwdWeight, dtype, N, C, K, H, W}, &pl)) return (size_t)-1;
+  if (!plan(Problem{kBwdWeight, kdt(dtype), N, C, K, H, W}, &pl)) return (size_t)-1;
   return pl.workspace_bytes;
 }
 

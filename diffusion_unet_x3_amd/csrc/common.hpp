@@ -84,4 +84,18 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t v, uint32_t
                                         (int)soff, 0);
 }
 
+// Store the low 16 bits of x at byte offset voff + soff of a view (same
+// range check as buffer_store4).
+__device__ __forceinline__ void buffer_store2(__amdgpu_buffer_rsrc_t v, uint32_t voff,
+                                              uint32_t soff, uint32_t x) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)x, v, (int)voff, (int)soff, 0);
+}
+
+// float32 -> bfloat16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 }  // namespace conv3x3

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
     float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
-    uint32_t dst1_bytes, int act, float* __restrict__ zout) {
+    uint32_t dst1_bytes, int act, float* __restrict__ zout, int outb) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -588,8 +588,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // ---------------- epilogue: NCHW stores ----------------
   // Forward with a fused activation: y = act(z), z = the accumulator (bias
-  // included), also written to zout when it is given.
+  // included), also written to zout (float32) when it is given.
   // (zout, forward only, has the shape of dst; the output is then one tensor.)
+  // outb: dst (and dst1) hold bfloat16, rounded to nearest even.
   const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
   const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
   float* const od = oseg ? dst1 : dst;
@@ -600,34 +601,68 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     // step a uniform (scalar) offset.  Pixels outside the image get an offset
     // past the view and the hardware drops their stores.
     const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
-    const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : od_bytes);
-    const uint32_t plane = (uint32_t)HW * 4u;
+    const __amdgpu_buffer_rsrc_t zov =
+        buffer_view(zout, plain ? 0u : (outb ? 2u : 1u) * od_bytes);
+    const uint32_t es = outb ? 2u : 4u;  // bytes per output element
+    // bfloat16 with an even width: lanes 2m and 2m + 1 hold horizontally
+    // adjacent pixels, so for each pair of rows (v, v + 1) the two lanes
+    // swap one value and lane 2m stores row v's pixel pair, lane 2m + 1 row
+    // v + 1's, as one 4-byte store each (half the store instructions; the
+    // epilogue is bound by their count, not by bytes).
+    const bool pack = outb && (W & 1) == 0;
+    const bool odd = l32 & 1;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int p = wpx * (BM / WPX) + j * 32 + l32;
       const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
       const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
-      const uint32_t off =
-          (n < N && h < H && w < W)
-              ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
-              : kOutside;
-      if (plain) {
+      const bool in = n < N && h < H && w < W;
+      const uint32_t e = ((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w);
+      const uint32_t off = in ? e * es : kOutside, zoff = in ? e * 4u : kOutside;
+      if (pack) {
+        // pair start (the even lane's pixel); the odd lane's row is one
+        // plane further
+        const uint32_t poff = in ? (e - (odd ? 1u : 0u) + (odd ? (uint32_t)HW : 0u)) * 2u
+                                 : kOutside;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
-                          acc[i][j][v]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const uint32_t so = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane;
-            if (zout) buffer_store4(zov, off, so, acc[i][j][v]);
-            buffer_store4(dv, off, so, act_value(act, acc[i][j][v]));
+          for (int v = 0; v < 16; v += 2) {
+            const uint32_t rowoff = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * (uint32_t)HW;
+            float a0 = acc[i][j][v], a1 = acc[i][j][v + 1];
+            if (!plain) {
+              if (zout) {
+                buffer_store4(zov, zoff, rowoff * 4u, a0);
+                buffer_store4(zov, zoff, (rowoff + (uint32_t)HW) * 4u, a1);
+              }
+              a0 = act_value(act, a0);
+              a1 = act_value(act, a1);
+            }
+            // quad_perm [1, 0, 3, 2]: each lane reads its neighbour 2m <-> 2m + 1
+            const float got = __builtin_bit_cast(
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, odd ? a0 : a1), 0xB1,
+                                                0xF, 0xF, false));
+            const float lo = odd ? got : a0, hi2 = odd ? a1 : got;
+            buffer_store4(dv, poff, rowoff * 2u,
+                          __builtin_bit_cast(float, bf16_rne(lo) | (bf16_rne(hi2) << 16)));
           }
+        continue;
       }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t rowoff = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * (uint32_t)HW;
+          float val = acc[i][j][v];
+          if (!plain) {
+            if (zout) buffer_store4(zov, zoff, rowoff * 4u, val);
+            val = act_value(act, val);
+          }
+          if (outb)
+            buffer_store2(dv, off, rowoff * 2u, bf16_rne(val));
+          else
+            buffer_store4(dv, off, rowoff * 4u, val);
+        }
     }
     return;
   }
@@ -637,19 +672,23 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
     if (n >= N || h >= H || w >= W) continue;
-    float* out = od + (long)n * ocs * HW + (long)h * W + w;
+    const long base = (long)n * ocs * HW + (long)h * W + w;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int co = cw + i * 32 + acc_row(v, hi);
         if (co < ocs) {
-          if (plain) {
-            out[(long)co * HW] = acc[i][j][v];
-          } else {
-            if (zout) zout[(out - od) + (long)co * HW] = acc[i][j][v];
-            out[(long)co * HW] = act_value(act, acc[i][j][v]);
+          const long ei = base + (long)co * HW;
+          float val = acc[i][j][v];
+          if (!plain) {
+            if (zout) zout[ei] = val;
+            val = act_value(act, val);
           }
+          if (outb)
+            reinterpret_cast<uint16_t*>(od)[ei] = (uint16_t)bf16_rne(val);
+          else
+            od[ei] = val;
         }
       }
     }
@@ -659,31 +698,34 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
 static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                             const uint16_t* wt, const float* bias, Split<float> dst, int N,
-                            int Cin, int Cout, int H, int W, const ActArgs& a,
+                            int Cin, int Cout, int H, int W, const ActArgs& a, bool out_bf16,
                             hipStream_t stream) {
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(64 * NW, 1, 1);
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
-  // offsets); otherwise both take the plain-store path.
+  // offsets), and a float32 z beside bfloat16 outputs twice that; otherwise
+  // the plain-store path runs.
   const long hw = (long)H * W;
-  const long ob0 = (long)N * dst.c0 * hw * 4, ob1 = (long)N * (Cout - dst.c0) * hw * 4;
-  const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
+  const long es = out_bf16 ? 2 : 4, zf = a.zout ? 4 / es : 1;
+  const long ob0 = (long)N * dst.c0 * hw * es, ob1 = (long)N * (Cout - dst.c0) * hw * es;
+  const bool small = ob0 * zf < 2147483648L && ob1 * zf < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
   if (vec)
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true>), grid, block, 0,
                        stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
                        Cout, H, W, pl.tiles_w, pl.tiles_h, (uint32_t)(N * src.c0 * hw * 2),
                        (uint32_t)(N * (Cin - src.c0) * hw * 2),
-                       (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout);
+                       (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout,
+                       out_bf16 ? 1 : 0);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false>), grid, block,
                        0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N,
                        Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1, a.act,
-                       a.zout);
+                       a.zout, out_bf16 ? 1 : 0);
 }
 
 bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
                      const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
-                     const ActArgs& a, hipStream_t stream) {
+                     const ActArgs& a, bool out_bf16, hipStream_t stream) {
   if (pl.chunk != 16) return false;
   // The bfloat16 backward-data pass has no fused activation and neither
   // pass has the input prologue (the caller rejects them).
@@ -693,10 +735,12 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \
     if (pl.pass == kFwd)                                                                        \
       launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, bias, dst, N,    \
-                                                             Cin, Cout, H, W, a, stream);       \
+                                                             Cin, Cout, H, W, a, out_bf16,      \
+                                                             stream);                           \
     else                                                                                        \
       launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, nullptr, dst, \
-                                                                 N, Cin, Cout, H, W, a, stream); \
+                                                                 N, Cin, Cout, H, W, a,          \
+                                                                 out_bf16, stream);              \
     return true;                                                                                \
   }
   CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)

@@ -26,6 +26,11 @@
  *   CONV3X3_BF16 : x, w, g are bfloat16 (raw 16-bit patterns); products are
  *                  exact and accumulate in float32.
  *   In both modes bias is float32 and every output (y, dx, dw, db) is float32.
+ *   CONV3X3_BF16_IO : as CONV3X3_BF16, but y and dx (the activations and
+ *                  input gradients that the next layer reads) are written
+ *                  as bfloat16, rounded to nearest even from the float32
+ *                  accumulators; dw, db (and a fused activation's z) stay
+ *                  float32.  Halves the bytes of the two largest stores.
  *
  * Memory and ownership: every pointer is a device pointer (hipMalloc'd or
  * torch-allocated) owned by the caller.  The library allocates nothing,
@@ -59,7 +64,8 @@ typedef struct ihipStream_t* conv3x3_stream_t;
 
 typedef enum {
   CONV3X3_F32 = 0,
-  CONV3X3_BF16 = 1
+  CONV3X3_BF16 = 1,
+  CONV3X3_BF16_IO = 2
 } conv3x3_dtype_t;
 
 typedef enum {
@@ -105,7 +111,8 @@ typedef enum {
  * Forward with fused bias:  y = conv(x; w) + bias.
  *   x    : [N][C][H][W], dtype          w : [K][C][3][3], dtype
  *   bias : [K] float32, or NULL for no bias
- *   y    : [N][K][H][W] float32 (overwritten)
+ *   y    : [N][K][H][W] float32 (overwritten); for CONV3X3_BF16_IO bfloat16,
+ *          the pointer then addressing 16-bit values
  * Implicit GEMM with M = N*H*W pixels, N = K output channels and a
  * reduction of length 9*C; input tiles and their one-pixel halo are staged
  * in LDS, the products run on MFMA.
@@ -117,7 +124,7 @@ int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y,
 /*
  * Backward-data:  dx = gradient of <conv(x; w), g> with respect to x.
  *   g  : [N][K][H][W], dtype      w : [K][C][3][3], dtype
- *   dx : [N][C][H][W] float32 (overwritten)
+ *   dx : [N][C][H][W] float32 (overwritten); bfloat16 for CONV3X3_BF16_IO
  * The same implicit GEMM as the forward pass over g, with the weight tile
  * transposed (k <-> c) and rotated by 180 degrees while it is staged in LDS.
  */

@@ -65,7 +65,7 @@ def test_null_pointers_rejected():
     assert L.conv3x3_bwd_weight(X, G, None, B, WS, 1 << 40, *d, 0, None) == S["ERR_NULL_POINTER"]
 
 
-@pytest.mark.parametrize("dtype", [-1, 2, 7])
+@pytest.mark.parametrize("dtype", [-1, 3, 7])
 def test_bad_dtype_rejected(dtype):
     d = (2, 3, 4, 5, 6)
     assert L.conv3x3_fwd(X, Wt, B, Y, *d, dtype, None) == S["ERR_BAD_DTYPE"]
@@ -115,7 +115,7 @@ def test_activation_argument_checks():
     # shapes, dtypes and required pointers as the plain entry points
     assert L.conv3x3_fwd_act(X, Wt, B, Y, Z, 0, 3, 4, 5, 6, 0, silu, None) == S["ERR_BAD_SHAPE"]
     assert L.conv3x3_fwd_act(None, Wt, B, Y, Z, *d, 0, silu, None) == S["ERR_NULL_POINTER"]
-    assert L.conv3x3_fwd_act(X, Wt, B, Y, Z, *d, 2, silu, None) == S["ERR_BAD_DTYPE"]
+    assert L.conv3x3_fwd_act(X, Wt, B, Y, Z, *d, 3, silu, None) == S["ERR_BAD_DTYPE"]
     # z may not alias another argument
     assert L.conv3x3_fwd_act(X, Wt, B, Y, Y, *d, 0, silu, None) == S["ERR_ALIAS"]
     assert L.conv3x3_fwd_act(X, Wt, B, Y, X, *d, 0, silu, None) == S["ERR_ALIAS"]
