@@ -50,7 +50,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libconv3x3.so")
+# CONV3X3_LIB selects another build of the same library (e.g. to compare two
+# builds in one process); by default the in-tree one is loaded.
+LIB_PATH = os.environ.get("CONV3X3_LIB") or os.path.join(_HERE, "libconv3x3.so")
 
 CONV3X3_F32 = 0
 CONV3X3_BF16 = 1

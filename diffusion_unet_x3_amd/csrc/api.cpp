@@ -122,8 +122,12 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && x.c0 % 4 == 0 && parts_aligned(x) &&
-                     aligned16(w) && buffer_sized(2L * N * C * hw) && buffer_sized(2L * K * C * 9);
+    // (3 input channels in one tensor: the packed-tap forward, vector x
+    // loads and scalar weight loads)
+    const bool pack3 = C == 3 && x.c0 == C && !pr.on();
+    const bool vec = W % 4 == 0 && ((C % 4 == 0 && x.c0 % 4 == 0) || pack3) &&
+                     parts_aligned(x) && aligned16(w) && buffer_sized(2L * N * C * hw) &&
+                     buffer_sized(2L * K * C * 9);
     Split<const float> xs{(const float*)x.p0, (const float*)x.p1, x.c0};
     ok = launch_fwd_f32(pl, vec, xs, (const float*)w, bias, one(y, K), N, C, K, H, W, a, s);
   } else {

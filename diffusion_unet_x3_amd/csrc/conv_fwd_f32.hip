@@ -38,8 +38,13 @@ namespace conv3x3 {
 // PRO: the input prologue (forward: SiLU(x * scale + shift) in the loader;
 // backward-data: du = acc * SiLU'(u) in the epilogue); a separate
 // instantiation, so that the plain kernels keep their registers.
+// PC (forward, vector path, 3 or 4 input channels, e.g. an RGB image): the
+// reduction runs over the 9 * PC (channel, tap) pairs packed two per MFMA
+// step -- ceil(9 PC / 2) steps instead of the 36 of an 8-channel fill.  The
+// tile's weights w[co0 .. co0 + BCO - 1, 0..PC-1, 0..8] are one contiguous
+// run of BCO * 9 PC floats, staged with 16-byte loads.
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
-          bool PRO = false>
+          bool PRO = false, int PC = 0>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -59,7 +64,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int PL = fwd_f32_plane(IMGS, TH, TW);
   constexpr int WS = fwd_f32_wstride(BCO);
   constexpr int HR = TH + 2;  // staged rows per image (with halo)
-  constexpr int NSTEP = CB / 2 * 9;
+  static_assert(PC == 0 || (MODE == kFwd && VEC && PC < CB), "packed taps: forward only");
+  constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * 9;
 
   __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
@@ -150,6 +156,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int WS_ITEMS = CB * 9 * BCO;
   constexpr int WS_N = (WS_ITEMS + NT - 1) / NT;
   f32x4 wv[VEC ? WV_N : 1];
+  // packed taps: float4 items of the tile's contiguous weight run
+  constexpr int PW = PC ? BCO * PC * 9 / 4 : 1;
+  constexpr int PW_N = (PW + NT - 1) / NT;
+  static_assert(PC == 0 || (BCO * PC * 9 % 4 == 0 && PW_N <= WV_N), "packed weight items fit");
 
   // Vector path: global -> registers here (one fill ahead), registers -> LDS
   // in store_tiles.  Scalar path: everything happens in store_tiles.
@@ -209,8 +219,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           pth[k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
         }
       }
+      if constexpr (PC != 0) {
+#pragma unroll
+        for (int k = 0; k < PW_N; ++k) {
+          const int it = tid + k * NT;
+          const bool ok = (PW % NT == 0 || it < PW) && 4 * it < co_n * PC * 9;
+          wv[k] = __builtin_bit_cast(
+              f32x4, buffer_load16(wview, ok ? 4u * (uint32_t)(co0 * PC * 9 + 4 * it) : kOutside));
+        }
+      }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
+        if constexpr (PC != 0) break;  // packed taps: the contiguous run above
         const int it = tid + k * NT;
         const int run = it / (RUN / 4);
         const int e = 4 * (it % (RUN / 4));
@@ -272,8 +292,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           xs[t * RS + 4 + (side ? TW : -1)] = v;
         }
       }
+      if constexpr (PC != 0) {
+        // packed taps: element q of the run is weight e = q % 9PC of output
+        // channel q / 9PC; with 9 PC odd the last step's second element
+        // (e = 9 PC) reads a zero slot
+        if constexpr (PC * 9 % 2 != 0)
+          for (int r = tid; r < BCO; r += NT) ws[w_slot(r, PC * 9)] = 0.f;
+#pragma unroll
+        for (int k = 0; k < PW_N; ++k) {
+          const int it = tid + k * NT;
+          if (PW % NT == 0 || it < PW) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int q = 4 * it + u;
+              ws[w_slot(q / (PC * 9), q % (PC * 9))] = wv[k][u];
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int k = 0; k < WV_N; ++k) {
+        if constexpr (PC != 0) break;
         const int it = tid + k * NT;
         if (WV_ITEMS % NT == 0 || it < WV_ITEMS) {
           const int run = it / (RUN / 4);
@@ -337,18 +376,31 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   for (int j = 0; j < NJ; ++j) {
     const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
-    boff[j] = hi * PL + (img * HR + row) * RS + 4 + col - 1;
+    boff[j] = (PC ? 0 : hi * PL) + (img * HR + row) * RS + 4 + col - 1;
   }
-  const int aoff = hi * 9 * WS + wco * (BCO / WCO) + l32;
+  const int aoff = (PC ? hi : hi * 9) * WS + wco * (BCO / WCO) + l32;
 
   // Operands of one MFMA step st = (cp, r, s), cp the channel pair.
   float a[2][MI], b[2][NJ];
   auto read_step = [&](int buf, int st) {
-    const int cp = st / 9, r = (st % 9) / 3, s = st % 3;
+    if constexpr (PC != 0) {
+      // reduction elements e = 2 st (lanes 0-31) and 2 st + 1 (32-63), each
+      // a (channel, tap) pair; weight slot e, pixel offset of (c, r, s)
+      const int e0 = 2 * st, e1 = 2 * st + 1;
+      const int o0 = (e0 / 9) * PL + ((e0 % 9) / 3) * RS + e0 % 3;
+      const int o1 = (e1 / 9) * PL + ((e1 % 9) / 3) * RS + e1 % 3;
+      const int ob = hi ? o1 : o0;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + (2 * cp * 9 + r * 3 + s) * WS + i * 32];
+      for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + e0 * WS + i * 32];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
+      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + ob];
+    } else {
+      const int cp = st / 9, r = (st % 9) / 3, s = st % 3;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + (2 * cp * 9 + r * 3 + s) * WS + i * 32];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
+    }
   };
 
   // Forward: the accumulators start at the tile's biases (zero without
@@ -531,21 +583,27 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * hw4) : 0u;
   const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * hw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_)                                                                     \
-  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_>), grid,     \
+#define CONV3X3_L(VEC_, PRO_, PC_)                                                                \
+  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_>), grid,\
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,       \
                      a.zout, a.zsrc, a.pscale, a.pshift, a.px)
+  // packed taps: the forward of a 3- or 4-channel single tensor
+  const int pc = (MODE == kFwd && vec && !a.pscale && src.c0 == Cin) ? Cin : 0;
   if (a.pscale) {
     if (vec)
-      CONV3X3_L(true, true);
+      CONV3X3_L(true, true, 0);
     else
-      CONV3X3_L(false, true);
+      CONV3X3_L(false, true, 0);
+  } else if (pc == 3) {
+    CONV3X3_L(true, false, MODE == kFwd ? 3 : 0);
+  } else if (pc == 4) {
+    CONV3X3_L(true, false, MODE == kFwd ? 4 : 0);
   } else {
     if (vec)
-      CONV3X3_L(true, false);
+      CONV3X3_L(true, false, 0);
     else
-      CONV3X3_L(false, false);
+      CONV3X3_L(false, false, 0);
   }
 #undef CONV3X3_L
 }

@@ -142,3 +142,10 @@ def make_prologue(layer):
     scale = torch.rand((N, C), generator=gen) + 0.5
     shift = torch.randn((N, C), generator=gen) * 0.5
     return scale.contiguous(), shift.contiguous()
+
+
+# The first convolution of the UNet: the 3-channel 64x64 image into the 128
+# base channels (the shape of the diffusion UNet's stem; not one of the
+# benchmark configurations, a case for the few-channel paths).
+IMAGE_STEM = {dt: Layer(f"image_stem_32x3to128_64x64_{dt}", 32, 3, 128, 64, 64, dt, 6, 0)
+              for dt in ("f32", "bf16")}
