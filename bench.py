@@ -143,7 +143,8 @@ class LayerRun:
     runs the *_cat entry points on its two halves.  prologue: the *_gnsilu
     entry points (GroupNorm-apply + SiLU in the loader; float32)."""
 
-    def __init__(self, layer, act="none", cat=False, prologue=False, out_bf16=False):
+    def __init__(self, layer, act="none", cat=False, prologue=False, out_bf16=False,
+                 split=True):
         import torch
         import diffusion_unet_x3_amd as lib3
         import workloads as wl
@@ -164,6 +165,7 @@ class LayerRun:
         self.fused_bwd = fused_backward(act, layer.dtype)
         self.z = torch.empty((N, K, H, W), device=dev) if self.act else None
         code = lib3.CONV3X3_F32 if layer.dtype == "f32" else lib3.CONV3X3_BF16
+        self.split = split
         self.C0 = layer.cat if cat else 0
         self.pro = prologue
         if prologue:
@@ -207,7 +209,7 @@ class LayerRun:
         elif self.act:
             self.lib3.conv3x3_fwd_act(self.x, self.w, self.b, act=self.act, out=self.y, z=self.z)
         else:
-            self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y)
+            self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y, split=self.split)
 
     def bwd_data(self):
         if self.pro:
@@ -219,7 +221,7 @@ class LayerRun:
         elif self.fused_bwd:
             self.lib3.conv3x3_bwd_data_act(self.g, self.z, self.w, act=self.act, out=self.dx)
         else:
-            self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx)
+            self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx, split=self.split)
 
     def bwd_weight(self):
         if self.pro:
@@ -293,7 +295,7 @@ def cpu_baseline(layer, budget_s=15.0):
 
 
 def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False,
-          out_bf16=False):
+          out_bf16=False, split=True):
     import re
     import torch
     import workloads as wl
@@ -305,7 +307,7 @@ def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=F
             if (cat and not layer.cat) or (prologue and layer.dtype != "f32") or \
                     (out_bf16 and layer.dtype != "bf16"):
                 continue
-            run = LayerRun(layer, act, cat, prologue, out_bf16)
+            run = LayerRun(layer, act, cat, prologue, out_bf16, split)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
             f = flops_per_pass(N, C, K, H, W)
@@ -350,6 +352,9 @@ def main():
     ap.add_argument("--out-bf16", action="store_true",
                     help="with --sweep: time the bfloat16 layers with y and dx written as "
                          "bfloat16 (CONV3X3_BF16_IO)")
+    ap.add_argument("--no-split", action="store_true",
+                    help="with --sweep: call the entry points without a workspace (no split "
+                         "reduction on small bf16 images)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -409,7 +414,7 @@ def main():
         torch.cuda.empty_cache()
     if args.sweep:
         sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat,
-              args.gnsilu, args.out_bf16)
+              args.gnsilu, args.out_bf16, not args.no_split)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -4,8 +4,11 @@ Argument marshalling only: every step of the convolution runs in the HIP
 kernels behind the C ABI declared in ``include/conv3x3.h``; PyTorch supplies
 device memory and the current stream.  The functions carry the C names:
 
-    conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None)    -> y
-    conv3x3_bwd_data(g, w, out=None, out_dtype=None)          -> dx
+    conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None, split=True,
+                workspace=None)                               -> y
+    conv3x3_bwd_data(g, w, out=None, out_dtype=None, split=True,
+                     workspace=None)                          -> dx
+    conv3x3_workspace_size(pass_, N, C, K, H, W, dtype)       -> bytes
     conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None,
                        workspace=None)                        -> (dw, db)
     conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)   -> bytes
@@ -69,7 +72,8 @@ EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_siz
             "conv3x3_fwd_act", "conv3x3_bwd_data_act", "conv3x3_bwd_weight_act",
             "conv3x3_fwd_cat", "conv3x3_bwd_data_cat", "conv3x3_bwd_weight_cat_workspace_size",
             "conv3x3_bwd_weight_cat", "conv3x3_plan_cat", "conv3x3_fwd_gnsilu",
-            "conv3x3_bwd_data_gnsilu", "conv3x3_bwd_weight_gnsilu"]
+            "conv3x3_bwd_data_gnsilu", "conv3x3_bwd_weight_gnsilu", "conv3x3_workspace_size",
+            "conv3x3_fwd_ws", "conv3x3_bwd_data_ws"]
 
 
 class Plan(ctypes.Structure):
@@ -117,6 +121,12 @@ def _load():
     lib.conv3x3_bwd_weight_cat.restype = i
     lib.conv3x3_plan_cat.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.conv3x3_plan_cat.restype = i
+    lib.conv3x3_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.conv3x3_workspace_size.restype = ctypes.c_size_t
+    lib.conv3x3_fwd_ws.argtypes = [vp, vp, fp, fp, vp, ctypes.c_size_t, i, i, i, i, i, i, vp]
+    lib.conv3x3_fwd_ws.restype = i
+    lib.conv3x3_bwd_data_ws.argtypes = [vp, vp, fp, vp, ctypes.c_size_t, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data_ws.restype = i
     lib.conv3x3_fwd_gnsilu.argtypes = [vp, fp, fp, vp, fp, fp, i, i, i, i, i, i, vp]
     lib.conv3x3_fwd_gnsilu.restype = i
     lib.conv3x3_bwd_data_gnsilu.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, vp]
@@ -186,9 +196,28 @@ def _f32_out(out, shape, like, name):
     return out
 
 
-def conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None):
+def conv3x3_workspace_size(pass_, N, C, K, H, W, dtype=CONV3X3_F32):
+    n = lib.conv3x3_workspace_size(pass_, N, C, K, H, W, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid problem for conv3x3_workspace_size")
+    return n
+
+
+def _workspace(need, workspace, like):
+    """(pointer, bytes) of a workspace of at least `need` bytes: the given
+    one, or a new torch allocation."""
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=like.device)
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None, split=True, workspace=None):
     """y = conv3x3(x; w) + bias (stride 1, zero padding 1); float32 output, or
-    bfloat16 for bfloat16 inputs with a bfloat16 out / out_dtype."""
+    bfloat16 for bfloat16 inputs with a bfloat16 out / out_dtype.  split:
+    run through conv3x3_fwd_ws, which may split a small-image bf16
+    reduction (the workspace is allocated unless given)."""
     _check(x, "x", 4)
     _check(w, "w", 4)
     N, C, H, W = x.shape
@@ -200,16 +229,22 @@ def conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None):
         if bias.dtype != torch.float32 or bias.shape[0] != K:
             raise ValueError("bias must be float32 [K]")
     y, code = _act_out(out, (N, K, H, W), x, "out", out_dtype)
-    rc = lib.conv3x3_fwd(x.data_ptr(), w.data_ptr(),
-                         None if bias is None else bias.data_ptr(), y.data_ptr(),
-                         N, C, K, H, W, code, _stream(x))
-    _raise(rc, "conv3x3_fwd")
+    b = None if bias is None else bias.data_ptr()
+    if split:
+        ws, nb = _workspace(conv3x3_workspace_size(PASS_FWD, N, C, K, H, W, code), workspace, x)
+        rc = lib.conv3x3_fwd_ws(x.data_ptr(), w.data_ptr(), b, y.data_ptr(), ws, nb,
+                                N, C, K, H, W, code, _stream(x))
+        _raise(rc, "conv3x3_fwd_ws")
+    else:
+        rc = lib.conv3x3_fwd(x.data_ptr(), w.data_ptr(), b, y.data_ptr(),
+                             N, C, K, H, W, code, _stream(x))
+        _raise(rc, "conv3x3_fwd")
     return y
 
 
-def conv3x3_bwd_data(g, w, out=None, out_dtype=None):
+def conv3x3_bwd_data(g, w, out=None, out_dtype=None, split=True, workspace=None):
     """dx = d<conv3x3(x; w), g>/dx; float32 output, or bfloat16 as
-    conv3x3_fwd."""
+    conv3x3_fwd; split / workspace as conv3x3_fwd."""
     _check(g, "g", 4)
     _check(w, "w", 4)
     N, K, H, W = g.shape
@@ -217,9 +252,16 @@ def conv3x3_bwd_data(g, w, out=None, out_dtype=None):
     if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
         raise ValueError("w must be [K, C, 3, 3] with g's dtype")
     dx, code = _act_out(out, (N, C, H, W), g, "out", out_dtype)
-    rc = lib.conv3x3_bwd_data(g.data_ptr(), w.data_ptr(), dx.data_ptr(),
-                              N, C, K, H, W, code, _stream(g))
-    _raise(rc, "conv3x3_bwd_data")
+    if split:
+        ws, nb = _workspace(conv3x3_workspace_size(PASS_BWD_DATA, N, C, K, H, W, code),
+                            workspace, g)
+        rc = lib.conv3x3_bwd_data_ws(g.data_ptr(), w.data_ptr(), dx.data_ptr(), ws, nb,
+                                     N, C, K, H, W, code, _stream(g))
+        _raise(rc, "conv3x3_bwd_data_ws")
+    else:
+        rc = lib.conv3x3_bwd_data(g.data_ptr(), w.data_ptr(), dx.data_ptr(),
+                                  N, C, K, H, W, code, _stream(g))
+        _raise(rc, "conv3x3_bwd_data")
     return dx
 
 

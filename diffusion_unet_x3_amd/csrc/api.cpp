@@ -96,9 +96,13 @@ int check_prologue(const Prologue& pr, int dtype) {
   return CONV3X3_OK;
 }
 
+// ws_call: the *_ws entry points -- the caller passes a workspace (possibly
+// NULL when conv3x3_workspace_size says 0), so a bf16 plan may split its
+// reduction.
 int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, float* z, int N,
              int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
-             Prologue pr = Prologue()) {
+             Prologue pr = Prologue(), bool ws_call = false, void* ws = nullptr,
+             size_t ws_bytes = 0) {
   if (!parts_present(x, C) || !w || !y) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -112,7 +116,14 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
   if (pr.on() && (y == pr.scale || y == pr.shift)) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kFwd, kdt(dtype), N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  Problem pb{kFwd, kdt(dtype), N, C, K, H, W, x.c0};
+  pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z;
+  if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
+    return CONV3X3_ERR_WORKSPACE;
+  if (pl.workspace_bytes > 0 &&
+      (is_part(x, ws) || ws == w || ws == (const void*)bias || ws == (void*)y))
+    return CONV3X3_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   a.act = act;
@@ -136,7 +147,7 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
                      buffer_sized((long)K * C * 9);
     Split<const uint16_t> xs{(const uint16_t*)x.p0, (const uint16_t*)x.p1, x.c0};
     ok = launch_fwd_bf16(pl, vec, xs, (const uint16_t*)w, bias, one(y, K), N, C, K, H, W, a,
-                         dtype == CONV3X3_BF16_IO, s);
+                         dtype == CONV3X3_BF16_IO, (float*)ws, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
@@ -144,7 +155,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
 
 int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx, int N, int C,
                   int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
-                  Prologue pr = Prologue(), const void* px = nullptr) {
+                  Prologue pr = Prologue(), const void* px = nullptr, bool ws_call = false,
+                  void* ws = nullptr, size_t ws_bytes = 0) {
   if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
   if (pr.on() && !px) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
@@ -165,7 +177,13 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   // du's epilogue reads x through a 32-bit buffer view, like the stores
   if (pr.on() && 4L * N * C * H * W >= 2147483648L) return CONV3X3_ERR_UNSUPPORTED;
   Plan pl;
-  if (!plan(Problem{kBwdData, kdt(dtype), N, C, K, H, W, dx.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  Problem pb{kBwdData, kdt(dtype), N, C, K, H, W, dx.c0};
+  pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE;
+  if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
+    return CONV3X3_ERR_WORKSPACE;
+  if (pl.workspace_bytes > 0 && (ws == g || ws == w || is_part(dx, ws)))
+    return CONV3X3_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ActArgs a;
   if (act != CONV3X3_ACT_NONE) {
@@ -188,7 +206,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
                      aligned16(g) && aligned16(w) && buffer_sized((long)N * K * hw) &&
                      buffer_sized((long)K * C * 9);
     ok = launch_fwd_bf16(pl, vec, one((const uint16_t*)g, K), (const uint16_t*)w, nullptr, dx, N,
-                         K, C, H, W, a, dtype == CONV3X3_BF16_IO, s);
+                         K, C, H, W, a, dtype == CONV3X3_BF16_IO, (float*)ws, s);
   }
   if (!ok) return CONV3X3_ERR_BAD_SHAPE;
   return launch_status();
@@ -417,6 +435,30 @@ int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* sh
   if (!scale || !shift) return CONV3X3_ERR_NULL_POINTER;
   return bwd_weight_impl(one(x, C), g, nullptr, dw, db, workspace, workspace_bytes, N, C, K, H,
                          W, dtype, CONV3X3_ACT_NONE, stream, Prologue{scale, shift});
+}
+
+size_t conv3x3_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype) {
+  if (pass < CONV3X3_PASS_FWD || pass > CONV3X3_PASS_BWD_WEIGHT) return (size_t)-1;
+  if (check_dims(N, C, K, H, W) || check_dtype(dtype)) return (size_t)-1;
+  Problem pb{pass, kdt(dtype), N, C, K, H, W};
+  pb.allow_split = true;
+  Plan pl;
+  if (!plan(pb, &pl)) return (size_t)-1;
+  return pl.workspace_bytes;
+}
+
+int conv3x3_fwd_ws(const void* x, const void* w, const float* bias, float* y, void* workspace,
+                   size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                   conv3x3_stream_t stream) {
+  return fwd_impl(one(x, C), w, bias, y, nullptr, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
+                  Prologue(), true, workspace, workspace_bytes);
+}
+
+int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace,
+                        size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                        conv3x3_stream_t stream) {
+  return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
+                       Prologue(), nullptr, true, workspace, workspace_bytes);
 }
 
 }  // extern "C"

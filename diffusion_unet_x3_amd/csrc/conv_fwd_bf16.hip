@@ -99,7 +99,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
     float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
-    uint32_t dst1_bytes, int act, float* __restrict__ zout, int outb) {
+    uint32_t dst1_bytes, int act, float* __restrict__ zout, int outb, int per_split,
+    float* __restrict__ part) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -138,9 +139,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const int ocs = oseg ? Cout - cout0 : cout0;
   const int co0 = (oseg ? cout0 : 0) + col0;
   const int co_n = min(BCO, ocs - col0);
-  // Reduction fills: nq0 over src's channels, then src1's.
+  // Reduction fills: nq0 over src's channels, then src1's.  A split
+  // reduction (part != null) gives slice blockIdx.z the fills fbase ..
+  // fbase + nchunks - 1; `chunk` below counts this workgroup's fills.
   const int nq0 = (cin0 + CB - 1) / CB;
-  const int nchunks = nq0 + (Cin - cin0 + CB - 1) / CB;
+  const int nfills = nq0 + (Cin - cin0 + CB - 1) / CB;
+  const int fbase = part ? (int)blockIdx.z * per_split : 0;
+  const int nchunks = part ? min(per_split, nfills - fbase) : nfills;
   // staging thread index (-1: this thread stages nothing)
   const int sp = WSPEC ? (wave >= NC ? tid - 64 * NC : -1) : tid;
 
@@ -265,8 +270,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // (fills are whole here, so fill f of src1 starts at weight channel
   // 16 (nq0 + f); items outside the image keep kOutside through the select)
-  auto load_tiles = [&](auto set_c, int chunk) {
+  auto load_tiles = [&](auto set_c, int lchunk) {
     constexpr int S = decltype(set_c)::value;
+    const int chunk = fbase + lchunk;  // fill index over the whole reduction
     const uint32_t f = (uint32_t)chunk;
     const bool s1 = chunk >= nq0;
     const __amdgpu_buffer_rsrc_t sv = s1 ? sv1 : sv0;
@@ -356,8 +362,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // Scalar path (ragged shapes): 16-bit loads straight into LDS buffer buf,
   // by the staging threads.
-  auto fill_scalar = [&](int chunk, int buf) {
+  auto fill_scalar = [&](int lchunk, int buf) {
     if (sp < 0) return;
+    const int chunk = fbase + lchunk;  // fill index over the whole reduction
     const bool s1 = chunk >= nq0;
     const int cl0 = (chunk - (s1 ? nq0 : 0)) * CB;  // first channel within its tensor
     const int cs = s1 ? Cin - cin0 : cin0;            // channels of that tensor
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // ---- prologue: fill 0 in buffer 0, the next NSET fills in registers ----
   if constexpr (MODE == kFwd) {
     for (int i = tid; i < BCO; i += NT)
-      bias_s[i] = (bias != nullptr && i < co_n) ? bias[co0 + i] : 0.f;
+      bias_s[i] = (bias != nullptr && i < co_n && fbase == 0) ? bias[co0 + i] : 0.f;
   }
   if constexpr (VEC) {
     load_tiles(Set0{}, 0);
@@ -591,10 +598,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // included), also written to zout (float32) when it is given.
   // (zout, forward only, has the shape of dst; the output is then one tensor.)
   // outb: dst (and dst1) hold bfloat16, rounded to nearest even.
+  // A split reduction writes this slice's partial sums (bias in slice 0),
+  // float32, to its slot of the workspace (one tensor of dst's shape per
+  // slice); the reduce kernel adds the slices and applies the rest.
   const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
-  const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
-  float* const od = oseg ? dst1 : dst;
-  const uint32_t od_bytes = oseg ? dst1_bytes : dst_bytes;
+  const bool plain = part != nullptr || MODE != kFwd || (act == kActNone && zout == nullptr);
+  const uint32_t slot_bytes = (uint32_t)N * (uint32_t)Cout * (uint32_t)HW * 4u;
+  float* const od = part ? part + (size_t)blockIdx.z * ((size_t)slot_bytes / 4) : oseg ? dst1 : dst;
+  const uint32_t od_bytes = part ? slot_bytes : oseg ? dst1_bytes : dst_bytes;
+  if (part) outb = 0;
   if (od_bytes != 0 && co_n == BCO) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the channel
@@ -695,12 +707,58 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   }
 }
 
+// Sum of the S partial-output slots of a split reduction, in slice order,
+// then the activation and the store (float32, or bfloat16 when outb; z, the
+// sum before the activation, to zout when given).  Four elements per thread.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int S, long slot,
+                                                           float* __restrict__ dst, int outb,
+                                                           int act, float* __restrict__ zout) {
+  const long e0 = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= slot) return;
+  if (e0 + 4 <= slot && slot % 4 == 0) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(part + e0);
+    for (int s = 1; s < S; ++s) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(part + (long)s * slot + e0);
+      v.x += q.x;
+      v.y += q.y;
+      v.z += q.z;
+      v.w += q.w;
+    }
+    if (zout) *reinterpret_cast<f32x4*>(zout + e0) = v;
+    v.x = act_value(act, v.x);
+    v.y = act_value(act, v.y);
+    v.z = act_value(act, v.z);
+    v.w = act_value(act, v.w);
+    if (outb) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(dst) + e0);
+      d[0] = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+      d[1] = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+    } else {
+      *reinterpret_cast<f32x4*>(dst + e0) = v;
+    }
+    return;
+  }
+  for (long e = e0; e < e0 + 4 && e < slot; ++e) {
+    float v = part[e];
+    for (int s = 1; s < S; ++s) v += part[(long)s * slot + e];
+    if (zout) zout[e] = v;
+    v = act_value(act, v);
+    if (outb)
+      reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)bf16_rne(v);
+    else
+      dst[e] = v;
+  }
+}
+
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
 static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                             const uint16_t* wt, const float* bias, Split<float> dst, int N,
                             int Cin, int Cout, int H, int W, const ActArgs& a, bool out_bf16,
-                            hipStream_t stream) {
-  dim3 grid(pl.grid_x, pl.grid_y, 1), block(64 * NW, 1, 1);
+                            float* ws, hipStream_t stream) {
+  // split reduction: partial sums into ws, then split_reduce_kernel
+  float* const part = pl.split > 1 ? ws : nullptr;
+  dim3 grid(pl.grid_x, pl.grid_y, part ? pl.split : 1), block(64 * NW, 1, 1);
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets), and a float32 z beside bfloat16 outputs twice that; otherwise
   // the plain-store path runs.
@@ -715,18 +773,26 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                        Cout, H, W, pl.tiles_w, pl.tiles_h, (uint32_t)(N * src.c0 * hw * 2),
                        (uint32_t)(N * (Cin - src.c0) * hw * 2),
                        (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout,
-                       out_bf16 ? 1 : 0);
+                       out_bf16 ? 1 : 0, pl.chunks_per_split, part);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false>), grid, block,
                        0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N,
                        Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1, a.act,
-                       a.zout, out_bf16 ? 1 : 0);
+                       a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part);
+  if (part) {
+    const long slot = (long)N * Cout * hw;
+    dim3 rg((unsigned)((slot + 1023) / 1024)), rb(256);
+    hipLaunchKernelGGL(split_reduce_kernel, rg, rb, 0, stream, part, pl.split, slot, dst.p0,
+                       out_bf16 ? 1 : 0, a.act, a.zout);
+  }
 }
 
 bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
                      const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
-                     const ActArgs& a, bool out_bf16, hipStream_t stream) {
+                     const ActArgs& a, bool out_bf16, float* ws, hipStream_t stream) {
   if (pl.chunk != 16) return false;
+  // a split reduction needs its workspace and one output tensor
+  if (pl.split > 1 && (ws == nullptr || dst.c0 != Cout)) return false;
   // The bfloat16 backward-data pass has no fused activation and neither
   // pass has the input prologue (the caller rejects them).
   if ((pl.pass != kFwd && a.zsrc != nullptr) || a.pscale != nullptr) return false;
@@ -735,12 +801,12 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \
     if (pl.pass == kFwd)                                                                        \
       launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, bias, dst, N,    \
-                                                             Cin, Cout, H, W, a, out_bf16,      \
+                                                             Cin, Cout, H, W, a, out_bf16, ws,  \
                                                              stream);                           \
     else                                                                                        \
       launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, nullptr, dst, \
                                                                  N, Cin, Cout, H, W, a,          \
-                                                                 out_bf16, stream);              \
+                                                                 out_bf16, ws, stream);          \
     return true;                                                                                \
   }
   CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)

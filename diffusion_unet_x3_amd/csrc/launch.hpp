@@ -29,10 +29,12 @@ bool launch_fwd_f32(const Plan& pl, bool vec, Split<const float> src, const floa
 
 // Same, bfloat16 inputs (raw 16-bit patterns); outputs float32, or bfloat16
 // (round to nearest even) when out_bf16 (dst then points to 16-bit values;
-// a.zout stays float32).
+// a.zout stays float32).  pl.split > 1: the reduction is split over
+// pl.split workgroups per tile, their partial sums kept in ws (pl.split
+// float32 copies of the output) and added by a second kernel.
 bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
                      const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
-                     const ActArgs& a, bool out_bf16, hipStream_t stream);
+                     const ActArgs& a, bool out_bf16, float* ws, hipStream_t stream);
 
 // Backward-weight (+ optional db), float32; ws holds the per-slice partials
 // when pl.split > 1.  g is multiplied by act'(a.zsrc) as it is staged.

@@ -81,6 +81,10 @@ constexpr int kWgradTargetWGs = 256;
 
 }  // namespace
 
+long fwd_slot_elems(const Problem& p) {
+  return (long)p.N * (p.pass == kFwd ? p.K : p.C) * p.H * p.W;
+}
+
 size_t wgrad_workspace_bytes(const Plan& pl, int C, int K) {
   if (pl.split <= 1) return 0;
   return (size_t)pl.split * ((size_t)K * C * 9 + (size_t)K) * sizeof(float);
@@ -139,6 +143,27 @@ bool plan(const Problem& p, Plan* out) {
       pick = i;
       if (wgs[i] >= kMinWGs && eff[i] >= 0.8 * best_eff) break;
     }
+    // bf16 with a workspace: when the eight-wave 256 x 128 tile leaves the
+    // device short of workgroups (small images) and the reduction is long
+    // (>= 64 fills of 16 channels), keep that tile and split the reduction
+    // instead of falling back to the smaller tiles, which re-stage all the
+    // weights for every pixel tile.  The split stays within one round of
+    // workgroups and keeps at least 8 fills per slice (measured: shorter
+    // reductions and a second round of workgroups both lose to the small
+    // tiles).
+    int split = 1;
+    const int cin = p.pass == kFwd ? p.C : p.K;
+    const int fills = ceil_div(cin, 16);
+    if (p.allow_split && p.dtype == kBF16 && cout > 64 && wgs[0] > 0 && wgs[0] < kMinWGs &&
+        fills >= 64 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
+      int s = kMinWGs / wgs[0];
+      if (s > fills / 8) s = fills / 8;
+      if (s > 8) s = 8;
+      if (s >= 2) {
+        pick = 0;
+        split = s;
+      }
+    }
     const Block blk = pick >= 0 ? blks[pick] : Block{};
     if (pick < 0) return false;
     pl.tw = blk.tw;
@@ -153,12 +178,18 @@ bool plan(const Problem& p, Plan* out) {
     pl.grid_x = pl.tiles_n * pl.tiles_h * pl.tiles_w;
     pl.grid_y = channel_tiles(cout, cout0, pl.tile_co);
     pl.grid_z = 1;
+    pl.split = 1;
+    if (split > 1) {
+      pl.chunks_per_split = ceil_div(fills, split);
+      pl.split = ceil_div(fills, pl.chunks_per_split);  // no empty slices
+      pl.grid_z = pl.split;
+      pl.workspace_bytes = (size_t)pl.split * (size_t)fwd_slot_elems(p) * sizeof(float);
+    }
     pl.threads = 64 * cands[pick].nw;
     pl.lds_bytes = p.dtype == kF32
         ? fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
         : fwd_bf16_lds_bytes(pl.imgs, pl.th, pl.tw, pl.tile_co);
     if (p.pass == kFwd) pl.lds_bytes += 4 * pl.tile_co;  // the tile's biases
-    pl.split = 1;
   } else if (p.pass == kBwdWeight) {
     // float32: 64-pixel chunks (32 MFMA steps); bfloat16: 128-pixel chunks
     // (8 MFMA steps of 16 pixels), 64 for images at most 8 wide.

@@ -34,7 +34,7 @@ struct Plan {
   int tiles_w = 0, tiles_h = 0, tiles_n = 0;
   int grid_x = 0, grid_y = 0, grid_z = 0;
   int lds_bytes = 0;
-  int split = 1;          // bwd_weight: reduction slices
+  int split = 1;          // reduction slices (bwd_weight; bf16 fwd / bwd_data with a workspace)
   int chunks_per_split = 0;
   int nchunks = 0;
   int vec = 0;            // 1: 128-bit global paths allowed (decided at launch; 0 here)
@@ -50,11 +50,18 @@ struct Problem {
   int pass, dtype;
   int N, C, K, H, W;
   int C0 = -1;
+  // bf16 forward / backward-data: the caller provides a workspace, so the
+  // reduction may be split over several workgroups per output tile (partial
+  // sums in the workspace, then a fixed-order reduce)
+  bool allow_split = false;
 };
 
 bool plan(const Problem& p, Plan* out);
 
 // Minimum workspace bytes for a bwd_weight plan.
 size_t wgrad_workspace_bytes(const Plan& pl, int C, int K);
+
+// Elements of one partial-output slot of a split fwd / bwd_data plan.
+long fwd_slot_elems(const Problem& p);
 
 }  // namespace conv3x3

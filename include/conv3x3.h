@@ -261,6 +261,30 @@ int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* sh
                               size_t workspace_bytes, int N, int C, int K, int H, int W,
                               int dtype, conv3x3_stream_t stream);
 
+/*
+ * Forward / backward-data with a caller-provided workspace.  Same operation,
+ * arguments and results as conv3x3_fwd / conv3x3_bwd_data, plus
+ *   workspace : device buffer of at least conv3x3_workspace_size(pass, ...)
+ *               bytes (may be NULL when that size is 0); its contents are
+ *               scratch, it must not overlap an input or output.
+ * With a workspace, a bfloat16 problem whose output tiles are too few to
+ * fill the device (small images: the 8 x 8 and 16 x 16 layers) splits its
+ * channel reduction over up to 8 workgroups per tile; each writes its
+ * partial sums (float32, one output-sized slot per slice) to the workspace
+ * and a second kernel on the same stream adds the slots in slice order --
+ * no atomics, bitwise-reproducible results (which can differ in the last
+ * bits from the unsplit entry points: another summation order).
+ */
+size_t conv3x3_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype);
+
+int conv3x3_fwd_ws(const void* x, const void* w, const float* bias, float* y, void* workspace,
+                   size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                   conv3x3_stream_t stream);
+
+int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace,
+                        size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                        conv3x3_stream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* conv3x3_status_string(int status);
 

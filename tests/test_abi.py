@@ -228,3 +228,29 @@ def test_prologue_argument_checks():
     # backward-data's x must stay below 2 GiB (a 32-bit buffer view)
     big = (64, 1024, 4, 128, 128)
     assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, Y, *big, 0, None) == unsup
+
+
+def test_split_workspace_checks():
+    """A bf16 small-image problem needs a workspace on the *_ws entry
+    points; without one, or with too little, nothing is launched."""
+    d = (32, 1024, 512, 8, 8)
+    bf16 = lib3.CONV3X3_BF16
+    need = lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, bf16)
+    assert need == 8 * (32 * 512 * 64 * 4)  # eight float32 output-sized slots
+    # backward-data's reduction (K = 512) is too short to split
+    assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, *d, bf16) == 0
+    assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 512, 1024, 8, 8, bf16) == need
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, lib3.CONV3X3_F32) == 0
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 64, 512, 512, 16, 16, bf16) == 0
+    assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_WEIGHT, *d, bf16) == \
+        lib3.conv3x3_bwd_weight_workspace_size(*d, bf16)
+    ws_err, alias = S["ERR_WORKSPACE"], S["ERR_ALIAS"]
+    assert L.conv3x3_fwd_ws(X, Wt, B, Y, None, 0, *d, bf16, None) == ws_err
+    assert L.conv3x3_fwd_ws(X, Wt, B, Y, WS, need - 1, *d, bf16, None) == ws_err
+    db = (32, 512, 1024, 8, 8)
+    assert L.conv3x3_bwd_data_ws(G, Wt, Y, None, 0, *db, bf16, None) == ws_err
+    assert L.conv3x3_fwd_ws(X, Wt, B, Y, X, need, *d, bf16, None) == alias
+    assert L.conv3x3_bwd_data_ws(G, Wt, Y, Y, need, *db, bf16, None) == alias
+    # the plain entry points never need one
+    assert L.conv3x3_fwd_ws(X, Wt, B, Y, None, 0, *d, 7, None) == S["ERR_BAD_DTYPE"]
+    assert lib3.conv3x3_plan(lib3.PASS_FWD, *d, bf16)["split"] == 1

@@ -1,0 +1,75 @@
+"""GPU parity of the split-reduction bf16 forward / backward-data (the *_ws
+entry points on small images) against the oracle, through the C ABI.
+
+Each slice of the channel reduction writes float32 partial sums to the
+workspace and a second kernel adds them in slice order.  Same bar as the
+plain bf16 passes (the 1e-4 trip-wire; exact on integer inputs, where the
+split and unsplit entry points must also agree bit for bit)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity_util import TRIPWIRE, rel_err
+
+pytestmark = pytest.mark.gpu
+
+# (N, C, K, H, W): a few output tiles and a long reduction (>= 64 fills of
+# 16 channels): forward splits with C >= 1024, backward-data with K >= 1024;
+# 1032 channels leave a partly filled last fill and a short last slice
+SHAPES = [(4, 1024, 512, 8, 8), (8, 1024, 256, 8, 8), (4, 2048, 128, 8, 8),
+          (4, 1024, 128, 16, 16), (4, 256, 1024, 8, 8), (4, 1032, 256, 8, 8)]
+
+
+def _run(inp, split, out_dtype=None):
+    import diffusion_unet_x3_amd as lib3
+    dev = torch.device("cuda", 0)
+    x, w, g, b = (inp[k].to(dev) for k in ("x", "w", "g", "b"))
+    y = lib3.conv3x3_fwd(x, w, b, out_dtype=out_dtype, split=split)
+    dx = lib3.conv3x3_bwd_data(g, w, out_dtype=out_dtype, split=split)
+    torch.cuda.synchronize()
+    return y.float().cpu().double().numpy(), dx.float().cpu().double().numpy()
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_split_reduction_full_compare(shape, integer):
+    import diffusion_unet_x3_amd as lib3
+    N, C, K, H, W = shape
+    assert any(lib3.conv3x3_workspace_size(p, *shape, lib3.CONV3X3_BF16) > 0
+               for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA)), "shape no longer takes a split plan"
+    layer = wl.small_layer(*shape, dtype="bf16", seed=71)
+    print(f"[parity] split {shape} integer={integer}", flush=True)
+    inp = wl.make_inputs(layer, integer_exact=integer)
+    y, dx = _run(inp, split=True)
+    y_ref = oracle.conv3x3_fwd(inp["x"], inp["w"], inp["b"])
+    dx_ref = oracle.conv3x3_bwd_data(inp["g"], inp["w"])
+    if integer:
+        assert np.array_equal(y, y_ref) and np.array_equal(dx, dx_ref)
+        y0, dx0 = _run(inp, split=False)
+        assert np.array_equal(y, y0) and np.array_equal(dx, dx0)
+    else:
+        errs = {"y": rel_err(y, y_ref), "dx": rel_err(dx, dx_ref)}
+        print(errs)
+        for k, e in errs.items():
+            assert e <= TRIPWIRE["bf16"], (shape, k, e)
+
+
+def test_split_reduction_bf16_outputs():
+    """The reduce kernel writes bfloat16 outputs too (integer inputs:
+    exactly the oracle rounded to bfloat16)."""
+    layer = wl.small_layer(4, 1024, 256, 8, 8, dtype="bf16", seed=73)
+    inp = wl.make_inputs(layer, integer_exact=True)
+    y, dx = _run(inp, split=True, out_dtype=torch.bfloat16)
+    assert np.array_equal(y, oracle.round_to_bf16(oracle.conv3x3_fwd(inp["x"], inp["w"],
+                                                                     inp["b"])))
+    assert np.array_equal(dx, oracle.round_to_bf16(oracle.conv3x3_bwd_data(inp["g"], inp["w"])))
+
+
+def test_split_reduction_is_reproducible():
+    layer = wl.small_layer(4, 1024, 128, 8, 8, dtype="bf16", seed=79)
+    inp = wl.make_inputs(layer)
+    a = _run(inp, split=True)
+    b = _run(inp, split=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
