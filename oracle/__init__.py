@@ -357,3 +357,43 @@ def round_to_bf16(a):
     q = x / ulp
     out[nz] = np.round(q) * ulp      # np.round: half to even
     return out
+
+
+# ---------------------------------------------------------------------------
+# Nearest-neighbour 2x upsampling before the convolution (a UNet up-path
+# block).  The project-guide page on StyleGAN2's custom kernels describes
+# upsampling as zero insertion followed by an FIR filter; nearest-neighbour
+# upsampling is that with the 2x2 box filter.  The oracle writes it as its
+# plain definition -- u[n, c, i, j] = x[n, c, i // 2, j // 2] -- and the
+# adjoint for backward-data: each x pixel receives the sum of the gradients
+# at its four copies.
+
+
+def upsample2(x):
+    """u = nearest 2x upsampling of x [N, C, H, W] -> [N, C, 2H, 2W]."""
+    x = _f64(x)
+    return np.repeat(np.repeat(x, 2, axis=2), 2, axis=3)
+
+
+def downsum2(du):
+    """Adjoint of upsample2: [N, C, 2H, 2W] -> [N, C, H, W], the sum of each
+    2x2 block."""
+    du = _f64(du)
+    N, C, H2, W2 = du.shape
+    return du.reshape(N, C, H2 // 2, 2, W2 // 2, 2).sum(axis=(3, 5))
+
+
+def conv3x3_fwd_up2(x, w, b=None):
+    """y = conv3x3_fwd(upsample2(x), w, b), y at twice x's resolution."""
+    return conv3x3_fwd(upsample2(x), w, b)
+
+
+def conv3x3_bwd_data_up2(g, w):
+    """dx of <conv3x3(upsample2(x); w), g>: the 2x2 block sums of the
+    input gradient at the upsampled resolution."""
+    return downsum2(conv3x3_bwd_data(g, w))
+
+
+def conv3x3_bwd_weight_up2(x, g, want_db=True):
+    """(dw, db) of <conv3x3(upsample2(x); w) + b, g>."""
+    return conv3x3_bwd_weight(upsample2(x), g, want_db)
