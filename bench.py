@@ -241,6 +241,38 @@ class LayerRun:
         return (("fwd", self.fwd), ("bwd_data", self.bwd_data), ("bwd_weight", self.bwd_weight))
 
 
+class Up2Run:
+    """The three passes of an upsample-then-convolve layer (conv3x3_*_up2):
+    x at H x W, y and g at 2H x 2W."""
+
+    def __init__(self, layer):
+        import torch
+        import diffusion_unet_x3_amd as lib3
+        import workloads as wl
+        from dataclasses import replace
+        self.lib3 = lib3
+        dev = torch.device("cuda", 0)
+        N, C, K, H, W = layer.shape
+        big = wl.make_inputs(replace(layer, H=2 * H, W=2 * W))
+        self.x = big["x"][:, :, :H, :W].contiguous().to(dev)
+        self.w, self.b, self.g = (big[k].to(dev) for k in ("w", "b", "g"))
+        self.y = torch.empty((N, K, 2 * H, 2 * W), device=dev)
+        self.dx = torch.empty((N, C, H, W), device=dev)
+        self.dw = torch.empty((K, C, 3, 3), device=dev)
+        self.db = torch.empty((K,), device=dev)
+        self.ws_d = torch.empty(max(lib3.conv3x3_up2_workspace_size(1, N, C, K, H, W), 1),
+                                dtype=torch.uint8, device=dev)
+        self.ws_w = torch.empty(max(lib3.conv3x3_up2_workspace_size(2, N, C, K, H, W), 1),
+                                dtype=torch.uint8, device=dev)
+
+    def passes(self):
+        return [("fwd", lambda: self.lib3.conv3x3_fwd_up2(self.x, self.w, self.b, out=self.y)),
+                ("bwd_data", lambda: self.lib3.conv3x3_bwd_data_up2(self.g, self.w, out=self.dx,
+                                                                    workspace=self.ws_d)),
+                ("bwd_weight", lambda: self.lib3.conv3x3_bwd_weight_up2(
+                    self.x, self.g, dw=self.dw, db=self.db, workspace=self.ws_w))]
+
+
 def time_layer(run, steps, warmup):
     """Per-pass average ms (events between the passes) and per-step ms."""
     import torch
@@ -295,11 +327,27 @@ def cpu_baseline(layer, budget_s=15.0):
 
 
 def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False,
-          out_bf16=False, split=True):
+          out_bf16=False, split=True, up2=False):
     import re
     import torch
     import workloads as wl
     rows = []
+    if up2:
+        for layer in wl.UPSAMPLE:
+            run = Up2Run(layer)
+            ms, per = time_layer(run, steps, warmup)
+            N, C, K, H, W = layer.shape
+            f = flops_per_pass(N, C, K, 2 * H, 2 * W)
+            row = {"layer": layer.name, "dtype": "f32", "up2": True, "shape": [N, C, K, H, W],
+                   "ms_step": ms}
+            for p, t in per.items():
+                row[p] = {"ms": t, "tflops": f / (t * 1e-3) / 1e12}
+            rows.append(row)
+            print(f"{layer.name:44s} " + " ".join(f"{p}={row[p]['ms'] * 1e3:8.1f}us" for p in per),
+                  file=sys.stderr, flush=True)
+        with open(out_path, "w") as fh:
+            json.dump(rows, fh, indent=1)
+        return
     for cfg, layers in sorted(wl.CONFIGS.items()):
         for layer in layers:
             if match and not re.search(match, layer.name):
@@ -355,6 +403,9 @@ def main():
     ap.add_argument("--no-split", action="store_true",
                     help="with --sweep: call the entry points without a workspace (no split "
                          "reduction on small bf16 images)")
+    ap.add_argument("--up2", action="store_true",
+                    help="with --sweep: time the UNet's upsample convolutions through the "
+                         "*_up2 entry points (nearest 2x upsampling in the loader)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -414,7 +465,7 @@ def main():
         torch.cuda.empty_cache()
     if args.sweep:
         sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat,
-              args.gnsilu, args.out_bf16, not args.no_split)
+              args.gnsilu, args.out_bf16, not args.no_split, args.up2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -26,6 +26,11 @@ device memory and the current stream.  The functions carry the C names:
     conv3x3_bwd_data_gnsilu(g, w, x, scale, shift, out=None)  -> du
     conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True, dw=None,
                               db=None, workspace=None)        -> (dw, db)
+    conv3x3_fwd_up2(x, w, bias=None, out=None)                -> y [N, K, 2H, 2W]
+    conv3x3_bwd_data_up2(g, w, out=None, workspace=None)      -> dx [N, C, H, W]
+    conv3x3_bwd_weight_up2(x, g, want_db=True, dw=None, db=None,
+                           workspace=None)                    -> (dw, db)
+    conv3x3_up2_workspace_size(pass_, N, C, K, H, W, dtype)   -> bytes
     conv3x3_status_string(code)                               -> str
     conv3x3_plan(pass_, N, C, K, H, W, dtype)                 -> dict
     conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype)        -> dict
@@ -73,7 +78,8 @@ EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_siz
             "conv3x3_fwd_cat", "conv3x3_bwd_data_cat", "conv3x3_bwd_weight_cat_workspace_size",
             "conv3x3_bwd_weight_cat", "conv3x3_plan_cat", "conv3x3_fwd_gnsilu",
             "conv3x3_bwd_data_gnsilu", "conv3x3_bwd_weight_gnsilu", "conv3x3_workspace_size",
-            "conv3x3_fwd_ws", "conv3x3_bwd_data_ws"]
+            "conv3x3_fwd_ws", "conv3x3_bwd_data_ws", "conv3x3_up2_workspace_size",
+            "conv3x3_fwd_up2", "conv3x3_bwd_data_up2", "conv3x3_bwd_weight_up2"]
 
 
 class Plan(ctypes.Structure):
@@ -127,6 +133,15 @@ def _load():
     lib.conv3x3_fwd_ws.restype = i
     lib.conv3x3_bwd_data_ws.argtypes = [vp, vp, fp, vp, ctypes.c_size_t, i, i, i, i, i, i, vp]
     lib.conv3x3_bwd_data_ws.restype = i
+    lib.conv3x3_up2_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.conv3x3_up2_workspace_size.restype = ctypes.c_size_t
+    lib.conv3x3_fwd_up2.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_fwd_up2.restype = i
+    lib.conv3x3_bwd_data_up2.argtypes = [vp, vp, fp, vp, ctypes.c_size_t, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data_up2.restype = i
+    lib.conv3x3_bwd_weight_up2.argtypes = [vp, vp, fp, fp, vp, ctypes.c_size_t,
+                                           i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight_up2.restype = i
     lib.conv3x3_fwd_gnsilu.argtypes = [vp, fp, fp, vp, fp, fp, i, i, i, i, i, i, vp]
     lib.conv3x3_fwd_gnsilu.restype = i
     lib.conv3x3_bwd_data_gnsilu.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, vp]
@@ -544,4 +559,73 @@ def conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True, dw=None, db=None
                                        None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
                                        N, C, K, H, W, code, _stream(x))
     _raise(rc, "conv3x3_bwd_weight_gnsilu")
+    return dw, db
+
+
+def conv3x3_up2_workspace_size(pass_, N, C, K, H, W, dtype=CONV3X3_F32):
+    n = lib.conv3x3_up2_workspace_size(pass_, N, C, K, H, W, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid problem for conv3x3_up2_workspace_size")
+    return n
+
+
+def conv3x3_fwd_up2(x, w, bias=None, out=None):
+    """y = conv3x3(nearest_upsample_2x(x); w) + bias, y [N, K, 2H, 2W]."""
+    _check(x, "x", 4)
+    _check(w, "w", 4)
+    N, C, H, W = x.shape
+    K = w.shape[0]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != x.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with x's dtype")
+    if bias is not None:
+        _check(bias, "bias", 1)
+        if bias.dtype != torch.float32 or bias.shape[0] != K:
+            raise ValueError("bias must be float32 [K]")
+    y = _f32_out(out, (N, K, 2 * H, 2 * W), x, "out")
+    rc = lib.conv3x3_fwd_up2(x.data_ptr(), w.data_ptr(),
+                             None if bias is None else bias.data_ptr(), y.data_ptr(),
+                             N, C, K, H, W, _dtype_code(x), _stream(x))
+    _raise(rc, "conv3x3_fwd_up2")
+    return y
+
+
+def conv3x3_bwd_data_up2(g, w, out=None, workspace=None):
+    """dx [N, C, H, W] of <conv3x3(nearest_upsample_2x(x); w), g>, g being
+    [N, K, 2H, 2W]."""
+    _check(g, "g", 4)
+    _check(w, "w", 4)
+    N, K, H2, W2 = g.shape
+    if H2 % 2 or W2 % 2:
+        raise ValueError("g must have even height and width")
+    H, W = H2 // 2, W2 // 2
+    C = w.shape[1]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with g's dtype")
+    code = _dtype_code(g)
+    dx = _f32_out(out, (N, C, H, W), g, "out")
+    ws, nb = _workspace(conv3x3_up2_workspace_size(PASS_BWD_DATA, N, C, K, H, W, code),
+                        workspace, g)
+    rc = lib.conv3x3_bwd_data_up2(g.data_ptr(), w.data_ptr(), dx.data_ptr(), ws, nb,
+                                  N, C, K, H, W, code, _stream(g))
+    _raise(rc, "conv3x3_bwd_data_up2")
+    return dx
+
+
+def conv3x3_bwd_weight_up2(x, g, want_db=True, dw=None, db=None, workspace=None):
+    """(dw, db) of <conv3x3(nearest_upsample_2x(x); w) + b, g>."""
+    _check(x, "x", 4)
+    _check(g, "g", 4)
+    N, C, H, W = x.shape
+    K = g.shape[1]
+    if tuple(g.shape) != (N, K, 2 * H, 2 * W) or g.dtype != x.dtype:
+        raise ValueError("g must be [N, K, 2H, 2W] with x's dtype")
+    code = _dtype_code(x)
+    dw = _f32_out(dw, (K, C, 3, 3), x, "dw")
+    db = _f32_out(db, (K,), x, "db") if want_db else None
+    ws, nb = _workspace(conv3x3_up2_workspace_size(PASS_BWD_WEIGHT, N, C, K, H, W, code),
+                        workspace, x)
+    rc = lib.conv3x3_bwd_weight_up2(x.data_ptr(), g.data_ptr(), dw.data_ptr(),
+                                    None if db is None else db.data_ptr(), ws, nb,
+                                    N, C, K, H, W, code, _stream(x))
+    _raise(rc, "conv3x3_bwd_weight_up2")
     return dw, db

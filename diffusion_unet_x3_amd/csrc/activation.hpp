@@ -38,6 +38,9 @@ struct ActArgs {
   const float* pscale = nullptr;
   const float* pshift = nullptr;
   const float* px = nullptr;
+  // the source (forward) or x (backward-weight) is upsampled 2x by nearest
+  // neighbour as it is staged; the problem's H, W are the upsampled sizes
+  bool up2 = false;
 };
 
 // sigmoid(z) = 1 / (1 + e^-z) with the hardware exponential and reciprocal

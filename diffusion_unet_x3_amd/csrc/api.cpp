@@ -102,7 +102,8 @@ int check_prologue(const Prologue& pr, int dtype) {
 int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, float* z, int N,
              int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
              Prologue pr = Prologue(), bool ws_call = false, void* ws = nullptr,
-             size_t ws_bytes = 0) {
+             size_t ws_bytes = 0, bool up2 = false) {
+  // up2: H, W are the output's (upsampled) sizes; x is H/2 x W/2
   if (!parts_present(x, C) || !w || !y) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -130,6 +131,7 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   a.zout = z;
   a.pscale = pr.scale;
   a.pshift = pr.shift;
+  a.up2 = up2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -214,7 +216,8 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
 
 int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* dw, float* db,
                     void* workspace, size_t workspace_bytes, int N, int C, int K, int H, int W,
-                    int dtype, int act, conv3x3_stream_t stream, Prologue pr = Prologue()) {
+                    int dtype, int act, conv3x3_stream_t stream, Prologue pr = Prologue(),
+                    bool up2 = false) {
   if (!parts_present(x, C) || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -249,6 +252,7 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   }
   a.pscale = pr.scale;
   a.pshift = pr.shift;
+  a.up2 = up2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -459,6 +463,72 @@ int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace
                         conv3x3_stream_t stream) {
   return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
                        Prologue(), nullptr, true, workspace, workspace_bytes);
+}
+
+// ---- nearest 2x upsampling before the convolution (H, W: x's sizes) ----
+
+namespace {
+
+// The upsampled grid must satisfy the plain limits; float32 only.
+int check_up2(int N, int C, int K, int H, int W, int dtype) {
+  if (H < 1 || W < 1 || H > (1 << 29) || W > (1 << 29)) return CONV3X3_ERR_BAD_SHAPE;
+  int rc = check_dims(N, C, K, 2 * H, 2 * W);
+  if (rc) return rc;
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  return dtype == CONV3X3_F32 ? CONV3X3_OK : CONV3X3_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+size_t conv3x3_up2_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype) {
+  if (pass < CONV3X3_PASS_FWD || pass > CONV3X3_PASS_BWD_WEIGHT) return (size_t)-1;
+  if (check_up2(N, C, K, H, W, dtype)) return (size_t)-1;
+  if (pass == CONV3X3_PASS_FWD) return 0;
+  if (pass == CONV3X3_PASS_BWD_DATA) return (size_t)N * C * 4 * H * W * sizeof(float);
+  Plan pl;
+  if (!plan(Problem{kBwdWeight, kdt(dtype), N, C, K, 2 * H, 2 * W}, &pl)) return (size_t)-1;
+  return pl.workspace_bytes;
+}
+
+int conv3x3_fwd_up2(const void* x, const void* w, const float* bias, float* y, int N, int C,
+                    int K, int H, int W, int dtype, conv3x3_stream_t stream) {
+  if (!x || !w || !y) return CONV3X3_ERR_NULL_POINTER;
+  const int rc = check_up2(N, C, K, H, W, dtype);
+  if (rc) return rc;
+  return fwd_impl(one(x, C), w, bias, y, nullptr, N, C, K, 2 * H, 2 * W, dtype, CONV3X3_ACT_NONE,
+                  stream, Prologue(), false, nullptr, 0, true);
+}
+
+int conv3x3_bwd_data_up2(const void* g, const void* w, float* dx, void* workspace,
+                         size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                         conv3x3_stream_t stream) {
+  if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
+  int rc = check_up2(N, C, K, H, W, dtype);
+  if (rc) return rc;
+  const size_t need = (size_t)N * C * 4 * H * W * sizeof(float);
+  if (!workspace || workspace_bytes < need) return CONV3X3_ERR_WORKSPACE;
+  if (workspace == g || workspace == w || workspace == (void*)dx || (const void*)dx == g ||
+      (const void*)dx == w)
+    return CONV3X3_ERR_ALIAS;
+  // the gradient at the upsampled resolution into the workspace, then the
+  // 2x2 block sums into dx
+  float* big = (float*)workspace;
+  rc = bwd_data_impl(g, nullptr, w, one(big, C), N, C, K, 2 * H, 2 * W, dtype, CONV3X3_ACT_NONE,
+                     stream);
+  if (rc) return rc;
+  launch_downsum2(big, dx, (long)N * C, H, W, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, void* workspace,
+                           size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                           conv3x3_stream_t stream) {
+  if (!x || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
+  const int rc = check_up2(N, C, K, H, W, dtype);
+  if (rc) return rc;
+  return bwd_weight_impl(one(x, C), g, nullptr, dw, db, workspace, workspace_bytes, N, C, K,
+                         2 * H, 2 * W, dtype, CONV3X3_ACT_NONE, stream, Prologue(), true);
 }
 
 }  // extern "C"

@@ -71,6 +71,15 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t v, uint32_
 __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t v, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(v, (int)off, 0, 0);
 }
+// Two consecutive floats at byte offset off (two 32-bit loads, which the
+// compiler merges into one 64-bit load).  Returned as scalars: a bit-cast of
+// an ext-vector lane (v.y) reads lane x with this compiler.
+__device__ __forceinline__ void buffer_load_2f(__amdgpu_buffer_rsrc_t v, uint32_t off, float& a,
+                                               float& b) {
+  a = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(v, (int)off, 0, 0));
+  b = __builtin_bit_cast(float,
+                         (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(v, (int)(off + 4u), 0, 0));
+}
 __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t v, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(v, (int)off, 0, 0);
 }

@@ -43,8 +43,12 @@ namespace conv3x3 {
 // step -- ceil(9 PC / 2) steps instead of the 36 of an 8-channel fill.  The
 // tile's weights w[co0 .. co0 + BCO - 1, 0..PC-1, 0..8] are one contiguous
 // run of BCO * 9 PC floats, staged with 16-byte loads.
+// UP2 (forward): the source is upsampled 2x by nearest neighbour as it is
+// staged -- H and W are the upsampled (output) sizes, the source tensor is
+// H/2 x W/2, and staged pixel (h, w) reads source pixel (h/2, w/2); a vector
+// item of four output columns is two source floats, each used twice.
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
-          bool PRO = false, int PC = 0>
+          bool PRO = false, int PC = 0, bool UP2 = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -65,6 +69,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int WS = fwd_f32_wstride(BCO);
   constexpr int HR = TH + 2;  // staged rows per image (with halo)
   static_assert(PC == 0 || (MODE == kFwd && VEC && PC < CB), "packed taps: forward only");
+  static_assert(!UP2 || (MODE == kFwd && PC == 0 && !PRO), "upsampling: plain forward only");
+  // source rows and columns (the upsampled grid's halves with UP2)
+  const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;
   constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * 9;
 
   __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
@@ -185,6 +192,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w < W;
+        if constexpr (UP2) {
+          const uint32_t so =
+              ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + h / 2) * Ws + w / 2) : kOutside;
+          float xa, xb;
+          buffer_load_2f(sview, so, xa, xb);
+          xv[k] = f32x4{xa, xa, xb, xb};
+          continue;
+        }
         const uint32_t off =
             ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xv[k] = __builtin_bit_cast(f32x4, buffer_load16(sview, off));
@@ -210,7 +225,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
         const uint32_t off =
-            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
+            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + (UP2 ? h / 2 : h)) * Ws +
+                                 (UP2 ? w / 2 : w))
+               : kOutside;
         xf[k] = __builtin_bit_cast(float, buffer_load4(sview, off));
         if (zs) zf[k] = __builtin_bit_cast(float, buffer_load4(zview, off));
         if constexpr (pro) {
@@ -339,7 +356,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
           if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W) {
-            const long e = ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
+            const long e = UP2 ? ((long)n * f.cs + f.cl0 + ch) * Hs * Ws + (long)(h / 2) * Ws + w / 2
+                               : ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
             v = sp[e];
             if (zs) v *= act_slope(act, zsrc[e]);
             if constexpr (pro) {
@@ -580,30 +598,38 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   const long ob0 = (long)N * dst.c0 * hw4, ob1 = (long)N * (Cout - dst.c0) * hw4;
   const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
-  const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * hw4) : 0u;
-  const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * hw4) : 0u;
+  const long shw4 = a.up2 ? hw4 / 4 : hw4;  // source plane bytes
+  const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * shw4) : 0u;
+  const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * shw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_, PC_)                                                                \
-  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_>), grid,\
+#define CONV3X3_L(VEC_, PRO_, PC_, UP_)                                                           \
+  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_>), \
+                     grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,       \
                      a.zout, a.zsrc, a.pscale, a.pshift, a.px)
   // packed taps: the forward of a 3- or 4-channel single tensor
-  const int pc = (MODE == kFwd && vec && !a.pscale && src.c0 == Cin) ? Cin : 0;
-  if (a.pscale) {
+  const int pc = (MODE == kFwd && vec && !a.pscale && !a.up2 && src.c0 == Cin) ? Cin : 0;
+  constexpr bool kF = MODE == kFwd;
+  if (a.up2) {
     if (vec)
-      CONV3X3_L(true, true, 0);
+      CONV3X3_L(true, false, 0, kF);
     else
-      CONV3X3_L(false, true, 0);
+      CONV3X3_L(false, false, 0, kF);
+  } else if (a.pscale) {
+    if (vec)
+      CONV3X3_L(true, true, 0, false);
+    else
+      CONV3X3_L(false, true, 0, false);
   } else if (pc == 3) {
-    CONV3X3_L(true, false, MODE == kFwd ? 3 : 0);
+    CONV3X3_L(true, false, kF ? 3 : 0, false);
   } else if (pc == 4) {
-    CONV3X3_L(true, false, MODE == kFwd ? 4 : 0);
+    CONV3X3_L(true, false, kF ? 4 : 0, false);
   } else {
     if (vec)
-      CONV3X3_L(true, false, 0);
+      CONV3X3_L(true, false, 0, false);
     else
-      CONV3X3_L(false, false, 0);
+      CONV3X3_L(false, false, 0, false);
   }
 #undef CONV3X3_L
 }

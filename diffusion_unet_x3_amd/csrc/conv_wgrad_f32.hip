@@ -30,7 +30,9 @@
 
 namespace conv3x3 {
 
-template <int TW, int TH, int IMGS, bool VEC>
+// UP2: x is upsampled 2x by nearest neighbour as it is staged (H, W are the
+// upsampled sizes, g's; x is H/2 x W/2).
+template <int TW, int TH, int IMGS, bool VEC, bool UP2 = false>
 __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ x1, int cx0,
     const float* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const float* const xp = xseg ? x1 : x;
   const int k0 = (tile / tiles_c) * 64;
   const long HW = (long)H * W;
+  const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;  // x's rows and columns
   const bool do_db = out_db != nullptr && tile % tiles_c == 0;
 
   // g tile: 64 k x P pixels.  x tile: 64 c x IMGS x HR rows x (TW + 2) columns.
@@ -149,9 +152,19 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && cl < cn && h >= 0 &&
                         h < H && w < W;
-        xv[k] = __builtin_bit_cast(
-            f32x4, buffer_load16(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
-                                            : kOutside));
+        if constexpr (UP2) {
+          // four upsampled columns: two x values, each used twice
+          float xa, xb;
+          buffer_load_2f(xview,
+                         ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * Hs + h / 2) * Ws + w / 2)
+                            : kOutside,
+                         xa, xb);
+          xv[k] = f32x4{xa, xa, xb, xb};
+        } else {
+          xv[k] = __builtin_bit_cast(
+              f32x4, buffer_load16(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
+                                              : kOutside));
+        }
         if (pro) {
           const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
           psv[k] = __builtin_bit_cast(float, buffer_load4(psview, po));
@@ -173,7 +186,9 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && cl < cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
         xf[k] = __builtin_bit_cast(
-            float, buffer_load4(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w)
+            float, buffer_load4(xview, ok ? 4u * (uint32_t)(((n * cs + cl0 + cl) * Hs +
+                                                             (UP2 ? h / 2 : h)) * Ws +
+                                                            (UP2 ? w / 2 : w))
                                           : kOutside));
         if (pro) {
           const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
@@ -278,7 +293,8 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
           const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
           if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W) {
-            v = xp[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
+            v = UP2 ? xp[((long)n * cs + cl0 + cl) * Hs * Ws + (long)(h / 2) * Ws + w / 2]
+                    : xp[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
             if (pro) {
               const long pc = (long)n * C + c0 + cl;
               v = act_value(kActSilu, v * pscale[pc] + pshift[pc]);
@@ -498,17 +514,27 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, Split<const float> x, co
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
   const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
   const long hw4 = (long)H * W * 4;
-  if (vec)
-    hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x.p0, x.p1,
-                       x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h, pl.nchunks,
-                       pl.chunks_per_split, slice_stride, pl.split, tiles_c, (K + 63) / 64,
-                       (uint32_t)(N * x.c0 * hw4), (uint32_t)(N * (C - x.c0) * hw4),
-                       (uint32_t)(N * K * hw4), a.act, a.zsrc, a.pscale, a.pshift);
-  else
-    hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x.p0,
-                       x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
-                       pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
-                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc, a.pscale, a.pshift);
+  const long xhw4 = a.up2 ? hw4 / 4 : hw4;  // x's plane bytes
+  const uint32_t xb0 = vec ? (uint32_t)(N * x.c0 * xhw4) : 0u;
+  const uint32_t xb1 = vec ? (uint32_t)(N * (C - x.c0) * xhw4) : 0u;
+  const uint32_t gb = vec ? (uint32_t)(N * K * hw4) : 0u;
+#define CONV3X3_L(VEC_, UP_)                                                                      \
+  hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, VEC_, UP_>), grid, block, 0, stream, x.p0,    \
+                     x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,            \
+                     pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,             \
+                     (K + 63) / 64, xb0, xb1, gb, a.act, a.zsrc, a.pscale, a.pshift)
+  if (a.up2) {
+    if (vec)
+      CONV3X3_L(true, true);
+    else
+      CONV3X3_L(false, true);
+  } else {
+    if (vec)
+      CONV3X3_L(true, false);
+    else
+      CONV3X3_L(false, false);
+  }
+#undef CONV3X3_L
 }
 
 bool launch_wgrad_f32(const Plan& pl, bool vec, Split<const float> x, const float* g, float* dw,

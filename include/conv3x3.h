@@ -285,6 +285,39 @@ int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace
                         size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
                         conv3x3_stream_t stream);
 
+/*
+ * Nearest-neighbour 2x upsampling fused into the convolution's loader (a
+ * UNet up block).  The project-guide page on StyleGAN2's custom kernels
+ * describes upsampling as zero insertion followed by an FIR filter;
+ * nearest-neighbour is its 2x2 box-filter case.  Here H, W are x's sizes:
+ *   x  : [N][C][H][W]                the small input
+ *   y  : [N][K][2H][2W]              y = conv(upsample2(x); w) + bias,
+ *                                    upsample2(x)[n,c,i,j] = x[n,c,i/2,j/2]
+ *   g  : [N][K][2H][2W]              the gradient at y
+ *   dx : [N][C][H][W]                the sum of the input gradient over each
+ *                                    2x2 block of the upsampled grid
+ * The forward and backward-weight loaders read x at (h/2, w/2) as they stage
+ * the upsampled tile (it never exists in memory).  Backward-data runs the
+ * plain backward-data at the upsampled resolution into the workspace and
+ * adds its 2x2 blocks in a second kernel (fixed order).  Workspace bytes:
+ * conv3x3_up2_workspace_size(pass, ...) -- 0 for the forward, 16 N C H W
+ * for backward-data, the split-K size of the 2H x 2W problem for
+ * backward-weight.  float32 only (CONV3X3_ERR_UNSUPPORTED for bfloat16);
+ * the limits apply to the 2H x 2W problem.
+ */
+size_t conv3x3_up2_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype);
+
+int conv3x3_fwd_up2(const void* x, const void* w, const float* bias, float* y, int N, int C,
+                    int K, int H, int W, int dtype, conv3x3_stream_t stream);
+
+int conv3x3_bwd_data_up2(const void* g, const void* w, float* dx, void* workspace,
+                         size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                         conv3x3_stream_t stream);
+
+int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, void* workspace,
+                           size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                           conv3x3_stream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* conv3x3_status_string(int status);
 

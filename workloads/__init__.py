@@ -149,3 +149,10 @@ def make_prologue(layer):
 # benchmark configurations, a case for the few-channel paths).
 IMAGE_STEM = {dt: Layer(f"image_stem_32x3to128_64x64_{dt}", 32, 3, 128, 64, 64, dt, 6, 0)
               for dt in ("f32", "bf16")}
+
+
+# The convolutions of the UNet's upsample blocks (nearest 2x, then a 3x3
+# convolution keeping the channels): 8->16, 16->32 and 32->64 at N = 32.
+# H, W are the input's (pre-upsampling) sizes; g is drawn at 2H x 2W.
+UPSAMPLE = [Layer(f"upsample_{c}ch_{r}to{2 * r}_f32", 32, c, c, r, r, "f32", 7, i)
+            for i, (c, r) in enumerate(((512, 8), (384, 16), (256, 32)))]
