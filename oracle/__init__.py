@@ -397,3 +397,38 @@ def conv3x3_bwd_data_up2(g, w):
 def conv3x3_bwd_weight_up2(x, g, want_db=True):
     """(dw, db) of <conv3x3(upsample2(x); w) + b, g>."""
     return conv3x3_bwd_weight(upsample2(x), g, want_db)
+
+
+# ---------------------------------------------------------------------------
+# Stride-2 3x3 convolution, zero padding 1 (a UNet's downsample block):
+# y[n,k,h,w] = b[k] + sum x[n,c,2h+r-1,2w+s-1] w[k,c,r,s], output H/2 x W/2
+# for even H, W -- PyTorch's Conv2d(kernel 3, stride 2, padding 1), read as
+# the downsampling of the StyleGAN2 page's resampling section (filter, then
+# keep every second sample).  Written as its plain definition: the stride-1
+# convolution at every second output pixel.  The adjoints insert zeros: the
+# gradient g of the small output placed at the even pixels of the full grid.
+
+
+def zero_insert2(g):
+    """[N, K, H, W] -> [N, K, 2H, 2W] with g at the even pixels, zeros
+    elsewhere."""
+    g = _f64(g)
+    N, K, H, W = g.shape
+    z = np.zeros((N, K, 2 * H, 2 * W))
+    z[:, :, ::2, ::2] = g
+    return z
+
+
+def conv3x3_fwd_s2(x, w, b=None):
+    """y = stride-2 convolution of x (H, W even): [N, K, H/2, W/2]."""
+    return conv3x3_fwd(x, w, b)[:, :, ::2, ::2]
+
+
+def conv3x3_bwd_data_s2(g, w):
+    """dx [N, C, 2h, 2w] of <conv_s2(x; w), g> for g [N, K, h, w]."""
+    return conv3x3_bwd_data(zero_insert2(g), w)
+
+
+def conv3x3_bwd_weight_s2(x, g, want_db=True):
+    """(dw, db) of <conv_s2(x; w) + b, g>."""
+    return conv3x3_bwd_weight(x, zero_insert2(g), want_db)
