@@ -273,6 +273,34 @@ class Up2Run:
                     self.x, self.g, dw=self.dw, db=self.db, workspace=self.ws_w))]
 
 
+class S2Run:
+    """The three passes of a stride-2 layer (conv3x3_*_s2): x at H x W, y and
+    g at H/2 x W/2."""
+
+    def __init__(self, layer):
+        import torch
+        import diffusion_unet_x3_amd as lib3
+        import workloads as wl
+        self.lib3 = lib3
+        dev = torch.device("cuda", 0)
+        N, C, K, H, W = layer.shape
+        inp = wl.make_inputs(layer)
+        self.x, self.w, self.b = (inp[k].to(dev) for k in ("x", "w", "b"))
+        self.g = inp["g"][:, :, :H // 2, :W // 2].contiguous().to(dev)
+        self.y = torch.empty((N, K, H // 2, W // 2), device=dev)
+        self.dx = torch.empty((N, C, H, W), device=dev)
+        self.dw = torch.empty((K, C, 3, 3), device=dev)
+        self.db = torch.empty((K,), device=dev)
+        self.ws = torch.empty(max(lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W), 1),
+                              dtype=torch.uint8, device=dev)
+
+    def passes(self):
+        return [("fwd", lambda: self.lib3.conv3x3_fwd_s2(self.x, self.w, self.b, out=self.y)),
+                ("bwd_data", lambda: self.lib3.conv3x3_bwd_data_s2(self.g, self.w, out=self.dx)),
+                ("bwd_weight", lambda: self.lib3.conv3x3_bwd_weight_s2(
+                    self.x, self.g, dw=self.dw, db=self.db, workspace=self.ws))]
+
+
 def time_layer(run, steps, warmup):
     """Per-pass average ms (events between the passes) and per-step ms."""
     import torch
@@ -327,19 +355,21 @@ def cpu_baseline(layer, budget_s=15.0):
 
 
 def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False,
-          out_bf16=False, split=True, up2=False):
+          out_bf16=False, split=True, up2=False, s2=False):
     import re
     import torch
     import workloads as wl
     rows = []
-    if up2:
-        for layer in wl.UPSAMPLE:
-            run = Up2Run(layer)
+    if up2 or s2:
+        for layer in (wl.UPSAMPLE if up2 else wl.DOWNSAMPLE):
+            run = Up2Run(layer) if up2 else S2Run(layer)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
-            f = flops_per_pass(N, C, K, 2 * H, 2 * W)
-            row = {"layer": layer.name, "dtype": "f32", "up2": True, "shape": [N, C, K, H, W],
-                   "ms_step": ms}
+            # useful FLOPs: at the output's resolution
+            f = flops_per_pass(N, C, K, 2 * H, 2 * W) if up2 else \
+                flops_per_pass(N, C, K, H // 2, W // 2)
+            row = {"layer": layer.name, "dtype": "f32", "up2": up2, "s2": s2,
+                   "shape": [N, C, K, H, W], "ms_step": ms}
             for p, t in per.items():
                 row[p] = {"ms": t, "tflops": f / (t * 1e-3) / 1e12}
             rows.append(row)
@@ -406,6 +436,9 @@ def main():
     ap.add_argument("--up2", action="store_true",
                     help="with --sweep: time the UNet's upsample convolutions through the "
                          "*_up2 entry points (nearest 2x upsampling in the loader)")
+    ap.add_argument("--s2", action="store_true",
+                    help="with --sweep: time the UNet's stride-2 downsample convolutions "
+                         "(*_s2 entry points)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -465,7 +498,7 @@ def main():
         torch.cuda.empty_cache()
     if args.sweep:
         sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat,
-              args.gnsilu, args.out_bf16, not args.no_split, args.up2)
+              args.gnsilu, args.out_bf16, not args.no_split, args.up2, args.s2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer)
     print(json.dumps(result), flush=True)

@@ -31,6 +31,10 @@ device memory and the current stream.  The functions carry the C names:
     conv3x3_bwd_weight_up2(x, g, want_db=True, dw=None, db=None,
                            workspace=None)                    -> (dw, db)
     conv3x3_up2_workspace_size(pass_, N, C, K, H, W, dtype)   -> bytes
+    conv3x3_fwd_s2(x, w, bias=None, out=None)                 -> y [N, K, H/2, W/2]
+    conv3x3_bwd_data_s2(g, w, out=None)                       -> dx [N, C, 2h, 2w]
+    conv3x3_bwd_weight_s2(x, g, want_db=True, dw=None, db=None,
+                          workspace=None)                     -> (dw, db)
     conv3x3_status_string(code)                               -> str
     conv3x3_plan(pass_, N, C, K, H, W, dtype)                 -> dict
     conv3x3_plan_cat(pass_, N, C0, C1, K, H, W, dtype)        -> dict
@@ -79,7 +83,8 @@ EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_siz
             "conv3x3_bwd_weight_cat", "conv3x3_plan_cat", "conv3x3_fwd_gnsilu",
             "conv3x3_bwd_data_gnsilu", "conv3x3_bwd_weight_gnsilu", "conv3x3_workspace_size",
             "conv3x3_fwd_ws", "conv3x3_bwd_data_ws", "conv3x3_up2_workspace_size",
-            "conv3x3_fwd_up2", "conv3x3_bwd_data_up2", "conv3x3_bwd_weight_up2"]
+            "conv3x3_fwd_up2", "conv3x3_bwd_data_up2", "conv3x3_bwd_weight_up2",
+            "conv3x3_fwd_s2", "conv3x3_bwd_data_s2", "conv3x3_bwd_weight_s2"]
 
 
 class Plan(ctypes.Structure):
@@ -142,6 +147,12 @@ def _load():
     lib.conv3x3_bwd_weight_up2.argtypes = [vp, vp, fp, fp, vp, ctypes.c_size_t,
                                            i, i, i, i, i, i, vp]
     lib.conv3x3_bwd_weight_up2.restype = i
+    lib.conv3x3_fwd_s2.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_fwd_s2.restype = i
+    lib.conv3x3_bwd_data_s2.argtypes = [vp, vp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_data_s2.restype = i
+    lib.conv3x3_bwd_weight_s2.argtypes = [vp, vp, fp, fp, vp, ctypes.c_size_t, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight_s2.restype = i
     lib.conv3x3_fwd_gnsilu.argtypes = [vp, fp, fp, vp, fp, fp, i, i, i, i, i, i, vp]
     lib.conv3x3_fwd_gnsilu.restype = i
     lib.conv3x3_bwd_data_gnsilu.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, vp]
@@ -628,4 +639,59 @@ def conv3x3_bwd_weight_up2(x, g, want_db=True, dw=None, db=None, workspace=None)
                                     None if db is None else db.data_ptr(), ws, nb,
                                     N, C, K, H, W, code, _stream(x))
     _raise(rc, "conv3x3_bwd_weight_up2")
+    return dw, db
+
+
+def conv3x3_fwd_s2(x, w, bias=None, out=None):
+    """Stride-2 3x3 convolution (padding 1) of x [N, C, H, W] (H, W even):
+    y [N, K, H/2, W/2]."""
+    _check(x, "x", 4)
+    _check(w, "w", 4)
+    N, C, H, W = x.shape
+    K = w.shape[0]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != x.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with x's dtype")
+    if bias is not None:
+        _check(bias, "bias", 1)
+        if bias.dtype != torch.float32 or bias.shape[0] != K:
+            raise ValueError("bias must be float32 [K]")
+    y = _f32_out(out, (N, K, H // 2, W // 2), x, "out")
+    rc = lib.conv3x3_fwd_s2(x.data_ptr(), w.data_ptr(),
+                            None if bias is None else bias.data_ptr(), y.data_ptr(),
+                            N, C, K, H, W, _dtype_code(x), _stream(x))
+    _raise(rc, "conv3x3_fwd_s2")
+    return y
+
+
+def conv3x3_bwd_data_s2(g, w, out=None):
+    """dx [N, C, 2h, 2w] of <conv_s2(x; w), g> for g [N, K, h, w]."""
+    _check(g, "g", 4)
+    _check(w, "w", 4)
+    N, K, h, wd = g.shape
+    C = w.shape[1]
+    if tuple(w.shape) != (K, C, 3, 3) or w.dtype != g.dtype:
+        raise ValueError("w must be [K, C, 3, 3] with g's dtype")
+    dx = _f32_out(out, (N, C, 2 * h, 2 * wd), g, "out")
+    rc = lib.conv3x3_bwd_data_s2(g.data_ptr(), w.data_ptr(), dx.data_ptr(),
+                                 N, C, K, 2 * h, 2 * wd, _dtype_code(g), _stream(g))
+    _raise(rc, "conv3x3_bwd_data_s2")
+    return dx
+
+
+def conv3x3_bwd_weight_s2(x, g, want_db=True, dw=None, db=None, workspace=None):
+    """(dw, db) of <conv_s2(x; w) + b, g>, x [N, C, H, W], g [N, K, H/2, W/2]."""
+    _check(x, "x", 4)
+    _check(g, "g", 4)
+    N, C, H, W = x.shape
+    K = g.shape[1]
+    if tuple(g.shape) != (N, K, H // 2, W // 2) or g.dtype != x.dtype:
+        raise ValueError("g must be [N, K, H/2, W/2] with x's dtype")
+    code = _dtype_code(x)
+    dw = _f32_out(dw, (K, C, 3, 3), x, "dw")
+    db = _f32_out(db, (K,), x, "db") if want_db else None
+    ws, nb = _workspace(conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code), workspace, x)
+    rc = lib.conv3x3_bwd_weight_s2(x.data_ptr(), g.data_ptr(), dw.data_ptr(),
+                                   None if db is None else db.data_ptr(), ws, nb,
+                                   N, C, K, H, W, code, _stream(x))
+    _raise(rc, "conv3x3_bwd_weight_s2")
     return dw, db

@@ -102,8 +102,9 @@ int check_prologue(const Prologue& pr, int dtype) {
 int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, float* z, int N,
              int C, int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
              Prologue pr = Prologue(), bool ws_call = false, void* ws = nullptr,
-             size_t ws_bytes = 0, bool up2 = false) {
-  // up2: H, W are the output's (upsampled) sizes; x is H/2 x W/2
+             size_t ws_bytes = 0, int geom = 0) {
+  // geom 1 (upsampling): H, W are the output's (upsampled) sizes, x is
+  // H/2 x W/2; geom 2 (stride 2): H, W are x's, y is H/2 x W/2
   if (!parts_present(x, C) || !w || !y) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -131,7 +132,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   a.zout = z;
   a.pscale = pr.scale;
   a.pshift = pr.shift;
-  a.up2 = up2;
+  a.up2 = geom == 1;
+  a.sub2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -158,7 +160,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
 int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx, int N, int C,
                   int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
                   Prologue pr = Prologue(), const void* px = nullptr, bool ws_call = false,
-                  void* ws = nullptr, size_t ws_bytes = 0) {
+                  void* ws = nullptr, size_t ws_bytes = 0, bool zi2 = false) {
+  // zi2 (stride 2): H, W are dx's; g is H/2 x W/2
   if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
   if (pr.on() && !px) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
@@ -195,6 +198,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   a.pscale = pr.scale;
   a.pshift = pr.shift;
   a.px = (const float*)px;
+  a.zi2 = zi2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -217,7 +221,9 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
 int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* dw, float* db,
                     void* workspace, size_t workspace_bytes, int N, int C, int K, int H, int W,
                     int dtype, int act, conv3x3_stream_t stream, Prologue pr = Prologue(),
-                    bool up2 = false) {
+                    int geom = 0) {
+  // geom 1: x is upsampled (H, W are g's, x is H/2 x W/2); geom 2: stride 2
+  // (H, W are x's, g is H/2 x W/2)
   if (!parts_present(x, C) || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
@@ -252,7 +258,8 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   }
   a.pscale = pr.scale;
   a.pshift = pr.shift;
-  a.up2 = up2;
+  a.up2 = geom == 1;
+  a.zi2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -497,7 +504,7 @@ int conv3x3_fwd_up2(const void* x, const void* w, const float* bias, float* y, i
   const int rc = check_up2(N, C, K, H, W, dtype);
   if (rc) return rc;
   return fwd_impl(one(x, C), w, bias, y, nullptr, N, C, K, 2 * H, 2 * W, dtype, CONV3X3_ACT_NONE,
-                  stream, Prologue(), false, nullptr, 0, true);
+                  stream, Prologue(), false, nullptr, 0, 1);
 }
 
 int conv3x3_bwd_data_up2(const void* g, const void* w, float* dx, void* workspace,
@@ -528,7 +535,50 @@ int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, v
   const int rc = check_up2(N, C, K, H, W, dtype);
   if (rc) return rc;
   return bwd_weight_impl(one(x, C), g, nullptr, dw, db, workspace, workspace_bytes, N, C, K,
-                         2 * H, 2 * W, dtype, CONV3X3_ACT_NONE, stream, Prologue(), true);
+                         2 * H, 2 * W, dtype, CONV3X3_ACT_NONE, stream, Prologue(), 1);
+}
+
+// ---- stride-2 convolution (H, W: x's sizes, both even) ----
+
+namespace {
+
+int check_s2(int N, int C, int K, int H, int W, int dtype) {
+  int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  if (H % 2 || W % 2) return CONV3X3_ERR_BAD_SHAPE;
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  return dtype == CONV3X3_F32 ? CONV3X3_OK : CONV3X3_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int conv3x3_fwd_s2(const void* x, const void* w, const float* bias, float* y, int N, int C,
+                   int K, int H, int W, int dtype, conv3x3_stream_t stream) {
+  if (!x || !w || !y) return CONV3X3_ERR_NULL_POINTER;
+  const int rc = check_s2(N, C, K, H, W, dtype);
+  if (rc) return rc;
+  return fwd_impl(one(x, C), w, bias, y, nullptr, N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
+                  Prologue(), false, nullptr, 0, 2);
+}
+
+int conv3x3_bwd_data_s2(const void* g, const void* w, float* dx, int N, int C, int K, int H,
+                        int W, int dtype, conv3x3_stream_t stream) {
+  if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
+  const int rc = check_s2(N, C, K, H, W, dtype);
+  if (rc) return rc;
+  return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
+                       Prologue(), nullptr, false, nullptr, 0, true);
+}
+
+int conv3x3_bwd_weight_s2(const void* x, const void* g, float* dw, float* db, void* workspace,
+                          size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                          conv3x3_stream_t stream) {
+  if (!x || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
+  const int rc = check_s2(N, C, K, H, W, dtype);
+  if (rc) return rc;
+  return bwd_weight_impl(one(x, C), g, nullptr, dw, db, workspace, workspace_bytes, N, C, K, H, W,
+                         dtype, CONV3X3_ACT_NONE, stream, Prologue(), 2);
 }
 
 }  // extern "C"

@@ -47,8 +47,12 @@ namespace conv3x3 {
 // staged -- H and W are the upsampled (output) sizes, the source tensor is
 // H/2 x W/2, and staged pixel (h, w) reads source pixel (h/2, w/2); a vector
 // item of four output columns is two source floats, each used twice.
+// ZI2 (backward-data of a stride-2 convolution): the source g is H/2 x W/2
+// and is staged zero-inserted -- g[h/2, w/2] at even (h, w), zero
+// elsewhere -- so that the stride-1 backward-data of the full grid is the
+// stride-2 one.
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
-          bool PRO = false, int PC = 0, bool UP2 = false>
+          bool PRO = false, int PC = 0, bool UP2 = false, bool ZI2 = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
     uint32_t dst1_bytes, int act, float* __restrict__ zout, const float* __restrict__ zsrc,
     const float* __restrict__ pscale, const float* __restrict__ pshift,
-    const float* __restrict__ px) {
+    const float* __restrict__ px, int sub2) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -70,8 +74,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int HR = TH + 2;  // staged rows per image (with halo)
   static_assert(PC == 0 || (MODE == kFwd && VEC && PC < CB), "packed taps: forward only");
   static_assert(!UP2 || (MODE == kFwd && PC == 0 && !PRO), "upsampling: plain forward only");
-  // source rows and columns (the upsampled grid's halves with UP2)
-  const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;
+  static_assert(!ZI2 || (MODE == kBwdData && !PRO), "zero insertion: plain backward-data only");
+  // source rows and columns (the full grid's halves with UP2 or ZI2)
+  const int Hs = (UP2 || ZI2) ? H / 2 : H, Ws = (UP2 || ZI2) ? W / 2 : W;
   constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * 9;
 
   __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
@@ -192,12 +197,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w < W;
-        if constexpr (UP2) {
+        if constexpr (UP2 || ZI2) {
+          // four full-grid columns from two source floats: each used twice
+          // (upsampling), or at the even columns of even rows (zero
+          // insertion; odd rows read nothing)
+          const bool okz = ok && (!ZI2 || (h & 1) == 0);
           const uint32_t so =
-              ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + h / 2) * Ws + w / 2) : kOutside;
+              okz ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + h / 2) * Ws + w / 2)
+                  : kOutside;
           float xa, xb;
           buffer_load_2f(sview, so, xa, xb);
-          xv[k] = f32x4{xa, xa, xb, xb};
+          xv[k] = ZI2 ? f32x4{xa, 0.f, xb, 0.f} : f32x4{xa, xa, xb, xb};
           continue;
         }
         const uint32_t off =
@@ -223,10 +233,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, h = o.h0 + rr - 1;
         const int w = o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
-                        h < H && w >= 0 && w < W;
+                        h < H && w >= 0 && w < W && (!ZI2 || ((h | w) & 1) == 0);
+        constexpr bool half = UP2 || ZI2;
         const uint32_t off =
-            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + (UP2 ? h / 2 : h)) * Ws +
-                                 (UP2 ? w / 2 : w))
+            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + (half ? h / 2 : h)) * Ws +
+                                 (half ? w / 2 : w))
                : kOutside;
         xf[k] = __builtin_bit_cast(float, buffer_load4(sview, off));
         if (zs) zf[k] = __builtin_bit_cast(float, buffer_load4(zview, off));
@@ -355,9 +366,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int ch = t / (HR * IMGS);
           const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           float v = 0.f;
-          if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W) {
-            const long e = UP2 ? ((long)n * f.cs + f.cl0 + ch) * Hs * Ws + (long)(h / 2) * Ws + w / 2
-                               : ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
+          if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W &&
+              (!ZI2 || ((h | w) & 1) == 0)) {
+            const long e = (UP2 || ZI2)
+                ? ((long)n * f.cs + f.cl0 + ch) * Hs * Ws + (long)(h / 2) * Ws + w / 2
+                : ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
             v = sp[e];
             if (zs) v *= act_slope(act, zsrc[e]);
             if constexpr (pro) {
@@ -521,6 +534,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     return;
   }
   const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
+  // sub2 (forward of a stride-2 convolution): only the even pixels of the
+  // full grid are outputs, stored at (h/2, w/2) of the H/2 x W/2 output
+  const int sh = sub2 ? 1 : 0;
+  const int Wo = W >> sh;
+  const long HWo = (long)(H >> sh) * Wo;
   if (od_bytes != 0 && co_n == BCO) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the
@@ -528,16 +546,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     // an offset past the view and the hardware drops their stores.
     const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
     const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : od_bytes);
-    const uint32_t plane = (uint32_t)HW * 4u;
+    const uint32_t plane = (uint32_t)HWo * 4u;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int p = wpx * (BM / WPX) + j * 32 + l32;
       const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
       const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      const bool keep = n < N && h < H && w < W && (sh == 0 || ((h | w) & 1) == 0);
       const uint32_t off =
-          (n < N && h < H && w < W)
-              ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w)) * 4u
-              : kOutside;
+          keep ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HWo +
+                  (uint32_t)((h >> sh) * Wo + (w >> sh))) * 4u
+               : kOutside;
       if (plain) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -563,8 +582,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
-    if (n >= N || h >= H || w >= W) continue;
-    float* out = od + (long)n * ocs * HW + (long)h * W + w;
+    if (n >= N || h >= H || w >= W || (sh && ((h | w) & 1))) continue;
+    float* out = od + (long)n * ocs * HWo + (long)(h >> sh) * Wo + (w >> sh);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -572,10 +591,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int co = cw + i * 32 + acc_row(v, hi);
         if (co < ocs) {
           if (plain) {
-            out[(long)co * HW] = acc[i][j][v];
+            out[(long)co * HWo] = acc[i][j][v];
           } else {
-            if (zout) zout[(out - od) + (long)co * HW] = acc[i][j][v];
-            out[(long)co * HW] = act_value(act, acc[i][j][v]);
+            if (zout) zout[(out - od) + (long)co * HWo] = acc[i][j][v];
+            out[(long)co * HWo] = act_value(act, acc[i][j][v]);
           }
         }
       }
@@ -595,41 +614,50 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets); otherwise both take the plain-store path.
   const long hw4 = (long)H * W * 4;
-  const long ob0 = (long)N * dst.c0 * hw4, ob1 = (long)N * (Cout - dst.c0) * hw4;
+  // output plane bytes (a stride-2 forward keeps a quarter of the grid)
+  const long ohw4 = a.sub2 ? (long)(H / 2) * (W / 2) * 4 : hw4;
+  const long ob0 = (long)N * dst.c0 * ohw4, ob1 = (long)N * (Cout - dst.c0) * ohw4;
   const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
-  const long shw4 = a.up2 ? hw4 / 4 : hw4;  // source plane bytes
+  const long shw4 = (a.up2 || a.zi2) ? hw4 / 4 : hw4;  // source plane bytes
   const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * shw4) : 0u;
   const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * shw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_, PC_, UP_)                                                           \
-  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_>), \
+#define CONV3X3_L(VEC_, PRO_, PC_, UP_, ZI_)                                                      \
+  hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_,   \
+                                     ZI_>),                                                       \
                      grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,       \
-                     a.zout, a.zsrc, a.pscale, a.pshift, a.px)
+                     a.zout, a.zsrc, a.pscale, a.pshift, a.px, a.sub2 ? 1 : 0)
   // packed taps: the forward of a 3- or 4-channel single tensor
-  const int pc = (MODE == kFwd && vec && !a.pscale && !a.up2 && src.c0 == Cin) ? Cin : 0;
+  const int pc =
+      (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.sub2 && src.c0 == Cin) ? Cin : 0;
   constexpr bool kF = MODE == kFwd;
   if (a.up2) {
     if (vec)
-      CONV3X3_L(true, false, 0, kF);
+      CONV3X3_L(true, false, 0, kF, false);
     else
-      CONV3X3_L(false, false, 0, kF);
+      CONV3X3_L(false, false, 0, kF, false);
+  } else if (a.zi2) {
+    if (vec)
+      CONV3X3_L(true, false, 0, false, !kF);
+    else
+      CONV3X3_L(false, false, 0, false, !kF);
   } else if (a.pscale) {
     if (vec)
-      CONV3X3_L(true, true, 0, false);
+      CONV3X3_L(true, true, 0, false, false);
     else
-      CONV3X3_L(false, true, 0, false);
+      CONV3X3_L(false, true, 0, false, false);
   } else if (pc == 3) {
-    CONV3X3_L(true, false, kF ? 3 : 0, false);
+    CONV3X3_L(true, false, kF ? 3 : 0, false, false);
   } else if (pc == 4) {
-    CONV3X3_L(true, false, kF ? 4 : 0, false);
+    CONV3X3_L(true, false, kF ? 4 : 0, false, false);
   } else {
     if (vec)
-      CONV3X3_L(true, false, 0, false);
+      CONV3X3_L(true, false, 0, false, false);
     else
-      CONV3X3_L(false, false, 0, false);
+      CONV3X3_L(false, false, 0, false, false);
   }
 #undef CONV3X3_L
 }

@@ -31,8 +31,9 @@
 namespace conv3x3 {
 
 // UP2: x is upsampled 2x by nearest neighbour as it is staged (H, W are the
-// upsampled sizes, g's; x is H/2 x W/2).
-template <int TW, int TH, int IMGS, bool VEC, bool UP2 = false>
+// upsampled sizes, g's; x is H/2 x W/2).  ZI2 (a stride-2 convolution): g
+// is H/2 x W/2 and is staged zero-inserted, g[h/2, w/2] at even (h, w).
+template <int TW, int TH, int IMGS, bool VEC, bool UP2 = false, bool ZI2 = false>
 __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ x1, int cx0,
     const float* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const int k0 = (tile / tiles_c) * 64;
   const long HW = (long)H * W;
   const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;  // x's rows and columns
+  const int Hg = ZI2 ? H / 2 : H, Wg = ZI2 ? W / 2 : W;  // g's rows and columns
   const bool do_db = out_db != nullptr && tile % tiles_c == 0;
 
   // g tile: 64 k x P pixels.  x tile: 64 c x IMGS x HR rows x (TW + 2) columns.
@@ -136,6 +138,17 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 4 * q;
         const bool ok = (GV_ITEMS % NT == 0 || it < GV_ITEMS) && n < N && kk < K && h < H && w < W;
+        if constexpr (ZI2) {
+          // four columns of an even row: g at the even ones; odd rows zero
+          float ga, gb;
+          buffer_load_2f(gview,
+                         ok && (h & 1) == 0
+                             ? 4u * (uint32_t)(((n * K + kk) * Hg + h / 2) * Wg + w / 2)
+                             : kOutside,
+                         ga, gb);
+          gv[k] = f32x4{ga, 0.f, gb, 0.f};
+          continue;
+        }
         const uint32_t off = ok ? 4u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside;
         gv[k] = __builtin_bit_cast(f32x4, buffer_load16(gview, off));
         if (zs) zv[k] = __builtin_bit_cast(f32x4, buffer_load16(zview, off));
@@ -275,7 +288,10 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         float v = 0.f;
         if (n < N && kk < K && h < H && w < W) {
           const long e = ((long)n * K + kk) * HW + (long)h * W + w;
-          v = g[e];
+          if constexpr (ZI2)
+            v = ((h | w) & 1) ? 0.f : g[((long)n * K + kk) * Hg * Wg + (long)(h / 2) * Wg + w / 2];
+          else
+            v = g[e];
           if (zs) v *= act_slope(act, zsrc[e]);
         }
         gs[kl * GS + it % P] = v;
@@ -517,22 +533,28 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, Split<const float> x, co
   const long xhw4 = a.up2 ? hw4 / 4 : hw4;  // x's plane bytes
   const uint32_t xb0 = vec ? (uint32_t)(N * x.c0 * xhw4) : 0u;
   const uint32_t xb1 = vec ? (uint32_t)(N * (C - x.c0) * xhw4) : 0u;
-  const uint32_t gb = vec ? (uint32_t)(N * K * hw4) : 0u;
-#define CONV3X3_L(VEC_, UP_)                                                                      \
-  hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, VEC_, UP_>), grid, block, 0, stream, x.p0,    \
+  const uint32_t gb = vec ? (uint32_t)(N * K * (a.zi2 ? hw4 / 4 : hw4)) : 0u;
+#define CONV3X3_L(VEC_, UP_, ZI_)                                                                 \
+  hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, VEC_, UP_, ZI_>), grid, block, 0, stream,     \
+                     x.p0,                                                                        \
                      x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,            \
                      pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,             \
                      (K + 63) / 64, xb0, xb1, gb, a.act, a.zsrc, a.pscale, a.pshift)
   if (a.up2) {
     if (vec)
-      CONV3X3_L(true, true);
+      CONV3X3_L(true, true, false);
     else
-      CONV3X3_L(false, true);
+      CONV3X3_L(false, true, false);
+  } else if (a.zi2) {
+    if (vec)
+      CONV3X3_L(true, false, true);
+    else
+      CONV3X3_L(false, false, true);
   } else {
     if (vec)
-      CONV3X3_L(true, false);
+      CONV3X3_L(true, false, false);
     else
-      CONV3X3_L(false, false);
+      CONV3X3_L(false, false, false);
   }
 #undef CONV3X3_L
 }

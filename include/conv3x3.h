@@ -318,6 +318,29 @@ int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, v
                            size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
                            conv3x3_stream_t stream);
 
+/*
+ * Stride-2 3x3 convolution, zero padding 1 (a UNet's downsample block; the
+ * StyleGAN2 page's downsampling keeps every second sample after filtering):
+ * y[n,k,h,w] = bias[k] + sum x[n,c,2h+r-1,2w+s-1] w[k,c,r,s].  H, W are x's
+ * sizes and must be even; y, g are [N][K][H/2][W/2]; dx is [N][C][H][W];
+ * backward-weight takes the workspace of conv3x3_bwd_weight_workspace_size
+ * (N, C, K, H, W, dtype).  The kernels are the stride-1 ones on the full
+ * grid: the forward stores only its even pixels, the backward passes read g
+ * zero-inserted into the full grid as they stage it -- three quarters of
+ * their MFMA work multiplies zeros or is discarded (a first version; the
+ * pixel-parity decomposition would remove it).  float32 only
+ * (CONV3X3_ERR_UNSUPPORTED for bfloat16).
+ */
+int conv3x3_fwd_s2(const void* x, const void* w, const float* bias, float* y, int N, int C,
+                   int K, int H, int W, int dtype, conv3x3_stream_t stream);
+
+int conv3x3_bwd_data_s2(const void* g, const void* w, float* dx, int N, int C, int K, int H,
+                        int W, int dtype, conv3x3_stream_t stream);
+
+int conv3x3_bwd_weight_s2(const void* x, const void* g, float* dw, float* db, void* workspace,
+                          size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
+                          conv3x3_stream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* conv3x3_status_string(int status);
 

@@ -271,3 +271,15 @@ def test_up2_argument_checks():
     assert L.conv3x3_bwd_data_up2(G, Wt, Y, WS, 2 * 4 * 4 * 30 * 4 - 1, *d, 0, None) == ws_err
     assert L.conv3x3_bwd_data_up2(G, Wt, Y, Y, 1 << 30, *d, 0, None) == alias
     assert L.conv3x3_fwd_up2(X, Wt, B, X, *d, 0, None) == alias
+
+
+def test_s2_argument_checks():
+    d = (2, 4, 4, 6, 8)
+    assert L.conv3x3_fwd_s2(X, Wt, B, Y, 2, 4, 4, 5, 8, 0, None) == S["ERR_BAD_SHAPE"]  # odd H
+    assert L.conv3x3_bwd_data_s2(G, Wt, Y, 2, 4, 4, 6, 7, 0, None) == S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_fwd_s2(X, Wt, B, Y, *d, 1, None) == S["ERR_UNSUPPORTED"]
+    assert L.conv3x3_bwd_weight_s2(X, G, Y, B, WS, 1 << 30, *d, 1, None) == S["ERR_UNSUPPORTED"]
+    assert L.conv3x3_fwd_s2(None, Wt, B, Y, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_fwd_s2(X, Wt, B, X, *d, 0, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_bwd_weight_s2(X, G, Y, B, None, 0, 2, 64, 64, 64, 64, 0, None) == \
+        S["ERR_WORKSPACE"]

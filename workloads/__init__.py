@@ -156,3 +156,9 @@ IMAGE_STEM = {dt: Layer(f"image_stem_32x3to128_64x64_{dt}", 32, 3, 128, 64, 64, 
 # H, W are the input's (pre-upsampling) sizes; g is drawn at 2H x 2W.
 UPSAMPLE = [Layer(f"upsample_{c}ch_{r}to{2 * r}_f32", 32, c, c, r, r, "f32", 7, i)
             for i, (c, r) in enumerate(((512, 8), (384, 16), (256, 32)))]
+
+
+# The convolutions of the UNet's downsample blocks (3x3, stride 2, keeping
+# the channels): 64->32, 32->16 and 16->8 at N = 32; H, W are the input's.
+DOWNSAMPLE = [Layer(f"downsample_{c}ch_{r}to{r // 2}_f32", 32, c, c, r, r, "f32", 8, i)
+              for i, (c, r) in enumerate(((128, 64), (256, 32), (384, 16)))]
