@@ -41,10 +41,10 @@ struct ActArgs {
   // the source (forward) or x (backward-weight) is upsampled 2x by nearest
   // neighbour as it is staged; the problem's H, W are the upsampled sizes
   bool up2 = false;
-  // stride 2 (H, W even): the forward stores only the even pixels, at
-  // (h/2, w/2) of its H/2 x W/2 output; the backward passes read their
-  // H/2 x W/2 gradient zero-inserted into the H x W grid
-  bool sub2 = false;
+  // stride 2 (H, W even, the input's sizes): the forward reads its input at
+  // stride 2 and writes the H/2 x W/2 output (s2); the backward passes read
+  // their H/2 x W/2 gradient zero-inserted into the H x W grid (zi2)
+  bool s2 = false;
   bool zi2 = false;
 };
 

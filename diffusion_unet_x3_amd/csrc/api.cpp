@@ -118,7 +118,9 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
   if (pr.on() && (y == pr.scale || y == pr.shift)) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  Problem pb{kFwd, kdt(dtype), N, C, K, H, W, x.c0};
+  // a stride-2 forward tiles its H/2 x W/2 output
+  Problem pb{kFwd, kdt(dtype), N, C, K, geom == 2 ? H / 2 : H, geom == 2 ? W / 2 : W, x.c0};
+  pb.stride2 = geom == 2;
   pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
@@ -133,7 +135,7 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   a.pscale = pr.scale;
   a.pshift = pr.shift;
   a.up2 = geom == 1;
-  a.sub2 = geom == 2;
+  a.s2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {

@@ -51,8 +51,13 @@ namespace conv3x3 {
 // and is staged zero-inserted -- g[h/2, w/2] at even (h, w), zero
 // elsewhere -- so that the stride-1 backward-data of the full grid is the
 // stride-2 one.
+// S2 (forward of a stride-2 convolution): H, W are the input's sizes and the
+// pixel block tiles the H/2 x W/2 output; output pixel (ho, wo) at tap (r, s)
+// reads input pixel (2 ho + r - 1, 2 wo + s - 1).  The block's 2 TH + 1 input
+// rows are staged with their columns split by parity (odd columns, then even
+// ones), so that each tap's operand read is unit-stride across the lanes.
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
-          bool PRO = false, int PC = 0, bool UP2 = false, bool ZI2 = false>
+          bool PRO = false, int PC = 0, bool UP2 = false, bool ZI2 = false, bool S2 = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
     uint32_t dst1_bytes, int act, float* __restrict__ zout, const float* __restrict__ zsrc,
     const float* __restrict__ pscale, const float* __restrict__ pshift,
-    const float* __restrict__ px, int sub2) {
+    const float* __restrict__ px) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -68,18 +73,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int NJ = BM / (32 * WPX);   // 32x32 tiles per wave along pixels
   static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
                 "tile does not split into 32x32 wave tiles");
-  constexpr int RS = fwd_f32_rs(TW);
-  constexpr int PL = fwd_f32_plane(IMGS, TH, TW);
+  constexpr int RS = S2 ? fwd_f32_s2_rs(TW) : fwd_f32_rs(TW);
+  constexpr int PL = S2 ? fwd_f32_s2_plane(IMGS, TH, TW) : fwd_f32_plane(IMGS, TH, TW);
   constexpr int WS = fwd_f32_wstride(BCO);
-  constexpr int HR = TH + 2;  // staged rows per image (with halo)
+  constexpr int HR = S2 ? 2 * TH + 1 : TH + 2;  // staged rows per image (with halo)
+  constexpr int EV = fwd_f32_s2_even(TW);       // S2: row offset of the even columns
   static_assert(PC == 0 || (MODE == kFwd && VEC && PC < CB), "packed taps: forward only");
   static_assert(!UP2 || (MODE == kFwd && PC == 0 && !PRO), "upsampling: plain forward only");
   static_assert(!ZI2 || (MODE == kBwdData && !PRO), "zero insertion: plain backward-data only");
+  static_assert(!S2 || (MODE == kFwd && PC == 0 && !PRO && !UP2), "stride 2: plain forward only");
   // source rows and columns (the full grid's halves with UP2 or ZI2)
   const int Hs = (UP2 || ZI2) ? H / 2 : H, Ws = (UP2 || ZI2) ? W / 2 : W;
+  // output rows and columns (the pixel grid the blocks tile)
+  const int OH = S2 ? H / 2 : H, OW = S2 ? W / 2 : W;
   constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * 9;
 
-  __shared__ __attribute__((aligned(16))) float xs[fwd_f32_x_floats(CB, IMGS, TH, TW)];
+  __shared__ __attribute__((aligned(16))) float xs[CB * PL];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
   __shared__ float bias_s[MODE == kFwd ? BCO : 1];  // this tile's biases (0 without bias)
 
@@ -119,16 +128,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 
   // ---------------- staging: source tile ----------------
   // Vector path: interior columns as float4 (W % 4 == 0 so a float4 never
-  // straddles the image edge), the two halo columns as scalars.
+  // straddles the image edge), the two halo columns as scalars.  S2: an item
+  // is 8 input columns (two float4) = 4 output columns, and the only halo
+  // column is the left one (input column 2 w0 - 1; the right one, 2 (w0 +
+  // TW) - 1, is the last odd column of the last item).
   constexpr int XQ = TW / 4;
   constexpr int XV_ITEMS = CB * IMGS * HR * XQ;
   constexpr int XV_N = (XV_ITEMS + NT - 1) / NT;
-  constexpr int XH_ITEMS = CB * IMGS * HR * 2;
+  constexpr int XH_ITEMS = CB * IMGS * HR * (S2 ? 1 : 2);
   constexpr int XH_N = (XH_ITEMS + NT - 1) / NT;
   // Scalar path: every column of the staged rows.
-  constexpr int XS_ITEMS = CB * IMGS * HR * (TW + 2);
+  constexpr int XCOLS = S2 ? 2 * TW + 1 : TW + 2;
+  constexpr int XS_ITEMS = CB * IMGS * HR * XCOLS;
   constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
   f32x4 xv[VEC ? XV_N : 1];
+  f32x4 xv2[VEC && S2 ? XV_N : 1];  // S2: the item's second float4
   float xf[VEC ? XH_N : 1];
   // Backward-data with a fused activation: z at the same positions as the
   // gradient source; the source is multiplied by act'(z) when it is written
@@ -194,6 +208,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int ch = t / IMGS;
+        if constexpr (S2) {
+          // input row 2 h0 - 1 + rr, columns c .. c + 7
+          const int n = o.n0 + img, h = 2 * o.h0 + rr - 1, c = 2 * o.w0 + 8 * q;
+          const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn &&
+                          h >= 0 && h < H;
+          const uint32_t base = 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + c);
+          xv[k] = __builtin_bit_cast(f32x4, buffer_load16(sview, ok && c < W ? base : kOutside));
+          xv2[k] = __builtin_bit_cast(
+              f32x4, buffer_load16(sview, ok && c + 4 < W ? base + 16u : kOutside));
+          continue;
+        }
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w < W;
@@ -224,14 +249,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       for (int k = 0; k < XH_N; ++k) {
         if (!halo_loads) break;
         const int it = tid + k * NT;
-        const int side = it & 1;
-        int t = it >> 1;
+        const int side = S2 ? 0 : it & 1;
+        int t = S2 ? it : it >> 1;
         const int rr = t % HR;
         t /= HR;
         const int img = t % IMGS;
         const int ch = t / IMGS;
-        const int n = o.n0 + img, h = o.h0 + rr - 1;
-        const int w = o.w0 + (side ? TW : -1);
+        const int n = o.n0 + img, h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+        const int w = S2 ? 2 * o.w0 - 1 : o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w >= 0 && w < W && (!ZI2 || ((h | w) & 1) == 0);
         constexpr bool half = UP2 || ZI2;
@@ -293,6 +318,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
           const int q = it % XQ;
           const int t = it / XQ;  // (ch * IMGS + img) * HR + rr
+          if constexpr (S2) {
+            // columns c .. c + 7 = even 4q .. 4q + 3 and odd 4q + 1 .. 4q + 4
+            const f32x4 u = xv[k], u2 = xv2[k];
+            *reinterpret_cast<f32x4*>(&xs[t * RS + EV + 4 * q]) = f32x4{u.x, u.z, u2.x, u2.z};
+            *reinterpret_cast<f32x4*>(&xs[t * RS + kS2Odd + 1 + 4 * q]) =
+                f32x4{u.y, u.w, u2.y, u2.w};
+            continue;
+          }
           f32x4 v = xv[k];
           if (zs) {
             v.x *= act_slope(act, zv[k].x);
@@ -313,6 +346,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       for (int k = 0; k < XH_N; ++k) {
         const int it = tid + k * NT;
         if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
+          if constexpr (S2) {
+            xs[it * RS + kS2Odd] = xf[k];  // odd column 0 = input column 2 w0 - 1
+            continue;
+          }
           const int side = it & 1;
           const int t = it >> 1;
           float v = zs ? xf[k] * act_slope(act, zf[k]) : xf[k];
@@ -359,12 +396,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       for (int k = 0; k < XS_N; ++k) {
         const int it = tid + k * NT;
         if (XS_ITEMS % NT == 0 || it < XS_ITEMS) {
-          const int cc = it % (TW + 2) - 1;
-          const int t = it / (TW + 2);  // (ch * IMGS + img) * HR + rr
+          const int cc = it % XCOLS - 1;
+          const int t = it / XCOLS;  // (ch * IMGS + img) * HR + rr
           const int rr = t % HR;
           const int img = (t / HR) % IMGS;
           const int ch = t / (HR * IMGS);
-          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
+          const int n = o.n0 + img;
+          // S2: input column 2 w0 + cc, cc = -1 .. 2 TW - 1 (odd column
+          // (cc + 1) / 2 for even cc + 1, even column cc / 2 otherwise)
+          const int h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+          const int w = S2 ? 2 * o.w0 + cc : o.w0 + cc;
+          const int slot = S2 ? ((cc & 1) ? kS2Odd + (cc + 1) / 2 : EV + cc / 2) : 4 + cc;
           float v = 0.f;
           if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W &&
               (!ZI2 || ((h | w) & 1) == 0)) {
@@ -378,7 +420,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
               v = act_value(kActSilu, v * pscale[pc] + pshift[pc]);
             }
           }
-          xs[t * RS + 4 + cc] = v;
+          xs[t * RS + slot] = v;
         }
       }
 #pragma unroll 4
@@ -407,7 +449,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   for (int j = 0; j < NJ; ++j) {
     const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
-    boff[j] = (PC ? 0 : hi * PL) + (img * HR + row) * RS + 4 + col - 1;
+    boff[j] = S2 ? hi * PL + (img * HR + 2 * row) * RS + col
+                 : (PC ? 0 : hi * PL) + (img * HR + row) * RS + 4 + col - 1;
   }
   const int aoff = (PC ? hi : hi * 9) * WS + wco * (BCO / WCO) + l32;
 
@@ -429,8 +472,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       const int cp = st / 9, r = (st % 9) / 3, s = st % 3;
 #pragma unroll
       for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + (2 * cp * 9 + r * 3 + s) * WS + i * 32];
+      // S2: taps s = 0, 1, 2 read odd column j, even column j, odd column j + 1
+      const int so = S2 ? (s == 1 ? EV : kS2Odd + s / 2) : s;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + s];
+      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + r * RS + so];
     }
   };
 
@@ -534,11 +579,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     return;
   }
   const bool plain = MODE != kFwd || (act == kActNone && zout == nullptr);
-  // sub2 (forward of a stride-2 convolution): only the even pixels of the
-  // full grid are outputs, stored at (h/2, w/2) of the H/2 x W/2 output
-  const int sh = sub2 ? 1 : 0;
-  const int Wo = W >> sh;
-  const long HWo = (long)(H >> sh) * Wo;
+  const long HWo = (long)OH * OW;
   if (od_bytes != 0 && co_n == BCO) {
     // Whole channel tile in range: one buffer store per accumulator element,
     // the lane's byte offset computed once per pixel column j and the
@@ -552,10 +593,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       const int p = wpx * (BM / WPX) + j * 32 + l32;
       const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
       const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
-      const bool keep = n < N && h < H && w < W && (sh == 0 || ((h | w) & 1) == 0);
+      const bool keep = n < N && h < OH && w < OW;
       const uint32_t off =
-          keep ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HWo +
-                  (uint32_t)((h >> sh) * Wo + (w >> sh))) * 4u
+          keep ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HWo + (uint32_t)(h * OW + w)) * 4u
                : kOutside;
       if (plain) {
 #pragma unroll
@@ -582,8 +622,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
-    if (n >= N || h >= H || w >= W || (sh && ((h | w) & 1))) continue;
-    float* out = od + (long)n * ocs * HWo + (long)(h >> sh) * Wo + (w >> sh);
+    if (n >= N || h >= OH || w >= OW) continue;
+    float* out = od + (long)n * ocs * HWo + (long)h * OW + w;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -614,8 +654,8 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets); otherwise both take the plain-store path.
   const long hw4 = (long)H * W * 4;
-  // output plane bytes (a stride-2 forward keeps a quarter of the grid)
-  const long ohw4 = a.sub2 ? (long)(H / 2) * (W / 2) * 4 : hw4;
+  // output plane bytes (a stride-2 forward writes an H/2 x W/2 output)
+  const long ohw4 = a.s2 ? (long)(H / 2) * (W / 2) * 4 : hw4;
   const long ob0 = (long)N * dst.c0 * ohw4, ob1 = (long)N * (Cout - dst.c0) * ohw4;
   const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
@@ -623,41 +663,46 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * shw4) : 0u;
   const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * shw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_, PC_, UP_, ZI_)                                                      \
+#define CONV3X3_L(VEC_, PRO_, PC_, UP_, ZI_, S2_)                                                 \
   hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_,   \
-                                     ZI_>),                                                       \
+                                     ZI_, S2_>),                                                  \
                      grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,       \
-                     a.zout, a.zsrc, a.pscale, a.pshift, a.px, a.sub2 ? 1 : 0)
+                     a.zout, a.zsrc, a.pscale, a.pshift, a.px)
   // packed taps: the forward of a 3- or 4-channel single tensor
   const int pc =
-      (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.sub2 && src.c0 == Cin) ? Cin : 0;
+      (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.s2 && src.c0 == Cin) ? Cin : 0;
   constexpr bool kF = MODE == kFwd;
-  if (a.up2) {
+  if (a.s2) {
     if (vec)
-      CONV3X3_L(true, false, 0, kF, false);
+      CONV3X3_L(true, false, 0, false, false, kF);
     else
-      CONV3X3_L(false, false, 0, kF, false);
+      CONV3X3_L(false, false, 0, false, false, kF);
+  } else if (a.up2) {
+    if (vec)
+      CONV3X3_L(true, false, 0, kF, false, false);
+    else
+      CONV3X3_L(false, false, 0, kF, false, false);
   } else if (a.zi2) {
     if (vec)
-      CONV3X3_L(true, false, 0, false, !kF);
+      CONV3X3_L(true, false, 0, false, !kF, false);
     else
-      CONV3X3_L(false, false, 0, false, !kF);
+      CONV3X3_L(false, false, 0, false, !kF, false);
   } else if (a.pscale) {
     if (vec)
-      CONV3X3_L(true, true, 0, false, false);
+      CONV3X3_L(true, true, 0, false, false, false);
     else
-      CONV3X3_L(false, true, 0, false, false);
+      CONV3X3_L(false, true, 0, false, false, false);
   } else if (pc == 3) {
-    CONV3X3_L(true, false, kF ? 3 : 0, false, false);
+    CONV3X3_L(true, false, kF ? 3 : 0, false, false, false);
   } else if (pc == 4) {
-    CONV3X3_L(true, false, kF ? 4 : 0, false, false);
+    CONV3X3_L(true, false, kF ? 4 : 0, false, false, false);
   } else {
     if (vec)
-      CONV3X3_L(true, false, 0, false, false);
+      CONV3X3_L(true, false, 0, false, false, false);
     else
-      CONV3X3_L(false, false, 0, false, false);
+      CONV3X3_L(false, false, 0, false, false, false);
   }
 #undef CONV3X3_L
 }

@@ -50,6 +50,23 @@ CONV3X3_HD constexpr int fwd_f32_lds_bytes(int cb, int imgs, int th, int tw, int
   return 4 * (fwd_f32_x_floats(cb, imgs, th, tw) + fwd_f32_w_floats(cb, co_tile));
 }
 
+// Forward of a stride-2 convolution, float32: for an output block of th x tw
+// pixels the input rows 2 h0 - 1 .. 2 h0 + 2 th - 1 are staged (2 th + 1 of
+// them) with their columns split by parity: odd input columns 2 (w0 + j) - 1,
+// j = 0..tw, at row offset kS2Odd + j, even columns 2 (w0 + j) at kS2Even(tw)
+// + j.  The taps s = 0, 1, 2 of output column j then read odd j, even j and
+// odd j + 1: unit stride across the lanes.  Both runs are 16-byte aligned
+// where the loader writes them (odd j = 1.., even j = 0..).
+constexpr int kS2Odd = 3;
+CONV3X3_HD constexpr int fwd_f32_s2_even(int tw) { return tw + 8; }
+CONV3X3_HD constexpr int fwd_f32_s2_rs(int tw) { return 2 * tw + 8; }
+CONV3X3_HD constexpr int fwd_f32_s2_plane(int imgs, int th, int tw) {
+  return imgs * (2 * th + 1) * fwd_f32_s2_rs(tw);
+}
+CONV3X3_HD constexpr int fwd_f32_s2_lds_bytes(int cb, int imgs, int th, int tw, int co_tile) {
+  return 4 * (cb * fwd_f32_s2_plane(imgs, th, tw) + fwd_f32_w_floats(cb, co_tile));
+}
+
 // ---- forward / backward-data, bfloat16 ----
 // Plane of one 8-channel group, in 16-byte words, padded to 8 mod 16 words
 // so that the two groups' words written by one transpose step fall in
