@@ -41,9 +41,9 @@ struct ActArgs {
   // the source (forward) or x (backward-weight) is upsampled 2x by nearest
   // neighbour as it is staged; the problem's H, W are the upsampled sizes
   bool up2 = false;
-  // stride 2 (H, W even, the input's sizes): the forward reads its input at
-  // stride 2 and writes the H/2 x W/2 output (s2); the backward passes read
-  // their H/2 x W/2 gradient zero-inserted into the H x W grid (zi2)
+  // stride 2 (H, W even, the input's sizes): the forward and backward-weight
+  // read x at stride 2 over the H/2 x W/2 output grid (s2); backward-data
+  // reads its H/2 x W/2 gradient zero-inserted into the H x W grid (zi2)
   bool s2 = false;
   bool zi2 = false;
 };

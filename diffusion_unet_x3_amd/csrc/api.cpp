@@ -245,7 +245,10 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
                   (db && (db == pr.scale || db == pr.shift))))
     return CONV3X3_ERR_ALIAS;
   Plan pl;
-  if (!plan(Problem{kBwdWeight, kdt(dtype), N, C, K, H, W, x.c0}, &pl)) return CONV3X3_ERR_BAD_SHAPE;
+  // stride 2: the pixel chunks tile g's H/2 x W/2 grid
+  Problem pb{kBwdWeight, kdt(dtype), N, C, K, geom == 2 ? H / 2 : H, geom == 2 ? W / 2 : W, x.c0};
+  pb.stride2 = geom == 2;
+  if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
   if (workspace && (is_part(x, workspace) || workspace == g || workspace == dw ||
@@ -261,11 +264,12 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   a.pscale = pr.scale;
   a.pshift = pr.shift;
   a.up2 = geom == 1;
-  a.zi2 = geom == 2;
+  a.s2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && parts_aligned(x) && aligned16(g) &&
+    // (stride 2: g's rows, W/2 floats, must hold whole float4 items too)
+    const bool vec = W % (geom == 2 ? 8 : 4) == 0 && parts_aligned(x) && aligned16(g) &&
                      (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * C * hw) &&
                      buffer_sized(2L * N * K * hw);
     Split<const float> xs{(const float*)x.p0, (const float*)x.p1, x.c0};

@@ -31,9 +31,10 @@
 namespace conv3x3 {
 
 // UP2: x is upsampled 2x by nearest neighbour as it is staged (H, W are the
-// upsampled sizes, g's; x is H/2 x W/2).  ZI2 (a stride-2 convolution): g
-// is H/2 x W/2 and is staged zero-inserted, g[h/2, w/2] at even (h, w).
-template <int TW, int TH, int IMGS, bool VEC, bool UP2 = false, bool ZI2 = false>
+// upsampled sizes, g's; x is H/2 x W/2).  S2 (a stride-2 convolution): H, W
+// are x's, g is H/2 x W/2 and the chunks tile g's pixels; chunk pixel
+// (ho, wo) pairs with x at (2 ho + r - 1, 2 wo + s - 1).
+template <int TW, int TH, int IMGS, bool VEC, bool UP2 = false, bool S2 = false>
 __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ x1, int cx0,
     const float* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
@@ -43,15 +44,17 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const float* __restrict__ pshift) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P == 64, "pixel chunk must hold 64 pixels");
+  static_assert(!(UP2 && S2), "upsampling or stride 2");
   constexpr int GS = wgrad_f32_gstride(IMGS, TH, TW);
-  constexpr int RSW = wgrad_f32_rs(TW);
-  constexpr int PLW = wgrad_f32_plane(IMGS, TH, TW);
-  constexpr int HR = TH + 2;
+  constexpr int RSW = S2 ? wgrad_f32_s2_rs(TW) : wgrad_f32_rs(TW);
+  constexpr int PLW = S2 ? wgrad_f32_s2_plane(IMGS, TH, TW) : wgrad_f32_plane(IMGS, TH, TW);
+  constexpr int HR = S2 ? 2 * TH + 1 : TH + 2;  // staged x rows per image
 
   // Two LDS buffers: chunk i is read from one while chunk i + 1 is written
-  // into the other.
-  __shared__ float gs_buf[2][64 * GS];
-  __shared__ float xs_buf[2][64 * PLW];
+  // into the other.  S2: one (the next chunk is written after a barrier).
+  constexpr int NBUF = S2 ? 1 : 2;
+  __shared__ float gs_buf[NBUF][64 * GS];
+  __shared__ float xs_buf[NBUF][64 * PLW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -78,28 +81,34 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   const int k0 = (tile / tiles_c) * 64;
   const long HW = (long)H * W;
   const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;  // x's rows and columns
-  const int Hg = ZI2 ? H / 2 : H, Wg = ZI2 ? W / 2 : W;  // g's rows and columns
+  const int Hg = S2 ? H / 2 : H, Wg = S2 ? W / 2 : W;    // g's rows and columns (the chunk grid)
   const bool do_db = out_db != nullptr && tile % tiles_c == 0;
 
-  // g tile: 64 k x P pixels.  x tile: 64 c x IMGS x HR rows x (TW + 2) columns.
+  // g tile: 64 k x P pixels.  x tile: 64 c x IMGS x HR rows x (TW + 2)
+  // columns; S2: 2 TW + 1 columns, of which the vector items cover the 2 TW
+  // from 2 w0 and the halo item the left one (2 w0 - 1).
   constexpr int XQ = TW / 4;
+  constexpr int XQX = S2 ? TW / 2 : TW / 4;  // vector items per staged x row
   constexpr int GV_ITEMS = 64 * IMGS * TH * XQ;
   constexpr int NT = 768;
   constexpr int GV_N = (GV_ITEMS + NT - 1) / NT;
-  constexpr int XV_ITEMS = 64 * IMGS * HR * XQ;
+  constexpr int XV_ITEMS = 64 * IMGS * HR * XQX;
   constexpr int XV_N = (XV_ITEMS + NT - 1) / NT;
-  constexpr int XH_ITEMS = 64 * IMGS * HR * 2;
+  constexpr int XH_ITEMS = 64 * IMGS * HR * (S2 ? 1 : 2);
   constexpr int XH_N = (XH_ITEMS + NT - 1) / NT;
   constexpr int GS_ITEMS = 64 * P;
   constexpr int GS_N = (GS_ITEMS + NT - 1) / NT;
-  constexpr int XS_ITEMS = 64 * IMGS * HR * (TW + 2);
+  constexpr int XCOLS = S2 ? 2 * TW + 1 : TW + 2;
+  constexpr int XS_ITEMS = 64 * IMGS * HR * XCOLS;
   constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
 
   f32x4 gv[VEC ? GV_N : 1];
   // Fused activation: z at the positions of g; g is multiplied by act'(z)
   // when it is written to LDS.
-  const bool zs = zsrc != nullptr;
-  f32x4 zv[VEC ? GV_N : 1];
+  // (neither this nor the prologue below goes with stride 2, whose larger
+  // x items need the registers)
+  const bool zs = !S2 && zsrc != nullptr;
+  f32x4 zv[VEC && !S2 ? GV_N : 1];
   f32x4 xv[VEC ? XV_N : 1];
   float xf[VEC ? XH_N : 1];
   // With a single tile across the width both halo columns are padding: they
@@ -110,10 +119,11 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
   // Input prologue: each staged x value becomes SiLU(x * scale[n, c] +
   // shift[n, c]); items outside the image or the channels load x = scale =
   // shift = 0 and stage SiLU(0) = 0, so the padding stays zero.
-  const bool pro = pscale != nullptr;
-  float psv[VEC ? XV_N : 1], ptv[VEC ? XV_N : 1], psh[VEC ? XH_N : 1], pth[VEC ? XH_N : 1];
+  const bool pro = !S2 && pscale != nullptr;
+  constexpr int PV_N = VEC && !S2 ? XV_N : 1, PH_N = VEC && !S2 ? XH_N : 1;
+  float psv[PV_N], ptv[PV_N], psh[PH_N], pth[PH_N];
 #pragma unroll
-  for (int k = 0; k < (VEC ? XH_N : 1); ++k) psh[k] = pth[k] = 0.f;
+  for (int k = 0; k < PH_N; ++k) psh[k] = pth[k] = 0.f;
   const uint32_t pbytes = pro ? 4u * (uint32_t)(N * C) : 0u;
   const __amdgpu_buffer_rsrc_t psview = buffer_view(pscale, pbytes);
   const __amdgpu_buffer_rsrc_t ptview = buffer_view(pshift, pbytes);
@@ -137,32 +147,26 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int img = t % IMGS;
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 4 * q;
-        const bool ok = (GV_ITEMS % NT == 0 || it < GV_ITEMS) && n < N && kk < K && h < H && w < W;
-        if constexpr (ZI2) {
-          // four columns of an even row: g at the even ones; odd rows zero
-          float ga, gb;
-          buffer_load_2f(gview,
-                         ok && (h & 1) == 0
-                             ? 4u * (uint32_t)(((n * K + kk) * Hg + h / 2) * Wg + w / 2)
-                             : kOutside,
-                         ga, gb);
-          gv[k] = f32x4{ga, 0.f, gb, 0.f};
-          continue;
-        }
-        const uint32_t off = ok ? 4u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside;
+        const bool ok =
+            (GV_ITEMS % NT == 0 || it < GV_ITEMS) && n < N && kk < K && h < Hg && w < Wg;
+        const uint32_t off = ok ? 4u * (uint32_t)(((n * K + kk) * Hg + h) * Wg + w) : kOutside;
         gv[k] = __builtin_bit_cast(f32x4, buffer_load16(gview, off));
         if (zs) zv[k] = __builtin_bit_cast(f32x4, buffer_load16(zview, off));
       }
 #pragma unroll
       for (int k = 0; k < XV_N; ++k) {
         const int it = tid + k * NT;
-        const int q = it % XQ;
-        int t = it / XQ;
+        const int q = it % XQX;
+        int t = it / XQX;
         const int rr = t % HR;
         t /= HR;
         const int img = t % IMGS;
         const int cl = t / IMGS;
-        const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
+        // x row and first column of the item (S2: input row 2 h0 - 1 + rr,
+        // columns 2 w0 + 4q ..)
+        const int n = o.n0 + img;
+        const int h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+        const int w = S2 ? 2 * o.w0 + 4 * q : o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && cl < cn && h >= 0 &&
                         h < H && w < W;
         if constexpr (UP2) {
@@ -188,14 +192,14 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       for (int k = 0; k < XH_N; ++k) {
         if (!halo_loads) break;
         const int it = tid + k * NT;
-        const int side = it & 1;
-        int t = it >> 1;
+        const int side = S2 ? 0 : it & 1;
+        int t = S2 ? it : it >> 1;
         const int rr = t % HR;
         t /= HR;
         const int img = t % IMGS;
         const int cl = t / IMGS;
-        const int n = o.n0 + img, h = o.h0 + rr - 1;
-        const int w = o.w0 + (side ? TW : -1);
+        const int n = o.n0 + img, h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+        const int w = S2 ? 2 * o.w0 - 1 : o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && cl < cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
         xf[k] = __builtin_bit_cast(
@@ -243,8 +247,8 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       for (int k = 0; k < XV_N; ++k) {
         const int it = tid + k * NT;
         if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
-          const int q = it % XQ;
-          const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
+          const int q = it % XQX;
+          const int t = it / XQX;  // (cl * IMGS + img) * HR + rr
           const int cl = t / (IMGS * HR);
           float* d = &xs[cl * PLW + (t % (IMGS * HR)) * RSW + 1 + 4 * q];
           f32x4 v = xv[k];
@@ -264,8 +268,8 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       for (int k = 0; k < XH_N; ++k) {
         const int it = tid + k * NT;
         if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
-          const int side = it & 1;
-          const int t = it >> 1;
+          const int side = S2 ? 0 : it & 1;
+          const int t = S2 ? it : it >> 1;
           const int cl = t / (IMGS * HR);
           xs[cl * PLW + (t % (IMGS * HR)) * RSW + 1 + (side ? TW : -1)] =
               pro ? act_value(kActSilu, xf[k] * psh[k] + pth[k]) : xf[k];
@@ -286,12 +290,9 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + col;
         float v = 0.f;
-        if (n < N && kk < K && h < H && w < W) {
-          const long e = ((long)n * K + kk) * HW + (long)h * W + w;
-          if constexpr (ZI2)
-            v = ((h | w) & 1) ? 0.f : g[((long)n * K + kk) * Hg * Wg + (long)(h / 2) * Wg + w / 2];
-          else
-            v = g[e];
+        if (n < N && kk < K && h < Hg && w < Wg) {
+          const long e = ((long)n * K + kk) * Hg * Wg + (long)h * Wg + w;
+          v = g[e];
           if (zs) v *= act_slope(act, zsrc[e]);
         }
         gs[kl * GS + it % P] = v;
@@ -300,13 +301,15 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       for (int k = 0; k < XS_N; ++k) {
         const int it = tid + k * NT;
         if (XS_ITEMS % NT == 0 || it < XS_ITEMS) {
-          const int cc = it % (TW + 2) - 1;
-          int t = it / (TW + 2);
+          const int cc = it % XCOLS - 1;
+          int t = it / XCOLS;
           const int rr = t % HR;
           t /= HR;
           const int img = t % IMGS;
           const int cl = t / IMGS;
-          const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
+          const int n = o.n0 + img;
+          const int h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+          const int w = S2 ? 2 * o.w0 + cc : o.w0 + cc;
           float v = 0.f;
           if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W) {
             v = UP2 ? xp[((long)n * cs + cl0 + cl) * Hs * Ws + (long)(h / 2) * Ws + w / 2]
@@ -339,7 +342,9 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     const int p = 2 * q2 + hi;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
     a[buf] = gs[goff + p];
-    const int xb = xoff + (img * HR + row) * RSW + col;
+    // S2: x row 2 row + r and column 2 col + s of the staged tile
+    const int xb = S2 ? xoff + (img * HR + 2 * row) * RSW + 2 * col
+                      : xoff + (img * HR + row) * RSW + col;
 #pragma unroll
     for (int s = 0; s < 3; ++s) b[buf][s] = xs[xb + s];
   };
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
     __syncthreads();
   }
   for (int chunk = chunk_begin; chunk < chunk_end; ++chunk) {
-    const int cur_buf = (chunk - chunk_begin) & 1;
+    const int cur_buf = S2 ? 0 : (chunk - chunk_begin) & 1;
     const float* gs = gs_buf[cur_buf];
     const float* xs = xs_buf[cur_buf];
     // Step q2 (two pixels) reads its operands while step q2-1's MFMAs run.
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 3; ++s) acc[s] = mfma_32x32x2_f32(a[cur], b[cur][s], acc[s]);
-      if (q2 == kStoreStep && chunk + 1 < chunk_end) {
+      if (!S2 && q2 == kStoreStep && chunk + 1 < chunk_end) {
         __builtin_amdgcn_sched_barrier(0);
         store_tiles(chunk + 1, cur_buf ^ 1);
         if (chunk + 2 < chunk_end) load_tiles(chunk + 2);
@@ -382,6 +387,13 @@ __global__ __launch_bounds__(768) void wgrad_f32_kernel(
       for (int i = 0; i < P / 4; ++i) dbsum += gs[kl * GS + part + 4 * i];
     }
     __syncthreads();
+    if (S2 && chunk + 1 < chunk_end) {
+      // single buffer: the next chunk is written once every wave is done
+      // with this one
+      store_tiles(chunk + 1, 0);
+      if (chunk + 2 < chunk_end) load_tiles(chunk + 2);
+      __syncthreads();
+    }
   }
 
   // Partial dw of this slice.  Split: tap-major [tap][k][c] slot at
@@ -533,9 +545,9 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, Split<const float> x, co
   const long xhw4 = a.up2 ? hw4 / 4 : hw4;  // x's plane bytes
   const uint32_t xb0 = vec ? (uint32_t)(N * x.c0 * xhw4) : 0u;
   const uint32_t xb1 = vec ? (uint32_t)(N * (C - x.c0) * xhw4) : 0u;
-  const uint32_t gb = vec ? (uint32_t)(N * K * (a.zi2 ? hw4 / 4 : hw4)) : 0u;
-#define CONV3X3_L(VEC_, UP_, ZI_)                                                                 \
-  hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, VEC_, UP_, ZI_>), grid, block, 0, stream,     \
+  const uint32_t gb = vec ? (uint32_t)(N * K * (a.s2 ? hw4 / 4 : hw4)) : 0u;
+#define CONV3X3_L(VEC_, UP_, S2_)                                                                 \
+  hipLaunchKernelGGL((wgrad_f32_kernel<TW, TH, IMGS, VEC_, UP_, S2_>), grid, block, 0, stream,     \
                      x.p0,                                                                        \
                      x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,            \
                      pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,             \
@@ -545,7 +557,7 @@ static void launch_wgrad_geom(const Plan& pl, bool vec, Split<const float> x, co
       CONV3X3_L(true, true, false);
     else
       CONV3X3_L(false, true, false);
-  } else if (a.zi2) {
+  } else if (a.s2) {
     if (vec)
       CONV3X3_L(true, false, true);
     else

@@ -99,6 +99,17 @@ CONV3X3_HD constexpr int wgrad_f32_plane(int imgs, int th, int tw) {
 CONV3X3_HD constexpr int wgrad_f32_lds_bytes(int imgs, int th, int tw) {
   return 2 * 4 * 64 * (wgrad_f32_gstride(imgs, th, tw) + wgrad_f32_plane(imgs, th, tw));
 }
+// Stride 2 (the chunk's th x tw pixels are output pixels): x holds the
+// 2 th + 1 input rows 2 h0 - 1 .. of 2 tw + 1 columns 2 w0 - 1 .. (column t
+// at row offset t), about four times the stride-1 tile, so both tiles are
+// single-buffered.
+CONV3X3_HD constexpr int wgrad_f32_s2_rs(int tw) { return 2 * tw + 2; }
+CONV3X3_HD constexpr int wgrad_f32_s2_plane(int imgs, int th, int tw) {
+  return (imgs * (2 * th + 1) * wgrad_f32_s2_rs(tw)) | 1;
+}
+CONV3X3_HD constexpr int wgrad_f32_s2_lds_bytes(int imgs, int th, int tw) {
+  return 4 * 64 * (wgrad_f32_gstride(imgs, th, tw) + wgrad_f32_s2_plane(imgs, th, tw));
+}
 
 // ---- backward-weight, bfloat16 ----
 // g tile : [64 k][P + 8] bf16 (row stride 2P + 16 bytes: eight lanes reading

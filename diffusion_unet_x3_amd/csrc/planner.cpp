@@ -221,7 +221,8 @@ bool plan(const Problem& p, Plan* out) {
     pl.grid_z = 1;
     pl.threads = 768;
     pl.lds_bytes = p.dtype == kF32
-        ? wgrad_f32_lds_bytes(pl.imgs, pl.th, pl.tw)
+        ? (p.stride2 ? wgrad_f32_s2_lds_bytes(pl.imgs, pl.th, pl.tw)
+                     : wgrad_f32_lds_bytes(pl.imgs, pl.th, pl.tw))
         : wgrad_bf16_lds_bytes(pl.imgs, pl.th, pl.tw);
     pl.workspace_bytes = wgrad_workspace_bytes(pl, p.C, p.K);
   } else {

@@ -54,8 +54,9 @@ struct Problem {
   // reduction may be split over several workgroups per output tile (partial
   // sums in the workspace, then a fixed-order reduce)
   bool allow_split = false;
-  // float32 forward of a stride-2 convolution: H, W are the output's; the
-  // x tile holds 2 th + 1 input rows of 2 tw + 1 columns
+  // float32 forward / backward-weight of a stride-2 convolution: H, W are
+  // the output's (g's); the x tile holds 2 th + 1 input rows of 2 tw + 1
+  // columns
   bool stride2 = false;
 };
 
