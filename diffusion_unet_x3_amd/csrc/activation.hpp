@@ -41,11 +41,11 @@ struct ActArgs {
   // the source (forward) or x (backward-weight) is upsampled 2x by nearest
   // neighbour as it is staged; the problem's H, W are the upsampled sizes
   bool up2 = false;
-  // stride 2 (H, W even, the input's sizes): the forward and backward-weight
-  // read x at stride 2 over the H/2 x W/2 output grid (s2); backward-data
-  // reads its H/2 x W/2 gradient zero-inserted into the H x W grid (zi2)
+  // stride 2 (H, W even, the input's sizes; the output and g are H/2 x W/2):
+  // the forward and backward-weight read x at stride 2 over the output grid;
+  // backward-data runs one dense convolution of g per output-pixel parity
+  // class
   bool s2 = false;
-  bool zi2 = false;
 };
 
 // sigmoid(z) = 1 / (1 + e^-z) with the hardware exponential and reciprocal

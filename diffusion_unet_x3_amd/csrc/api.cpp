@@ -162,8 +162,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
 int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx, int N, int C,
                   int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
                   Prologue pr = Prologue(), const void* px = nullptr, bool ws_call = false,
-                  void* ws = nullptr, size_t ws_bytes = 0, bool zi2 = false) {
-  // zi2 (stride 2): H, W are dx's; g is H/2 x W/2
+                  void* ws = nullptr, size_t ws_bytes = 0, bool s2 = false) {
+  // s2 (stride 2): H, W are dx's; g is H/2 x W/2
   if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
   if (pr.on() && !px) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
@@ -184,7 +184,10 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   // du's epilogue reads x through a 32-bit buffer view, like the stores
   if (pr.on() && 4L * N * C * H * W >= 2147483648L) return CONV3X3_ERR_UNSUPPORTED;
   Plan pl;
-  Problem pb{kBwdData, kdt(dtype), N, C, K, H, W, dx.c0};
+  // stride 2: the plan tiles g's H/2 x W/2 grid; each tile computes the four
+  // output-pixel parity classes of its pixels
+  Problem pb{kBwdData, kdt(dtype), N, C, K, s2 ? H / 2 : H, s2 ? W / 2 : W, dx.c0};
+  pb.stride2 = s2;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
@@ -200,11 +203,12 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   a.pscale = pr.scale;
   a.pshift = pr.shift;
   a.px = (const float*)px;
-  a.zi2 = zi2;
+  a.s2 = s2;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
-    const bool vec = W % 4 == 0 && C % 4 == 0 && dx.c0 % 4 == 0 && aligned16(g) &&
+    // (stride 2: g's rows, W/2 floats, hold whole float4 items)
+    const bool vec = W % (s2 ? 8 : 4) == 0 && C % 4 == 0 && dx.c0 % 4 == 0 && aligned16(g) &&
                      aligned16(w) && (!a.zsrc || aligned16(a.zsrc)) &&
                      buffer_sized(2L * N * K * hw) && buffer_sized(2L * K * C * 9);
     ok = launch_fwd_f32(pl, vec, one((const float*)g, K), (const float*)w, nullptr, dx, N, K, C,

@@ -47,17 +47,22 @@ namespace conv3x3 {
 // staged -- H and W are the upsampled (output) sizes, the source tensor is
 // H/2 x W/2, and staged pixel (h, w) reads source pixel (h/2, w/2); a vector
 // item of four output columns is two source floats, each used twice.
-// ZI2 (backward-data of a stride-2 convolution): the source g is H/2 x W/2
-// and is staged zero-inserted -- g[h/2, w/2] at even (h, w), zero
-// elsewhere -- so that the stride-1 backward-data of the full grid is the
-// stride-2 one.
+// S2B (backward-data of a stride-2 convolution; H, W are g's sizes, dx is
+// 2H x 2W): dx[2i + ph, 2j + pw] receives only the taps (r, s) with r = 1
+// for ph = 0 and r = 0, 2 for ph = 1 (the same for s and pw), tap r reading
+// g row i + (ph + 1 - r) / 2.  The block tiles g's grid, stages g with its
+// halo as a plain backward-data does, and runs the nine taps once each: tap
+// (r, s) feeds the accumulators of its parity class (ph, pw) = (r != 1,
+// s != 1) -- four accumulator sets -- and the epilogue stores each set to
+// its class's pixels.  The MFMA work is the useful work, and each staged
+// tile serves all four classes.
 // S2 (forward of a stride-2 convolution): H, W are the input's sizes and the
 // pixel block tiles the H/2 x W/2 output; output pixel (ho, wo) at tap (r, s)
 // reads input pixel (2 ho + r - 1, 2 wo + s - 1).  The block's 2 TH + 1 input
 // rows are staged with their columns split by parity (odd columns, then even
 // ones), so that each tap's operand read is unit-stride across the lanes.
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
-          bool PRO = false, int PC = 0, bool UP2 = false, bool ZI2 = false, bool S2 = false>
+          bool PRO = false, int PC = 0, bool UP2 = false, bool S2B = false, bool S2 = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -80,13 +85,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int EV = fwd_f32_s2_even(TW);       // S2: row offset of the even columns
   static_assert(PC == 0 || (MODE == kFwd && VEC && PC < CB), "packed taps: forward only");
   static_assert(!UP2 || (MODE == kFwd && PC == 0 && !PRO), "upsampling: plain forward only");
-  static_assert(!ZI2 || (MODE == kBwdData && !PRO), "zero insertion: plain backward-data only");
+  static_assert(!S2B || (MODE == kBwdData && !PRO && PC == 0 && !UP2),
+                "stride-2 parity classes: plain backward-data only");
   static_assert(!S2 || (MODE == kFwd && PC == 0 && !PRO && !UP2), "stride 2: plain forward only");
-  // source rows and columns (the full grid's halves with UP2 or ZI2)
-  const int Hs = (UP2 || ZI2) ? H / 2 : H, Ws = (UP2 || ZI2) ? W / 2 : W;
+  // source rows and columns (the full grid's halves with UP2)
+  const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;
   // output rows and columns (the pixel grid the blocks tile)
   const int OH = S2 ? H / 2 : H, OW = S2 ? W / 2 : W;
   constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * 9;
+  constexpr int NACC = S2B ? 4 : 1;  // accumulator sets (S2B: one per parity class)
 
   __shared__ __attribute__((aligned(16))) float xs[CB * PL];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
@@ -222,17 +229,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w < W;
-        if constexpr (UP2 || ZI2) {
-          // four full-grid columns from two source floats: each used twice
-          // (upsampling), or at the even columns of even rows (zero
-          // insertion; odd rows read nothing)
-          const bool okz = ok && (!ZI2 || (h & 1) == 0);
+        if constexpr (UP2) {
+          // four upsampled columns from two source floats, each used twice
           const uint32_t so =
-              okz ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + h / 2) * Ws + w / 2)
-                  : kOutside;
+              ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + h / 2) * Ws + w / 2)
+                 : kOutside;
           float xa, xb;
           buffer_load_2f(sview, so, xa, xb);
-          xv[k] = ZI2 ? f32x4{xa, 0.f, xb, 0.f} : f32x4{xa, xa, xb, xb};
+          xv[k] = f32x4{xa, xa, xb, xb};
           continue;
         }
         const uint32_t off =
@@ -258,8 +262,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
         const int w = S2 ? 2 * o.w0 - 1 : o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
-                        h < H && w >= 0 && w < W && (!ZI2 || ((h | w) & 1) == 0);
-        constexpr bool half = UP2 || ZI2;
+                        h < H && w >= 0 && w < W;
+        constexpr bool half = UP2;
         const uint32_t off =
             ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + (half ? h / 2 : h)) * Ws +
                                  (half ? w / 2 : w))
@@ -408,9 +412,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int w = S2 ? 2 * o.w0 + cc : o.w0 + cc;
           const int slot = S2 ? ((cc & 1) ? kS2Odd + (cc + 1) / 2 : EV + cc / 2) : 4 + cc;
           float v = 0.f;
-          if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W &&
-              (!ZI2 || ((h | w) & 1) == 0)) {
-            const long e = (UP2 || ZI2)
+          if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W) {
+            const long e = UP2
                 ? ((long)n * f.cs + f.cl0 + ch) * Hs * Ws + (long)(h / 2) * Ws + w / 2
                 : ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
             v = sp[e];
@@ -454,6 +457,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   }
   const int aoff = (PC ? hi : hi * 9) * WS + wco * (BCO / WCO) + l32;
 
+
   // Operands of one MFMA step st = (cp, r, s), cp the channel pair.
   float a[2][MI], b[2][NJ];
   auto read_step = [&](int buf, int st) {
@@ -468,6 +472,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + e0 * WS + i * 32];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + ob];
+    } else if constexpr (S2B) {
+      // weight tap (r, s): LDS slot 8 - (3 r + s) (the backward rotation);
+      // g at tile offset ((ph + 1 - r) / 2 + 1, (pw + 1 - s) / 2 + 1)
+      const int cp = st / 9, r = (st % 9) / 3, s = st % 3;
+      const int tr = ((r != 1) + 1 - r) / 2 + 1, ts = ((s != 1) + 1 - s) / 2 + 1;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        a[buf][i] = ws[aoff + (2 * cp * 9 + 8 - (3 * r + s)) * WS + i * 32];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + tr * RS + ts];
     } else {
       const int cp = st / 9, r = (st % 9) / 3, s = st % 3;
 #pragma unroll
@@ -486,13 +500,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       bias_s[i] = (bias != nullptr && i < co_n) ? bias[co0 + i] : 0.f;
     __syncthreads();
   }
-  f32x16 acc[MI][NJ];
+  // (S2B: parity class c's tiles are acc[c * MI + i])
+  f32x16 acc[NACC * MI][NJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < NACC * MI; ++i) {
     f32x16 init;
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      init[v] = MODE == kFwd ? bias_s[wco * (BCO / WCO) + i * 32 + acc_row(v, hi)] : 0.f;
+      init[v] = MODE == kFwd ? bias_s[wco * (BCO / WCO) + (i % MI) * 32 + acc_row(v, hi)] : 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
@@ -511,11 +526,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       // Keep the next step's LDS reads ahead of this step's MFMAs (the
       // scheduler would otherwise sink them next to their use).
       __builtin_amdgcn_sched_barrier(0);
+      // S2B: the parity class of this step's tap picks the accumulator set
+      const int c = S2B ? 2 * ((st % 9) / 3 != 1) + (st % 3 != 1) : 0;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = mfma_32x32x2_f32(a[cur][i], b[cur][j], acc[i][j]);
+          acc[c * MI + i][j] = mfma_32x32x2_f32(a[cur][i], b[cur][j], acc[c * MI + i][j]);
     }
   }
 
@@ -573,6 +590,44 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
             buffer_store4(dview_b, xo[v - v0], 0u,
                           acc[i][j][v] * act_slope(kActSilu, xe[v - v0] * ps_s[e] + pt_s[e]));
           }
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (S2B) {
+    // parity class c = (ph, pw) writes pixel (h, w) of g's grid to
+    // (2h + ph, 2w + pw) of the 2H x 2W dx
+    const uint32_t plane2 = 4u * (uint32_t)H * (uint32_t)W;  // dx plane, floats
+    const bool bufst = od_bytes != 0 && co_n == BCO;
+    const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wpx * (BM / WPX) + j * 32 + l32;
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      const bool keep = n < N && h < H && w < W;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t pix = (uint32_t)((2 * h + (c >> 1)) * (2 * W) + 2 * w + (c & 1));
+        if (bufst) {
+          const uint32_t off =
+              keep ? (((uint32_t)n * ocs + cw + 4 * hi) * plane2 + pix) * 4u : kOutside;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane2 * 4u,
+                            acc[c * MI + i][j][v]);
+        } else if (keep) {
+          float* out = od + (long)n * ocs * plane2 + pix;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int co = cw + i * 32 + acc_row(v, hi);
+              if (co < ocs) out[(long)co * plane2] = acc[c * MI + i][j][v];
+            }
         }
       }
     }
@@ -646,49 +701,60 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 // Host launcher: dispatch the plan's tile to its instantiation.
 
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
-static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const float* wt,
+static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const float* wt,
                        const float* bias, Split<float> dst, int N, int Cin, int Cout, int H,
                        int W, const ActArgs& a, hipStream_t stream) {
   constexpr int CB = 8;
+  const bool s2b = MODE == kBwdData && a.s2;
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets); otherwise both take the plain-store path.
+  // A stride-2 backward-data runs its parity classes over g's H/2 x W/2
+  // grid (the kernel's H, W); H, W here are dx's.
+  const int kH = s2b ? H / 2 : H, kW = s2b ? W / 2 : W;
   const long hw4 = (long)H * W * 4;
   // output plane bytes (a stride-2 forward writes an H/2 x W/2 output)
-  const long ohw4 = a.s2 ? (long)(H / 2) * (W / 2) * 4 : hw4;
+  const long ohw4 = (MODE == kFwd && a.s2) ? hw4 / 4 : hw4;
   const long ob0 = (long)N * dst.c0 * ohw4, ob1 = (long)N * (Cout - dst.c0) * ohw4;
   const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
-  const long shw4 = (a.up2 || a.zi2) ? hw4 / 4 : hw4;  // source plane bytes
+  const long shw4 = (a.up2 || s2b) ? hw4 / 4 : hw4;  // source plane bytes
   const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * shw4) : 0u;
   const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * shw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_, PC_, UP_, ZI_, S2_)                                                 \
+#define CONV3X3_L(VEC_, PRO_, PC_, UP_, S2B_, S2_)                                                \
   hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_,   \
-                                     ZI_, S2_>),                                                  \
+                                     S2B_, S2_>),                                                 \
                      grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
-                     Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,       \
+                     Cin, Cout, kH, kW, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,     \
                      a.zout, a.zsrc, a.pscale, a.pshift, a.px)
   // packed taps: the forward of a 3- or 4-channel single tensor
   const int pc =
       (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.s2 && src.c0 == Cin) ? Cin : 0;
   constexpr bool kF = MODE == kFwd;
+  // one 32 x 32 MFMA tile per wave (64 x 64 workgroup tiles), so that the
+  // four accumulator sets of a stride-2 backward-data fit
+  constexpr bool one_tile = BCO / (32 * WCO) * (IMGS * TH * TW) / (32 * (4 / WCO)) == 1;
   if (a.s2) {
-    if (vec)
-      CONV3X3_L(true, false, 0, false, false, kF);
-    else
-      CONV3X3_L(false, false, 0, false, false, kF);
+    if constexpr (kF) {
+      if (vec)
+        CONV3X3_L(true, false, 0, false, false, true);
+      else
+        CONV3X3_L(false, false, 0, false, false, true);
+    } else if constexpr (one_tile) {
+      if (vec)
+        CONV3X3_L(true, false, 0, false, true, false);
+      else
+        CONV3X3_L(false, false, 0, false, true, false);
+    } else {
+      return false;  // the planner gives stride-2 backward-data 64 x 64 tiles
+    }
   } else if (a.up2) {
     if (vec)
       CONV3X3_L(true, false, 0, kF, false, false);
     else
       CONV3X3_L(false, false, 0, kF, false, false);
-  } else if (a.zi2) {
-    if (vec)
-      CONV3X3_L(true, false, 0, false, !kF, false);
-    else
-      CONV3X3_L(false, false, 0, false, !kF, false);
   } else if (a.pscale) {
     if (vec)
       CONV3X3_L(true, true, 0, false, false, false);
@@ -705,6 +771,7 @@ static void launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
       CONV3X3_L(false, false, 0, false, false, false);
   }
 #undef CONV3X3_L
+  return true;
 }
 
 template <int MODE>
@@ -715,9 +782,8 @@ static bool launch_mode(const Plan& pl, bool vec, Split<const float> src, const 
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                               \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&              \
       pl.wave_co == WCO_) {                                                                 \
-    launch_cfg<MODE, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin, Cout, \
-                                                 H, W, a, s);                               \
-    return true;                                                                            \
+    return launch_cfg<MODE, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin, \
+                                                        Cout, H, W, a, s);                  \
   }
   CONV3X3_FWD_F32_CONFIGS(CONV3X3_X)
 #undef CONV3X3_X

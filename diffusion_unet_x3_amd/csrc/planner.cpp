@@ -104,7 +104,12 @@ bool plan(const Problem& p, Plan* out) {
     };
     Cand cands[3];
     int ncand;
-    if (p.dtype == kF32) {
+    if (p.dtype == kF32 && p.stride2 && p.pass == kBwdData) {
+      // stride-2 backward-data: four accumulator sets per wave (one per
+      // output parity class) fit only with one 32 x 32 tile per wave
+      cands[0] = Cand{64, 64, 2, 4};
+      ncand = 1;
+    } else if (p.dtype == kF32) {
       cands[0] = cout <= 64 ? Cand{256, 64, 1, 4} : Cand{128, 128, 2, 4};
       cands[1] = Cand{64, 64, 2, 4};
       ncand = 2;
@@ -187,7 +192,8 @@ bool plan(const Problem& p, Plan* out) {
     }
     pl.threads = 64 * cands[pick].nw;
     pl.lds_bytes = p.dtype == kF32
-        ? (p.stride2 ? fwd_f32_s2_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
+        ? (p.stride2 && p.pass == kFwd
+               ? fwd_f32_s2_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
                      : fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co))
         : fwd_bf16_lds_bytes(pl.imgs, pl.th, pl.tw, pl.tile_co);
     if (p.pass == kFwd) pl.lds_bytes += 4 * pl.tile_co;  // the tile's biases

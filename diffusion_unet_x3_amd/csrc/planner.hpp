@@ -54,9 +54,9 @@ struct Problem {
   // reduction may be split over several workgroups per output tile (partial
   // sums in the workspace, then a fixed-order reduce)
   bool allow_split = false;
-  // float32 forward / backward-weight of a stride-2 convolution: H, W are
-  // the output's (g's); the x tile holds 2 th + 1 input rows of 2 tw + 1
-  // columns
+  // float32 stride-2 convolution, H, W being the output's (g's): the forward
+  // and backward-weight x tiles hold 2 th + 1 input rows of 2 tw + 1
+  // columns; backward-data takes 64 x 64 tiles (four accumulator sets)
   bool stride2 = false;
 };
 
