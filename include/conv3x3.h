@@ -324,12 +324,13 @@ int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, v
  * y[n,k,h,w] = bias[k] + sum x[n,c,2h+r-1,2w+s-1] w[k,c,r,s].  H, W are x's
  * sizes and must be even; y, g are [N][K][H/2][W/2]; dx is [N][C][H][W];
  * backward-weight takes the workspace of conv3x3_bwd_weight_workspace_size
- * (N, C, K, H, W, dtype).  The kernels are the stride-1 ones on the full
- * grid: the forward stores only its even pixels, the backward passes read g
- * zero-inserted into the full grid as they stage it -- three quarters of
- * their MFMA work multiplies zeros or is discarded (a first version; the
- * pixel-parity decomposition would remove it).  float32 only
- * (CONV3X3_ERR_UNSUPPORTED for bfloat16).
+ * (N, C, K, H, W, dtype) (its plan over the H/2 x W/2 grid never needs
+ * more).  The forward and backward-weight tile the H/2 x W/2 output and
+ * stage x at stride 2; backward-data tiles g's grid and computes the four
+ * output-pixel parity classes (dx[2i + ph, 2j + pw] takes the taps r = 1 for
+ * ph = 0, r = 0 and 2 for ph = 1, likewise s and pw) from one staged tile.
+ * No pass multiplies inserted zeros.  float32 only (CONV3X3_ERR_UNSUPPORTED
+ * for bfloat16).
  */
 int conv3x3_fwd_s2(const void* x, const void* w, const float* bias, float* y, int N, int C,
                    int K, int H, int W, int dtype, conv3x3_stream_t stream);

@@ -1,8 +1,12 @@
 """GPU parity of the stride-2 entry points (conv3x3_*_s2, a UNet's
 downsample block) against the oracle, through the C ABI.  Same float32 bar
 as the plain passes (2e-5; exact on integer inputs), on small and ragged
-shapes in full (vector and scalar staging) and on the three UNet downsample
-layers by sampled elements."""
+shapes in full and on the three UNet downsample layers by sampled elements.
+The shapes reach the vector staging (W % 8 == 0, 16-byte aligned) and the
+scalar one, output grids wider than one tile (the left halo column of the
+stride-2 x tile is loaded), ragged channel fills and tiles, several images
+per block, and g grids with odd sizes (every output-pixel parity class of
+backward-data gets a ragged edge)."""
 import numpy as np
 import pytest
 import torch
@@ -42,7 +46,8 @@ def _run(inp):
 
 # (N, C, K, H, W) of the input; H, W even
 SHAPES = [(2, 64, 64, 32, 32), (2, 8, 16, 8, 12), (1, 3, 5, 6, 10), (2, 17, 33, 10, 14),
-          (2, 32, 48, 16, 80), (1, 16, 24, 4, 136), (4, 128, 64, 16, 16)]
+          (2, 32, 48, 16, 80), (1, 16, 24, 4, 136), (4, 128, 64, 16, 16),
+          (3, 24, 40, 18, 40), (2, 72, 136, 8, 8), (1, 8, 8, 2, 2)]
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
