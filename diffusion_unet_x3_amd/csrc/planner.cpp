@@ -150,21 +150,22 @@ bool plan(const Problem& p, Plan* out) {
     }
     // bf16 with a workspace: when the eight-wave 256 x 128 tile leaves the
     // device short of workgroups (small images) and the reduction is long
-    // (>= 64 fills of 16 channels), keep that tile and split the reduction
+    // (>= 32 fills of 16 channels), keep that tile and split the reduction
     // instead of falling back to the smaller tiles, which re-stage all the
     // weights for every pixel tile.  The split stays within one round of
-    // workgroups and keeps at least 8 fills per slice (measured: shorter
-    // reductions and a second round of workgroups both lose to the small
-    // tiles).
+    // workgroups, keeps at least 8 fills per slice and must bring the grid
+    // to three quarters of a round (measured: shorter reductions, a second
+    // round of workgroups and split grids of half a round all lose to the
+    // small tiles; 48- and 56-fill reductions on 16x16 images gain 10-16%).
     int split = 1;
     const int cin = p.pass == kFwd ? p.C : p.K;
     const int fills = ceil_div(cin, 16);
     if (p.allow_split && p.dtype == kBF16 && cout > 64 && wgs[0] > 0 && wgs[0] < kMinWGs &&
-        fills >= 64 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
+        fills >= 32 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
       int s = kMinWGs / wgs[0];
       if (s > fills / 8) s = fills / 8;
       if (s > 8) s = 8;
-      if (s >= 2) {
+      if (s >= 2 && wgs[0] * s >= 3 * kMinWGs / 4) {
         pick = 0;
         split = s;
       }

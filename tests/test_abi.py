@@ -237,8 +237,10 @@ def test_split_workspace_checks():
     bf16 = lib3.CONV3X3_BF16
     need = lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, bf16)
     assert need == 8 * (32 * 512 * 64 * 4)  # eight float32 output-sized slots
-    # backward-data's reduction (K = 512) is too short to split
-    assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, *d, bf16) == 0
+    # a 16-fill reduction (K = 256) is too short to split
+    assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 1024, 256, 8, 8, bf16) == 0
+    # a split that would leave the grid at half a round is not taken
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 1024, 512, 8, 8, bf16) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 512, 1024, 8, 8, bf16) == need
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, lib3.CONV3X3_F32) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 64, 512, 512, 16, 16, bf16) == 0

@@ -15,11 +15,13 @@ from parity_util import TRIPWIRE, rel_err
 
 pytestmark = pytest.mark.gpu
 
-# (N, C, K, H, W): a few output tiles and a long reduction (>= 64 fills of
-# 16 channels): forward splits with C >= 1024, backward-data with K >= 1024;
-# 1032 channels leave a partly filled last fill and a short last slice
-SHAPES = [(4, 1024, 512, 8, 8), (8, 1024, 256, 8, 8), (4, 2048, 128, 8, 8),
-          (4, 1024, 128, 16, 16), (4, 256, 1024, 8, 8), (4, 1032, 256, 8, 8)]
+# (N, C, K, H, W): few output tiles and a long reduction.  1032 channels
+# leave a partly filled last fill and a short last slice.
+# Shapes that take a split plan in forward and / or backward-data: 8x8 and
+# 16x16 images, 32 to 65 fills (1032 channels: a ragged last fill), split
+# grids of 192 and 256 workgroups.
+SHAPES = [(32, 1024, 512, 8, 8), (24, 1032, 512, 8, 8), (24, 1024, 128, 16, 16),
+          (48, 256, 1024, 8, 8), (32, 512, 384, 16, 16)]
 
 
 def _run(inp, split, out_dtype=None):
@@ -59,7 +61,9 @@ def test_split_reduction_full_compare(shape, integer):
 def test_split_reduction_bf16_outputs():
     """The reduce kernel writes bfloat16 outputs too (integer inputs:
     exactly the oracle rounded to bfloat16)."""
-    layer = wl.small_layer(4, 1024, 256, 8, 8, dtype="bf16", seed=73)
+    import diffusion_unet_x3_amd as lib3
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 48, 1024, 256, 8, 8, lib3.CONV3X3_BF16) > 0
+    layer = wl.small_layer(48, 1024, 256, 8, 8, dtype="bf16", seed=73)
     inp = wl.make_inputs(layer, integer_exact=True)
     y, dx = _run(inp, split=True, out_dtype=torch.bfloat16)
     assert np.array_equal(y, oracle.round_to_bf16(oracle.conv3x3_fwd(inp["x"], inp["w"],
