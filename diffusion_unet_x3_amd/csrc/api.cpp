@@ -118,9 +118,11 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
   if (pr.on() && (y == pr.scale || y == pr.shift)) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  // a stride-2 forward tiles its H/2 x W/2 output
-  Problem pb{kFwd, kdt(dtype), N, C, K, geom == 2 ? H / 2 : H, geom == 2 ? W / 2 : W, x.c0};
+  // a stride-2 forward tiles its H/2 x W/2 output, an upsampling one the
+  // H/2 x W/2 input (each tile computing the four output parity classes)
+  Problem pb{kFwd, kdt(dtype), N, C, K, geom ? H / 2 : H, geom ? W / 2 : W, x.c0};
   pb.stride2 = geom == 2;
+  pb.quad = geom == 1;
   pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
@@ -142,7 +144,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
     // (3 input channels in one tensor: the packed-tap forward, vector x
     // loads and scalar weight loads)
     const bool pack3 = C == 3 && x.c0 == C && !pr.on();
-    const bool vec = W % 4 == 0 && ((C % 4 == 0 && x.c0 % 4 == 0) || pack3) &&
+    // (upsampling: the staged rows are the small input's, W/2 floats)
+    const bool vec = W % (geom == 1 ? 8 : 4) == 0 && ((C % 4 == 0 && x.c0 % 4 == 0) || pack3) &&
                      parts_aligned(x) && aligned16(w) && buffer_sized(2L * N * C * hw) &&
                      buffer_sized(2L * K * C * 9);
     Split<const float> xs{(const float*)x.p0, (const float*)x.p1, x.c0};
@@ -187,7 +190,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   // stride 2: the plan tiles g's H/2 x W/2 grid; each tile computes the four
   // output-pixel parity classes of its pixels
   Problem pb{kBwdData, kdt(dtype), N, C, K, s2 ? H / 2 : H, s2 ? W / 2 : W, dx.c0};
-  pb.stride2 = s2;
+  pb.quad = s2;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))

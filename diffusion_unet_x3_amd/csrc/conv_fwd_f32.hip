@@ -43,10 +43,17 @@ namespace conv3x3 {
 // step -- ceil(9 PC / 2) steps instead of the 36 of an 8-channel fill.  The
 // tile's weights w[co0 .. co0 + BCO - 1, 0..PC-1, 0..8] are one contiguous
 // run of BCO * 9 PC floats, staged with 16-byte loads.
-// UP2 (forward): the source is upsampled 2x by nearest neighbour as it is
-// staged -- H and W are the upsampled (output) sizes, the source tensor is
-// H/2 x W/2, and staged pixel (h, w) reads source pixel (h/2, w/2); a vector
-// item of four output columns is two source floats, each used twice.
+// UP2 (forward of a convolution of the 2x nearest-upsampled input; H, W are
+// the small input's sizes, y is 2H x 2W): output row 2i + ph reads
+// upsampled rows 2i + ph - 1 .. 2i + ph + 1, i.e. small rows i - 1 and i
+// (ph = 0; kernel rows {0}, {1, 2}) or i and i + 1 (ph = 1; rows {0, 1},
+// {2}), and likewise for columns.  So each output parity class (ph, pw) is
+// a 2x2-tap convolution of the small input whose weights are sums of the
+// 3x3 taps: 16 (class, tap) pairs instead of the 36 that the upsampled
+// grid needs per small pixel.  The block tiles the small grid, stages x
+// with its halo as a plain forward does, keeps one accumulator set per
+// class, sums each pair's taps as it reads them, and stores each set to its
+// class's pixels.
 // S2B (backward-data of a stride-2 convolution; H, W are g's sizes, dx is
 // 2H x 2W): dx[2i + ph, 2j + pw] receives only the taps (r, s) with r = 1
 // for ph = 0 and r = 0, 2 for ph = 1 (the same for s and pw), tap r reading
@@ -88,12 +95,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   static_assert(!S2B || (MODE == kBwdData && !PRO && PC == 0 && !UP2),
                 "stride-2 parity classes: plain backward-data only");
   static_assert(!S2 || (MODE == kFwd && PC == 0 && !PRO && !UP2), "stride 2: plain forward only");
-  // source rows and columns (the full grid's halves with UP2)
-  const int Hs = UP2 ? H / 2 : H, Ws = UP2 ? W / 2 : W;
   // output rows and columns (the pixel grid the blocks tile)
   const int OH = S2 ? H / 2 : H, OW = S2 ? W / 2 : W;
-  constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * 9;
-  constexpr int NACC = S2B ? 4 : 1;  // accumulator sets (S2B: one per parity class)
+  constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * (UP2 ? 16 : 9);
+  constexpr int NACC = (S2B || UP2) ? 4 : 1;  // accumulator sets (one per parity class)
 
   __shared__ __attribute__((aligned(16))) float xs[CB * PL];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
@@ -229,16 +234,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 4 * q;
         const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w < W;
-        if constexpr (UP2) {
-          // four upsampled columns from two source floats, each used twice
-          const uint32_t so =
-              ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + h / 2) * Ws + w / 2)
-                 : kOutside;
-          float xa, xb;
-          buffer_load_2f(sview, so, xa, xb);
-          xv[k] = f32x4{xa, xa, xb, xb};
-          continue;
-        }
         const uint32_t off =
             ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xv[k] = __builtin_bit_cast(f32x4, buffer_load16(sview, off));
@@ -263,11 +258,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         const int w = S2 ? 2 * o.w0 - 1 : o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
-        constexpr bool half = UP2;
         const uint32_t off =
-            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * Hs + (half ? h / 2 : h)) * Ws +
-                                 (half ? w / 2 : w))
-               : kOutside;
+            ok ? 4u * (uint32_t)(((n * f.cs + f.cl0 + ch) * H + h) * W + w) : kOutside;
         xf[k] = __builtin_bit_cast(float, buffer_load4(sview, off));
         if (zs) zf[k] = __builtin_bit_cast(float, buffer_load4(zview, off));
         if constexpr (pro) {
@@ -413,9 +405,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int slot = S2 ? ((cc & 1) ? kS2Odd + (cc + 1) / 2 : EV + cc / 2) : 4 + cc;
           float v = 0.f;
           if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W) {
-            const long e = UP2
-                ? ((long)n * f.cs + f.cl0 + ch) * Hs * Ws + (long)(h / 2) * Ws + w / 2
-                : ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
+            const long e = ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
             v = sp[e];
             if (zs) v *= act_slope(act, zsrc[e]);
             if constexpr (pro) {
@@ -472,6 +462,26 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + e0 * WS + i * 32];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + ob];
+    } else if constexpr (UP2) {
+      // step q of channel pair cp: class c = (ph, pw) = q % 4 (consecutive
+      // steps feed different accumulators), small-grid tap (u, v) = q / 4;
+      // kernel rows rlo..rhi and columns slo..shi land on that tap
+      const int cp = st / 16, q = st % 16;
+      const int ph = (q >> 1) & 1, pw = q & 1, u = q >> 3, v = (q >> 2) & 1;
+      const int rlo = ph ? 2 * u : u, rhi = ph ? 1 + u : 2 * u;
+      const int slo = pw ? 2 * v : v, shi = pw ? 1 + v : 2 * v;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        float sum = 0.f;
+#pragma unroll
+        for (int r = rlo; r <= rhi; ++r)
+#pragma unroll
+          for (int s = slo; s <= shi; ++s) sum += ws[aoff + (2 * cp * 9 + 3 * r + s) * WS + i * 32];
+        a[buf][i] = sum;
+      }
+      // small row i + u + ph - 1 = tile row row + u + ph (likewise columns)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + (u + ph) * RS + v + pw];
     } else if constexpr (S2B) {
       // weight tap (r, s): LDS slot 8 - (3 r + s) (the backward rotation);
       // g at tile offset ((ph + 1 - r) / 2 + 1, (pw + 1 - s) / 2 + 1)
@@ -526,8 +536,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       // Keep the next step's LDS reads ahead of this step's MFMAs (the
       // scheduler would otherwise sink them next to their use).
       __builtin_amdgcn_sched_barrier(0);
-      // S2B: the parity class of this step's tap picks the accumulator set
-      const int c = S2B ? 2 * ((st % 9) / 3 != 1) + (st % 3 != 1) : 0;
+      // S2B: the parity class of this step's tap picks the accumulator set;
+      // UP2: the class of this step
+      const int c = S2B ? 2 * ((st % 9) / 3 != 1) + (st % 3 != 1) : UP2 ? st % 4 : 0;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -595,10 +606,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     }
     return;
   }
-  if constexpr (S2B) {
-    // parity class c = (ph, pw) writes pixel (h, w) of g's grid to
-    // (2h + ph, 2w + pw) of the 2H x 2W dx
-    const uint32_t plane2 = 4u * (uint32_t)H * (uint32_t)W;  // dx plane, floats
+  if constexpr (S2B || UP2) {
+    // parity class c = (ph, pw) writes pixel (h, w) of the tiled grid to
+    // (2h + ph, 2w + pw) of the 2H x 2W output
+    const uint32_t plane2 = 4u * (uint32_t)H * (uint32_t)W;  // output plane, floats
     const bool bufst = od_bytes != 0 && co_n == BCO;
     const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
 #pragma unroll
@@ -709,9 +720,11 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets); otherwise both take the plain-store path.
-  // A stride-2 backward-data runs its parity classes over g's H/2 x W/2
-  // grid (the kernel's H, W); H, W here are dx's.
-  const int kH = s2b ? H / 2 : H, kW = s2b ? W / 2 : W;
+  // A stride-2 backward-data and an upsampling forward run their parity
+  // classes over the H/2 x W/2 grid of g or x (the kernel's H, W); H, W here
+  // are the output's.
+  const bool quad = s2b || (MODE == kFwd && a.up2);
+  const int kH = quad ? H / 2 : H, kW = quad ? W / 2 : W;
   const long hw4 = (long)H * W * 4;
   // output plane bytes (a stride-2 forward writes an H/2 x W/2 output)
   const long ohw4 = (MODE == kFwd && a.s2) ? hw4 / 4 : hw4;
@@ -734,7 +747,8 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
       (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.s2 && src.c0 == Cin) ? Cin : 0;
   constexpr bool kF = MODE == kFwd;
   // one 32 x 32 MFMA tile per wave (64 x 64 workgroup tiles), so that the
-  // four accumulator sets of a stride-2 backward-data fit
+  // four accumulator sets of a stride-2 backward-data or an upsampling
+  // forward fit
   constexpr bool one_tile = BCO / (32 * WCO) * (IMGS * TH * TW) / (32 * (4 / WCO)) == 1;
   if (a.s2) {
     if constexpr (kF) {
@@ -751,10 +765,14 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
       return false;  // the planner gives stride-2 backward-data 64 x 64 tiles
     }
   } else if (a.up2) {
-    if (vec)
-      CONV3X3_L(true, false, 0, kF, false, false);
-    else
-      CONV3X3_L(false, false, 0, kF, false, false);
+    if constexpr (kF && one_tile) {
+      if (vec)
+        CONV3X3_L(true, false, 0, true, false, false);
+      else
+        CONV3X3_L(false, false, 0, true, false, false);
+    } else {
+      return false;  // the planner gives the upsampling forward 64 x 64 tiles
+    }
   } else if (a.pscale) {
     if (vec)
       CONV3X3_L(true, true, 0, false, false, false);

@@ -104,9 +104,9 @@ bool plan(const Problem& p, Plan* out) {
     };
     Cand cands[3];
     int ncand;
-    if (p.dtype == kF32 && p.stride2 && p.pass == kBwdData) {
-      // stride-2 backward-data: four accumulator sets per wave (one per
-      // output parity class) fit only with one 32 x 32 tile per wave
+    if (p.dtype == kF32 && p.quad) {
+      // four accumulator sets per wave (one per output parity class) fit
+      // only with one 32 x 32 tile per wave
       cands[0] = Cand{64, 64, 2, 4};
       ncand = 1;
     } else if (p.dtype == kF32) {

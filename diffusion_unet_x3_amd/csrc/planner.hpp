@@ -54,10 +54,13 @@ struct Problem {
   // reduction may be split over several workgroups per output tile (partial
   // sums in the workspace, then a fixed-order reduce)
   bool allow_split = false;
-  // float32 stride-2 convolution, H, W being the output's (g's): the forward
-  // and backward-weight x tiles hold 2 th + 1 input rows of 2 tw + 1
-  // columns; backward-data takes 64 x 64 tiles (four accumulator sets)
+  // float32 stride-2 forward / backward-weight, H, W being the output's
+  // (g's): the x tiles hold 2 th + 1 input rows of 2 tw + 1 columns
   bool stride2 = false;
+  // float32 passes that keep one accumulator set per output-pixel parity
+  // class (stride-2 backward-data, upsampling forward; H, W the grid they
+  // tile): 64 x 64 tiles, one 32 x 32 MFMA tile per wave and set
+  bool quad = false;
 };
 
 bool plan(const Problem& p, Plan* out);
