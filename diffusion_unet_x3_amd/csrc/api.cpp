@@ -165,8 +165,10 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
 int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx, int N, int C,
                   int K, int H, int W, int dtype, int act, conv3x3_stream_t stream,
                   Prologue pr = Prologue(), const void* px = nullptr, bool ws_call = false,
-                  void* ws = nullptr, size_t ws_bytes = 0, bool s2 = false) {
-  // s2 (stride 2): H, W are dx's; g is H/2 x W/2
+                  void* ws = nullptr, size_t ws_bytes = 0, int geom = 0) {
+  // geom 1 (upsampling): H, W are g's, dx is H/2 x W/2; geom 2 (stride 2):
+  // H, W are dx's, g is H/2 x W/2
+  const bool s2 = geom == 2;
   if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
   if (pr.on() && !px) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
@@ -187,10 +189,12 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   // du's epilogue reads x through a 32-bit buffer view, like the stores
   if (pr.on() && 4L * N * C * H * W >= 2147483648L) return CONV3X3_ERR_UNSUPPORTED;
   Plan pl;
-  // stride 2: the plan tiles g's H/2 x W/2 grid; each tile computes the four
-  // output-pixel parity classes of its pixels
-  Problem pb{kBwdData, kdt(dtype), N, C, K, s2 ? H / 2 : H, s2 ? W / 2 : W, dx.c0};
+  // stride 2: the plan tiles g's H/2 x W/2 grid, each tile computing the
+  // four output-pixel parity classes of its pixels; upsampling: it tiles
+  // dx's H/2 x W/2 grid and stages g at stride 2
+  Problem pb{kBwdData, kdt(dtype), N, C, K, geom ? H / 2 : H, geom ? W / 2 : W, dx.c0};
   pb.quad = s2;
+  pb.stride2 = geom == 1;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
@@ -207,6 +211,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   a.pshift = pr.shift;
   a.px = (const float*)px;
   a.s2 = s2;
+  a.up2 = geom == 1;
   const long hw = (long)H * W;
   bool ok;
   if (dtype == CONV3X3_F32) {
@@ -504,8 +509,7 @@ int check_up2(int N, int C, int K, int H, int W, int dtype) {
 size_t conv3x3_up2_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype) {
   if (pass < CONV3X3_PASS_FWD || pass > CONV3X3_PASS_BWD_WEIGHT) return (size_t)-1;
   if (check_up2(N, C, K, H, W, dtype)) return (size_t)-1;
-  if (pass == CONV3X3_PASS_FWD) return 0;
-  if (pass == CONV3X3_PASS_BWD_DATA) return (size_t)N * C * 4 * H * W * sizeof(float);
+  if (pass == CONV3X3_PASS_FWD || pass == CONV3X3_PASS_BWD_DATA) return 0;
   Plan pl;
   if (!plan(Problem{kBwdWeight, kdt(dtype), N, C, K, 2 * H, 2 * W}, &pl)) return (size_t)-1;
   return pl.workspace_bytes;
@@ -523,22 +527,14 @@ int conv3x3_fwd_up2(const void* x, const void* w, const float* bias, float* y, i
 int conv3x3_bwd_data_up2(const void* g, const void* w, float* dx, void* workspace,
                          size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
                          conv3x3_stream_t stream) {
+  (void)workspace;  // none needed (kept for the calling convention)
+  (void)workspace_bytes;
   if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
-  int rc = check_up2(N, C, K, H, W, dtype);
+  const int rc = check_up2(N, C, K, H, W, dtype);
   if (rc) return rc;
-  const size_t need = (size_t)N * C * 4 * H * W * sizeof(float);
-  if (!workspace || workspace_bytes < need) return CONV3X3_ERR_WORKSPACE;
-  if (workspace == g || workspace == w || workspace == (void*)dx || (const void*)dx == g ||
-      (const void*)dx == w)
-    return CONV3X3_ERR_ALIAS;
-  // the gradient at the upsampled resolution into the workspace, then the
-  // 2x2 block sums into dx
-  float* big = (float*)workspace;
-  rc = bwd_data_impl(g, nullptr, w, one(big, C), N, C, K, 2 * H, 2 * W, dtype, CONV3X3_ACT_NONE,
-                     stream);
-  if (rc) return rc;
-  launch_downsum2(big, dx, (long)N * C, H, W, reinterpret_cast<hipStream_t>(stream));
-  return launch_status();
+  // one pass over dx's grid: each pixel gathers g's 4 x 4 window at stride 2
+  return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, 2 * H, 2 * W, dtype, CONV3X3_ACT_NONE,
+                       stream, Prologue(), nullptr, false, nullptr, 0, 1);
 }
 
 int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, void* workspace,
@@ -581,7 +577,7 @@ int conv3x3_bwd_data_s2(const void* g, const void* w, float* dx, int N, int C, i
   const int rc = check_s2(N, C, K, H, W, dtype);
   if (rc) return rc;
   return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, H, W, dtype, CONV3X3_ACT_NONE, stream,
-                       Prologue(), nullptr, false, nullptr, 0, true);
+                       Prologue(), nullptr, false, nullptr, 0, 2);
 }
 
 int conv3x3_bwd_weight_s2(const void* x, const void* g, float* dw, float* db, void* workspace,

@@ -68,8 +68,18 @@ namespace conv3x3 {
 // reads input pixel (2 ho + r - 1, 2 wo + s - 1).  The block's 2 TH + 1 input
 // rows are staged with their columns split by parity (odd columns, then even
 // ones), so that each tap's operand read is unit-stride across the lanes.
+// U2B (backward-data of a convolution of the 2x nearest-upsampled input; H,
+// W are g's sizes, dx is H/2 x W/2): dx[i, j] sums the upsampled-grid
+// gradient over its 2x2 block, i.e. g rows 2i - 1 .. 2i + 2 and columns
+// 2j - 1 .. 2j + 2, row offset d taking kernel rows {2}, {1, 2}, {0, 1},
+// {0} for d = -1, 0, 1, 2 (likewise columns): a stride-2 convolution of g
+// with a 4 x 4 kernel of summed taps, 16 MFMA steps per pixel and channel
+// pair instead of 36 plus a 2x2 block sum.  The block tiles dx's grid and
+// stages g like the S2 forward stages x, with one more row and one more
+// even column (2 w0 + 2 TW).
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
-          bool PRO = false, int PC = 0, bool UP2 = false, bool S2B = false, bool S2 = false>
+          bool PRO = false, int PC = 0, bool UP2 = false, bool S2B = false, bool S2 = false,
+          bool U2B = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -85,19 +95,26 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int NJ = BM / (32 * WPX);   // 32x32 tiles per wave along pixels
   static_assert(MI >= 1 && NJ >= 1 && MI * 32 * WCO == BCO && NJ * 32 * WPX == BM,
                 "tile does not split into 32x32 wave tiles");
-  constexpr int RS = S2 ? fwd_f32_s2_rs(TW) : fwd_f32_rs(TW);
-  constexpr int PL = S2 ? fwd_f32_s2_plane(IMGS, TH, TW) : fwd_f32_plane(IMGS, TH, TW);
+  // S2 and U2B stage their source at stride 2 with parity-split columns
+  constexpr bool STR2 = S2 || U2B;
+  constexpr int RS = S2 ? fwd_f32_s2_rs(TW) : U2B ? fwd_f32_u2b_rs(TW) : fwd_f32_rs(TW);
+  constexpr int PL = S2    ? fwd_f32_s2_plane(IMGS, TH, TW)
+                     : U2B ? fwd_f32_u2b_plane(IMGS, TH, TW)
+                           : fwd_f32_plane(IMGS, TH, TW);
   constexpr int WS = fwd_f32_wstride(BCO);
-  constexpr int HR = S2 ? 2 * TH + 1 : TH + 2;  // staged rows per image (with halo)
-  constexpr int EV = fwd_f32_s2_even(TW);       // S2: row offset of the even columns
+  // staged rows per image (with halo)
+  constexpr int HR = S2 ? 2 * TH + 1 : U2B ? 2 * TH + 2 : TH + 2;
+  constexpr int EV = fwd_f32_s2_even(TW);  // S2, U2B: row offset of the even columns
   static_assert(PC == 0 || (MODE == kFwd && VEC && PC < CB), "packed taps: forward only");
   static_assert(!UP2 || (MODE == kFwd && PC == 0 && !PRO), "upsampling: plain forward only");
   static_assert(!S2B || (MODE == kBwdData && !PRO && PC == 0 && !UP2),
                 "stride-2 parity classes: plain backward-data only");
   static_assert(!S2 || (MODE == kFwd && PC == 0 && !PRO && !UP2), "stride 2: plain forward only");
+  static_assert(!U2B || (MODE == kBwdData && PC == 0 && !PRO && !S2B),
+                "upsampling: plain backward-data only");
   // output rows and columns (the pixel grid the blocks tile)
-  const int OH = S2 ? H / 2 : H, OW = S2 ? W / 2 : W;
-  constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * (UP2 ? 16 : 9);
+  const int OH = STR2 ? H / 2 : H, OW = STR2 ? W / 2 : W;
+  constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * ((UP2 || U2B) ? 16 : 9);
   constexpr int NACC = (S2B || UP2) ? 4 : 1;  // accumulator sets (one per parity class)
 
   __shared__ __attribute__((aligned(16))) float xs[CB * PL];
@@ -147,14 +164,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   constexpr int XQ = TW / 4;
   constexpr int XV_ITEMS = CB * IMGS * HR * XQ;
   constexpr int XV_N = (XV_ITEMS + NT - 1) / NT;
-  constexpr int XH_ITEMS = CB * IMGS * HR * (S2 ? 1 : 2);
+  constexpr int XH_ITEMS = CB * IMGS * HR * (S2 ? 1 : 2);  // U2B: left and right
   constexpr int XH_N = (XH_ITEMS + NT - 1) / NT;
   // Scalar path: every column of the staged rows.
-  constexpr int XCOLS = S2 ? 2 * TW + 1 : TW + 2;
+  constexpr int XCOLS = S2 ? 2 * TW + 1 : U2B ? 2 * TW + 2 : TW + 2;
   constexpr int XS_ITEMS = CB * IMGS * HR * XCOLS;
   constexpr int XS_N = (XS_ITEMS + NT - 1) / NT;
   f32x4 xv[VEC ? XV_N : 1];
-  f32x4 xv2[VEC && S2 ? XV_N : 1];  // S2: the item's second float4
+  f32x4 xv2[VEC && STR2 ? XV_N : 1];  // S2, U2B: the item's second float4
   float xf[VEC ? XH_N : 1];
   // Backward-data with a fused activation: z at the same positions as the
   // gradient source; the source is multiplied by act'(z) when it is written
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int ch = t / IMGS;
-        if constexpr (S2) {
+        if constexpr (STR2) {
           // input row 2 h0 - 1 + rr, columns c .. c + 7
           const int n = o.n0 + img, h = 2 * o.h0 + rr - 1, c = 2 * o.w0 + 8 * q;
           const bool ok = (XV_ITEMS % NT == 0 || it < XV_ITEMS) && n < N && ch < f.cn &&
@@ -254,8 +271,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         t /= HR;
         const int img = t % IMGS;
         const int ch = t / IMGS;
-        const int n = o.n0 + img, h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
-        const int w = S2 ? 2 * o.w0 - 1 : o.w0 + (side ? TW : -1);
+        const int n = o.n0 + img, h = STR2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+        // (U2B: input columns 2 w0 - 1 and 2 w0 + 2 TW)
+        const int w = S2 ? 2 * o.w0 - 1
+                         : U2B ? 2 * o.w0 + (side ? 2 * TW : -1) : o.w0 + (side ? TW : -1);
         const bool ok = (XH_ITEMS % NT == 0 || it < XH_ITEMS) && n < N && ch < f.cn && h >= 0 &&
                         h < H && w >= 0 && w < W;
         const uint32_t off =
@@ -314,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         if (XV_ITEMS % NT == 0 || it < XV_ITEMS) {
           const int q = it % XQ;
           const int t = it / XQ;  // (ch * IMGS + img) * HR + rr
-          if constexpr (S2) {
+          if constexpr (STR2) {
             // columns c .. c + 7 = even 4q .. 4q + 3 and odd 4q + 1 .. 4q + 4
             const f32x4 u = xv[k], u2 = xv2[k];
             *reinterpret_cast<f32x4*>(&xs[t * RS + EV + 4 * q]) = f32x4{u.x, u.z, u2.x, u2.z};
@@ -344,6 +363,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
         if (XH_ITEMS % NT == 0 || it < XH_ITEMS) {
           if constexpr (S2) {
             xs[it * RS + kS2Odd] = xf[k];  // odd column 0 = input column 2 w0 - 1
+            continue;
+          }
+          if constexpr (U2B) {
+            // odd column 0 and even column TW
+            xs[(it >> 1) * RS + ((it & 1) ? EV + TW : kS2Odd)] = xf[k];
             continue;
           }
           const int side = it & 1;
@@ -398,11 +422,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
           const int img = (t / HR) % IMGS;
           const int ch = t / (HR * IMGS);
           const int n = o.n0 + img;
-          // S2: input column 2 w0 + cc, cc = -1 .. 2 TW - 1 (odd column
-          // (cc + 1) / 2 for even cc + 1, even column cc / 2 otherwise)
-          const int h = S2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
-          const int w = S2 ? 2 * o.w0 + cc : o.w0 + cc;
-          const int slot = S2 ? ((cc & 1) ? kS2Odd + (cc + 1) / 2 : EV + cc / 2) : 4 + cc;
+          // S2, U2B: input column 2 w0 + cc, cc = -1 .. 2 TW - 1 (U2B: .. 2 TW)
+          // (odd column (cc + 1) / 2 for even cc + 1, even column cc / 2
+          // otherwise)
+          const int h = STR2 ? 2 * o.h0 + rr - 1 : o.h0 + rr - 1;
+          const int w = STR2 ? 2 * o.w0 + cc : o.w0 + cc;
+          const int slot = STR2 ? ((cc & 1) ? kS2Odd + (cc + 1) / 2 : EV + cc / 2) : 4 + cc;
           float v = 0.f;
           if (n < N && ch < f.cn && h >= 0 && h < H && w >= 0 && w < W) {
             const long e = ((long)n * f.cs + f.cl0 + ch) * HW + (long)h * W + w;
@@ -442,14 +467,47 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   for (int j = 0; j < NJ; ++j) {
     const int p = wpx * (BM / WPX) + j * 32 + l32;
     const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
-    boff[j] = S2 ? hi * PL + (img * HR + 2 * row) * RS + col
+    boff[j] = STR2 ? hi * PL + (img * HR + 2 * row) * RS + col
                  : (PC ? 0 : hi * PL) + (img * HR + row) * RS + 4 + col - 1;
   }
   const int aoff = (PC ? hi : hi * 9) * WS + wco * (BCO / WCO) + l32;
 
 
+  // UP2 / U2B: the 3x3 taps summed into the weight of step q (kernel rows
+  // rlo..rhi, columns slo..shi) and the tile offset of its pixel operand.
+  // UP2: q % 4 = output class (ph, pw) -- consecutive steps feed different
+  // accumulator sets -- and q / 4 = small-grid tap (u, v); the kernel rows
+  // on small row i + u + ph - 1 = tile row row + u + ph are {0}, {1, 2} for
+  // ph = 0 and {0, 1}, {2} for ph = 1 (likewise columns).  U2B: g row offset
+  // ri - 1 = q / 4 - 1 and column offset si - 1 = q % 4 - 1 from (2i, 2j);
+  // kernel rows {2}, {1, 2}, {0, 1}, {0}; columns 2j - 1 .. 2j + 2 are odd
+  // j, even j, odd j + 1, even j + 1 of the staged tile.
+  struct TapSet {
+    int rlo, rhi, slo, shi, boff;
+  };
+  auto tap_set = [&](int q) {
+    TapSet t;
+    if constexpr (UP2) {
+      const int ph = (q >> 1) & 1, pw = q & 1, u = q >> 3, v = (q >> 2) & 1;
+      t.rlo = ph ? 2 * u : u;
+      t.rhi = ph ? 1 + u : 2 * u;
+      t.slo = pw ? 2 * v : v;
+      t.shi = pw ? 1 + v : 2 * v;
+      t.boff = (u + ph) * RS + v + pw;
+    } else {
+      const int ri = q >> 2, si = q & 3;
+      t.rlo = ri < 2 ? 2 - ri : 0;
+      t.rhi = ri < 2 ? 2 : 3 - ri;
+      t.slo = si < 2 ? 2 - si : 0;
+      t.shi = si < 2 ? 2 : 3 - si;
+      t.boff = ri * RS + (si & 1 ? EV : kS2Odd) + (si >> 1);
+    }
+    return t;
+  };
+
   // Operands of one MFMA step st = (cp, r, s), cp the channel pair.
   float a[2][MI], b[2][NJ];
+  float araw[(UP2 || U2B) ? 2 : 1][MI][4];  // UP2 / U2B: the step's weight taps
   auto read_step = [&](int buf, int st) {
     if constexpr (PC != 0) {
       // reduction elements e = 2 st (lanes 0-31) and 2 st + 1 (32-63), each
@@ -462,26 +520,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
       for (int i = 0; i < MI; ++i) a[buf][i] = ws[aoff + e0 * WS + i * 32];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + ob];
-    } else if constexpr (UP2) {
-      // step q of channel pair cp: class c = (ph, pw) = q % 4 (consecutive
-      // steps feed different accumulators), small-grid tap (u, v) = q / 4;
-      // kernel rows rlo..rhi and columns slo..shi land on that tap
-      const int cp = st / 16, q = st % 16;
-      const int ph = (q >> 1) & 1, pw = q & 1, u = q >> 3, v = (q >> 2) & 1;
-      const int rlo = ph ? 2 * u : u, rhi = ph ? 1 + u : 2 * u;
-      const int slo = pw ? 2 * v : v, shi = pw ? 1 + v : 2 * v;
+    } else if constexpr (UP2 || U2B) {
+      // the weight taps of step st = 16 cp + q (summed into a just before
+      // the step's MFMAs, so that waiting for these reads never holds up the
+      // MFMAs of the step before) and its pixel operand
+      const int cp = st >> 4;
+      const TapSet ts = tap_set(st & 15);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        float sum = 0.f;
+        int k = 0;
 #pragma unroll
-        for (int r = rlo; r <= rhi; ++r)
+        for (int r = ts.rlo; r <= ts.rhi; ++r)
 #pragma unroll
-          for (int s = slo; s <= shi; ++s) sum += ws[aoff + (2 * cp * 9 + 3 * r + s) * WS + i * 32];
-        a[buf][i] = sum;
+          for (int s = ts.slo; s <= ts.shi; ++s, ++k)
+            araw[buf][i][k] = ws[aoff + (2 * cp * 9 + (U2B ? 8 - (3 * r + s) : 3 * r + s)) * WS +
+                                 i * 32];
       }
-      // small row i + u + ph - 1 = tile row row + u + ph (likewise columns)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + (u + ph) * RS + v + pw];
+      for (int j = 0; j < NJ; ++j) b[buf][j] = xs[boff[j] + 2 * cp * PL + ts.boff];
     } else if constexpr (S2B) {
       // weight tap (r, s): LDS slot 8 - (3 r + s) (the backward rotation);
       // g at tile offset ((ph + 1 - r) / 2 + 1, (pw + 1 - s) / 2 + 1)
@@ -529,21 +585,52 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     __syncthreads();
     if (chunk + 1 < nchunks) load_tiles(chunk + 1);
     read_step(0, 0);
+    if constexpr (UP2 || U2B) {
+      // 16 (class, tap) steps per channel pair: the channel pairs are a
+      // plain loop and the 16 steps are unrolled, so that every step's
+      // class, taps and accumulator set are compile-time (a fully unrolled
+      // fill of 64 such steps is past the compiler's unroll budget, and a
+      // runtime accumulator index turns into selects over all four sets)
+#pragma unroll 1
+      for (int cp = 0; cp < CB / 2; ++cp) {
 #pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int cur = st & 1;
-      if (st + 1 < NSTEP) read_step(cur ^ 1, st + 1);
-      // Keep the next step's LDS reads ahead of this step's MFMAs (the
-      // scheduler would otherwise sink them next to their use).
-      __builtin_amdgcn_sched_barrier(0);
-      // S2B: the parity class of this step's tap picks the accumulator set;
-      // UP2: the class of this step
-      const int c = S2B ? 2 * ((st % 9) / 3 != 1) + (st % 3 != 1) : UP2 ? st % 4 : 0;
+        for (int q = 0; q < 16; ++q) {
+          const int cur = q & 1;
+          if (q + 1 < 16 || cp + 1 < CB / 2) read_step(cur ^ 1, 16 * cp + q + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const TapSet ts = tap_set(q);
+          const int nt = (ts.rhi - ts.rlo + 1) * (ts.shi - ts.slo + 1);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+          for (int i = 0; i < MI; ++i) {
+            float sum = araw[cur][i][0];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[c * MI + i][j] = mfma_32x32x2_f32(a[cur][i], b[cur][j], acc[c * MI + i][j]);
+            for (int k = 1; k < nt; ++k) sum += araw[cur][i][k];
+            a[cur][i] = sum;
+          }
+          const int c = UP2 ? q % 4 : 0;  // UP2: the output class of this step
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[c * MI + i][j] = mfma_32x32x2_f32(a[cur][i], b[cur][j], acc[c * MI + i][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        const int cur = st & 1;
+        if (st + 1 < NSTEP) read_step(cur ^ 1, st + 1);
+        // Keep the next step's LDS reads ahead of this step's MFMAs (the
+        // scheduler would otherwise sink them next to their use).
+        __builtin_amdgcn_sched_barrier(0);
+        // S2B: the parity class of this step's tap picks the accumulator set
+        const int c = S2B ? 2 * ((st % 9) / 3 != 1) + (st % 3 != 1) : 0;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[c * MI + i][j] = mfma_32x32x2_f32(a[cur][i], b[cur][j], acc[c * MI + i][j]);
+      }
     }
   }
 
@@ -726,18 +813,19 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   const bool quad = s2b || (MODE == kFwd && a.up2);
   const int kH = quad ? H / 2 : H, kW = quad ? W / 2 : W;
   const long hw4 = (long)H * W * 4;
-  // output plane bytes (a stride-2 forward writes an H/2 x W/2 output)
-  const long ohw4 = (MODE == kFwd && a.s2) ? hw4 / 4 : hw4;
+  // output plane bytes (a stride-2 forward and an upsampling backward-data
+  // write an H/2 x W/2 output)
+  const long ohw4 = (MODE == kFwd ? a.s2 : a.up2) ? hw4 / 4 : hw4;
   const long ob0 = (long)N * dst.c0 * ohw4, ob1 = (long)N * (Cout - dst.c0) * ohw4;
   const bool small = ob0 < 2147483648L && ob1 < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
-  const long shw4 = (a.up2 || s2b) ? hw4 / 4 : hw4;  // source plane bytes
+  const long shw4 = quad ? hw4 / 4 : hw4;  // source plane bytes
   const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * shw4) : 0u;
   const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * shw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_, PC_, UP_, S2B_, S2_)                                                \
+#define CONV3X3_L(VEC_, PRO_, PC_, UP_, S2B_, S2_, U2B_)                                          \
   hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_,   \
-                                     S2B_, S2_>),                                                 \
+                                     S2B_, S2_, U2B_>),                                           \
                      grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, kH, kW, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,     \
@@ -753,40 +841,45 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   if (a.s2) {
     if constexpr (kF) {
       if (vec)
-        CONV3X3_L(true, false, 0, false, false, true);
+        CONV3X3_L(true, false, 0, false, false, true, false);
       else
-        CONV3X3_L(false, false, 0, false, false, true);
+        CONV3X3_L(false, false, 0, false, false, true, false);
     } else if constexpr (one_tile) {
       if (vec)
-        CONV3X3_L(true, false, 0, false, true, false);
+        CONV3X3_L(true, false, 0, false, true, false, false);
       else
-        CONV3X3_L(false, false, 0, false, true, false);
+        CONV3X3_L(false, false, 0, false, true, false, false);
     } else {
       return false;  // the planner gives stride-2 backward-data 64 x 64 tiles
     }
   } else if (a.up2) {
-    if constexpr (kF && one_tile) {
+    if constexpr (!kF) {
       if (vec)
-        CONV3X3_L(true, false, 0, true, false, false);
+        CONV3X3_L(true, false, 0, false, false, false, true);
       else
-        CONV3X3_L(false, false, 0, true, false, false);
+        CONV3X3_L(false, false, 0, false, false, false, true);
+    } else if constexpr (one_tile) {
+      if (vec)
+        CONV3X3_L(true, false, 0, true, false, false, false);
+      else
+        CONV3X3_L(false, false, 0, true, false, false, false);
     } else {
       return false;  // the planner gives the upsampling forward 64 x 64 tiles
     }
   } else if (a.pscale) {
     if (vec)
-      CONV3X3_L(true, true, 0, false, false, false);
+      CONV3X3_L(true, true, 0, false, false, false, false);
     else
-      CONV3X3_L(false, true, 0, false, false, false);
+      CONV3X3_L(false, true, 0, false, false, false, false);
   } else if (pc == 3) {
-    CONV3X3_L(true, false, kF ? 3 : 0, false, false, false);
+    CONV3X3_L(true, false, kF ? 3 : 0, false, false, false, false);
   } else if (pc == 4) {
-    CONV3X3_L(true, false, kF ? 4 : 0, false, false, false);
+    CONV3X3_L(true, false, kF ? 4 : 0, false, false, false, false);
   } else {
     if (vec)
-      CONV3X3_L(true, false, 0, false, false, false);
+      CONV3X3_L(true, false, 0, false, false, false, false);
     else
-      CONV3X3_L(false, false, 0, false, false, false);
+      CONV3X3_L(false, false, 0, false, false, false, false);
   }
 #undef CONV3X3_L
   return true;

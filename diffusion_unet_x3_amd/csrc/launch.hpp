@@ -52,10 +52,4 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const 
                        float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
                        hipStream_t stream);
 
-// small[p, i, j] = sum of big[p, 2i + a, 2j + b] over a, b in {0, 1}: the
-// adjoint of nearest 2x upsampling over `planes` planes of Hs x Ws pixels
-// (big: planes x 2Hs x 2Ws float32).
-void launch_downsum2(const float* big, float* small, long planes, int Hs, int Ws,
-                     hipStream_t stream);
-
 }  // namespace conv3x3

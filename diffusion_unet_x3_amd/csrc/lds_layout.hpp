@@ -66,6 +66,17 @@ CONV3X3_HD constexpr int fwd_f32_s2_plane(int imgs, int th, int tw) {
 CONV3X3_HD constexpr int fwd_f32_s2_lds_bytes(int cb, int imgs, int th, int tw, int co_tile) {
   return 4 * (cb * fwd_f32_s2_plane(imgs, th, tw) + fwd_f32_w_floats(cb, co_tile));
 }
+// Backward-data of an upsampling convolution reads a 4 x 4 window of g at
+// stride 2 per output pixel: one more staged row (2 th + 2) and one more
+// even column (j = tw), so the row stride grows to keep the even run 16-byte
+// aligned.
+CONV3X3_HD constexpr int fwd_f32_u2b_rs(int tw) { return 2 * tw + 12; }
+CONV3X3_HD constexpr int fwd_f32_u2b_plane(int imgs, int th, int tw) {
+  return imgs * (2 * th + 2) * fwd_f32_u2b_rs(tw);
+}
+CONV3X3_HD constexpr int fwd_f32_u2b_lds_bytes(int cb, int imgs, int th, int tw, int co_tile) {
+  return 4 * (cb * fwd_f32_u2b_plane(imgs, th, tw) + fwd_f32_w_floats(cb, co_tile));
+}
 
 // ---- forward / backward-data, bfloat16 ----
 // Plane of one 8-channel group, in 16-byte words, padded to 8 mod 16 words

@@ -195,6 +195,7 @@ bool plan(const Problem& p, Plan* out) {
     pl.lds_bytes = p.dtype == kF32
         ? (p.stride2 && p.pass == kFwd
                ? fwd_f32_s2_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
+           : p.stride2 ? fwd_f32_u2b_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co)
                      : fwd_f32_lds_bytes(pl.chunk, pl.imgs, pl.th, pl.tw, pl.tile_co))
         : fwd_bf16_lds_bytes(pl.imgs, pl.th, pl.tw, pl.tile_co);
     if (p.pass == kFwd) pl.lds_bytes += 4 * pl.tile_co;  // the tile's biases

@@ -54,8 +54,10 @@ struct Problem {
   // reduction may be split over several workgroups per output tile (partial
   // sums in the workspace, then a fixed-order reduce)
   bool allow_split = false;
-  // float32 stride-2 forward / backward-weight, H, W being the output's
-  // (g's): the x tiles hold 2 th + 1 input rows of 2 tw + 1 columns
+  // float32 passes that stage their source at stride 2, H, W being the
+  // output's: the stride-2 forward / backward-weight (x tiles of 2 th + 1
+  // input rows of 2 tw + 1 columns) and the upsampling backward-data (g
+  // tiles of 2 th + 2 rows of 2 tw + 2 columns)
   bool stride2 = false;
   // float32 passes that keep one accumulator set per output-pixel parity
   // class (stride-2 backward-data, upsampling forward; H, W the grid they

@@ -260,18 +260,17 @@ def test_split_workspace_checks():
 
 def test_up2_argument_checks():
     d = (2, 4, 4, 5, 6)  # N, C, K, H, W of the small input
-    unsup, ws_err, alias = S["ERR_UNSUPPORTED"], S["ERR_WORKSPACE"], S["ERR_ALIAS"]
+    unsup, alias = S["ERR_UNSUPPORTED"], S["ERR_ALIAS"]
     assert lib3.conv3x3_up2_workspace_size(lib3.PASS_FWD, *d) == 0
-    assert lib3.conv3x3_up2_workspace_size(lib3.PASS_BWD_DATA, *d) == 2 * 4 * 4 * 5 * 6 * 4
+    assert lib3.conv3x3_up2_workspace_size(lib3.PASS_BWD_DATA, *d) == 0
     assert lib3.conv3x3_up2_workspace_size(lib3.PASS_BWD_WEIGHT, *d) == \
         lib3.conv3x3_bwd_weight_workspace_size(2, 4, 4, 10, 12)
     assert L.conv3x3_fwd_up2(X, Wt, B, Y, *d, 1, None) == unsup
     assert L.conv3x3_bwd_data_up2(G, Wt, Y, WS, 1 << 30, *d, 1, None) == unsup
     assert L.conv3x3_bwd_weight_up2(X, G, Y, B, WS, 1 << 30, *d, 1, None) == unsup
     assert L.conv3x3_fwd_up2(X, Wt, B, Y, 2, 4, 4, 0, 6, 0, None) == S["ERR_BAD_SHAPE"]
-    assert L.conv3x3_bwd_data_up2(G, Wt, Y, None, 0, *d, 0, None) == ws_err
-    assert L.conv3x3_bwd_data_up2(G, Wt, Y, WS, 2 * 4 * 4 * 30 * 4 - 1, *d, 0, None) == ws_err
-    assert L.conv3x3_bwd_data_up2(G, Wt, Y, Y, 1 << 30, *d, 0, None) == alias
+    # backward-data needs no workspace; dx may not be g
+    assert L.conv3x3_bwd_data_up2(G, Wt, G, None, 0, *d, 0, None) == alias
     assert L.conv3x3_fwd_up2(X, Wt, B, X, *d, 0, None) == alias
 
 
