@@ -296,14 +296,19 @@ int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace
  *   g  : [N][K][2H][2W]              the gradient at y
  *   dx : [N][C][H][W]                the sum of the input gradient over each
  *                                    2x2 block of the upsampled grid
- * The forward and backward-weight loaders read x at (h/2, w/2) as they stage
- * the upsampled tile (it never exists in memory).  Backward-data runs the
- * plain backward-data at the upsampled resolution into the workspace and
- * adds its 2x2 blocks in a second kernel (fixed order).  Workspace bytes:
- * conv3x3_up2_workspace_size(pass, ...) -- 0 for the forward, 16 N C H W
- * for backward-data, the split-K size of the 2H x 2W problem for
- * backward-weight.  float32 only (CONV3X3_ERR_UNSUPPORTED for bfloat16);
- * the limits apply to the 2H x 2W problem.
+ * The upsampled tensor never exists.  Forward: each output pixel parity
+ * class (2i + ph, 2j + pw) is a 2x2-tap convolution of x whose weights are
+ * sums of the 3x3 taps (kernel rows {0}, {1, 2} on x rows i - 1, i for
+ * ph = 0; {0, 1}, {2} on rows i, i + 1 for ph = 1; likewise columns).
+ * Backward-data: dx[i, j] gathers g rows and columns 2i - 1 .. 2i + 2 at
+ * stride 2 with a 4 x 4 kernel of summed taps.  Backward-weight's loader
+ * reads x at (h/2, w/2) as it stages the upsampled tile.  Workspace bytes:
+ * conv3x3_up2_workspace_size(pass, ...) -- 0 for the forward and
+ * backward-data (whose workspace arguments may be NULL, 0), the split-K
+ * size of the 2H x 2W problem for backward-weight.  The summed taps round
+ * differently from the upsampled-grid sums (within the float32 bar).
+ * float32 only (CONV3X3_ERR_UNSUPPORTED for bfloat16); the limits apply to
+ * the 2H x 2W problem.
  */
 size_t conv3x3_up2_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype);
 

@@ -1,9 +1,13 @@
 """GPU parity of the upsample-then-convolve entry points (conv3x3_*_up2:
-nearest 2x upsampling read by the convolution's loader) against the oracle,
+nearest 2x upsampling fused into the convolution) against the oracle,
 through the C ABI.  Same float32 bar as the plain passes (2e-5; exact on
-integer inputs), on small and ragged shapes in full (widths that give the
-vector and the scalar staging paths, one and several tiles across) and on
-a full-size up-path layer by sampled elements."""
+integer inputs, where the summed taps of the parity-class forward and the
+4x4-gather backward-data are exact too), on small and ragged shapes in full
+(widths that give the vector and the scalar staging paths, one and several
+tiles across -- the backward-data tile's right halo column --, odd heights,
+ragged channel fills and tiles, several images per block) and on a
+full-size up-path layer by sampled elements.  The calls pass no workspace
+to backward-data, which needs none."""
 import numpy as np
 import pytest
 import torch
@@ -44,7 +48,8 @@ def _inputs(N, C, K, H, W, seed, integer=False):
 
 # (N, C, K, H, W) of the small input
 SHAPES = [(2, 64, 64, 16, 16), (2, 8, 16, 4, 6), (1, 3, 5, 7, 9), (2, 17, 33, 5, 13),
-          (2, 32, 48, 8, 40), (1, 16, 24, 3, 68), (4, 128, 64, 8, 8)]
+          (2, 32, 48, 8, 40), (1, 16, 24, 3, 68), (4, 128, 64, 8, 8),
+          (3, 40, 136, 9, 20), (2, 136, 72, 4, 4), (1, 8, 8, 1, 1)]
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
