@@ -90,3 +90,13 @@ def test_downsample_layers_sampled(layer):
     print(layer.name, errs)
     for name, e in errs.items():
         assert e <= TRIPWIRE["f32"], (layer.name, name, e)
+
+
+def test_s2_deterministic_bitwise():
+    """No atomics in any stride-2 pass: two runs agree bit for bit (the
+    128-channel downsample layer, split-K backward-weight included)."""
+    layer = wl.DOWNSAMPLE[0]
+    inp = _inputs(*layer.shape, seed=103)
+    a, b = _run(inp), _run(inp)
+    for k in ("y", "dx", "dw", "db"):
+        assert np.array_equal(a[k], b[k]), k

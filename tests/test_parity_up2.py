@@ -95,3 +95,11 @@ def test_full_size_up_layer_sampled():
     print(errs)
     for name, e in errs.items():
         assert e <= TRIPWIRE["f32"], (name, e)
+
+
+def test_up2_deterministic_bitwise():
+    """No atomics in any upsampling pass: two runs agree bit for bit."""
+    inp = _inputs(4, 128, 64, 8, 8, seed=107)
+    a, b = _run(inp), _run(inp)
+    for k in ("y", "dx", "dw", "db"):
+        assert np.array_equal(a[k], b[k]), k
