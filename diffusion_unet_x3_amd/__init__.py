@@ -97,7 +97,7 @@ class Plan(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it first (python -m diffusion_unet_x3_amd.build "
+            f"{LIB_PATH} is missing: build it first (python diffusion_unet_x3_amd/build.py "
             "or __graft_entry__.build()); there is no CPU fallback")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p

@@ -1,6 +1,6 @@
 """Build libconv3x3.so (the HIP library) in-tree for gfx950.
 
-Usage: python -m diffusion_unet_x3_amd.build   (or build() from Python).
+Usage: python diffusion_unet_x3_amd/build.py   (or __graft_entry__.build()).
 Every source is compiled with hipcc to an object next to the sources, in
 parallel, then linked into diffusion_unet_x3_amd/libconv3x3.so.
 """
