@@ -230,6 +230,25 @@ def test_prologue_argument_checks():
     assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, Y, *big, 0, None) == unsup
 
 
+def test_small_tile_split_rule():
+    """bf16 with a workspace: 64 x 64 tiles that make half a round to one
+    round of workgroups split a reduction of at least 32 fills in two."""
+    bf16 = lib3.CONV3X3_BF16
+    slot = 32 * 512 * 64 * 4  # one float32 output of a 32-image 8x8 layer with 512 channels
+    for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
+        assert lib3.conv3x3_workspace_size(p, 32, 512, 512, 8, 8, bf16) == 2 * slot
+    # 384 input channels: a 24-fill forward reduction stays whole, its
+    # 32-fill backward-data (over 512 channels) splits
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 384, 512, 8, 8, bf16) == 0
+    assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 384, 512, 8, 8, bf16) == \
+        2 * 32 * 384 * 64 * 4
+    # a grid below half a round (4 images: 32 workgroups) is not split
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 512, 512, 8, 8, bf16) == 0
+    # float32 never splits
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 512, 512, 8, 8,
+                                       lib3.CONV3X3_F32) == 0
+
+
 def test_split_workspace_checks():
     """A bf16 small-image problem needs a workspace on the *_ws entry
     points; without one, or with too little, nothing is launched."""

@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 # 16x16 images, 32 to 65 fills (1032 channels: a ragged last fill), split
 # grids of 192 and 256 workgroups.
 SHAPES = [(32, 1024, 512, 8, 8), (24, 1032, 512, 8, 8), (24, 1024, 128, 16, 16),
-          (48, 256, 1024, 8, 8), (32, 512, 384, 16, 16)]
+          (48, 256, 1024, 8, 8), (32, 512, 384, 16, 16),
+          (32, 512, 512, 8, 8), (32, 384, 512, 8, 8)]
 
 
 def _run(inp, split, out_dtype=None):
