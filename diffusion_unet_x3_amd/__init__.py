@@ -242,7 +242,7 @@ def _workspace(need, workspace, like):
 def conv3x3_fwd(x, w, bias=None, out=None, out_dtype=None, split=True, workspace=None):
     """y = conv3x3(x; w) + bias (stride 1, zero padding 1); float32 output, or
     bfloat16 for bfloat16 inputs with a bfloat16 out / out_dtype.  split:
-    run through conv3x3_fwd_ws, which may split a small-image bf16
+    run through conv3x3_fwd_ws, which may split a small-image
     reduction (the workspace is allocated unless given)."""
     _check(x, "x", 4)
     _check(w, "w", 4)

@@ -123,7 +123,7 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   Problem pb{kFwd, kdt(dtype), N, C, K, geom ? H / 2 : H, geom ? W / 2 : W, x.c0};
   pb.stride2 = geom == 2;
   pb.quad = geom == 1;
-  pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z;
+  pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z && !pr.on() && !geom;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -149,7 +149,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
                      parts_aligned(x) && aligned16(w) && buffer_sized(2L * N * C * hw) &&
                      buffer_sized(2L * K * C * 9);
     Split<const float> xs{(const float*)x.p0, (const float*)x.p1, x.c0};
-    ok = launch_fwd_f32(pl, vec, xs, (const float*)w, bias, one(y, K), N, C, K, H, W, a, s);
+    ok = launch_fwd_f32(pl, vec, xs, (const float*)w, bias, one(y, K), N, C, K, H, W, a,
+                        (float*)ws, s);
   } else {
     const bool vec = W % 8 == 0 && C % 16 == 0 && x.c0 % 16 == 0 && parts_aligned(x) &&
                      aligned16(w) && buffer_sized((long)N * C * hw) &&
@@ -195,7 +196,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   Problem pb{kBwdData, kdt(dtype), N, C, K, geom ? H / 2 : H, geom ? W / 2 : W, dx.c0};
   pb.quad = s2;
   pb.stride2 = geom == 1;
-  pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE;
+  pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE && !pr.on() && !geom;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -220,7 +221,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
                      aligned16(w) && (!a.zsrc || aligned16(a.zsrc)) &&
                      buffer_sized(2L * N * K * hw) && buffer_sized(2L * K * C * 9);
     ok = launch_fwd_f32(pl, vec, one((const float*)g, K), (const float*)w, nullptr, dx, N, K, C,
-                        H, W, a, s);
+                        H, W, a, (float*)ws, s);
   } else {
     const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && dx.c0 % 8 == 0 &&
                      aligned16(g) && aligned16(w) && buffer_sized((long)N * K * hw) &&

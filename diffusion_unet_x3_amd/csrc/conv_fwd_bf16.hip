@@ -751,6 +751,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   }
 }
 
+void launch_split_reduce(const float* part, int S, long slot, float* dst, hipStream_t stream) {
+  dim3 rg((unsigned)((slot + 1023) / 1024)), rb(256);
+  hipLaunchKernelGGL(split_reduce_kernel, rg, rb, 0, stream, part, S, slot, dst, 0, (int)kActNone,
+                     (float*)nullptr);
+}
+
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
 static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                             const uint16_t* wt, const float* bias, Split<float> dst, int N,

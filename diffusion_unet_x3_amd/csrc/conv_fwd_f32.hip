@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
     uint32_t dst1_bytes, int act, float* __restrict__ zout, const float* __restrict__ zsrc,
     const float* __restrict__ pscale, const float* __restrict__ pshift,
-    const float* __restrict__ px) {
+    const float* __restrict__ px, float* __restrict__ part, int per_split, long slot) {
   constexpr int BM = IMGS * TH * TW;
   constexpr int NT = 64 * NW;  // threads
   constexpr int WPX = NW / WCO;
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // bias), so the epilogue is stores only.
   if constexpr (MODE == kFwd) {
     for (int i = tid; i < BCO; i += NT)
-      bias_s[i] = (bias != nullptr && i < co_n) ? bias[co0 + i] : 0.f;
+      bias_s[i] = (bias != nullptr && i < co_n && blockIdx.z == 0) ? bias[co0 + i] : 0.f;
     __syncthreads();
   }
   // (S2B: parity class c's tiles are acc[c * MI + i])
@@ -578,12 +578,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
-  load_tiles(0);
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    if (chunk) __syncthreads();
+  // A split reduction (part != null) gives slice blockIdx.z the fills
+  // fbase .. fbase + per_split - 1 and writes its partial sums (the bias in
+  // slice 0 only) to slot blockIdx.z of part.
+  const int fbase = part ? (int)blockIdx.z * per_split : 0;
+  const int fend = part ? min(nchunks, fbase + per_split) : nchunks;
+  load_tiles(fbase);
+  for (int chunk = fbase; chunk < fend; ++chunk) {
+    if (chunk != fbase) __syncthreads();
     store_tiles(chunk);
     __syncthreads();
-    if (chunk + 1 < nchunks) load_tiles(chunk + 1);
+    if (chunk + 1 < fend) load_tiles(chunk + 1);
     read_step(0, 0);
     if constexpr (UP2 || U2B) {
       // 16 (class, tap) steps per channel pair: the channel pairs are a
@@ -641,7 +646,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // Backward-data with the input prologue: du = acc * SiLU'(x * scale +
   // shift) at the output position (px has dx's shape, one tensor).
   const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
-  float* const od = oseg ? dst1 : dst;
+  float* const od = part ? part + (long)blockIdx.z * slot : oseg ? dst1 : dst;
   const uint32_t od_bytes = oseg ? dst1_bytes : dst_bytes;
   if constexpr (MODE == kBwdData && PRO) {
     // scale and shift of the tile's channels and images, through LDS (the
@@ -801,10 +806,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO>
 static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const float* wt,
                        const float* bias, Split<float> dst, int N, int Cin, int Cout, int H,
-                       int W, const ActArgs& a, hipStream_t stream) {
+                       int W, const ActArgs& a, float* ws, hipStream_t stream) {
   constexpr int CB = 8;
   const bool s2b = MODE == kBwdData && a.s2;
-  dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
+  // split reduction: partial sums into ws (one output-sized slot per
+  // slice), then the slot-order reduce
+  float* const part = pl.split > 1 ? ws : nullptr;
+  const long slot = (long)N * Cout * H * W;
+  dim3 grid(pl.grid_x, pl.grid_y, part ? pl.split : 1), block(256, 1, 1);
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets); otherwise both take the plain-store path.
   // A stride-2 backward-data and an upsampling forward run their parity
@@ -829,7 +838,7 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
                      grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, kH, kW, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,     \
-                     a.zout, a.zsrc, a.pscale, a.pshift, a.px)
+                     a.zout, a.zsrc, a.pscale, a.pshift, a.px, part, pl.chunks_per_split, slot)
   // packed taps: the forward of a 3- or 4-channel single tensor
   const int pc =
       (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.s2 && src.c0 == Cin) ? Cin : 0;
@@ -882,19 +891,25 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
       CONV3X3_L(false, false, 0, false, false, false, false);
   }
 #undef CONV3X3_L
+  if (part) launch_split_reduce(part, pl.split, slot, dst.p0, stream);
   return true;
 }
 
 template <int MODE>
 static bool launch_mode(const Plan& pl, bool vec, Split<const float> src, const float* wt,
                         const float* bias, Split<float> dst, int N, int Cin, int Cout, int H,
-                        int W, const ActArgs& a, hipStream_t s) {
+                        int W, const ActArgs& a, float* ws, hipStream_t s) {
   if (pl.chunk != 8) return false;
+  // a split reduction: plain passes only, with a workspace and one output
+  // tensor
+  if (pl.split > 1 && (ws == nullptr || dst.c0 != Cout || a.act != kActNone || a.zout || a.zsrc ||
+                       a.pscale || a.up2 || a.s2))
+    return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_)                                               \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&              \
       pl.wave_co == WCO_) {                                                                 \
     return launch_cfg<MODE, TW_, TH_, IMGS_, CO_, WCO_>(pl, vec, src, wt, bias, dst, N, Cin, \
-                                                        Cout, H, W, a, s);                  \
+                                                        Cout, H, W, a, ws, s);              \
   }
   CONV3X3_FWD_F32_CONFIGS(CONV3X3_X)
 #undef CONV3X3_X
@@ -903,10 +918,11 @@ static bool launch_mode(const Plan& pl, bool vec, Split<const float> src, const 
 
 bool launch_fwd_f32(const Plan& pl, bool vec, Split<const float> src, const float* wt,
                     const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
-                    const ActArgs& a, hipStream_t stream) {
+                    const ActArgs& a, float* ws, hipStream_t stream) {
   if (pl.pass == kFwd)
-    return launch_mode<kFwd>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, stream);
-  return launch_mode<kBwdData>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, stream);
+    return launch_mode<kFwd>(pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, ws, stream);
+  return launch_mode<kBwdData>(pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, ws,
+                               stream);
 }
 
 }  // namespace conv3x3

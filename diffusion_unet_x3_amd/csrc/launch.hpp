@@ -22,10 +22,16 @@ struct Split {
 // (pl.pass == kBwdData; src = g, Cin = K, Cout = C; bias ignored), float32.
 // a: forward -- a.act and a.zout fused into the epilogue (dst one tensor);
 // backward-data -- the source is multiplied by act'(a.zsrc) as it is staged
-// (a.zsrc has the source's shape; src one tensor).
+// (a.zsrc has the source's shape; src one tensor).  pl.split > 1 (plain
+// passes only): the reduction is split as for bfloat16 below, partial sums
+// in ws.
 bool launch_fwd_f32(const Plan& pl, bool vec, Split<const float> src, const float* wt,
                     const float* bias, Split<float> dst, int N, int Cin, int Cout, int H, int W,
-                    const ActArgs& a, hipStream_t stream);
+                    const ActArgs& a, float* ws, hipStream_t stream);
+
+// Slot-order sum of the S float32 partial outputs (slot floats each) of a
+// split forward / backward-data reduction into dst (float32, no activation).
+void launch_split_reduce(const float* part, int S, long slot, float* dst, hipStream_t stream);
 
 // Same, bfloat16 inputs (raw 16-bit patterns); outputs float32, or bfloat16
 // (round to nearest even) when out_bf16 (dst then points to 16-bit values;

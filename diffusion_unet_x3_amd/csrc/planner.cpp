@@ -159,7 +159,7 @@ bool plan(const Problem& p, Plan* out) {
     // small tiles; 48- and 56-fill reductions on 16x16 images gain 10-16%).
     int split = 1;
     const int cin = p.pass == kFwd ? p.C : p.K;
-    const int fills = ceil_div(cin, 16);
+    const int fills = ceil_div(cin, p.dtype == kF32 ? 8 : 16);  // channels per fill
     if (p.allow_split && p.dtype == kBF16 && cout > 64 && wgs[0] > 0 && wgs[0] < kMinWGs &&
         fills >= 32 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
       int s = kMinWGs / wgs[0];
@@ -170,14 +170,14 @@ bool plan(const Problem& p, Plan* out) {
         split = s;
       }
     }
-    // bf16 with a workspace, smallest tile: when the 64 x 64 tiles make half
-    // a round to one round of workgroups and the reduction has >= 32 fills,
-    // split it in two, so two workgroups share each compute unit and cover each
-    // other's per-fill staging and barrier waits (measured on 8x8 images
-    // with 512 channels: backward-data 33.5 -> 30.3 us, forward 39.5 ->
-    // 37.5 us; a split of four is slower, and 24-fill reductions gain
-    // nothing).
-    if (split == 1 && p.allow_split && p.dtype == kBF16 && pick == ncand - 1 && wgs[pick] > 0 &&
+    // With a workspace, smallest tile (both dtypes): when the 64 x 64 tiles
+    // make half a round to one round of workgroups and the reduction has >=
+    // 32 fills, split it in two, so two workgroups share each compute unit
+    // and cover each other's per-fill staging and barrier waits (measured on
+    // 8x8 images with 512 channels, bf16: backward-data 33.5 -> 30.3 us,
+    // forward 39.5 -> 37.5 us; a split of four is slower, and 24-fill
+    // reductions gain nothing).
+    if (split == 1 && p.allow_split && !p.quad && !p.stride2 && pick == ncand - 1 && wgs[pick] > 0 &&
         2 * wgs[pick] >= kMinWGs && wgs[pick] <= kMinWGs && fills >= 32 &&
         (cout0 < 0 || cout0 >= cout))
       split = 2;

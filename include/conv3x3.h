@@ -267,9 +267,10 @@ int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* sh
  *   workspace : device buffer of at least conv3x3_workspace_size(pass, ...)
  *               bytes (may be NULL when that size is 0); its contents are
  *               scratch, it must not overlap an input or output.
- * With a workspace, a bfloat16 problem whose output tiles are too few to
- * fill the device (small images: the 8 x 8 and 16 x 16 layers) splits its
- * channel reduction over up to 8 workgroups per tile; each writes its
+ * With a workspace, a problem whose output tiles are too few to fill the
+ * device (small images: bfloat16 8 x 8 and 16 x 16 layers, float32 8 x 8
+ * layers with 256+ channels) splits its channel reduction over up to 8
+ * (float32: 2) workgroups per tile; each writes its
  * partial sums (float32, one output-sized slot per slice) to the workspace
  * and a second kernel on the same stream adds the slots in slice order --
  * no atomics, bitwise-reproducible results (which can differ in the last

@@ -231,8 +231,9 @@ def test_prologue_argument_checks():
 
 
 def test_small_tile_split_rule():
-    """bf16 with a workspace: 64 x 64 tiles that make half a round to one
-    round of workgroups split a reduction of at least 32 fills in two."""
+    """With a workspace: 64 x 64 tiles that make half a round to one round
+    of workgroups split a reduction of at least 32 fills in two (fills of 16
+    channels for bf16, 8 for float32)."""
     bf16 = lib3.CONV3X3_BF16
     slot = 32 * 512 * 64 * 4  # one float32 output of a 32-image 8x8 layer with 512 channels
     for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
@@ -244,9 +245,15 @@ def test_small_tile_split_rule():
         2 * 32 * 384 * 64 * 4
     # a grid below half a round (4 images: 32 workgroups) is not split
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 512, 512, 8, 8, bf16) == 0
-    # float32 never splits
-    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 512, 512, 8, 8,
-                                       lib3.CONV3X3_F32) == 0
+    f32 = lib3.CONV3X3_F32
+    for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
+        assert lib3.conv3x3_workspace_size(p, 32, 512, 512, 8, 8, f32) == 2 * slot
+    # float32, 128 channels: 16 fills, too short
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 128, 512, 8, 8, f32) == 0
+    # float32 16x16 images take 768 workgroups of the 64 x 64 tile: no split
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 384, 384, 16, 16, f32) == 0
+    # the resampling and prologue entry points take no workspace, so never split
+    assert lib3.conv3x3_up2_workspace_size(lib3.PASS_FWD, 32, 512, 512, 16, 16, f32) == 0
 
 
 def test_split_workspace_checks():
@@ -261,7 +268,8 @@ def test_split_workspace_checks():
     # a split that would leave the grid at half a round is not taken
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 1024, 512, 8, 8, bf16) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 512, 1024, 8, 8, bf16) == need
-    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, lib3.CONV3X3_F32) == 0
+    # float32: 128 fills of 8 channels on 256 workgroups of 64 x 64 tiles, two slices
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, lib3.CONV3X3_F32) == 2 * (32 * 512 * 64 * 4)
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 64, 512, 512, 16, 16, bf16) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_WEIGHT, *d, bf16) == \
         lib3.conv3x3_bwd_weight_workspace_size(*d, bf16)

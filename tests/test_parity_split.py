@@ -78,3 +78,43 @@ def test_split_reduction_is_reproducible():
     a = _run(inp, split=True)
     b = _run(inp, split=True)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# float32: fills of 8 channels; 8x8 images whose 64 x 64 tiles make half a
+# round to one round of workgroups, 32+ fills.  520 channels: 65 fills, a
+# slice of 33 and one of 32; 384 -> 512: a 48-fill forward and a 64-fill
+# backward-data; 1024 -> 512: only the forward splits (backward-data has
+# 512 workgroups).
+F32_SHAPES = [(32, 512, 512, 8, 8), (24, 520, 512, 8, 8), (32, 384, 512, 8, 8),
+              (32, 1024, 512, 8, 8)]
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_split_reduction_f32_full_compare(shape, integer):
+    import diffusion_unet_x3_amd as lib3
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *shape, lib3.CONV3X3_F32) > 0, \
+        "shape no longer takes a split plan"
+    layer = wl.small_layer(*shape, dtype="f32", seed=83)
+    print(f"[parity] f32 split {shape} integer={integer}", flush=True)
+    inp = wl.make_inputs(layer, integer_exact=integer)
+    y, dx = _run(inp, split=True)
+    y_ref = oracle.conv3x3_fwd(inp["x"], inp["w"], inp["b"])
+    dx_ref = oracle.conv3x3_bwd_data(inp["g"], inp["w"])
+    if integer:
+        assert np.array_equal(y, y_ref) and np.array_equal(dx, dx_ref)
+        y0, dx0 = _run(inp, split=False)
+        assert np.array_equal(y, y0) and np.array_equal(dx, dx0)
+    else:
+        errs = {"y": rel_err(y, y_ref), "dx": rel_err(dx, dx_ref)}
+        print(errs)
+        for k, e in errs.items():
+            assert e <= TRIPWIRE["f32"], (shape, k, e)
+
+
+def test_split_reduction_f32_is_reproducible():
+    layer = wl.small_layer(32, 512, 512, 8, 8, dtype="f32", seed=89)
+    inp = wl.make_inputs(layer)
+    a = _run(inp, split=True)
+    b = _run(inp, split=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
