@@ -79,7 +79,7 @@ namespace conv3x3 {
 // even column (2 w0 + 2 TW).
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int CB, bool VEC, int NW = 4,
           bool PRO = false, int PC = 0, bool UP2 = false, bool S2B = false, bool S2 = false,
-          bool U2B = false>
+          bool U2B = false, bool SPL = false>
 __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const float* __restrict__ src, const float* __restrict__ src1, int cin0,
     const float* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -116,6 +116,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   const int OH = STR2 ? H / 2 : H, OW = STR2 ? W / 2 : W;
   constexpr int NSTEP = PC ? (9 * PC + 1) / 2 : CB / 2 * ((UP2 || U2B) ? 16 : 9);
   constexpr int NACC = (S2B || UP2) ? 4 : 1;  // accumulator sets (one per parity class)
+  static_assert(!SPL || (!PRO && PC == 0 && !UP2 && !S2B && !S2 && !U2B),
+                "split reduction: plain passes only");
+  // SPL: a split reduction (compile-time, so that the unsplit kernels carry
+  // none of it)
+  const int slice = SPL ? (int)blockIdx.z : 0;
 
   __shared__ __attribute__((aligned(16))) float xs[CB * PL];
   __shared__ float ws[fwd_f32_w_floats(CB, BCO)];
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // bias), so the epilogue is stores only.
   if constexpr (MODE == kFwd) {
     for (int i = tid; i < BCO; i += NT)
-      bias_s[i] = (bias != nullptr && i < co_n && blockIdx.z == 0) ? bias[co0 + i] : 0.f;
+      bias_s[i] = (bias != nullptr && i < co_n && slice == 0) ? bias[co0 + i] : 0.f;
     __syncthreads();
   }
   // (S2B: parity class c's tiles are acc[c * MI + i])
@@ -578,11 +583,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     for (int j = 0; j < NJ; ++j) acc[i][j] = init;
   }
 
-  // A split reduction (part != null) gives slice blockIdx.z the fills
-  // fbase .. fbase + per_split - 1 and writes its partial sums (the bias in
-  // slice 0 only) to slot blockIdx.z of part.
-  const int fbase = part ? (int)blockIdx.z * per_split : 0;
-  const int fend = part ? min(nchunks, fbase + per_split) : nchunks;
+  // A split reduction (SPL) gives slice blockIdx.z the fills fbase ..
+  // fbase + per_split - 1 and writes its partial sums (the bias in slice 0
+  // only) to slot blockIdx.z of part.
+  const int fbase = SPL ? slice * per_split : 0;
+  const int fend = SPL ? min(nchunks, fbase + per_split) : nchunks;
   load_tiles(fbase);
   for (int chunk = fbase; chunk < fend; ++chunk) {
     if (chunk != fbase) __syncthreads();
@@ -646,7 +651,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
   // Backward-data with the input prologue: du = acc * SiLU'(x * scale +
   // shift) at the output position (px has dx's shape, one tensor).
   const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
-  float* const od = part ? part + (long)blockIdx.z * slot : oseg ? dst1 : dst;
+  float* const od = SPL ? part + (long)slice * slot : oseg ? dst1 : dst;
   const uint32_t od_bytes = oseg ? dst1_bytes : dst_bytes;
   if constexpr (MODE == kBwdData && PRO) {
     // scale and shift of the tile's channels and images, through LDS (the
@@ -832,13 +837,15 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
   const uint32_t sb0 = vec ? (uint32_t)(N * src.c0 * shw4) : 0u;
   const uint32_t sb1 = vec ? (uint32_t)(N * (Cin - src.c0) * shw4) : 0u;
   const uint32_t wb = vec ? (uint32_t)((long)Cin * Cout * 9 * 4) : 0u;
-#define CONV3X3_L(VEC_, PRO_, PC_, UP_, S2B_, S2_, U2B_)                                          \
+#define CONV3X3_LS(VEC_, PRO_, PC_, UP_, S2B_, S2_, U2B_, SPL_)                                  \
   hipLaunchKernelGGL((fwd_f32_kernel<MODE, TW, TH, IMGS, BCO, WCO, CB, VEC_, 4, PRO_, PC_, UP_,   \
-                                     S2B_, S2_, U2B_>),                                           \
+                                     S2B_, S2_, U2B_, SPL_>),                                     \
                      grid,                                                                        \
                      block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, \
                      Cin, Cout, kH, kW, pl.tiles_w, pl.tiles_h, sb0, sb1, wb, db0, db1, a.act,     \
                      a.zout, a.zsrc, a.pscale, a.pshift, a.px, part, pl.chunks_per_split, slot)
+#define CONV3X3_L(VEC_, PRO_, PC_, UP_, S2B_, S2_, U2B_) \
+  CONV3X3_LS(VEC_, PRO_, PC_, UP_, S2B_, S2_, U2B_, false)
   // packed taps: the forward of a 3- or 4-channel single tensor
   const int pc =
       (MODE == kFwd && vec && !a.pscale && !a.up2 && !a.s2 && src.c0 == Cin) ? Cin : 0;
@@ -884,6 +891,16 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
     CONV3X3_L(true, false, kF ? 3 : 0, false, false, false, false);
   } else if (pc == 4) {
     CONV3X3_L(true, false, kF ? 4 : 0, false, false, false, false);
+  } else if (part) {
+    // the planner splits only 64-pixel x 64-channel tiles of four waves
+    if constexpr (BCO == 64 && WCO == 2 && IMGS * TH * TW == 64) {
+      if (vec)
+        CONV3X3_LS(true, false, 0, false, false, false, false, true);
+      else
+        CONV3X3_LS(false, false, 0, false, false, false, false, true);
+    } else {
+      return false;
+    }
   } else {
     if (vec)
       CONV3X3_L(true, false, 0, false, false, false, false);
@@ -891,6 +908,7 @@ static bool launch_cfg(const Plan& pl, bool vec, Split<const float> src, const f
       CONV3X3_L(false, false, 0, false, false, false, false);
   }
 #undef CONV3X3_L
+#undef CONV3X3_LS
   if (part) launch_split_reduce(part, pl.split, slot, dst.p0, stream);
   return true;
 }
