@@ -172,15 +172,17 @@ bool plan(const Problem& p, Plan* out) {
     }
     // With a workspace, smallest tile (both dtypes): when the 64 x 64 tiles
     // make half a round to one round of workgroups and the reduction has >=
-    // 32 fills, split it in two, so two workgroups share each compute unit
-    // and cover each other's per-fill staging and barrier waits (measured on
-    // 8x8 images with 512 channels, bf16: backward-data 33.5 -> 30.3 us,
-    // forward 39.5 -> 37.5 us; a split of four is slower, and 24-fill
-    // reductions gain nothing).
+    // 32 fills, split it (bf16 in two, float32 in four: >= 8 fills of 8
+    // channels per slice), so several workgroups share each compute unit and
+    // cover each other's per-fill staging and barrier waits.  Measured on
+    // 8x8 images with 512 channels: bf16 backward-data 33.5 -> 30.3 us,
+    // forward 39.5 -> 37.5 us (a split of four is slower, and 24-fill
+    // reductions gain nothing); float32 forward 117 -> 103 us, backward-data
+    // 124 -> 103 us (a split of two: 109 / 110 us).
     if (split == 1 && p.allow_split && !p.quad && !p.stride2 && pick == ncand - 1 && wgs[pick] > 0 &&
         2 * wgs[pick] >= kMinWGs && wgs[pick] <= kMinWGs && fills >= 32 &&
         (cout0 < 0 || cout0 >= cout))
-      split = 2;
+      split = p.dtype == kF32 ? 4 : 2;
     const Block blk = pick >= 0 ? blks[pick] : Block{};
     if (pick < 0) return false;
     pl.tw = blk.tw;

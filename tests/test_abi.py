@@ -232,8 +232,8 @@ def test_prologue_argument_checks():
 
 def test_small_tile_split_rule():
     """With a workspace: 64 x 64 tiles that make half a round to one round
-    of workgroups split a reduction of at least 32 fills in two (fills of 16
-    channels for bf16, 8 for float32)."""
+    of workgroups split a reduction of at least 32 fills, bf16 (fills of 16
+    channels) in two, float32 (fills of 8) in four."""
     bf16 = lib3.CONV3X3_BF16
     slot = 32 * 512 * 64 * 4  # one float32 output of a 32-image 8x8 layer with 512 channels
     for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
@@ -247,7 +247,7 @@ def test_small_tile_split_rule():
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 512, 512, 8, 8, bf16) == 0
     f32 = lib3.CONV3X3_F32
     for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
-        assert lib3.conv3x3_workspace_size(p, 32, 512, 512, 8, 8, f32) == 2 * slot
+        assert lib3.conv3x3_workspace_size(p, 32, 512, 512, 8, 8, f32) == 4 * slot
     # float32, 128 channels: 16 fills, too short
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 128, 512, 8, 8, f32) == 0
     # float32 16x16 images take 768 workgroups of the 64 x 64 tile: no split
@@ -268,8 +268,8 @@ def test_split_workspace_checks():
     # a split that would leave the grid at half a round is not taken
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 1024, 512, 8, 8, bf16) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 512, 1024, 8, 8, bf16) == need
-    # float32: 128 fills of 8 channels on 256 workgroups of 64 x 64 tiles, two slices
-    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, lib3.CONV3X3_F32) == 2 * (32 * 512 * 64 * 4)
+    # float32: 128 fills of 8 channels on 256 workgroups of 64 x 64 tiles, four slices
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, *d, lib3.CONV3X3_F32) == 4 * (32 * 512 * 64 * 4)
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 64, 512, 512, 16, 16, bf16) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_WEIGHT, *d, bf16) == \
         lib3.conv3x3_bwd_weight_workspace_size(*d, bf16)

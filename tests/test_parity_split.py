@@ -80,9 +80,9 @@ def test_split_reduction_is_reproducible():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-# float32: fills of 8 channels; 8x8 images whose 64 x 64 tiles make half a
-# round to one round of workgroups, 32+ fills.  520 channels: 65 fills, a
-# slice of 33 and one of 32; 384 -> 512: a 48-fill forward and a 64-fill
+# float32: fills of 8 channels, four slices; 8x8 images whose 64 x 64 tiles
+# make half a round to one round of workgroups, 32+ fills.  520 channels:
+# 65 fills, slices of 17, 17, 17 and 14; 384 -> 512: a 48-fill forward and a 64-fill
 # backward-data; 1024 -> 512: only the forward splits (backward-data has
 # 512 workgroups).
 F32_SHAPES = [(32, 512, 512, 8, 8), (24, 520, 512, 8, 8), (32, 384, 512, 8, 8),
