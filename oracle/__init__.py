@@ -77,12 +77,11 @@ class Oracle:
         lib.oracle_conv3x3_bias_grad_at.argtypes = [_D, _i, _i, _i, _i, _I64, _n, _D]
         lib.oracle_act_forward.argtypes = [_D, _D, _n, _i]
         lib.oracle_act_grad.argtypes = [_D, _D, _D, _n, _i]
-        lib.oracle_act_grad_bf16.argtypes = [_D, _D, _D, _n, _i]
         for f in ("oracle_conv3x3_fwd", "oracle_conv3x3_bwd_data",
                   "oracle_conv3x3_bwd_weight", "oracle_conv3x3_fwd_at",
                   "oracle_conv3x3_bwd_data_at", "oracle_conv3x3_bwd_weight_at",
                   "oracle_conv3x3_bias_grad_at", "oracle_act_forward", "oracle_act_grad",
-                  "oracle_act_grad_bf16", "oracle_num_threads"):
+                  "oracle_num_threads"):
             getattr(lib, f).restype = _i
         self.lib = lib
 
@@ -162,14 +161,12 @@ class Oracle:
         _check(self.lib.oracle_act_forward(_p(z), _p(y), z.size, act), "act_forward")
         return y
 
-    def act_grad(self, gy, z, act, bf16=False):
-        """g = gy * act'(z), elementwise.  bf16=True: the product is formed in
-        float32 and rounded to bfloat16 (the bfloat16 path's operand)."""
+    def act_grad(self, gy, z, act):
+        """g = gy * act'(z), elementwise, in float64."""
         gy, z = _f64(gy), _f64(z)
         assert gy.shape == z.shape
         g = np.empty_like(gy)
-        f = self.lib.oracle_act_grad_bf16 if bf16 else self.lib.oracle_act_grad
-        _check(f(_p(gy), _p(z), _p(g), gy.size, act), "act_grad")
+        _check(self.lib.oracle_act_grad(_p(gy), _p(z), _p(g), gy.size, act), "act_grad")
         return g
 
     def conv3x3_bias_grad_at(self, g, idx):
@@ -232,7 +229,11 @@ def act_forward(z, act):
 
 
 def act_grad(gy, z, act, bf16=False):
-    return _o().act_grad(gy, z, act, bf16)
+    """g = gy * act'(z).  bf16=True: the bfloat16 operand the bfloat16 path
+    contracts, i.e. that exact product rounded once to the nearest bfloat16
+    value, ties to even (round_to_bf16 below)."""
+    g = _o().act_grad(gy, z, act)
+    return round_to_bf16(g) if bf16 else g
 
 
 def conv3x3_fwd_act(x, w, b, act):

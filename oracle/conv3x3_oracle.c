@@ -37,7 +37,6 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
-#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -263,26 +262,6 @@ static double act_slope(int act, double z) {
   return 1.0;
 }
 
-/* The same slope evaluated in float arithmetic: the bfloat16 path forms
- * g = gy * act'(z) in float32 before rounding it to a bfloat16 operand. */
-static float act_slope_f32(int act, float z) {
-  if (act == 1) {
-    float sg = 1.0f / (1.0f + expf(-z));
-    return sg * (1.0f + z * (1.0f - sg));
-  }
-  if (act == 2) return z > 0.0f ? 1.0f : 0.2f;
-  return 1.0f;
-}
-
-/* float -> bfloat16 -> float, round to nearest, ties to even (finite inputs). */
-static float round_bf16(float v) {
-  uint32_t u;
-  memcpy(&u, &v, sizeof u);
-  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
-  memcpy(&v, &u, sizeof v);
-  return v;
-}
-
 static int bad_act(int act) { return act < 0 || act > 2; }
 
 int oracle_act_forward(const double* z, double* y, int64_t n, int act) {
@@ -296,16 +275,6 @@ int oracle_act_grad(const double* gy, const double* z, double* g, int64_t n, int
   if (!gy || !z || !g || n < 0 || bad_act(act)) return 1;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) g[i] = gy[i] * act_slope(act, z[i]);
-  return 0;
-}
-
-/* bfloat16 path: gy is a bfloat16 value and z a float32 value (both exact in
- * double); g = bf16(float(gy) * act'_f32(float(z))). */
-int oracle_act_grad_bf16(const double* gy, const double* z, double* g, int64_t n, int act) {
-  if (!gy || !z || !g || n < 0 || bad_act(act)) return 1;
-#pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i)
-    g[i] = (double)round_bf16((float)gy[i] * act_slope_f32(act, (float)z[i]));
   return 0;
 }
 

@@ -5,8 +5,8 @@ biased convolution output; the backward multiplies by act'(z)) is checked
 against things other than itself: special values worked out by hand, the
 exact identities silu(z) - silu(-z) = z and silu'(z) + silu'(-z) = 1, torch's
 float64 activations and autograd, central finite differences (elementwise
-and through the whole fused convolution), and torch's float32 -> bfloat16
-rounding for the bfloat16 operand."""
+and through the whole fused convolution), and, for the bfloat16 operand, a
+brute-force nearest-value search over every bfloat16 value."""
 import numpy as np
 import pytest
 import torch
@@ -103,28 +103,62 @@ def test_fused_backward_is_gradient_of_fused_forward(act):
             assert abs((lp - lm) / (2 * h) - grad[i]) < 1e-6, (i, grad[i])
 
 
-def test_bf16_operand_rounding_matches_torch():
-    rng = np.random.default_rng(5)
-    gy32 = rng.normal(size=4000).astype(np.float32)
-    # exact ties and near-ties of the bfloat16 grid
-    ties = (np.arange(1, 65, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
-    gy32 = np.concatenate([gy32, ties, -ties])
-    z = rng.normal(size=gy32.size).astype(np.float32)
-    # identity: g = bf16(gy)
-    g = oracle.act_grad(gy32, z, oracle.ACT_NONE, bf16=True)
-    ref = torch.from_numpy(gy32).bfloat16().double().numpy()
-    assert np.array_equal(g, ref)
-    # leaky ReLU: g = bf16(float32(gy) * float32(slope))
-    g = oracle.act_grad(gy32, z, oracle.ACT_LRELU, bf16=True)
-    slope = torch.where(torch.from_numpy(z) > 0, torch.tensor(1.0), torch.tensor(0.2))
-    ref = (torch.from_numpy(gy32) * slope).bfloat16().double().numpy()
-    assert np.array_equal(g, ref)
-    # SiLU: the float32 slope may differ from torch's own float32 evaluation
-    # in the last bit, so allow one bfloat16 step
-    g = oracle.act_grad(gy32, z, oracle.ACT_SILU, bf16=True)
+def _bf16_grid():
+    """Every finite non-negative bfloat16 value, ascending, with its bit
+    pattern (the brute-force rounding below searches this list)."""
+    bits = np.arange(0, 0x7f80, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    return vals, bits
+
+
+def _nearest_bf16(x):
+    """Round to the nearest bfloat16 value, ties to the even bit pattern,
+    by search over the whole grid (independent of round_to_bf16)."""
+    vals, bits = _bf16_grid()
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a), 1, vals.size - 1)
+    lo = hi - 1
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(bits[lo] % 2 == 0, lo, hi)))
+    return np.sign(x) * vals[pick]
+
+
+def _torch_slope(z, act):
+    zt = torch.from_numpy(np.asarray(z, np.float64)).requires_grad_(True)
+    f = torch.nn.functional.silu if act == oracle.ACT_SILU else \
+        (lambda t: torch.nn.functional.leaky_relu(t, negative_slope=0.2))
+    (s,) = torch.autograd.grad(f(zt), zt, torch.ones_like(zt))
+    return s.numpy()
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_bf16_operand_is_exact_product_rounded_once(act):
+    """The bfloat16 path's operand: g = gy * act'(z) exactly, rounded once to
+    the nearest bfloat16 value (ties to even).  gy is a bfloat16 gradient and
+    z the float32 pre-activation."""
+    rng = np.random.default_rng(5 + act)
+    gy = torch.from_numpy(rng.normal(size=20000)).bfloat16().double().numpy()
+    z = rng.normal(0.0, 3.0, size=20000).astype(np.float32).astype(np.float64)
+    slope = np.ones_like(z) if act == oracle.ACT_NONE else _torch_slope(z, act)
+    g = oracle.act_grad(gy, z, act, bf16=True)
+    assert np.array_equal(g, _nearest_bf16(gy * slope))
+    # every value is a bfloat16 value
+    assert np.array_equal(g, torch.from_numpy(g).float().bfloat16().double().numpy())
+
+
+def test_bf16_operand_does_not_round_through_float32():
+    """Where the float32 product gy32 * silu'32(z) lands on the other side of a
+    bfloat16 rounding boundary than the exact product, the operand follows
+    the exact product.  The search keeps only such elements, so a
+    float32-product oracle would fail every one of them."""
+    rng = np.random.default_rng(11)
+    gy = torch.from_numpy(rng.normal(size=2_000_000)).bfloat16().double().numpy()
+    z = rng.normal(0.0, 3.0, size=gy.size).astype(np.float32)
     zt = torch.from_numpy(z).requires_grad_(True)
-    (slope,) = torch.autograd.grad(torch.nn.functional.silu(zt), zt, torch.ones_like(zt))
-    ref = (torch.from_numpy(gy32) * slope).bfloat16().double().numpy()
-    step = np.abs(ref) * 2.0 ** -7 + 1e-30
-    assert np.all(np.abs(g - ref) <= step)
-    assert np.mean(g == ref) > 0.99
+    (s32,) = torch.autograd.grad(torch.nn.functional.silu(zt), zt, torch.ones_like(zt))
+    f32_path = (torch.from_numpy(gy.astype(np.float32)) * s32).bfloat16().double().numpy()
+    exact = _nearest_bf16(gy * _torch_slope(z, oracle.ACT_SILU))
+    differ = f32_path != exact
+    assert differ.sum() >= 10
+    g = oracle.act_grad(gy[differ], z[differ].astype(np.float64), oracle.ACT_SILU, bf16=True)
+    assert np.array_equal(g, exact[differ])
