@@ -25,6 +25,18 @@ int check_dims(int N, int C, int K, int H, int W) {
   return CONV3X3_OK;
 }
 
+// The kernels address every tensor through 32-bit buffer offsets, so each
+// one (counted as float32: the outputs y, dx, dw are float32 in every mode)
+// must stay below 2 GiB: N*C*H*W, N*K*H*W and 9*K*C below 2^29 elements.
+// H, W: the call's largest grid.
+int check_bytes(int N, int C, int K, int H, int W) {
+  constexpr long kLimit = 2147483648L;
+  const long hw = (long)H * W;
+  if (4L * N * C * hw >= kLimit || 4L * N * K * hw >= kLimit || 36L * K * C >= kLimit)
+    return CONV3X3_ERR_UNSUPPORTED;
+  return CONV3X3_OK;
+}
+
 int check_dtype(int dtype) {
   return (dtype == CONV3X3_F32 || dtype == CONV3X3_BF16 || dtype == CONV3X3_BF16_IO)
              ? CONV3X3_OK
@@ -108,6 +120,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (!parts_present(x, C) || !w || !y) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
   if (rc) return rc;
+  rc = check_bytes(N, C, K, H, W);
+  if (rc) return rc;
   rc = check_dtype(dtype);
   if (rc) return rc;
   rc = check_act(act);
@@ -173,6 +187,8 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   if (!g || !w || !parts_present(dx, C)) return CONV3X3_ERR_NULL_POINTER;
   if (pr.on() && !px) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  rc = check_bytes(N, C, K, H, W);
   if (rc) return rc;
   rc = check_dtype(dtype);
   if (rc) return rc;
@@ -241,6 +257,8 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   // (H, W are x's, g is H/2 x W/2)
   if (!parts_present(x, C) || !g || !dw) return CONV3X3_ERR_NULL_POINTER;
   int rc = check_dims(N, C, K, H, W);
+  if (rc) return rc;
+  rc = check_bytes(N, C, K, H, W);
   if (rc) return rc;
   rc = check_dtype(dtype);
   if (rc) return rc;
@@ -349,7 +367,7 @@ const char* conv3x3_status_string(int status) {
     case CONV3X3_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case CONV3X3_ERR_BAD_PASS: return "unknown pass";
     case CONV3X3_ERR_BAD_ACT: return "unknown activation (expected a conv3x3_act_t value)";
-    case CONV3X3_ERR_UNSUPPORTED: return "this fusion is not provided for this dtype or size";
+    case CONV3X3_ERR_UNSUPPORTED: return "not provided for this dtype or size (fusions by dtype; every tensor must be below 2 GiB as float32)";
     default: return "unknown status code";
   }
 }

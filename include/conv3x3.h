@@ -47,7 +47,12 @@
  * synchronisation, as usual for HIP.
  *
  * Size limits: N, C, K, H, W >= 1; every tensor holds fewer than 2^31
- * elements (else CONV3X3_ERR_BAD_SHAPE).
+ * elements (else CONV3X3_ERR_BAD_SHAPE).  The compute entry points also
+ * need every tensor they touch below 2 GiB counted as float32 -- N*C*H*W,
+ * N*K*H*W and 9*K*C each below 2^29, H x W being the call's largest grid --
+ * because the kernels address tensors through 32-bit buffer offsets; larger
+ * problems return CONV3X3_ERR_UNSUPPORTED before anything is enqueued
+ * (the plan and workspace-size queries still answer for them).
  */
 #ifndef CONV3X3_H
 #define CONV3X3_H
@@ -268,13 +273,19 @@ int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* sh
  *               bytes (may be NULL when that size is 0); its contents are
  *               scratch, it must not overlap an input or output.
  * With a workspace, a problem whose output tiles are too few to fill the
- * device (small images: bfloat16 8 x 8 and 16 x 16 layers, float32 8 x 8
- * layers with 256+ channels) splits its channel reduction over up to 8
- * (float32: 2) workgroups per tile; each writes its
- * partial sums (float32, one output-sized slot per slice) to the workspace
- * and a second kernel on the same stream adds the slots in slice order --
- * no atomics, bitwise-reproducible results (which can differ in the last
- * bits from the unsplit entry points: another summation order).
+ * device splits its channel reduction over several workgroups per tile:
+ *   - bfloat16, largest tile (256 pixels x 128 channels) short of a round of
+ *     256 workgroups and at least 32 fills of 16 channels: 2 to 8 slices,
+ *     as long as the split grid reaches 192 workgroups;
+ *   - either dtype, smallest tile (64 x 64) whose grid is 128 to 256
+ *     workgroups, with at least 32 fills (16 channels bfloat16, 8 float32):
+ *     2 slices (bfloat16) or 4 (float32).
+ * Plain passes only (no activation, prologue, resampling or concatenation).
+ * Each slice writes its partial sums (float32, one output-sized slot per
+ * slice) to the workspace and a second kernel on the same stream adds the
+ * slots in slice order -- no atomics, bitwise-reproducible results (which
+ * can differ in the last bits from the unsplit entry points: another
+ * summation order).  The plan's `split` field reports the slices.
  */
 size_t conv3x3_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype);
 
@@ -368,7 +379,8 @@ typedef struct {
   int threads;         /* threads per workgroup */
   int grid_x, grid_y, grid_z;
   int lds_bytes;       /* static LDS per workgroup */
-  int split;           /* bwd_weight: number of reduction slices (1 = none) */
+  int split;           /* reduction slices (1 = none): bwd_weight's split-K, and the
+                          forward / backward-data split of conv3x3_workspace_size */
   size_t workspace_bytes;
 } conv3x3_plan_t;
 

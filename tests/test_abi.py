@@ -311,3 +311,19 @@ def test_s2_argument_checks():
     assert L.conv3x3_fwd_s2(X, Wt, B, X, *d, 0, None) == S["ERR_ALIAS"]
     assert L.conv3x3_bwd_weight_s2(X, G, Y, B, None, 0, 2, 64, 64, 64, 64, 0, None) == \
         S["ERR_WORKSPACE"]
+
+
+@pytest.mark.parametrize("dims", [(1, 1 << 13, 4, 256, 256),    # x: 2^29 floats = 2 GiB
+                                  (2, 4, 1 << 12, 256, 256),    # y, g: 2 GiB
+                                  (1, 1 << 13, 1 << 13, 1, 1)])  # w, dw: 2.25 GiB
+def test_tensors_of_2gib_or_more_unsupported(dims):
+    """Every tensor a call touches must be below 2 GiB (counted as float32):
+    larger ones are refused before anything is enqueued."""
+    N, C, K, H, W = dims
+    un = S["ERR_UNSUPPORTED"]
+    for dt in (0, 1):
+        assert L.conv3x3_fwd(X, Wt, B, Y, N, C, K, H, W, dt, None) == un
+        assert L.conv3x3_bwd_data(G, Wt, Y, N, C, K, H, W, dt, None) == un
+        assert L.conv3x3_bwd_weight(X, G, Y, B, WS, 1 << 40, N, C, K, H, W, dt, None) == un
+        assert L.conv3x3_fwd_ws(X, Wt, B, Y, WS, 1 << 40, N, C, K, H, W, dt, None) == un
+
