@@ -1,21 +1,28 @@
 """Benchmark of the gfx950 conv3x3 path: forward + bias, backward-data and
-backward-weight (+ bias gradient) of one UNet stem layer on one GPU.
+backward-weight (+ bias gradient) over the 32 convolutions of one 64x64
+diffusion-UNet training step, on one GPU.
 
 One step = the whole path over one batch of seeded synthetic input already
-resident in device memory: conv3x3_fwd, conv3x3_bwd_data, conv3x3_bwd_weight.
-The workload is the UNet stem convolution at 64x64 image resolution
-(N=32, C=64 -> K=64, H=W=64, float32); the diffusion UNet these layers come
-from is trained on ImageNet 64x64 in the sources, and seeded N(0,1)
-activations / gradients with Kaiming-uniform weights stand in for that data.
+resident in device memory: conv3x3_fwd, conv3x3_bwd_data and
+conv3x3_bwd_weight of every stride-1 3x3 convolution of the UNet (N=32,
+channel multipliers [1,2,3,4] on base 128 at 64/32/16/8 pixels, two convs
+per residual block, two blocks per level, down and up paths, the up-path
+inputs carrying the skip concatenation), float32; the same sweep in
+bfloat16 (bf16 x, w, g; float32 accumulation and outputs) is reported in an
+extra key.  The diffusion UNet these layers come from is trained on
+ImageNet 64x64 in the sources; seeded N(0,1) activations / gradients with
+Kaiming-uniform weights stand in for that data.
 
 Prints ONE JSON line: throughput in TFLOP/s (2*N*H*W*C*K*9 per pass, three
-passes per step), the roofline figure of the slowest kernel (timed with HIP
-events on the stream the kernels run on) and the fp64 CPU oracle's
-throughput on a bounded sample of the same layer (test infrastructure, timed
-only as a reported baseline).
+passes per layer), per-pass median / p10 / p90 times from HIP events on the
+stream the kernels run on, the roofline figure of the pass family that
+takes the most time, and the fp64 CPU oracle's throughput on a sampled
+subset of the same outputs (test infrastructure, timed only as a reported
+baseline; its full-sweep time is extrapolated from the sample).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--sweep OUT.json]
+                    [--workload unet_sweep|stem|small|mid|bottleneck]
+                    [--sweep OUT.json] [--cold] [--detail OUT.json]
 """
 import argparse
 import json
@@ -29,13 +36,222 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "conv3x3 fwd+bwd TFLOP/s and % of MFMA/HBM roofline on 1 MI355X"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_f32_unet_stem_32x64to64_64x64_traffic.json")
-# Kernels launched by each pass of the stem layer (name prefixes in profiler output).
-PASS_KERNELS = {"fwd": ["conv3x3::fwd_f32_kernel<0,"],
-                "bwd_data": ["conv3x3::fwd_f32_kernel<1,"],
-                "bwd_weight": ["conv3x3::wgrad_f32_kernel<", "conv3x3::wgrad_reduce"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3_f32_unet_sweep_32layers_traffic.json")
+PASSES = ("fwd", "bwd_data", "bwd_weight")
+# The main kernel of each pass, by dtype (name prefixes in profiler output).
+# A pass may add a second, fixed-order reduce kernel right after its main
+# kernel on the same stream: split_reduce_kernel (split forward /
+# backward-data) or wgrad_reduce*_kernel (backward-weight split-K); profile
+# summaries count it toward the pass whose main kernel precedes it.
+MAIN_KERNELS = {("f32", "fwd"): "conv3x3::fwd_f32_kernel<0,",
+                ("f32", "bwd_data"): "conv3x3::fwd_f32_kernel<1,",
+                ("f32", "bwd_weight"): "conv3x3::wgrad_f32_kernel<",
+                ("bf16", "fwd"): "conv3x3::fwd_bf16_kernel<0,",
+                ("bf16", "bwd_data"): "conv3x3::fwd_bf16_kernel<1,",
+                ("bf16", "bwd_weight"): "conv3x3::wgrad_bf16_kernel<"}
+REDUCE_KERNELS = ("conv3x3::split_reduce_kernel", "conv3x3::wgrad_reduce")
+
+
+def pass_kernels(dtype, pass_):
+    """Name prefixes of the kernels one pass launches."""
+    return [MAIN_KERNELS[(dtype, pass_)]] + list(REDUCE_KERNELS)
+
+
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # dense MFMA peaks, MI355X
 PEAK_HBM_GBS = 8000.0
+
+
+def _kernel_name(row):
+    return row["Kernel_Name"].replace("void ", "")
+
+
+def attribute_passes(rows):
+    """Group profiler rows (dicts with Kernel_Name and Dispatch_Id) into
+    pass launches: each main kernel starts a launch of its (dtype, pass), and
+    a reduce kernel joins the launch of the main kernel dispatched before it.
+    Returns a list of ((dtype, pass), [rows]) in dispatch order."""
+    launches = []
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        name = _kernel_name(r)
+        fam = next((k for k, pre in MAIN_KERNELS.items() if name.startswith(pre)), None)
+        if fam is not None:
+            launches.append((fam, [r]))
+        elif name.startswith(REDUCE_KERNELS) and launches:
+            launches[-1][1].append(r)
+    return launches
+
+
+def summarize_trace(trace_csv):
+    """Per (dtype, pass): number of pass launches, total and average
+    duration (ns, main kernel + its reduce), and per-kernel averages, from a
+    rocprofv3 kernel-trace CSV."""
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(trace_csv)))
+    out = {}
+    for fam, rs in attribute_passes(rows):
+        d = out.setdefault(f"{fam[0]}/{fam[1]}", {"launches": 0, "total_ns": 0, "kernels": {}})
+        d["launches"] += 1
+        for r in rs:
+            dt = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            d["total_ns"] += dt
+            d["kernels"].setdefault(_kernel_name(r).split("(")[0], []).append(dt)
+    for d in out.values():
+        d["avg_us_per_launch"] = d["total_ns"] / d["launches"] / 1e3
+        d["kernels"] = {k: {"dispatches": len(v), "avg_us": statistics.mean(v) / 1e3}
+                        for k, v in d["kernels"].items()}
+    return out
+
+
+def summarize_counters(csv_paths):
+    """Per (dtype, pass): sums of every counter over all launches and the
+    launch count, from rocprofv3 --pmc counter-collection CSVs (one row per
+    dispatch and counter).  Derived: MFMA busy fraction =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 4 SIMDs * 256 CUs), MFMA
+    FLOPs = 512 * SQ_INSTS_VALU_MFMA_MOPS_*, LDS bank-conflict fraction =
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    import csv
+    rows = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            rows.setdefault(key, {"Dispatch_Id": r["Dispatch_Id"],
+                                  "Kernel_Name": r["Kernel_Name"]})[r["Counter_Name"]] = \
+                float(r["Counter_Value"])
+    out = {}
+    for fam, rs in attribute_passes(list(rows.values())):
+        d = out.setdefault(f"{fam[0]}/{fam[1]}", {"launches": 0})
+        d["launches"] += 1
+        for r in rs[:1]:  # main kernel only: the reduce has no MFMA work
+            for k, v in r.items():
+                if k not in ("Dispatch_Id", "Kernel_Name"):
+                    d[k] = d.get(k, 0.0) + v
+    for d in out.values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("GRBM_GUI_ACTIVE"):
+            d["mfma_busy_frac"] = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] * 4 * 256)
+        for dt in ("F32", "BF16"):
+            if f"SQ_INSTS_VALU_MFMA_MOPS_{dt}" in d:
+                d[f"mfma_flops_{dt.lower()}"] = 512.0 * d[f"SQ_INSTS_VALU_MFMA_MOPS_{dt}"]
+        if d.get("SQ_LDS_IDX_ACTIVE"):
+            d["lds_bank_conflict_frac"] = d.get("SQ_LDS_BANK_CONFLICT", 0.0) / d["SQ_LDS_IDX_ACTIVE"]
+    return out
+
+
+def _per_launch(rows_by_family, nlayers):
+    """Split each family's launches (dispatch order) by layer: launch i of a
+    family belongs to layer i mod nlayers (every step runs the layers in
+    order)."""
+    out = {}
+    for fam, launches in rows_by_family.items():
+        for i, rs in enumerate(launches):
+            out.setdefault((fam, i % nlayers), []).append(rs)
+    return out
+
+
+def profile_report(trace_csv, counter_csvs, layers_by_dtype, title, commands, focus=()):
+    """Markdown summary of one profiled bench run: per pass family, the
+    trace's average time per launch (main kernel + its reduce) and, from
+    the counter runs, MFMA busy fraction, MFMA FLOPs against the algorithmic
+    count and the LDS bank-conflict fraction; then the same per layer for
+    the layers whose names contain one of the `focus` strings.
+    layers_by_dtype: dtype -> the layers of that dtype in timing order."""
+    import csv
+    trace = list(csv.DictReader(open(trace_csv)))
+    fams = {}
+    for fam, rs in attribute_passes(trace):
+        fams.setdefault(fam, []).append(rs)
+    ctr = {}
+    if counter_csvs:
+        rows = {}
+        for path in counter_csvs:
+            for r in csv.DictReader(open(path)):
+                d = rows.setdefault(r["Dispatch_Id"], {"Dispatch_Id": r["Dispatch_Id"],
+                                                       "Kernel_Name": r["Kernel_Name"],
+                                                       "Start_Timestamp": r["Start_Timestamp"],
+                                                       "End_Timestamp": r["End_Timestamp"]})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+        for fam, rs in attribute_passes(list(rows.values())):
+            ctr.setdefault(fam, []).append(rs)
+    order = sorted(fams, key=lambda f: (f[0] != "f32", PASSES.index(f[1])))
+
+    def dur(rs):
+        return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs) / 1e3
+
+    def counters(launches):
+        tot = {}
+        for rs in launches:
+            m = rs[0]  # the main kernel (the reduce has no MFMA work)
+            for k in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                      "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
+                tot[k] = tot.get(k, 0.0) + m.get(k, 0.0)
+            tot["ns"] = tot.get("ns", 0.0) + int(m["End_Timestamp"]) - int(m["Start_Timestamp"])
+        if not tot.get("GRBM_GUI_ACTIVE"):
+            return None
+        # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (8 x the clock per ns)
+        busy = tot["SQ_VALU_MFMA_BUSY_CYCLES"] / (tot["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        flops = 512.0 * (tot["SQ_INSTS_VALU_MFMA_MOPS_F32"] + tot["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+        lds = (tot["SQ_LDS_BANK_CONFLICT"] / tot["SQ_LDS_IDX_ACTIVE"]
+               if tot["SQ_LDS_IDX_ACTIVE"] else 0.0)
+        return busy, flops, lds, tot["GRBM_GUI_ACTIVE"] / tot["ns"]
+
+    lines = [f"# {title}", "", "Commands (from /tmp with TMPDIR=/tmp; ROOT = the repository):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Per pass family over all its layers.  Time: kernel-trace duration per pass "
+              "launch (main kernel + its reduce).  MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / "
+              "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); GRBM_GUI_ACTIVE is reported summed over "
+              "the 8 XCDs (the last column is that sum per ns).  MFMA FLOPs: 512 x "
+              "SQ_INSTS_VALU_MFMA_MOPS_*, against 2*N*H*W*C*K*9 per layer.  LDS conflict: "
+              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+              "| pass family | launches | avg us / launch | TFLOP/s | of peak | MFMA busy | "
+              "MFMA FLOPs / algorithmic | LDS conflict | GRBM cycles / ns |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for fam in order:
+        layers = layers_by_dtype.get(fam[0], [])
+        if not layers:
+            continue
+        n = len(layers)
+        launches = fams[fam]
+        t = sum(dur(rs) for rs in launches) / len(launches)
+        gf = sum(flops_per_pass(*l.shape) for l in layers) / 1e9
+        tf = gf / (t * n) * 1e3 if t else 0.0
+        c = counters(ctr.get(fam, []))
+        extra = ["-"] * 4 if c is None else [
+            f"{c[0]:.3f}", f"{c[1] / (gf * 1e9 * len(ctr[fam]) / n):.4f}", f"{c[2]:.3f}",
+            f"{c[3]:.2f}"]
+        lines.append(f"| {fam[0]}/{fam[1]} | {len(launches)} ({len(launches) / n:g} per layer) "
+                     f"| {t:.1f} | {tf:.1f} | {tf / PEAK_TFLOPS[fam[0]]:.3f} | "
+                     + " | ".join(extra) + " |")
+    lines += ["", "Kernels per family (dispatches, average us):", ""]
+    for fam in order:
+        ks = {}
+        for rs in fams[fam]:
+            for r in rs:
+                ks.setdefault(_kernel_name(r).split("(")[0], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append(f"- {fam[0]}/{fam[1]}: " + "; ".join(
+            f"`{k}` {len(v)}, {sum(v) / len(v):.1f}" for k, v in sorted(ks.items())))
+    if focus:
+        lines += ["", "Selected layers (trace average per launch; counters as above):", "",
+                  "| layer | pass | avg us | TFLOP/s | of peak | MFMA busy | LDS conflict |",
+                  "|---|---|---|---|---|---|---|"]
+        for dt, layers in layers_by_dtype.items():
+            n = len(layers)
+            tl = _per_launch({f: v for f, v in fams.items() if f[0] == dt}, n)
+            cl = _per_launch({f: v for f, v in ctr.items() if f[0] == dt}, n)
+            for i, layer in enumerate(layers):
+                if not any(k in layer.name for k in focus):
+                    continue
+                for fam in order:
+                    if (fam, i) not in tl:
+                        continue
+                    ls = tl[(fam, i)]
+                    t = sum(dur(rs) for rs in ls) / len(ls)
+                    tf = flops_per_pass(*layer.shape) / (t * 1e-6) / 1e12
+                    c = counters(cl.get((fam, i), []))
+                    cc = "- | -" if c is None else f"{c[0]:.3f} | {c[2]:.3f}"
+                    lines.append(f"| {layer.name} | {fam[1]} | {t:.1f} | {tf:.1f} | "
+                                 f"{tf / PEAK_TFLOPS[fam[0]]:.3f} | {cc} |")
+    return "\n".join(lines) + "\n"
 
 
 def library_source_digest():
@@ -51,56 +267,62 @@ def library_source_digest():
 
 
 def record_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
-    of `bench.py --copy-calibration-mb 512` into per-pass HBM bytes.  Each
-    counter is scaled so that the 512 MiB device copy reads what it moved."""
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-calibration-mb 512` into HBM bytes per pass
+    launch.  Each counter is scaled so that the 512 MiB device copy reads
+    what it moved; a pass launch counts its main kernel and its reduce."""
     import csv
     import statistics
 
-    def per_kernel(path, counter):
-        vals = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == counter:
-                name = r["Kernel_Name"].replace("void ", "")
-                vals.setdefault((name, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
-        return vals
+    def by_dispatch(path, counter):
+        return {r["Dispatch_Id"]: r for r in csv.DictReader(open(path))
+                if r["Counter_Name"] == counter}
 
-    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    big = max((k for k in write if k[0].startswith("__amd_rocclr_copyBuffer")), key=lambda k: k[1])
-    copy_kib = 512 * 1024
-    f_factor = copy_kib / statistics.median(fetch[big])
-    w_factor = copy_kib / statistics.median(write[big])
-    kernels = {}
-    for (name, grid), v in fetch.items():
-        if name.startswith("conv3x3::"):
-            kernels[name] = {"grid": grid, "fetch_kib": statistics.median(v),
-                             "write_kib": statistics.median(write[(name, grid)])}
+    fetch, write = by_dispatch(fetch_csv, "FETCH_SIZE"), by_dispatch(write_csv, "WRITE_SIZE")
+
+    def copy_kib(rows):
+        big = [r for r in rows.values() if _kernel_name(r).startswith("__amd_rocclr_copyBuffer")]
+        grid = max(int(r["Grid_Size"]) for r in big)
+        return statistics.median(float(r["Counter_Value"]) for r in big
+                                 if int(r["Grid_Size"]) == grid)
+
+    copy_kib_moved = 512 * 1024
+    f_factor = copy_kib_moved / copy_kib(fetch)
+    w_factor = copy_kib_moved / copy_kib(write)
     passes = {}
-    for p, prefixes in PASS_KERNELS.items():
-        ks = [k for k in kernels if any(k.startswith(q) for q in prefixes)]
-        passes[p] = {"kernels": ks, "hbm_bytes": sum(
-            (kernels[k]["fetch_kib"] * f_factor + kernels[k]["write_kib"] * w_factor) * 1024
-            for k in ks)}
+    for fam, rs in attribute_passes(list(fetch.values())):
+        d = passes.setdefault(f"{fam[0]}/{fam[1]}", {"launches": 0, "hbm_bytes_total": 0.0,
+                                                      "kernels": set()})
+        d["launches"] += 1
+        for r in rs:
+            w = write.get(r["Dispatch_Id"])
+            wk = float(w["Counter_Value"]) if w is not None else 0.0
+            d["hbm_bytes_total"] += (float(r["Counter_Value"]) * f_factor + wk * w_factor) * 1024
+            d["kernels"].add(_kernel_name(r).split("(")[0])
+    for d in passes.values():
+        d["hbm_bytes"] = d["hbm_bytes_total"] / d["launches"]
+        d["kernels"] = sorted(d["kernels"])
     rec = {"source_digest": library_source_digest(),
-           "calibration": {"copy_mib": 512, "fetch_kib_read": statistics.median(fetch[big]),
-                           "write_kib_read": statistics.median(write[big]),
+           "calibration": {"copy_mib": 512, "fetch_kib_read": copy_kib(fetch),
+                           "write_kib_read": copy_kib(write),
                            "fetch_factor": f_factor, "write_factor": w_factor},
-           "kernels": kernels, "passes": passes}
+           "passes": passes}
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
     return rec
 
 
-def recorded_traffic(pass_name):
-    """HBM bytes per launch of a pass, or None if not recorded for these sources."""
+def recorded_traffic(family, path=None):
+    """HBM bytes per launch of a pass family ("f32/bwd_weight"), or None if
+    not recorded for these kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path or TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
     if rec.get("source_digest") != library_source_digest():
         return None
-    b = rec.get("passes", {}).get(pass_name, {}).get("hbm_bytes")
+    b = rec.get("passes", {}).get(family, {}).get("hbm_bytes")
     return int(b) if b else None
 
 
@@ -144,13 +366,13 @@ class LayerRun:
     entry points (GroupNorm-apply + SiLU in the loader; float32)."""
 
     def __init__(self, layer, act="none", cat=False, prologue=False, out_bf16=False,
-                 split=True):
+                 split=True, inputs=None):
         import torch
         import diffusion_unet_x3_amd as lib3
         import workloads as wl
         self.lib3, self.layer = lib3, layer
         dev = torch.device("cuda", 0)
-        inp = wl.make_inputs(layer)
+        inp = inputs if inputs is not None else wl.make_inputs(layer)
         self.x, self.w, self.g = (inp[k].to(dev) for k in ("x", "w", "g"))
         self.b = inp["b"].to(dev)
         N, C, K, H, W = layer.shape
@@ -184,6 +406,14 @@ class LayerRun:
         else:
             ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        # split forward / backward-data workspaces, allocated here and not in
+        # the timed calls
+        self.ws_f = self.ws_d = None
+        if split:
+            n_f = lib3.conv3x3_workspace_size(lib3.PASS_FWD, N, C, K, H, W, code)
+            n_d = lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, N, C, K, H, W, code)
+            self.ws_f = torch.empty(max(n_f, 1), dtype=torch.uint8, device=dev)
+            self.ws_d = torch.empty(max(n_d, 1), dtype=torch.uint8, device=dev)
 
     def concat_copy_ms(self, steps=10):
         """Average time of the copy that forms [x0 ; x1] as one tensor (what
@@ -209,7 +439,8 @@ class LayerRun:
         elif self.act:
             self.lib3.conv3x3_fwd_act(self.x, self.w, self.b, act=self.act, out=self.y, z=self.z)
         else:
-            self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y, split=self.split)
+            self.lib3.conv3x3_fwd(self.x, self.w, self.b, out=self.y, split=self.split,
+                                  workspace=self.ws_f)
 
     def bwd_data(self):
         if self.pro:
@@ -221,7 +452,8 @@ class LayerRun:
         elif self.fused_bwd:
             self.lib3.conv3x3_bwd_data_act(self.g, self.z, self.w, act=self.act, out=self.dx)
         else:
-            self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx, split=self.split)
+            self.lib3.conv3x3_bwd_data(self.g, self.w, out=self.dx, split=self.split,
+                                       workspace=self.ws_d)
 
     def bwd_weight(self):
         if self.pro:
@@ -301,34 +533,140 @@ class S2Run:
                     self.x, self.g, dw=self.dw, db=self.db, workspace=self.ws))]
 
 
-def time_layer(run, steps, warmup):
-    """Per-pass average ms (events between the passes) and per-step ms."""
+def _stats(v):
+    """mean, median, p10, p90 of a list of times (ms)."""
+    import statistics
+    q = sorted(v)
+
+    def pct(p):
+        k = (len(q) - 1) * p
+        lo = int(k)
+        hi = min(lo + 1, len(q) - 1)
+        return q[lo] + (q[hi] - q[lo]) * (k - lo)
+    return {"mean": statistics.mean(q), "median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)}
+
+
+def time_runs(runs, steps, warmup, flush=None):
+    """Time `steps` steps of every pass of every run, in order, with HIP
+    events recorded between the passes on the current stream.  Returns the
+    per-step ms (events around the whole step loop) and, per run, a dict
+    pass -> list of per-step ms.  flush: a tensor overwritten before every
+    pass, outside its event pair (cold caches); the step time then includes
+    the flushes and only the pass times are meaningful."""
     import torch
     for _ in range(warmup):
-        for _, f in run.passes():
-            f()
+        for run in runs:
+            for _, f in run.passes():
+                f()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    npass = sum(len(run.passes()) for run in runs)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(npass)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        ev[i][0].record()
-        for j, (_, f) in enumerate(run.passes()):
-            f()
-            ev[i][j + 1].record()
+        j = 0
+        for run in runs:
+            for _, f in run.passes():
+                if flush is not None:
+                    flush.fill_(i + j)
+                ev[i][j][0].record()
+                f()
+                ev[i][j][1].record()
+                j += 1
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    per = {}
-    for j, (name, _) in enumerate(run.passes()):
-        per[name] = sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
-    return total_ms / steps, per
+    per = []
+    j = 0
+    for run in runs:
+        d = {}
+        for name, _ in run.passes():
+            d[name] = [ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]
+            j += 1
+        per.append(d)
+    return t0.elapsed_time(t1) / steps, per
+
+
+def time_layer(run, steps, warmup):
+    """Per-pass average ms and per-step ms of one run."""
+    ms, per = time_runs([run], steps, warmup)
+    return ms, {p: _stats(v)["mean"] for p, v in per[0].items()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _sample_idx(rng, shape, n):
+    """n seeded flat indices into a tensor of `shape`, always including the
+    first and last element."""
+    import numpy as np
+    total = int(np.prod(shape))
+    n = max(2, min(n, total))
+    idx = rng.choice(total, size=n - 2, replace=False) if total > n else np.arange(total)
+    return np.unique(np.concatenate([idx, [0, total - 1]]))
+
+
+def cpu_baseline_sampled(layers, inputs, budget_s=15.0):
+    """fp64 oracle on a seeded sample of the outputs of every layer's three
+    passes: y and dx elements (one output each, 18*C or 18*K FLOPs) and dw
+    elements (2*N*H*W FLOPs), with the same padded-tap FLOP count as the
+    GPU figure (only the oracle calls are timed).  Returns the
+    rate in TFLOP/s and the full sweep's time extrapolated from it.  The
+    sample grows until one run takes at least 60% of budget_s; only the
+    last run is reported."""
+    import numpy as np
+    import oracle
+
+    def run(scale):
+        rng = np.random.default_rng(12345)
+        dt, fl = 0.0, 0.0
+        for layer in layers:
+            inp = inputs[layer.name]
+            x, w, b, g = (oracle._f64(inp[k]) for k in ("x", "w", "b", "g"))
+            N, C, K, H, W = layer.shape
+            n_out = max(2, int(scale * 4096))
+            n_dw = max(2, int(scale * 64))
+            iy = _sample_idx(rng, (N, K, H, W), n_out)
+            ix = _sample_idx(rng, (N, C, H, W), n_out)
+            iw = _sample_idx(rng, (K, C, 3, 3), n_dw)
+            t = time.perf_counter()
+            oracle.conv3x3_fwd_at(x, w, b, iy)
+            oracle.conv3x3_bwd_data_at(g, w, ix)
+            oracle.conv3x3_bwd_weight_at(x, g, iw)
+            dt += time.perf_counter() - t
+            fl += iy.size * 18.0 * C + ix.size * 18.0 * K + iw.size * 2.0 * N * H * W
+        return dt, fl
+
+    scale = 0.05
+    for _ in range(4):
+        dt, fl = run(scale)
+        if dt >= 0.6 * budget_s or scale >= 1000.0:
+            break
+        scale = min(1000.0, scale * budget_s / max(dt, 1e-3))
+    rate = fl / dt
+    total = sum(3 * flops_per_pass(*layer.shape) for layer in layers)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"seeded sample of every layer's outputs, all {len(layers)} layers: "
+                      f"{max(2, int(scale * 4096))} y and dx elements and "
+                      f"{max(2, int(scale * 64))} dw elements per layer ({fl / 1e9:.1f} GFLOP "
+                      f"fp64 in {dt:.1f} s); full sweep extrapolated to "
+                      f"{total / rate / 3600:.2f} h at this rate; cpu: {cpu_model()}",
+            "extrapolated_full_step_s": total / rate}
 
 
 def cpu_baseline(layer, budget_s=15.0, min_s=10.0):
-    """fp64 oracle on the layer's shape with the batch cut to fit the budget."""
+    """fp64 oracle on one layer's shape with the batch cut to fit the budget."""
     import oracle
     import workloads as wl
     from dataclasses import replace
@@ -357,7 +695,57 @@ def cpu_baseline(layer, budget_s=15.0, min_s=10.0):
             "kind": "oracle",
             "sample": f"all three passes of the same layer at N={n} of {N} images, "
                       f"{reps} run(s) ({fl / 1e9:.1f} GFLOP fp64, {dt:.1f} s); "
-                      f"cpu: {platform.processor() or platform.machine()}"}
+                      f"cpu: {cpu_model()}"}
+
+
+def measure_layers(layers, dtype, inputs, steps, warmup, flush=None, act="none"):
+    """Time the three passes of every layer (one step = all of them, in
+    order).  Returns (step ms, per-layer rows with per-pass statistics,
+    per-pass totals).  act: the *_act entry points (fused activation)."""
+    import torch
+    runs = [LayerRun(layer, act, inputs=inputs[layer.name]) for layer in layers]
+    ms, per = time_runs(runs, steps, warmup, flush)
+    del runs
+    torch.cuda.empty_cache()
+    rows, fam = [], {p: {"ms": 0.0, "gflop": 0.0, "alg_gb": 0.0} for p in PASSES}
+    for layer, d in zip(layers, per):
+        N, C, K, H, W = layer.shape
+        f = flops_per_pass(N, C, K, H, W)
+        row = {"layer": layer.name, "shape": [N, C, K, H, W]}
+        for p, v in d.items():
+            st = _stats(v)
+            ab = alg_bytes(p, N, C, K, H, W, dtype, act)
+            row[p] = {k: round(t * 1e3, 2) for k, t in st.items()}  # us
+            row[p]["tflops"] = round(f / (st["median"] * 1e-3) / 1e12, 2)
+            fam[p]["ms"] += st["mean"]
+            fam[p]["gflop"] += f / 1e9
+            fam[p]["alg_gb"] += ab / 1e9
+        rows.append(row)
+    return ms, rows, fam
+
+
+def sweep_summary(dtype, layers, ms, fam, act="none"):
+    """The throughput and roofline entries of one timed sweep."""
+    total = sum(3 * flops_per_pass(*layer.shape) for layer in layers)
+    dom = max(PASSES, key=lambda p: fam[p]["ms"])
+    n = len(layers)
+    achieved = fam[dom]["gflop"] / fam[dom]["ms"]  # GFLOP/ms = TFLOP/s
+    roof = {"bound": "mfma", "kernel": f"{dtype}/{dom}",
+            "kernels": pass_kernels(dtype, dom),
+            "launches_per_step": n,
+            "flops_per_launch": fam[dom]["gflop"] * 1e9 / n,
+            "avg_launch_us": fam[dom]["ms"] * 1e3 / n,
+            "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
+            "traffic": (recorded_traffic(f"{dtype}/{dom}")
+                        if dtype == "f32" and act == "none" and len(layers) == 32 else None),
+            "alg_bytes_per_launch": int(fam[dom]["alg_gb"] * 1e9 / n)}
+    passes = {p: {"ms_per_step": round(fam[p]["ms"], 4),
+                  "tflops": round(fam[p]["gflop"] / fam[p]["ms"], 2),
+                  "mfma_frac": round(fam[p]["gflop"] / fam[p]["ms"] / PEAK_TFLOPS[dtype], 4),
+                  "alg_gbs": round(fam[p]["alg_gb"] / fam[p]["ms"] * 1e3, 1)} for p in PASSES}
+    return {"value": round(total / (ms * 1e-3) / 1e12, 3), "ms_per_step": round(ms, 4),
+            "gflop_per_step": round(total / 1e9, 2), "roofline": roof, "passes": passes}
 
 
 def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False,
@@ -416,17 +804,32 @@ def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=F
         json.dump(rows, fh, indent=1)
 
 
+WORKLOADS = {"unet_sweep": 5, "small": 1, "stem": 2, "mid": 3, "bottleneck": 4}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="unet_sweep",
+                    help="unet_sweep: the 32 convolutions of a 64x64 UNet training step, "
+                         "float32 (bfloat16 in an extra key); the others time one "
+                         "configured layer group")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="unet_sweep: skip the bfloat16 sweep")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 512 MiB buffer before every pass (outside its event "
+                         "pair), so each pass starts with cold caches; reported as "
+                         "per-pass times")
+    ap.add_argument("--detail", metavar="OUT_JSON",
+                    help="write per-layer, per-pass time statistics to OUT_JSON")
     ap.add_argument("--sweep", metavar="OUT_JSON", help="also time every configured layer")
     ap.add_argument("--sweep-match", metavar="REGEX", help="only sweep layers whose name matches")
     ap.add_argument("--act", choices=sorted(ACT_CODES), default="none",
                     help="time the fused-activation entry points (forward epilogue; "
-                         "float32 backward prologue) instead of the plain ones")
+                         "backward prologue) instead of the plain ones")
     ap.add_argument("--cat", action="store_true",
                     help="with --sweep: time only the layers whose input is a skip "
                          "concatenation, through the *_cat entry points")
@@ -438,7 +841,7 @@ def main():
                          "bfloat16 (CONV3X3_BF16_IO)")
     ap.add_argument("--no-split", action="store_true",
                     help="with --sweep: call the entry points without a workspace (no split "
-                         "reduction on small bf16 images)")
+                         "reduction on small images)")
     ap.add_argument("--up2", action="store_true",
                     help="with --sweep: time the UNet's upsample convolutions through the "
                          "*_up2 entry points (nearest 2x upsampling in the loader)")
@@ -448,12 +851,42 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print per-pass kernel times from a rocprofv3 kernel trace and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-pass sums of rocprofv3 --pmc counters and exit")
+    ap.add_argument("--profile-report", nargs="+", metavar="CSV",
+                    help="KERNEL_TRACE_CSV [COUNTER_CSV ...]: print a markdown summary of a "
+                         "profiled run of this workload (with --workload, --focus, "
+                         "--commands) and exit")
+    ap.add_argument("--focus", default="", help="with --profile-report: comma-separated layer "
+                                                "names (substrings) to list one by one")
+    ap.add_argument("--commands", nargs="*", default=[],
+                    help="with --profile-report: the commands that made the CSVs")
     ap.add_argument("--copy-calibration-mb", type=int, default=0, metavar="MB",
                     help="also run a plain device-to-device copy of MB megabytes (a known "
                          "amount of HBM traffic for scaling profiler byte counters)")
     args = ap.parse_args()
     if args.record_traffic:
         print(json.dumps(record_traffic(*args.record_traffic)["passes"]))
+        return
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
+    if args.profile_report:
+        import workloads as wl
+        cfg = WORKLOADS[args.workload]
+        by_dt = {}
+        for l in wl.CONFIGS[cfg]:
+            if cfg == 5 and args.no_bf16 and l.dtype == "bf16":
+                continue
+            by_dt.setdefault(l.dtype, []).append(l)
+        print(profile_report(args.profile_report[0], args.profile_report[1:], by_dt,
+                             f"conv3x3 {args.workload}: kernel times and counters",
+                             args.commands, [k for k in args.focus.split(",") if k]), end="")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -462,37 +895,77 @@ def main():
 
     import torch
     import workloads as wl
-    layer = wl.CONFIGS[2][0]
-    N, C, K, H, W = layer.shape
-    run = LayerRun(layer, args.act)
-    ms, per = time_layer(run, args.steps, args.warmup)
-    f = flops_per_pass(N, C, K, H, W)
-    value = 3 * f / (ms * 1e-3) / 1e12
-    dom = max(per, key=per.get)
-    achieved = f / (per[dom] * 1e-3) / 1e12
+    cfg = WORKLOADS[args.workload]
+    layers = [l for l in wl.CONFIGS[cfg] if l.dtype == "f32"] or list(wl.CONFIGS[cfg])
+    dtype = layers[0].dtype
+    t_gen = time.perf_counter()
+    inputs = {l.name: wl.make_inputs(l) for l in layers}
+    print(f"inputs drawn for {len(layers)} {dtype} layers in "
+          f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    flush = torch.empty(512 << 18, device="cuda") if args.cold else None
+    ms, rows, fam = measure_layers(layers, dtype, inputs, args.steps, args.warmup, flush,
+                                   args.act)
+    summ = sweep_summary(dtype, layers, ms, fam, args.act)
+    if args.cold:
+        # the step bracket holds the flushes too: the step is the passes' sum
+        ms = sum(fam[p]["ms"] for p in PASSES)
+        summ["value"] = round(sum(3 * flops_per_pass(*l.shape) for l in layers) /
+                              (ms * 1e-3) / 1e12, 3)
+        summ["ms_per_step"] = round(ms, 4)
+    print(f"{dtype}: {summ['ms_per_step']} ms/step, {summ['value']} TFLOP/s",
+          file=sys.stderr, flush=True)
+    names = {5: "unet64_conv3x3_sweep_32layers_fwd_bias+bwd_data+bwd_weight",
+             1: "single_conv3x3_2x64to64_32x32_fwd_bias+bwd_data+bwd_weight",
+             2: "unet_stem_conv3x3_32x64to64_64x64_fwd_bias+bwd_data+bwd_weight",
+             3: "unet_mid_resblock_convs_32x(128to256,256to256)_32x32_fwd_bias+bwd_data+bwd_weight",
+             4: "unet_bottleneck_convs_64x512to512_(16x16,8x8)_fwd_bias+bwd_data+bwd_weight"}
+    wname = names[cfg] if args.act == "none" else names[cfg].replace(
+        "fwd_bias", f"fwd_bias_{args.act}") + f" (fused {args.act})"
+    config = {"workload": wname, "layers": len(layers), "N": layers[0].N,
+              "layout": "NCHW", "stride": 1, "pad": 1, "seed": layers[0].seed,
+              "global_batch": layers[0].N, "parallelism": "single_gpu",
+              "timing": "HIP events on the kernels' stream; inputs resident in HBM; "
+                        + ("512 MiB overwritten before every pass (cold caches)"
+                           if args.cold else "passes back to back in sweep order")}
+    if cfg == 5:
+        config.update({"channels": "128x[1,2,3,4]", "resolutions": [64, 32, 16, 8],
+                       "convs": "2 per resblock, 2 resblocks per level, down and up paths; "
+                                "up-path C_in includes the skip concatenation"})
+    else:
+        config["shapes"] = [list(l.shape) for l in layers]
     result = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "metric": METRIC, "value": summ["value"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": summ["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": layer.dtype, "data": "synthetic",
-        "config": {"workload": "unet_stem_conv3x3_fwd_bias+bwd_data+bwd_weight" if args.act == "none"
-                   else f"unet_stem_conv3x3_fwd_bias_{args.act}+bwd_data+bwd_weight (fused {args.act})",
-                   "N": N, "C_in": C, "C_out": K, "H": H, "W": W, "stride": 1, "pad": 1,
-                   "layout": "NCHW", "seed": layer.seed, "global_batch": N,
-                   "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "kernel": dom, "kernels": PASS_KERNELS[dom],
-                     "achieved": round(achieved, 3),
-                     "peak": PEAK_TFLOPS[layer.dtype], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS[layer.dtype], 4),
-                     "traffic": recorded_traffic(dom) if args.act == "none" else None,
-                     "alg_bytes": alg_bytes(dom, N, C, K, H, W, layer.dtype, args.act)},
-        "passes": {p: {"us": round(t * 1e3, 2),
-                       "tflops": round(f / (t * 1e-3) / 1e12, 2),
-                       "alg_gbs": round(alg_bytes(p, N, C, K, H, W, layer.dtype, args.act) /
-                                        (t * 1e-3) / 1e9, 1)} for p, t in per.items()},
+        "dtype": "fp32" if dtype == "f32" else "bf16", "data": "synthetic",
+        "config": config, "roofline": summ["roofline"], "passes": summ["passes"],
     }
-    del run
-    torch.cuda.empty_cache()
+    detail = {dtype: rows}
+    if cfg == 5 and not args.no_bf16:
+        blayers = [l for l in wl.CONFIGS[5] if l.dtype == "bf16"]
+        by_idx = {l.index: l for l in layers}
+        binputs = {}
+        for l in blayers:
+            src = inputs[by_idx[l.index].name]  # the same draws, rounded to bfloat16
+            binputs[l.name] = {"x": src["x"].bfloat16(), "w": src["w"].bfloat16(),
+                               "b": src["b"], "g": src["g"].bfloat16()}
+        bms, brows, bfam = measure_layers(blayers, "bf16", binputs, args.steps, args.warmup,
+                                          flush, args.act)
+        bsum = sweep_summary("bf16", blayers, bms, bfam, args.act)
+        if args.cold:
+            bms = sum(bfam[p]["ms"] for p in PASSES)
+            bsum["value"] = round(sum(3 * flops_per_pass(*l.shape) for l in blayers) /
+                                  (bms * 1e-3) / 1e12, 3)
+            bsum["ms_per_step"] = round(bms, 4)
+        print(f"bf16: {bsum['ms_per_step']} ms/step, {bsum['value']} TFLOP/s",
+              file=sys.stderr, flush=True)
+        bsum["dtype"] = "bf16 inputs, fp32 accumulation and outputs"
+        result["bf16_sweep"] = bsum
+        detail["bf16"] = brows
+        del binputs
+    if args.detail:
+        with open(args.detail, "w") as fh:
+            json.dump(detail, fh, indent=1)
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb * (1 << 20) // 4
         a = torch.ones(n, device="cuda")
@@ -503,10 +976,13 @@ def main():
         del a, b
         torch.cuda.empty_cache()
     if args.sweep:
-        sweep(args.sweep, max(5, args.steps // 5), 3, args.sweep_match, args.act, args.cat,
+        sweep(args.sweep, max(5, args.steps // 4), 3, args.sweep_match, args.act, args.cat,
               args.gnsilu, args.out_bf16, not args.no_split, args.up2, args.s2)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(layer)
+        if cfg == 5:
+            result["cpu_baseline"] = cpu_baseline_sampled(layers, inputs)
+        else:
+            result["cpu_baseline"] = cpu_baseline(layers[0])
     print(json.dumps(result), flush=True)
 
 

@@ -1,6 +1,7 @@
 """CPU checks of bench.py's contract and bookkeeping: the multi-GPU refusal,
-the FLOP and algorithmic-byte formulas of the stem layer, and the scaling
-of profiler byte counters into per-pass HBM traffic (which is reported only
+the FLOP and algorithmic-byte formulas, the attribution of reduce kernels
+to the pass that launched them in profiler output, and the scaling of
+profiler byte counters into per-pass HBM traffic (which is reported only
 while the kernel sources match the digest it was recorded for)."""
 import csv
 import json
@@ -49,38 +50,82 @@ def test_fused_activation_bytes():
 
 def _write_counters(path, counter, rows):
     with open(path, "w", newline="") as fh:
-        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
+                                           "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for name, grid, value in rows:
-            w.writerow({"Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter,
-                        "Counter_Value": value})
+        for i, (name, grid, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Grid_Size": grid,
+                        "Counter_Name": counter, "Counter_Value": value})
+
+
+COPY = ("__amd_rocclr_copyBuffer", 1 << 20)
+WG = ("void conv3x3::wgrad_f32_kernel<64, 1, 1, true>(...)", 196608)
+RED = ("conv3x3::wgrad_reduce4_kernel(...)", 74240)
+FW = ("void conv3x3::fwd_f32_kernel<0, 64, 4, 1, 64, 1, 8, true, 4>(...)", 131072)
+SPL = ("void conv3x3::split_reduce_kernel(...)", 4096)
+BD = ("void conv3x3::fwd_f32_kernel<1, 64, 4, 1, 64, 1, 8, true, 4>(...)", 131072)
 
 
 def test_counter_bytes_are_scaled_by_the_copy_and_summed_per_pass(tmp_path, monkeypatch):
     fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
-    copy = ("__amd_rocclr_copyBuffer", 1 << 20)
-    wg = ("void conv3x3::wgrad_f32_kernel<64, 1, 1, true>(...)", 196608)
-    red = ("conv3x3::wgrad_reduce4_kernel(...)", 74240)
-    fw = ("void conv3x3::fwd_f32_kernel<0, 64, 4, 1, 64, 1, 8, true, 4>(...)", 131072)
+    # dispatch order: copy, fwd, bwd_data + its split reduce, two backward-weight
+    # launches each with its reduce
+    order = [COPY, FW, BD, SPL, WG, RED, WG, RED]
     # the copy moves 512 MiB: FETCH_SIZE reads half of it, WRITE_SIZE all of it
-    _write_counters(fetch, "FETCH_SIZE", [(*copy, 262144), (*wg, 100), (*wg, 100), (*red, 40),
-                                          (*fw, 10)])
-    _write_counters(write, "WRITE_SIZE", [(*copy, 524288), (*wg, 50), (*wg, 50), (*red, 1),
-                                          (*fw, 20)])
+    fv = [262144, 10, 30, 4, 100, 40, 100, 40]
+    wv = [524288, 20, 25, 3, 50, 1, 50, 1]
+    _write_counters(fetch, "FETCH_SIZE", [(*k, v) for k, v in zip(order, fv)])
+    _write_counters(write, "WRITE_SIZE", [(*k, v) for k, v in zip(order, wv)])
     out = tmp_path / "traffic.json"
     rec = bench.record_traffic(str(fetch), str(write), out_path=str(out))
     assert abs(rec["calibration"]["fetch_factor"] - 2.0) < 1e-12
     assert rec["calibration"]["write_factor"] == 1.0
-    # both backward-weight kernels count toward the pass
-    assert len(rec["passes"]["bwd_weight"]["kernels"]) == 2
-    assert rec["passes"]["bwd_weight"]["hbm_bytes"] == ((100 + 40) * 2 + (50 + 1)) * 1024
-    assert rec["passes"]["fwd"]["hbm_bytes"] == (10 * 2 + 20) * 1024
-    assert rec["passes"]["bwd_data"]["hbm_bytes"] == 0
+    p = rec["passes"]
+    # each backward-weight launch counts its reduce; bytes are per launch
+    assert p["f32/bwd_weight"]["launches"] == 2
+    assert len(p["f32/bwd_weight"]["kernels"]) == 2
+    assert p["f32/bwd_weight"]["hbm_bytes"] == ((100 + 40) * 2 + (50 + 1)) * 1024
+    assert p["f32/fwd"]["hbm_bytes"] == (10 * 2 + 20) * 1024
+    # the split reduce after the backward-data kernel belongs to backward-data
+    assert p["f32/bwd_data"]["hbm_bytes"] == ((30 + 4) * 2 + (25 + 3)) * 1024
 
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    assert bench.recorded_traffic("bwd_weight") == ((100 + 40) * 2 + (50 + 1)) * 1024
+    assert bench.recorded_traffic("f32/bwd_weight") == ((100 + 40) * 2 + (50 + 1)) * 1024
     # a record made for other kernel sources is not reported
     stale = json.loads(out.read_text())
     stale["source_digest"] = "0" * 64
     out.write_text(json.dumps(stale))
-    assert bench.recorded_traffic("bwd_weight") is None
+    assert bench.recorded_traffic("f32/bwd_weight") is None
+
+
+def test_trace_summary_attributes_reduces_to_their_pass(tmp_path):
+    path = tmp_path / "trace.csv"
+    rows = [(COPY, 0, 5000), (FW, 10000, 110000), (BD, 120000, 200000), (SPL, 200500, 210500),
+            (WG, 220000, 320000), (RED, 320500, 328500), (FW, 330000, 420000)]
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                           "End_Timestamp"])
+        w.writeheader()
+        for i, ((name, _), t0, t1) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Start_Timestamp": t0,
+                        "End_Timestamp": t1})
+    s = bench.summarize_trace(str(path))
+    assert s["f32/fwd"]["launches"] == 2
+    assert s["f32/fwd"]["avg_us_per_launch"] == (100.0 + 90.0) / 2
+    assert s["f32/bwd_data"]["avg_us_per_launch"] == 80.0 + 10.0
+    assert s["f32/bwd_weight"]["avg_us_per_launch"] == 100.0 + 8.0
+    assert "__amd_rocclr_copyBuffer" not in json.dumps(s)
+
+
+def test_stats_percentiles():
+    st = bench._stats([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert st["median"] == 3.0 and st["mean"] == 3.0
+    assert abs(st["p10"] - 1.4) < 1e-12 and abs(st["p90"] - 4.6) < 1e-12
+
+
+def test_unet_sweep_flops():
+    import workloads as wl
+    layers = [l for l in wl.CONFIGS[5] if l.dtype == "f32"]
+    assert len(layers) == 32
+    total = sum(3 * bench.flops_per_pass(*l.shape) for l in layers)
+    assert abs(total / 1e9 - 3370.2) < 0.1
