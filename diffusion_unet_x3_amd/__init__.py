@@ -12,6 +12,7 @@ device memory and the current stream.  The functions carry the C names:
     conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None,
                        workspace=None)                        -> (dw, db)
     conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)   -> bytes
+    conv3x3_bwd_weight_noalloc(x, g, dw, db=None)             -> (dw, db)
     conv3x3_fwd_act(x, w, bias=None, act=ACT_SILU, want_z=True,
                     out=None, z=None)                         -> (y, z)
     conv3x3_bwd_data_act(gy, z, w, act=ACT_SILU, out=None)    -> dx
@@ -74,7 +75,7 @@ ACT_NONE, ACT_SILU, ACT_LRELU = 0, 1, 2
 STATUS = {
     "OK": 0, "ERR_NULL_POINTER": 1, "ERR_BAD_SHAPE": 2, "ERR_BAD_DTYPE": 3,
     "ERR_WORKSPACE": 4, "ERR_ALIAS": 5, "ERR_HIP": 6, "ERR_BAD_PASS": 7,
-    "ERR_BAD_ACT": 8, "ERR_UNSUPPORTED": 9,
+    "ERR_BAD_ACT": 8, "ERR_UNSUPPORTED": 9, "ERR_NOALLOC": 10,
 }
 EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_size",
             "conv3x3_bwd_weight", "conv3x3_status_string", "conv3x3_plan",
@@ -84,7 +85,8 @@ EXPORTED = ["conv3x3_fwd", "conv3x3_bwd_data", "conv3x3_bwd_weight_workspace_siz
             "conv3x3_bwd_data_gnsilu", "conv3x3_bwd_weight_gnsilu", "conv3x3_workspace_size",
             "conv3x3_fwd_ws", "conv3x3_bwd_data_ws", "conv3x3_up2_workspace_size",
             "conv3x3_fwd_up2", "conv3x3_bwd_data_up2", "conv3x3_bwd_weight_up2",
-            "conv3x3_fwd_s2", "conv3x3_bwd_data_s2", "conv3x3_bwd_weight_s2"]
+            "conv3x3_fwd_s2", "conv3x3_bwd_data_s2", "conv3x3_bwd_weight_s2",
+            "conv3x3_bwd_weight_noalloc"]
 
 
 class Plan(ctypes.Structure):
@@ -160,6 +162,8 @@ def _load():
     lib.conv3x3_bwd_weight_gnsilu.argtypes = [vp, fp, fp, vp, fp, fp, vp, ctypes.c_size_t,
                                               i, i, i, i, i, i, vp]
     lib.conv3x3_bwd_weight_gnsilu.restype = i
+    lib.conv3x3_bwd_weight_noalloc.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, vp]
+    lib.conv3x3_bwd_weight_noalloc.restype = i
     return lib
 
 
@@ -321,6 +325,26 @@ def conv3x3_bwd_weight(x, g, want_db=True, dw=None, db=None, workspace=None):
                                 None if db is None else db.data_ptr(), ws_ptr, ws_bytes,
                                 N, C, K, H, W, code, _stream(x))
     _raise(rc, "conv3x3_bwd_weight")
+    return dw, db
+
+
+def conv3x3_bwd_weight_noalloc(x, g, dw, db=None):
+    """conv3x3_bwd_weight with the split-K partial sums in the library's own
+    device array instead of a workspace: the call allocates nothing (dw and
+    the optional db are given).  Calls that overlap on one GPU race."""
+    _check(x, "x", 4)
+    _check(g, "g", 4)
+    N, C, H, W = x.shape
+    K = g.shape[1]
+    if tuple(g.shape) != (N, K, H, W) or g.dtype != x.dtype:
+        raise ValueError("g must be [N, K, H, W] with x's dtype")
+    dw = _f32_out(dw, (K, C, 3, 3), x, "dw")
+    if db is not None:
+        db = _f32_out(db, (K,), x, "db")
+    rc = lib.conv3x3_bwd_weight_noalloc(x.data_ptr(), g.data_ptr(), dw.data_ptr(),
+                                        None if db is None else db.data_ptr(),
+                                        N, C, K, H, W, _dtype_code(x), _stream(x))
+    _raise(rc, "conv3x3_bwd_weight_noalloc")
     return dw, db
 
 

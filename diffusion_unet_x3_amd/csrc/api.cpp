@@ -368,6 +368,7 @@ const char* conv3x3_status_string(int status) {
     case CONV3X3_ERR_BAD_PASS: return "unknown pass";
     case CONV3X3_ERR_BAD_ACT: return "unknown activation (expected a conv3x3_act_t value)";
     case CONV3X3_ERR_UNSUPPORTED: return "not provided for this dtype or size (fusions by dtype; every tensor must be below 2 GiB as float32)";
+    case CONV3X3_ERR_NOALLOC: return "conv3x3_bwd_weight_noalloc: the problem needs more scratch than the library's array holds, or the stream is not on the current device";
     default: return "unknown status code";
   }
 }

@@ -33,9 +33,9 @@
  *                  float32.  Halves the bytes of the two largest stores.
  *
  * Memory and ownership: every pointer is a device pointer (hipMalloc'd or
- * torch-allocated) owned by the caller.  The library allocates nothing,
- * keeps no mutable global state and is safe to call from several host
- * threads.  Outputs are overwritten, never accumulated into.  Outputs must
+ * torch-allocated) owned by the caller.  The library allocates nothing and
+ * is safe to call from several host threads; its only global state is the
+ * scratch array of conv3x3_bwd_weight_noalloc (see there).  Outputs are overwritten, never accumulated into.  Outputs must
  * not alias inputs (identical base pointers are rejected; partial overlap is
  * undefined).  No alignment is required: 128-bit paths are used when the
  * base address and row length allow it.
@@ -83,7 +83,10 @@ typedef enum {
   CONV3X3_ERR_HIP = 6,          /* the HIP runtime rejected a launch */
   CONV3X3_ERR_BAD_PASS = 7,     /* conv3x3_plan: unknown pass */
   CONV3X3_ERR_BAD_ACT = 8,      /* act is not a conv3x3_act_t value */
-  CONV3X3_ERR_UNSUPPORTED = 9   /* a fusion this dtype (or size) does not provide */
+  CONV3X3_ERR_UNSUPPORTED = 9,  /* a fusion this dtype (or size) does not provide */
+  CONV3X3_ERR_NOALLOC = 10      /* conv3x3_bwd_weight_noalloc: the problem needs more than
+                                   CONV3X3_NOALLOC_SCRATCH_BYTES of scratch, or the stream
+                                   is not on the current device */
 } conv3x3_status_t;
 
 /*
@@ -159,6 +162,33 @@ int conv3x3_bwd_weight(const void* x, const void* g, float* dw, float* db,
                        void* workspace, size_t workspace_bytes,
                        int N, int C, int K, int H, int W, int dtype,
                        conv3x3_stream_t stream);
+
+/*
+ * Backward-weight without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same operation, arguments, kernels
+ * and results as conv3x3_bwd_weight (bitwise), but the split-K partial sums
+ * go to a device array the library holds: CONV3X3_NOALLOC_SCRATCH_BYTES per
+ * GPU, reserved when the library's code is loaded on that GPU and held
+ * until the process ends.  The call allocates nothing.  Its device address
+ * is looked up once per device, on the first call that needs it (with the
+ * stream's device current).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (two streams, or two host threads) race and give undefined results.
+ *   Calls in one stream are ordered and safe.  Each call writes every
+ *   scratch byte it later reads, so nothing needs clearing between calls.
+ * Errors: as conv3x3_bwd_weight, plus CONV3X3_ERR_NOALLOC when the problem's
+ * workspace size (conv3x3_bwd_weight_workspace_size) exceeds the array or
+ * the stream belongs to another device than the current one, and
+ * CONV3X3_ERR_HIP when the array's address cannot be found.  The planner
+ * never splits beyond 256 slice-tiles of 64 x 64 x 9 floats, so every
+ * valid problem fits (the largest needs about 36.1 MiB).
+ */
+#define CONV3X3_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+
+int conv3x3_bwd_weight_noalloc(const void* x, const void* g, float* dw, float* db,
+                               int N, int C, int K, int H, int W, int dtype,
+                               conv3x3_stream_t stream);
 
 /*
  * Forward with fused bias and activation:  z = conv(x; w) + bias,  y = act(z).

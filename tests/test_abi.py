@@ -34,7 +34,7 @@ def test_header_functions_are_exported():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         assert lib3.conv3x3_status_string(code)
         assert "unknown status" not in lib3.conv3x3_status_string(code)
     assert lib3.conv3x3_status_string(0) == "success"
@@ -326,4 +326,33 @@ def test_tensors_of_2gib_or_more_unsupported(dims):
         assert L.conv3x3_bwd_data(G, Wt, Y, N, C, K, H, W, dt, None) == un
         assert L.conv3x3_bwd_weight(X, G, Y, B, WS, 1 << 40, N, C, K, H, W, dt, None) == un
         assert L.conv3x3_fwd_ws(X, Wt, B, Y, WS, 1 << 40, N, C, K, H, W, dt, None) == un
+        assert L.conv3x3_bwd_weight_noalloc(X, G, Y, B, N, C, K, H, W, dt, None) == un
 
+
+def test_noalloc_argument_checks():
+    """The no-allocation backward-weight validates like conv3x3_bwd_weight
+    (no call here reaches the scratch lookup or a launch)."""
+    d = (2, 3, 4, 5, 6)
+    assert L.conv3x3_bwd_weight_noalloc(None, G, Y, B, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_weight_noalloc(X, G, None, B, *d, 0, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_weight_noalloc(X, G, Y, B, 0, 3, 4, 5, 6, 0, None) == S["ERR_BAD_SHAPE"]
+    assert L.conv3x3_bwd_weight_noalloc(X, G, Y, B, *d, 7, None) == S["ERR_BAD_DTYPE"]
+    assert L.conv3x3_bwd_weight_noalloc(X, G, X, B, *d, 0, None) == S["ERR_ALIAS"]
+    assert "scratch" in lib3.conv3x3_status_string(S["ERR_NOALLOC"])
+
+
+def test_noalloc_scratch_covers_every_plan():
+    """The planner keeps split x channel tiles <= 256 (64 x 64 x 9 floats
+    each), so no problem needs more split-K workspace than the
+    no-allocation entry point's 40 MiB array."""
+    limit = 40 << 20
+    worst = 0
+    for dt in (0, 1):
+        for C in (1, 3, 17, 64, 65, 128, 200, 256, 384, 512, 640, 1024, 2048, 4096):
+            for K in (1, 8, 64, 100, 128, 256, 512, 1024, 4096, 8192):
+                for H in (1, 8, 16, 33, 64, 128):
+                    for N in (1, 4, 32, 64):
+                        n = L.conv3x3_bwd_weight_workspace_size(N, C, K, H, H, dt)
+                        if n != ctypes.c_size_t(-1).value:
+                            worst = max(worst, n)
+    assert 30 << 20 < worst <= limit
