@@ -42,7 +42,8 @@ device memory and the current stream.  The functions carry the C names:
 
 The *_act functions fuse an activation (ACT_NONE, ACT_SILU, ACT_LRELU) into
 the forward epilogue and, through z = the forward's pre-activation, into the
-gradient loader of the backward passes (float32 backward only).  The *_cat
+gradient loader of the backward passes (bfloat16: g = gy * act'(z) rounded
+to bfloat16 as it is staged).  The *_cat
 functions take the input as two tensors x0, x1 whose channel concatenation
 [x0 ; x1] is the convolution's input (a UNet's up-path skip input) and never
 form the concatenation; backward-data returns the two gradient halves.  The

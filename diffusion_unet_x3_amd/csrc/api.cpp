@@ -195,7 +195,6 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   rc = check_act(act);
   if (rc) return rc;
   if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
-  if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
   rc = check_prologue(pr, dtype);
   if (rc) return rc;
   if (is_part(dx, g) || is_part(dx, w) || (act != CONV3X3_ACT_NONE && is_part(dx, z)) ||
@@ -213,6 +212,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   pb.quad = s2;
   pb.stride2 = geom == 1;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE && !pr.on() && !geom;
+  pb.four_waves = dtype != CONV3X3_F32 && act != CONV3X3_ACT_NONE;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -240,8 +240,8 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
                         H, W, a, (float*)ws, s);
   } else {
     const bool vec = W % 8 == 0 && K % 16 == 0 && C % 8 == 0 && dx.c0 % 8 == 0 &&
-                     aligned16(g) && aligned16(w) && buffer_sized((long)N * K * hw) &&
-                     buffer_sized((long)K * C * 9);
+                     aligned16(g) && aligned16(w) && (!a.zsrc || aligned16(a.zsrc)) &&
+                     buffer_sized((long)N * K * hw) && buffer_sized((long)K * C * 9);
     ok = launch_fwd_bf16(pl, vec, one((const uint16_t*)g, K), (const uint16_t*)w, nullptr, dx, N,
                          K, C, H, W, a, dtype == CONV3X3_BF16_IO, (float*)ws, s);
   }
@@ -265,7 +265,6 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   rc = check_act(act);
   if (rc) return rc;
   if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
-  if (act != CONV3X3_ACT_NONE && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
   if (is_part(x, dw) || (const void*)dw == g ||
       (db && (is_part(x, db) || (const void*)db == g || db == dw)))
     return CONV3X3_ERR_ALIAS;
@@ -308,7 +307,8 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
                           a, s);
   } else {
     const bool vec = W % 8 == 0 && parts_aligned(x) && aligned16(g) &&
-                     buffer_sized((long)N * C * hw) && buffer_sized((long)N * K * hw);
+                     (!a.zsrc || aligned16(a.zsrc)) && buffer_sized((long)N * C * hw) &&
+                     buffer_sized((long)N * K * hw);
     Split<const uint16_t> xs{(const uint16_t*)x.p0, (const uint16_t*)x.p1, x.c0};
     ok = launch_wgrad_bf16(pl, vec, xs, (const uint16_t*)g, dw, db, (float*)workspace, N, C, K, H,
                            W, a, s);

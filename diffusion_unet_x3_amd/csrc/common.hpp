@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "activation.hpp"
+
 namespace conv3x3 {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -105,6 +107,97 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The bfloat16 passes' fused gradient operand: g = gy * act'(z) for a
+// bfloat16 gy and a float32 z, rounded to the nearest bfloat16 value (ties
+// to even) as the exact product rounds.  The float32 product p decides
+// unless the interval p +- |gy| 2^-17 -- wider than p's error: the slope's
+// absolute error stays below 1e-6 for every z (the exponential's error
+// scales with s (1 - s), which vanishes where |z| is large), and p's own
+// rounding is 2^-24 relative -- holds a bfloat16 rounding boundary, or p
+// is one; then the product is formed again in double precision (a few
+// elements in a thousand).
+__device__ __forceinline__ uint32_t bf16_rne_f64(double g) {
+  if (g != g) return 0x7fc0u;
+  if (__builtin_fabs(g) < 0x1p-120) return bf16_rne((float)g);  // (no such g in practice)
+  uint64_t u = __builtin_bit_cast(uint64_t, g);
+  // keep 7 of the 52 fraction bits, round to nearest even on the other 45
+  u = (u + 0x00000FFFFFFFFFFFull + ((u >> 45) & 1u)) & ~0x00001FFFFFFFFFFFull;
+  return __builtin_bit_cast(uint32_t, (float)__builtin_bit_cast(double, u)) >> 16;
+}
+
+// e^x in double precision for that rare path, inline (a library call would
+// give the kernels a call frame in scratch memory): x = k ln2 + r with
+// |r| <= ln2 / 2 (to within the rounding of k ln2, about 1e-14 absolute,
+// far below what the rounding decision needs), e^r by its Taylor series up
+// to r^13 / 13! (the remainder is below 2e-16 relative), and 2^k formed in
+// the exponent field in two halves so that each stays a normal double.
+__device__ __forceinline__ double exp_f64(double x) {
+  if (x > 709.0) return __builtin_inf();
+  if (x < -745.0) return 0.0;
+  const double k = __builtin_rint(x * 1.4426950408889634);  // x / ln2
+  const double r = x - k * 0.6931471805599453;              // x - k ln2
+  // sum_{n=0}^{13} r^n / n!, Horner form
+  double p = 1.0 / 6227020800.0;                  // 1 / 13!
+  p = p * r + 1.0 / 479001600.0;                  // 1 / 12!
+  p = p * r + 1.0 / 39916800.0;                   // 1 / 11!
+  p = p * r + 1.0 / 3628800.0;                    // 1 / 10!
+  p = p * r + 1.0 / 362880.0;                     // 1 / 9!
+  p = p * r + 1.0 / 40320.0;                      // 1 / 8!
+  p = p * r + 1.0 / 5040.0;                       // 1 / 7!
+  p = p * r + 1.0 / 720.0;                        // 1 / 6!
+  p = p * r + 1.0 / 120.0;                        // 1 / 5!
+  p = p * r + 1.0 / 24.0;                         // 1 / 4!
+  p = p * r + 1.0 / 6.0;                          // 1 / 3!
+  p = p * r + 0.5;                                // 1 / 2!
+  p = p * r + 1.0;
+  p = p * r + 1.0;
+  const int ki = (int)k, k1 = ki / 2, k2 = ki - k1;  // each in [-538, 512]
+  const double f1 = __builtin_bit_cast(double, (uint64_t)(k1 + 1023) << 52);
+  const double f2 = __builtin_bit_cast(double, (uint64_t)(k2 + 1023) << 52);
+  return p * f1 * f2;
+}
+
+__device__ __forceinline__ uint32_t act_grad_bf16_f64_inl(float gy, float z, int act) {
+  double sl = 1.0;
+  if (act == kActSilu) {
+    const double zd = z, s = 1.0 / (1.0 + exp_f64(-zd));
+    sl = s * (1.0 + zd * (1.0 - s));
+  } else if (act == kActLrelu) {
+    sl = z > 0.f ? 1.0 : 0.2;
+  }
+  return bf16_rne_f64((double)gy * sl);
+}
+
+// The same as a call (kernels whose register budget cannot hold the double
+// precision path inline at every staged element).
+__device__ __noinline__ uint32_t act_grad_bf16_f64_call(float gy, float z, int act) {
+  return act_grad_bf16_f64_inl(gy, z, act);
+}
+
+// INL: the rare double-precision path inline (true) or as a call (false).
+template <bool INL>
+__device__ __forceinline__ uint32_t act_grad_bf16_f32(float gy, float z, int act) {
+  const float p = gy * act_slope(act, z);
+  const float e = __builtin_fabsf(gy) * 0x1p-17f;
+  const uint32_t r = bf16_rne(p);
+  const bool tie = (__builtin_bit_cast(uint32_t, p) & 0xffffu) == 0x8000u;
+  if (!tie && bf16_rne(p - e) == r && bf16_rne(p + e) == r) return r;
+  return INL ? act_grad_bf16_f64_inl(gy, z, act) : act_grad_bf16_f64_call(gy, z, act);
+}
+
+// gp packs two bfloat16 gradients (the first in the low half); the result
+// packs the two operands the same way.
+template <bool INL>
+__device__ __forceinline__ uint32_t act_grad_bf16x2(uint32_t gp, float z0, float z1, int act) {
+  return act_grad_bf16_f32<INL>(__builtin_bit_cast(float, gp << 16), z0, act) |
+         (act_grad_bf16_f32<INL>(__builtin_bit_cast(float, gp & 0xffff0000u), z1, act) << 16);
+}
+
+template <bool INL>
+__device__ __forceinline__ uint32_t act_grad_bf16(uint32_t g, float z, int act) {
+  return act_grad_bf16_f32<INL>(__builtin_bit_cast(float, (g & 0xffffu) << 16), z, act);
 }
 
 }  // namespace conv3x3

@@ -93,14 +93,14 @@ __device__ __forceinline__ u32x4 tap_word(const uint32_t* d) {
 
 }  // namespace
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC>
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC, bool ZG>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ src1, int cin0,
     const uint16_t* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
     float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
     uint32_t dst1_bytes, int act, float* __restrict__ zout, int outb, int per_split,
-    float* __restrict__ part) {
+    float* __restrict__ part, const float* __restrict__ zsrc) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -191,13 +191,19 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // words stay zero and nothing is loaded for them.
   const bool halo_loads = tiles_w > 1;
 
-  constexpr int NSET = WSPEC ? 1 : 2;
+  // (ZG: the source is a gradient gy multiplied by act'(zsrc) as it is
+  // staged; its float32 z items take the registers of the second set)
+  constexpr int NSET = (WSPEC || ZG) ? 1 : 2;
   constexpr int WBASE = WSPEC ? 8 : 0;  // first register word of the weight items
   constexpr int SLOTS = WSPEC ? 8 + WK * NSTG : (NSTG > 8 ? NSTG : 8);
   u32x4 st[NSET][VEC ? SLOTS : 1];
   // halo values as loaded (one channel each); packed into a word when the
   // fill is written, so that issuing the loads never waits for them
   uint32_t hv[NSET][8];
+  // ZG: z of the x item (row i's 8 floats in words 2i, 2i + 1) and of the
+  // halo item
+  f32x4 zx[NSET][ZG && VEC ? 16 : 1];
+  float zh[NSET][ZG && VEC ? 8 : 1];
 #pragma unroll
   for (int k = 0; k < NSET; ++k)
 #pragma unroll
@@ -211,6 +217,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t sv0 = buffer_view(src, src_bytes);
   const __amdgpu_buffer_rsrc_t sv1 = buffer_view(src1, src1_bytes);
   const __amdgpu_buffer_rsrc_t wv = buffer_view(wt, wt_bytes);
+  // z has the source's shape in float32: twice its byte offsets (below 2^31:
+  // the caller keeps every float32 tensor under 2 GiB)
+  const __amdgpu_buffer_rsrc_t zv = buffer_view(zsrc, ZG ? 2u * src_bytes : 0u);
   const uint32_t hw2 = 2u * (uint32_t)(H * W);
   // x and halo item offsets in src (channel 8g of image n) and in src1
   uint32_t xoff = kOutside, hoff = kOutside, xoff1 = kOutside, hoff1 = kOutside, woff[WK];
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // (fills are whole here, so fill f of src1 starts at weight channel
   // 16 (nq0 + f); items outside the image keep kOutside through the select)
-  auto load_tiles = [&](auto set_c, int lchunk) {
+  auto load_tiles = [&](auto set_c, int lchunk) __attribute__((always_inline)) {
     constexpr int S = decltype(set_c)::value;
     const int chunk = fbase + lchunk;  // fill index over the whole reduction
     const uint32_t f = (uint32_t)chunk;
@@ -281,11 +290,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const uint32_t b = (s1 ? xoff1 : xoff) + fx;
 #pragma unroll
       for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, b + (uint32_t)i * hw2);
+      if constexpr (ZG) {
+        // (one source tensor: s1 is false)
+        const uint32_t zb = (xoff == kOutside ? kOutside : 2u * xoff) + 2u * fx;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          zx[S][2 * i] = __builtin_bit_cast(f32x4, buffer_load16(zv, zb + 2u * (uint32_t)i * hw2));
+          zx[S][2 * i + 1] =
+              __builtin_bit_cast(f32x4, buffer_load16(zv, zb + 2u * (uint32_t)i * hw2 + 16u));
+        }
+      }
     }
     if (hrole && halo_loads) {
       const uint32_t b = (s1 ? hoff1 : hoff) + fx;
 #pragma unroll
       for (int i = 0; i < 8; ++i) hv[S][i] = buffer_load2(sv, b + (uint32_t)i * hw2);
+      if constexpr (ZG) {
+        const uint32_t zb = (hoff == kOutside ? kOutside : 2u * hoff) + 2u * fx;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          zh[S][i] = __builtin_bit_cast(float, buffer_load4(zv, zb + 2u * (uint32_t)i * hw2));
+      }
     }
 #pragma unroll
     for (int k = 0; k < WK; ++k) {
@@ -302,8 +327,25 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
   };
 
-  auto store_tiles = [&](auto set_c, int buf) {
+  auto store_tiles = [&](auto set_c, int buf) __attribute__((always_inline)) {
     constexpr int S = decltype(set_c)::value;
+    if constexpr (ZG) {
+      // g = gy * act'(z), rounded to bfloat16, before the transposes
+      if (xrole) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4 za = zx[S][2 * i], zb = zx[S][2 * i + 1];
+          st[S][i].x = act_grad_bf16x2<false>(st[S][i].x, za.x, za.y, act);
+          st[S][i].y = act_grad_bf16x2<false>(st[S][i].y, za.z, za.w, act);
+          st[S][i].z = act_grad_bf16x2<false>(st[S][i].z, zb.x, zb.y, act);
+          st[S][i].w = act_grad_bf16x2<false>(st[S][i].w, zb.z, zb.w, act);
+        }
+      }
+      if (hrole && halo_loads) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[S][i] = act_grad_bf16<false>(hv[S][i], zh[S][i], act);
+      }
+    }
     if (xrole) {
       u32x4* d = xs + buf * XW + xdst;
       d[0] = column_word<0>(st[S]);
@@ -362,7 +404,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // Scalar path (ragged shapes): 16-bit loads straight into LDS buffer buf,
   // by the staging threads.
-  auto fill_scalar = [&](int lchunk, int buf) {
+  auto fill_scalar = [&](int lchunk, int buf) __attribute__((always_inline)) {
     if (sp < 0) return;
     const int chunk = fbase + lchunk;  // fill index over the whole reduction
     const bool s1 = chunk >= nq0;
@@ -385,8 +427,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
         const int ch = t / (HR * IMGS);
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
         uint16_t v = 0;
-        if (n < N && ch < cn && h >= 0 && h < H && w >= 0 && w < W)
-          v = sx[((long)n * cs + cl0 + ch) * HW + (long)h * W + w];
+        if (n < N && ch < cn && h >= 0 && h < H && w >= 0 && w < W) {
+          const long e = ((long)n * cs + cl0 + ch) * HW + (long)h * W + w;
+          v = sx[e];
+          if constexpr (ZG) v = (uint16_t)act_grad_bf16<false>(v, zsrc[e], act);
+        }
         xh[((ch >> 3) * PLW + (img * HR + rr) * RS + 4 + cc) * 8 + (ch & 7)] = v;
       }
     }
@@ -416,7 +461,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   };
   // Write fill chunk + 1 (held in set_c) to LDS and load fill
   // chunk + 1 + NSET into the same set.
-  auto stage_next = [&](auto set_c, int chunk) {
+  auto stage_next = [&](auto set_c, int chunk) __attribute__((always_inline)) {
     if constexpr (VEC) {
       if (chunk + 1 < nchunks) store_tiles(set_c, (chunk + 1) & 1);
       if (chunk + 1 + NSET < nchunks) load_tiles(set_c, chunk + 1 + NSET);
@@ -505,7 +550,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     };
 #pragma unroll
     for (int t = 0; t < 9; ++t) read_slot(0, t);
-    auto run_fill = [&](auto set_c, int chunk) {
+    auto run_fill = [&](auto set_c, int chunk) __attribute__((always_inline)) {
       const int cur = chunk & 1;
       const bool next = chunk + 1 < nchunks;
 #pragma unroll
@@ -554,7 +599,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     // waves, or here after tap 0) and every lane has read its last operands of
     // this one, so tap 0 of the next fill is read while tap 8 runs.
     // One fill; set_c is the staging register set that holds fill chunk + 1.
-    auto run_fill = [&](auto set_c, int chunk) {
+    auto run_fill = [&](auto set_c, int chunk) __attribute__((always_inline)) {
       const int cur = chunk & 1;
       const bool next = chunk + 1 < nchunks;
 #pragma unroll
@@ -757,11 +802,14 @@ void launch_split_reduce(const float* part, int S, long slot, float* dst, hipStr
                      (float*)nullptr);
 }
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW>
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool ZG>
 static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                             const uint16_t* wt, const float* bias, Split<float> dst, int N,
                             int Cin, int Cout, int H, int W, const ActArgs& a, bool out_bf16,
                             float* ws, hipStream_t stream) {
+  if constexpr (ZG && NW != 4) {
+    return;  // not instantiated: launch_fwd_bf16 refuses these plans
+  } else {
   // split reduction: partial sums into ws, then split_reduce_kernel
   float* const part = pl.split > 1 ? ws : nullptr;
   dim3 grid(pl.grid_x, pl.grid_y, part ? pl.split : 1), block(64 * NW, 1, 1);
@@ -774,22 +822,23 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
   const bool small = ob0 * zf < 2147483648L && ob1 * zf < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
   if (vec)
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true>), grid, block, 0,
-                       stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N, Cin,
-                       Cout, H, W, pl.tiles_w, pl.tiles_h, (uint32_t)(N * src.c0 * hw * 2),
-                       (uint32_t)(N * (Cin - src.c0) * hw * 2),
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true, ZG>), grid,
+                       block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
+                       dst.c0, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                       (uint32_t)(N * src.c0 * hw * 2), (uint32_t)(N * (Cin - src.c0) * hw * 2),
                        (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout,
-                       out_bf16 ? 1 : 0, pl.chunks_per_split, part);
+                       out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false>), grid, block,
-                       0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1, dst.c0, N,
-                       Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1, a.act,
-                       a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part);
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false, ZG>), grid,
+                       block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
+                       dst.c0, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1,
+                       a.act, a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc);
   if (part) {
     const long slot = (long)N * Cout * hw;
     dim3 rg((unsigned)((slot + 1023) / 1024)), rb(256);
     hipLaunchKernelGGL(split_reduce_kernel, rg, rb, 0, stream, part, pl.split, slot, dst.p0,
                        out_bf16 ? 1 : 0, a.act, a.zout);
+  }
   }
 }
 
@@ -799,20 +848,26 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
   if (pl.chunk != 16) return false;
   // a split reduction needs its workspace and one output tensor
   if (pl.split > 1 && (ws == nullptr || dst.c0 != Cout)) return false;
-  // The bfloat16 backward-data pass has no fused activation and neither
-  // pass has the input prologue (the caller rejects them).
-  if ((pl.pass != kFwd && a.zsrc != nullptr) || a.pscale != nullptr) return false;
+  // Neither pass has the input prologue (the caller rejects it); a fused
+  // activation gradient (a.zsrc) needs one source tensor, no split and a
+  // four-wave tile (the eight-wave tile's staging waves cannot also hold
+  // the float32 z rows; the planner keeps to the four-wave tiles for it).
+  if (a.pscale != nullptr) return false;
+  if (a.zsrc != nullptr &&
+      (pl.pass == kFwd || src.c0 != Cin || pl.split > 1 || pl.threads != 256))
+    return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_, NW_)                                              \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                  \
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \
     if (pl.pass == kFwd)                                                                        \
-      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, bias, dst, N,    \
-                                                             Cin, Cout, H, W, a, out_bf16, ws,  \
-                                                             stream);                           \
+      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_, false>(                            \
+          pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);            \
+    else if (a.zsrc == nullptr)                                                                 \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, false>(                        \
+          pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);         \
     else                                                                                        \
-      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_>(pl, vec, src, wt, nullptr, dst, \
-                                                                 N, Cin, Cout, H, W, a,          \
-                                                                 out_bf16, ws, stream);          \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, true>(                         \
+          pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);         \
     return true;                                                                                \
   }
   CONV3X3_FWD_BF16_CONFIGS(CONV3X3_X)

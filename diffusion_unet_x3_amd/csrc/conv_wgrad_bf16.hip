@@ -30,13 +30,15 @@ namespace {
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 }  // namespace
 
-template <int TW, int TH, int IMGS, bool VEC>
+// ZG: g is a gradient gy at an activation's output, multiplied by act'(zsrc)
+// (zsrc float32, g's shape) and rounded to bfloat16 as it is staged.
+template <int TW, int TH, int IMGS, bool VEC, bool ZG>
 __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ x1, int cx0,
     const uint16_t* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
     int C, int K, int H, int W, int tiles_w, int tiles_h, int nchunks, int per_split,
     long slice_stride, int split, int tiles_c, int tiles_k, uint32_t x_bytes, uint32_t x1_bytes,
-    uint32_t g_bytes) {
+    uint32_t g_bytes, int act, const float* __restrict__ zsrc) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P % 16 == 0, "whole 16-pixel MFMA steps");
   static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
@@ -86,21 +88,29 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   constexpr int HN = (HI_ + NT - 1) / NT;
   // Two register sets: the global loads of chunk i + 3 are issued into the
   // set just emptied into LDS for chunk i + 1, so each load has two chunks of
-  // MFMA work to arrive.
-  u32x4 gv[2][VEC ? GN : 1];
-  u32x4 xv[2][VEC ? XN : 1];
-  uint16_t xh[2][VEC ? HN : 1];
+  // MFMA work to arrive.  With ZG the float32 z items take the registers of
+  // the second set: one set, loads one chunk ahead.
+  constexpr int NSET = ZG ? 1 : 2;
+  u32x4 gv[NSET][VEC ? GN : 1];
+  u32x4 xv[NSET][VEC ? XN : 1];
+  uint16_t xh[NSET][VEC ? HN : 1];
+  f32x4 zv[NSET][ZG && VEC ? 2 * GN : 1];
   // With a single tile across the width both halo columns are padding: they
   // stay zero and are not loaded.
   const bool halo_loads = tiles_w > 1;
 #pragma unroll
-  for (int k = 0; k < (VEC ? HN : 1); ++k) xh[0][k] = xh[1][k] = 0;
+  for (int k = 0; k < (VEC ? HN : 1); ++k)
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) xh[j][k] = 0;
 
   // Vector path: buffer views; an item outside the tensors or the image
   // reads zero through an offset past the view (32-bit offset arithmetic).
   const __amdgpu_buffer_rsrc_t gview = buffer_view(g, g_bytes);
   const __amdgpu_buffer_rsrc_t xview = buffer_view(xsrc, xseg ? x1_bytes : x_bytes);
-  auto load_tiles = [&](auto set_c, int chunk) {
+  // z: g's shape in float32, twice g's byte offsets (below 2^31: the caller
+  // keeps every float32 tensor under 2 GiB)
+  const __amdgpu_buffer_rsrc_t zview = buffer_view(zsrc, ZG ? 2u * g_bytes : 0u);
+  auto load_tiles = [&](auto set_c, int chunk) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     if constexpr (VEC) {
       const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
@@ -115,7 +125,13 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 8 * q;
         const bool ok = (GI % NT == 0 || it < GI) && n < N && kk < K && h < H && w < W;
-        gv[SET][k] = buffer_load16(gview, ok ? 2u * (uint32_t)(((n * K + kk) * H + h) * W + w) : kOutside);
+        const uint32_t e = (uint32_t)(((n * K + kk) * H + h) * W + w);
+        gv[SET][k] = buffer_load16(gview, ok ? 2u * e : kOutside);
+        if constexpr (ZG) {
+          zv[SET][2 * k] = __builtin_bit_cast(f32x4, buffer_load16(zview, ok ? 4u * e : kOutside));
+          zv[SET][2 * k + 1] =
+              __builtin_bit_cast(f32x4, buffer_load16(zview, ok ? 4u * e + 16u : kOutside));
+        }
       }
 #pragma unroll
       for (int k = 0; k < XN; ++k) {
@@ -151,21 +167,11 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     }
   };
 
-  auto store_tiles = [&](auto set_c, int chunk, int buf) {
+  auto store_tiles = [&](auto set_c, int chunk, int buf) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     uint16_t* gs = gs_buf[buf];
     uint16_t* xs = xs_buf[buf];
     if constexpr (VEC) {
-#pragma unroll
-      for (int k = 0; k < GN; ++k) {
-        const int it = tid + k * NT;
-        if (GI % NT == 0 || it < GI) {
-          const int q = it % XQ;
-          const int t = it / XQ;  // (kl * IMGS + img) * TH + row
-          const int kl = t / (IMGS * TH);
-          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = gv[SET][k];
-        }
-      }
 #pragma unroll
       for (int k = 0; k < XN; ++k) {
         const int it = tid + k * NT;
@@ -186,6 +192,33 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + (side ? TW : -1)] = xh[SET][k];
         }
       }
+      if constexpr (ZG) {
+        // g = gy * act'(z), rounded to bfloat16, in place (after the x
+        // stores have freed their registers; constant indices only)
+        static_assert(GN <= 2, "ZG staging handles up to two g items per thread");
+        auto mul = [&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          const f32x4 za = zv[SET][2 * k], zb = zv[SET][2 * k + 1];
+          u32x4 v = gv[SET][k];
+          v.x = act_grad_bf16x2<false>(v.x, za.x, za.y, act);
+          v.y = act_grad_bf16x2<false>(v.y, za.z, za.w, act);
+          v.z = act_grad_bf16x2<false>(v.z, zb.x, zb.y, act);
+          v.w = act_grad_bf16x2<false>(v.w, zb.z, zb.w, act);
+          gv[SET][k] = v;
+        };
+        mul(std::integral_constant<int, 0>{});
+        if constexpr (GN > 1) mul(std::integral_constant<int, 1>{});
+      }
+#pragma unroll
+      for (int k = 0; k < GN; ++k) {
+        const int it = tid + k * NT;
+        if (GI % NT == 0 || it < GI) {
+          const int q = it % XQ;
+          const int t = it / XQ;  // (kl * IMGS + img) * TH + row
+          const int kl = t / (IMGS * TH);
+          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = gv[SET][k];
+        }
+      }
     } else {
       // Scalar path (ragged shapes): 16-bit loads straight into LDS.
       const BlockOrigin o = block_origin<TW, TH, IMGS>(chunk, tiles_w, tiles_h);
@@ -202,7 +235,11 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int kl = t / IMGS;
           const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + col;
           uint16_t v = 0;
-          if (n < N && kk < K && h < H && w < W) v = g[((long)n * K + kk) * HW + (long)h * W + w];
+          if (n < N && kk < K && h < H && w < W) {
+            const long e = ((long)n * K + kk) * HW + (long)h * W + w;
+            v = g[e];
+            if constexpr (ZG) v = (uint16_t)act_grad_bf16<false>(v, zsrc[e], act);
+          }
           gs[kl * GSB + it % P] = v;
         }
       }
@@ -259,16 +296,16 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   // of waves that are still computing.  One barrier per chunk.
   constexpr int kStoreStep = 1;
   using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
+  using Set1 = std::integral_constant<int, NSET - 1>;
   if (chunk_begin < chunk_end) {
     load_tiles(Set0{}, chunk_begin);
     store_tiles(Set0{}, chunk_begin, 0);
     if (chunk_begin + 1 < chunk_end) load_tiles(Set1{}, chunk_begin + 1);
-    if (chunk_begin + 2 < chunk_end) load_tiles(Set0{}, chunk_begin + 2);
+    if (NSET == 2 && chunk_begin + 2 < chunk_end) load_tiles(Set0{}, chunk_begin + 2);
     __syncthreads();
   }
   // One chunk; SET is the register set that holds chunk + 1.
-  auto run_chunk = [&](auto set_c, int chunk) {
+  auto run_chunk = [&](auto set_c, int chunk) __attribute__((always_inline)) {
     const int cur = (chunk - chunk_begin) & 1;
     const uint16_t* gs = gs_buf[cur];
     const uint16_t* xs = xs_buf[cur];
@@ -295,7 +332,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
       if (ks == kStoreStep && chunk + 1 < chunk_end) {
         __builtin_amdgcn_sched_barrier(0);
         store_tiles(set_c, chunk + 1, cur ^ 1);
-        if (chunk + 3 < chunk_end) load_tiles(set_c, chunk + 3);
+        if (chunk + 1 + NSET < chunk_end) load_tiles(set_c, chunk + 1 + NSET);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -335,34 +372,34 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   }
 }
 
-template <int TW, int TH, int IMGS>
+template <int TW, int TH, int IMGS, bool ZG>
 static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, Split<const uint16_t> x,
                                    const uint16_t* g, float* out, float* out_db,
                                    long slice_stride, int N, int C, int K, int H, int W,
-                                   hipStream_t stream) {
+                                   const ActArgs& a, hipStream_t stream) {
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
   const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
   const long hw2 = (long)H * W * 2;
   if (vec)
-    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true>), grid, block, 0, stream, x.p0,
-                       x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, ZG>), grid, block, 0, stream,
+                       x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
                        (K + 63) / 64, (uint32_t)(N * x.c0 * hw2),
-                       (uint32_t)(N * (C - x.c0) * hw2), (uint32_t)(N * K * hw2));
+                       (uint32_t)(N * (C - x.c0) * hw2), (uint32_t)(N * K * hw2), a.act, a.zsrc);
   else
-    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false>), grid, block, 0, stream, x.p0,
-                       x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false, ZG>), grid, block, 0, stream,
+                       x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
-                       (K + 63) / 64, 0u, 0u, 0u);
+                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc);
 }
 
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
                        float* dw, float* db, float* ws, int N, int C, int K, int H, int W,
                        const ActArgs& a, hipStream_t stream) {
   if (pl.threads != 768) return false;
-  // No fused activation or input prologue on the bfloat16 backward-weight
-  // pass (the caller rejects them).
-  if (a.zsrc != nullptr || a.pscale != nullptr) return false;
+  // No input prologue on the bfloat16 backward-weight pass (the caller
+  // rejects it).
+  if (a.pscale != nullptr) return false;
   const long n_dw = (long)K * C * 9;
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
@@ -370,8 +407,12 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const 
   bool found = false;
 #define CONV3X3_X(TW_, TH_, IMGS_)                                                          \
   if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                         \
-    launch_wgrad_bf16_geom<TW_, TH_, IMGS_>(pl, vec, x, g, out, out_db, stride, N, C, K, H, \
-                                            W, stream);                                     \
+    if (a.zsrc)                                                                             \
+      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, true>(pl, vec, x, g, out, out_db, stride, N, C, \
+                                                    K, H, W, a, stream);                      \
+    else                                                                                      \
+      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, false>(pl, vec, x, g, out, out_db, stride, N, C,\
+                                                     K, H, W, a, stream);                     \
     found = true;                                                                           \
   }
   CONV3X3_WGRAD_BF16_CONFIGS(CONV3X3_X)

@@ -113,7 +113,7 @@ bool plan(const Problem& p, Plan* out) {
       cands[0] = cout <= 64 ? Cand{256, 64, 1, 4} : Cand{128, 128, 2, 4};
       cands[1] = Cand{64, 64, 2, 4};
       ncand = 2;
-    } else if (cout > 64) {
+    } else if (cout > 64 && !p.four_waves) {
       cands[0] = Cand{256, 128, 1, 8};
       cands[1] = Cand{128, 64, 2, 4};
       cands[2] = Cand{64, 64, 2, 4};

@@ -63,6 +63,9 @@ struct Problem {
   // class (stride-2 backward-data, upsampling forward; H, W the grid they
   // tile): 64 x 64 tiles, one 32 x 32 MFMA tile per wave and set
   bool quad = false;
+  // bfloat16 backward-data with a fused activation gradient: four-wave
+  // tiles only (their staging threads hold the float32 z rows beside gy)
+  bool four_waves = false;
 };
 
 bool plan(const Problem& p, Plan* out);

@@ -210,8 +210,10 @@ int conv3x3_fwd_act(const void* x, const void* w, const float* bias, float* y, f
  *        only when act is CONV3X3_ACT_NONE)
  *   w, dx : as conv3x3_bwd_data
  * g is formed as gy and z are staged into LDS; it never exists in memory.
- * float32 only for now: a bfloat16 call with an activation other than
- * CONV3X3_ACT_NONE returns CONV3X3_ERR_UNSUPPORTED.
+ * bfloat16 modes: gy is bfloat16 and z float32; the contraction's operand g
+ * is bfloat16, formed in float32 as gy * act'(z) and rounded to nearest
+ * even (so it can differ from the exact product's rounding by one bfloat16
+ * step in rare elements).
  */
 int conv3x3_bwd_data_act(const void* gy, const float* z, const void* w, float* dx,
                          int N, int C, int K, int H, int W, int dtype, int act,
@@ -221,7 +223,8 @@ int conv3x3_bwd_data_act(const void* gy, const float* z, const void* w, float* d
  * Backward-weight and bias gradient through the activation:
  *   dw, db = conv3x3_bwd_weight(x, g = gy * act'(z)); arguments as
  *   conv3x3_bwd_weight, plus gy / z / act as conv3x3_bwd_data_act (same
- *   workspace size).  float32 only for now, as conv3x3_bwd_data_act.
+ *   workspace size and the same bfloat16 rounding of g; db is the sum of
+ *   that g).
  */
 int conv3x3_bwd_weight_act(const void* x, const void* gy, const float* z, float* dw, float* db,
                            void* workspace, size_t workspace_bytes,

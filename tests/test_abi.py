@@ -126,10 +126,11 @@ def test_activation_argument_checks():
     assert L.conv3x3_bwd_data_act(G, Z, Wt, Z, *d, 0, silu, None) == S["ERR_ALIAS"]
     assert L.conv3x3_bwd_weight_act(X, G, Z, Z, B, WS, 1 << 40, *d, 0, silu, None) == \
         S["ERR_ALIAS"]
-    # ... and fuse one on float32 only
-    assert L.conv3x3_bwd_data_act(G, Z, Wt, Y, *d, 1, silu, None) == S["ERR_UNSUPPORTED"]
-    assert L.conv3x3_bwd_weight_act(X, G, Z, Y, B, WS, 1 << 40, *d, 1, lib3.ACT_LRELU, None) == \
-        S["ERR_UNSUPPORTED"]
+    # ... in both dtypes (bfloat16 validates like float32)
+    assert L.conv3x3_bwd_data_act(G, None, Wt, Y, *d, 1, silu, None) == S["ERR_NULL_POINTER"]
+    assert L.conv3x3_bwd_data_act(G, Z, Wt, Z, *d, 1, silu, None) == S["ERR_ALIAS"]
+    assert L.conv3x3_bwd_weight_act(X, G, Z, Z, B, WS, 1 << 40, *d, 1, lib3.ACT_LRELU, None) == \
+        S["ERR_ALIAS"]
     # workspace rules carry over
     N, C, K, H, W = 32, 64, 64, 64, 64
     need = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W)
