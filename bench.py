@@ -391,8 +391,8 @@ class LayerRun:
         self.C0 = layer.cat if cat else 0
         self.pro = prologue
         if prologue:
-            if self.act or cat or layer.dtype != "f32":
-                raise ValueError("the *_gnsilu entry points: float32, no other fusion")
+            if self.act or cat:
+                raise ValueError("the *_gnsilu entry points take no other fusion")
             self.scale, self.shift = (v.to(dev) for v in wl.make_prologue(layer))
         if self.C0:
             if self.act:
@@ -776,8 +776,7 @@ def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=F
         for layer in layers:
             if match and not re.search(match, layer.name):
                 continue
-            if (cat and not layer.cat) or (prologue and layer.dtype != "f32") or \
-                    (out_bf16 and layer.dtype != "bf16"):
+            if (cat and not layer.cat) or (out_bf16 and layer.dtype != "bf16"):
                 continue
             run = LayerRun(layer, act, cat, prologue, out_bf16, split)
             ms, per = time_layer(run, steps, warmup)
@@ -834,8 +833,8 @@ def main():
                     help="with --sweep: time only the layers whose input is a skip "
                          "concatenation, through the *_cat entry points")
     ap.add_argument("--gnsilu", action="store_true",
-                    help="with --sweep: time the float32 layers through the *_gnsilu entry "
-                         "points (GroupNorm-apply + SiLU input prologue)")
+                    help="with --sweep: time the layers through the *_gnsilu entry points "
+                         "(GroupNorm-apply + SiLU input prologue)")
     ap.add_argument("--out-bf16", action="store_true",
                     help="with --sweep: time the bfloat16 layers with y and dx written as "
                          "bfloat16 (CONV3X3_BF16_IO)")

@@ -30,7 +30,8 @@ enum Act { kActNone = 0, kActSilu = 1, kActLrelu = 2 };
 // What a launch fuses.  zout: where the forward also writes z (may be null).
 // zsrc: z for the backward passes' gradient source (null: g is used as is).
 // pscale / pshift ([N][C] float32, null: no prologue): the input prologue's
-// scale and shift; px: x for backward-data's SiLU'(u) (same shape as dx).
+// scale and shift; px: x for backward-data's SiLU'(u) (same shape as dx;
+// for the bfloat16 kernels it points to bfloat16 values).
 struct ActArgs {
   int act = kActNone;
   float* zout = nullptr;

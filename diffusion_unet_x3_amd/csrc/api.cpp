@@ -94,17 +94,16 @@ bool is_part(const Split<T>& s, const void* p) {
 }
 
 // The input prologue's per-sample, per-channel scale and shift (both or
-// neither); float32 only.
+// neither).
 struct Prologue {
   const float* scale = nullptr;
   const float* shift = nullptr;
   bool on() const { return scale || shift; }
 };
 
-int check_prologue(const Prologue& pr, int dtype) {
+int check_prologue(const Prologue& pr) {
   if (!pr.on()) return CONV3X3_OK;
   if (!pr.scale || !pr.shift) return CONV3X3_ERR_NULL_POINTER;
-  if (dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
   return CONV3X3_OK;
 }
 
@@ -126,7 +125,7 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (rc) return rc;
   rc = check_act(act);
   if (rc) return rc;
-  rc = check_prologue(pr, dtype);
+  rc = check_prologue(pr);
   if (rc) return rc;
   if (is_part(x, y) || (const void*)y == w || (bias && y == bias)) return CONV3X3_ERR_ALIAS;
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
@@ -138,6 +137,9 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   pb.stride2 = geom == 2;
   pb.quad = geom == 1;
   pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z && !pr.on() && !geom;
+  // (bf16 prologue: four-wave tiles, whose staging threads hold scale and
+  // shift beside the x rows)
+  pb.four_waves = dtype != CONV3X3_F32 && pr.on();
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -167,8 +169,8 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
                         (float*)ws, s);
   } else {
     const bool vec = W % 8 == 0 && C % 16 == 0 && x.c0 % 16 == 0 && parts_aligned(x) &&
-                     aligned16(w) && buffer_sized((long)N * C * hw) &&
-                     buffer_sized((long)K * C * 9);
+                     aligned16(w) && (!pr.on() || (aligned16(pr.scale) && aligned16(pr.shift))) &&
+                     buffer_sized((long)N * C * hw) && buffer_sized((long)K * C * 9);
     Split<const uint16_t> xs{(const uint16_t*)x.p0, (const uint16_t*)x.p1, x.c0};
     ok = launch_fwd_bf16(pl, vec, xs, (const uint16_t*)w, bias, one(y, K), N, C, K, H, W, a,
                          dtype == CONV3X3_BF16_IO, (float*)ws, s);
@@ -195,7 +197,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   rc = check_act(act);
   if (rc) return rc;
   if (act != CONV3X3_ACT_NONE && !z) return CONV3X3_ERR_NULL_POINTER;
-  rc = check_prologue(pr, dtype);
+  rc = check_prologue(pr);
   if (rc) return rc;
   if (is_part(dx, g) || is_part(dx, w) || (act != CONV3X3_ACT_NONE && is_part(dx, z)) ||
       (dx.c0 > 0 && dx.c0 < C && dx.p0 == dx.p1))
@@ -212,7 +214,7 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   pb.quad = s2;
   pb.stride2 = geom == 1;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE && !pr.on() && !geom;
-  pb.four_waves = dtype != CONV3X3_F32 && act != CONV3X3_ACT_NONE;
+  pb.four_waves = dtype != CONV3X3_F32 && (act != CONV3X3_ACT_NONE || pr.on());
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -269,7 +271,7 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
       (db && (is_part(x, db) || (const void*)db == g || db == dw)))
     return CONV3X3_ERR_ALIAS;
   if (act != CONV3X3_ACT_NONE && (dw == z || (db && db == z))) return CONV3X3_ERR_ALIAS;
-  rc = check_prologue(pr, dtype);
+  rc = check_prologue(pr);
   if (rc) return rc;
   if (pr.on() && (dw == pr.scale || dw == pr.shift ||
                   (db && (db == pr.scale || db == pr.shift))))

@@ -187,6 +187,44 @@ __device__ __forceinline__ uint32_t act_grad_bf16_f32(float gy, float z, int act
   return INL ? act_grad_bf16_f64_inl(gy, z, act) : act_grad_bf16_f64_call(gy, z, act);
 }
 
+// The bfloat16 input prologue's operand: a = SiLU(u), u = x * scale +
+// shift, for a bfloat16 x, rounded to the nearest bfloat16 value as the
+// exact a rounds.  The float32 value (u by one fused multiply-add, the fast
+// sigmoid) is within |u| 1.2e-6 of the exact one; it decides unless
+// a +- |u| 2^-17 holds a rounding boundary (or a is one), and then a is
+// formed again in double precision.
+__device__ __forceinline__ uint32_t silu_affine_bf16_f64_inl(float x, float s, float t) {
+  const double u = (double)x * (double)s + (double)t;
+  return bf16_rne_f64(u / (1.0 + exp_f64(-u)));
+}
+
+__device__ __noinline__ uint32_t silu_affine_bf16_f64_call(float x, float s, float t) {
+  return silu_affine_bf16_f64_inl(x, s, t);
+}
+
+template <bool INL>
+__device__ __forceinline__ uint32_t silu_affine_bf16_f32(float x, float s, float t) {
+  const float u = __builtin_fmaf(x, s, t);
+  const float a = u * sigmoid_fast(u);
+  const float e = __builtin_fabsf(u) * 0x1p-17f;
+  const uint32_t r = bf16_rne(a);
+  const bool tie = (__builtin_bit_cast(uint32_t, a) & 0xffffu) == 0x8000u;
+  if (!tie && bf16_rne(a - e) == r && bf16_rne(a + e) == r) return r;
+  return INL ? silu_affine_bf16_f64_inl(x, s, t) : silu_affine_bf16_f64_call(x, s, t);
+}
+
+// xp packs two bfloat16 inputs of one channel (the first in the low half).
+template <bool INL>
+__device__ __forceinline__ uint32_t silu_affine_bf16x2(uint32_t xp, float s, float t) {
+  return silu_affine_bf16_f32<INL>(__builtin_bit_cast(float, xp << 16), s, t) |
+         (silu_affine_bf16_f32<INL>(__builtin_bit_cast(float, xp & 0xffff0000u), s, t) << 16);
+}
+
+template <bool INL>
+__device__ __forceinline__ uint32_t silu_affine_bf16(uint32_t x, float s, float t) {
+  return silu_affine_bf16_f32<INL>(__builtin_bit_cast(float, (x & 0xffffu) << 16), s, t);
+}
+
 // gp packs two bfloat16 gradients (the first in the low half); the result
 // packs the two operands the same way.
 template <bool INL>

@@ -93,14 +93,22 @@ __device__ __forceinline__ u32x4 tap_word(const uint32_t* d) {
 
 }  // namespace
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC, bool ZG>
+// ZG (backward-data): the source is a gradient gy at an activation's output,
+// multiplied by act'(zsrc) and rounded to bfloat16 as it is staged.
+// PRO: the input prologue -- forward: the staged input is
+// a = SiLU(x * pscale[n, c] + pshift[n, c]) rounded to bfloat16;
+// backward-data: the output is du = acc * SiLU'(u) with u from px (x, the
+// forward's bfloat16 input), pscale and pshift at the output position.
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC, bool ZG,
+          bool PRO>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ src1, int cin0,
     const uint16_t* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
     float* __restrict__ dst1, int cout0, int N, int Cin, int Cout, int H, int W, int tiles_w,
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
     uint32_t dst1_bytes, int act, float* __restrict__ zout, int outb, int per_split,
-    float* __restrict__ part, const float* __restrict__ zsrc) {
+    float* __restrict__ part, const float* __restrict__ zsrc, const float* __restrict__ pscale,
+    const float* __restrict__ pshift, const uint16_t* __restrict__ px) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -193,7 +201,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 
   // (ZG: the source is a gradient gy multiplied by act'(zsrc) as it is
   // staged; its float32 z items take the registers of the second set)
-  constexpr int NSET = (WSPEC || ZG) ? 1 : 2;
+  constexpr bool SPRO = PRO && MODE == kFwd;  // the prologue in the loader
+  constexpr int NSET = (WSPEC || ZG || SPRO) ? 1 : 2;
   constexpr int WBASE = WSPEC ? 8 : 0;  // first register word of the weight items
   constexpr int SLOTS = WSPEC ? 8 + WK * NSTG : (NSTG > 8 ? NSTG : 8);
   u32x4 st[NSET][VEC ? SLOTS : 1];
@@ -204,6 +213,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // halo item
   f32x4 zx[NSET][ZG && VEC ? 16 : 1];
   float zh[NSET][ZG && VEC ? 8 : 1];
+  // SPRO: scale (words 0, 1) and shift (2, 3) of the x item's and of the
+  // halo item's 8 channels
+  f32x4 psx[NSET][SPRO && VEC ? 4 : 1];
+  f32x4 psh[NSET][SPRO && VEC ? 4 : 1];
 #pragma unroll
   for (int k = 0; k < NSET; ++k)
 #pragma unroll
@@ -220,9 +233,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // z has the source's shape in float32: twice its byte offsets (below 2^31:
   // the caller keeps every float32 tensor under 2 GiB)
   const __amdgpu_buffer_rsrc_t zv = buffer_view(zsrc, ZG ? 2u * src_bytes : 0u);
+  // scale / shift: [N][Cin] float32
+  const uint32_t ps_bytes = SPRO ? 4u * (uint32_t)N * (uint32_t)Cin : 0u;
+  const __amdgpu_buffer_rsrc_t psv = buffer_view(pscale, ps_bytes);
+  const __amdgpu_buffer_rsrc_t ptv = buffer_view(pshift, ps_bytes);
   const uint32_t hw2 = 2u * (uint32_t)(H * W);
   // x and halo item offsets in src (channel 8g of image n) and in src1
   uint32_t xoff = kOutside, hoff = kOutside, xoff1 = kOutside, hoff1 = kOutside, woff[WK];
+  uint32_t pxo = kOutside, pho = kOutside;  // SPRO: scale / shift of the x and halo items
   int xdst = 0;  // LDS word of the x item's first pixel
 #pragma unroll
   for (int k = 0; k < WK; ++k) woff[k] = kOutside;
@@ -241,6 +259,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if (n < N && h >= 0 && h < H && w < W) {
         xoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * H + h) * W + w);
         xoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * H + h) * W + w);
+        pxo = 4u * (uint32_t)(n * Cin + 8 * g);
       }
       xdst = g * PLW + (img * HR + rr) * RS + 4 + 8 * q;
     }
@@ -255,6 +274,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if (n < N && h >= 0 && h < H && w >= 0 && w < W) {
         hoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * H + h) * W + w);
         hoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * H + h) * W + w);
+        pho = 4u * (uint32_t)(n * Cin + 8 * g);
       }
     }
 #pragma unroll
@@ -290,6 +310,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const uint32_t b = (s1 ? xoff1 : xoff) + fx;
 #pragma unroll
       for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, b + (uint32_t)i * hw2);
+      if constexpr (SPRO) {
+        // (one source tensor: s1 is false) 16 channels per fill
+        const uint32_t pb = pxo + 64u * f;
+        psx[S][0] = __builtin_bit_cast(f32x4, buffer_load16(psv, pb));
+        psx[S][1] = __builtin_bit_cast(f32x4, buffer_load16(psv, pb + 16u));
+        psx[S][2] = __builtin_bit_cast(f32x4, buffer_load16(ptv, pb));
+        psx[S][3] = __builtin_bit_cast(f32x4, buffer_load16(ptv, pb + 16u));
+      }
       if constexpr (ZG) {
         // (one source tensor: s1 is false)
         const uint32_t zb = (xoff == kOutside ? kOutside : 2u * xoff) + 2u * fx;
@@ -305,6 +333,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const uint32_t b = (s1 ? hoff1 : hoff) + fx;
 #pragma unroll
       for (int i = 0; i < 8; ++i) hv[S][i] = buffer_load2(sv, b + (uint32_t)i * hw2);
+      if constexpr (SPRO) {
+        const uint32_t pb = pho + 64u * f;
+        psh[S][0] = __builtin_bit_cast(f32x4, buffer_load16(psv, pb));
+        psh[S][1] = __builtin_bit_cast(f32x4, buffer_load16(psv, pb + 16u));
+        psh[S][2] = __builtin_bit_cast(f32x4, buffer_load16(ptv, pb));
+        psh[S][3] = __builtin_bit_cast(f32x4, buffer_load16(ptv, pb + 16u));
+      }
       if constexpr (ZG) {
         const uint32_t zb = (hoff == kOutside ? kOutside : 2u * hoff) + 2u * fx;
 #pragma unroll
@@ -344,6 +379,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       if (hrole && halo_loads) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[S][i] = act_grad_bf16<false>(hv[S][i], zh[S][i], act);
+      }
+    }
+    if constexpr (SPRO) {
+      // a = SiLU(x * scale + shift), rounded to bfloat16, before the
+      // transposes (row i is channel 8g + i; items outside the image load
+      // x = scale = shift = 0 and stage SiLU(0) = 0, the zero padding of a)
+      if (xrole) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sc = psx[S][i >> 2][i & 3], sh = psx[S][2 + (i >> 2)][i & 3];
+          st[S][i].x = silu_affine_bf16x2<false>(st[S][i].x, sc, sh);
+          st[S][i].y = silu_affine_bf16x2<false>(st[S][i].y, sc, sh);
+          st[S][i].z = silu_affine_bf16x2<false>(st[S][i].z, sc, sh);
+          st[S][i].w = silu_affine_bf16x2<false>(st[S][i].w, sc, sh);
+        }
+      }
+      if (hrole && halo_loads) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          hv[S][i] = silu_affine_bf16<false>(hv[S][i], psh[S][i >> 2][i & 3],
+                                             psh[S][2 + (i >> 2)][i & 3]);
       }
     }
     if (xrole) {
@@ -431,6 +487,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
           const long e = ((long)n * cs + cl0 + ch) * HW + (long)h * W + w;
           v = sx[e];
           if constexpr (ZG) v = (uint16_t)act_grad_bf16<false>(v, zsrc[e], act);
+          if constexpr (SPRO) {
+            const long pc = (long)n * Cin + cl0 + ch;  // (one source tensor)
+            v = (uint16_t)silu_affine_bf16<false>(v, pscale[pc], pshift[pc]);
+          }
         }
         xh[((ch >> 3) * PLW + (img * HR + rr) * RS + 4 + cc) * 8 + (ch & 7)] = v;
       }
@@ -647,6 +707,64 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   // float32, to its slot of the workspace (one tensor of dst's shape per
   // slice); the reduce kernel adds the slices and applies the rest.
   const int cw = col0 + wco * (BCO / WCO);  // first output channel of this wave
+  if constexpr (MODE == kBwdData && PRO) {
+    // du = acc * SiLU'(u), u = x * scale + shift at the output position (px
+    // has dx's shape, one tensor).  Scale and shift of the tile's channels
+    // and images go through LDS (the operand tiles are no longer read);
+    // then, four elements at a time, x's bfloat16 value, du and its store
+    // (elements outside the tensor read zero and store nothing).
+    static_assert(2 * IMGS * BCO <= 4 * 2 * XW, "scale/shift fit");
+    float* ps_s = reinterpret_cast<float*>(xs);
+    float* pt_s = ps_s + IMGS * BCO;
+    __syncthreads();
+    for (int e = tid; e < IMGS * BCO; e += NT) {
+      const int n = o.n0 + e / BCO, co = col0 + e % BCO;
+      const bool ok = n < N && co < Cout;
+      ps_s[e] = ok ? pscale[(long)n * Cout + co] : 0.f;
+      pt_s[e] = ok ? pshift[(long)n * Cout + co] : 0.f;
+    }
+    __syncthreads();
+    if (wave >= NC) return;
+    const uint32_t es = outb ? 2u : 4u;
+    const __amdgpu_buffer_rsrc_t xv_b =
+        buffer_view(px, 2u * (uint32_t)N * (uint32_t)Cout * (uint32_t)HW);
+    const __amdgpu_buffer_rsrc_t dv_b = buffer_view(dst, dst_bytes);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wpx * (BM / WPX) + j * 32 + l32;
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      const bool in = n < N && h < H && w < W;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int v0 = 0; v0 < 16; v0 += 4) {
+          float xe[4];
+          uint32_t so[4];  // store offsets (kOutside: no store)
+#pragma unroll
+          for (int v = v0; v < v0 + 4; ++v) {
+            const int co = cw + i * 32 + acc_row(v, hi);
+            const bool ok = in && co < Cout;
+            const uint32_t e = ((uint32_t)n * Cout + co) * (uint32_t)HW + (uint32_t)(h * W + w);
+            so[v - v0] = ok ? es * e : kOutside;
+            xe[v - v0] =
+                __builtin_bit_cast(float, buffer_load2(xv_b, ok ? 2u * e : kOutside) << 16);
+          }
+#pragma unroll
+          for (int v = v0; v < v0 + 4; ++v) {
+            const int e = img * BCO + (cw - col0) + i * 32 + acc_row(v, hi);
+            const float du =
+                acc[i][j][v] * act_slope(kActSilu, __builtin_fmaf(xe[v - v0], ps_s[e], pt_s[e]));
+            if (outb)
+              buffer_store2(dv_b, so[v - v0], 0u, bf16_rne(du));
+            else
+              buffer_store4(dv_b, so[v - v0], 0u, du);
+          }
+        }
+      }
+    }
+    return;
+  }
   const bool plain = part != nullptr || MODE != kFwd || (act == kActNone && zout == nullptr);
   const uint32_t slot_bytes = (uint32_t)N * (uint32_t)Cout * (uint32_t)HW * 4u;
   float* const od = part ? part + (size_t)blockIdx.z * ((size_t)slot_bytes / 4) : oseg ? dst1 : dst;
@@ -802,12 +920,12 @@ void launch_split_reduce(const float* part, int S, long slot, float* dst, hipStr
                      (float*)nullptr);
 }
 
-template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool ZG>
+template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool ZG, bool PRO>
 static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                             const uint16_t* wt, const float* bias, Split<float> dst, int N,
                             int Cin, int Cout, int H, int W, const ActArgs& a, bool out_bf16,
                             float* ws, hipStream_t stream) {
-  if constexpr (ZG && NW != 4) {
+  if constexpr ((ZG || PRO) && NW != 4) {
     return;  // not instantiated: launch_fwd_bf16 refuses these plans
   } else {
   // split reduction: partial sums into ws, then split_reduce_kernel
@@ -822,17 +940,19 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
   const bool small = ob0 * zf < 2147483648L && ob1 * zf < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
   if (vec)
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true, ZG>), grid,
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true, ZG, PRO>), grid,
                        block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
                        dst.c0, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
                        (uint32_t)(N * src.c0 * hw * 2), (uint32_t)(N * (Cin - src.c0) * hw * 2),
                        (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout,
-                       out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc);
+                       out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc, a.pscale, a.pshift,
+                       (const uint16_t*)a.px);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false, ZG>), grid,
-                       block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
+    hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false, ZG, PRO>),
+                       grid, block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
                        dst.c0, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1,
-                       a.act, a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc);
+                       a.act, a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc,
+                       a.pscale, a.pshift, (const uint16_t*)a.px);
   if (part) {
     const long slot = (long)N * Cout * hw;
     dim3 rg((unsigned)((slot + 1023) / 1024)), rb(256);
@@ -848,25 +968,34 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
   if (pl.chunk != 16) return false;
   // a split reduction needs its workspace and one output tensor
   if (pl.split > 1 && (ws == nullptr || dst.c0 != Cout)) return false;
-  // Neither pass has the input prologue (the caller rejects it); a fused
-  // activation gradient (a.zsrc) needs one source tensor, no split and a
+  // A fused activation gradient (a.zsrc, backward-data) or the input
+  // prologue (a.pscale) needs one source / output tensor, no split and a
   // four-wave tile (the eight-wave tile's staging waves cannot also hold
-  // the float32 z rows; the planner keeps to the four-wave tiles for it).
-  if (a.pscale != nullptr) return false;
-  if (a.zsrc != nullptr &&
-      (pl.pass == kFwd || src.c0 != Cin || pl.split > 1 || pl.threads != 256))
+  // their float32 operands; the planner keeps to the four-wave tiles for
+  // them).  The forward's prologue and a fused gradient do not combine.
+  const bool pro = a.pscale != nullptr;
+  if ((a.zsrc != nullptr || pro) &&
+      (src.c0 != Cin || dst.c0 != Cout || pl.split > 1 || pl.threads != 256))
     return false;
+  if (a.zsrc != nullptr && (pl.pass == kFwd || pro)) return false;
+  if (pro && pl.pass == kBwdData && a.px == nullptr) return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_, NW_)                                              \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                  \
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \
-    if (pl.pass == kFwd)                                                                        \
-      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_, false>(                            \
+    if (pl.pass == kFwd && !pro)                                                                \
+      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_, false, false>(                     \
           pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);            \
-    else if (a.zsrc == nullptr)                                                                 \
-      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, false>(                        \
+    else if (pl.pass == kFwd)                                                                   \
+      launch_bf16_cfg<kFwd, TW_, TH_, IMGS_, CO_, WCO_, NW_, false, true>(                      \
+          pl, vec, src, wt, bias, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);            \
+    else if (a.zsrc != nullptr)                                                                 \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, true, false>(                  \
+          pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);         \
+    else if (pro)                                                                               \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, false, true>(                  \
           pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);         \
     else                                                                                        \
-      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, true>(                         \
+      launch_bf16_cfg<kBwdData, TW_, TH_, IMGS_, CO_, WCO_, NW_, false, false>(                 \
           pl, vec, src, wt, nullptr, dst, N, Cin, Cout, H, W, a, out_bf16, ws, stream);         \
     return true;                                                                                \
   }

@@ -32,13 +32,16 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 
 // ZG: g is a gradient gy at an activation's output, multiplied by act'(zsrc)
 // (zsrc float32, g's shape) and rounded to bfloat16 as it is staged.
-template <int TW, int TH, int IMGS, bool VEC, bool ZG>
+// PRO: the input prologue -- x is staged as a = SiLU(x * pscale[n, c] +
+// pshift[n, c]) rounded to bfloat16 (one x tensor).
+template <int TW, int TH, int IMGS, bool VEC, bool ZG, bool PRO>
 __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ x1, int cx0,
     const uint16_t* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
     int C, int K, int H, int W, int tiles_w, int tiles_h, int nchunks, int per_split,
     long slice_stride, int split, int tiles_c, int tiles_k, uint32_t x_bytes, uint32_t x1_bytes,
-    uint32_t g_bytes, int act, const float* __restrict__ zsrc) {
+    uint32_t g_bytes, int act, const float* __restrict__ zsrc, const float* __restrict__ pscale,
+    const float* __restrict__ pshift) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P % 16 == 0, "whole 16-pixel MFMA steps");
   static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
@@ -90,11 +93,14 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   // set just emptied into LDS for chunk i + 1, so each load has two chunks of
   // MFMA work to arrive.  With ZG the float32 z items take the registers of
   // the second set: one set, loads one chunk ahead.
-  constexpr int NSET = ZG ? 1 : 2;
+  constexpr int NSET = (ZG || PRO) ? 1 : 2;
   u32x4 gv[NSET][VEC ? GN : 1];
   u32x4 xv[NSET][VEC ? XN : 1];
   uint16_t xh[NSET][VEC ? HN : 1];
   f32x4 zv[NSET][ZG && VEC ? 2 * GN : 1];
+  // PRO: scale and shift of each x item's and halo element's channel
+  float pxs[NSET][PRO && VEC ? XN : 1], pxt[NSET][PRO && VEC ? XN : 1];
+  float phs[NSET][PRO && VEC ? HN : 1], pht[NSET][PRO && VEC ? HN : 1];
   // With a single tile across the width both halo columns are padding: they
   // stay zero and are not loaded.
   const bool halo_loads = tiles_w > 1;
@@ -110,6 +116,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   // z: g's shape in float32, twice g's byte offsets (below 2^31: the caller
   // keeps every float32 tensor under 2 GiB)
   const __amdgpu_buffer_rsrc_t zview = buffer_view(zsrc, ZG ? 2u * g_bytes : 0u);
+  // scale / shift: [N][C] float32
+  const uint32_t ps_bytes = PRO ? 4u * (uint32_t)N * (uint32_t)C : 0u;
+  const __amdgpu_buffer_rsrc_t psview = buffer_view(pscale, ps_bytes);
+  const __amdgpu_buffer_rsrc_t ptview = buffer_view(pshift, ps_bytes);
   auto load_tiles = [&](auto set_c, int chunk) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     if constexpr (VEC) {
@@ -146,6 +156,12 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const bool ok = (XI % NT == 0 || it < XI) && n < N && cl < cn && h >= 0 && h < H && w < W;
         xv[SET][k] = buffer_load16(
             xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w) : kOutside);
+        if constexpr (PRO) {
+          // (one x tensor: channel c0 + cl)
+          const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
+          pxs[SET][k] = __builtin_bit_cast(float, buffer_load4(psview, po));
+          pxt[SET][k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
+        }
       }
 #pragma unroll
       for (int k = 0; k < HN; ++k) {
@@ -163,6 +179,11 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
                         w >= 0 && w < W;
         xh[SET][k] = (uint16_t)buffer_load2(
             xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w) : kOutside);
+        if constexpr (PRO) {
+          const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
+          phs[SET][k] = __builtin_bit_cast(float, buffer_load4(psview, po));
+          pht[SET][k] = __builtin_bit_cast(float, buffer_load4(ptview, po));
+        }
       }
     }
   };
@@ -179,7 +200,16 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int q = it % XQ;
           const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
           const int cl = t / (IMGS * HR);
-          *reinterpret_cast<u32x4*>(&xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + 8 * q]) = xv[SET][k];
+          u32x4 v = xv[SET][k];
+          if constexpr (PRO) {
+            // a = SiLU(x * scale + shift), rounded to bfloat16 (items outside
+            // the image load x = scale = shift = 0: the zero padding of a)
+            v.x = silu_affine_bf16x2<false>(v.x, pxs[SET][k], pxt[SET][k]);
+            v.y = silu_affine_bf16x2<false>(v.y, pxs[SET][k], pxt[SET][k]);
+            v.z = silu_affine_bf16x2<false>(v.z, pxs[SET][k], pxt[SET][k]);
+            v.w = silu_affine_bf16x2<false>(v.w, pxs[SET][k], pxt[SET][k]);
+          }
+          *reinterpret_cast<u32x4*>(&xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + 8 * q]) = v;
         }
       }
 #pragma unroll
@@ -189,7 +219,11 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int side = it & 1;
           const int t = it >> 1;
           const int cl = t / (IMGS * HR);
-          xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + (side ? TW : -1)] = xh[SET][k];
+          uint16_t v = xh[SET][k];
+          if constexpr (PRO) {
+            if (halo_loads) v = (uint16_t)silu_affine_bf16<false>(v, phs[SET][k], pht[SET][k]);
+          }
+          xs[cl * PLX + (t % (IMGS * HR)) * RSX + 8 + (side ? TW : -1)] = v;
         }
       }
       if constexpr (ZG) {
@@ -256,8 +290,13 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int cl = t / IMGS;
           const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           uint16_t v = 0;
-          if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W)
+          if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W) {
             v = xsrc[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
+            if constexpr (PRO) {
+              const long pc = (long)n * C + c0 + cl;
+              v = (uint16_t)silu_affine_bf16<false>(v, pscale[pc], pshift[pc]);
+            }
+          }
           xs[cl * PLX + (img * HR + rr) * RSX + 8 + cc] = v;
         }
       }
@@ -372,7 +411,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
   }
 }
 
-template <int TW, int TH, int IMGS, bool ZG>
+template <int TW, int TH, int IMGS, bool ZG, bool PRO>
 static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, Split<const uint16_t> x,
                                    const uint16_t* g, float* out, float* out_db,
                                    long slice_stride, int N, int C, int K, int H, int W,
@@ -381,25 +420,26 @@ static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, Split<const uint16_
   const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
   const long hw2 = (long)H * W * 2;
   if (vec)
-    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, ZG>), grid, block, 0, stream,
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, ZG, PRO>), grid, block, 0, stream,
                        x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
                        (K + 63) / 64, (uint32_t)(N * x.c0 * hw2),
-                       (uint32_t)(N * (C - x.c0) * hw2), (uint32_t)(N * K * hw2), a.act, a.zsrc);
+                       (uint32_t)(N * (C - x.c0) * hw2), (uint32_t)(N * K * hw2), a.act, a.zsrc,
+                       a.pscale, a.pshift);
   else
-    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false, ZG>), grid, block, 0, stream,
+    hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false, ZG, PRO>), grid, block, 0, stream,
                        x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
-                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc);
+                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc, a.pscale, a.pshift);
 }
 
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
                        float* dw, float* db, float* ws, int N, int C, int K, int H, int W,
                        const ActArgs& a, hipStream_t stream) {
   if (pl.threads != 768) return false;
-  // No input prologue on the bfloat16 backward-weight pass (the caller
-  // rejects it).
-  if (a.pscale != nullptr) return false;
+  // the prologue needs one x tensor and does not combine with a fused
+  // activation gradient
+  if (a.pscale != nullptr && (a.zsrc != nullptr || x.c0 != C)) return false;
   const long n_dw = (long)K * C * 9;
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);
@@ -408,11 +448,14 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const 
 #define CONV3X3_X(TW_, TH_, IMGS_)                                                          \
   if (!found && pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_) {                         \
     if (a.zsrc)                                                                             \
-      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, true>(pl, vec, x, g, out, out_db, stride, N, C, \
-                                                    K, H, W, a, stream);                      \
+      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, true, false>(pl, vec, x, g, out, out_db, stride, \
+                                                           N, C, K, H, W, a, stream);          \
+    else if (a.pscale)                                                                        \
+      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, false, true>(pl, vec, x, g, out, out_db, stride, \
+                                                           N, C, K, H, W, a, stream);          \
     else                                                                                      \
-      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, false>(pl, vec, x, g, out, out_db, stride, N, C,\
-                                                     K, H, W, a, stream);                     \
+      launch_wgrad_bf16_geom<TW_, TH_, IMGS_, false, false>(pl, vec, x, g, out, out_db,        \
+                                                            stride, N, C, K, H, W, a, stream); \
     found = true;                                                                           \
   }
   CONV3X3_WGRAD_BF16_CONFIGS(CONV3X3_X)

@@ -279,12 +279,15 @@ int conv3x3_bwd_weight_cat(const void* x0, const void* x1, int C0, int C1, const
  *                               gradient with respect to u (what a GroupNorm
  *                               backward takes); x, scale, shift are the
  *                               forward's and du is [N][C][H][W] float32
+ *                               (bfloat16 for CONV3X3_BF16_IO)
  *   conv3x3_bwd_weight_gnsilu : dw, db of the convolution on a (as
  *                               conv3x3_bwd_weight, same workspace size)
  *
- * float32 only (CONV3X3_ERR_UNSUPPORTED for bfloat16); backward-data also
- * needs x below 2 GiB (else CONV3X3_ERR_UNSUPPORTED).  scale and shift must
- * not be NULL.  Other arguments, limits and errors as the plain passes.
+ * bfloat16 modes: x is bfloat16 and the contraction's operand a is
+ * bfloat16, rounded to the nearest bfloat16 value (ties to even) as the
+ * exact SiLU(x * scale + shift) rounds; du is not rounded (float32, unless
+ * CONV3X3_BF16_IO).  scale and shift must not be NULL.  Other arguments,
+ * limits and errors as the plain passes.
  */
 int conv3x3_fwd_gnsilu(const void* x, const float* scale, const float* shift, const void* w,
                        const float* bias, float* y, int N, int C, int K, int H, int W, int dtype,

@@ -299,7 +299,9 @@ def conv3x3_bwd_weight_cat_at(x0, x1, g, idx):
 # offset per sample and channel.  The convolution pads a (not x) with zeros.
 # The backward passes: the gradient with respect to u is
 # bwd_data(g, w) * SiLU'(u) (what the GroupNorm backward consumes), and dw is
-# the plain backward-weight with the input a.
+# the plain backward-weight with the input a.  In bfloat16 mode a is a
+# bfloat16 operand: the exact a rounded once to the nearest bfloat16 value
+# (du stays unrounded: it is a float32 output).
 
 
 def _prologue_u(x, scale, shift):
@@ -310,14 +312,17 @@ def _prologue_u(x, scale, shift):
     return x * s[:, :, None, None] + t[:, :, None, None]
 
 
-def prologue_apply(x, scale, shift):
-    """a = SiLU(x * scale[n, c] + shift[n, c])."""
-    return act_forward(_prologue_u(x, scale, shift), ACT_SILU)
+def prologue_apply(x, scale, shift, bf16=False):
+    """a = SiLU(x * scale[n, c] + shift[n, c]).  bf16=True: the bfloat16
+    path's operand, a rounded once to the nearest bfloat16 value, ties to
+    even (round_to_bf16 below)."""
+    a = act_forward(_prologue_u(x, scale, shift), ACT_SILU)
+    return round_to_bf16(a) if bf16 else a
 
 
-def conv3x3_fwd_gnsilu(x, scale, shift, w, b=None):
-    """y = conv3x3_fwd(SiLU(x * scale + shift), w, b)."""
-    return conv3x3_fwd(prologue_apply(x, scale, shift), w, b)
+def conv3x3_fwd_gnsilu(x, scale, shift, w, b=None, bf16=False):
+    """y = conv3x3_fwd(SiLU(x * scale + shift), w, b) (bf16: on the rounded a)."""
+    return conv3x3_fwd(prologue_apply(x, scale, shift, bf16), w, b)
 
 
 def conv3x3_bwd_data_gnsilu(g, w, x, scale, shift):
@@ -325,9 +330,10 @@ def conv3x3_bwd_data_gnsilu(g, w, x, scale, shift):
     return act_grad(conv3x3_bwd_data(g, w), _prologue_u(x, scale, shift), ACT_SILU)
 
 
-def conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True):
-    """(dw, db) of <conv3x3(SiLU(x * scale + shift); w) + b, g>."""
-    return conv3x3_bwd_weight(prologue_apply(x, scale, shift), g, want_db)
+def conv3x3_bwd_weight_gnsilu(x, scale, shift, g, want_db=True, bf16=False):
+    """(dw, db) of <conv3x3(SiLU(x * scale + shift); w) + b, g> (bf16: on the
+    rounded a)."""
+    return conv3x3_bwd_weight(prologue_apply(x, scale, shift, bf16), g, want_db)
 
 
 # ---------------------------------------------------------------------------

@@ -217,10 +217,11 @@ def test_prologue_argument_checks():
     assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, None, Y, *d, 0, None) == null
     assert L.conv3x3_bwd_data_gnsilu(G, Wt, None, SC, SH, Y, *d, 0, None) == null
     assert L.conv3x3_bwd_weight_gnsilu(X, None, SH, G, Y, B, WS, 1 << 30, *d, 0, None) == null
-    # float32 only
-    assert L.conv3x3_fwd_gnsilu(X, SC, SH, Wt, B, Y, *d, 1, None) == unsup
-    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, Y, *d, 1, None) == unsup
-    assert L.conv3x3_bwd_weight_gnsilu(X, SC, SH, G, Y, B, WS, 1 << 30, *d, 1, None) == unsup
+    # both dtypes (bfloat16 validates like float32)
+    assert L.conv3x3_fwd_gnsilu(X, SC, None, Wt, B, Y, *d, 1, None) == null
+    assert L.conv3x3_fwd_gnsilu(X, SC, SH, Wt, B, SC, *d, 1, None) == alias
+    assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, X, *d, 1, None) == alias
+    assert L.conv3x3_bwd_weight_gnsilu(X, SC, SH, G, SC, B, WS, 1 << 30, *d, 1, None) == alias
     # outputs may not alias scale / shift / x
     assert L.conv3x3_fwd_gnsilu(X, SC, SH, Wt, B, SC, *d, 0, None) == alias
     assert L.conv3x3_bwd_data_gnsilu(G, Wt, X, SC, SH, X, *d, 0, None) == alias

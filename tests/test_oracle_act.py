@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+from bf16_ref import nearest_bf16
 
 ACTS = [oracle.ACT_NONE, oracle.ACT_SILU, oracle.ACT_LRELU]
 
@@ -103,26 +104,6 @@ def test_fused_backward_is_gradient_of_fused_forward(act):
             assert abs((lp - lm) / (2 * h) - grad[i]) < 1e-6, (i, grad[i])
 
 
-def _bf16_grid():
-    """Every finite non-negative bfloat16 value, ascending, with its bit
-    pattern (the brute-force rounding below searches this list)."""
-    bits = np.arange(0, 0x7f80, dtype=np.uint32)
-    vals = (bits << 16).view(np.float32).astype(np.float64)
-    return vals, bits
-
-
-def _nearest_bf16(x):
-    """Round to the nearest bfloat16 value, ties to the even bit pattern,
-    by search over the whole grid (independent of round_to_bf16)."""
-    vals, bits = _bf16_grid()
-    a = np.abs(x)
-    hi = np.clip(np.searchsorted(vals, a), 1, vals.size - 1)
-    lo = hi - 1
-    dlo, dhi = a - vals[lo], vals[hi] - a
-    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(bits[lo] % 2 == 0, lo, hi)))
-    return np.sign(x) * vals[pick]
-
-
 def _torch_slope(z, act):
     zt = torch.from_numpy(np.asarray(z, np.float64)).requires_grad_(True)
     f = torch.nn.functional.silu if act == oracle.ACT_SILU else \
@@ -141,7 +122,7 @@ def test_bf16_operand_is_exact_product_rounded_once(act):
     z = rng.normal(0.0, 3.0, size=20000).astype(np.float32).astype(np.float64)
     slope = np.ones_like(z) if act == oracle.ACT_NONE else _torch_slope(z, act)
     g = oracle.act_grad(gy, z, act, bf16=True)
-    assert np.array_equal(g, _nearest_bf16(gy * slope))
+    assert np.array_equal(g, nearest_bf16(gy * slope))
     # every value is a bfloat16 value
     assert np.array_equal(g, torch.from_numpy(g).float().bfloat16().double().numpy())
 
@@ -157,7 +138,7 @@ def test_bf16_operand_does_not_round_through_float32():
     zt = torch.from_numpy(z).requires_grad_(True)
     (s32,) = torch.autograd.grad(torch.nn.functional.silu(zt), zt, torch.ones_like(zt))
     f32_path = (torch.from_numpy(gy.astype(np.float32)) * s32).bfloat16().double().numpy()
-    exact = _nearest_bf16(gy * _torch_slope(z, oracle.ACT_SILU))
+    exact = nearest_bf16(gy * _torch_slope(z, oracle.ACT_SILU))
     differ = f32_path != exact
     assert differ.sum() >= 10
     g = oracle.act_grad(gy[differ], z[differ].astype(np.float64), oracle.ACT_SILU, bf16=True)

@@ -149,3 +149,28 @@ def _valid_conv(a_padded, w, b):
         for s in range(3):
             y += np.einsum("nchw,kc->nkhw", a_padded[:, :, r:r + H, s:s + W], w[:, :, r, s])
     return y
+
+
+def test_bf16_operand_is_exact_activation_rounded_once():
+    """bfloat16 mode: the operand is a = SiLU(x * scale + shift) for the
+    bfloat16 x, rounded once to the nearest bfloat16 value -- against torch's
+    float64 SiLU and a brute-force nearest search over all bfloat16 values;
+    the zero padding and the convolutions on it follow."""
+    from bf16_ref import nearest_bf16
+    x, s, t, w, b, g = _draw(2, 6, 3, 5, 7, 51)
+    x = torch.from_numpy(x).bfloat16().double().numpy()
+    s = s.astype(np.float32).astype(np.float64)
+    t = t.astype(np.float32).astype(np.float64)
+    u = torch.from_numpy(x * s[:, :, None, None] + t[:, :, None, None])
+    ref = nearest_bf16(F.silu(u).numpy())
+    a = oracle.prologue_apply(x, s, t, bf16=True)
+    assert np.array_equal(a, ref)
+    assert not np.array_equal(a, oracle.prologue_apply(x, s, t))  # it does round
+    y = oracle.conv3x3_fwd_gnsilu(x, s, t, w, b, bf16=True)
+    assert np.allclose(y, F.conv2d(torch.from_numpy(ref), torch.from_numpy(w),
+                                   torch.from_numpy(b), padding=1).numpy(), rtol=0, atol=1e-12)
+    dw, db = oracle.conv3x3_bwd_weight_gnsilu(x, s, t, g, bf16=True)
+    dw_ref = torch.nn.grad.conv2d_weight(torch.from_numpy(ref), w.shape, torch.from_numpy(g),
+                                         padding=1).numpy()
+    assert np.allclose(dw, dw_ref, rtol=0, atol=1e-12)
+    assert np.allclose(db, g.sum(axis=(0, 2, 3)), rtol=0, atol=1e-12)
