@@ -43,18 +43,21 @@ PASSES = ("fwd", "bwd_data", "bwd_weight")
 # kernel on the same stream: split_reduce_kernel (split forward /
 # backward-data) or wgrad_reduce*_kernel (backward-weight split-K); profile
 # summaries count it toward the pass whose main kernel precedes it.
-MAIN_KERNELS = {("f32", "fwd"): "conv3x3::fwd_f32_kernel<0,",
-                ("f32", "bwd_data"): "conv3x3::fwd_f32_kernel<1,",
-                ("f32", "bwd_weight"): "conv3x3::wgrad_f32_kernel<",
-                ("bf16", "fwd"): "conv3x3::fwd_bf16_kernel<0,",
-                ("bf16", "bwd_data"): "conv3x3::fwd_bf16_kernel<1,",
-                ("bf16", "bwd_weight"): "conv3x3::wgrad_bf16_kernel<"}
-REDUCE_KERNELS = ("conv3x3::split_reduce_kernel", "conv3x3::wgrad_reduce")
+MAIN_KERNELS = {("f32", "fwd"): ("conv3x3::fwd_f32_kernel<0,",),
+                ("f32", "bwd_data"): ("conv3x3::fwd_f32_kernel<1,",),
+                ("f32", "bwd_weight"): ("conv3x3::wgrad_f32_kernel<",
+                                        "conv3x3::wgrad_stem_kernel<float,"),
+                ("bf16", "fwd"): ("conv3x3::fwd_bf16_kernel<0,",),
+                ("bf16", "bwd_data"): ("conv3x3::fwd_bf16_kernel<1,",),
+                ("bf16", "bwd_weight"): ("conv3x3::wgrad_bf16_kernel<",
+                                         "conv3x3::wgrad_stem_kernel<unsigned short,")}
+REDUCE_KERNELS = ("conv3x3::split_reduce_kernel", "conv3x3::wgrad_reduce",
+                  "conv3x3::stem_reduce_kernel")
 
 
 def pass_kernels(dtype, pass_):
     """Name prefixes of the kernels one pass launches."""
-    return [MAIN_KERNELS[(dtype, pass_)]] + list(REDUCE_KERNELS)
+    return list(MAIN_KERNELS[(dtype, pass_)]) + list(REDUCE_KERNELS)
 
 
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # dense MFMA peaks, MI355X
@@ -74,6 +77,7 @@ def attribute_passes(rows):
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         name = _kernel_name(r)
         fam = next((k for k, pre in MAIN_KERNELS.items() if name.startswith(pre)), None)
+        # (str.startswith takes the tuple of a family's prefixes)
         if fam is not None:
             launches.append((fam, [r]))
         elif name.startswith(REDUCE_KERNELS) and launches:
@@ -729,14 +733,20 @@ def sweep_summary(dtype, layers, ms, fam, act="none"):
     total = sum(3 * flops_per_pass(*layer.shape) for layer in layers)
     dom = max(PASSES, key=lambda p: fam[p]["ms"])
     n = len(layers)
-    achieved = fam[dom]["gflop"] / fam[dom]["ms"]  # GFLOP/ms = TFLOP/s
-    roof = {"bound": "mfma", "kernel": f"{dtype}/{dom}",
+    # the binding roof of the family: MFMA unless its arithmetic intensity
+    # (algorithmic FLOPs / bytes) is below the ridge peak / 8 TB/s
+    hbm = fam[dom]["gflop"] / fam[dom]["alg_gb"] < PEAK_TFLOPS[dtype] * 1e3 / PEAK_HBM_GBS
+    if hbm:
+        achieved, peak, unit = fam[dom]["alg_gb"] / fam[dom]["ms"] * 1e3, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = fam[dom]["gflop"] / fam[dom]["ms"], PEAK_TFLOPS[dtype], "TFLOP/s"
+    roof = {"bound": "hbm" if hbm else "mfma", "kernel": f"{dtype}/{dom}",
             "kernels": pass_kernels(dtype, dom),
             "launches_per_step": n,
             "flops_per_launch": fam[dom]["gflop"] * 1e9 / n,
             "avg_launch_us": fam[dom]["ms"] * 1e3 / n,
-            "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
+            "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": (recorded_traffic(f"{dtype}/{dom}")
                         if dtype == "f32" and act == "none" and len(layers) == 32 else None),
             "alg_bytes_per_launch": int(fam[dom]["alg_gb"] * 1e9 / n)}
@@ -803,7 +813,20 @@ def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=F
         json.dump(rows, fh, indent=1)
 
 
-WORKLOADS = {"unet_sweep": 5, "small": 1, "stem": 2, "mid": 3, "bottleneck": 4}
+WORKLOADS = {"unet_sweep": 5, "small": 1, "stem": 2, "mid": 3, "bottleneck": 4,
+             "image_stem": 6}
+
+
+def workload_layers(cfg):
+    """(main layers, bfloat16 layers timed beside them or None) of a workload:
+    the configured layer groups, or (6) the UNet's first convolution on the
+    3-channel image in both dtypes."""
+    import workloads as wl
+    if cfg == 6:
+        return [wl.IMAGE_STEM["f32"]], [wl.IMAGE_STEM["bf16"]]
+    layers = [l for l in wl.CONFIGS[cfg] if l.dtype == "f32"] or list(wl.CONFIGS[cfg])
+    extra = [l for l in wl.CONFIGS[5] if l.dtype == "bf16"] if cfg == 5 else None
+    return layers, extra
 
 
 def main():
@@ -879,9 +902,8 @@ def main():
         import workloads as wl
         cfg = WORKLOADS[args.workload]
         by_dt = {}
-        for l in wl.CONFIGS[cfg]:
-            if cfg == 5 and args.no_bf16 and l.dtype == "bf16":
-                continue
+        main_l, extra_l = workload_layers(cfg)
+        for l in main_l + ([] if args.no_bf16 else (extra_l or [])):
             by_dt.setdefault(l.dtype, []).append(l)
         print(profile_report(args.profile_report[0], args.profile_report[1:], by_dt,
                              f"conv3x3 {args.workload}: kernel times and counters",
@@ -895,7 +917,7 @@ def main():
     import torch
     import workloads as wl
     cfg = WORKLOADS[args.workload]
-    layers = [l for l in wl.CONFIGS[cfg] if l.dtype == "f32"] or list(wl.CONFIGS[cfg])
+    layers, extra_layers = workload_layers(cfg)
     dtype = layers[0].dtype
     t_gen = time.perf_counter()
     inputs = {l.name: wl.make_inputs(l) for l in layers}
@@ -917,7 +939,8 @@ def main():
              1: "single_conv3x3_2x64to64_32x32_fwd_bias+bwd_data+bwd_weight",
              2: "unet_stem_conv3x3_32x64to64_64x64_fwd_bias+bwd_data+bwd_weight",
              3: "unet_mid_resblock_convs_32x(128to256,256to256)_32x32_fwd_bias+bwd_data+bwd_weight",
-             4: "unet_bottleneck_convs_64x512to512_(16x16,8x8)_fwd_bias+bwd_data+bwd_weight"}
+             4: "unet_bottleneck_convs_64x512to512_(16x16,8x8)_fwd_bias+bwd_data+bwd_weight",
+             6: "unet_image_stem_conv3x3_32x3to128_64x64_fwd_bias+bwd_data+bwd_weight"}
     wname = names[cfg] if args.act == "none" else names[cfg].replace(
         "fwd_bias", f"fwd_bias_{args.act}") + f" (fused {args.act})"
     config = {"workload": wname, "layers": len(layers), "N": layers[0].N,
@@ -926,7 +949,9 @@ def main():
               "timing": "HIP events on the kernels' stream; inputs resident in HBM; "
                         + ("512 MiB overwritten before every pass (cold caches)"
                            if args.cold else "passes back to back in sweep order")}
-    if cfg == 5:
+    if cfg == 6:
+        config["shapes"] = [list(l.shape) for l in layers]
+    elif cfg == 5:
         config.update({"channels": "128x[1,2,3,4]", "resolutions": [64, 32, 16, 8],
                        "convs": "2 per resblock, 2 resblocks per level, down and up paths; "
                                 "up-path C_in includes the skip concatenation"})
@@ -940,8 +965,8 @@ def main():
         "config": config, "roofline": summ["roofline"], "passes": summ["passes"],
     }
     detail = {dtype: rows}
-    if cfg == 5 and not args.no_bf16:
-        blayers = [l for l in wl.CONFIGS[5] if l.dtype == "bf16"]
+    if extra_layers and not args.no_bf16:
+        blayers = extra_layers
         by_idx = {l.index: l for l in layers}
         binputs = {}
         for l in blayers:
@@ -959,7 +984,7 @@ def main():
         print(f"bf16: {bsum['ms_per_step']} ms/step, {bsum['value']} TFLOP/s",
               file=sys.stderr, flush=True)
         bsum["dtype"] = "bf16 inputs, fp32 accumulation and outputs"
-        result["bf16_sweep"] = bsum
+        result["bf16_sweep" if cfg == 5 else "bf16"] = bsum
         detail["bf16"] = brows
         del binputs
     if args.detail:

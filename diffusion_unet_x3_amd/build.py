@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "planner.cpp", "noalloc.hip", "conv_fwd_f32.hip", "conv_fwd_bf16.hip",
-           "conv_wgrad_f32.hip", "conv_wgrad_bf16.hip"]
+           "conv_wgrad_f32.hip", "conv_wgrad_bf16.hip", "conv_stem.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-I", os.path.join(HERE, "..", "include")]

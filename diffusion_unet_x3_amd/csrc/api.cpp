@@ -280,6 +280,8 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   // stride 2: the pixel chunks tile g's H/2 x W/2 grid
   Problem pb{kBwdWeight, kdt(dtype), N, C, K, geom == 2 ? H / 2 : H, geom == 2 ? W / 2 : W, x.c0};
   pb.stride2 = geom == 2;
+  // (at most four input channels, no fusion: the packed-pair kernel)
+  pb.stem = C <= 4 && x.c0 == C && geom == 0 && act == CONV3X3_ACT_NONE && !pr.on();
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!workspace || workspace_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -299,7 +301,16 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   a.s2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
-  if (dtype == CONV3X3_F32) {
+  if (pl.threads == 256) {
+    // packed (channel, tap) pairs; 128-bit g loads need whole 16-byte
+    // pixel runs
+    const bool f32 = dtype == CONV3X3_F32;
+    const bool vs = W % (f32 ? 4 : 8) == 0 && aligned16(g);
+    ok = f32 ? launch_wgrad_stem_f32(pl, vs, (const float*)x.p0, (const float*)g, dw, db,
+                                     (float*)workspace, N, C, K, H, W, s)
+             : launch_wgrad_stem_bf16(pl, vs, (const uint16_t*)x.p0, (const uint16_t*)g, dw, db,
+                                      (float*)workspace, N, C, K, H, W, s);
+  } else if (dtype == CONV3X3_F32) {
     // (stride 2: g's rows, W/2 floats, must hold whole float4 items too)
     const bool vec = W % (geom == 2 ? 8 : 4) == 0 && parts_aligned(x) && aligned16(g) &&
                      (!a.zsrc || aligned16(a.zsrc)) && buffer_sized(2L * N * C * hw) &&
@@ -348,7 +359,11 @@ int plan_impl(int pass, int N, int C, int K, int H, int W, int dtype, int C0,
   rc = check_dtype(dtype);
   if (rc) return rc;
   Plan pl;
-  if (!plan(Problem{pass, kdt(dtype), N, C, K, H, W, C0}, &pl)) return CONV3X3_ERR_BAD_PASS;
+  Problem pb{pass, kdt(dtype), N, C, K, H, W, C0};
+  // the plan of the plain call (a fused backward-weight of a few-channel
+  // input runs the general kernel; its workspace size is the same)
+  pb.stem = pass == CONV3X3_PASS_BWD_WEIGHT && C <= 4 && (C0 < 0 || C0 == C);
+  if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_PASS;
   rc = fill_plan(pl, pass, out);
   out->dtype = dtype;
   return rc;

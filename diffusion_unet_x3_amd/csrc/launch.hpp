@@ -52,6 +52,17 @@ bool launch_wgrad_f32(const Plan& pl, bool vec, Split<const float> x, const floa
 void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C, int K,
                          hipStream_t stream);
 
+// Backward-weight (+ optional db) of a convolution with at most four input
+// channels (one tensor; plans with 256 threads): the (channel, tap) pairs
+// are the MFMA's columns.  float32 or bfloat16 inputs (raw 16-bit
+// patterns); ws holds the per-slice partials when pl.split > 1.
+bool launch_wgrad_stem_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
+                           float* db, float* ws, int N, int C, int K, int H, int W,
+                           hipStream_t stream);
+bool launch_wgrad_stem_bf16(const Plan& pl, bool vec, const uint16_t* x, const uint16_t* g,
+                            float* dw, float* db, float* ws, int N, int C, int K, int H, int W,
+                            hipStream_t stream);
+
 // Same, bfloat16 inputs.
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
                        float* dw,

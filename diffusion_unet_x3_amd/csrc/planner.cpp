@@ -246,6 +246,43 @@ bool plan(const Problem& p, Plan* out) {
                      : wgrad_f32_lds_bytes(pl.imgs, pl.th, pl.tw))
         : wgrad_bf16_lds_bytes(pl.imgs, pl.th, pl.tw);
     pl.workspace_bytes = wgrad_workspace_bytes(pl, p.C, p.K);
+    if (p.C <= 4 && (p.C0 < 0 || p.C0 >= p.C) && !p.stride2) {
+      // At most four input channels: the packed-pair kernel -- 128 k rows
+      // and all 9C (channel, tap) pairs per 256-thread workgroup, 64-pixel
+      // chunks tw x th (the narrowest power-of-two width holding a row, 8
+      // to 64), about two workgroups per compute unit.  Its workspace also
+      // bounds the other backward-weight variants' of the shape (they share
+      // the size query), so the larger of the two is reported.
+      Plan st = pl;
+      int tw = 8;
+      while (tw < 64 && tw < p.W) tw *= 2;
+      st.tw = tw;
+      st.th = 64 / tw;
+      st.imgs = 1;
+      st.tile_co = 128;
+      st.tile_ci = p.C;
+      st.chunk = 64;
+      st.tiles_w = ceil_div(p.W, st.tw);
+      st.tiles_h = ceil_div(p.H, st.th);
+      st.tiles_n = p.N;
+      st.nchunks = st.tiles_n * st.tiles_h * st.tiles_w;
+      const int tiles_k = ceil_div(p.K, 128);
+      int sp = 2 * kWgradTargetWGs / tiles_k;
+      if (sp > st.nchunks) sp = st.nchunks;
+      if (sp < 1) sp = 1;
+      st.chunks_per_split = ceil_div(st.nchunks, sp);
+      st.split = ceil_div(st.nchunks, st.chunks_per_split);
+      st.grid_x = st.split * tiles_k;
+      st.grid_y = 1;
+      st.grid_z = 1;
+      st.threads = 256;
+      st.lds_bytes = 2 * 4 * (128 * 68 + 4 * (st.th + 2) * (st.tw + 2));
+      st.workspace_bytes = wgrad_workspace_bytes(st, p.C, p.K);
+      const size_t ws = st.workspace_bytes > pl.workspace_bytes ? st.workspace_bytes
+                                                                : pl.workspace_bytes;
+      if (p.stem) pl = st;
+      pl.workspace_bytes = ws;
+    }
   } else {
     return false;
   }

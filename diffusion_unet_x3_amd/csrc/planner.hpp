@@ -66,6 +66,10 @@ struct Problem {
   // bfloat16 backward-data with a fused activation gradient: four-wave
   // tiles only (their staging threads hold the float32 z rows beside gy)
   bool four_waves = false;
+  // backward-weight with at most four input channels in one tensor and no
+  // fusion: the packed-pair kernel (256 threads, 128 k x all (c, tap)
+  // pairs per workgroup, 64-pixel chunks)
+  bool stem = false;
 };
 
 bool plan(const Problem& p, Plan* out);

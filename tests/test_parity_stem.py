@@ -1,9 +1,11 @@
 """GPU parity of the few-channel inputs (an RGB image stem, a 4-channel
 latent) against the oracle, through the C ABI.  With 3 or 4 input channels
 the float32 forward packs the (channel, tap) pairs of the reduction two per
-MFMA step; these cases cover it (whole and ragged output tiles, widths that
-are and are not a multiple of 4, integer-exact inputs) together with the
-plain backward passes of the same layers."""
+MFMA step, and backward-weight (both dtypes) runs the packed-pair kernel
+whose MFMA columns are the 9C (channel, tap) pairs; these cases cover both
+(whole and ragged output tiles and pixel chunks, widths that are and are
+not a multiple of 4 or 8, one to four channels, k tiles of 128 with ragged
+ends, integer-exact inputs) together with the backward-data pass."""
 import pytest
 
 import workloads as wl
@@ -12,7 +14,8 @@ from parity_util import check, oracle_full, oracle_sampled, pairs, run_gpu
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(2, 3, 64, 32, 32), (2, 4, 128, 16, 16), (3, 3, 5, 7, 12), (2, 3, 17, 9, 8),
-          (2, 4, 130, 10, 72), (1, 3, 64, 13, 10), (4, 3, 128, 8, 8), (2, 3, 256, 16, 16)]
+          (2, 4, 130, 10, 72), (1, 3, 64, 13, 10), (4, 3, 128, 8, 8), (2, 3, 256, 16, 16),
+          (2, 1, 40, 10, 12), (2, 2, 33, 16, 16), (3, 4, 64, 31, 33), (1, 3, 128, 64, 64)]
 
 
 @pytest.mark.parametrize("exact", [False, True], ids=["random", "integer"])
