@@ -301,7 +301,7 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
   a.s2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
-  if (pl.threads == 256) {
+  if (pl.stem) {
     // packed (channel, tap) pairs; 128-bit g loads need whole 16-byte
     // pixel runs
     const bool f32 = dtype == CONV3X3_F32;

@@ -140,4 +140,33 @@ CONV3X3_HD constexpr int wgrad_bf16_lds_bytes(int imgs, int th, int tw) {
   return 2 * 2 * 64 * (wgrad_bf16_gstride(imgs, th, tw) + wgrad_bf16_plane(imgs, th, tw));
 }
 
+// ---- backward-weight, at most four input channels (packed pairs) ----
+// Eight waves per workgroup (two per 32-row k block, taking alternate
+// chunks), each with private g rows:
+//   g rows : [8 waves][32 k][68] floats (64 pixels; rows 68 floats apart put
+//            the 8 lanes of a 128-bit read on all 32 banks).
+//   x      : one group of kStemGroup chunks, shared (wave w stages chunk w
+//            of the group): [group chunk][cp][XP] floats, a plane = th + 2
+//            rows of XR floats, XR = tw + 2 padded to 3 (mod 32) and XP
+//            padded to 9 (mod 32), so that (channel, tap) column
+//            e = 9 c + 3 r + s reads bank e + const; then a plane of zeros
+//            (which also takes the staging items past the planes), a bank
+//            shift and a plane of ones.
+// Split-K slot: [K][32 NB] floats per slice, NB = 32-column MFMA blocks of
+// the 9C pairs and the bias column.
+constexpr int kStemWaves = 8;
+constexpr int kStemGroup = 8;  // chunks per staged x group
+CONV3X3_HD constexpr int stem_xr(int tw) { return tw + 2 + ((3 - (tw + 2)) % 32 + 32) % 32; }
+CONV3X3_HD constexpr int stem_xp(int th, int tw) {
+  return (th + 2) * stem_xr(tw) + ((9 - (th + 2) * stem_xr(tw)) % 32 + 32) % 32;
+}
+CONV3X3_HD constexpr int stem_x_items(int th, int tw, int cp) {  // per lane (a chunk per wave)
+  return (cp * stem_xp(th, tw) + 63) / 64;
+}
+CONV3X3_HD constexpr int stem_lds_bytes(int th, int tw, int cp) {
+  return 4 * (kStemWaves * 32 * 68 + kStemGroup * cp * stem_xp(th, tw) + stem_xp(th, tw) + 32 +
+              stem_xp(th, tw));
+}
+CONV3X3_HD constexpr int stem_slot_columns(int C) { return 32 * ((9 * C + 1 + 31) / 32); }
+
 }  // namespace conv3x3

@@ -267,7 +267,7 @@ bool plan(const Problem& p, Plan* out) {
       st.tiles_n = p.N;
       st.nchunks = st.tiles_n * st.tiles_h * st.tiles_w;
       const int tiles_k = ceil_div(p.K, 128);
-      int sp = 2 * kWgradTargetWGs / tiles_k;
+      int sp = kWgradTargetWGs / tiles_k;
       if (sp > st.nchunks) sp = st.nchunks;
       if (sp < 1) sp = 1;
       st.chunks_per_split = ceil_div(st.nchunks, sp);
@@ -275,9 +275,13 @@ bool plan(const Problem& p, Plan* out) {
       st.grid_x = st.split * tiles_k;
       st.grid_y = 1;
       st.grid_z = 1;
-      st.threads = 256;
-      st.lds_bytes = 2 * 4 * (128 * 68 + 4 * (st.th + 2) * (st.tw + 2));
-      st.workspace_bytes = wgrad_workspace_bytes(st, p.C, p.K);
+      st.threads = 64 * kStemWaves;
+      st.stem = 1;
+      st.lds_bytes = stem_lds_bytes(st.th, st.tw, p.C <= 3 ? 3 : 4);
+      // slots [split][K][32 NB] (the 9C pairs and the bias column)
+      st.workspace_bytes = st.split > 1 ? (size_t)st.split * p.K * stem_slot_columns(p.C) *
+                                              sizeof(float)
+                                        : 0;
       const size_t ws = st.workspace_bytes > pl.workspace_bytes ? st.workspace_bytes
                                                                 : pl.workspace_bytes;
       if (p.stem) pl = st;

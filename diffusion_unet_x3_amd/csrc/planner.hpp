@@ -38,6 +38,7 @@ struct Plan {
   int chunks_per_split = 0;
   int nchunks = 0;
   int vec = 0;            // 1: 128-bit global paths allowed (decided at launch; 0 here)
+  int stem = 0;           // bwd_weight: the packed-pair kernel (at most four input channels)
   size_t workspace_bytes = 0;
 };
 
@@ -67,7 +68,7 @@ struct Problem {
   // tiles only (their staging threads hold the float32 z rows beside gy)
   bool four_waves = false;
   // backward-weight with at most four input channels in one tensor and no
-  // fusion: the packed-pair kernel (256 threads, 128 k x all (c, tap)
+  // fusion: the packed-pair kernel (512 threads, 128 k x all (c, tap)
   // pairs per workgroup, 64-pixel chunks)
   bool stem = false;
 };

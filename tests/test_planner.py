@@ -60,16 +60,19 @@ def test_weight_gradient_plans(shape, dtype):
     assert (S - 1) * per < chunks <= S * per  # no empty slice
     ws = lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, dtype)
     if C <= 4:
-        # the packed-pair kernel: 128 k rows x all 9C pairs per 256-thread
-        # workgroup, 64-pixel chunks, up to two workgroups per compute unit;
-        # the reported workspace also covers the general kernel's
-        assert p["threads"] == 256 and p["tile_m"] == 128 and p["tile_n"] == C
+        # the packed-pair kernel: 128 k rows x all 9C pairs per 512-thread
+        # workgroup, 64-pixel chunks, a workgroup per compute unit; slots of
+        # K rows x 32 (C <= 3) or 64 columns; the reported workspace also
+        # covers the general kernel's
+        assert p["threads"] == 512 and p["tile_m"] == 128 and p["tile_n"] == C
         assert p["tile_imgs"] == 1 and p["tile_h"] * p["tile_w"] == 64
         assert p["tile_w"] >= min(W, 64) and p["tile_w"] in (8, 16, 32, 64)
+        assert 0 < p["lds_bytes"] <= LDS_PER_CU
         tiles = math.ceil(K / 128)
-        assert p["grid_x"] == S * tiles and S * tiles <= 512 or S == 1
+        assert p["grid_x"] == S * tiles and S * tiles <= 256 or S == 1
         assert ws == p["workspace_bytes"]
-        assert ws >= (0 if S == 1 else S * (K * C * 9 + K) * 4)
+        cols = 32 if C <= 3 else 64
+        assert ws >= (0 if S == 1 else S * K * cols * 4)
         return
     tiles = math.ceil(C / p["tile_n"]) * math.ceil(K / p["tile_m"])
     # 1-D grid: S x tiles workgroups padded to whole rounds of the 8 XCDs
