@@ -50,5 +50,41 @@ def build(verbose=True):
     return LIB
 
 
+# Host-code sanitizer build, for the CPU tests only: the host parts of these
+# sources (argument checks, planning, the entry points) are compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer, device code as usual
+# (-Xarch_host keeps the sanitizers off the GPU code), every other object is
+# the regular build's.  The library then needs the sanitizer runtime
+# preloaded into the process.
+SANITIZED = ["api.cpp", "planner.cpp", "noalloc.hip"]
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(out_lib):
+    """Link a host-sanitized copy of the library at out_lib (the regular
+    objects must exist: run build() first)."""
+    objs = []
+    for src in SOURCES:
+        stem = os.path.splitext(src)[0]
+        if src in SANITIZED:
+            o = os.path.join(OBJ, "sanitized_" + stem + ".o")
+            cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else []) + SANITIZE + \
+                  ["-c", os.path.join(CSRC, src), "-o", o]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        else:
+            o = os.path.join(OBJ, stem + ".o")
+            if not os.path.exists(o):
+                raise RuntimeError(f"{o} is missing: run build() first")
+        objs.append(o)
+    subprocess.check_call([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", out_lib] + objs)
+    return out_lib
+
+
 if __name__ == "__main__":
-    print(build())
+    if len(sys.argv) == 3 and sys.argv[1] == "--sanitize":
+        print(build_sanitized(sys.argv[2]))
+    else:
+        print(build())

@@ -83,21 +83,73 @@ def _dw_indices(K, C, count, rng):
     return np.unique(np.array(idx, dtype=np.int64))
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def tile_strata(shape, plan, rng):
+    """Flat indices into an output [N, Co, H, W] (y of the forward, dx of
+    backward-data): one random element in every (pixel tile of the plan,
+    32-channel group) -- so every workgroup's tile and every wave's 32-row
+    block within it has a compared element.  (A split reduction adds every
+    slice into every element of its tile, so the slices are covered too.)"""
+    N, Co, H, W = shape
+    ti, th, tw = plan["tile_imgs"], plan["tile_h"], plan["tile_w"]
+    nb, hb, wb, cb = np.meshgrid(np.arange(_cdiv(N, ti)), np.arange(_cdiv(H, th)),
+                                 np.arange(_cdiv(W, tw)), np.arange(_cdiv(Co, 32)),
+                                 indexing="ij")
+    nb, hb, wb, cb = (a.ravel() for a in (nb, hb, wb, cb))
+
+    def pick(block, size, extent):
+        lo = block * size
+        return lo + (rng.random(lo.shape) * np.minimum(size, extent - lo)).astype(np.int64)
+
+    n, h, w, c = pick(nb, ti, N), pick(hb, th, H), pick(wb, tw, W), pick(cb, 32, Co)
+    return ((n * Co + c) * H + h) * W + w
+
+
+def dw_strata(K, C, rng):
+    """Flat indices into dw [K, C, 3, 3]: one random element in every
+    (32-k block, 32-c block, tap) -- every wave's accumulator block of every
+    backward-weight tile."""
+    kb, cb, t = np.meshgrid(np.arange(_cdiv(K, 32)), np.arange(_cdiv(C, 32)), np.arange(9),
+                            indexing="ij")
+    kb, cb, t = kb.ravel(), cb.ravel(), t.ravel()
+    k = kb * 32 + (rng.random(kb.shape) * np.minimum(32, K - kb * 32)).astype(np.int64)
+    c = cb * 32 + (rng.random(cb.shape) * np.minimum(32, C - cb * 32)).astype(np.int64)
+    return (k * C + c) * 9 + t
+
+
+def stratified_indices(N, C, K, H, W, dtype, count, rng):
+    """The compared elements of y, dx and dw: the borders, `count` random
+    elements, and the strata of the launch plans the library uses."""
+    import diffusion_unet_x3_amd as lib3
+    code = lib3.CONV3X3_BF16 if dtype == "bf16" else lib3.CONV3X3_F32
+    pf = lib3.conv3x3_plan(lib3.PASS_FWD, N, C, K, H, W, code)
+    pd = lib3.conv3x3_plan(lib3.PASS_BWD_DATA, N, C, K, H, W, code)
+    iy = np.unique(np.concatenate([_border_and_random((N, K, H, W), count, rng),
+                                   tile_strata((N, K, H, W), pf, rng)]))
+    idx = np.unique(np.concatenate([_border_and_random((N, C, H, W), count, rng),
+                                    tile_strata((N, C, H, W), pd, rng)]))
+    iw = np.unique(np.concatenate([_dw_indices(K, C, count // 4, rng), dw_strata(K, C, rng)]))
+    return iy, idx, iw
+
+
 def oracle_sampled(inp, gpu, seed=0, count=1500, with_bias=True):
-    """Compare gpu outputs with the oracle on sampled elements; returns
+    """Compare gpu outputs with the oracle on sampled elements (every tile of
+    the launch plans, the borders and random elements); returns
     {name: (got, ref)} for y, dx, dw, db."""
     rng = np.random.default_rng(seed)
     x, w, g = inp["x"], inp["w"], inp["g"]
     b = inp["b"] if with_bias else None
     N, C, H, W = x.shape
     K = w.shape[0]
+    dtype = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    iy, idx, iw = stratified_indices(N, C, K, H, W, dtype, count, rng)
     res = {}
-    i = _border_and_random((N, K, H, W), count, rng)
-    res["y"] = (gpu["y"].ravel()[i], oracle.conv3x3_fwd_at(x, w, b, i))
-    i = _border_and_random((N, C, H, W), count, rng)
-    res["dx"] = (gpu["dx"].ravel()[i], oracle.conv3x3_bwd_data_at(g, w, i))
-    i = _dw_indices(K, C, count // 4, rng)
-    res["dw"] = (gpu["dw"].ravel()[i], oracle.conv3x3_bwd_weight_at(x, g, i))
+    res["y"] = (gpu["y"].ravel()[iy], oracle.conv3x3_fwd_at(x, w, b, iy))
+    res["dx"] = (gpu["dx"].ravel()[idx], oracle.conv3x3_bwd_data_at(g, w, idx))
+    res["dw"] = (gpu["dw"].ravel()[iw], oracle.conv3x3_bwd_weight_at(x, g, iw))
     if gpu.get("db") is not None:
         i = np.arange(K) if K <= 512 else np.unique(rng.integers(0, K, 512))
         res["db"] = (gpu["db"][i], oracle.conv3x3_bias_grad_at(g, i))
