@@ -478,60 +478,62 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   }
 }
 
-// The same epilogue with 128-bit loads, for workspaces whose slots and db
-// rows are 16-byte aligned ((K * C) % 4 == 0, K % 4 == 0 when db is
-// wanted).  Each lane owns 4 consecutive elements; eight waves each add a
-// fixed contiguous eighth of the slices in slice order, and wave 0 adds the
-// eight partial sums in wave order.
-__global__ __launch_bounds__(512) void wgrad_reduce4_kernel(const float* __restrict__ ws,
+// The same epilogue with 128-bit loads and stores, for workspaces whose
+// slots and db rows are 16-byte aligned ((K * C) % 4 == 0, K % 4 == 0 when
+// db is wanted) and 16-byte aligned dw / db.  A workgroup of 9 waves owns 256
+// consecutive (k, c) pairs kc0 .. kc0 + 255: wave t adds tap t's slot rows
+// of them (4 pairs per lane, the slots in slice order), the 9 x 256 sums go
+// through LDS, and the workgroup writes dw[kc0 * 9 .. (kc0 + 256) * 9) --
+// one contiguous [k][c][tap] run -- with 128-bit stores.  Workgroups past the
+// dw part add the db rows (256 per workgroup, wave 0).  The order never
+// changes, so the result is bitwise reproducible.
+__global__ __launch_bounds__(576) void wgrad_reduce4_kernel(const float* __restrict__ ws,
                                                             float* __restrict__ dw,
                                                             float* __restrict__ db, int S,
                                                             int C, int K) {
-  __shared__ f32x4 part[8][64];
-  const long n_dw = (long)K * C * 9;
-  const long total = n_dw + (db != nullptr ? K : 0);
-  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const long e = ((long)blockIdx.x * 64 + lane) * 4;
-  const int per = (S + 7) / 8;
-  const int s0 = min(S, q * per), s1 = min(S, s0 + per);
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  if (e < total) {
-    const float* base;
-    long stride;
-    if (e < n_dw) {
-      base = ws + e;
-      stride = n_dw;
-    } else {
-      base = ws + (long)S * n_dw + (e - n_dw);
-      stride = K;
-    }
-    int i = s0;
-    for (; i + 8 <= s1; i += 8) {
+  __shared__ __attribute__((aligned(16))) float tr[9][256];
+  const long KC = (long)K * C;
+  const long n_dw = KC * 9;
+  const long nblk = (KC + 255) / 256;
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  auto slot_sum = [&](const float* base, long stride) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    // loads issued eight slots at a time; the adds stay in slot order
+    int i = 0;
+    for (; i + 8 <= S; i += 8) {
       f32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (long)(i + u) * stride);
 #pragma unroll
       for (int u = 0; u < 8; ++u) sum += v[u];
     }
-    for (; i < s1; ++i) sum += *reinterpret_cast<const f32x4*>(base + (long)i * stride);
+    for (; i < S; ++i) sum += *reinterpret_cast<const f32x4*>(base + (long)i * stride);
+    return sum;
+  };
+  if ((long)blockIdx.x >= nblk) {
+    // db rows [S][K] after the dw slots (the whole workgroup takes this branch)
+    const long k4 = ((long)blockIdx.x - nblk) * 256 + 4 * (long)threadIdx.x;
+    if (t == 0 && k4 < K)
+      *reinterpret_cast<f32x4*>(db + k4) = slot_sum(ws + (long)S * n_dw + k4, K);
+    return;
   }
-  part[q][lane] = sum;
+  const long kc0 = (long)blockIdx.x * 256;
+  const long kc = kc0 + 4 * lane;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  if (kc < KC) sum = slot_sum(ws + (long)t * KC + kc, n_dw);  // (KC % 4 == 0: kc + 3 < KC)
+  *reinterpret_cast<f32x4*>(&tr[t][4 * lane]) = sum;
   __syncthreads();
-  if (q == 0 && e < total) {
-    f32x4 v = part[0][lane];
+  const long nvalid = (KC - kc0 < 256 ? KC - kc0 : 256) * 9;
+  const int o = 4 * threadIdx.x;  // 576 threads x 4 = 2304 = 256 x 9 outputs
+  float v[4];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) v += part[j][lane];
+  for (int j = 0; j < 4; ++j) v[j] = tr[(o + j) % 9][(o + j) / 9];
+  if (o + 3 < nvalid) {
+    *reinterpret_cast<f32x4*>(dw + kc0 * 9 + o) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long ej = e + j;
-      if (ej < n_dw) {
-        const long t = ej / ((long)K * C);
-        const long kc = ej % ((long)K * C);
-        dw[kc * 9 + t] = v[j];
-      } else {
-        db[ej - n_dw] = v[j];
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      if (o + j < nvalid) dw[kc0 * 9 + o + j] = v[j];
   }
 }
 
@@ -597,9 +599,12 @@ void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C
                          hipStream_t stream) {
   const long total = (long)K * C * 9 + (db ? K : 0);
   const bool vec4 = ((long)K * C) % 4 == 0 && (db == nullptr || K % 4 == 0) &&
-                    (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
+                    (reinterpret_cast<uintptr_t>(ws) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(dw) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(db) & 15) == 0;
   if (vec4) {
-    dim3 grid((unsigned)((total + 255) / 256)), block(512);
+    const long KC = (long)K * C;
+    dim3 grid((unsigned)((KC + 255) / 256 + (db ? (K + 255) / 256 : 0))), block(576);
     hipLaunchKernelGGL(wgrad_reduce4_kernel, grid, block, 0, stream, ws, dw, db, split, C, K);
   } else {
     dim3 grid((unsigned)((total + 63) / 64)), block(256);
