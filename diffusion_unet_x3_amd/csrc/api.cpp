@@ -140,6 +140,10 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   // (bf16 prologue: four-wave tiles, whose staging threads hold scale and
   // shift beside the x rows)
   pb.four_waves = dtype != CONV3X3_F32 && pr.on();
+  // at most four input channels, bfloat16 inputs, float32 outputs, no
+  // fusion: the packed-pair forward
+  pb.stem = C <= 4 && x.c0 == C && !geom && !pr.on() && dtype == CONV3X3_BF16 &&
+            act == CONV3X3_ACT_NONE && !z;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
@@ -156,7 +160,10 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   a.s2 = geom == 2;
   const long hw = (long)H * W;
   bool ok;
-  if (dtype == CONV3X3_F32) {
+  if (pl.stem) {
+    ok = launch_fwd_stem_bf16(pl, (const uint16_t*)x.p0, (const uint16_t*)w, bias, y, N, C, K,
+                              H, W, s);
+  } else if (dtype == CONV3X3_F32) {
     // (3 input channels in one tensor: the packed-tap forward, vector x
     // loads and scalar weight loads)
     const bool pack3 = C == 3 && x.c0 == C && !pr.on();
@@ -360,9 +367,11 @@ int plan_impl(int pass, int N, int C, int K, int H, int W, int dtype, int C0,
   if (rc) return rc;
   Plan pl;
   Problem pb{pass, kdt(dtype), N, C, K, H, W, C0};
-  // the plan of the plain call (a fused backward-weight of a few-channel
-  // input runs the general kernel; its workspace size is the same)
-  pb.stem = pass == CONV3X3_PASS_BWD_WEIGHT && C <= 4 && (C0 < 0 || C0 == C);
+  // the plan of the plain call (a fused pass with a few-channel input runs
+  // the general kernels; a backward-weight's workspace size is the same)
+  pb.stem = (pass == CONV3X3_PASS_BWD_WEIGHT ||
+             (pass == CONV3X3_PASS_FWD && dtype == CONV3X3_BF16)) &&
+            C <= 4 && (C0 < 0 || C0 == C);
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_PASS;
   rc = fill_plan(pl, pass, out);
   out->dtype = dtype;

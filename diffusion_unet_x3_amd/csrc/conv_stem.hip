@@ -469,6 +469,212 @@ static bool launch_stem(const Plan& pl, bool vec, const T* x, const T* g, float*
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Forward (+ bias) of a convolution whose input has at most four channels,
+// bfloat16 inputs, float32 output: y[n, k, p] = b[k] + sum over e = (c, tap)
+// of w[k, e] x[n, c, p + offset(e)].  A GEMM with rows k, columns pixels and
+// a reduction of only 9C (channel, tap) pairs, so the pass is bound by its
+// output (K float32 per pixel).  MFMA 32x32x16 (products exact in float32):
+// step s takes the pairs e = 16 s + 8 (l / 32) + 0..7, pairs past 9C are
+// zero (two steps for C = 3); the bias (float32, from LDS) is added to the
+// sums as they are stored.  Each wave keeps its weights in registers for the
+// whole launch, and the workgroups loop over 128-pixel tiles (persistent),
+// so that a wave's stores of one tile drain while it computes the next.
+// Workgroup: 4 waves, kStemFwdCo = 64 output channels (2 blocks of 32,
+// masked past K) x one tile; wave w computes the tile's pixels 32 w .. 32 w +
+// 31 for all 64 channels.  The tile's x (with its halo, zero outside the
+// image, widened to float32) is staged by the workgroup into one of two LDS
+// buffers; one barrier per tile.  Stores: the lane's offset is one
+// register, each channel's plane offset the store's scalar offset.  (A
+// fused activation or z output takes the general kernel.  The float32
+// forward keeps the packed-tap path of the general kernel, which measured
+// faster than this structure with 32x32x2 MFMAs.)
+template <int TW, int C>
+__global__ __launch_bounds__(256) void fwd_stem_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, float* __restrict__ y, int N, int K, int H, int W,
+    int tiles_w, int tiles_h, int ntiles, uint32_t x_bytes, uint32_t y_bytes) {
+  constexpr int TH = kStemFwdPix / TW;
+  constexpr int XR = stem_xr(TW);
+  constexpr int XP = stem_xp(TH, TW);
+  constexpr int XI = C * XP;                     // x floats per tile (with padding)
+  constexpr int XN = (XI + 255) / 256;           // x items per thread
+  constexpr int XF = stem_fwd_x_floats(TH, TW, C);
+  static_assert(XN * 256 - XI <= XP, "items past the planes land in the plane of zeros");
+  constexpr int NS = (9 * C + 15) / 16;           // MFMA steps of 16 pairs
+  constexpr int NB = kStemFwdCo / 32;            // channel blocks per wave
+  __shared__ __attribute__((aligned(16))) float xs[2][XF];
+  __shared__ float bias_s[kStemFwdCo];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int k0 = blockIdx.y * kStemFwdCo;
+  const long HW = (long)H * W;
+
+  // the plane of zeros (pairs past 9C read it), in both buffers
+  for (int i = tid; i < XP; i += 256) {
+    xs[0][XI + i] = 0.f;
+    xs[1][XI + i] = 0.f;
+  }
+  if (tid < kStemFwdCo) bias_s[tid] = bias != nullptr && k0 + tid < K ? bias[k0 + tid] : 0.f;
+
+  // This lane's pixel of the tile: p = 32 wave + l32 -> (row, col), and
+  // its LDS base in a staged plane.
+  const int p = 32 * wave + l32;
+  const int prow = p / TW, pcol = p % TW;
+  const int pbase = prow * XR + pcol;
+  // LDS offset of pair e at this lane's pixel (a constant of e; the zero
+  // plane is read at its first element by every lane)
+  auto e_off = [&](int e) -> int {
+    if (e < 9 * C) return pbase + (e / 9) * XP + ((e % 9) / 3) * XR + (e % 9) % 3;
+    return XI;
+  };
+
+  // Weights (A) for the NB channel blocks, held for the whole launch: lane
+  // (l32, hi) packs w[k, e], e = 16 s + 8 hi + 0..7, two per 32-bit word.
+  uint32_t aw[NB][4 * NS];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int k = k0 + 32 * b + l32;
+    auto wval = [&](int e) -> uint32_t {
+      return k < K && e < 9 * C ? (uint32_t)w[(long)k * 9 * C + e] : 0u;
+    };
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e = 16 * s + 8 * hi + 2 * m;
+        aw[b][4 * s + m] = wval(e) | wval(e + 1) << 16;
+      }
+  }
+
+  const __amdgpu_buffer_rsrc_t xv = buffer_view(x, x_bytes);
+  const __amdgpu_buffer_rsrc_t yv = buffer_view(y, y_bytes);
+  uint16_t xraw[XN];
+  auto load_x = [&](int tile) __attribute__((always_inline)) {
+    const bool live = tile < ntiles;
+    const BlockOrigin o = block_origin<TW, TH, 1>(live ? tile : 0, tiles_w, tiles_h);
+#pragma unroll
+    for (int j = 0; j < XN; ++j) {
+      const int it = tid + 256 * j;
+      const int c = it / XP, rc = it % XP;
+      const int hr = rc / XR, wr = rc % XR;  // (padding: hr >= th + 2 or wr >= tw + 2)
+      const int h = o.h0 + hr - 1, ww = o.w0 + wr - 1;
+      // (& rather than &&: a select, not a branch)
+      const bool ok = live & (it < XI) & (o.n0 < N) & (hr < TH + 2) & (wr < TW + 2) & (h >= 0) &
+                      (h < H) & (ww >= 0) & (ww < W);
+      const uint32_t off = ok ? (uint32_t)((o.n0 * C + c) * HW + h * W + ww) * 2u : kOutside;
+      xraw[j] = (uint16_t)buffer_load2(xv, off);
+    }
+  };
+  auto store_x = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < XN; ++j) xs[buf][tid + 256 * j] = widen(xraw[j]);
+  };
+
+  const uint32_t plane4 = (uint32_t)(HW * 4);
+  // The tile loop, for a whole channel tile or the partial last one (the
+  // choice made once, outside the loop).  Iteration i: barrier, tile i's
+  // MFMAs from buffer i & 1, tile i + 1's x loads, tile i's stores, then
+  // tile i + 1's x into the other buffer (last read in iteration i - 1,
+  // before this iteration's barrier).  Every wait for memory sits in
+  // straight-line code after the stores, so the compiler counts them
+  // exactly and waits for the x loads only -- the stores drain while the
+  // next tile computes.
+  auto tiles = [&](auto whole_c) __attribute__((always_inline)) {
+    constexpr bool WHOLE = decltype(whole_c)::value;
+    int tile = blockIdx.x;
+    load_x(tile);
+    store_x(0);
+    for (int i = 0; tile < ntiles; ++i, tile += gridDim.x) {
+      const int buf = i & 1;
+      __syncthreads();
+      const float* xb = xs[buf];
+      f32x16 acc[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        u32x4 bw;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int e0 = 16 * s + 2 * m, e1 = e0 + 8;  // (lanes 0-31 / 32-63)
+          const float v0 = xb[hi ? e_off(e1) : e_off(e0)];
+          const float v1 = xb[hi ? e_off(e1 + 1) : e_off(e0 + 1)];
+          // (staged values are bfloat16 widened: the high halves are exact)
+          bw[m] = (__builtin_bit_cast(uint32_t, v0) >> 16) |
+                  (__builtin_bit_cast(uint32_t, v1) & 0xffff0000u);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const u32x4 a4 = {aw[b][4 * s], aw[b][4 * s + 1], aw[b][4 * s + 2], aw[b][4 * s + 3]};
+          acc[b] = mfma_32x32x16_bf16(a4, bw, acc[b]);
+        }
+      }
+      load_x(tile + gridDim.x);  // (past the last tile: zeros, no memory access)
+      // y of this lane's pixel for its channels: lane offset of channel
+      // k0 + 4 hi, plus channel 32 b + 8 (v / 4) + v % 4's plane as the
+      // scalar offset; out-of-range elements store nothing (the range check)
+      const BlockOrigin o = block_origin<TW, TH, 1>(tile, tiles_w, tiles_h);
+      const int h = o.h0 + prow, ww = o.w0 + pcol;
+      const bool pix_ok = (o.n0 < N) & (h < H) & (ww < W);
+      const uint32_t lane_off =
+          (uint32_t)((((long)o.n0 * K + k0 + 4 * hi) * H + h) * W + ww) * 4u;
+      const uint32_t pix_off = pix_ok ? lane_off : kOutside;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kr = 32 * b + 8 * (v / 4) + v % 4;  // channel row less 4 hi
+          const uint32_t voff = WHOLE || k0 + kr + 4 * hi < K ? pix_off : kOutside;
+          buffer_store4(yv, voff, (uint32_t)kr * plane4, acc[b][v] + bias_s[kr + 4 * hi]);
+        }
+      store_x(buf ^ 1);
+    }
+  };
+  if (k0 + kStemFwdCo <= K)
+    tiles(std::true_type{});
+  else
+    tiles(std::false_type{});
+}
+
+template <int TW>
+static void launch_fwd_stem_geom(const Plan& pl, const uint16_t* x, const uint16_t* w,
+                                 const float* bias, float* y, int N, int C, int K, int H, int W,
+                                 hipStream_t stream) {
+  dim3 grid(pl.grid_x, pl.grid_y, 1), block(256, 1, 1);
+  const long hw = (long)H * W;
+  const uint32_t xb = (uint32_t)(N * C * hw * 2L);
+  const uint32_t yb = (uint32_t)(N * K * hw * 4L);
+#define CONV3X3_F(C_)                                                                          \
+  hipLaunchKernelGGL((fwd_stem_bf16_kernel<TW, C_>), grid, block, 0, stream, x, w, bias, y, N, K, \
+                     H, W, pl.tiles_w, pl.tiles_h, pl.nchunks, xb, yb)
+  switch (C) {
+    case 1: CONV3X3_F(1); break;
+    case 2: CONV3X3_F(2); break;
+    case 3: CONV3X3_F(3); break;
+    default: CONV3X3_F(4); break;
+  }
+#undef CONV3X3_F
+}
+
+bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
+                          const float* bias, float* y, int N, int C, int K, int H, int W,
+                          hipStream_t stream) {
+  if (C > 4 || !pl.stem || pl.threads != 256 || pl.tw * pl.th != kStemFwdPix) return false;
+  switch (pl.tw) {
+    case 64: launch_fwd_stem_geom<64>(pl, x, w, bias, y, N, C, K, H, W, stream); break;
+    case 32: launch_fwd_stem_geom<32>(pl, x, w, bias, y, N, C, K, H, W, stream); break;
+    case 16: launch_fwd_stem_geom<16>(pl, x, w, bias, y, N, C, K, H, W, stream); break;
+    case 8: launch_fwd_stem_geom<8>(pl, x, w, bias, y, N, C, K, H, W, stream); break;
+    default: return false;
+  }
+  return true;
+}
+
 bool launch_wgrad_stem_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
                            float* db, float* ws, int N, int C, int K, int H, int W,
                            hipStream_t stream) {

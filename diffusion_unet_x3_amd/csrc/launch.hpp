@@ -63,6 +63,15 @@ bool launch_wgrad_stem_bf16(const Plan& pl, bool vec, const uint16_t* x, const u
                             float* dw, float* db, float* ws, int N, int C, int K, int H, int W,
                             hipStream_t stream);
 
+// Forward (+ bias; float32 outputs, no fused activation) of a convolution
+// with at most four input channels, bfloat16 inputs (raw 16-bit patterns;
+// one tensor; plans with pl.stem): the (channel, tap) pairs are the MFMA's
+// reduction, the weights stay in registers, the workgroups loop over
+// 128-pixel tiles.
+bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
+                          const float* bias, float* y, int N, int C, int K, int H, int W,
+                          hipStream_t stream);
+
 // Same, bfloat16 inputs.
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
                        float* dw,

@@ -169,4 +169,17 @@ CONV3X3_HD constexpr int stem_lds_bytes(int th, int tw, int cp) {
 }
 CONV3X3_HD constexpr int stem_slot_columns(int C) { return 32 * ((9 * C + 1 + 31) / 32); }
 
+// ---- forward, at most four input channels, bfloat16 (packed pairs) ----
+// 128-pixel tiles (tw x th); two buffers of the x tile: [c][XP] floats (the
+// planes as above, th + 2 rows of XR, bfloat16 widened), then a plane of
+// zeros.
+constexpr int kStemFwdPix = 128;
+constexpr int kStemFwdCo = 64;  // output channels per workgroup
+CONV3X3_HD constexpr int stem_fwd_x_floats(int th, int tw, int c) {
+  return (c + 1) * stem_xp(th, tw);
+}
+CONV3X3_HD constexpr int stem_fwd_lds_bytes(int th, int tw, int cp) {
+  return 2 * 4 * stem_fwd_x_floats(th, tw, cp);
+}
+
 }  // namespace conv3x3

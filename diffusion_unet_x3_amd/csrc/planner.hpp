@@ -38,7 +38,7 @@ struct Plan {
   int chunks_per_split = 0;
   int nchunks = 0;
   int vec = 0;            // 1: 128-bit global paths allowed (decided at launch; 0 here)
-  int stem = 0;           // bwd_weight: the packed-pair kernel (at most four input channels)
+  int stem = 0;           // fwd / bwd_weight: the packed-pair kernel (at most four input channels)
   size_t workspace_bytes = 0;
 };
 
@@ -67,9 +67,11 @@ struct Problem {
   // bfloat16 backward-data with a fused activation gradient: four-wave
   // tiles only (their staging threads hold the float32 z rows beside gy)
   bool four_waves = false;
-  // backward-weight with at most four input channels in one tensor and no
-  // fusion: the packed-pair kernel (512 threads, 128 k x all (c, tap)
-  // pairs per workgroup, 64-pixel chunks)
+  // at most four input channels in one tensor: the packed-pair kernels --
+  // backward-weight without fusion (512 threads, 128 k x all (c, tap) pairs
+  // per workgroup, 64-pixel chunks), bfloat16 forward without fusion and
+  // with float32 outputs (256 threads, 64 output channels x 128-pixel
+  // tiles, persistent)
   bool stem = false;
 };
 

@@ -1,11 +1,14 @@
 """GPU parity of the few-channel inputs (an RGB image stem, a 4-channel
 latent) against the oracle, through the C ABI.  With 3 or 4 input channels
 the float32 forward packs the (channel, tap) pairs of the reduction two per
-MFMA step, and backward-weight (both dtypes) runs the packed-pair kernel
-whose MFMA columns are the 9C (channel, tap) pairs; these cases cover both
-(whole and ragged output tiles and pixel chunks, widths that are and are
-not a multiple of 4 or 8, one to four channels, k tiles of 128 with ragged
-ends, integer-exact inputs) together with the backward-data pass."""
+MFMA step; with one to four, the bfloat16 forward runs the persistent
+packed-pair kernel (the pairs as the MFMA's reduction, 64-channel tiles,
+workgroups looping over 128-pixel tiles -- four tiles each on the full-size
+stem) and backward-weight (both dtypes) the packed-pair kernel whose MFMA
+columns are the 9C (channel, tap) pairs; these cases cover them (whole and
+ragged output tiles and pixel chunks, widths that are and are not a
+multiple of 4 or 8, one to four channels, channel tiles with ragged ends,
+integer-exact inputs) together with the backward-data pass."""
 import pytest
 
 import workloads as wl
