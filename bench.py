@@ -496,9 +496,10 @@ class Up2Run:
         self.dx = torch.empty((N, C, H, W), device=dev)
         self.dw = torch.empty((K, C, 3, 3), device=dev)
         self.db = torch.empty((K,), device=dev)
-        self.ws_d = torch.empty(max(lib3.conv3x3_up2_workspace_size(1, N, C, K, H, W), 1),
+        code = lib3.CONV3X3_BF16 if layer.dtype == "bf16" else lib3.CONV3X3_F32
+        self.ws_d = torch.empty(max(lib3.conv3x3_up2_workspace_size(1, N, C, K, H, W, code), 1),
                                 dtype=torch.uint8, device=dev)
-        self.ws_w = torch.empty(max(lib3.conv3x3_up2_workspace_size(2, N, C, K, H, W), 1),
+        self.ws_w = torch.empty(max(lib3.conv3x3_up2_workspace_size(2, N, C, K, H, W, code), 1),
                                 dtype=torch.uint8, device=dev)
 
     def passes(self):
@@ -527,7 +528,8 @@ class S2Run:
         self.dx = torch.empty((N, C, H, W), device=dev)
         self.dw = torch.empty((K, C, 3, 3), device=dev)
         self.db = torch.empty((K,), device=dev)
-        self.ws = torch.empty(max(lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W), 1),
+        code = lib3.CONV3X3_BF16 if layer.dtype == "bf16" else lib3.CONV3X3_F32
+        self.ws = torch.empty(max(lib3.conv3x3_bwd_weight_workspace_size(N, C, K, H, W, code), 1),
                               dtype=torch.uint8, device=dev)
 
     def passes(self):
@@ -759,20 +761,23 @@ def sweep_summary(dtype, layers, ms, fam, act="none"):
 
 
 def sweep(out_path, steps, warmup, match=None, act="none", cat=False, prologue=False,
-          out_bf16=False, split=True, up2=False, s2=False):
+          out_bf16=False, split=True, up2=False, s2=False, geo_bf16=False):
     import re
     import torch
     import workloads as wl
+    from dataclasses import replace
     rows = []
     if up2 or s2:
         for layer in (wl.UPSAMPLE if up2 else wl.DOWNSAMPLE):
+            if geo_bf16:
+                layer = replace(layer, dtype="bf16", name=layer.name.replace("_f32", "_bf16"))
             run = Up2Run(layer) if up2 else S2Run(layer)
             ms, per = time_layer(run, steps, warmup)
             N, C, K, H, W = layer.shape
             # useful FLOPs: at the output's resolution
             f = flops_per_pass(N, C, K, 2 * H, 2 * W) if up2 else \
                 flops_per_pass(N, C, K, H // 2, W // 2)
-            row = {"layer": layer.name, "dtype": "f32", "up2": up2, "s2": s2,
+            row = {"layer": layer.name, "dtype": layer.dtype, "up2": up2, "s2": s2,
                    "shape": [N, C, K, H, W], "ms_step": ms}
             for p, t in per.items():
                 row[p] = {"ms": t, "tflops": f / (t * 1e-3) / 1e12}
@@ -870,6 +875,9 @@ def main():
     ap.add_argument("--s2", action="store_true",
                     help="with --sweep: time the UNet's stride-2 downsample convolutions "
                          "(*_s2 entry points)")
+    ap.add_argument("--geo-bf16", action="store_true",
+                    help="with --up2 or --s2: bfloat16 inputs (the stride-1 bfloat16 kernels "
+                         "over the full-resolution grid)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) and exit")
@@ -1001,7 +1009,7 @@ def main():
         torch.cuda.empty_cache()
     if args.sweep:
         sweep(args.sweep, max(5, args.steps // 4), 3, args.sweep_match, args.act, args.cat,
-              args.gnsilu, args.out_bf16, not args.no_split, args.up2, args.s2)
+              args.gnsilu, args.out_bf16, not args.no_split, args.up2, args.s2, args.geo_bf16)
     if not args.no_cpu_baseline:
         if cfg == 5:
             result["cpu_baseline"] = cpu_baseline_sampled(layers, inputs)

@@ -88,6 +88,12 @@ bool parts_aligned(const Split<T>& s) {
 }
 
 // p (non-null) is the base pointer of one of the parts
+// Whether the byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 template <typename T>
 bool is_part(const Split<T>& s, const void* p) {
   return p && (p == (const void*)s.p0 || p == (const void*)s.p1);
@@ -131,11 +137,15 @@ int fwd_impl(Split<const void> x, const void* w, const float* bias, float* y, fl
   if (z && (is_part(x, z) || (const void*)z == w || z == bias || z == y)) return CONV3X3_ERR_ALIAS;
   if (pr.on() && (y == pr.scale || y == pr.shift)) return CONV3X3_ERR_ALIAS;
   Plan pl;
-  // a stride-2 forward tiles its H/2 x W/2 output, an upsampling one the
-  // H/2 x W/2 input (each tile computing the four output parity classes)
-  Problem pb{kFwd, kdt(dtype), N, C, K, geom ? H / 2 : H, geom ? W / 2 : W, x.c0};
-  pb.stride2 = geom == 2;
-  pb.quad = geom == 1;
+  // float32: a stride-2 forward tiles its H/2 x W/2 output, an upsampling
+  // one the H/2 x W/2 input (each tile computing the four output parity
+  // classes); bfloat16 runs the stride-1 convolution over the full H x W
+  // grid (the upsampled input read at half coordinates; the stride-2
+  // outputs kept at the even pixels)
+  const bool fgeo = geom && dtype == CONV3X3_F32;
+  Problem pb{kFwd, kdt(dtype), N, C, K, fgeo ? H / 2 : H, fgeo ? W / 2 : W, x.c0};
+  pb.stride2 = fgeo && geom == 2;
+  pb.quad = fgeo && geom == 1;
   pb.allow_split = ws_call && aligned16(y) && act == CONV3X3_ACT_NONE && !z && !pr.on() && !geom;
   // (bf16 prologue: four-wave tiles, whose staging threads hold scale and
   // shift beside the x rows)
@@ -214,12 +224,16 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   // du's epilogue reads x through a 32-bit buffer view, like the stores
   if (pr.on() && 4L * N * C * H * W >= 2147483648L) return CONV3X3_ERR_UNSUPPORTED;
   Plan pl;
-  // stride 2: the plan tiles g's H/2 x W/2 grid, each tile computing the
-  // four output-pixel parity classes of its pixels; upsampling: it tiles
-  // dx's H/2 x W/2 grid and stages g at stride 2
-  Problem pb{kBwdData, kdt(dtype), N, C, K, geom ? H / 2 : H, geom ? W / 2 : W, dx.c0};
-  pb.quad = s2;
-  pb.stride2 = geom == 1;
+  // float32 stride 2: the plan tiles g's H/2 x W/2 grid, each tile
+  // computing the four output-pixel parity classes of its pixels;
+  // upsampling: it tiles dx's H/2 x W/2 grid and stages g at stride 2.
+  // bfloat16 stride 2: the stride-1 backward-data over dx's full grid, g
+  // read zero-inserted (upsampling is composed by its entry point).
+  if (geom == 1 && dtype != CONV3X3_F32) return CONV3X3_ERR_UNSUPPORTED;
+  const bool fgeo = geom && dtype == CONV3X3_F32;
+  Problem pb{kBwdData, kdt(dtype), N, C, K, fgeo ? H / 2 : H, fgeo ? W / 2 : W, dx.c0};
+  pb.quad = fgeo && s2;
+  pb.stride2 = fgeo && geom == 1;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE && !pr.on() && !geom;
   pb.four_waves = dtype != CONV3X3_F32 && (act != CONV3X3_ACT_NONE || pr.on());
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
@@ -284,9 +298,11 @@ int bwd_weight_impl(Split<const void> x, const void* g, const float* z, float* d
                   (db && (db == pr.scale || db == pr.shift))))
     return CONV3X3_ERR_ALIAS;
   Plan pl;
-  // stride 2: the pixel chunks tile g's H/2 x W/2 grid
-  Problem pb{kBwdWeight, kdt(dtype), N, C, K, geom == 2 ? H / 2 : H, geom == 2 ? W / 2 : W, x.c0};
-  pb.stride2 = geom == 2;
+  // float32 stride 2: the pixel chunks tile g's H/2 x W/2 grid; bfloat16
+  // stride 2 runs the full H x W grid with g read zero-inserted
+  const bool fs2 = geom == 2 && dtype == CONV3X3_F32;
+  Problem pb{kBwdWeight, kdt(dtype), N, C, K, fs2 ? H / 2 : H, fs2 ? W / 2 : W, x.c0};
+  pb.stride2 = fs2;
   // (at most four input channels, no fusion: the packed-pair kernel)
   pb.stem = C <= 4 && x.c0 == C && geom == 0 && act == CONV3X3_ACT_NONE && !pr.on();
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
@@ -540,14 +556,15 @@ int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace
 
 namespace {
 
-// The upsampled grid must satisfy the plain limits; float32 only.
+// The upsampled grid must satisfy the plain limits; float32, or bfloat16
+// inputs with float32 outputs.
 int check_up2(int N, int C, int K, int H, int W, int dtype) {
   if (H < 1 || W < 1 || H > (1 << 29) || W > (1 << 29)) return CONV3X3_ERR_BAD_SHAPE;
   int rc = check_dims(N, C, K, 2 * H, 2 * W);
   if (rc) return rc;
   rc = check_dtype(dtype);
   if (rc) return rc;
-  return dtype == CONV3X3_F32 ? CONV3X3_OK : CONV3X3_ERR_UNSUPPORTED;
+  return dtype == CONV3X3_F32 || dtype == CONV3X3_BF16 ? CONV3X3_OK : CONV3X3_ERR_UNSUPPORTED;
 }
 
 }  // namespace
@@ -555,7 +572,11 @@ int check_up2(int N, int C, int K, int H, int W, int dtype) {
 size_t conv3x3_up2_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype) {
   if (pass < CONV3X3_PASS_FWD || pass > CONV3X3_PASS_BWD_WEIGHT) return (size_t)-1;
   if (check_up2(N, C, K, H, W, dtype)) return (size_t)-1;
-  if (pass == CONV3X3_PASS_FWD || pass == CONV3X3_PASS_BWD_DATA) return 0;
+  if (pass == CONV3X3_PASS_FWD) return 0;
+  // bfloat16 backward-data: the float32 gradient of the upsampled grid,
+  // summed over 2 x 2 blocks afterwards
+  if (pass == CONV3X3_PASS_BWD_DATA)
+    return dtype == CONV3X3_F32 ? 0 : (size_t)N * C * 4 * (size_t)H * W * sizeof(float);
   Plan pl;
   if (!plan(Problem{kBwdWeight, kdt(dtype), N, C, K, 2 * H, 2 * W}, &pl)) return (size_t)-1;
   return pl.workspace_bytes;
@@ -573,11 +594,27 @@ int conv3x3_fwd_up2(const void* x, const void* w, const float* bias, float* y, i
 int conv3x3_bwd_data_up2(const void* g, const void* w, float* dx, void* workspace,
                          size_t workspace_bytes, int N, int C, int K, int H, int W, int dtype,
                          conv3x3_stream_t stream) {
-  (void)workspace;  // none needed (kept for the calling convention)
-  (void)workspace_bytes;
   if (!g || !w || !dx) return CONV3X3_ERR_NULL_POINTER;
-  const int rc = check_up2(N, C, K, H, W, dtype);
+  int rc = check_up2(N, C, K, H, W, dtype);
   if (rc) return rc;
+  if (dtype != CONV3X3_F32) {
+    // bfloat16: the stride-1 backward-data over the upsampled grid into the
+    // workspace (float32), then the sum of each 2 x 2 block into dx
+    const size_t need = (size_t)N * C * 4 * (size_t)H * W * sizeof(float);
+    if (!workspace || workspace_bytes < need) return CONV3X3_ERR_WORKSPACE;
+    if (overlaps(workspace, need, g, (size_t)N * K * 4 * (size_t)H * W * 2) ||
+        overlaps(workspace, need, w, (size_t)K * C * 9 * 2) ||
+        overlaps(workspace, need, dx, (size_t)N * C * (size_t)H * W * sizeof(float)))
+      return CONV3X3_ERR_ALIAS;
+    rc = bwd_data_impl(g, nullptr, w, one((float*)workspace, C), N, C, K, 2 * H, 2 * W, dtype,
+                       CONV3X3_ACT_NONE, stream);
+    if (rc) return rc;
+    launch_block_sum2((const float*)workspace, dx, (long)N * C, H, W,
+                      reinterpret_cast<hipStream_t>(stream));
+    return launch_status();
+  }
+  (void)workspace;  // float32: none needed (kept for the calling convention)
+  (void)workspace_bytes;
   // one pass over dx's grid: each pixel gathers g's 4 x 4 window at stride 2
   return bwd_data_impl(g, nullptr, w, one(dx, C), N, C, K, 2 * H, 2 * W, dtype, CONV3X3_ACT_NONE,
                        stream, Prologue(), nullptr, false, nullptr, 0, 1);
@@ -603,7 +640,7 @@ int check_s2(int N, int C, int K, int H, int W, int dtype) {
   if (H % 2 || W % 2) return CONV3X3_ERR_BAD_SHAPE;
   rc = check_dtype(dtype);
   if (rc) return rc;
-  return dtype == CONV3X3_F32 ? CONV3X3_OK : CONV3X3_ERR_UNSUPPORTED;
+  return dtype == CONV3X3_F32 || dtype == CONV3X3_BF16 ? CONV3X3_OK : CONV3X3_ERR_UNSUPPORTED;
 }
 
 }  // namespace

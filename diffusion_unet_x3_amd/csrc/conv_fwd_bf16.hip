@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     int tiles_h, uint32_t src_bytes, uint32_t src1_bytes, uint32_t wt_bytes, uint32_t dst_bytes,
     uint32_t dst1_bytes, int act, float* __restrict__ zout, int outb, int per_split,
     float* __restrict__ part, const float* __restrict__ zsrc, const float* __restrict__ pscale,
-    const float* __restrict__ pshift, const uint16_t* __restrict__ px) {
+    const float* __restrict__ pshift, const uint16_t* __restrict__ px, int geo) {
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
@@ -483,8 +483,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
         const int ch = t / (HR * IMGS);
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
         uint16_t v = 0;
-        if (n < N && ch < cn && h >= 0 && h < H && w >= 0 && w < W) {
-          const long e = ((long)n * cs + cl0 + ch) * HW + (long)h * W + w;
+        // (an upsampled or zero-inserted source is an H/2 x W/2 tensor read
+        // at (h / 2, w / 2); zero-inserted: only at even (h, w))
+        const bool half = geo == kGeoUp || geo == kGeoZero;
+        const int sh = half ? h >> 1 : h, sw = half ? w >> 1 : w;
+        const int sW = half ? W >> 1 : W;
+        const long sHW = half ? (long)(H >> 1) * sW : HW;
+        if (n < N && ch < cn && h >= 0 && h < H && w >= 0 && w < W &&
+            (geo != kGeoZero || ((h | w) & 1) == 0)) {
+          const long e = ((long)n * cs + cl0 + ch) * sHW + (long)sh * sW + sw;
           v = sx[e];
           if constexpr (ZG) v = (uint16_t)act_grad_bf16<false>(v, zsrc[e], act);
           if constexpr (SPRO) {
@@ -765,6 +772,29 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
     return;
   }
+  if (geo == kGeoSub) {
+    // stride-2 forward: the stride-1 sums at the even pixels are the
+    // strided convolution's outputs, stored to the H/2 x W/2 output (one
+    // tensor, float32, no split, no activation)
+    const int OH = H >> 1, OW = W >> 1;
+    const long OHW = (long)OH * OW;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int p = wpx * (BM / WPX) + j * 32 + l32;
+      const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+      const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+      if (n >= N || h >= H || w >= W || ((h | w) & 1)) continue;
+      const long base = (long)n * ocs * OHW + (long)(h >> 1) * OW + (w >> 1);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int co = cw + i * 32 + acc_row(v, hi);
+          if (co < ocs) dst[base + (long)co * OHW] = acc[i][j][v];
+        }
+    }
+    return;
+  }
   const bool plain = part != nullptr || MODE != kFwd || (act == kActNone && zout == nullptr);
   const uint32_t slot_bytes = (uint32_t)N * (uint32_t)Cout * (uint32_t)HW * 4u;
   float* const od = part ? part + (size_t)blockIdx.z * ((size_t)slot_bytes / 4) : oseg ? dst1 : dst;
@@ -914,6 +944,26 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   }
 }
 
+// dx = the 2 x 2 block sums of du (see launch.hpp), ((00 + 01) + 10) + 11.
+__global__ __launch_bounds__(256) void block_sum2_kernel(const float* __restrict__ du,
+                                                         float* __restrict__ dx, long total,
+                                                         int H, int W) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const long plane = e / ((long)H * W);
+  const int r = (int)(e % ((long)H * W));
+  const int i = r / W, j = r % W;
+  const float* d = du + plane * 4L * H * W + (long)(2 * i) * (2 * W) + 2 * j;
+  dx[e] = ((d[0] + d[1]) + d[2 * W]) + d[2 * W + 1];
+}
+
+void launch_block_sum2(const float* du, float* dx, long planes, int H, int W,
+                       hipStream_t stream) {
+  const long total = planes * H * W;
+  dim3 g((unsigned)((total + 255) / 256)), b(256);
+  hipLaunchKernelGGL(block_sum2_kernel, g, b, 0, stream, du, dx, total, H, W);
+}
+
 void launch_split_reduce(const float* part, int S, long slot, float* dst, hipStream_t stream) {
   dim3 rg((unsigned)((slot + 1023) / 1024)), rb(256);
   hipLaunchKernelGGL(split_reduce_kernel, rg, rb, 0, stream, part, S, slot, dst, 0, (int)kActNone,
@@ -931,6 +981,10 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
   // split reduction: partial sums into ws, then split_reduce_kernel
   float* const part = pl.split > 1 ? ws : nullptr;
   dim3 grid(pl.grid_x, pl.grid_y, part ? pl.split : 1), block(64 * NW, 1, 1);
+  // resampling geometry (scalar path only)
+  const int geo = MODE == kFwd ? (a.up2 ? kGeoUp : a.s2 ? kGeoSub : kGeoPlain)
+                               : (a.s2 ? kGeoZero : kGeoPlain);
+  if (geo != kGeoPlain) vec = false;
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets), and a float32 z beside bfloat16 outputs twice that; otherwise
   // the plain-store path runs.
@@ -946,13 +1000,13 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                        (uint32_t)(N * src.c0 * hw * 2), (uint32_t)(N * (Cin - src.c0) * hw * 2),
                        (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout,
                        out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc, a.pscale, a.pshift,
-                       (const uint16_t*)a.px);
+                       (const uint16_t*)a.px, (int)kGeoPlain);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false, ZG, PRO>),
                        grid, block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
                        dst.c0, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h, 0u, 0u, 0u, db0, db1,
                        a.act, a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc,
-                       a.pscale, a.pshift, (const uint16_t*)a.px);
+                       a.pscale, a.pshift, (const uint16_t*)a.px, geo);
   if (part) {
     const long slot = (long)N * Cout * hw;
     dim3 rg((unsigned)((slot + 1023) / 1024)), rb(256);
@@ -979,6 +1033,15 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
     return false;
   if (a.zsrc != nullptr && (pl.pass == kFwd || pro)) return false;
   if (pro && pl.pass == kBwdData && a.px == nullptr) return false;
+  // Resampling (scalar staging over the full-resolution grid): one source
+  // and one output tensor, float32 output, no split or fusion; backward-data
+  // of the upsampling call is composed by the caller (its full-resolution
+  // result summed over 2 x 2 blocks).
+  if ((a.up2 || a.s2) &&
+      (src.c0 != Cin || dst.c0 != Cout || pl.split > 1 || out_bf16 || pro ||
+       a.zsrc != nullptr || a.zout != nullptr || a.act != kActNone ||
+       (pl.pass == kBwdData && a.up2) || (H & 1) || (W & 1)))
+    return false;
 #define CONV3X3_X(TW_, TH_, IMGS_, CO_, WCO_, NW_)                                              \
   if (pl.tw == TW_ && pl.th == TH_ && pl.imgs == IMGS_ && pl.tile_co == CO_ &&                  \
       pl.wave_co == WCO_ && pl.threads == 64 * NW_) {                                           \

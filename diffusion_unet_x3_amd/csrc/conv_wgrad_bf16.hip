@@ -41,7 +41,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     int C, int K, int H, int W, int tiles_w, int tiles_h, int nchunks, int per_split,
     long slice_stride, int split, int tiles_c, int tiles_k, uint32_t x_bytes, uint32_t x1_bytes,
     uint32_t g_bytes, int act, const float* __restrict__ zsrc, const float* __restrict__ pscale,
-    const float* __restrict__ pshift) {
+    const float* __restrict__ pshift, int xgeo, int ggeo) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P % 16 == 0, "whole 16-pixel MFMA steps");
   static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
@@ -269,8 +269,13 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int kl = t / IMGS;
           const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + col;
           uint16_t v = 0;
-          if (n < N && kk < K && h < H && w < W) {
-            const long e = ((long)n * K + kk) * HW + (long)h * W + w;
+          // (a zero-inserted g is an H/2 x W/2 tensor read at (h / 2, w / 2)
+          // for even (h, w), zero elsewhere)
+          const bool zi = ggeo == kGeoZero;
+          if (n < N && kk < K && h < H && w < W && (!zi || ((h | w) & 1) == 0)) {
+            const long e = zi ? ((long)n * K + kk) * (long)(H >> 1) * (W >> 1) +
+                                    (long)(h >> 1) * (W >> 1) + (w >> 1)
+                              : ((long)n * K + kk) * HW + (long)h * W + w;
             v = g[e];
             if constexpr (ZG) v = (uint16_t)act_grad_bf16<false>(v, zsrc[e], act);
           }
@@ -291,7 +296,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + cc;
           uint16_t v = 0;
           if (n < N && cl < cn && h >= 0 && h < H && w >= 0 && w < W) {
-            v = xsrc[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
+            // (an upsampled x is an H/2 x W/2 tensor read at (h / 2, w / 2))
+            v = xgeo == kGeoUp ? xsrc[((long)n * cs + cl0 + cl) * (long)(H >> 1) * (W >> 1) +
+                                      (long)(h >> 1) * (W >> 1) + (w >> 1)]
+                               : xsrc[((long)n * cs + cl0 + cl) * HW + (long)h * W + w];
             if constexpr (PRO) {
               const long pc = (long)n * C + c0 + cl;
               v = (uint16_t)silu_affine_bf16<false>(v, pscale[pc], pshift[pc]);
@@ -419,18 +427,21 @@ static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, Split<const uint16_
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
   const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
   const long hw2 = (long)H * W * 2;
+  // resampling geometry (scalar path only)
+  const int xgeo = a.up2 ? kGeoUp : kGeoPlain, ggeo = a.s2 ? kGeoZero : kGeoPlain;
+  if (a.up2 || a.s2) vec = false;
   if (vec)
     hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, ZG, PRO>), grid, block, 0, stream,
                        x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
                        (K + 63) / 64, (uint32_t)(N * x.c0 * hw2),
                        (uint32_t)(N * (C - x.c0) * hw2), (uint32_t)(N * K * hw2), a.act, a.zsrc,
-                       a.pscale, a.pshift);
+                       a.pscale, a.pshift, (int)kGeoPlain, (int)kGeoPlain);
   else
     hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, false, ZG, PRO>), grid, block, 0, stream,
                        x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
                        pl.nchunks, pl.chunks_per_split, slice_stride, pl.split, tiles_c,
-                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc, a.pscale, a.pshift);
+                       (K + 63) / 64, 0u, 0u, 0u, a.act, a.zsrc, a.pscale, a.pshift, xgeo, ggeo);
 }
 
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
@@ -440,6 +451,11 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const 
   // the prologue needs one x tensor and does not combine with a fused
   // activation gradient
   if (a.pscale != nullptr && (a.zsrc != nullptr || x.c0 != C)) return false;
+  // resampling (scalar staging over the full-resolution grid): one x
+  // tensor, no fusion, even sizes
+  if ((a.up2 || a.s2) && (x.c0 != C || a.zsrc != nullptr || a.pscale != nullptr || (H & 1) ||
+                          (W & 1)))
+    return false;
   const long n_dw = (long)K * C * 9;
   float* out = pl.split > 1 ? ws : dw;
   float* out_db = db == nullptr ? nullptr : (pl.split > 1 ? ws + (long)pl.split * n_dw : db);

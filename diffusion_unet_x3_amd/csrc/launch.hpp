@@ -9,6 +9,17 @@
 
 namespace conv3x3 {
 
+// Resampling geometry of the bfloat16 kernels' scalar staging paths (the
+// stride-2 and upsampling entry points): the kernel runs the stride-1
+// convolution over the full-resolution grid (its H x W) and
+//   kGeoUp   : reads its source at (h / 2, w / 2) of an H/2 x W/2 tensor
+//              (nearest 2x upsampling of the input);
+//   kGeoZero : reads it there only at even (h, w), zero elsewhere (the
+//              zero-inserted gradient of a stride-2 convolution);
+//   kGeoSub  : (forward) stores only the even pixels, to (h / 2, w / 2) of
+//              an H/2 x W/2 output (the stride-2 convolution's outputs).
+enum Geo { kGeoPlain = 0, kGeoUp = 1, kGeoZero = 2, kGeoSub = 3 };
+
 // A channel axis held by two tensors: channels [0, c0) in p0 and [c0, C) in
 // p1 (the concatenation [p0 ; p1]).  One tensor is c0 = C (p1 unused).
 template <typename T>
@@ -33,9 +44,16 @@ bool launch_fwd_f32(const Plan& pl, bool vec, Split<const float> src, const floa
 // split forward / backward-data reduction into dst (float32, no activation).
 void launch_split_reduce(const float* part, int S, long slot, float* dst, hipStream_t stream);
 
+// dx[p, i, j] = the sum of du[p, 2i .. 2i + 1, 2j .. 2j + 1] in a fixed
+// order, for planes p < planes of an H x W dx (du: 2H x 2W planes).
+void launch_block_sum2(const float* du, float* dx, long planes, int H, int W,
+                       hipStream_t stream);
+
 // Same, bfloat16 inputs (raw 16-bit patterns); outputs float32, or bfloat16
 // (round to nearest even) when out_bf16 (dst then points to 16-bit values;
-// a.zout stays float32).  pl.split > 1: the reduction is split over
+// a.zout stays float32).  a.up2 (forward: x upsampled) and a.s2 (forward:
+// strided outputs; backward-data: g zero-inserted) run the plan's
+// full-resolution grid through the scalar staging path (Geo above).  pl.split > 1: the reduction is split over
 // pl.split workgroups per tile, their partial sums kept in ws (pl.split
 // float32 copies of the output) and added by a second kernel.
 bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
@@ -72,7 +90,8 @@ bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
                           const float* bias, float* y, int N, int C, int K, int H, int W,
                           hipStream_t stream);
 
-// Same, bfloat16 inputs.
+// Same, bfloat16 inputs; a.up2 stages x upsampled, a.s2 stages g
+// zero-inserted, over the plan's full-resolution grid (scalar path).
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
                        float* dw,
                        float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,

@@ -350,13 +350,20 @@ int conv3x3_bwd_data_ws(const void* g, const void* w, float* dx, void* workspace
  * ph = 0; {0, 1}, {2} on rows i, i + 1 for ph = 1; likewise columns).
  * Backward-data: dx[i, j] gathers g rows and columns 2i - 1 .. 2i + 2 at
  * stride 2 with a 4 x 4 kernel of summed taps.  Backward-weight's loader
- * reads x at (h/2, w/2) as it stages the upsampled tile.  Workspace bytes:
- * conv3x3_up2_workspace_size(pass, ...) -- 0 for the forward and
- * backward-data (whose workspace arguments may be NULL, 0), the split-K
- * size of the 2H x 2W problem for backward-weight.  The summed taps round
- * differently from the upsampled-grid sums (within the float32 bar).
- * float32 only (CONV3X3_ERR_UNSUPPORTED for bfloat16); the limits apply to
- * the 2H x 2W problem.
+ * reads x at (h/2, w/2) as it stages the upsampled tile.  The summed taps
+ * round differently from the upsampled-grid sums (within the float32 bar).
+ * CONV3X3_BF16 (bfloat16 x, w, g; float32 y, dx, dw, db) runs the stride-1
+ * bfloat16 kernels over the 2H x 2W grid instead: the forward and
+ * backward-weight stage x read at (h/2, w/2) (no summed taps, so every
+ * product is one of the upsampled grid's); backward-data writes the
+ * upsampled grid's float32 input gradient into the workspace and then sums
+ * each 2 x 2 block into dx.  Workspace bytes:
+ * conv3x3_up2_workspace_size(pass, ...) -- 0 for the forward (whose
+ * workspace arguments may be NULL, 0); for backward-data 0 for float32 and
+ * N * C * 2H * 2W * 4 for bfloat16; the split-K size of the 2H x 2W
+ * problem for backward-weight.  A bfloat16 backward-data workspace that
+ * overlaps g, w or dx is CONV3X3_ERR_ALIAS.  CONV3X3_BF16_IO is
+ * CONV3X3_ERR_UNSUPPORTED; the limits apply to the 2H x 2W problem.
  */
 size_t conv3x3_up2_workspace_size(int pass, int N, int C, int K, int H, int W, int dtype);
 
@@ -382,8 +389,12 @@ int conv3x3_bwd_weight_up2(const void* x, const void* g, float* dw, float* db, v
  * stage x at stride 2; backward-data tiles g's grid and computes the four
  * output-pixel parity classes (dx[2i + ph, 2j + pw] takes the taps r = 1 for
  * ph = 0, r = 0 and 2 for ph = 1, likewise s and pw) from one staged tile.
- * No pass multiplies inserted zeros.  float32 only (CONV3X3_ERR_UNSUPPORTED
- * for bfloat16).
+ * No float32 pass multiplies inserted zeros.  CONV3X3_BF16 (bfloat16 x, w,
+ * g; float32 outputs) runs the stride-1 bfloat16 kernels over the full
+ * H x W grid: the forward keeps the even output pixels, backward-data and
+ * backward-weight read g zero-inserted (g[i/2, j/2] at even (i, j), zero
+ * elsewhere), so they spend four times the float32 paths' multiplies.
+ * CONV3X3_BF16_IO is CONV3X3_ERR_UNSUPPORTED.
  */
 int conv3x3_fwd_s2(const void* x, const void* w, const float* bias, float* y, int N, int C,
                    int K, int H, int W, int dtype, conv3x3_stream_t stream);

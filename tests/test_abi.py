@@ -294,21 +294,34 @@ def test_up2_argument_checks():
     assert lib3.conv3x3_up2_workspace_size(lib3.PASS_BWD_DATA, *d) == 0
     assert lib3.conv3x3_up2_workspace_size(lib3.PASS_BWD_WEIGHT, *d) == \
         lib3.conv3x3_bwd_weight_workspace_size(2, 4, 4, 10, 12)
-    assert L.conv3x3_fwd_up2(X, Wt, B, Y, *d, 1, None) == unsup
-    assert L.conv3x3_bwd_data_up2(G, Wt, Y, WS, 1 << 30, *d, 1, None) == unsup
-    assert L.conv3x3_bwd_weight_up2(X, G, Y, B, WS, 1 << 30, *d, 1, None) == unsup
+    # bfloat16 inputs: float32 outputs only (no bf16-output mode)
+    assert L.conv3x3_fwd_up2(X, Wt, B, Y, *d, 2, None) == unsup
+    assert L.conv3x3_bwd_data_up2(G, Wt, Y, WS, 1 << 30, *d, 2, None) == unsup
+    assert L.conv3x3_bwd_weight_up2(X, G, Y, B, WS, 1 << 30, *d, 2, None) == unsup
     assert L.conv3x3_fwd_up2(X, Wt, B, Y, 2, 4, 4, 0, 6, 0, None) == S["ERR_BAD_SHAPE"]
-    # backward-data needs no workspace; dx may not be g
+    # float32 backward-data needs no workspace; dx may not be g
     assert L.conv3x3_bwd_data_up2(G, Wt, G, None, 0, *d, 0, None) == alias
     assert L.conv3x3_fwd_up2(X, Wt, B, X, *d, 0, None) == alias
+    # bfloat16 backward-data: the upsampled-grid float32 gradient in the
+    # workspace, summed over 2 x 2 blocks afterwards
+    need = 2 * 4 * 4 * 5 * 6 * 4
+    assert lib3.conv3x3_up2_workspace_size(lib3.PASS_BWD_DATA, *d, 1) == need
+    assert lib3.conv3x3_up2_workspace_size(lib3.PASS_FWD, *d, 1) == 0
+    assert L.conv3x3_bwd_data_up2(G, Wt, Y, None, 0, *d, 1, None) == S["ERR_WORKSPACE"]
+    assert L.conv3x3_bwd_data_up2(G, Wt, Y, WS, need - 1, *d, 1, None) == S["ERR_WORKSPACE"]
+    assert L.conv3x3_bwd_data_up2(G, Wt, Y, G, need, *d, 1, None) == alias
+    assert L.conv3x3_bwd_data_up2(G, Wt, Y, Y, need, *d, 1, None) == alias
 
 
 def test_s2_argument_checks():
     d = (2, 4, 4, 6, 8)
     assert L.conv3x3_fwd_s2(X, Wt, B, Y, 2, 4, 4, 5, 8, 0, None) == S["ERR_BAD_SHAPE"]  # odd H
     assert L.conv3x3_bwd_data_s2(G, Wt, Y, 2, 4, 4, 6, 7, 0, None) == S["ERR_BAD_SHAPE"]
-    assert L.conv3x3_fwd_s2(X, Wt, B, Y, *d, 1, None) == S["ERR_UNSUPPORTED"]
-    assert L.conv3x3_bwd_weight_s2(X, G, Y, B, WS, 1 << 30, *d, 1, None) == S["ERR_UNSUPPORTED"]
+    # bfloat16 inputs with float32 outputs run; the bf16-output mode does not
+    assert L.conv3x3_fwd_s2(X, Wt, B, Y, *d, 2, None) == S["ERR_UNSUPPORTED"]
+    assert L.conv3x3_bwd_weight_s2(X, G, Y, B, WS, 1 << 30, *d, 2, None) == S["ERR_UNSUPPORTED"]
+    assert L.conv3x3_bwd_weight_s2(X, G, Y, B, None, 0, 2, 64, 64, 64, 64, 1, None) == \
+        S["ERR_WORKSPACE"]
     assert L.conv3x3_fwd_s2(None, Wt, B, Y, *d, 0, None) == S["ERR_NULL_POINTER"]
     assert L.conv3x3_fwd_s2(X, Wt, B, X, *d, 0, None) == S["ERR_ALIAS"]
     assert L.conv3x3_bwd_weight_s2(X, G, Y, B, None, 0, 2, 64, 64, 64, 64, 0, None) == \

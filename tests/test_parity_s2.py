@@ -6,7 +6,11 @@ The shapes reach the vector staging (W % 8 == 0, 16-byte aligned) and the
 scalar one, output grids wider than one tile (the left halo column of the
 stride-2 x tile is loaded), ragged channel fills and tiles, several images
 per block, and g grids with odd sizes (every output-pixel parity class of
-backward-data gets a ragged edge)."""
+backward-data gets a ragged edge).  bfloat16 inputs run the stride-1
+passes over the full-resolution grid through the scalar staging paths
+(the forward keeping the even pixels; backward-data and backward-weight
+reading g zero-inserted), to the bf16 trip-wire (1e-4; exact on integer
+inputs)."""
 import numpy as np
 import pytest
 import torch
@@ -18,9 +22,9 @@ from parity_util import TRIPWIRE, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(N, C, K, H, W, seed, integer=False):
+def _inputs(N, C, K, H, W, seed, integer=False, dtype="f32"):
     """x at H x W, g at H/2 x W/2 (a corner of the full-size draw)."""
-    layer = wl.small_layer(N, C, K, H, W, dtype="f32", seed=seed)
+    layer = wl.small_layer(N, C, K, H, W, dtype=dtype, seed=seed)
     inp = wl.make_inputs(layer, integer_exact=integer)
     inp["g"] = inp["g"][:, :, :H // 2, :W // 2].contiguous()
     return inp
@@ -51,10 +55,11 @@ SHAPES = [(2, 64, 64, 32, 32), (2, 8, 16, 8, 12), (1, 3, 5, 6, 10), (2, 17, 33, 
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_s2_full_compare(shape, integer):
-    print(f"[parity] s2 {shape} integer={integer}", flush=True)
-    inp = _inputs(*shape, seed=97, integer=integer)
+def test_s2_full_compare(shape, dtype, integer):
+    print(f"[parity] s2 {dtype} {shape} integer={integer}", flush=True)
+    inp = _inputs(*shape, seed=97, integer=integer, dtype=dtype)
     gpu = _run(inp)
     ref = {"y": oracle.conv3x3_fwd_s2(inp["x"], inp["w"], inp["b"]),
            "dx": oracle.conv3x3_bwd_data_s2(inp["g"], inp["w"])}
@@ -65,14 +70,15 @@ def test_s2_full_compare(shape, integer):
             assert np.array_equal(gpu[k], r), (shape, k)
         else:
             e = rel_err(gpu[k], r)
-            assert e <= TRIPWIRE["f32"], (shape, k, e)
+            assert e <= TRIPWIRE[dtype], (shape, k, e)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("layer", wl.DOWNSAMPLE, ids=lambda l: l.name)
-def test_downsample_layers_sampled(layer):
+def test_downsample_layers_sampled(layer, dtype):
     N, C, K, H, W = layer.shape
-    print(f"[parity] s2 {layer.name}", flush=True)
-    inp = _inputs(N, C, K, H, W, seed=101)
+    print(f"[parity] s2 {layer.name} {dtype}", flush=True)
+    inp = _inputs(N, C, K, H, W, seed=101, dtype=dtype)
     gpu = _run(inp)
     x, w, b, g = inp["x"], inp["w"], inp["b"], inp["g"]
     gz = oracle.zero_insert2(g)
@@ -89,14 +95,15 @@ def test_downsample_layers_sampled(layer):
     errs["dw"] = rel_err(gpu["dw"].ravel()[j], oracle.conv3x3_bwd_weight_at(x, gz, j))
     print(layer.name, errs)
     for name, e in errs.items():
-        assert e <= TRIPWIRE["f32"], (layer.name, name, e)
+        assert e <= TRIPWIRE[dtype], (layer.name, name, e)
 
 
-def test_s2_deterministic_bitwise():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_s2_deterministic_bitwise(dtype):
     """No atomics in any stride-2 pass: two runs agree bit for bit (the
     128-channel downsample layer, split-K backward-weight included)."""
     layer = wl.DOWNSAMPLE[0]
-    inp = _inputs(*layer.shape, seed=103)
+    inp = _inputs(*layer.shape, seed=103, dtype=dtype)
     a, b = _run(inp), _run(inp)
     for k in ("y", "dx", "dw", "db"):
         assert np.array_equal(a[k], b[k]), k

@@ -6,8 +6,12 @@ integer inputs, where the summed taps of the parity-class forward and the
 (widths that give the vector and the scalar staging paths, one and several
 tiles across -- the backward-data tile's right halo column --, odd heights,
 ragged channel fills and tiles, several images per block) and on a
-full-size up-path layer by sampled elements.  The calls pass no workspace
-to backward-data, which needs none."""
+full-size up-path layer by sampled elements.  bfloat16 inputs run the
+stride-1 passes over the upsampled grid, the upsampled x read at half
+coordinates by the scalar staging paths and backward-data's upsampled-grid
+gradient summed over 2 x 2 blocks afterwards (through the workspace the
+binding sizes with conv3x3_up2_workspace_size); the bar is then the bf16
+trip-wire (1e-4), and integer inputs are exact."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +24,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(inp):
+    """All three passes through the C ABI (the binding supplies the
+    workspaces)."""
     import diffusion_unet_x3_amd as lib3
     dev = torch.device("cuda", 0)
     x, w, g, b = (inp[k].to(dev) for k in ("x", "w", "g", "b"))
@@ -37,10 +43,10 @@ def _run(inp):
     return {k: v.cpu().double().numpy() for k, v in dict(y=y, dx=dx, dw=dw, db=db).items()}
 
 
-def _inputs(N, C, K, H, W, seed, integer=False):
+def _inputs(N, C, K, H, W, seed, integer=False, dtype="f32"):
     """x at H x W, g at 2H x 2W (the layer record is drawn at the upsampled
     size; x is its top-left quarter, so every draw stays seeded)."""
-    layer = wl.small_layer(N, C, K, 2 * H, 2 * W, dtype="f32", seed=seed)
+    layer = wl.small_layer(N, C, K, 2 * H, 2 * W, dtype=dtype, seed=seed)
     inp = wl.make_inputs(layer, integer_exact=integer)
     inp["x"] = inp["x"][:, :, :H, :W].contiguous()
     return inp
@@ -53,10 +59,11 @@ SHAPES = [(2, 64, 64, 16, 16), (2, 8, 16, 4, 6), (1, 3, 5, 7, 9), (2, 17, 33, 5,
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_up2_full_compare(shape, integer):
-    print(f"[parity] up2 {shape} integer={integer}", flush=True)
-    inp = _inputs(*shape, seed=83, integer=integer)
+def test_up2_full_compare(shape, dtype, integer):
+    print(f"[parity] up2 {dtype} {shape} integer={integer}", flush=True)
+    inp = _inputs(*shape, seed=83, integer=integer, dtype=dtype)
     gpu = _run(inp)
     ref = {"y": oracle.conv3x3_fwd_up2(inp["x"], inp["w"], inp["b"]),
            "dx": oracle.conv3x3_bwd_data_up2(inp["g"], inp["w"])}
@@ -67,13 +74,15 @@ def test_up2_full_compare(shape, integer):
             assert np.array_equal(gpu[k], r), (shape, k)
         else:
             e = rel_err(gpu[k], r)
-            assert e <= TRIPWIRE["f32"], (shape, k, e)
+            assert e <= TRIPWIRE[dtype], (shape, k, e)
 
 
-def test_full_size_up_layer_sampled():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_size_up_layer_sampled(dtype):
     """The 32x32 -> 64x64 up step of the UNet (N = 32, 128 channels)."""
     N, C, K, H, W = 32, 128, 128, 32, 32
-    inp = _inputs(N, C, K, H, W, seed=89)
+    print(f"[parity] up2 full-size {dtype}", flush=True)
+    inp = _inputs(N, C, K, H, W, seed=89, dtype=dtype)
     gpu = _run(inp)
     x, w, b, g = inp["x"], inp["w"], inp["b"], inp["g"]
     u = oracle.upsample2(x)
@@ -94,12 +103,13 @@ def test_full_size_up_layer_sampled():
     errs["dw"] = rel_err(gpu["dw"].ravel()[k], oracle.conv3x3_bwd_weight_at(u, g, k))
     print(errs)
     for name, e in errs.items():
-        assert e <= TRIPWIRE["f32"], (name, e)
+        assert e <= TRIPWIRE[dtype], (name, e)
 
 
-def test_up2_deterministic_bitwise():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_up2_deterministic_bitwise(dtype):
     """No atomics in any upsampling pass: two runs agree bit for bit."""
-    inp = _inputs(4, 128, 64, 8, 8, seed=107)
+    inp = _inputs(4, 128, 64, 8, 8, seed=107, dtype=dtype)
     a, b = _run(inp), _run(inp)
     for k in ("y", "dx", "dw", "db"):
         assert np.array_equal(a[k], b[k]), k
