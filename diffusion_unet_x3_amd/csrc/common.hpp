@@ -85,6 +85,22 @@ __device__ __forceinline__ void buffer_load_2f(__amdgpu_buffer_rsrc_t v, uint32_
 __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t v, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(v, (int)off, 0, 0);
 }
+// Eight bytes at byte offset off (one 64-bit load); callers split the words
+// with shifts, not ext-vector lanes.
+__device__ __forceinline__ uint64_t buffer_load8(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(v, (int)off, 0, 0));
+}
+
+// Four bfloat16 values (words a = e0 | e1 << 16, b = e2 | e3 << 16) spread
+// over eight pixels.  Nearest-neighbour 2x along a row: e0 e0 e1 e1 e2 e2 e3 e3.
+__device__ __forceinline__ u32x4 bf16x4_repeat2(uint32_t a, uint32_t b) {
+  return {(a & 0xffffu) | (a << 16), (a >> 16) | (a & 0xffff0000u), (b & 0xffffu) | (b << 16),
+          (b >> 16) | (b & 0xffff0000u)};
+}
+// Zero insertion along a row: e0 0 e1 0 e2 0 e3 0.
+__device__ __forceinline__ u32x4 bf16x4_zero_insert(uint32_t a, uint32_t b) {
+  return {a & 0xffffu, a >> 16, b & 0xffffu, b >> 16};
+}
 
 // Store one float at byte offset voff + soff of a view; soff is uniform
 // across the wave (a scalar register).  The range check applies to voff, so

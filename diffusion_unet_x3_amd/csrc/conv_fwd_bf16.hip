@@ -100,7 +100,7 @@ __device__ __forceinline__ u32x4 tap_word(const uint32_t* d) {
 // backward-data: the output is du = acc * SiLU'(u) with u from px (x, the
 // forward's bfloat16 input), pscale and pshift at the output position.
 template <int MODE, int TW, int TH, int IMGS, int BCO, int WCO, int NW, bool VEC, bool ZG,
-          bool PRO>
+          bool PRO, int XG = kGeoPlain>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ src, const uint16_t* __restrict__ src1, int cin0,
     const uint16_t* __restrict__ wt, const float* __restrict__ bias, float* __restrict__ dst,
@@ -112,6 +112,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   constexpr int NT = 64 * NW;
   constexpr int CB = 16;
   constexpr int BM = IMGS * TH * TW;
+  // XG: the vector path's source is an H/2 x W/2 tensor read at (h/2, w/2)
+  // (kGeoUp) or zero-inserted (kGeoZero: only at even h, w); one source
+  // tensor, no fusion.  The scalar path takes its geometry from `geo`.
+  static_assert(XG == kGeoPlain || (VEC && !ZG && !PRO && (XG == kGeoUp || XG == kGeoZero)),
+                "resampled vector staging: plain operands only");
   // Eight-wave workgroups are wave-specialised: waves 0-3 (one per SIMD)
   // only read operands from LDS and run MFMAs, waves 4-7 only stage tiles.
   // Four-wave workgroups do both in every wave.
@@ -237,7 +242,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const uint32_t ps_bytes = SPRO ? 4u * (uint32_t)N * (uint32_t)Cin : 0u;
   const __amdgpu_buffer_rsrc_t psv = buffer_view(pscale, ps_bytes);
   const __amdgpu_buffer_rsrc_t ptv = buffer_view(pshift, ps_bytes);
-  const uint32_t hw2 = 2u * (uint32_t)(H * W);
+  // bytes of one source channel plane
+  const int SH = XG == kGeoPlain ? H : H >> 1, SW = XG == kGeoPlain ? W : W >> 1;
+  const uint32_t hw2 = 2u * (uint32_t)(SH * SW);
   // x and halo item offsets in src (channel 8g of image n) and in src1
   uint32_t xoff = kOutside, hoff = kOutside, xoff1 = kOutside, hoff1 = kOutside, woff[WK];
   uint32_t pxo = kOutside, pho = kOutside;  // SPRO: scale / shift of the x and halo items
@@ -256,9 +263,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const int img = t % IMGS;
       const int g = t / IMGS;
       const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
-      if (n < N && h >= 0 && h < H && w < W) {
-        xoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * H + h) * W + w);
-        xoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * H + h) * W + w);
+      if (n < N && h >= 0 && h < H && w < W && (XG != kGeoZero || (h & 1) == 0)) {
+        // (resampled: 8 pixels of the row are 4 source elements at w/2)
+        const int sh = XG == kGeoPlain ? h : h >> 1, sw = XG == kGeoPlain ? w : w >> 1;
+        xoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * SH + sh) * SW + sw);
+        xoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * SH + sh) * SW + sw);
         pxo = 4u * (uint32_t)(n * Cin + 8 * g);
       }
       xdst = g * PLW + (img * HR + rr) * RS + 4 + 8 * q;
@@ -271,9 +280,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const int img = t % IMGS;
       const int g = t / IMGS;
       const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + (side ? TW : -1);
-      if (n < N && h >= 0 && h < H && w >= 0 && w < W) {
-        hoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * H + h) * W + w);
-        hoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * H + h) * W + w);
+      if (n < N && h >= 0 && h < H && w >= 0 && w < W &&
+          (XG != kGeoZero || ((h | w) & 1) == 0)) {
+        const int sh = XG == kGeoPlain ? h : h >> 1, sw = XG == kGeoPlain ? w : w >> 1;
+        hoff = 2u * (uint32_t)(((n * cin0 + 8 * g) * SH + sh) * SW + sw);
+        hoff1 = 2u * (uint32_t)(((n * (Cin - cin0) + 8 * g) * SH + sh) * SW + sw);
         pho = 4u * (uint32_t)(n * Cin + 8 * g);
       }
     }
@@ -308,8 +319,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const uint32_t fx = (uint32_t)(chunk - (s1 ? nq0 : 0)) * xstep;
     if (xrole) {
       const uint32_t b = (s1 ? xoff1 : xoff) + fx;
+      if constexpr (XG == kGeoPlain) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, b + (uint32_t)i * hw2);
+        for (int i = 0; i < 8; ++i) st[S][i] = buffer_load16(sv, b + (uint32_t)i * hw2);
+      } else {
+        // four source elements per channel row, spread when written
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint64_t u = buffer_load8(sv, b + (uint32_t)i * hw2);
+          st[S][i].x = (uint32_t)u;
+          st[S][i].y = (uint32_t)(u >> 32);
+        }
+      }
       if constexpr (SPRO) {
         // (one source tensor: s1 is false) 16 channels per fill
         const uint32_t pb = pxo + 64u * f;
@@ -400,6 +421,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
         for (int i = 0; i < 8; ++i)
           hv[S][i] = silu_affine_bf16<false>(hv[S][i], psh[S][i >> 2][i & 3],
                                              psh[S][2 + (i >> 2)][i & 3]);
+      }
+    }
+    if constexpr (XG != kGeoPlain) {
+      if (xrole) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          st[S][i] = XG == kGeoUp ? bf16x4_repeat2(st[S][i].x, st[S][i].y)
+                                  : bf16x4_zero_insert(st[S][i].x, st[S][i].y);
       }
     }
     if (xrole) {
@@ -981,10 +1010,10 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
   // split reduction: partial sums into ws, then split_reduce_kernel
   float* const part = pl.split > 1 ? ws : nullptr;
   dim3 grid(pl.grid_x, pl.grid_y, part ? pl.split : 1), block(64 * NW, 1, 1);
-  // resampling geometry (scalar path only)
+  // resampling geometry: the source read at half coordinates (kGeoUp,
+  // kGeoZero) or the outputs kept at the even pixels (kGeoSub)
   const int geo = MODE == kFwd ? (a.up2 ? kGeoUp : a.s2 ? kGeoSub : kGeoPlain)
                                : (a.s2 ? kGeoZero : kGeoPlain);
-  if (geo != kGeoPlain) vec = false;
   // Buffer-view stores need each output tensor below 2 GiB (32-bit byte
   // offsets), and a float32 z beside bfloat16 outputs twice that; otherwise
   // the plain-store path runs.
@@ -993,6 +1022,19 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
   const long ob0 = (long)N * dst.c0 * hw * es, ob1 = (long)N * (Cout - dst.c0) * hw * es;
   const bool small = ob0 * zf < 2147483648L && ob1 * zf < 2147483648L;
   const uint32_t db0 = small ? (uint32_t)ob0 : 0u, db1 = small ? (uint32_t)ob1 : 0u;
+  constexpr int XG = MODE == kFwd ? kGeoUp : kGeoZero;  // this pass's resampled source
+  if constexpr (!ZG && !PRO) {
+    if (vec && geo == XG) {
+      // one source tensor of N x Cin x H/2 x W/2
+      hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true, false, false, XG>),
+                         grid, block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
+                         dst.c0, N, Cin, Cout, H, W, pl.tiles_w, pl.tiles_h,
+                         (uint32_t)(N * Cin * (hw / 4) * 2), 0u, (uint32_t)((long)Cin * Cout * 9 * 2),
+                         db0, db1, a.act, a.zout, out_bf16 ? 1 : 0, pl.chunks_per_split, part,
+                         a.zsrc, a.pscale, a.pshift, (const uint16_t*)a.px, (int)kGeoPlain);
+      return;
+    }
+  }
   if (vec)
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, true, ZG, PRO>), grid,
                        block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
@@ -1000,7 +1042,7 @@ static void launch_bf16_cfg(const Plan& pl, bool vec, Split<const uint16_t> src,
                        (uint32_t)(N * src.c0 * hw * 2), (uint32_t)(N * (Cin - src.c0) * hw * 2),
                        (uint32_t)((long)Cin * Cout * 9 * 2), db0, db1, a.act, a.zout,
                        out_bf16 ? 1 : 0, pl.chunks_per_split, part, a.zsrc, a.pscale, a.pshift,
-                       (const uint16_t*)a.px, (int)kGeoPlain);
+                       (const uint16_t*)a.px, geo);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<MODE, TW, TH, IMGS, BCO, WCO, NW, false, ZG, PRO>),
                        grid, block, 0, stream, src.p0, src.p1, src.c0, wt, bias, dst.p0, dst.p1,
@@ -1033,10 +1075,10 @@ bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const 
     return false;
   if (a.zsrc != nullptr && (pl.pass == kFwd || pro)) return false;
   if (pro && pl.pass == kBwdData && a.px == nullptr) return false;
-  // Resampling (scalar staging over the full-resolution grid): one source
-  // and one output tensor, float32 output, no split or fusion; backward-data
-  // of the upsampling call is composed by the caller (its full-resolution
-  // result summed over 2 x 2 blocks).
+  // Resampling (the stride-1 kernels over the full-resolution grid): one
+  // source and one output tensor, float32 output, no split or fusion;
+  // backward-data of the upsampling call is composed by the caller (its
+  // full-resolution result summed over 2 x 2 blocks).
   if ((a.up2 || a.s2) &&
       (src.c0 != Cin || dst.c0 != Cout || pl.split > 1 || out_bf16 || pro ||
        a.zsrc != nullptr || a.zout != nullptr || a.act != kActNone ||

@@ -34,7 +34,7 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 // (zsrc float32, g's shape) and rounded to bfloat16 as it is staged.
 // PRO: the input prologue -- x is staged as a = SiLU(x * pscale[n, c] +
 // pshift[n, c]) rounded to bfloat16 (one x tensor).
-template <int TW, int TH, int IMGS, bool VEC, bool ZG, bool PRO>
+template <int TW, int TH, int IMGS, bool VEC, bool ZG, bool PRO, int GEO = kGeoPlain>
 __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ x1, int cx0,
     const uint16_t* __restrict__ g, float* __restrict__ out, float* __restrict__ out_db, int N,
@@ -44,6 +44,13 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
     const float* __restrict__ pshift, int xgeo, int ggeo) {
   constexpr int P = IMGS * TH * TW;
   static_assert(P % 16 == 0, "whole 16-pixel MFMA steps");
+  // GEO: the vector path reads x as an H/2 x W/2 tensor at (h/2, w/2)
+  // (kGeoUp), or g as an H/2 x W/2 tensor zero-inserted (kGeoZero: only at
+  // even h, w); one x tensor, no fusion.  The scalar path takes its geometry
+  // from xgeo / ggeo.
+  static_assert(GEO == kGeoPlain || (VEC && !ZG && !PRO && (GEO == kGeoUp || GEO == kGeoZero)),
+                "resampled vector staging: plain operands only");
+  constexpr bool XUP = GEO == kGeoUp, GZI = GEO == kGeoZero;
   static_assert(TW % 8 == 0, "8-pixel operand runs must stay in one row");
   constexpr int GSB = wgrad_bf16_gstride(IMGS, TH, TW);
   constexpr int RSX = wgrad_bf16_rs(TW);
@@ -135,6 +142,14 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int kl = t / IMGS;
         const int n = o.n0 + img, kk = k0 + kl, h = o.h0 + row, w = o.w0 + 8 * q;
         const bool ok = (GI % NT == 0 || it < GI) && n < N && kk < K && h < H && w < W;
+        if constexpr (GZI) {
+          // 8 pixels of an even row: 4 source elements at (h/2, w/2)
+          const uint32_t e = (uint32_t)(((n * K + kk) * (H >> 1) + (h >> 1)) * (W >> 1) + (w >> 1));
+          const uint64_t u = buffer_load8(gview, ok && (h & 1) == 0 ? 2u * e : kOutside);
+          gv[SET][k].x = (uint32_t)u;
+          gv[SET][k].y = (uint32_t)(u >> 32);
+          continue;
+        }
         const uint32_t e = (uint32_t)(((n * K + kk) * H + h) * W + w);
         gv[SET][k] = buffer_load16(gview, ok ? 2u * e : kOutside);
         if constexpr (ZG) {
@@ -154,6 +169,16 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int cl = t / IMGS;
         const int n = o.n0 + img, h = o.h0 + rr - 1, w = o.w0 + 8 * q;
         const bool ok = (XI % NT == 0 || it < XI) && n < N && cl < cn && h >= 0 && h < H && w < W;
+        if constexpr (XUP) {
+          // 8 pixels of the upsampled row: 4 source elements at (h/2, w/2)
+          const uint64_t u = buffer_load8(
+              xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * (H >> 1) + (h >> 1)) * (W >> 1) +
+                                          (w >> 1))
+                        : kOutside);
+          xv[SET][k].x = (uint32_t)u;
+          xv[SET][k].y = (uint32_t)(u >> 32);
+          continue;
+        }
         xv[SET][k] = buffer_load16(
             xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w) : kOutside);
         if constexpr (PRO) {
@@ -177,8 +202,10 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
         const int w = o.w0 + (side ? TW : -1);
         const bool ok = (HI_ % NT == 0 || it < HI_) && n < N && cl < cn && h >= 0 && h < H &&
                         w >= 0 && w < W;
-        xh[SET][k] = (uint16_t)buffer_load2(
-            xview, ok ? 2u * (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w) : kOutside);
+        const uint32_t e = XUP ? (uint32_t)(((n * cs + cl0 + cl) * (H >> 1) + (h >> 1)) * (W >> 1) +
+                                            (w >> 1))
+                               : (uint32_t)(((n * cs + cl0 + cl) * H + h) * W + w);
+        xh[SET][k] = (uint16_t)buffer_load2(xview, ok ? 2u * e : kOutside);
         if constexpr (PRO) {
           const uint32_t po = ok ? 4u * (uint32_t)(n * C + c0 + cl) : kOutside;
           phs[SET][k] = __builtin_bit_cast(float, buffer_load4(psview, po));
@@ -201,6 +228,7 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int t = it / XQ;  // (cl * IMGS + img) * HR + rr
           const int cl = t / (IMGS * HR);
           u32x4 v = xv[SET][k];
+          if constexpr (XUP) v = bf16x4_repeat2(v.x, v.y);
           if constexpr (PRO) {
             // a = SiLU(x * scale + shift), rounded to bfloat16 (items outside
             // the image load x = scale = shift = 0: the zero padding of a)
@@ -250,7 +278,8 @@ __global__ __launch_bounds__(768) void wgrad_bf16_kernel(
           const int q = it % XQ;
           const int t = it / XQ;  // (kl * IMGS + img) * TH + row
           const int kl = t / (IMGS * TH);
-          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = gv[SET][k];
+          const u32x4 v = GZI ? bf16x4_zero_insert(gv[SET][k].x, gv[SET][k].y) : gv[SET][k];
+          *reinterpret_cast<u32x4*>(&gs[kl * GSB + (t % (IMGS * TH)) * TW + 8 * q]) = v;
         }
       }
     } else {
@@ -427,9 +456,29 @@ static void launch_wgrad_bf16_geom(const Plan& pl, bool vec, Split<const uint16_
   dim3 grid(pl.grid_x, 1, 1), block(pl.threads, 1, 1);
   const int tiles_c = (x.c0 + 63) / 64 + (C - x.c0 + 63) / 64;
   const long hw2 = (long)H * W * 2;
-  // resampling geometry (scalar path only)
+  // resampling geometry: x upsampled (read at (h/2, w/2)) or g zero-inserted
   const int xgeo = a.up2 ? kGeoUp : kGeoPlain, ggeo = a.s2 ? kGeoZero : kGeoPlain;
-  if (a.up2 || a.s2) vec = false;
+  if constexpr (!ZG && !PRO) {
+    if (vec && (a.up2 || a.s2)) {
+      // the resampled tensor is N x (C or K) x H/2 x W/2
+      const long q2 = hw2 / 4;
+      if (a.up2)
+        hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, false, false, kGeoUp>), grid,
+                           block, 0, stream, x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W,
+                           pl.tiles_w, pl.tiles_h, pl.nchunks, pl.chunks_per_split, slice_stride,
+                           pl.split, tiles_c, (K + 63) / 64, (uint32_t)(N * C * q2), 0u,
+                           (uint32_t)(N * K * hw2), a.act, a.zsrc, a.pscale, a.pshift,
+                           (int)kGeoPlain, (int)kGeoPlain);
+      else
+        hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, false, false, kGeoZero>), grid,
+                           block, 0, stream, x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W,
+                           pl.tiles_w, pl.tiles_h, pl.nchunks, pl.chunks_per_split, slice_stride,
+                           pl.split, tiles_c, (K + 63) / 64, (uint32_t)(N * C * hw2), 0u,
+                           (uint32_t)(N * K * q2), a.act, a.zsrc, a.pscale, a.pshift,
+                           (int)kGeoPlain, (int)kGeoPlain);
+      return;
+    }
+  }
   if (vec)
     hipLaunchKernelGGL((wgrad_bf16_kernel<TW, TH, IMGS, true, ZG, PRO>), grid, block, 0, stream,
                        x.p0, x.p1, x.c0, g, out, out_db, N, C, K, H, W, pl.tiles_w, pl.tiles_h,
@@ -451,7 +500,7 @@ bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const 
   // the prologue needs one x tensor and does not combine with a fused
   // activation gradient
   if (a.pscale != nullptr && (a.zsrc != nullptr || x.c0 != C)) return false;
-  // resampling (scalar staging over the full-resolution grid): one x
+  // resampling (the stride-1 kernel over the full-resolution grid): one x
   // tensor, no fusion, even sizes
   if ((a.up2 || a.s2) && (x.c0 != C || a.zsrc != nullptr || a.pscale != nullptr || (H & 1) ||
                           (W & 1)))

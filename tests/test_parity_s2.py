@@ -7,10 +7,11 @@ scalar one, output grids wider than one tile (the left halo column of the
 stride-2 x tile is loaded), ragged channel fills and tiles, several images
 per block, and g grids with odd sizes (every output-pixel parity class of
 backward-data gets a ragged edge).  bfloat16 inputs run the stride-1
-passes over the full-resolution grid through the scalar staging paths
-(the forward keeping the even pixels; backward-data and backward-weight
-reading g zero-inserted), to the bf16 trip-wire (1e-4; exact on integer
-inputs)."""
+passes over the full-resolution grid (the forward keeping the even pixels;
+backward-data and backward-weight reading g zero-inserted), through the
+vector staging paths where the full grid's width is a multiple of 8 and the
+channels fill whole 16-channel steps, the scalar ones elsewhere, to the
+bf16 trip-wire (1e-4; exact on integer inputs)."""
 import numpy as np
 import pytest
 import torch

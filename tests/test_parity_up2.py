@@ -8,10 +8,11 @@ tiles across -- the backward-data tile's right halo column --, odd heights,
 ragged channel fills and tiles, several images per block) and on a
 full-size up-path layer by sampled elements.  bfloat16 inputs run the
 stride-1 passes over the upsampled grid, the upsampled x read at half
-coordinates by the scalar staging paths and backward-data's upsampled-grid
-gradient summed over 2 x 2 blocks afterwards (through the workspace the
-binding sizes with conv3x3_up2_workspace_size); the bar is then the bf16
-trip-wire (1e-4), and integer inputs are exact."""
+coordinates as it is staged (four source elements spread over eight pixels
+by the vector paths, single elements by the scalar ones) and
+backward-data's upsampled-grid gradient summed over 2 x 2 blocks afterwards
+(through the workspace the binding sizes with conv3x3_up2_workspace_size);
+the bar is then the bf16 trip-wire (1e-4), and integer inputs are exact."""
 import numpy as np
 import pytest
 import torch
