@@ -845,6 +845,30 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     // epilogue is bound by their count, not by bytes).
     const bool pack = outb && (W & 1) == 0;
     const bool odd = l32 & 1;
+    if (plain && !outb) {
+      // float32 without an activation (also the split slices): a separate,
+      // branch-free loop nest.  Inside the general one below the run-time
+      // tests of plain / outb stay per element, with a wait on the stores
+      // at every merge (measured on 16x16 images, 512 channels: that
+      // epilogue took 15 us of a 77 us forward).
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int p = wpx * (BM / WPX) + j * 32 + l32;
+        const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+        const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+        const bool in = n < N && h < H && w < W;
+        const uint32_t e =
+            ((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w);
+        const uint32_t off = in ? e * 4u : kOutside;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * (uint32_t)HW * 4u,
+                          acc[i][j][v]);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int p = wpx * (BM / WPX) + j * 32 + l32;

@@ -751,32 +751,40 @@ __global__ __launch_bounds__(64 * NW) void fwd_f32_kernel(
     const __amdgpu_buffer_rsrc_t dv = buffer_view(od, od_bytes);
     const __amdgpu_buffer_rsrc_t zov = buffer_view(zout, plain ? 0u : od_bytes);
     const uint32_t plane = (uint32_t)HWo * 4u;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    auto lane_offset = [&](int j) -> uint32_t {
       const int p = wpx * (BM / WPX) + j * 32 + l32;
       const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
       const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
       const bool keep = n < N && h < OH && w < OW;
-      const uint32_t off =
-          keep ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HWo + (uint32_t)(h * OW + w)) * 4u
-               : kOutside;
-      if (plain) {
+      return keep ? (((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HWo + (uint32_t)(h * OW + w)) * 4u
+                  : kOutside;
+    };
+    // The plain stores are a loop nest of their own: with the run-time test
+    // inside the loop over j, every merge after it waits on the stores.
+    if (plain) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t off = lane_offset(j);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             buffer_store4(dv, off, (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane,
                           acc[i][j][v]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const uint32_t so = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane;
-            if (zout) buffer_store4(zov, off, so, acc[i][j][v]);
-            buffer_store4(dv, off, so, act_value(act, acc[i][j][v]));
-          }
       }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t off = lane_offset(j);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t so = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * plane;
+          if (zout) buffer_store4(zov, off, so, acc[i][j][v]);
+          buffer_store4(dv, off, so, act_value(act, acc[i][j][v]));
+        }
     }
     return;
   }
