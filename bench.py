@@ -896,9 +896,13 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0, metavar="MB",
                     help="also run a plain device-to-device copy of MB megabytes (a known "
                          "amount of HBM traffic for scaling profiler byte counters)")
+    ap.add_argument("--traffic-out", metavar="JSON",
+                    help="with --record-traffic: write the summary here instead of the "
+                         "headline workload's record")
     args = ap.parse_args()
     if args.record_traffic:
-        print(json.dumps(record_traffic(*args.record_traffic)["passes"]))
+        out = args.traffic_out or TRAFFIC_FILE
+        print(json.dumps(record_traffic(*args.record_traffic, out_path=out)["passes"]))
         return
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace), indent=1))

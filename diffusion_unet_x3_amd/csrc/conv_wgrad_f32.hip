@@ -602,8 +602,14 @@ void launch_wgrad_reduce(const float* ws, float* dw, float* db, int split, int C
                     (reinterpret_cast<uintptr_t>(ws) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(dw) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(db) & 15) == 0;
-  if (vec4) {
-    const long KC = (long)K * C;
+  // The 9-wave kernel gives each lane a chain of S slot loads over 256 (k, c)
+  // pairs per workgroup: with many slices and few workgroups (64 -> 64
+  // channels: 256 slices, 16 workgroups) it is latency-bound (23.8 us
+  // against 7.2 us for the 4-wave kernel, which spreads the slices over four
+  // waves and 64 outputs per workgroup).
+  const long KC = (long)K * C;
+  const bool deep = split > 64 && (KC + 255) / 256 < 128;
+  if (vec4 && !deep) {
     dim3 grid((unsigned)((KC + 255) / 256 + (db ? (K + 255) / 256 : 0))), block(576);
     hipLaunchKernelGGL(wgrad_reduce4_kernel, grid, block, 0, stream, ws, dw, db, split, C, K);
   } else {
