@@ -191,14 +191,19 @@ bool plan(const Problem& p, Plan* out) {
     // to three quarters of a round (measured: shorter reductions, a second
     // round of workgroups and split grids of half a round all lose to the
     // small tiles; 48- and 56-fill reductions on 16x16 images gain 10-16%).
+    // From 24 fills a split in two (12+ fills per slice) pays too: 384 -> 384
+    // channels at 16x16, N = 32: forward 45.6 -> 39.1 us, backward-data 40.7
+    // -> 38.2 us against the 128 x 64 tile; a split in three (8 fills per
+    // slice, 256 -> 384 backward-data) lost, 31.0 -> 33.2 us.
     int split = 1;
     const int cin = p.pass == kFwd ? p.C : p.K;
     const int fills = ceil_div(cin, p.dtype == kF32 ? 8 : 16);  // channels per fill
     if (p.allow_split && p.dtype == kBF16 && cout > 64 && wgs[0] > 0 && wgs[0] < kMinWGs &&
-        fills >= 32 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
+        fills >= 24 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
       int s = kMinWGs / wgs[0];
       if (s > fills / 8) s = fills / 8;
       if (s > 8) s = 8;
+      if (fills < 32 && s > 2) s = 2;
       if (s >= 2 && wgs[0] * s >= 3 * kMinWGs / 4) {
         pick = 0;
         split = s;
