@@ -200,8 +200,12 @@ bool plan(const Problem& p, Plan* out) {
     const int fills = ceil_div(cin, p.dtype == kF32 ? 8 : 16);  // channels per fill
     if (p.allow_split && p.dtype == kBF16 && cout > 64 && wgs[0] > 0 && wgs[0] < kMinWGs &&
         fills >= 24 && eff[0] >= 0.8 * best_eff && (cout0 < 0 || cout0 >= cout)) {
+      // (at least 4 fills per slice: the 512-channel 8x8 layers at N = 32,
+      // 32 big tiles split in eight, forward 35.8 -> 28.3 us, backward-data
+      // 28.9 -> 27.9 us against the 64 x 64 tile; at least 8 fills per
+      // slice before the forward epilogue became branch-free)
       int s = kMinWGs / wgs[0];
-      if (s > fills / 8) s = fills / 8;
+      if (s > fills / 4) s = fills / 4;
       if (s > 8) s = 8;
       if (fills < 32 && s > 2) s = 2;
       if (s >= 2 && wgs[0] * s >= 3 * kMinWGs / 4) {

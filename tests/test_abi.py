@@ -233,18 +233,24 @@ def test_prologue_argument_checks():
 
 
 def test_small_tile_split_rule():
-    """With a workspace: 64 x 64 tiles that make half a round to one round
-    of workgroups split a reduction of at least 32 fills, bf16 (fills of 16
-    channels) in two, float32 (fills of 8) in four."""
+    """With a workspace: bf16 32-image 8x8 layers with 512 channels split the
+    eight-wave 256 x 128 tile's 32 fills in eight (32 tiles -> 256
+    workgroups, 4 fills per slice); float32 64 x 64 tiles that make half a
+    round to one round of workgroups split a reduction of at least 32
+    fills (of 8 channels) in four."""
     bf16 = lib3.CONV3X3_BF16
     slot = 32 * 512 * 64 * 4  # one float32 output of a 32-image 8x8 layer with 512 channels
     for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
-        assert lib3.conv3x3_workspace_size(p, 32, 512, 512, 8, 8, bf16) == 2 * slot
-    # 384 input channels: a 24-fill forward reduction stays whole, its
-    # 32-fill backward-data (over 512 channels) splits
+        assert lib3.conv3x3_workspace_size(p, 32, 512, 512, 8, 8, bf16) == 8 * slot
+    # 384 input channels: a 24-fill forward reduction stays whole (a split
+    # in two of its 32 big tiles would leave 64 workgroups), its 32-fill
+    # backward-data (over 512 channels, 24 big tiles) splits in eight
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 384, 512, 8, 8, bf16) == 0
     assert lib3.conv3x3_workspace_size(lib3.PASS_BWD_DATA, 32, 384, 512, 8, 8, bf16) == \
-        2 * 32 * 384 * 64 * 4
+        8 * 32 * 384 * 64 * 4
+    # 16x16, 384 -> 384: 24 fills, 96 big tiles split in two
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 32, 384, 384, 16, 16, bf16) == \
+        2 * 32 * 384 * 256 * 4
     # a grid below half a round (4 images: 32 workgroups) is not split
     assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 512, 512, 8, 8, bf16) == 0
     f32 = lib3.CONV3X3_F32
