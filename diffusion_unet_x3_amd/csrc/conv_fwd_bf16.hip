@@ -869,6 +869,35 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       }
       return;
     }
+    if (plain && pack) {
+      // bfloat16 pairs without an activation: the same, with the lane-pair
+      // exchange below (as a separate loop nest for the same reason)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int p = wpx * (BM / WPX) + j * 32 + l32;
+        const int img = p / (TH * TW), row = (p / TW) % TH, col = p % TW;
+        const int n = o.n0 + img, h = o.h0 + row, w = o.w0 + col;
+        const bool in = n < N && h < H && w < W;
+        const uint32_t e =
+            ((uint32_t)n * ocs + cw + 4 * hi) * (uint32_t)HW + (uint32_t)(h * W + w);
+        const uint32_t poff =
+            in ? (e - (odd ? 1u : 0u) + (odd ? (uint32_t)HW : 0u)) * 2u : kOutside;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const uint32_t rowoff = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3)) * (uint32_t)HW;
+            const float a0 = acc[i][j][v], a1 = acc[i][j][v + 1];
+            const float got = __builtin_bit_cast(
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, odd ? a0 : a1), 0xB1,
+                                                0xF, 0xF, false));
+            const float lo = odd ? got : a0, hi2 = odd ? a1 : got;
+            buffer_store4(dv, poff, rowoff * 2u,
+                          __builtin_bit_cast(float, bf16_rne(lo) | (bf16_rne(hi2) << 16)));
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int p = wpx * (BM / WPX) + j * 32 + l32;
