@@ -311,8 +311,9 @@ int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* sh
  * With a workspace, a problem whose output tiles are too few to fill the
  * device splits its channel reduction over several workgroups per tile:
  *   - bfloat16, largest tile (256 pixels x 128 channels) short of a round of
- *     256 workgroups and at least 32 fills of 16 channels: 2 to 8 slices,
- *     as long as the split grid reaches 192 workgroups;
+ *     256 workgroups and at least 24 fills of 16 channels: 2 to 8 slices of
+ *     at least 4 fills (only 2 slices below 32 fills), as long as the split
+ *     grid reaches 192 workgroups;
  *   - either dtype, smallest tile (64 x 64) whose grid is 128 to 256
  *     workgroups, with at least 32 fills (16 channels bfloat16, 8 float32):
  *     2 slices (bfloat16) or 4 (float32).

@@ -18,11 +18,15 @@ pytestmark = pytest.mark.gpu
 # (N, C, K, H, W): few output tiles and a long reduction.  1032 channels
 # leave a partly filled last fill and a short last slice.
 # Shapes that take a split plan in forward and / or backward-data: 8x8 and
-# 16x16 images, 32 to 65 fills (1032 channels: a ragged last fill), split
-# grids of 192 and 256 workgroups.
+# 16x16 images, 24 to 65 fills (1032 channels: a ragged last fill), split
+# grids of 192 and 256 workgroups; 512 -> 512 at 8x8 splits in eight slices
+# of 4 fills, 520 channels in seven (five fills each, a last one of three),
+# 384 -> 384 at 16x16 its 24 fills in two, and 392 -> 384 only its
+# backward-data (a ragged last channel tile).
 SHAPES = [(32, 1024, 512, 8, 8), (24, 1032, 512, 8, 8), (24, 1024, 128, 16, 16),
           (48, 256, 1024, 8, 8), (32, 512, 384, 16, 16),
-          (32, 512, 512, 8, 8), (32, 384, 512, 8, 8)]
+          (32, 512, 512, 8, 8), (32, 384, 512, 8, 8), (32, 520, 512, 8, 8),
+          (32, 384, 384, 16, 16), (24, 392, 384, 16, 16)]
 
 
 def _run(inp, split, out_dtype=None):
@@ -85,8 +89,11 @@ def test_split_reduction_is_reproducible():
 # 65 fills, slices of 17, 17, 17 and 14; 384 -> 512: a 48-fill forward and a 64-fill
 # backward-data; 1024 -> 512: only the forward splits (backward-data has
 # 512 workgroups).
+# Beyond 8x8 tiles: 32x32 (32 x 2 tile) and 16x16 (16 x 4 tile) images with
+# 64 fills; 514 channels take the scalar staging path.
 F32_SHAPES = [(32, 512, 512, 8, 8), (24, 520, 512, 8, 8), (32, 384, 512, 8, 8),
-              (32, 1024, 512, 8, 8)]
+              (32, 1024, 512, 8, 8), (2, 512, 512, 32, 32), (8, 512, 512, 16, 16),
+              (24, 514, 512, 8, 8)]
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
