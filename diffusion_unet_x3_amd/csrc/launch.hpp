@@ -53,7 +53,8 @@ void launch_block_sum2(const float* du, float* dx, long planes, int H, int W,
 // (round to nearest even) when out_bf16 (dst then points to 16-bit values;
 // a.zout stays float32).  a.up2 (forward: x upsampled) and a.s2 (forward:
 // strided outputs; backward-data: g zero-inserted) run the plan's
-// full-resolution grid through the scalar staging path (Geo above).  pl.split > 1: the reduction is split over
+// full-resolution grid with the resampling modes (Geo above) in the vector
+// and the scalar staging paths.  pl.split > 1: the reduction is split over
 // pl.split workgroups per tile, their partial sums kept in ws (pl.split
 // float32 copies of the output) and added by a second kernel.
 bool launch_fwd_bf16(const Plan& pl, bool vec, Split<const uint16_t> src, const uint16_t* wt,
@@ -91,7 +92,8 @@ bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
                           hipStream_t stream);
 
 // Same, bfloat16 inputs; a.up2 stages x upsampled, a.s2 stages g
-// zero-inserted, over the plan's full-resolution grid (scalar path).
+// zero-inserted, over the plan's full-resolution grid (vector or scalar
+// staging).
 bool launch_wgrad_bf16(const Plan& pl, bool vec, Split<const uint16_t> x, const uint16_t* g,
                        float* dw,
                        float* db, float* ws, int N, int C, int K, int H, int W, const ActArgs& a,
