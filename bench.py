@@ -44,11 +44,13 @@ PASSES = ("fwd", "bwd_data", "bwd_weight")
 # backward-data) or wgrad_reduce*_kernel (backward-weight split-K); profile
 # summaries count it toward the pass whose main kernel precedes it.
 MAIN_KERNELS = {("f32", "fwd"): ("conv3x3::fwd_f32_kernel<0,",),
-                ("f32", "bwd_data"): ("conv3x3::fwd_f32_kernel<1,",),
+                ("f32", "bwd_data"): ("conv3x3::fwd_f32_kernel<1,",
+                                      "conv3x3::bwd_data_stem_kernel<float,"),
                 ("f32", "bwd_weight"): ("conv3x3::wgrad_f32_kernel<",
                                         "conv3x3::wgrad_stem_kernel<float,"),
                 ("bf16", "fwd"): ("conv3x3::fwd_bf16_kernel<0,", "conv3x3::fwd_stem_bf16_kernel<"),
-                ("bf16", "bwd_data"): ("conv3x3::fwd_bf16_kernel<1,",),
+                ("bf16", "bwd_data"): ("conv3x3::fwd_bf16_kernel<1,",
+                                       "conv3x3::bwd_data_stem_kernel<unsigned short,"),
                 ("bf16", "bwd_weight"): ("conv3x3::wgrad_bf16_kernel<",
                                          "conv3x3::wgrad_stem_kernel<unsigned short,")}
 REDUCE_KERNELS = ("conv3x3::split_reduce_kernel", "conv3x3::wgrad_reduce",

@@ -236,12 +236,27 @@ int bwd_data_impl(const void* g, const float* z, const void* w, Split<float> dx,
   pb.stride2 = fgeo && geom == 1;
   pb.allow_split = ws_call && aligned16(dx.p0) && act == CONV3X3_ACT_NONE && !pr.on() && !geom;
   pb.four_waves = dtype != CONV3X3_F32 && (act != CONV3X3_ACT_NONE || pr.on());
+  // (at most three dx channels in one tensor, no fusion: the (channel,
+  // tap)-row kernel; g through a 32-bit buffer view)
+  pb.stem = dx.c0 == C && geom == 0 && act == CONV3X3_ACT_NONE && !pr.on() &&
+            stem_bwd_data_fits(C, K, W) &&
+            (long)N * K * H * W * (dtype == CONV3X3_F32 ? 4 : 2) < 2147483648L;
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_SHAPE;
   if (pl.workspace_bytes > 0 && (!ws || ws_bytes < pl.workspace_bytes))
     return CONV3X3_ERR_WORKSPACE;
   if (pl.workspace_bytes > 0 && (ws == g || ws == w || is_part(dx, ws)))
     return CONV3X3_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (pl.stem) {
+    const bool ok =
+        dtype == CONV3X3_F32
+            ? launch_bwd_data_stem_f32(pl, (const float*)g, (const float*)w, dx.p0, N, C, K, H, W,
+                                       s)
+            : launch_bwd_data_stem_bf16(pl, (const uint16_t*)g, (const uint16_t*)w, dx.p0, N, C,
+                                        K, H, W, dtype == CONV3X3_BF16_IO, s);
+    if (!ok) return CONV3X3_ERR_BAD_SHAPE;
+    return launch_status();
+  }
   ActArgs a;
   if (act != CONV3X3_ACT_NONE) {
     a.act = act;
@@ -385,9 +400,12 @@ int plan_impl(int pass, int N, int C, int K, int H, int W, int dtype, int C0,
   Problem pb{pass, kdt(dtype), N, C, K, H, W, C0};
   // the plan of the plain call (a fused pass with a few-channel input runs
   // the general kernels; a backward-weight's workspace size is the same)
-  pb.stem = (pass == CONV3X3_PASS_BWD_WEIGHT ||
-             (pass == CONV3X3_PASS_FWD && dtype == CONV3X3_BF16)) &&
-            C <= 4 && (C0 < 0 || C0 == C);
+  pb.stem = ((pass == CONV3X3_PASS_BWD_WEIGHT ||
+              (pass == CONV3X3_PASS_FWD && dtype == CONV3X3_BF16)) &&
+             C <= 4 && (C0 < 0 || C0 == C)) ||
+            (pass == CONV3X3_PASS_BWD_DATA && (C0 < 0 || C0 == C) &&
+             stem_bwd_data_fits(C, K, W) &&
+             (long)N * K * H * W * (dtype == CONV3X3_F32 ? 4 : 2) < 2147483648L);
   if (!plan(pb, &pl)) return CONV3X3_ERR_BAD_PASS;
   rc = fill_plan(pl, pass, out);
   out->dtype = dtype;

@@ -675,6 +675,167 @@ bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Backward-data of a 3x3 convolution whose input has at most three channels
+// (a UNet's first convolution on an RGB image):
+//   dx[c, i, j] = sum over k, (r, s) of g[k, i + 1 - r, j + 1 - s] w[k, c, r, s].
+// The general backward-data kernel tiles 64 output channels, 61 of them
+// zero here.  Instead the (channel, tap) pairs m = 9 c + 3 r + s are the
+// rows of a GEMM: P[m, p] = sum_k w[k, m] g[k, p] for every pixel p of a
+// band of th + 2 image rows (the band's th output rows and one row above
+// and below), 27 of 32 MFMA rows, 32-pixel columns, the reduction over k.
+// v_mfma_f32_32x32x2_f32: lane l supplies B = g[k][p], k = 2 i + l / 32 and
+// p = l % 32 of a 32-pixel block, one float (or widened bfloat16) per lane,
+// so a wave's load reads two 32-pixel runs of two g planes and g streams
+// from HBM once with no transpose; A = w[k][m] is read from w^T staged in
+// LDS.  P goes to LDS, and each thread then adds the nine shifted taps of an
+// output pixel per channel, in a fixed order.  Eight waves take the bands'
+// 32-pixel blocks in turn, each loading its next block's operands while the
+// MFMAs of the current one run.
+template <typename T>
+__device__ __forceinline__ float load_widen(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  if constexpr (std::is_same<T, float>::value)
+    return __builtin_bit_cast(float, buffer_load4(v, off));
+  else
+    return __builtin_bit_cast(float, buffer_load2(v, off) << 16);
+}
+
+// KS: MFMA steps (two k each) of the sweep, K <= 2 KS.
+template <typename T, int KS>
+__global__ __launch_bounds__(512) void bwd_data_stem_kernel(
+    const T* __restrict__ g, const T* __restrict__ w, float* __restrict__ dx, int N, int C,
+    int K, int H, int W, int th, int bands, uint32_t g_bytes, int outb) {
+  static_assert(2 * KS <= kStemBdMaxK, "w^T fits its LDS rows");
+  __shared__ float ps[27 * kStemBdPx];  // P[m][band pixel]
+  __shared__ float wt[kStemBdMaxK * 32];  // w^T: row k, column m (zero past 9C and K)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int n = blockIdx.x / bands, h0 = (blockIdx.x % bands) * th;
+  const int nc = 9 * C;
+  for (int e = tid; e < 2 * KS * 32; e += 512) {
+    const int k = e >> 5, m = e & 31;
+    wt[e] = (k < K && m < nc) ? widen(w[(long)k * nc + m]) : 0.f;
+  }
+  __syncthreads();
+  const int px = (th + 2) * W;  // band pixels, rows h0 - 1 .. h0 + th
+  const int nblk = (px + 31) / 32;
+  const long hw = (long)H * W;
+  const __amdgpu_buffer_rsrc_t gv = buffer_view(g, g_bytes);
+  // A operands: this lane's column of w^T, the same for every block
+  float wa[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i) wa[i] = wt[(2 * i + hi) * 32 + l32];
+  // B operands, two register sets that take the wave's blocks in turn.  A
+  // block's KS steps form four quarters; loads run three quarters ahead of
+  // the MFMAs (into the other set across a block boundary), so each wait
+  // names loads issued three quarters earlier and leaves at most 3 KS / 4
+  // younger ones in flight, within what a wait counter can name.  Rows
+  // outside the image, pixels past the band (also blocks past the last)
+  // and k >= K read zero.
+  constexpr int QS = KS / 4;
+  float ba[KS], bb[KS];
+  auto load_q = [&](float(&dst)[KS], int blk, int qi) __attribute__((always_inline)) {
+    const int q = blk * 32 + l32;
+    const int row = h0 - 1 + q / W, col = q % W;
+    const bool in = q < px && row >= 0 && row < H;
+    const uint32_t e0 = in ? (uint32_t)(((long)n * K + hi) * hw + (long)row * W + col) : 0u;
+#pragma unroll
+    for (int i = qi * QS; i < (qi + 1) * QS; ++i)
+      dst[i] = load_widen<T>(gv, in & (2 * i + hi < K)
+                                     ? (e0 + (uint32_t)(2 * i) * (uint32_t)hw) * (uint32_t)sizeof(T)
+                                     : kOutside);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mfma_q = [&](f32x16& acc, const float(&src)[KS], int qi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = qi * QS; i < (qi + 1) * QS; ++i) acc = mfma_32x32x2_f32(wa[i], src[i], acc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // one block (its first three quarters already requested), then P to LDS
+  auto step = [&](int blk, float(&cur)[KS], float(&nxt)[KS]) __attribute__((always_inline)) {
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    load_q(cur, blk, 3);
+    mfma_q(acc, cur, 0);
+    load_q(nxt, blk + 8, 0);
+    mfma_q(acc, cur, 1);
+    load_q(nxt, blk + 8, 1);
+    mfma_q(acc, cur, 2);
+    load_q(nxt, blk + 8, 2);
+    mfma_q(acc, cur, 3);
+    const int q = blk * 32 + l32;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = acc_row(v, hi);
+      if (m < 27) ps[m * kStemBdPx + q] = acc[v];
+    }
+  };
+  // (the block index is wave-uniform, so the loop carries no exec masks)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  load_q(ba, wv, 0);
+  load_q(ba, wv, 1);
+  load_q(ba, wv, 2);
+  for (int blk = wv; blk < nblk; blk += 16) {
+    step(blk, ba, bb);
+    if (blk + 8 >= nblk) break;
+    step(blk + 8, bb, ba);
+  }
+  __syncthreads();
+  for (int o = tid; o < th * W; o += 512) {
+    const int lr = o / W, j = o % W, i = h0 + lr;
+    if (i >= H) continue;
+    for (int c = 0; c < C; ++c) {
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          // g pixel (i + 1 - r, j + 1 - t): band row lr + 2 - r; columns
+          // outside the image add nothing
+          const int pc = j + 1 - t;
+          const bool ok = pc >= 0 && pc < W;
+          const float v = ps[(c * 9 + r * 3 + t) * kStemBdPx + (lr + 2 - r) * W + (ok ? pc : j)];
+          sum += ok ? v : 0.f;
+        }
+      const long e = (((long)n * C + c) * H + i) * W + j;
+      if (outb)
+        reinterpret_cast<uint16_t*>(dx)[e] = (uint16_t)bf16_rne(sum);
+      else
+        dx[e] = sum;
+    }
+  }
+}
+
+template <typename T>
+static bool launch_bd_stem(const Plan& pl, const T* g, const T* w, float* dx, int N, int C,
+                           int K, int H, int W, bool outb, hipStream_t stream) {
+  if (!pl.stem || C > 3 || K > kStemBdMaxK || pl.th != stem_bd_rows(W) || pl.th < 1 ||
+      pl.threads != 512)
+    return false;
+  const int bands = (H + pl.th - 1) / pl.th;
+  const uint32_t gb = (uint32_t)((long)N * K * H * W * (long)sizeof(T));
+  dim3 grid((unsigned)(N * bands)), block(512);
+  if (K <= 64)
+    hipLaunchKernelGGL((bwd_data_stem_kernel<T, 32>), grid, block, 0, stream, g, w, dx, N, C, K,
+                       H, W, pl.th, bands, gb, outb ? 1 : 0);
+  else
+    hipLaunchKernelGGL((bwd_data_stem_kernel<T, 64>), grid, block, 0, stream, g, w, dx, N, C, K,
+                       H, W, pl.th, bands, gb, outb ? 1 : 0);
+  return true;
+}
+
+bool launch_bwd_data_stem_f32(const Plan& pl, const float* g, const float* w, float* dx, int N,
+                              int C, int K, int H, int W, hipStream_t stream) {
+  return launch_bd_stem<float>(pl, g, w, dx, N, C, K, H, W, false, stream);
+}
+
+bool launch_bwd_data_stem_bf16(const Plan& pl, const uint16_t* g, const uint16_t* w, float* dx,
+                               int N, int C, int K, int H, int W, bool outb,
+                               hipStream_t stream) {
+  return launch_bd_stem<uint16_t>(pl, g, w, dx, N, C, K, H, W, outb, stream);
+}
+
 bool launch_wgrad_stem_f32(const Plan& pl, bool vec, const float* x, const float* g, float* dw,
                            float* db, float* ws, int N, int C, int K, int H, int W,
                            hipStream_t stream) {

@@ -91,6 +91,16 @@ bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
                           const float* bias, float* y, int N, int C, int K, int H, int W,
                           hipStream_t stream);
 
+// Backward-data with at most three dx channels (plan.stem): P = w^T g per
+// band of image rows on MFMA, then the nine shifted taps summed per pixel.
+// g through a 32-bit buffer view (N*K*H*W elements below 2 GiB).  bfloat16:
+// dx float32, or bfloat16 (nearest even) when outb.
+bool launch_bwd_data_stem_f32(const Plan& pl, const float* g, const float* w, float* dx, int N,
+                              int C, int K, int H, int W, hipStream_t stream);
+bool launch_bwd_data_stem_bf16(const Plan& pl, const uint16_t* g, const uint16_t* w, float* dx,
+                               int N, int C, int K, int H, int W, bool outb,
+                               hipStream_t stream);
+
 // Same, bfloat16 inputs; a.up2 stages x upsampled, a.s2 stages g
 // zero-inserted, over the plan's full-resolution grid (vector or scalar
 // staging).

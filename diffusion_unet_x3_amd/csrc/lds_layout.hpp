@@ -173,6 +173,18 @@ CONV3X3_HD constexpr int stem_slot_columns(int C) { return 32 * ((9 * C + 1 + 31
 // 128-pixel tiles (tw x th); two buffers of the x tile: [c][XP] floats (the
 // planes as above, th + 2 rows of XR, bfloat16 widened), then a plane of
 // zeros.
+// ---- backward-data, at most three output channels ----
+// P, the (channel, tap)-row sums of a band of th + 2 image rows, is kept in
+// LDS for at most kStemBdPx pixels; w^T for at most kStemBdMaxK channels.
+constexpr int kStemBdMaxK = 128;
+constexpr int kStemBdPx = 640;
+// Output rows per band: 8, fewer for rows wider than 64 pixels (0: a row
+// too wide for the band's LDS).
+CONV3X3_HD constexpr int stem_bd_rows(int w) {
+  return w < 1 || kStemBdPx / w < 3 ? 0 : (kStemBdPx / w - 2 < 8 ? kStemBdPx / w - 2 : 8);
+}
+CONV3X3_HD constexpr int stem_bd_lds_bytes() { return 4 * (27 * kStemBdPx + kStemBdMaxK * 32); }
+
 constexpr int kStemFwdPix = 128;
 constexpr int kStemFwdCo = 64;  // output channels per workgroup
 CONV3X3_HD constexpr int stem_fwd_x_floats(int th, int tw, int c) {

@@ -90,10 +90,37 @@ size_t wgrad_workspace_bytes(const Plan& pl, int C, int K) {
   return (size_t)pl.split * ((size_t)K * C * 9 + (size_t)K) * sizeof(float);
 }
 
+bool stem_bwd_data_fits(int C, int K, int W) {
+  return C >= 1 && C <= 3 && K >= 1 && K <= kStemBdMaxK && stem_bd_rows(W) >= 1;
+}
+
 bool plan(const Problem& p, Plan* out) {
   Plan pl;
   pl.pass = p.pass;
   pl.dtype = p.dtype;
+  if (p.pass == kBwdData && p.stem) {
+    // At most three output channels: the (channel, tap)-row backward-data,
+    // one workgroup per band of th output rows of one image.
+    if (!stem_bwd_data_fits(p.C, p.K, p.W)) return false;
+    pl.tw = p.W;
+    pl.th = stem_bd_rows(p.W);
+    pl.imgs = 1;
+    pl.tile_co = p.C;
+    pl.wave_co = 1;
+    pl.chunk = p.K;
+    pl.threads = 512;
+    pl.tiles_w = 1;
+    pl.tiles_h = ceil_div(p.H, pl.th);
+    pl.tiles_n = p.N;
+    pl.grid_x = p.N * pl.tiles_h;
+    pl.grid_y = 1;
+    pl.grid_z = 1;
+    pl.split = 1;
+    pl.stem = 1;
+    pl.lds_bytes = stem_bd_lds_bytes();
+    *out = pl;
+    return true;
+  }
   if (p.pass == kFwd && p.stem && p.dtype == kBF16) {
     // At most four input channels (bfloat16): the packed-pair forward -- 64
     // output channels x 128-pixel tiles (tw x th, tw the narrowest power of

@@ -38,7 +38,8 @@ struct Plan {
   int chunks_per_split = 0;
   int nchunks = 0;
   int vec = 0;            // 1: 128-bit global paths allowed (decided at launch; 0 here)
-  int stem = 0;           // fwd / bwd_weight: the packed-pair kernel (at most four input channels)
+  int stem = 0;           // fwd / bwd_weight: the packed-pair kernel (at most four input
+                          // channels); bwd_data: the (channel, tap)-row kernel (at most three)
   size_t workspace_bytes = 0;
 };
 
@@ -71,11 +72,18 @@ struct Problem {
   // backward-weight without fusion (512 threads, 128 k x all (c, tap) pairs
   // per workgroup, 64-pixel chunks), bfloat16 forward without fusion and
   // with float32 outputs (256 threads, 64 output channels x 128-pixel
-  // tiles, persistent)
+  // tiles, persistent); at most three output channels: the (channel,
+  // tap)-row backward-data (512 threads, one band of image rows per
+  // workgroup; see stem_bwd_data_fits)
   bool stem = false;
 };
 
 bool plan(const Problem& p, Plan* out);
+
+// Whether the (channel, tap)-row backward-data takes a problem: at most three
+// dx channels, at most 128 g channels, and image rows narrow enough for a
+// band of at least one output row in LDS (at most 213 pixels).
+bool stem_bwd_data_fits(int C, int K, int W);
 
 // Minimum workspace bytes for a bwd_weight plan.
 size_t wgrad_workspace_bytes(const Plan& pl, int C, int K);

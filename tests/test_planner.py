@@ -94,3 +94,23 @@ def test_wide_parity_shapes_span_several_tiles(shape, dtype):
     for pass_ in (lib3.PASS_FWD, lib3.PASS_BWD_DATA, lib3.PASS_BWD_WEIGHT):
         p = lib3.conv3x3_plan(pass_, N, C, K, H, W, dtype)
         assert math.ceil(W / p["tile_w"]) > 1
+
+
+@pytest.mark.parametrize("dtype", [lib3.CONV3X3_F32, lib3.CONV3X3_BF16])
+def test_few_channel_backward_data_plans(dtype):
+    """At most three dx channels and 128 g channels: one 512-thread
+    workgroup per band of output rows (8, fewer for rows wider than 64
+    pixels) whose band plus one halo row above and below fits 640 pixels;
+    rows of 214+ pixels, 129 g channels and four dx channels take the
+    general kernel."""
+    bd = lib3.PASS_BWD_DATA
+    p = lib3.conv3x3_plan(bd, 32, 3, 128, 64, 64, dtype)
+    assert (p["tile_m"], p["threads"], p["tile_h"], p["tile_w"]) == (3, 512, 8, 64)
+    assert p["grid_x"] == 32 * 8 and p["split"] == 1 and p["workspace_bytes"] == 0
+    for W, th in ((1, 8), (64, 8), (65, 7), (100, 4), (200, 1), (213, 1)):
+        p = lib3.conv3x3_plan(bd, 2, 2, 16, 13, W, dtype)
+        assert p["tile_m"] == 2 and p["tile_h"] == th, (W, p)
+        assert (th + 2) * W <= 640
+        assert p["grid_x"] == 2 * math.ceil(13 / th)
+    for shape in ((2, 3, 16, 13, 214), (2, 3, 129, 8, 8), (2, 4, 16, 8, 8)):
+        assert lib3.conv3x3_plan(bd, *shape, dtype)["tile_m"] >= 64, shape
