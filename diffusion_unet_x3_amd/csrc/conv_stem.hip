@@ -684,23 +684,16 @@ bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
 // rows of a GEMM: P[m, p] = sum_k w[k, m] g[k, p] for every pixel p of a
 // band of th + 2 image rows (the band's th output rows and one row above
 // and below), 27 of 32 MFMA rows, 32-pixel columns, the reduction over k.
-// v_mfma_f32_32x32x2_f32: lane l supplies B = g[k][p], k = 2 i + l / 32 and
-// p = l % 32 of a 32-pixel block, one float (or widened bfloat16) per lane,
-// so a wave's load reads two 32-pixel runs of two g planes and g streams
-// from HBM once with no transpose; A = w[k][m] is read from w^T staged in
-// LDS.  P goes to LDS, and each thread then adds the nine shifted taps of an
+// Lane l supplies B = g[k][p] for p = l % 32 of a 32-pixel block, one
+// element per load, so a wave's load reads two 32-pixel runs of two g
+// planes and g streams from HBM once with no transpose; A = w[k][m] comes
+// from w^T staged in LDS and is held in registers.  float32 runs
+// v_mfma_f32_32x32x2_f32, bfloat16 v_mfma_f32_32x32x16_bf16 (eight times
+// fewer MFMA cycles for the same loads).  P goes to LDS, and each thread then adds the nine shifted taps of an
 // output pixel per channel, in a fixed order.  Eight waves take the bands'
 // 32-pixel blocks in turn, each loading its next block's operands while the
 // MFMAs of the current one run.
-template <typename T>
-__device__ __forceinline__ float load_widen(__amdgpu_buffer_rsrc_t v, uint32_t off) {
-  if constexpr (std::is_same<T, float>::value)
-    return __builtin_bit_cast(float, buffer_load4(v, off));
-  else
-    return __builtin_bit_cast(float, buffer_load2(v, off) << 16);
-}
-
-// KS: MFMA steps (two k each) of the sweep, K <= 2 KS.
+// KS: g values a lane loads per 32-pixel block, K <= 2 KS.
 template <typename T, int KS>
 __global__ __launch_bounds__(512) void bwd_data_stem_kernel(
     const T* __restrict__ g, const T* __restrict__ w, float* __restrict__ dx, int N, int C,
@@ -721,38 +714,76 @@ __global__ __launch_bounds__(512) void bwd_data_stem_kernel(
   const int nblk = (px + 31) / 32;
   const long hw = (long)H * W;
   const __amdgpu_buffer_rsrc_t gv = buffer_view(g, g_bytes);
-  // A operands: this lane's column of w^T, the same for every block
-  float wa[KS];
+  // bfloat16 runs v_mfma_f32_32x32x16_bf16 (products exact in float32, so
+  // the same sums as float32 operands up to the order of additions): lane
+  // (l32, hi) of step s supplies k = 16 s + 8 hi + j, j = 0..7, packed in
+  // pairs.  float32 runs v_mfma_f32_32x32x2_f32: step i supplies
+  // k = 2 i + hi.  Either way a lane loads KS values of g per block.
+  constexpr bool BF = std::is_same<T, uint16_t>::value;
+  constexpr int NS = BF ? KS / 8 : KS;  // MFMA steps per block
+  using E = typename std::conditional<BF, uint32_t, float>::type;
+  // A operands: this lane's column of w^T, the same for every block (the
+  // staged w^T holds rows 0 .. 2 KS - 1, zero from K on)
+  float wa[BF ? 1 : KS];
+  u32x4 wb[BF ? NS : 1];
+  if constexpr (BF) {
 #pragma unroll
-  for (int i = 0; i < KS; ++i) wa[i] = wt[(2 * i + hi) * 32 + l32];
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int k = 16 * st + 8 * hi + 2 * d;
+        // (staged values are bfloat16 widened: the high halves are exact)
+        wb[st][d] = (__builtin_bit_cast(uint32_t, wt[k * 32 + l32]) >> 16) |
+                    (__builtin_bit_cast(uint32_t, wt[(k + 1) * 32 + l32]) & 0xffff0000u);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) wa[i] = wt[(2 * i + hi) * 32 + l32];
+  }
   // B operands, two register sets that take the wave's blocks in turn.  A
-  // block's KS steps form four quarters; loads run three quarters ahead of
+  // block's KS loads form four quarters; loads run three quarters ahead of
   // the MFMAs (into the other set across a block boundary), so each wait
   // names loads issued three quarters earlier and leaves at most 3 KS / 4
   // younger ones in flight, within what a wait counter can name.  Rows
   // outside the image, pixels past the band (also blocks past the last)
   // and k >= K read zero.
   constexpr int QS = KS / 4;
-  float ba[KS], bb[KS];
-  auto load_q = [&](float(&dst)[KS], int blk, int qi) __attribute__((always_inline)) {
+  static_assert(!BF || QS % 8 == 0, "a quarter holds whole bf16 steps");
+  E ba[KS], bb[KS];
+  auto load_q = [&](E(&dst)[KS], int blk, int qi) __attribute__((always_inline)) {
     const int q = blk * 32 + l32;
     const int row = h0 - 1 + q / W, col = q % W;
     const bool in = q < px && row >= 0 && row < H;
-    const uint32_t e0 = in ? (uint32_t)(((long)n * K + hi) * hw + (long)row * W + col) : 0u;
+    const uint32_t e0 = in ? (uint32_t)((long)n * K * hw + (long)row * W + col) : 0u;
 #pragma unroll
-    for (int i = qi * QS; i < (qi + 1) * QS; ++i)
-      dst[i] = load_widen<T>(gv, in & (2 * i + hi < K)
-                                     ? (e0 + (uint32_t)(2 * i) * (uint32_t)hw) * (uint32_t)sizeof(T)
-                                     : kOutside);
+    for (int i = qi * QS; i < (qi + 1) * QS; ++i) {
+      const int k = BF ? 16 * (i >> 3) + 8 * hi + (i & 7) : 2 * i + hi;
+      const uint32_t off =
+          in & (k < K) ? (e0 + (uint32_t)k * (uint32_t)hw) * (uint32_t)sizeof(T) : kOutside;
+      if constexpr (BF)
+        dst[i] = buffer_load2(gv, off);
+      else
+        dst[i] = __builtin_bit_cast(float, buffer_load4(gv, off));
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto mfma_q = [&](f32x16& acc, const float(&src)[KS], int qi) __attribute__((always_inline)) {
+  auto mfma_q = [&](f32x16& acc, const E(&src)[KS], int qi) __attribute__((always_inline)) {
+    if constexpr (BF) {
 #pragma unroll
-    for (int i = qi * QS; i < (qi + 1) * QS; ++i) acc = mfma_32x32x2_f32(wa[i], src[i], acc);
+      for (int st = qi * QS / 8; st < (qi + 1) * QS / 8; ++st) {
+        u32x4 bw;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) bw[d] = src[8 * st + 2 * d] | (src[8 * st + 2 * d + 1] << 16);
+        acc = mfma_32x32x16_bf16(wb[st], bw, acc);
+      }
+    } else {
+#pragma unroll
+      for (int i = qi * QS; i < (qi + 1) * QS; ++i) acc = mfma_32x32x2_f32(wa[i], src[i], acc);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   // one block (its first three quarters already requested), then P to LDS
-  auto step = [&](int blk, float(&cur)[KS], float(&nxt)[KS]) __attribute__((always_inline)) {
+  auto step = [&](int blk, E(&cur)[KS], E(&nxt)[KS]) __attribute__((always_inline)) {
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
