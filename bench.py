@@ -22,7 +22,7 @@ baseline; its full-sweep time is extrapolated from the sample).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--workload unet_sweep|stem|small|mid|bottleneck]
-                    [--sweep OUT.json] [--cold] [--detail OUT.json]
+                    [--sweep OUT.json] [--cold] [--graph] [--detail OUT.json]
 """
 import argparse
 import json
@@ -597,6 +597,56 @@ def time_runs(runs, steps, warmup, flush=None):
     return t0.elapsed_time(t1) / steps, per
 
 
+def time_runs_graph(runs, steps, warmup):
+    """As time_runs, with the passes replayed from HIP graphs captured once
+    after the warmup (what a caller with launch-bound layers would do):
+    each pass's own graph between its event pair for the per-pass times,
+    and one graph holding the whole step, replayed `steps` times between
+    one event pair, for the step time.  Every input, output and workspace
+    is allocated before the capture."""
+    import torch
+    for _ in range(warmup):
+        for run in runs:
+            for _, f in run.passes():
+                f()
+    torch.cuda.synchronize()
+    graphs = []
+    for run in runs:
+        for name, f in run.passes():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            graphs.append((run, name, g))
+    step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step):
+        for run in runs:
+            for _, f in run.passes():
+                f()
+    for _ in range(max(warmup, 1)):
+        step.replay()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in graphs] for _ in range(steps)]
+    for i in range(steps):
+        for j, (_, _, g) in enumerate(graphs):
+            ev[i][j][0].record()
+            g.replay()
+            ev[i][j][1].record()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    per = []
+    for run in runs:
+        per.append({name: [ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]
+                    for j, (r, name, _) in enumerate(graphs) if r is run})
+    return t0.elapsed_time(t1) / steps, per
+
+
 def time_layer(run, steps, warmup):
     """Per-pass average ms and per-step ms of one run."""
     ms, per = time_runs([run], steps, warmup)
@@ -706,13 +756,17 @@ def cpu_baseline(layer, budget_s=15.0, min_s=10.0):
                       f"cpu: {cpu_model()}"}
 
 
-def measure_layers(layers, dtype, inputs, steps, warmup, flush=None, act="none"):
+def measure_layers(layers, dtype, inputs, steps, warmup, flush=None, act="none", graph=False):
     """Time the three passes of every layer (one step = all of them, in
     order).  Returns (step ms, per-layer rows with per-pass statistics,
-    per-pass totals).  act: the *_act entry points (fused activation)."""
+    per-pass totals).  act: the *_act entry points (fused activation).
+    graph: replay the passes from HIP graphs."""
     import torch
     runs = [LayerRun(layer, act, inputs=inputs[layer.name]) for layer in layers]
-    ms, per = time_runs(runs, steps, warmup, flush)
+    if graph:
+        ms, per = time_runs_graph(runs, steps, warmup)
+    else:
+        ms, per = time_runs(runs, steps, warmup, flush)
     del runs
     torch.cuda.empty_cache()
     rows, fam = [], {p: {"ms": 0.0, "gflop": 0.0, "alg_gb": 0.0} for p in PASSES}
@@ -846,6 +900,9 @@ def main():
                     help="unet_sweep: the 32 convolutions of a 64x64 UNet training step, "
                          "float32 (bfloat16 in an extra key); the others time one "
                          "configured layer group")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the passes in HIP graphs and time their replays "
+                         "(for launch-bound layers)")
     ap.add_argument("--no-bf16", action="store_true",
                     help="unet_sweep: skip the bfloat16 sweep")
     ap.add_argument("--cold", action="store_true",
@@ -902,6 +959,8 @@ def main():
                     help="with --record-traffic: write the summary here instead of the "
                          "headline workload's record")
     args = ap.parse_args()
+    if args.graph and args.cold:
+        ap.error("--graph replays whole passes: no cache flush between them (drop --cold)")
     if args.record_traffic:
         out = args.traffic_out or TRAFFIC_FILE
         print(json.dumps(record_traffic(*args.record_traffic, out_path=out)["passes"]))
@@ -939,7 +998,7 @@ def main():
           f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     flush = torch.empty(512 << 18, device="cuda") if args.cold else None
     ms, rows, fam = measure_layers(layers, dtype, inputs, args.steps, args.warmup, flush,
-                                   args.act)
+                                   args.act, args.graph)
     summ = sweep_summary(dtype, layers, ms, fam, args.act)
     if args.cold:
         # the step bracket holds the flushes too: the step is the passes' sum
@@ -962,7 +1021,8 @@ def main():
               "global_batch": layers[0].N, "parallelism": "single_gpu",
               "timing": "HIP events on the kernels' stream; inputs resident in HBM; "
                         + ("512 MiB overwritten before every pass (cold caches)"
-                           if args.cold else "passes back to back in sweep order")}
+                           if args.cold else "passes back to back in sweep order")
+                        + ("; every step replayed from one HIP graph" if args.graph else "")}
     if cfg == 6:
         config["shapes"] = [list(l.shape) for l in layers]
     elif cfg == 5:
@@ -988,7 +1048,7 @@ def main():
             binputs[l.name] = {"x": src["x"].bfloat16(), "w": src["w"].bfloat16(),
                                "b": src["b"], "g": src["g"].bfloat16()}
         bms, brows, bfam = measure_layers(blayers, "bf16", binputs, args.steps, args.warmup,
-                                          flush, args.act)
+                                          flush, args.act, args.graph)
         bsum = sweep_summary("bf16", blayers, bms, bfam, args.act)
         if args.cold:
             bms = sum(bfam[p]["ms"] for p in PASSES)

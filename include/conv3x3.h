@@ -316,7 +316,10 @@ int conv3x3_bwd_weight_gnsilu(const void* x, const float* scale, const float* sh
  *     grid reaches 192 workgroups;
  *   - either dtype, smallest tile (64 x 64) whose grid is 128 to 256
  *     workgroups, with at least 32 fills (16 channels bfloat16, 8 float32):
- *     2 slices (bfloat16) or 4 (float32).
+ *     2 slices (bfloat16) or 4 (float32);
+ *   - float32, smallest tile with at most 64 workgroups and at least 4
+ *     fills of 8 channels: up to 4 slices of at least 2 fills, no more than
+ *     256 / workgroups.
  * Plain passes only (no activation, prologue, resampling or concatenation).
  * Each slice writes its partial sums (float32, one output-sized slot per
  * slice) to the workspace and a second kernel on the same stream adds the

@@ -264,6 +264,33 @@ def test_small_tile_split_rule():
     assert lib3.conv3x3_up2_workspace_size(lib3.PASS_FWD, 32, 512, 512, 16, 16, f32) == 0
 
 
+def test_tiny_grid_split_rule():
+    """float32 problems whose 64 x 64 tiles make at most 64 workgroups split
+    the reduction in up to four slices of at least two 8-channel fills, no
+    more than 256 / workgroups; bf16 and larger grids do not."""
+    f32, bf16 = lib3.CONV3X3_F32, lib3.CONV3X3_BF16
+    slot = 2 * 64 * 32 * 32 * 4  # one float32 output of N = 2, 64 channels, 32x32
+    for p in (lib3.PASS_FWD, lib3.PASS_BWD_DATA):
+        # 32 workgroups, 8 fills: four slices of two fills
+        assert lib3.conv3x3_workspace_size(p, 2, 64, 64, 32, 32, f32) == 4 * slot
+        # (the plan query describes the call without a workspace: unsplit)
+        plan = lib3.conv3x3_plan(p, 2, 64, 64, 32, 32, f32)
+        assert plan["split"] == 1 and plan["grid_x"] * plan["grid_y"] == 32
+    # 24 channels (3 fills): one slice of at least two fills only
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 2, 24, 64, 32, 32, f32) == 0
+    # 40 channels (5 fills): two slices (3 + 2 fills)
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 2, 40, 64, 32, 32, f32) == 2 * slot
+    # 160 workgroups (N = 10) is more than a quarter round: no split
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 10, 64, 64, 32, 32, f32) == 0
+    # 96 workgroups (N = 6) is too: 256 / 96 = 2 slices only at <= 64 workgroups
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 6, 64, 64, 32, 32, f32) == 0
+    # 64 workgroups (N = 4): four slices
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 4, 64, 64, 32, 32, f32) == \
+        4 * 2 * slot
+    # bf16 stays whole
+    assert lib3.conv3x3_workspace_size(lib3.PASS_FWD, 2, 64, 64, 32, 32, bf16) == 0
+
+
 def test_split_workspace_checks():
     """A bf16 small-image problem needs a workspace on the *_ws entry
     points; without one, or with too little, nothing is launched."""

@@ -57,8 +57,10 @@ def _run_plain(inp):
     import diffusion_unet_x3_amd as lib3
     dev = torch.device("cuda", 0)
     x, w, g, b = (inp[k].to(dev) for k in ("x", "w", "g", "b"))
-    y = lib3.conv3x3_fwd(x, w, b)
-    dx = lib3.conv3x3_bwd_data(g, w)
+    # (the *_cat entry points take no workspace, so they run the unsplit
+    # plan: compare with that)
+    y = lib3.conv3x3_fwd(x, w, b, split=False)
+    dx = lib3.conv3x3_bwd_data(g, w, split=False)
     dw, db = lib3.conv3x3_bwd_weight(x, g)
     torch.cuda.synchronize()
     return y.cpu(), dx.cpu(), dw.cpu(), db.cpu()

@@ -91,9 +91,15 @@ def test_split_reduction_is_reproducible():
 # 512 workgroups).
 # Beyond 8x8 tiles: 32x32 (32 x 2 tile) and 16x16 (16 x 4 tile) images with
 # 64 fills; 514 channels take the scalar staging path.
+# Grids of at most 64 workgroups (a small batch of small images), up to four
+# slices of at least two fills: 2 x 64 -> 64 at 32x32 (32 workgroups, four
+# slices of two fills), 40 -> 48 channels (two slices of 3 + 2 fills, a
+# partial channel tile), a 31 x 33 image on the scalar path (62 workgroups),
+# and 33 channels on a 5x7 image (one workgroup, the last fill one channel).
 F32_SHAPES = [(32, 512, 512, 8, 8), (24, 520, 512, 8, 8), (32, 384, 512, 8, 8),
               (32, 1024, 512, 8, 8), (2, 512, 512, 32, 32), (8, 512, 512, 16, 16),
-              (24, 514, 512, 8, 8)]
+              (24, 514, 512, 8, 8),
+              (2, 64, 64, 32, 32), (2, 40, 48, 32, 32), (2, 64, 64, 31, 33), (1, 33, 8, 5, 7)]
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
