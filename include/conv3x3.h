@@ -135,6 +135,10 @@ int conv3x3_fwd(const void* x, const void* w, const float* bias, float* y,
  *   dx : [N][C][H][W] float32 (overwritten); bfloat16 for CONV3X3_BF16_IO
  * The same implicit GEMM as the forward pass over g, with the weight tile
  * transposed (k <-> c) and rotated by 180 degrees while it is staged in LDS.
+ * dx with at most 3 channels (an image's gradient), K <= 128 and W <= 213
+ * (plain call, no fusion, g under 2 GiB) takes a kernel of its own: the
+ * 9*C (channel, tap) pairs are the rows of P = w^T g over bands of image
+ * rows, and each dx element is the sum of its nine shifted taps of P.
  */
 int conv3x3_bwd_data(const void* g, const void* w, float* dx,
                      int N, int C, int K, int H, int W, int dtype,
