@@ -22,6 +22,16 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.stdout.strip() == ""
 
 
+def test_graph_replay_refuses_cold_caches():
+    """--graph replays whole passes, so there is no point between them to
+    flush the caches: the combination is refused before anything runs."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--graph", "--cold"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--graph" in r.stderr and "--cold" in r.stderr
+    assert r.stdout.strip() == ""
+
+
 def test_stem_layer_flops_and_algorithmic_bytes():
     N, C, K, H, W = 32, 64, 64, 64, 64
     assert bench.flops_per_pass(N, C, K, H, W) == 2 * 32 * 4096 * 64 * 64 * 9
