@@ -693,8 +693,9 @@ bool launch_fwd_stem_bf16(const Plan& pl, const uint16_t* x, const uint16_t* w,
 // output pixel per channel, in a fixed order.  Eight waves take the bands'
 // 32-pixel blocks in turn, each loading its next block's operands while the
 // MFMAs of the current one run.
-// KS: g values a lane loads per 32-pixel block, K <= 2 KS.
-template <typename T, int KS>
+// KS: g values a lane loads per 32-pixel block, K <= 2 KS.  FULL: K == 2 KS
+// (no load of a block reads past the last channel).
+template <typename T, int KS, bool FULL>
 __global__ __launch_bounds__(512) void bwd_data_stem_kernel(
     const T* __restrict__ g, const T* __restrict__ w, float* __restrict__ dx, int N, int C,
     int K, int H, int W, int th, int bands, uint32_t g_bytes, int outb) {
@@ -750,16 +751,28 @@ __global__ __launch_bounds__(512) void bwd_data_stem_kernel(
   constexpr int QS = KS / 4;
   static_assert(!BF || QS % 8 == 0, "a quarter holds whole bf16 steps");
   E ba[KS], bb[KS];
+  // Load i reads channel k(i) = k0 + dk(i), k0 = hi (float32) or 8 hi
+  // (bfloat16), dk a compile-time step.  With FULL every k < K, so a lane's
+  // offsets are one base (kOutside for a pixel outside the band or the
+  // image: kOutside plus any in-range offset stays past the view) plus a
+  // wave-uniform dk(i) planes -- one add per load; otherwise each load also
+  // checks k < K.
+  const uint32_t hwb = (uint32_t)hw * (uint32_t)sizeof(T);
   auto load_q = [&](E(&dst)[KS], int blk, int qi) __attribute__((always_inline)) {
     const int q = blk * 32 + l32;
     const int row = h0 - 1 + q / W, col = q % W;
     const bool in = q < px && row >= 0 && row < H;
+    const int k0 = BF ? 8 * hi : hi;
     const uint32_t e0 = in ? (uint32_t)((long)n * K * hw + (long)row * W + col) : 0u;
+    const uint32_t base = in ? (e0 + (uint32_t)k0 * (uint32_t)hw) * (uint32_t)sizeof(T) : kOutside;
 #pragma unroll
     for (int i = qi * QS; i < (qi + 1) * QS; ++i) {
-      const int k = BF ? 16 * (i >> 3) + 8 * hi + (i & 7) : 2 * i + hi;
-      const uint32_t off =
-          in & (k < K) ? (e0 + (uint32_t)k * (uint32_t)hw) * (uint32_t)sizeof(T) : kOutside;
+      const int dk = BF ? 16 * (i >> 3) + (i & 7) : 2 * i;
+      const int k = k0 + dk;
+      const uint32_t off = FULL ? base + (uint32_t)dk * hwb
+                                : (in & (k < K) ? (e0 + (uint32_t)k * (uint32_t)hw) *
+                                                      (uint32_t)sizeof(T)
+                                                : kOutside);
       if constexpr (BF)
         dst[i] = buffer_load2(gv, off);
       else
@@ -847,12 +860,18 @@ static bool launch_bd_stem(const Plan& pl, const T* g, const T* w, float* dx, in
   const int bands = (H + pl.th - 1) / pl.th;
   const uint32_t gb = (uint32_t)((long)N * K * H * W * (long)sizeof(T));
   dim3 grid((unsigned)(N * bands)), block(512);
-  if (K <= 64)
-    hipLaunchKernelGGL((bwd_data_stem_kernel<T, 32>), grid, block, 0, stream, g, w, dx, N, C, K,
-                       H, W, pl.th, bands, gb, outb ? 1 : 0);
+#define CONV3X3_BD(KS_, FULL_)                                                            \
+  hipLaunchKernelGGL((bwd_data_stem_kernel<T, KS_, FULL_>), grid, block, 0, stream, g, w, dx, N, \
+                     C, K, H, W, pl.th, bands, gb, outb ? 1 : 0)
+  if (K == 64)
+    CONV3X3_BD(32, true);
+  else if (K < 64)
+    CONV3X3_BD(32, false);
+  else if (K == 128)
+    CONV3X3_BD(64, true);
   else
-    hipLaunchKernelGGL((bwd_data_stem_kernel<T, 64>), grid, block, 0, stream, g, w, dx, N, C, K,
-                       H, W, pl.th, bands, gb, outb ? 1 : 0);
+    CONV3X3_BD(64, false);
+#undef CONV3X3_BD
   return true;
 }
 
