@@ -46,6 +46,13 @@
  * CONV3X3_ERR_HIP.  Faults inside a kernel surface at the caller's next
  * synchronisation, as usual for HIP.
  *
+ * Graph capture: a call enqueues only kernel launches on `stream` -- no
+ * allocation, memset, copy, event or synchronisation -- so a caller may
+ * capture calls into a HIP graph (hipStreamBeginCapture on a non-null
+ * stream) and replay it; each replay recomputes every output from the
+ * pointers captured, bit for bit as the eager call (the kernels are
+ * deterministic).  Workspaces must stay allocated while the graph lives.
+ *
  * Size limits: N, C, K, H, W >= 1; every tensor holds fewer than 2^31
  * elements (else CONV3X3_ERR_BAD_SHAPE).  The compute entry points also
  * need every tensor they touch below 2 GiB counted as float32 -- N*C*H*W,
