@@ -25,8 +25,9 @@
 // 68 floats apart put 8 lanes on all 32 banks), and the staged x rows and
 // planes are padded to 3 and 9 (mod 32) floats, so column e = 9 c + 3 r + s
 // reads bank e + const.  bfloat16 values are widened to float32 as they are
-// staged: products of bfloat16 values are exact in float32, so the
-// arithmetic is that of the bfloat16 MFMA with float32 accumulation.
+// staged and run v_mfma_f32_32x32x16_bf16 on their (exact) high halves:
+// step s covers 16 pixels, lane l the eight pixels 16 s + 8 (l / 32) + j,
+// so a chunk takes 4 MFMA steps instead of 32 (the same LDS reads).
 //
 // The chunks are split over `split` slices (slice s: chunks s, s + S, ... --
 // the workgroups running at one time read neighbouring pixel rows of each g
@@ -89,8 +90,13 @@ __global__ __launch_bounds__(512) void wgrad_stem_kernel(
   constexpr int XR = stem_xr(TW);
   constexpr int XP = stem_xp(TH, TW);
   static_assert(XR % 32 == 3 && XP % 32 == 9, "bank padding");
-  // the lane of a step's second pixel (s + 32) reads this much further
+  // bfloat16 runs v_mfma_f32_32x32x16_bf16 (see compute): lanes 32-63 take
+  // pixels 8 further; float32 the step's second pixel, 32 further.  The
+  // lane's x offset for that pixel:
+  constexpr bool BF = !std::is_same<T, float>::value;
   constexpr int OFF32 = TW >= 64 ? 32 : (32 / TW) * XR;
+  constexpr int OFF8 = TW >= 16 ? 8 : XR;
+  constexpr int OFFH = BF ? OFF8 : OFF32;
   constexpr int VP = GVec<T>::kPix;             // pixels per 16-byte g load
   constexpr int GI = kStemWaveK * kStemP / VP;  // g vector items per wave and chunk
   static_assert(GI % 64 == 0, "whole g items per lane");
@@ -134,9 +140,9 @@ __global__ __launch_bounds__(512) void wgrad_stem_kernel(
     edata[b] = e < 9 * C;
     if (e < 9 * C) {
       const int c = e / 9, t = e % 9;
-      eoff[b] = c * XP + (t / 3) * XR + (t % 3) + hi * OFF32;
+      eoff[b] = c * XP + (t / 3) * XR + (t % 3) + hi * OFFH;
     } else {
-      eoff[b] = (e == 9 * C ? ones : XGI) + hi * OFF32;
+      eoff[b] = (e == 9 * C ? ones : XGI) + hi * OFFH;
     }
   }
   for (int i = tid; i < ZP; i += 512) xs[XGI + i] = 0.f;
@@ -267,6 +273,41 @@ __global__ __launch_bounds__(512) void wgrad_stem_kernel(
     int eo[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) eo[b] = eoff[b] + (edata[b] ? xb : 0);
+    if constexpr (BF) {
+      // bfloat16: step s takes pixels 16 s .. 16 s + 15, lane (l32, hi) the
+      // eight pixels 16 s + 8 hi + j -- A from its g row, B from column e's
+      // staged x (eight consecutive pixels of one row: 8 | TW), each value
+      // bfloat16 widened to float32, so its high half is exact.  All the
+      // chunk's operands are read before its four MFMA steps.
+      u32x4 aw[kStemP / 16];
+      u32x4 bw[kStemP / 16][NB];
+      auto pack = [](float lo, float hi2) __attribute__((always_inline)) {
+        return (__builtin_bit_cast(uint32_t, lo) >> 16) |
+               (__builtin_bit_cast(uint32_t, hi2) & 0xffff0000u);
+      };
+#pragma unroll
+      for (int st = 0; st < kStemP / 16; ++st) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&gsw[l32 * GS + 16 * st + 8 * hi]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&gsw[l32 * GS + 16 * st + 8 * hi + 4]);
+        aw[st] = u32x4{pack(a0[0], a0[1]), pack(a0[2], a0[3]), pack(a1[0], a1[1]),
+                       pack(a1[2], a1[3])};
+        const int pb = ((16 * st) / TW) * XR + (16 * st) % TW;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float xv8[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv8[j] = xs[eo[b] + pb + j];
+          bw[st][b] = u32x4{pack(xv8[0], xv8[1]), pack(xv8[2], xv8[3]), pack(xv8[4], xv8[5]),
+                            pack(xv8[6], xv8[7])};
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < kStemP / 16; ++st)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b][st % CH] = mfma_32x32x16_bf16(aw[st], bw[st][b], acc[b][st % CH]);
+      return;
+    }
     f32x4 av[2][GSZ / 4];
     float bv[2][NB][GSZ];
     auto read = [&](int grp, int set) __attribute__((always_inline)) {
