@@ -18,10 +18,13 @@ from parity_util import TRIPWIRE, rel_err
 
 pytestmark = pytest.mark.gpu
 
-# (first, second): the second is smaller; both need split-K scratch
+# (first, second): the second is smaller; both need split-K scratch.  The
+# few-channel pair runs the image-stem backward-weight kernel, whose
+# slices use their own slot layout ([K][32 NB] per slice).
 PAIRS = [
     ((8, 64, 64, 32, 32, "f32"), (2, 24, 40, 10, 12, "f32")),
     ((8, 64, 64, 32, 32, "bf16"), (2, 32, 24, 8, 16, "bf16")),
+    ((8, 3, 128, 64, 64, "bf16"), (2, 4, 40, 16, 24, "bf16")),
 ]
 
 
@@ -67,7 +70,7 @@ def _noalloc(lib3, x, g):
     return dw, db
 
 
-@pytest.mark.parametrize("pair", PAIRS, ids=["f32", "bf16"])
+@pytest.mark.parametrize("pair", PAIRS, ids=["f32", "bf16", "bf16_few_channel"])
 def test_noalloc_matches_plain_entry_point(pair):
     lib3 = _lib()
     for i, shape in enumerate(pair):
