@@ -14,15 +14,17 @@ ImageNet 64x64 in the sources; seeded N(0,1) activations / gradients with
 Kaiming-uniform weights stand in for that data.
 
 Prints ONE JSON line: throughput in TFLOP/s (2*N*H*W*C*K*9 per pass, three
-passes per layer), per-pass median / p10 / p90 times from HIP events on the
-stream the kernels run on, the roofline figure of the pass family that
-takes the most time, and the fp64 CPU oracle's throughput on a sampled
+passes per layer) over the step time -- each timed step one replay of a HIP
+graph holding the step's kernels (`--eager`: launched from Python instead)
+-- per-pass median / p10 / p90 times from HIP events around eager launches
+on the stream the kernels run on, the roofline figure of the pass family
+that takes the most time, and the fp64 CPU oracle's throughput on a sampled
 subset of the same outputs (test infrastructure, timed only as a reported
 baseline; its full-sweep time is extrapolated from the sample).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--workload unet_sweep|stem|small|mid|bottleneck]
-                    [--sweep OUT.json] [--cold] [--graph] [--detail OUT.json]
+                    [--workload unet_sweep|stem|small|mid|bottleneck|image_stem]
+                    [--sweep OUT.json] [--cold] [--eager] [--detail OUT.json]
 """
 import argparse
 import json
@@ -598,25 +600,15 @@ def time_runs(runs, steps, warmup, flush=None):
 
 
 def time_runs_graph(runs, steps, warmup):
-    """As time_runs, with the passes replayed from HIP graphs captured once
-    after the warmup (what a caller with launch-bound layers would do):
-    each pass's own graph between its event pair for the per-pass times,
-    and one graph holding the whole step, replayed `steps` times between
-    one event pair, for the step time.  Every input, output and workspace
-    is allocated before the capture."""
+    """Per-pass times as in time_runs (eager launches, an event pair around
+    each pass), then the step time from one HIP graph holding the whole
+    step (every pass of every run, captured once after the eager timing),
+    replayed `steps` times between one event pair -- the same kernels on
+    the same buffers, without the host's launch overhead between them.
+    Every input, output and workspace is allocated before the capture.
+    Returns (graph step ms, per-pass lists, eager step ms)."""
     import torch
-    for _ in range(warmup):
-        for run in runs:
-            for _, f in run.passes():
-                f()
-    torch.cuda.synchronize()
-    graphs = []
-    for run in runs:
-        for name, f in run.passes():
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                f()
-            graphs.append((run, name, g))
+    ms_eager, per = time_runs(runs, steps, warmup)
     step = torch.cuda.CUDAGraph()
     with torch.cuda.graph(step):
         for run in runs:
@@ -624,27 +616,15 @@ def time_runs_graph(runs, steps, warmup):
                 f()
     for _ in range(max(warmup, 1)):
         step.replay()
-    torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in graphs] for _ in range(steps)]
-    for i in range(steps):
-        for j, (_, _, g) in enumerate(graphs):
-            ev[i][j][0].record()
-            g.replay()
-            ev[i][j][1].record()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
-    for i in range(steps):
+    for _ in range(steps):
         step.replay()
     t1.record()
     torch.cuda.synchronize()
-    per = []
-    for run in runs:
-        per.append({name: [ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]
-                    for j, (r, name, _) in enumerate(graphs) if r is run})
-    return t0.elapsed_time(t1) / steps, per
+    return t0.elapsed_time(t1) / steps, per, ms_eager
 
 
 def time_layer(run, steps, warmup):
@@ -759,12 +739,21 @@ def cpu_baseline(layer, budget_s=15.0, min_s=10.0):
 def measure_layers(layers, dtype, inputs, steps, warmup, flush=None, act="none", graph=False):
     """Time the three passes of every layer (one step = all of them, in
     order).  Returns (step ms, per-layer rows with per-pass statistics,
-    per-pass totals).  act: the *_act entry points (fused activation).
-    graph: replay the passes from HIP graphs."""
+    per-pass totals, note).  act: the *_act entry points (fused
+    activation).  graph: the step time from a HIP graph of the whole step
+    (per-pass statistics stay eager); if the capture fails the eager step
+    time is used and `note` says why."""
     import torch
     runs = [LayerRun(layer, act, inputs=inputs[layer.name]) for layer in layers]
+    note = None
     if graph:
-        ms, per = time_runs_graph(runs, steps, warmup)
+        try:
+            ms, per, ms_eager = time_runs_graph(runs, steps, warmup)
+            note = {"step": "hip_graph", "eager_ms_per_step": round(ms_eager, 4)}
+        except Exception as e:  # noqa: BLE001 -- fall back to eager timing
+            torch.cuda.synchronize()
+            ms, per = time_runs(runs, steps, warmup, flush)
+            note = {"step": "eager", "graph_capture_failed": f"{type(e).__name__}: {e}"[:200]}
     else:
         ms, per = time_runs(runs, steps, warmup, flush)
     del runs
@@ -783,7 +772,7 @@ def measure_layers(layers, dtype, inputs, steps, warmup, flush=None, act="none",
             fam[p]["gflop"] += f / 1e9
             fam[p]["alg_gb"] += ab / 1e9
         rows.append(row)
-    return ms, rows, fam
+    return ms, rows, fam, note
 
 
 def sweep_summary(dtype, layers, ms, fam, act="none"):
@@ -901,8 +890,11 @@ def main():
                          "float32 (bfloat16 in an extra key); the others time one "
                          "configured layer group")
     ap.add_argument("--graph", action="store_true",
-                    help="capture the passes in HIP graphs and time their replays "
-                         "(for launch-bound layers)")
+                    help="time each step as one HIP graph replay (the default; per-pass "
+                         "times stay eager)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time each step as eager launches from Python instead of a "
+                         "HIP graph replay")
     ap.add_argument("--no-bf16", action="store_true",
                     help="unet_sweep: skip the bfloat16 sweep")
     ap.add_argument("--cold", action="store_true",
@@ -959,8 +951,12 @@ def main():
                     help="with --record-traffic: write the summary here instead of the "
                          "headline workload's record")
     args = ap.parse_args()
-    if args.graph and args.cold:
-        ap.error("--graph replays whole passes: no cache flush between them (drop --cold)")
+    if args.graph and (args.cold or args.eager):
+        ap.error("--graph replays whole passes: no cache flush between them, and not "
+                 "with --eager (drop --cold / --eager)")
+    # a step is one HIP graph replay unless caches are flushed between passes
+    # or eager launches are asked for
+    args.graph = not (args.eager or args.cold)
     if args.record_traffic:
         out = args.traffic_out or TRAFFIC_FILE
         print(json.dumps(record_traffic(*args.record_traffic, out_path=out)["passes"]))
@@ -997,8 +993,8 @@ def main():
     print(f"inputs drawn for {len(layers)} {dtype} layers in "
           f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     flush = torch.empty(512 << 18, device="cuda") if args.cold else None
-    ms, rows, fam = measure_layers(layers, dtype, inputs, args.steps, args.warmup, flush,
-                                   args.act, args.graph)
+    ms, rows, fam, note = measure_layers(layers, dtype, inputs, args.steps, args.warmup,
+                                         flush, args.act, args.graph)
     summ = sweep_summary(dtype, layers, ms, fam, args.act)
     if args.cold:
         # the step bracket holds the flushes too: the step is the passes' sum
@@ -1022,7 +1018,9 @@ def main():
               "timing": "HIP events on the kernels' stream; inputs resident in HBM; "
                         + ("512 MiB overwritten before every pass (cold caches)"
                            if args.cold else "passes back to back in sweep order")
-                        + ("; every step replayed from one HIP graph" if args.graph else "")}
+                        + ("; each timed step is one replay of a HIP graph holding the "
+                           "step's kernels (per-pass times: eager launches, an event "
+                           "pair each)" if args.graph else "; eager launches")}
     if cfg == 6:
         config["shapes"] = [list(l.shape) for l in layers]
     elif cfg == 5:
@@ -1038,6 +1036,8 @@ def main():
         "dtype": "fp32" if dtype == "f32" else "bf16", "data": "synthetic",
         "config": config, "roofline": summ["roofline"], "passes": summ["passes"],
     }
+    if note:
+        result["step_timing"] = note
     detail = {dtype: rows}
     if extra_layers and not args.no_bf16:
         blayers = extra_layers
@@ -1047,9 +1047,11 @@ def main():
             src = inputs[by_idx[l.index].name]  # the same draws, rounded to bfloat16
             binputs[l.name] = {"x": src["x"].bfloat16(), "w": src["w"].bfloat16(),
                                "b": src["b"], "g": src["g"].bfloat16()}
-        bms, brows, bfam = measure_layers(blayers, "bf16", binputs, args.steps, args.warmup,
-                                          flush, args.act, args.graph)
+        bms, brows, bfam, bnote = measure_layers(blayers, "bf16", binputs, args.steps,
+                                                 args.warmup, flush, args.act, args.graph)
         bsum = sweep_summary("bf16", blayers, bms, bfam, args.act)
+        if bnote:
+            bsum["step_timing"] = bnote
         if args.cold:
             bms = sum(bfam[p]["ms"] for p in PASSES)
             bsum["value"] = round(sum(3 * flops_per_pass(*l.shape) for l in blayers) /
